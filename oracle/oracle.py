@@ -1,0 +1,315 @@
+"""Python (ctypes + numpy) front end of the CPU oracle in moe_oracle.c.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.  It shares no code with
+the HIP library.
+
+Formats: "f32" (float32), "bf16" (uint16 bit patterns), "mxfp8" (uint8 E4M3
+codes plus uint8 E8M0 scales, one per 32 elements along the last axis).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "moe_oracle.c")
+FMT = {"f32": 0, "bf16": 1, "mxfp8": 2}
+SCORE = {"softmax": 0, "sigmoid": 1}
+_NP = {"f32": np.float32, "bf16": np.uint16, "mxfp8": np.uint8}
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", "-o", LIB_PATH, SRC_PATH, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return LIB_PATH
+
+
+_lib = None
+P = ctypes.c_void_p
+I32 = ctypes.c_int
+I64 = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "or_bf16_from_double": (ctypes.c_uint16, [ctypes.c_double]),
+        "or_double_from_bf16": (ctypes.c_double, [ctypes.c_uint16]),
+        "or_e4m3_from_double": (ctypes.c_uint8, [ctypes.c_double]),
+        "or_double_from_e4m3": (ctypes.c_double, [ctypes.c_uint8]),
+        "or_double_from_e8m0": (ctypes.c_double, [ctypes.c_uint8]),
+        "or_bf16_from_double_array": (None, [P, P, I64]),
+        "or_e4m3_from_double_array": (None, [P, P, I64]),
+        "or_double_from_e4m3_array": (None, [P, P, I64]),
+        "or_mx_quantize_f32": (I32, [P, I64, I64, P, P]),
+        "or_route": (I32, [I32, I32, I32, I32, I32, P, P, P]),
+        "or_group": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P]),
+        "or_permute": (None, [I32, I32, I64, I64, P, P, P]),
+        "or_forward_tokens": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P,
+                                    P, P]),
+        "or_combine": (None, [I32, I32, I32, I32, P, P, P, P]),
+        "or_backward": (I32, [I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, I32, P, I32, P, P, P, P,
+                              P, P, P]),
+        "or_backward_dx_tokens": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]),
+        "or_backward_dw_entries": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, I32, P, P,
+                                         P, I32, P, P, P]),
+        "or_num_threads": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if dtype is not None and a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def num_threads() -> int:
+    return _load().or_num_threads()
+
+
+# ---------------------------------------------------------------- formats
+def bf16_from_f64(v) -> np.ndarray:
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    out = np.empty(v.shape, np.uint16)
+    _load().or_bf16_from_double_array(v.ctypes.data, out.ctypes.data, v.size)
+    return out
+
+
+def f64_from_bf16(b) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def e4m3_from_f64(v) -> np.ndarray:
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    out = np.empty(v.shape, np.uint8)
+    _load().or_e4m3_from_double_array(v.ctypes.data, out.ctypes.data, v.size)
+    return out
+
+
+def f64_from_e4m3(c) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(c, dtype=np.uint8))
+    out = np.empty(c.shape, np.float64)
+    _load().or_double_from_e4m3_array(c.ctypes.data, out.ctypes.data, c.size)
+    return out
+
+
+def f64_from_e8m0(c) -> np.ndarray:
+    c = np.asarray(c, dtype=np.uint8).astype(np.int64)
+    out = np.ldexp(1.0, c - 127).astype(np.float64)
+    return np.where(c == 255, np.nan, out)
+
+
+def mx_quantize(v) -> tuple:
+    """float32 [..., n] (n % 32 == 0) -> (E4M3 codes uint8 [..., n], E8M0 uint8 [..., n/32])."""
+    v = _c(v, np.float32)
+    cols = v.shape[-1]
+    rows = v.size // cols
+    codes = np.empty(v.shape, np.uint8)
+    scales = np.empty(v.shape[:-1] + (cols // 32,), np.uint8)
+    if _load().or_mx_quantize_f32(v.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data):
+        raise ValueError("last dimension must be a multiple of 32")
+    return codes, scales
+
+
+def mx_dequantize(codes, scales) -> np.ndarray:
+    d = f64_from_e4m3(codes)
+    s = f64_from_e8m0(scales)
+    return d * np.repeat(s, 32, axis=-1)
+
+
+def decode(fmt: str, data, scale=None) -> np.ndarray:
+    """Stored values to float64."""
+    if fmt == "f32":
+        return np.asarray(data, np.float32).astype(np.float64)
+    if fmt == "bf16":
+        return f64_from_bf16(data)
+    return mx_dequantize(data, scale)
+
+
+# ---------------------------------------------------------------- the path
+def route(logits, k: int, score: str = "softmax", renorm: bool = False):
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    if _load().or_route(T, E, k, SCORE[score], int(renorm), lg.ctypes.data, idx.ctypes.data, w.ctypes.data):
+        raise ValueError("bad routing sizes")
+    return idx, w
+
+
+def group(idx, E: int, align: int = 1, R_cap: int | None = None):
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    if R_cap is None:
+        R_cap = T * k + E * (align - 1)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    row_map = np.empty((T, k), np.int32)
+    src_map = np.empty(R_cap, np.int32)
+    bad = np.zeros(1, np.int32)
+    rc = _load().or_group(T, E, k, align, R_cap, idx.ctypes.data, counts.ctypes.data, offsets.ctypes.data,
+                          row_map.ctypes.data, src_map.ctypes.data, bad.ctypes.data)
+    if rc:
+        raise ValueError(f"or_group failed ({rc})")
+    return counts, offsets, row_map, src_map, int(bad[0])
+
+
+def permute(x, row_map, n_rows: int):
+    """Rows of x (any dtype, 2-D) copied to their routes' rows; padding zero."""
+    x = np.ascontiguousarray(x)
+    row_map = _c(row_map, np.int32)
+    T, k = row_map.shape
+    row_bytes = x.strides[0]
+    xp = np.empty((n_rows,) + x.shape[1:], x.dtype)
+    _load().or_permute(T, k, n_rows, row_bytes, x.ctypes.data, row_map.ctypes.data, xp.ctypes.data)
+    return xp
+
+
+def forward_tokens(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=None, w2_scale=None,
+                   want_stash: bool = False):
+    """Per-token evaluation of the expert FFN and the combine.
+
+    x, w1, w2 are stored arrays of format shape.dtype (w1 [E, 2F, H], w2 [E, H, F]).
+    Returns dict with h [n, k, F] (+ h_scale for MXFP8), yp [n, k, H], y [n, H]
+    and (optionally) stash [n, k, 2F], all in storage form."""
+    s = shape
+    fmt = s.dtype
+    y_fmt = "f32" if fmt == "f32" else "bf16"
+    h_fmt = fmt
+    s_fmt = "f32" if fmt == "f32" else "bf16"
+    tokens = _c(np.asarray(tokens, np.int32), np.int32)
+    n = tokens.size
+    k = s.k
+    h = np.empty((n, k, s.F), _NP[h_fmt])
+    h_scale = np.empty((n, k, s.F // 32), np.uint8) if h_fmt == "mxfp8" else None
+    yp = np.empty((n, k, s.H), _NP[y_fmt])
+    y = np.empty((n, s.H), _NP[y_fmt])
+    stash = np.empty((n, k, 2 * s.F), _NP[s_fmt]) if want_stash else None
+    x = np.ascontiguousarray(x)
+    w1 = np.ascontiguousarray(w1)
+    w2 = np.ascontiguousarray(w2)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    xs = None if x_scale is None else np.ascontiguousarray(x_scale)
+    w1s = None if w1_scale is None else np.ascontiguousarray(w1_scale)
+    w2s = None if w2_scale is None else np.ascontiguousarray(w2_scale)
+    rc = _load().or_forward_tokens(s.H, s.F, k, FMT[fmt], FMT[h_fmt], FMT[y_fmt], FMT[s_fmt], n, tokens.ctypes.data,
+                                   x.ctypes.data, _p(xs), w1.ctypes.data, _p(w1s), w2.ctypes.data, _p(w2s),
+                                   idx.ctypes.data, w.ctypes.data, h.ctypes.data, _p(h_scale), yp.ctypes.data,
+                                   _p(stash), y.ctypes.data)
+    if rc:
+        raise ValueError("or_forward_tokens: unsupported sizes")
+    out = {"h": h, "yp": yp, "y": y}
+    if h_scale is not None:
+        out["h_scale"] = h_scale
+    if stash is not None:
+        out["stash"] = stash
+    return out
+
+
+def combine(yp, row_map, w, y_fmt: str):
+    yp = np.ascontiguousarray(yp)
+    row_map = _c(row_map, np.int32)
+    w = _c(w, np.float32)
+    T, k = row_map.shape
+    H = yp.shape[1]
+    y = np.empty((T, H), _NP[y_fmt])
+    _load().or_combine(T, H, k, FMT[y_fmt], yp.ctypes.data, row_map.ctypes.data, w.ctypes.data, y.ctypes.data)
+    return y
+
+
+def backward(shape, x, w1, w2, w, row_map, src_map, offsets, h_rows, stash_rows, dy):
+    """Full backward (small shapes).  h_rows [R_cap, F] / stash_rows [R_cap, 2F]
+    are the forward's stored h and stash arranged by permuted row."""
+    s = shape
+    fmt = s.dtype
+    g_fmt = "f32" if fmt == "f32" else "bf16"
+    R_cap = src_map.shape[0]
+    gdt = _NP[g_fmt]
+    dyp = np.zeros((R_cap, s.H), gdt)
+    dgu = np.zeros((R_cap, 2 * s.F), gdt)
+    dxp = np.zeros((R_cap, s.H), gdt)
+    dx = np.empty((s.T, s.H), gdt)
+    dw1 = np.empty((s.E, 2 * s.F, s.H), np.float32)
+    dw2 = np.empty((s.E, s.H, s.F), np.float32)
+    args = [np.ascontiguousarray(a) for a in (x, w1, w2)]
+    w = _c(w, np.float32)
+    row_map = _c(row_map, np.int32)
+    src_map = _c(src_map, np.int32)
+    offsets = _c(offsets, np.int32)
+    h_rows = np.ascontiguousarray(h_rows)
+    stash_rows = np.ascontiguousarray(stash_rows)
+    dy = np.ascontiguousarray(dy)
+    rc = _load().or_backward(s.T, s.H, s.F, s.E, s.k, FMT[fmt], FMT[g_fmt], args[0].ctypes.data, args[1].ctypes.data,
+                             args[2].ctypes.data, w.ctypes.data, row_map.ctypes.data, src_map.ctypes.data,
+                             offsets.ctypes.data, h_rows.ctypes.data, FMT[fmt], stash_rows.ctypes.data,
+                             FMT[g_fmt], dy.ctypes.data, dyp.ctypes.data, dgu.ctypes.data, dxp.ctypes.data,
+                             dx.ctypes.data, dw1.ctypes.data, dw2.ctypes.data)
+    if rc:
+        raise ValueError("or_backward: unsupported format")
+    return {"dyp": dyp, "dgu": dgu, "dxp": dxp, "dx": dx, "dw1": dw1, "dw2": dw2}
+
+
+def backward_dx_tokens(shape, tokens, x, w1, w2, idx, w, dy):
+    s = shape
+    fmt = s.dtype
+    g_fmt = "f32" if fmt == "f32" else "bf16"
+    tokens = _c(np.asarray(tokens, np.int32), np.int32)
+    dx = np.empty((tokens.size, s.H), _NP[g_fmt])
+    a = [np.ascontiguousarray(v) for v in (x, w1, w2, dy)]
+    rc = _load().or_backward_dx_tokens(s.H, s.F, s.k, FMT[fmt], FMT[g_fmt], FMT[fmt], FMT[g_fmt], tokens.size,
+                                       tokens.ctypes.data, a[0].ctypes.data, a[1].ctypes.data, a[2].ctypes.data,
+                                       _c(idx, np.int32).ctypes.data, _c(w, np.float32).ctypes.data,
+                                       a[3].ctypes.data, dx.ctypes.data)
+    if rc:
+        raise ValueError("unsupported")
+    return dx
+
+
+def backward_dw_entries(shape, e, x, w1, w2, w, src_map, offsets, dy, dw2_idx, dw1_idx):
+    """dW2s[e][o, f] for (o, f) in dw2_idx and dW1s[e][n, c] for (n, c) in dw1_idx (float64)."""
+    s = shape
+    fmt = s.dtype
+    g_fmt = "f32" if fmt == "f32" else "bf16"
+    dw2_idx = np.asarray(dw2_idx, np.int32).reshape(-1, 2)
+    dw1_idx = np.asarray(dw1_idx, np.int32).reshape(-1, 2)
+    o2 = np.ascontiguousarray(dw2_idx[:, 0])
+    f2 = np.ascontiguousarray(dw2_idx[:, 1])
+    n1 = np.ascontiguousarray(dw1_idx[:, 0])
+    c1 = np.ascontiguousarray(dw1_idx[:, 1])
+    out2 = np.empty(len(o2), np.float64)
+    out1 = np.empty(len(n1), np.float64)
+    a = [np.ascontiguousarray(v) for v in (x, w1, w2, dy)]
+    rc = _load().or_backward_dw_entries(s.H, s.F, s.k, FMT[fmt], FMT[g_fmt], FMT[fmt], FMT[g_fmt], int(e),
+                                        a[0].ctypes.data, a[1].ctypes.data, a[2].ctypes.data,
+                                        _c(w, np.float32).ctypes.data, _c(src_map, np.int32).ctypes.data,
+                                        _c(offsets, np.int32).ctypes.data, a[3].ctypes.data, len(o2),
+                                        o2.ctypes.data, f2.ctypes.data, out2.ctypes.data, len(n1), n1.ctypes.data,
+                                        c1.ctypes.data, out1.ctypes.data)
+    if rc:
+        raise ValueError("unsupported")
+    return out2, out1
