@@ -1,0 +1,257 @@
+"""Benchmark of the MoE FFN hot path on one MI355X.
+
+One step = one pass of the whole forward hot path (route -> permute -> grouped
+gate/up GEMM + SwiGLU -> grouped down GEMM -> top-k combine, the fused
+moe_forward call) over one batch of seeded synthetic input already resident in
+HBM.  Default workload: the Mixtral-shaped layer (T=8192, H=4096, F=14336,
+E=8, top-2 softmax, bf16 with fp32 accumulation).  With --backward the step
+also runs the FFN backward (skewed workload).
+
+Prints one JSON line: tokens/s of the layer, per-kernel times measured with
+HIP events on the launch stream, the roofline of the dominant kernel (the
+grouped gate/up GEMM) and the CPU oracle timed on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="mixtral_bf16")
+    p.add_argument("--cpu-sample", type=int, default=96, help="tokens of the oracle CPU baseline (0 = skip)")
+    p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                   help="HBM bytes per dispatch measured with rocprofv3 counters (optional)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the MoE layer; multi-GPU runs are not part of this build "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import routing_permute_grouped_router_amd as moe
+    from routing_permute_grouped_router_amd import workload as wl
+
+    s = wl.BY_NAME[args.workload]
+    cfg = moe.MoEConfig.from_shape(s)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    w = wl.Workload(s)
+    t_gen = time.time()
+
+    def up(a, fmt):
+        if fmt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    logits = up(w.logits(), "f32")
+    gen_fmt = "bf16" if s.dtype == "bf16" else "f32"
+    x = up(w.x(), gen_fmt)
+    # weights expert by expert (bounded host memory)
+    sd = cfg.store_dtype
+    w1 = torch.empty(s.E, 2 * s.F, s.H, dtype=sd, device=dev)
+    w2 = torch.empty(s.E, s.H, s.F, dtype=sd, device=dev)
+    scales = {}
+    if s.dtype == "mxfp8":
+        scales["w1_scale"] = torch.empty(s.E, 2 * s.F, s.H // 32, dtype=torch.uint8, device=dev)
+        scales["w2_scale"] = torch.empty(s.E, s.H, s.F // 32, dtype=torch.uint8, device=dev)
+        xq = torch.empty(s.T, s.H, dtype=torch.uint8, device=dev)
+        scales["x_scale"] = torch.empty(s.T, s.H // 32, dtype=torch.uint8, device=dev)
+        moe.moe_quantize_mxfp8(x, xq, scales["x_scale"])
+        x = xq
+    step_e = max(1, (1 << 28) // (2 * s.F * s.H))
+    for e0 in range(0, s.E, step_e):
+        e1 = min(s.E, e0 + step_e)
+        a1, a2 = up(w.w1(e0, e1), gen_fmt), up(w.w2(e0, e1), gen_fmt)
+        if s.dtype == "mxfp8":
+            moe.moe_quantize_mxfp8(a1, w1[e0:e1], scales["w1_scale"][e0:e1])
+            moe.moe_quantize_mxfp8(a2, w2[e0:e1], scales["w2_scale"][e0:e1])
+        else:
+            w1[e0:e1].copy_(a1)
+            w2[e0:e1].copy_(a2)
+        del a1, a2
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    buf = moe.alloc_forward(cfg, training=s.backward)
+    bwd = moe.alloc_backward(cfg) if s.backward else None
+    dy = up(w.dy(), "bf16" if s.dtype != "f32" else "f32") if s.backward else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_forward(cfg, logits, x, w1, w2, buf, **scales)
+        if s.backward:
+            moe.moe_backward(cfg, dy, w1, w2, buf, bwd)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.time()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.time() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # Per-kernel durations: the same step issued call by call, events between
+    # the calls on the launch stream.
+    names = ["route", "permute", "swiglu_gemm", "down_gemm", "combine"]
+    if s.backward:
+        names += ["combine_bwd", "down_bwd", "swiglu_bwd", "permute_bwd"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    acc = {n: 0.0 for n in names}
+    g = {k: v for k, v in scales.items()}
+
+    def staged():
+        ev[0].record(stream)
+        moe.moe_route(cfg, logits, buf["idx"], buf["w"])
+        ev[1].record(stream)
+        moe.moe_permute(cfg, x, buf["idx"], buf["xp"], buf["counts"], buf["offsets"], buf["row_map"],
+                        buf["src_map"], buf["ws"], x_scale=g.get("x_scale"), xp_scale=buf.get("xp_scale"),
+                        err=buf["err"])
+        ev[2].record(stream)
+        moe.moe_grouped_swiglu_gemm(cfg, buf["xp"], w1, buf["offsets"], buf["h"], xp_scale=buf.get("xp_scale"),
+                                    w1_scale=g.get("w1_scale"), h_scale=buf.get("h_scale"),
+                                    gu_stash=buf.get("gu_stash"))
+        ev[3].record(stream)
+        moe.moe_grouped_down_gemm(cfg, buf["h"], w2, buf["offsets"], buf["yp"], h_scale=buf.get("h_scale"),
+                                  w2_scale=g.get("w2_scale"))
+        ev[4].record(stream)
+        moe.moe_combine(cfg, buf["yp"], buf["row_map"], buf["w"], buf["y"])
+        ev[5].record(stream)
+        if s.backward:
+            moe.moe_combine_bwd(cfg, dy, buf["src_map"], buf["offsets"], buf["w"], bwd["dyp"])
+            ev[6].record(stream)
+            moe.moe_grouped_down_bwd(cfg, bwd["dyp"], w2, buf["h"], buf["gu_stash"], buf["offsets"], bwd["dgu"],
+                                     bwd["dw2"], bwd["ws"])
+            ev[7].record(stream)
+            moe.moe_grouped_swiglu_bwd(cfg, bwd["dgu"], w1, buf["xp"], buf["offsets"], bwd["dxp"], bwd["dw1"],
+                                       bwd["ws"])
+            ev[8].record(stream)
+            moe.moe_permute_bwd(cfg, bwd["dxp"], buf["row_map"], bwd["dx"])
+            ev[9].record(stream)
+
+    staged()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        staged()
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    kern_ms = {n: acc[n] / args.steps for n in names}
+
+    R, T, H, F, E, k = s.R, s.T, s.H, s.F, s.E, s.k
+    esz = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32}[s.dtype]
+    osz = 4 if s.dtype == "f32" else 2
+    flops = {"swiglu_gemm": 4.0 * R * H * F, "down_gemm": 2.0 * R * H * F}
+    # algorithmic bytes (each operand read once, each output written once)
+    bytes_ = {
+        "route": T * E * 4 + T * k * 8,
+        "permute": T * k * 4 + T * H * esz + R * H * esz + T * k * 4 + R * 4,
+        "combine": R * H * osz + T * H * osz + T * k * 8,
+    }
+    peak_mm = {"f32": PEAK_FP32_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "mxfp8": PEAK_FP8_TFLOPS}[s.dtype]
+    kern = {}
+    for n in names:
+        d = {"ms": round(kern_ms[n], 4)}
+        if n in flops:
+            tf = flops[n] / (kern_ms[n] * 1e-3) / 1e12
+            d.update(tflops=round(tf, 1), frac_mfma=round(tf / peak_mm, 4))
+        if n in bytes_:
+            gbs = bytes_[n] / (kern_ms[n] * 1e-3) / 1e9
+            d.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        kern[n] = d
+
+    traffic = None
+    try:
+        tr = json.load(open(args.traffic))
+        if tr.get("workload") == s.name and tr.get("kernel") == "swiglu_gemm":
+            traffic = tr.get("bytes_per_dispatch")
+    except (OSError, ValueError):
+        pass
+    tf = flops["swiglu_gemm"] / (kern_ms["swiglu_gemm"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "grouped_gemm_swiglu", "achieved": round(tf, 2), "peak": peak_mm,
+                "unit": "TFLOP/s", "frac": round(tf / peak_mm, 4), "traffic": traffic,
+                "flops_per_launch": flops["swiglu_gemm"]}
+
+    cpu = None
+    if args.cpu_sample > 0:
+        from oracle import oracle as orc
+
+        lg = w.logits()
+        xs = w.x()
+        n = min(args.cpu_sample, T)
+        rng = np.random.default_rng(s.seed + 6)
+        toks = np.sort(rng.choice(T, n, replace=False)).astype(np.int32)
+        w1h, w2h = w.w1(), w.w2()
+        if s.dtype == "mxfp8":
+            xs, xsc = orc.mx_quantize(xs)
+            w1h, w1sc = orc.mx_quantize(w1h)
+            w2h, w2sc = orc.mx_quantize(w2h)
+        else:
+            xsc = w1sc = w2sc = None
+        t0 = time.time()
+        idx_o, w_o = orc.route(lg, k, s.score, s.renorm)
+        orc.group(idx_o, E, s.align)
+        t_route = time.time() - t0
+        t0 = time.time()
+        orc.forward_tokens(s, toks, xs, w1h, w2h, idx_o, w_o, xsc, w1sc, w2sc)
+        t_ffn = time.time() - t0
+        per_tok = t_ffn / n + t_route / T
+        cpu = {"value": round(1.0 / per_tok, 3), "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
+               "sample": f"route+group over all {T} tokens ({t_route:.2f} s), expert FFN + combine of {n} "
+                         f"seeded tokens ({t_ffn:.2f} s); tokens/s = 1 / (FFN s per token + routing s per token)"}
+
+    out = {
+        "metric": "MoE layer tokens/s; grouped-GEMM TFLOP/s as % of MFMA peak; permute GB/s",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8-e4m3"}[s.dtype],
+        "data": "synthetic",
+        "config": {"workload": s.name, "T": T, "H": H, "F": F, "E": E, "k": k, "score": s.score,
+                   "renorm": s.renorm, "storage": s.dtype, "accumulate": "f32", "backward": s.backward,
+                   "parallelism": "single GPU"},
+        "kernels": kern,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(t_wall, 3),
+        "setup_s": round(t_gen, 1),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

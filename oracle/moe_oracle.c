@@ -301,7 +301,8 @@ int or_route(int T, int E, int k, int score, int renorm, const float* logits, in
  *                 ascending (t, j) order within their expert's block; -1 for a
  *                 dropped route
  * src_map[row]  = t*k + j for a real row, -1 for padding and the unused tail
- * Ids outside [-1, E) are treated as dropped and counted in *n_bad.
+ * Ids outside [-1, E), and an id repeated within one token's k slots (top-k
+ * never repeats an expert), are treated as dropped and counted in *n_bad.
  * Returns 0, 1 on bad sizes, 2 if R_cap is too small.
  */
 int or_group(int T, int E, int k, int align, int64_t R_cap, const int32_t* idx, int32_t* counts,
@@ -309,15 +310,23 @@ int or_group(int T, int E, int k, int align, int64_t R_cap, const int32_t* idx, 
     if (T < 0 || E <= 0 || k <= 0 || align <= 0) return 1;
     int32_t bad = 0;
     for (int e = 0; e < E; ++e) counts[e] = 0;
+    /* route (t, j) is live when its id is in [0, E) and no earlier slot of
+     * token t holds the same id (top-k never repeats an expert; a repeat in a
+     * caller's table is dropped and counted like an out-of-range id) */
+    unsigned char* live = (unsigned char*)malloc((size_t)T * k + 1);
     for (int64_t i = 0; i < (int64_t)T * k; ++i) {
         int32_t e = idx[i];
+        live[i] = 0;
         if (e == -1) continue;
-        if (e < -1 || e >= E) { ++bad; continue; }
+        int dup = 0;
+        for (int64_t q = i - i % k; q < i; ++q) dup |= idx[q] == e;
+        if (e < -1 || e >= E || dup) { ++bad; continue; }
+        live[i] = 1;
         counts[e] += 1;
     }
     offsets[0] = 0;
     for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + ((counts[e] + align - 1) / align) * align;
-    if ((int64_t)offsets[E] > R_cap) return 2;
+    if ((int64_t)offsets[E] > R_cap) { free(live); return 2; }
     for (int64_t r = 0; r < R_cap; ++r) src_map[r] = -1;
     int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
     for (int e = 0; e < E; ++e) cursor[e] = offsets[e];
@@ -325,13 +334,14 @@ int or_group(int T, int E, int k, int align, int64_t R_cap, const int32_t* idx, 
         for (int j = 0; j < k; ++j) {
             int64_t i = (int64_t)t * k + j;
             int32_t e = idx[i];
-            if (e < 0 || e >= E) { row_map[i] = -1; continue; }
+            if (!live[i]) { row_map[i] = -1; continue; }
             int32_t row = cursor[e]++;
             row_map[i] = row;
             src_map[row] = (int32_t)i;
         }
     }
     free(cursor);
+    free(live);
     if (n_bad) *n_bad = bad;
     return 0;
 }

@@ -1,0 +1,343 @@
+// C ABI of the MoE hot path: argument validation and kernel launches.
+// Every entry point only enqueues work on the caller's stream (no allocation,
+// no synchronisation, no device-to-host copy).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return MOE_OK;
+    if (e == hipErrorNotSupported) return fail(MOE_ERR_UNSUPPORTED, "%s: not built for this configuration", what);
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define REQUIRE(ptr)                                                              \
+    do {                                                                          \
+        if ((ptr) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #ptr); \
+    } while (0)
+
+int64_t rows_capacity(const moe_config& c) { return (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1); }
+
+// Sizes and enums; does not look at pointers.
+moe_status check_config(const moe_config* cfg) {
+    if (!cfg) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+    const moe_config& c = *cfg;
+    if (c.T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", c.T);
+    if (c.E < 1 || c.E > kMaxExperts) return fail(MOE_ERR_INVALID_ARG, "E must be in [1, %d] (got %d)", kMaxExperts, c.E);
+    if (c.k < 1 || c.k > c.E || c.k > kMaxTopK)
+        return fail(MOE_ERR_INVALID_ARG, "k must be in [1, min(E, %d)] (got k=%d, E=%d)", kMaxTopK, c.k, c.E);
+    if (c.align < 1) return fail(MOE_ERR_INVALID_ARG, "align must be >= 1 (got %d)", c.align);
+    if (c.H < 1 || c.F < 1) return fail(MOE_ERR_INVALID_ARG, "H and F must be positive (got H=%d, F=%d)", c.H, c.F);
+    if (c.score != MOE_SOFTMAX && c.score != MOE_SIGMOID)
+        return fail(MOE_ERR_INVALID_ARG, "score must be MOE_SOFTMAX or MOE_SIGMOID (got %d)", c.score);
+    if (c.renorm != 0 && c.renorm != 1) return fail(MOE_ERR_INVALID_ARG, "renorm must be 0 or 1 (got %d)", c.renorm);
+    if (c.dtype != MOE_F32 && c.dtype != MOE_BF16 && c.dtype != MOE_MXFP8)
+        return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32, MOE_BF16 or MOE_MXFP8 (got %d)", c.dtype);
+    if (rows_capacity(c) >= (int64_t)1 << 31)
+        return fail(MOE_ERR_INVALID_ARG, "T*k + E*(align-1) must be below 2^31");
+    if ((int64_t)c.T * c.H >= (int64_t)1 << 40) return fail(MOE_ERR_INVALID_ARG, "T*H too large");
+    return MOE_OK;
+}
+
+// Shapes the GEMM and row kernels are built for.
+moe_status check_shapes(const moe_config& c) {
+    if (c.H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "H must be a multiple of 128 (got %d)", c.H);
+    if (c.F % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "F must be a multiple of 64 (got %d)", c.F);
+    return MOE_OK;
+}
+
+moe_status check_ws(const moe_config& c, const void* ws, size_t ws_bytes) {
+    const size_t need = moe_workspace_size(&c);
+    if (need == 0) return MOE_OK;
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu%s)", need, ws_bytes,
+                    ws ? "" : ", ws is NULL");
+    return MOE_OK;
+}
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_rows_capacity(const moe_config* cfg) {
+    if (check_config(cfg) != MOE_OK) return -1;
+    return rows_capacity(*cfg);
+}
+
+size_t moe_workspace_size(const moe_config* cfg) {
+    if (check_config(cfg) != MOE_OK) return 0;
+    const moe_config& c = *cfg;
+    const size_t group = round256((size_t)group_n_chunks(c.T, c.E) * c.E * sizeof(int32_t));
+    const size_t bwd = c.dtype == MOE_MXFP8 ? 0 : round256(bwd_workspace_bytes(c));
+    return group > bwd ? group : bwd;
+}
+
+moe_status moe_route(const moe_config* cfg, const float* logits, int32_t* idx, float* w, void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    if (cfg->T > 0) {
+        REQUIRE(logits);
+        REQUIRE(idx);
+        REQUIRE(w);
+    }
+    return hip_status(launch_route(*cfg, logits, idx, w, as_stream(stream)), "moe_route");
+}
+
+moe_status moe_permute(const moe_config* cfg, const void* x, const uint8_t* x_scale, const int32_t* idx, void* xp,
+                       uint8_t* xp_scale, int32_t* counts, int32_t* offsets, int32_t* row_map, int32_t* src_map,
+                       int32_t* err, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    const moe_config& c = *cfg;
+    if (c.dtype == MOE_MXFP8 && c.H % kMxBlock) return fail(MOE_ERR_UNSUPPORTED, "MXFP8 needs H % 32 == 0");
+    REQUIRE(counts);
+    REQUIRE(offsets);
+    if (rows_capacity(c) > 0) REQUIRE(src_map);
+    if (c.T > 0) {
+        REQUIRE(x);
+        REQUIRE(idx);
+        REQUIRE(xp);
+        REQUIRE(row_map);
+        if (c.dtype == MOE_MXFP8) {
+            REQUIRE(x_scale);
+            REQUIRE(xp_scale);
+        }
+    }
+    if ((st = check_ws(c, ws, ws_bytes))) return st;
+    hipStream_t s = as_stream(stream);
+    if ((st = hip_status(launch_group(c, idx, counts, offsets, row_map, src_map, err, (int32_t*)ws, s), "moe_permute")))
+        return st;
+    return hip_status(launch_permute_rows(c, x, x_scale, row_map, counts, offsets, xp, xp_scale, s), "moe_permute");
+}
+
+moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const uint8_t* xp_scale, const void* w1,
+                                   const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
+                                   void* gu_stash, void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    const moe_config& c = *cfg;
+    if ((st = check_shapes(c))) return st;
+    if (rows_capacity(c) == 0) return MOE_OK;
+    REQUIRE(xp);
+    REQUIRE(w1);
+    REQUIRE(offsets);
+    REQUIRE(h);
+    hipStream_t s = as_stream(stream);
+    switch (c.dtype) {
+    case MOE_BF16:
+        return hip_status(launch_swiglu_gemm_bf16(c, (const uint16_t*)xp, (const uint16_t*)w1, offsets, (uint16_t*)h,
+                                                  (uint16_t*)gu_stash, s),
+                          "moe_grouped_swiglu_gemm");
+    case MOE_F32:
+        return hip_status(
+            launch_swiglu_gemm_f32(c, (const float*)xp, (const float*)w1, offsets, (float*)h, (float*)gu_stash, s),
+            "moe_grouped_swiglu_gemm");
+    default:
+        REQUIRE(xp_scale);
+        REQUIRE(w1_scale);
+        REQUIRE(h_scale);
+        return hip_status(launch_swiglu_gemm_mxfp8(c, (const uint8_t*)xp, xp_scale, (const uint8_t*)w1, w1_scale,
+                                                   offsets, (uint8_t*)h, h_scale, (uint16_t*)gu_stash, s),
+                          "moe_grouped_swiglu_gemm");
+    }
+}
+
+moe_status moe_grouped_down_gemm(const moe_config* cfg, const void* h, const uint8_t* h_scale, const void* w2,
+                                 const uint8_t* w2_scale, const int32_t* offsets, void* yp, void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    const moe_config& c = *cfg;
+    if ((st = check_shapes(c))) return st;
+    if (rows_capacity(c) == 0) return MOE_OK;
+    REQUIRE(h);
+    REQUIRE(w2);
+    REQUIRE(offsets);
+    REQUIRE(yp);
+    hipStream_t s = as_stream(stream);
+    switch (c.dtype) {
+    case MOE_BF16:
+        return hip_status(
+            launch_down_gemm_bf16(c, (const uint16_t*)h, (const uint16_t*)w2, offsets, (uint16_t*)yp, s),
+            "moe_grouped_down_gemm");
+    case MOE_F32:
+        return hip_status(launch_down_gemm_f32(c, (const float*)h, (const float*)w2, offsets, (float*)yp, s),
+                          "moe_grouped_down_gemm");
+    default:
+        REQUIRE(h_scale);
+        REQUIRE(w2_scale);
+        return hip_status(launch_down_gemm_mxfp8(c, (const uint8_t*)h, h_scale, (const uint8_t*)w2, w2_scale, offsets,
+                                                 (uint16_t*)yp, s),
+                          "moe_grouped_down_gemm");
+    }
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* yp, const int32_t* row_map, const float* w, void* y,
+                       void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    if ((st = check_shapes(*cfg))) return st;
+    if (cfg->T > 0) {
+        REQUIRE(yp);
+        REQUIRE(row_map);
+        REQUIRE(w);
+        REQUIRE(y);
+    }
+    return hip_status(launch_combine(*cfg, yp, row_map, w, y, as_stream(stream)), "moe_combine");
+}
+
+moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x, const uint8_t* x_scale,
+                       const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, void* y,
+                       int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* row_map,
+                       int32_t* src_map, void* xp, uint8_t* xp_scale, void* h, uint8_t* h_scale, void* yp,
+                       void* gu_stash, int32_t* err, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    const moe_config& c = *cfg;
+    if ((st = check_shapes(c))) return st;
+    REQUIRE(w1);
+    REQUIRE(w2);
+    if (c.dtype == MOE_MXFP8) {
+        REQUIRE(w1_scale);
+        REQUIRE(w2_scale);
+    }
+    if ((st = moe_route(cfg, logits, idx, w, stream))) return st;
+    if ((st = moe_permute(cfg, x, x_scale, idx, xp, xp_scale, counts, offsets, row_map, src_map, err, ws, ws_bytes,
+                          stream)))
+        return st;
+    if ((st = moe_grouped_swiglu_gemm(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, gu_stash, stream)))
+        return st;
+    if ((st = moe_grouped_down_gemm(cfg, h, h_scale, w2, w2_scale, offsets, yp, stream))) return st;
+    return moe_combine(cfg, yp, row_map, w, y, stream);
+}
+
+moe_status moe_combine_bwd(const moe_config* cfg, const void* dy, const int32_t* src_map, const int32_t* offsets,
+                           const float* w, void* dyp, void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    if (cfg->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "the backward takes F32 or BF16 storage");
+    if ((st = check_shapes(*cfg))) return st;
+    REQUIRE(offsets);
+    if (rows_capacity(*cfg) > 0) {
+        REQUIRE(dy);
+        REQUIRE(src_map);
+        REQUIRE(w);
+        REQUIRE(dyp);
+    }
+    return hip_status(launch_combine_bwd(*cfg, dy, src_map, offsets, w, dyp, as_stream(stream)), "moe_combine_bwd");
+}
+
+moe_status moe_grouped_down_bwd(const moe_config* cfg, const void* dyp, const void* w2, const void* h,
+                                const void* gu_stash, const int32_t* offsets, void* dgu, float* dw2, void* ws,
+                                size_t ws_bytes, void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    if (cfg->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "the backward takes F32 or BF16 storage");
+    if ((st = check_shapes(*cfg))) return st;
+    REQUIRE(w2);
+    REQUIRE(dw2);
+    REQUIRE(offsets);
+    if ((st = check_ws(*cfg, ws, ws_bytes))) return st;
+    if (rows_capacity(*cfg) > 0) {
+        REQUIRE(dyp);
+        REQUIRE(h);
+        REQUIRE(gu_stash);
+        REQUIRE(dgu);
+    }
+    return hip_status(launch_down_bwd(*cfg, dyp, w2, h, gu_stash, offsets, dgu, dw2, ws, as_stream(stream)),
+                      "moe_grouped_down_bwd");
+}
+
+moe_status moe_grouped_swiglu_bwd(const moe_config* cfg, const void* dgu, const void* w1, const void* xp,
+                                  const int32_t* offsets, void* dxp, float* dw1, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    if (cfg->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "the backward takes F32 or BF16 storage");
+    if ((st = check_shapes(*cfg))) return st;
+    REQUIRE(w1);
+    REQUIRE(dw1);
+    REQUIRE(offsets);
+    if ((st = check_ws(*cfg, ws, ws_bytes))) return st;
+    if (rows_capacity(*cfg) > 0) {
+        REQUIRE(dgu);
+        REQUIRE(xp);
+        REQUIRE(dxp);
+    }
+    return hip_status(launch_swiglu_bwd(*cfg, dgu, w1, xp, offsets, dxp, dw1, ws, as_stream(stream)),
+                      "moe_grouped_swiglu_bwd");
+}
+
+moe_status moe_permute_bwd(const moe_config* cfg, const void* dxp, const int32_t* row_map, void* dx, void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    if (cfg->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "the backward takes F32 or BF16 storage");
+    if ((st = check_shapes(*cfg))) return st;
+    if (cfg->T > 0) {
+        REQUIRE(dxp);
+        REQUIRE(row_map);
+        REQUIRE(dx);
+    }
+    return hip_status(launch_permute_bwd(*cfg, dxp, row_map, dx, as_stream(stream)), "moe_permute_bwd");
+}
+
+moe_status moe_backward(const moe_config* cfg, const void* dy, const float* w, const void* w1, const void* w2,
+                        const int32_t* offsets, const int32_t* row_map, const int32_t* src_map, const void* xp,
+                        const void* h, const void* gu_stash, void* dyp, void* dgu, void* dxp, void* dx, float* dw1,
+                        float* dw2, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st;
+    if ((st = moe_combine_bwd(cfg, dy, src_map, offsets, w, dyp, stream))) return st;
+    if ((st = moe_grouped_down_bwd(cfg, dyp, w2, h, gu_stash, offsets, dgu, dw2, ws, ws_bytes, stream))) return st;
+    if ((st = moe_grouped_swiglu_bwd(cfg, dgu, w1, xp, offsets, dxp, dw1, ws, ws_bytes, stream))) return st;
+    return moe_permute_bwd(cfg, dxp, row_map, dx, stream);
+}
+
+moe_status moe_quantize_mxfp8(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                              void* stream) {
+    if (rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "rows and cols must be >= 0");
+    if (cols % kMxBlock) return fail(MOE_ERR_INVALID_ARG, "cols must be a multiple of 32 (got %lld)", (long long)cols);
+    if (rows * cols > 0) {
+        REQUIRE(in);
+        REQUIRE(codes);
+        REQUIRE(scales);
+    }
+    return hip_status(launch_quantize_mxfp8(in, rows, cols, codes, scales, as_stream(stream)), "moe_quantize_mxfp8");
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_version(void) { return "moe-gfx950 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Internal declarations of the MoE HIP library (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;              // CDNA wavefront width
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 64;
+constexpr int kMxBlock = 32;
+
+// ----------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round-to-nearest-even float32 -> bfloat16 (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// --------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// --------------------------------------------------------- host launchers
+// Each returns hipSuccess or the launch error; arguments were validated by
+// the API layer.
+hipError_t launch_route(const moe_config& c, const float* logits, int32_t* idx, float* w, hipStream_t s);
+
+// Grouping.  chunk_tokens(T,E) tokens per counting chunk; ws holds
+// n_chunks(T,E) * E int32.
+int group_chunk_tokens(int T, int E);
+int group_n_chunks(int T, int E);
+hipError_t launch_group(const moe_config& c, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                        int32_t* row_map, int32_t* src_map, int32_t* err, int32_t* ws, hipStream_t s);
+hipError_t launch_permute_rows(const moe_config& c, const void* x, const uint8_t* x_scale, const int32_t* row_map,
+                               const int32_t* counts, const int32_t* offsets, void* xp, uint8_t* xp_scale,
+                               hipStream_t s);
+
+hipError_t launch_combine(const moe_config& c, const void* yp, const int32_t* row_map, const float* w, void* y,
+                          hipStream_t s);
+hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const int32_t* src_map, const int32_t* offsets,
+                              const float* w, void* dyp, hipStream_t s);
+hipError_t launch_permute_bwd(const moe_config& c, const void* dxp, const int32_t* row_map, void* dx,
+                              hipStream_t s);
+
+// Grouped GEMMs.
+hipError_t launch_swiglu_gemm_bf16(const moe_config& c, const uint16_t* xp, const uint16_t* w1,
+                                   const int32_t* offsets, uint16_t* h, uint16_t* stash, hipStream_t s);
+hipError_t launch_down_gemm_bf16(const moe_config& c, const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
+                                 uint16_t* yp, hipStream_t s);
+hipError_t launch_swiglu_gemm_f32(const moe_config& c, const float* xp, const float* w1, const int32_t* offsets,
+                                  float* h, float* stash, hipStream_t s);
+hipError_t launch_down_gemm_f32(const moe_config& c, const float* h, const float* w2, const int32_t* offsets,
+                                float* yp, hipStream_t s);
+
+// MXFP8
+hipError_t launch_quantize_mxfp8(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s);
+hipError_t launch_swiglu_gemm_mxfp8(const moe_config& c, const uint8_t* xp, const uint8_t* xp_scale,
+                                    const uint8_t* w1, const uint8_t* w1_scale, const int32_t* offsets, uint8_t* h,
+                                    uint8_t* h_scale, uint16_t* stash, hipStream_t s);
+hipError_t launch_down_gemm_mxfp8(const moe_config& c, const uint8_t* h, const uint8_t* h_scale, const uint8_t* w2,
+                                  const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, hipStream_t s);
+
+// Backward GEMMs (bf16 / f32 storage).
+size_t bwd_workspace_bytes(const moe_config& c);
+hipError_t launch_down_bwd(const moe_config& c, const void* dyp, const void* w2, const void* h, const void* stash,
+                           const int32_t* offsets, void* dgu, float* dw2, void* ws, hipStream_t s);
+hipError_t launch_swiglu_bwd(const moe_config& c, const void* dgu, const void* w1, const void* xp,
+                             const int32_t* offsets, void* dxp, float* dw1, void* ws, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,49 @@
+// MXFP8 (OCP E4M3 elements, E8M0 scale per 32 consecutive elements).
+//
+// The block-32 scaled format is the MXFP8 BlockScaledTensor of the
+// cudnn-frontend page "Add MoE + expert-parallel Python API surface, PyTorch
+// reference, and tests" (review comment on BlockScaledTensor) and the grouped
+// MXFP8 quantisation listed by the tracking issue "MoE training
+// optimization".  The conversion rule is the public OCP Microscaling (MX)
+// Formats v1.0 one: shared exponent floor(log2(amax)) - 8 (E4M3's largest
+// exponent), clamped to the E8M0 range; elements rounded to nearest even,
+// saturating at +-448.
+#include "moe_internal.h"
+#include "mxfp8.h"
+
+namespace moe {
+namespace {
+
+// 8 lanes per block of 32 values, 4 values (16 bytes) per lane.
+__global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const float* __restrict__ in, int64_t n_blocks,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t blk = gid >> 3;
+    const bool live = blk < n_blocks;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) v = ((const float4*)in)[gid];
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if (!live) return;
+    const int se = mx_shared_exp(amax);
+    const uint32_t packed = (uint32_t)e4m3_rne(ldexpf(v.x, -se)) | ((uint32_t)e4m3_rne(ldexpf(v.y, -se)) << 8) |
+                            ((uint32_t)e4m3_rne(ldexpf(v.z, -se)) << 16) |
+                            ((uint32_t)e4m3_rne(ldexpf(v.w, -se)) << 24);
+    ((uint32_t*)codes)[gid] = packed;
+    if ((gid & 7) == 0) scales[blk] = (uint8_t)(se + 127);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_mxfp8(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s) {
+    const int64_t n_blocks = rows * (cols / kMxBlock);
+    if (n_blocks == 0) return hipSuccess;
+    const int64_t threads = n_blocks * 8;
+    quantize_mxfp8_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(in, n_blocks, codes, scales);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,95 @@
+"""The C ABI without a GPU: the library loads, exports every entry point
+include/moe.h declares, and rejects bad arguments on the host before any
+launch (status codes and messages)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routing_permute_grouped_router_amd as moe
+from routing_permute_grouped_router_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(b.EXPORTED) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def _cfg(**kw):
+    base = dict(T=64, H=128, F=64, E=8, k=2, align=1, score=0, renorm=0, dtype=1)
+    base.update(kw)
+    return b.moe_config(*[base[n] for n, _ in b.moe_config._fields_])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=9), b.MOE_ERR_INVALID_ARG),
+    (dict(k=0), b.MOE_ERR_INVALID_ARG),
+    (dict(E=0), b.MOE_ERR_INVALID_ARG),
+    (dict(E=2000), b.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), b.MOE_ERR_INVALID_ARG),
+    (dict(align=0), b.MOE_ERR_INVALID_ARG),
+    (dict(score=5), b.MOE_ERR_INVALID_ARG),
+    (dict(dtype=7), b.MOE_ERR_INVALID_ARG),
+])
+def test_bad_config_rejected_on_host(kw, status):
+    lib = moe.load_library()
+    c = _cfg(**kw)
+    st = lib.moe_route(ctypes.byref(c), 1, 1, 1, None)
+    assert st == status
+    assert lib.moe_last_error()
+
+
+def test_null_pointers_rejected():
+    lib = moe.load_library()
+    c = _cfg()
+    assert lib.moe_route(ctypes.byref(c), None, 1, 1, None) == b.MOE_ERR_INVALID_ARG
+    assert b"logits" in lib.moe_last_error()
+    assert lib.moe_combine(ctypes.byref(c), 1, None, 1, 1, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, 1, 1, 1, None) == b.MOE_ERR_INVALID_ARG
+
+
+def test_unsupported_shapes():
+    lib = moe.load_library()
+    c = _cfg(H=96)
+    assert lib.moe_grouped_swiglu_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, None, None) == \
+        b.MOE_ERR_UNSUPPORTED
+    c = _cfg(F=40)
+    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_checks():
+    lib = moe.load_library()
+    c = _cfg(T=5000, E=128, k=8)
+    need = lib.moe_workspace_size(ctypes.byref(c))
+    assert need > 0
+    st = lib.moe_permute(ctypes.byref(c), 1, None, 1, 1, None, 1, 1, 1, 1, None, 1, need - 1, None)
+    assert st == b.MOE_ERR_WORKSPACE
+    assert lib.moe_rows_capacity(ctypes.byref(c)) == 5000 * 8
+    c2 = _cfg(T=5000, E=128, k=8, align=128)
+    assert lib.moe_rows_capacity(ctypes.byref(c2)) == 5000 * 8 + 128 * 127
+
+
+def test_quantize_rejects_ragged_cols():
+    lib = moe.load_library()
+    assert lib.moe_quantize_mxfp8(1, 4, 33, 1, 1, None) == b.MOE_ERR_INVALID_ARG
+
+
+def test_python_layer_type_errors():
+    import torch
+    cfg = moe.MoEConfig(4, 128, 64, 8, 2)
+    with pytest.raises(ValueError):  # CPU tensors are refused before any call
+        moe.moe_route(cfg, torch.zeros(4, 8), torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2))
