@@ -37,6 +37,10 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=96, help="tokens of the oracle CPU baseline (0 = skip)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="HBM bytes per dispatch measured with rocprofv3 counters (optional)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="also run a plain device copy of this many MiB (reference for counter scaling)")
+    p.add_argument("--only", default="", help="comma list of staged kernels to run in the per-kernel loop "
+                   "(for profiling one kernel); default all")
     return p.parse_args()
 
 
@@ -156,6 +160,14 @@ def main():
             ev[8].record(stream)
             moe.moe_permute_bwd(cfg, bwd["dxp"], buf["row_map"], bwd["dx"])
             ev[9].record(stream)
+
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     staged()
     torch.cuda.synchronize()
