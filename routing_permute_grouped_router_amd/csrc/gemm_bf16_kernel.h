@@ -79,7 +79,7 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("s_barrier" ::: "memory");
 }
 
-template <bool SWIGLU, int SWZ, int GM>
+template <bool SWIGLU, int SWZ, int GM, int EARLY = 0>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     constexpr int BK = 64;                  // K depth of one stage
     constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
@@ -194,21 +194,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             if (more) {
 #pragma unroll
                 for (int i = 0; i < LOADS / 2; ++i) GG_LOAD_A(kt + 1, st ^ 1, i);
+                if (EARLY) {
+#pragma unroll
+                    for (int i = 0; i < LOADS / 2; ++i) GG_LOAD_B(kt + 1, st ^ 1, i);
+                }
             }
             GG_MFMAS(fa0, fb0);
             GG_READ(st, 2, fa0, fb0);
             if (more) {
 #pragma unroll
                 for (int i = LOADS / 2; i < LOADS; ++i) GG_LOAD_A(kt + 1, st ^ 1, i);
+                if (EARLY) {
+#pragma unroll
+                    for (int i = LOADS / 2; i < LOADS; ++i) GG_LOAD_B(kt + 1, st ^ 1, i);
+                }
             }
             GG_MFMAS(fa1, fb1);
             GG_READ(st, 3, fa1, fb1);
-            if (more) {
+            if (more && !EARLY) {
 #pragma unroll
                 for (int i = 0; i < LOADS / 2; ++i) GG_LOAD_B(kt + 1, st ^ 1, i);
             }
             GG_MFMAS(fa0, fb0);
-            if (more) {
+            if (more && !EARLY) {
 #pragma unroll
                 for (int i = LOADS / 2; i < LOADS; ++i) GG_LOAD_B(kt + 1, st ^ 1, i);
             }
