@@ -34,18 +34,85 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixtral_bf16")
-    p.add_argument("--cpu-sample", type=int, default=96, help="tokens of the oracle CPU baseline (0 = skip)")
+    p.add_argument("--cpu-sample", type=int, default=256, help="tokens of the oracle CPU baseline (0 = skip)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="HBM bytes per dispatch measured with rocprofv3 counters (optional)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="also run a plain device copy of this many MiB (reference for counter scaling)")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
+                        "--copy-calibration run into the traffic file and exit (no GPU needed)")
     p.add_argument("--only", default="", help="comma list of staged kernels to run in the per-kernel loop "
                    "(for profiling one kernel); default all")
     return p.parse_args()
 
 
+# Sources of the dominant kernel per storage dtype: measured traffic is used
+# only while these files are unchanged.
+GEMM1_SOURCES = {
+    "bf16": ["gemm_bf16_kernel.h", "gemm_bf16.hip", "tiles.h", "moe_internal.h"],
+    "mxfp8": ["gemm_mxfp8_kernel.h", "gemm_bf16_kernel.h", "mxfp8.hip", "mxfp8.h", "tiles.h", "moe_internal.h"],
+    "f32": ["gemm_f32.hip", "tiles.h", "moe_internal.h"],
+}
+GEMM1_KERNEL = {"bf16": "grouped_gemm_bf16<true", "mxfp8": "grouped_gemm_mxfp8<true", "f32": "grouped_gemm_f32<true"}
+
+
+def kernel_source_hash(dtype: str) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in GEMM1_SOURCES[dtype]:
+        with open(os.path.join(ROOT, "routing_permute_grouped_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str, out_path: str) -> None:
+    """Per-dispatch HBM bytes of the grouped GEMM1 from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the ratio the same counter shows for the
+    largest plain device copy in the run (the --copy-calibration copy)."""
+    import csv
+    import collections
+
+    import numpy as np
+
+    from routing_permute_grouped_router_amd import workload as wl
+
+    s = wl.BY_NAME[workload]
+    res = {}
+    for cnt, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per = collections.defaultdict(list)
+        copies = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != cnt:
+                continue
+            v = float(r["Counter_Value"])
+            if "copyBuffer" in r["Kernel_Name"]:
+                copies.append(v)
+            per[r["Kernel_Name"].split("(")[0]].append(v)
+        kib_copy = max(copies)  # the calibration copy of `cal` MiB is the largest copy
+        res[cnt] = (per, kib_copy)
+    cal_kib = res["WRITE_SIZE"][1]  # written bytes of a copy are its size (checked below)
+    f_scale = cal_kib / res["FETCH_SIZE"][1]
+    w_scale = 1.0
+    name = [n for n in res["FETCH_SIZE"][0] if GEMM1_KERNEL[s.dtype] in n][0]
+    fetch = float(np.mean(res["FETCH_SIZE"][0][name])) * f_scale * 1024
+    write = float(np.mean(res["WRITE_SIZE"][0][name])) * w_scale * 1024
+    out = {"workload": workload, "kernel": "swiglu_gemm", "kernel_name": name,
+           "source_hash": kernel_source_hash(s.dtype), "bytes_per_dispatch": round(fetch + write),
+           "fetch_bytes": round(fetch), "write_bytes": round(write), "copy_kib": cal_kib,
+           "fetch_scale": round(f_scale, 4), "write_scale": w_scale}
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the MoE layer; multi-GPU runs are not part of this build "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -187,6 +254,8 @@ def main():
         "route": T * E * 4 + T * k * 8,
         "permute": T * k * 4 + T * H * esz + R * H * esz + T * k * 4 + R * 4,
         "combine": R * H * osz + T * H * osz + T * k * 8,
+        "swiglu_gemm": R * H * esz + E * 2 * F * H * esz + R * F * esz,
+        "down_gemm": R * F * esz + E * H * F * esz + R * H * osz,
     }
     peak_mm = {"f32": PEAK_FP32_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "mxfp8": PEAK_FP8_TFLOPS}[s.dtype]
     kern = {}
@@ -203,14 +272,24 @@ def main():
     traffic = None
     try:
         tr = json.load(open(args.traffic))
-        if tr.get("workload") == s.name and tr.get("kernel") == "swiglu_gemm":
+        if (tr.get("workload") == s.name and tr.get("kernel") == "swiglu_gemm"
+                and tr.get("source_hash") == kernel_source_hash(s.dtype)):
             traffic = tr.get("bytes_per_dispatch")
     except (OSError, ValueError):
         pass
     tf = flops["swiglu_gemm"] / (kern_ms["swiglu_gemm"] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "grouped_gemm_swiglu", "achieved": round(tf, 2), "peak": peak_mm,
-                "unit": "TFLOP/s", "frac": round(tf / peak_mm, 4), "traffic": traffic,
-                "flops_per_launch": flops["swiglu_gemm"]}
+    if s.dtype == "mxfp8":
+        # MXFP8 weights are streamed once at ~433 FLOP/B, below the MXFP8 ridge
+        # (5000 TFLOP/s / 8 TB/s = 625 FLOP/B): the kernel is HBM-bound.
+        gbs = bytes_["swiglu_gemm"] / (kern_ms["swiglu_gemm"] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "grouped_gemm_mxfp8_swiglu", "achieved": round(gbs, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "bytes_per_launch": bytes_["swiglu_gemm"], "tflops": round(tf, 1),
+                    "frac_mfma": round(tf / peak_mm, 4)}
+    else:
+        roofline = {"bound": "mfma", "kernel": "grouped_gemm_swiglu", "achieved": round(tf, 2), "peak": peak_mm,
+                    "unit": "TFLOP/s", "frac": round(tf / peak_mm, 4), "traffic": traffic,
+                    "flops_per_launch": flops["swiglu_gemm"]}
 
     cpu = None
     if args.cpu_sample > 0:
@@ -221,17 +300,27 @@ def main():
         n = min(args.cpu_sample, T)
         rng = np.random.default_rng(s.seed + 6)
         toks = np.sort(rng.choice(T, n, replace=False)).astype(np.int32)
-        w1h, w2h = w.w1(), w.w2()
-        if s.dtype == "mxfp8":
-            xs, xsc = orc.mx_quantize(xs)
-            w1h, w1sc = orc.mx_quantize(w1h)
-            w2h, w2sc = orc.mx_quantize(w2h)
-        else:
-            xsc = w1sc = w2sc = None
         t0 = time.time()
         idx_o, w_o = orc.route(lg, k, s.score, s.renorm)
         orc.group(idx_o, E, s.align)
         t_route = time.time() - t0
+        # host weights of the experts the sample uses (the others stay zero pages)
+        need = np.unique(idx_o[toks])
+        mx = s.dtype == "mxfp8"
+        wdt = {"f32": np.float32, "bf16": np.uint16, "mxfp8": np.uint8}[s.dtype]
+        w1h = np.zeros((E, 2 * F, H), wdt)
+        w2h = np.zeros((E, H, F), wdt)
+        xsc = w1sc = w2sc = None
+        if mx:
+            xs, xsc = orc.mx_quantize(xs)
+            w1sc = np.zeros((E, 2 * F, H // 32), np.uint8)
+            w2sc = np.zeros((E, H, F // 32), np.uint8)
+        for e in need[need >= 0]:
+            a1, a2 = w.w1(int(e), int(e) + 1)[0], w.w2(int(e), int(e) + 1)[0]
+            if mx:
+                (w1h[e], w1sc[e]), (w2h[e], w2sc[e]) = orc.mx_quantize(a1), orc.mx_quantize(a2)
+            else:
+                w1h[e], w2h[e] = a1, a2
         t0 = time.time()
         orc.forward_tokens(s, toks, xs, w1h, w2h, idx_o, w_o, xsc, w1sc, w2sc)
         t_ffn = time.time() - t0

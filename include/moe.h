@@ -88,7 +88,7 @@ typedef enum moe_score { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
 typedef struct moe_config {
     int32_t T;      /* tokens (>= 0)                                         */
     int32_t H;      /* hidden size (multiple of 64; of 128 for MXFP8)        */
-    int32_t F;      /* per-expert FFN width (multiple of 64)                 */
+    int32_t F;      /* per-expert FFN width (multiple of 64; of 128 for MXFP8) */
     int32_t E;      /* experts (1..1024)                                     */
     int32_t k;      /* routes per token (1..min(E, 64))                      */
     int32_t align;  /* per-expert row alignment (>= 1)                       */
@@ -176,7 +176,8 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
                        void* gu_stash, int32_t* err, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------- */
-/* Backward of the expert FFN and the combine (F32 / BF16 storage).        */
+/* Backward of the expert FFN and the combine.  Built for BF16 storage;    */
+/* F32 and MXFP8 configs return MOE_ERR_UNSUPPORTED.                       */
 /* [TE-EP]: weight gradients of experts with no rows are zero; d_x keeps x's */
 /* dtype.  [CUDNN]: the backward re-dispatches the output gradient along the */
 /* forward routes and recomputes SwiGLU from the saved stash.  The routing   */

@@ -61,6 +61,11 @@ moe_status check_config(const moe_config* cfg) {
 moe_status check_shapes(const moe_config& c) {
     if (c.H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "H must be a multiple of 128 (got %d)", c.H);
     if (c.F % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "F must be a multiple of 64 (got %d)", c.F);
+    // one expert's weights are addressed with 32-bit byte offsets
+    if ((int64_t)c.F * c.H >= (int64_t)1 << 29)
+        return fail(MOE_ERR_UNSUPPORTED, "F*H must be below 2^29 (got F=%d, H=%d)", c.F, c.H);
+    if (c.dtype == MOE_MXFP8 && c.F % 128 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "MXFP8 needs F to be a multiple of 128 (got %d)", c.F);
     return MOE_OK;
 }
 

@@ -64,21 +64,6 @@ __device__ __forceinline__ int swz(int row) {
     return SWZ == 1 ? (((row >> 1) ^ (row >> 3)) & 3) : ((row >> 1) & 3);
 }
 
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0] in
-// bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Workgroup barrier for LDS data: this wave's LDS reads have returned before
-// it; outstanding global loads (later ring stages) are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __asm__ volatile("s_barrier" ::: "memory");
-}
-
 template <bool SWIGLU, int SWZ, int GM, int EARLY = 0>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     constexpr int BK = 64;                  // K depth of one stage
@@ -131,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             const int r = wid * 64 + i * RPL + lrow;  // tile row 0..255
             const int chunk = lslot ^ swz<SWZ>(r);
             const int ar = min(row0 + r, row_end - 1);
-            aoff[i] = (uint32_t)(((size_t)ar * K + chunk * 8) * 2);
+            aoff[i] = (uint32_t)(((size_t)(ar - row0) * K + chunk * 8) * 2);
             int br;
             if (SWIGLU) {
                 const int f = min(nt * 128 + (r & 127), p.n_out - 1);
@@ -141,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             }
             boff[i] = (uint32_t)(((size_t)br * K + chunk * 8) * 2);
         }
-        const char* abase = (const char*)p.A;
+        const char* abase = (const char*)(p.A + (size_t)row0 * K);  // A offsets are tile-relative
         const char* bbase = (const char*)(p.B + (size_t)e * p.b_rows * K);
 
         f32x16 acc[4][4];
@@ -234,202 +219,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         __syncthreads();  // every wave done with both stages before the next tile's loads
 
         // epilogue: lane holds column (lane & 31) and rows 8*(q/4) + 4*(lane/32) + q%4
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int r = row0 + wm * 128 + mi * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                if (r >= row_end) continue;
-                if (SWIGLU) {
-#pragma unroll
-                    for (int ni = 0; ni < 2; ++ni) {
-                        const int f = nt * 128 + wn * 64 + ni * 32 + (lane & 31);
-                        if (f >= p.n_out) continue;
-                        const float g = acc[mi][ni][q], u = acc[mi][ni + 2][q];
-                        p.C[(size_t)r * p.n_out + f] = f32_to_bf16(silu(g) * u);
-                        if (p.stash) {
-                            p.stash[(size_t)r * 2 * p.n_out + f] = f32_to_bf16(g);
-                            p.stash[(size_t)r * 2 * p.n_out + p.n_out + f] = f32_to_bf16(u);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const int n = nt * kTile + wn * 128 + ni * 32 + (lane & 31);
-                        if (n < p.n_out) p.C[(size_t)r * p.n_out + n] = f32_to_bf16(acc[mi][ni][q]);
-                    }
-                }
-            }
-        }
-    }
-}
-
-}  // namespace gemm
-}  // namespace moe
-
-namespace moe {
-namespace gemm {
-
-// Ring-buffered variant: STAGES LDS stages of depth BK.  The barrier that
-// publishes K step k+1 sits before the last MFMA group of step k, so the first
-// fragment reads of step k+1 overlap MFMAs of step k, and right after it the
-// loads of step k+STAGES go into the buffer step k has just released: STAGES
-// K steps of global-load latency are hidden.  Stage indices are compile-time
-// (the K loop is unrolled by STAGES).
-template <bool SWIGLU, int SWZ, int GM, int BK, int STAGES>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_ring(Args p) {
-    constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
-    constexpr int RPL = 64 / CH;            // rows per wave-wide load
-    constexpr int LOADS = 64 / RPL;         // loads per wave per operand per stage
-    constexpr int LPT = 2 * LOADS;          // loads per thread per stage
-    constexpr int STAGE_ELEMS = kTile * BK; // one operand of one stage
-    constexpr int SUB = BK / 16;            // MFMA K sub-steps per stage
-    static_assert(SUB % 2 == 0, "fragment double buffering needs an even sub-step count");
-    static_assert((STAGES - 1) * LPT < 64, "vmcnt range");
-
-    // one array per stage, so the compiler can tell the stage being refilled by
-    // DMA from the stage being read and adds no wait between them
-    __shared__ __attribute__((aligned(1024))) uint16_t lds0[2 * STAGE_ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds1[STAGES > 1 ? 2 * STAGE_ELEMS : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds2[STAGES > 2 ? 2 * STAGE_ELEMS : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds3[STAGES > 3 ? 2 * STAGE_ELEMS : 8];
-    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
-#define GR_BUF(s) ((s) == 0 ? lds0 : (s) == 1 ? lds1 : (s) == 2 ? lds2 : lds3)
-    __shared__ int32_t pre[kMaxExperts + 1];
-    __shared__ int scan_tmp[kThreads / 64];
-
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wm = wid >> 1, wn = wid & 1;
-    const int total_m = build_tile_prefix(p.offsets, p.E, kTile, pre, scan_tmp);
-    const int cols_per_tile = SWIGLU ? kTile / 2 : kTile;
-    const int n_tiles = (p.n_out + cols_per_tile - 1) / cols_per_tile;
-    const int total = total_m * n_tiles;
-
-    const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
-    const int lb = blockIdx.x / kXcds;
-    const int t_begin = (int)((int64_t)total * xcd / kXcds), t_end = (int)((int64_t)total * (xcd + 1) / kXcds);
-
-    const int K = p.K;
-    const int nk = K / BK;
-    const int lrow = lane / CH, lslot = lane % CH;
-
-    int arow[4], brow[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) arow[mi] = wm * 128 + mi * 32 + (lane & 31);
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-        brow[ni] = SWIGLU ? (ni < 2 ? 0 : 128) + wn * 64 + (ni & 1) * 32 + (lane & 31)
-                          : wn * 128 + ni * 32 + (lane & 31);
-
-    for (int t = t_begin + lb; t < t_end; t += per_xcd) {
-        int mt, nt;
-        tile_coords(t, total_m, n_tiles, GM, &mt, &nt);
-        const int e = find_expert(pre, p.E, mt);
-        const int row_end = min(p.offsets[e + 1], p.rows);
-        const int row0 = p.offsets[e] + (mt - pre[e]) * kTile;
-        if (row0 < 0 || row0 >= row_end) continue;  // only for inconsistent offsets
-
-        uint32_t aoff[LOADS], boff[LOADS];
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int r = wid * 64 + i * RPL + lrow;
-            const int chunk = lslot ^ swz<SWZ, CH>(r);
-            const int ar = min(row0 + r, row_end - 1);
-            aoff[i] = (uint32_t)(((size_t)ar * K + chunk * 8) * 2);
-            int br;
-            if (SWIGLU) {
-                const int f = min(nt * 128 + (r & 127), p.n_out - 1);
-                br = r < 128 ? f : p.n_out + f;
-            } else {
-                br = min(nt * kTile + r, p.n_out - 1);
-            }
-            boff[i] = (uint32_t)(((size_t)br * K + chunk * 8) * 2);
-        }
-        const char* abase = (const char*)p.A;
-        const char* bbase = (const char*)(p.B + (size_t)e * p.b_rows * K);
-
-        f32x16 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-#define GR_ISSUE(kt, stage)                                                                              \
-    _Pragma("unroll") for (int i = 0; i < LOADS; ++i) {                                                  \
-        __builtin_amdgcn_global_load_lds((glb_void*)(abase + aoff[i] + (size_t)(kt) * (BK * 2)),          \
-                                         (lds_void*)&GR_BUF(stage)[(wid * 64 + i * RPL) * BK], 16, 0, 0); \
-        __builtin_amdgcn_global_load_lds((glb_void*)(bbase + boff[i] + (size_t)(kt) * (BK * 2)),          \
-                                         (lds_void*)&GR_BUF(stage)[STAGE_ELEMS + (wid * 64 + i * RPL) * BK], 16, 0, 0); \
-    }
-#define GR_READ(stage, kk, FA, FB)                                                                       \
-    {                                                                                                    \
-        const int c_ = (kk) * 2 + (lane >> 5);                                                            \
-        _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) FA[mi] = __builtin_bit_cast(                    \
-            bf16x8, *(const uint4*)(&GR_BUF(stage)[arow[mi] * BK + ((c_ ^ swz<SWZ, CH>(arow[mi])) << 3)])); \
-        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) FB[ni] = __builtin_bit_cast(                    \
-            bf16x8, *(const uint4*)(&GR_BUF(stage)[STAGE_ELEMS + brow[ni] * BK + ((c_ ^ swz<SWZ, CH>(brow[ni])) << 3)])); \
-    }
-#define GR_MFMAS(FA, FB)                                                                                 \
-    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)    \
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0);
-
-        // prologue: all STAGES buffers loading
-#pragma unroll
-        for (int s = 0; s < STAGES; ++s)
-            if (s < nk) {
-                GR_ISSUE(s, s);
-            }
-        {
-            const int later = min(STAGES - 1, nk - 1);  // stages issued after stage 0
-#define GR_WAIT_LATER(L)                                                  \
-    {                                                                     \
-        if ((L) <= 0) wait_vmcnt<0>();                                    \
-        else if ((L) == 1) wait_vmcnt<LPT>();                             \
-        else if ((L) == 2) wait_vmcnt<(STAGES >= 3 ? 2 * LPT : 0)>();     \
-        else wait_vmcnt<(STAGES >= 4 ? 3 * LPT : 0)>();                   \
-    }
-            GR_WAIT_LATER(later);
-        }
-        lds_barrier();
-
-        bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-        GR_READ(0, 0, fa0, fb0);
-        for (int kb = 0; kb < nk; kb += STAGES) {
-#pragma unroll
-            for (int s = 0; s < STAGES; ++s) {
-                const int kt = kb + s;
-                if (kt < nk) {
-                    // invariant: fa0/fb0 hold sub-step 0 of stage s
-#pragma unroll
-                    for (int kk = 0; kk < SUB; kk += 2) {
-                        GR_READ(s, kk + 1, fa1, fb1);
-                        GR_MFMAS(fa0, fb0);
-                        if (kk + 2 < SUB) {
-                            GR_READ(s, kk + 2, fa0, fb0);
-                        } else if (kt + 1 < nk) {
-                            // publish step kt+1; buffer s is free once every wave passed here
-                            const int later = min(STAGES - 2, nk - 2 - kt);
-                            GR_WAIT_LATER(later);
-                            lds_barrier();
-                            if (kt + STAGES < nk) {
-                                GR_ISSUE(kt + STAGES, s);
-                            }
-                            GR_READ((s + 1) % STAGES, 0, fa0, fb0);
-                        }
-                        GR_MFMAS(fa1, fb1);
-                    }
-                }
-            }
-        }
-#undef GR_ISSUE
-#undef GR_READ
-#undef GR_MFMAS
-#undef GR_WAIT_LATER
-#undef GR_BUF
-        lds_barrier();  // every wave done with the ring before the next tile's loads
-
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll

@@ -69,6 +69,11 @@ def test_unsupported_shapes():
         b.MOE_ERR_UNSUPPORTED
     c = _cfg(F=40)
     assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+    c = _cfg(F=192, dtype=b.MOE_MXFP8)  # MXFP8 tiles F by 128
+    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, 1, 1, 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+    assert b"128" in lib.moe_last_error()
+    c = _cfg(H=32768, F=16384)  # one expert's weights must stay below 2^32 bytes
+    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
 
 
 def test_workspace_checks():
