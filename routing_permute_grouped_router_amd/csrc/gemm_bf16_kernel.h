@@ -64,6 +64,17 @@ __device__ __forceinline__ int swz(int row) {
     return SWZ == 1 ? (((row >> 1) ^ (row >> 3)) & 3) : ((row >> 1) & 3);
 }
 
+// Epilogue helpers.  GE_STAGE_TILE writes one 32 x 32 fp32 accumulator tile
+// (lane = column, slot q = row 8 (q / 4) + 4 (lane / 32) + q % 4) into a
+// wavefront-private LDS tile with a 33-float row pitch; GE_PACK8 packs eight
+// floats of an array into bf16 (round to nearest even) as one 16-byte word.
+#define GE_STAGE_TILE(BUF, ACC)                                                                          \
+    _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                      \
+        BUF[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * 33 + (lane & 31)] = (ACC)[q];
+#define GE_PACK8(V, O)                                                                                   \
+    make_uint4(pack_bf16x2((V)[(O)], (V)[(O) + 1]), pack_bf16x2((V)[(O) + 2], (V)[(O) + 3]),            \
+               pack_bf16x2((V)[(O) + 4], (V)[(O) + 5]), pack_bf16x2((V)[(O) + 6], (V)[(O) + 7]))
+
 template <bool SWIGLU, int SWZ, int GM, int EARLY = 0>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     constexpr int BK = 64;                  // K depth of one stage
@@ -218,34 +229,69 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #undef GG_ISSUE
         __syncthreads();  // every wave done with both stages before the next tile's loads
 
-        // epilogue: lane holds column (lane & 31) and rows 8*(q/4) + 4*(lane/32) + q%4
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int r = row0 + wm * 128 + mi * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                if (r >= row_end) continue;
-                if (SWIGLU) {
-#pragma unroll
-                    for (int ni = 0; ni < 2; ++ni) {
-                        const int f = nt * 128 + wn * 64 + ni * 32 + (lane & 31);
-                        if (f >= p.n_out) continue;
-                        const float g = acc[mi][ni][q], u = acc[mi][ni + 2][q];
-                        p.C[(size_t)r * p.n_out + f] = f32_to_bf16(silu(g) * u);
-                        if (p.stash) {
-                            p.stash[(size_t)r * 2 * p.n_out + f] = f32_to_bf16(g);
-                            p.stash[(size_t)r * 2 * p.n_out + p.n_out + f] = f32_to_bf16(u);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const int n = nt * kTile + wn * 128 + ni * 32 + (lane & 31);
-                        if (n < p.n_out) p.C[(size_t)r * p.n_out + n] = f32_to_bf16(acc[mi][ni][q]);
-                    }
-                }
-            }
+        // Epilogue through LDS, one 32 x 32 accumulator tile at a time per
+        // wavefront: the MFMA layout (lane = column, 16 rows per lane) is
+        // turned into 16 consecutive columns of one row per lane, so every
+        // store is 16 bytes wide.
+        float* wb = (float*)&lds[0][0][0] + wid * 2 * (32 * 33 + 32);
+        float* wb2 = wb + 32 * 33 + 32;
+        const int rr = lane >> 1, cc = (lane & 1) * 16;
+        if (SWIGLU) {
+#define GB_EPI_SW(MI, NI)                                                                                \
+    {                                                                                                    \
+        GE_STAGE_TILE(wb, acc[MI][NI])                                                                   \
+        GE_STAGE_TILE(wb2, acc[MI][(NI) + 2])                                                            \
+        __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
+        float gv[16], uv[16];                                                                            \
+        _Pragma("unroll") for (int j = 0; j < 16; ++j) {                                                 \
+            gv[j] = wb[rr * 33 + cc + j];                                                                \
+            uv[j] = wb2[rr * 33 + cc + j];                                                               \
+        }                                                                                                \
+        __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
+        const int r = row0 + wm * 128 + (MI) * 32 + rr;                                                  \
+        const int f = nt * 128 + wn * 64 + (NI) * 32 + cc;                                               \
+        if (r < row_end && f < p.n_out) {                                                                \
+            uint4* dst = (uint4*)(p.C + (size_t)r * p.n_out + f);                                        \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j) dst[j] = make_uint4(                          \
+                pack_bf16x2(silu(gv[8 * j]) * uv[8 * j], silu(gv[8 * j + 1]) * uv[8 * j + 1]),           \
+                pack_bf16x2(silu(gv[8 * j + 2]) * uv[8 * j + 2], silu(gv[8 * j + 3]) * uv[8 * j + 3]),   \
+                pack_bf16x2(silu(gv[8 * j + 4]) * uv[8 * j + 4], silu(gv[8 * j + 5]) * uv[8 * j + 5]),   \
+                pack_bf16x2(silu(gv[8 * j + 6]) * uv[8 * j + 6], silu(gv[8 * j + 7]) * uv[8 * j + 7]));  \
+            if (p.stash) {                                                                               \
+                uint4* gs = (uint4*)(p.stash + (size_t)r * 2 * p.n_out + f);                             \
+                uint4* us = (uint4*)(p.stash + (size_t)r * 2 * p.n_out + p.n_out + f);                   \
+                _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                         \
+                    gs[j] = GE_PACK8(gv, 8 * j);                                                         \
+                    us[j] = GE_PACK8(uv, 8 * j);                                                         \
+                }                                                                                        \
+            }                                                                                            \
+        }                                                                                                \
+    }
+            GB_EPI_SW(0, 0) GB_EPI_SW(0, 1) GB_EPI_SW(1, 0) GB_EPI_SW(1, 1)
+            GB_EPI_SW(2, 0) GB_EPI_SW(2, 1) GB_EPI_SW(3, 0) GB_EPI_SW(3, 1)
+#undef GB_EPI_SW
+        } else {
+#define GB_EPI_DN(MI, NI)                                                                                \
+    {                                                                                                    \
+        GE_STAGE_TILE(wb, acc[MI][NI])                                                                   \
+        __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
+        float v[16];                                                                                     \
+        _Pragma("unroll") for (int j = 0; j < 16; ++j) v[j] = wb[rr * 33 + cc + j];                      \
+        __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
+        const int r = row0 + wm * 128 + (MI) * 32 + rr;                                                  \
+        const int n = nt * kTile + wn * 128 + (NI) * 32 + cc;                                            \
+        if (r < row_end && n < p.n_out) {                                                                \
+            uint4* dst = (uint4*)(p.C + (size_t)r * p.n_out + n);                                        \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j) dst[j] = GE_PACK8(v, 8 * j);                  \
+        }                                                                                                \
+    }
+            GB_EPI_DN(0, 0) GB_EPI_DN(0, 1) GB_EPI_DN(0, 2) GB_EPI_DN(0, 3)
+            GB_EPI_DN(1, 0) GB_EPI_DN(1, 1) GB_EPI_DN(1, 2) GB_EPI_DN(1, 3)
+            GB_EPI_DN(2, 0) GB_EPI_DN(2, 1) GB_EPI_DN(2, 2) GB_EPI_DN(2, 3)
+            GB_EPI_DN(3, 0) GB_EPI_DN(3, 1) GB_EPI_DN(3, 2) GB_EPI_DN(3, 3)
+#undef GB_EPI_DN
         }
+        __syncthreads();  // LDS reused by the next tile's loads
     }
 }
 
