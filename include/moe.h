@@ -32,7 +32,8 @@
  *   current HIP device) allocated and owned by the caller; the library never
  *   allocates, frees or keeps a pointer after returning.  Scratch space comes
  *   only from the caller's workspace `ws` of `ws_bytes` bytes
- *   (moe_workspace_size).  Pointers are not checked for residency.
+ *   (moe_workspace_size for the forward calls, moe_backward_workspace_size for
+ *   the backward GEMMs).  Pointers are not checked for residency.
  * - Streams.  `stream` is a hipStream_t (NULL = the null stream).  Every call
  *   only enqueues kernels on it and returns: no host synchronisation, no
  *   device-to-host copy, no host read of counts or offsets ([ISSUE]), so the
@@ -78,7 +79,7 @@ typedef enum moe_status {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1, /* null pointer, bad size or enum value          */
     MOE_ERR_UNSUPPORTED = 2, /* valid but not built: e.g. H % 64 != 0          */
-    MOE_ERR_WORKSPACE = 3,   /* ws NULL or ws_bytes < moe_workspace_size()     */
+    MOE_ERR_WORKSPACE = 3,   /* ws NULL or ws_bytes below the call's need      */
     MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed    */
 } moe_status;
 
@@ -101,9 +102,16 @@ typedef struct moe_config {
 /* Rows of the permuted buffers: T*k + E*(align-1).  Host only. */
 int64_t moe_rows_capacity(const moe_config* cfg);
 
-/* Bytes of scratch every call of this config needs (0 is possible).  Host
- * only; no device access. */
+/* Bytes of scratch moe_permute and moe_forward need for this config (0 is
+ * possible).  Host only; no device access. */
 size_t moe_workspace_size(const moe_config* cfg);
+
+/* Bytes of scratch moe_grouped_down_bwd, moe_grouped_swiglu_bwd and
+ * moe_backward need (0 is possible; at most about 1 GiB).  The weight
+ * gradients cut an expert with many rows into row ranges computed in
+ * parallel; their float32 partial sums live here and are added in row order,
+ * so the result does not depend on scheduling.  Host only. */
+size_t moe_backward_workspace_size(const moe_config* cfg);
 
 /* Step 1, routing ([TE-EP] fp32 router with both score functions and the
  * sum + 1e-20 normalisation; [CUDNN] routing).  For each token t the k largest
@@ -196,7 +204,7 @@ moe_status moe_combine_bwd(const moe_config* cfg, const void* dy, const int32_t*
  *   dw2[e][o][f] = sum_{r of e, ascending} h[r][f] * dYp[r][o]   (float32,
  *   exactly 0 for an expert with no rows).
  * dgu [R_cap,2F] output dtype; dw2 [E][H][F] float32 (the w2 layout).
- * ws: moe_workspace_size(cfg) bytes. */
+ * ws: moe_backward_workspace_size(cfg) bytes. */
 moe_status moe_grouped_down_bwd(const moe_config* cfg, const void* dyp, const void* w2, const void* h,
                                 const void* gu_stash, const int32_t* offsets, void* dgu, float* dw2, void* ws,
                                 size_t ws_bytes, void* stream);
@@ -205,7 +213,8 @@ moe_status moe_grouped_down_bwd(const moe_config* cfg, const void* dyp, const vo
  *   dXp[r][c] = round( sum_n dgu[r][n] * w1[e][n][c] )
  *   dw1[e][n][c] = sum_{r of e, ascending} dgu[r][n] * Xp[r][c]  (float32,
  *   exactly 0 for an expert with no rows).
- * dxp [R_cap,H] output dtype; dw1 [E][2F][H] float32 (the w1 layout). */
+ * dxp [R_cap,H] output dtype; dw1 [E][2F][H] float32 (the w1 layout).
+ * ws: moe_backward_workspace_size(cfg) bytes. */
 moe_status moe_grouped_swiglu_bwd(const moe_config* cfg, const void* dgu, const void* w1, const void* xp,
                                   const int32_t* offsets, void* dxp, float* dw1, void* ws, size_t ws_bytes,
                                   void* stream);
@@ -218,7 +227,7 @@ moe_status moe_permute_bwd(const moe_config* cfg, const void* dxp, const int32_t
  * moe_grouped_swiglu_bwd, moe_permute_bwd.  Inputs: dy, the routing state and
  * saved tensors of moe_forward (w, offsets, row_map, src_map, xp, h,
  * gu_stash) and the weights; outputs dx, dw1, dw2; dyp, dgu, dxp are the
- * caller's intermediate buffers. */
+ * caller's intermediate buffers.  ws: moe_backward_workspace_size(cfg) bytes. */
 moe_status moe_backward(const moe_config* cfg, const void* dy, const float* w, const void* w1, const void* w2,
                         const int32_t* offsets, const int32_t* row_map, const int32_t* src_map, const void* xp,
                         const void* h, const void* gu_stash, void* dyp, void* dgu, void* dxp, void* dx, float* dw1,

@@ -30,4 +30,5 @@ from .binding import (  # noqa: F401
     moe_route,
     rows_capacity,
     workspace_size,
+    backward_workspace_size,
 )

@@ -94,6 +94,7 @@ CFG = ctypes.POINTER(moe_config)
 _SIGS = {
     "moe_rows_capacity": (ctypes.c_int64, [CFG]),
     "moe_workspace_size": (ctypes.c_size_t, [CFG]),
+    "moe_backward_workspace_size": (ctypes.c_size_t, [CFG]),
     "moe_route": (ctypes.c_int, [CFG, P, P, P, P]),
     "moe_permute": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_grouped_swiglu_gemm": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P]),
@@ -171,6 +172,11 @@ def rows_capacity(cfg: MoEConfig) -> int:
 def workspace_size(cfg: MoEConfig) -> int:
     c = cfg.c()
     return load_library().moe_workspace_size(ctypes.byref(c))
+
+
+def backward_workspace_size(cfg: MoEConfig) -> int:
+    c = cfg.c()
+    return load_library().moe_backward_workspace_size(ctypes.byref(c))
 
 
 def _ws(ws):
@@ -367,5 +373,5 @@ def alloc_backward(cfg: MoEConfig, device="cuda") -> dict:
         "dx": torch.empty(T, H, dtype=od, device=device),
         "dw1": torch.empty(E, 2 * F, H, dtype=torch.float32, device=device),
         "dw2": torch.empty(E, H, F, dtype=torch.float32, device=device),
-        "ws": torch.empty(max(workspace_size(cfg), 1), dtype=torch.uint8, device=device),
+        "ws": torch.empty(max(backward_workspace_size(cfg), 1), dtype=torch.uint8, device=device),
     }

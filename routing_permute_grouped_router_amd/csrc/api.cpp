@@ -69,8 +69,8 @@ moe_status check_shapes(const moe_config& c) {
     return MOE_OK;
 }
 
-moe_status check_ws(const moe_config& c, const void* ws, size_t ws_bytes) {
-    const size_t need = moe_workspace_size(&c);
+moe_status check_ws(const moe_config& c, const void* ws, size_t ws_bytes, bool backward = false) {
+    const size_t need = backward ? moe_backward_workspace_size(&c) : moe_workspace_size(&c);
     if (need == 0) return MOE_OK;
     if (ws == nullptr || ws_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu%s)", need, ws_bytes,
@@ -94,9 +94,12 @@ int64_t moe_rows_capacity(const moe_config* cfg) {
 size_t moe_workspace_size(const moe_config* cfg) {
     if (check_config(cfg) != MOE_OK) return 0;
     const moe_config& c = *cfg;
-    const size_t group = round256((size_t)group_n_chunks(c.T, c.E) * c.E * sizeof(int32_t));
-    const size_t bwd = c.dtype == MOE_MXFP8 ? 0 : round256(bwd_workspace_bytes(c));
-    return group > bwd ? group : bwd;
+    return round256((size_t)group_n_chunks(c.T, c.E) * c.E * sizeof(int32_t));
+}
+
+size_t moe_backward_workspace_size(const moe_config* cfg) {
+    if (check_config(cfg) != MOE_OK) return 0;
+    return cfg->dtype == MOE_BF16 ? round256(bwd_workspace_bytes(*cfg)) : 0;
 }
 
 moe_status moe_route(const moe_config* cfg, const float* logits, int32_t* idx, float* w, void* stream) {
@@ -263,7 +266,7 @@ moe_status moe_grouped_down_bwd(const moe_config* cfg, const void* dyp, const vo
     REQUIRE(w2);
     REQUIRE(dw2);
     REQUIRE(offsets);
-    if ((st = check_ws(*cfg, ws, ws_bytes))) return st;
+    if ((st = check_ws(*cfg, ws, ws_bytes, true))) return st;
     if (rows_capacity(*cfg) > 0) {
         REQUIRE(dyp);
         REQUIRE(h);
@@ -284,7 +287,7 @@ moe_status moe_grouped_swiglu_bwd(const moe_config* cfg, const void* dgu, const 
     REQUIRE(w1);
     REQUIRE(dw1);
     REQUIRE(offsets);
-    if ((st = check_ws(*cfg, ws, ws_bytes))) return st;
+    if ((st = check_ws(*cfg, ws, ws_bytes, true))) return st;
     if (rows_capacity(*cfg) > 0) {
         REQUIRE(dgu);
         REQUIRE(xp);

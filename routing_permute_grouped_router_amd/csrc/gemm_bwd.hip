@@ -5,15 +5,63 @@
 //   moe_grouped_swiglu_bwd: dXp = dGU * W1_e                    (DGRAD)
 //                           dW1_e = dGU_e^T * Xp_e              (WGRAD, zero for empty experts)
 // bf16 storage only.
+#include <algorithm>
+
 #include "gemm_bwd_kernel.h"
 
 namespace moe {
 
 int gemm_persistent_grid(int64_t max_tiles);
 
-size_t bwd_workspace_bytes(const moe_config&) { return 0; }
-
 namespace {
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t rows_cap(const moe_config& c) { return (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1); }
+
+constexpr int64_t kPartBudget = (int64_t)1 << 30;  // bytes of partial sums a weight gradient may use
+
+// Rows per weight-gradient work unit for an [M][N] gradient: at least 4096,
+// doubled until the partial sums of all split experts fit the budget.  An
+// expert with more than S rows has at most 2 rows / S units, so the experts
+// that are split use at most floor(2 R_cap / S) slots.
+int wgrad_split_rows(const moe_config& c, int64_t M, int64_t N) {
+    int64_t S = 4096;
+    while ((2 * rows_cap(c) / S) * M * N * 4 > kPartBudget) S *= 2;
+    return (int)S;
+}
+
+int64_t wgrad_slots(const moe_config& c, int64_t M, int64_t N) {
+    return 2 * rows_cap(c) / wgrad_split_rows(c, M, N);
+}
+
+size_t wgrad_ws_bytes(const moe_config& c, int64_t M, int64_t N) {
+    // partial sums, then E (units, first slot) pairs
+    return (size_t)(wgrad_slots(c, M, N) * M * N * 4) + (size_t)c.E * sizeof(int2) + 256;
+}
+
+// dW[e] = sum over the expert's units, in unit order, of the partial sums,
+// for experts with two or more units (the others were written directly).
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const int2* __restrict__ meta,
+                                                           const float4* __restrict__ part, int64_t n4, int slots,
+                                                           float4* __restrict__ dw) {
+    const int e = blockIdx.y;
+    const int2 m = meta[e];
+    if (m.x < 2 || m.y < 0 || m.y + m.x > slots) return;  // the last test only fails for inconsistent offsets
+    const float4* src = part + (size_t)m.y * n4;
+    float4* dst = dw + (size_t)e * n4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        float4 a = src[i];
+        for (int u = 1; u < m.x; ++u) {
+            const float4 b = src[(size_t)u * n4 + i];
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        dst[i] = a;
+    }
+}
 
 template <int MODE>
 hipError_t launch(const gemm::BwdArgs& a, int64_t max_tiles, hipStream_t s) {
@@ -22,34 +70,54 @@ hipError_t launch(const gemm::BwdArgs& a, int64_t max_tiles, hipStream_t s) {
     return hipGetLastError();
 }
 
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+hipError_t launch_wgrad(const moe_config& c, gemm::BwdArgs w, void* ws, hipStream_t s) {
+    const int64_t M = w.M, N = w.N;
+    const int64_t slots = wgrad_slots(c, M, N);
+    w.S = wgrad_split_rows(c, M, N);
+    w.slots = (int)slots;
+    w.part = (float*)ws;
+    w.meta = (int2*)((char*)ws + slots * M * N * 4);
+    // units are at most R_cap / S + E
+    const int64_t max_units = rows_cap(c) / w.S + c.E;
+    hipError_t e = launch<gemm::kWgrad>(w, max_units * cdiv(M, gemm::kTile) * cdiv(N, gemm::kTile), s);
+    if (e != hipSuccess || slots == 0) return e;
+    const int64_t n4 = M * N / 4;
+    const int bx = (int)std::min<int64_t>(cdiv(n4, 256 * 4), 512);
+    wgrad_reduce_kernel<<<dim3(bx, c.E), 256, 0, s>>>(w.meta, (const float4*)w.part, n4, w.slots, (float4*)w.Cw);
+    return hipGetLastError();
+}
 
 }  // namespace
 
+size_t bwd_workspace_bytes(const moe_config& c) {
+    const size_t a = wgrad_ws_bytes(c, c.H, c.F), b = wgrad_ws_bytes(c, 2 * (int64_t)c.F, c.H);
+    return a > b ? a : b;
+}
+
 hipError_t launch_down_bwd(const moe_config& c, const void* dyp, const void* w2, const void* h, const void* stash,
-                           const int32_t* offsets, void* dgu, float* dw2, void*, hipStream_t s) {
+                           const int32_t* offsets, void* dgu, float* dw2, void* ws, hipStream_t s) {
     if (c.dtype != MOE_BF16) return hipErrorNotSupported;
     const int64_t R = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     gemm::BwdArgs d{(const uint16_t*)dyp, (const uint16_t*)w2, offsets, c.E, (int)R, 0, c.F, c.H,
-                    (uint16_t*)dgu, nullptr, (const uint16_t*)stash};
+                    (uint16_t*)dgu, nullptr, (const uint16_t*)stash, nullptr, nullptr, 0, 0};
     hipError_t e = launch<gemm::kDgradDswiglu>(d, (R / gemm::kTile + c.E) * cdiv(c.F, gemm::kTile), s);
     if (e != hipSuccess) return e;
     gemm::BwdArgs w{(const uint16_t*)dyp, (const uint16_t*)h, offsets, c.E, (int)R, c.H, c.F, 0,
-                    nullptr, dw2, nullptr};
-    return launch<gemm::kWgrad>(w, (int64_t)c.E * cdiv(c.H, gemm::kTile) * cdiv(c.F, gemm::kTile), s);
+                    nullptr, dw2, nullptr, nullptr, nullptr, 0, 0};
+    return launch_wgrad(c, w, ws, s);
 }
 
 hipError_t launch_swiglu_bwd(const moe_config& c, const void* dgu, const void* w1, const void* xp,
-                             const int32_t* offsets, void* dxp, float* dw1, void*, hipStream_t s) {
+                             const int32_t* offsets, void* dxp, float* dw1, void* ws, hipStream_t s) {
     if (c.dtype != MOE_BF16) return hipErrorNotSupported;
     const int64_t R = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     gemm::BwdArgs d{(const uint16_t*)dgu, (const uint16_t*)w1, offsets, c.E, (int)R, 0, c.H, 2 * c.F,
-                    (uint16_t*)dxp, nullptr, nullptr};
+                    (uint16_t*)dxp, nullptr, nullptr, nullptr, nullptr, 0, 0};
     hipError_t e = launch<gemm::kDgrad>(d, (R / gemm::kTile + c.E) * cdiv(c.H, gemm::kTile), s);
     if (e != hipSuccess) return e;
     gemm::BwdArgs w{(const uint16_t*)dgu, (const uint16_t*)xp, offsets, c.E, (int)R, 2 * c.F, c.H, 0,
-                    nullptr, dw1, nullptr};
-    return launch<gemm::kWgrad>(w, (int64_t)c.E * cdiv(2 * c.F, gemm::kTile) * cdiv(c.H, gemm::kTile), s);
+                    nullptr, dw1, nullptr, nullptr, nullptr, 0, 0};
+    return launch_wgrad(c, w, ws, s);
 }
 
 }  // namespace moe

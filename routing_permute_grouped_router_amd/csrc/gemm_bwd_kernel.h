@@ -44,6 +44,14 @@ struct BwdArgs {
     uint16_t* C;            // DGRAD: [rows][N] bf16 (kDgrad) / [rows][2N] bf16 (kDgradDswiglu: dG | dU)
     float* Cw;              // WGRAD: [E][M][N] float32
     const uint16_t* stash;  // kDgradDswiglu: [rows][2N] bf16 (g | u)
+    // WGRAD work split: an expert's rows are cut into units of at most S rows;
+    // the partial sums of experts with two or more units go to workspace slots
+    // [slots][M][N] (summed in unit order by wgrad_reduce_kernel), and block 0
+    // records each expert's (units, first slot) in meta[E].
+    float* part;
+    int2* meta;
+    int S;
+    int slots;
 };
 
 // 8 x 8 bf16 transpose: in[i] holds row i (8 values along the contiguous axis);
@@ -71,12 +79,12 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
 
 // Epilogue of 16 consecutive output columns n..n+15 of row r (values v).
 template <int MODE>
-__device__ __forceinline__ void bwd_store16(const BwdArgs& p, const float (&v)[16], int e, int r, int n,
+__device__ __forceinline__ void bwd_store16(const BwdArgs& p, const float (&v)[16], float* cw, int r, int n,
                                             int row_end) {
     if (n >= p.N) return;
     if (MODE == kWgrad) {
         if (r >= p.M) return;
-        float4* dst = (float4*)(p.Cw + ((size_t)e * p.M + r) * p.N + n);
+        float4* dst = (float4*)(cw + (size_t)r * p.N + n);
 #pragma unroll
         for (int j = 0; j < 4; ++j) dst[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
         return;
@@ -127,6 +135,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
     constexpr int STAGE = kTile * BK;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][STAGE];
     __shared__ int32_t pre[kMaxExperts + 1];
+    __shared__ int32_t spre[WG ? kMaxExperts + 1 : 1];
     __shared__ int scan_tmp[kThreads / 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -134,14 +143,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
     const int n_tiles = (p.N + kTile - 1) / kTile;
     int total, m_tiles = 0;
     if (WG) {
+        // every expert owns at least one unit: empty ones write zeros
         m_tiles = (p.M + kTile - 1) / kTile;
-        total = p.E * m_tiles * n_tiles;  // every expert, empty ones included (they get zeros)
+        total = build_unit_prefix(p.offsets, p.E, p.S, pre, spre, scan_tmp) * m_tiles * n_tiles;
+        if (blockIdx.x == 0)
+            for (int e = tid; e < p.E; e += kThreads) p.meta[e] = make_int2(pre[e + 1] - pre[e], spre[e]);
     } else {
         total = build_tile_prefix(p.offsets, p.E, kTile, pre, scan_tmp) * n_tiles;
     }
     const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
     const int lb = blockIdx.x / kXcds;
-    const int t_begin = (int)((int64_t)total * xcd / kXcds), t_end = (int)((int64_t)total * (xcd + 1) / kXcds);
+    // Row-indexed GEMMs: every tile costs the same, so each XCD takes a
+    // contiguous range.  Weight gradients: units differ in rows (hot experts
+    // come first in expert order), so units are dealt to the XCDs round robin
+    // (unit u to XCD u % 8) and each XCD walks the tiles of its own units.
+    int t_begin, t_end;
+    if (WG) {
+        const int units = total / (m_tiles * n_tiles);
+        t_begin = 0;
+        t_end = (units > xcd ? (units - xcd + kXcds - 1) / kXcds : 0) * m_tiles * n_tiles;
+    } else {
+        t_begin = (int)((int64_t)total * xcd / kXcds);
+        t_end = (int)((int64_t)total * (xcd + 1) / kXcds);
+    }
 
     int arow[4], brow[4];
 #pragma unroll
@@ -154,13 +178,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
     // contiguous-operand loader: 8 chunks of 16 B per thread, chunk q = tid + 256 i
     for (int t = t_begin + lb; t < t_end; t += per_xcd) {
         int e, m0, n0, k_begin, k_end, row0 = 0, row_end = 0;
+        float* cw = nullptr;
         if (WG) {
-            e = t / (m_tiles * n_tiles);
-            const int rem = t - e * m_tiles * n_tiles;
+            const int j = t / (m_tiles * n_tiles);
+            const int rem = t - j * m_tiles * n_tiles;
+            const int u = xcd + kXcds * j;
+            e = find_expert(pre, p.E, u);
+            const int s = u - pre[e], units = pre[e + 1] - pre[e];
             m0 = (rem / n_tiles) * kTile;
             n0 = (rem % n_tiles) * kTile;
-            k_begin = max(0, p.offsets[e]);
-            k_end = min(p.offsets[e + 1], p.rows);
+            const int r_begin = max(0, p.offsets[e]), r_end = min(p.offsets[e + 1], p.rows);
+            k_begin = min(r_begin + s * p.S, r_end);
+            k_end = min(k_begin + p.S, r_end);
+            if (units == 1) {
+                cw = p.Cw + (size_t)e * p.M * p.N;
+            } else {
+                const int slot = spre[e] + s;
+                if (slot >= p.slots) continue;  // only for inconsistent offsets
+                cw = p.part + (size_t)slot * p.M * p.N;
+            }
         } else {
             int mt, nt;
             tile_coords(t, total / n_tiles, n_tiles, 4, &mt, &nt);
@@ -279,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
         float v[16];                                                                                     \
         _Pragma("unroll") for (int j = 0; j < 16; ++j) v[j] = wbuf[rr * 33 + c0 + j];                    \
         __builtin_amdgcn_s_waitcnt(0xC07F); /* reads done before the next tile overwrites */            \
-        bwd_store16<MODE>(p, v, e, m0 + wm * 128 + (MI) * 32 + rr, n0 + wn * 128 + (NI) * 32 + c0, row_end); \
+        bwd_store16<MODE>(p, v, cw, m0 + wm * 128 + (MI) * 32 + rr, n0 + wn * 128 + (NI) * 32 + c0, row_end); \
     }
         GB_EPI(0, 0) GB_EPI(0, 1) GB_EPI(0, 2) GB_EPI(0, 3)
         GB_EPI(1, 0) GB_EPI(1, 1) GB_EPI(1, 2) GB_EPI(1, 3)

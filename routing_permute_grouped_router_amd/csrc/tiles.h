@@ -53,6 +53,43 @@ __device__ __forceinline__ int build_tile_prefix(const int32_t* __restrict__ off
     return total;
 }
 
+// Work units of the weight-gradient GEMMs (ragged contraction over each
+// expert's rows).  An expert with rows(e) rows is cut into
+// units(e) = max(1, ceil(rows(e) / S)) row ranges of at most S rows; an
+// expert with no rows keeps one unit (it writes zeros).  pre[e] = sum of units
+// of the experts before e; slot[e] = the same sum restricted to experts with
+// two or more units (their partial sums take workspace slots).  Returns pre[E];
+// slot[E] is the number of slots used.
+__device__ __forceinline__ int build_unit_prefix(const int32_t* __restrict__ offsets, int E, int S, int32_t* pre,
+                                                 int32_t* slot, int* lds_tmp) {
+    const int per = (E + blockDim.x - 1) / blockDim.x;
+    const int e0 = threadIdx.x * per, e1 = min(E, e0 + per);
+    int lu = 0, ls = 0;
+    for (int e = e0; e < e1; ++e) {
+        const int rows = offsets[e + 1] - offsets[e];
+        const int u = rows > 0 ? (rows + S - 1) / S : 1;
+        lu += u;
+        ls += u >= 2 ? u : 0;
+    }
+    int total_u, total_s;
+    int run_u = block_exclusive_scan(lu, lds_tmp, &total_u);
+    int run_s = block_exclusive_scan(ls, lds_tmp, &total_s);
+    for (int e = e0; e < e1; ++e) {
+        pre[e] = run_u;
+        slot[e] = run_s;
+        const int rows = offsets[e + 1] - offsets[e];
+        const int u = rows > 0 ? (rows + S - 1) / S : 1;
+        run_u += u;
+        run_s += u >= 2 ? u : 0;
+    }
+    if (threadIdx.x == 0) {
+        pre[E] = total_u;
+        slot[E] = total_s;
+    }
+    __syncthreads();
+    return total_u;
+}
+
 // Largest e with pre[e] <= mt (that expert is non-empty and owns M-tile mt).
 __device__ __forceinline__ int find_expert(const int32_t* pre, int E, int mt) {
     int lo = 0, hi = E - 1;

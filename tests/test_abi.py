@@ -88,6 +88,23 @@ def test_workspace_checks():
     assert lib.moe_rows_capacity(ctypes.byref(c2)) == 5000 * 8 + 128 * 127
 
 
+def test_backward_workspace_bounds():
+    lib = moe.load_library()
+    # the skewed workload: the weight-gradient partial sums stay within about 1 GiB
+    c = _cfg(T=16384, H=2048, F=768, E=128, k=8)
+    need = lib.moe_backward_workspace_size(ctypes.byref(c))
+    assert 0 < need <= (1 << 30) + (1 << 20)
+    assert lib.moe_workspace_size(ctypes.byref(c)) < (1 << 20)  # the forward needs only the grouping scratch
+    # too few rows to split an expert: only the per-expert table
+    c = _cfg(T=64, H=128, F=64, E=8, k=2)
+    assert lib.moe_backward_workspace_size(ctypes.byref(c)) < 4096
+    # the backward is built for bf16 storage only
+    assert lib.moe_backward_workspace_size(ctypes.byref(_cfg(dtype=b.MOE_F32))) == 0
+    st = lib.moe_grouped_down_bwd(ctypes.byref(_cfg(T=16384, H=2048, F=768, E=128, k=8)), 1, 1, 1, 1, 1, 1, 1,
+                                  1, need - 1, None)
+    assert st == b.MOE_ERR_WORKSPACE
+
+
 def test_quantize_rejects_ragged_cols():
     lib = moe.load_library()
     assert lib.moe_quantize_mxfp8(1, 4, 33, 1, 1, None) == b.MOE_ERR_INVALID_ARG
