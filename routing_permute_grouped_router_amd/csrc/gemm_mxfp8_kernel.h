@@ -1,21 +1,31 @@
 // Grouped MXFP8 GEMMs on CDNA4 scaled matrix cores
 // (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 operands, E8M0 scales per 32).
 //
-// Same computation, tiling, device-side group handling and direct-to-LDS
-// operand streaming as the bf16 kernel (gemm_bf16_kernel.h), on the MXFP8
-// block-scaled format of the cudnn-frontend page "Add MoE + expert-parallel
-// Python API surface, PyTorch reference, and tests" (BlockScaledTensor, block
-// 32) with OCP E4M3 elements: one LDS stage is 256 rows x 128 bytes (four
-// scale blocks), the K step of one MFMA is 64 bytes (two blocks).
+// Same computation and device-side group handling as the bf16 kernel
+// (gemm_bf16_kernel.h), on the MXFP8 block-scaled format of the cudnn-frontend
+// page "Add MoE + expert-parallel Python API surface, PyTorch reference, and
+// tests" (BlockScaledTensor, block 32) with OCP E4M3 elements.
+//
+// These GEMMs stream their weights from HBM (each expert's weights serve only
+// its own few hundred rows), so the design favours bytes in flight over
+// on-chip reuse:
+//   - tiles are 128 rows x 256 columns (SwiGLU: 128 gate + 128 up rows of W1),
+//     so an expert with a few hundred rows wastes at most one partial 128-row
+//     tile;
+//   - one LDS stage is 128 bytes of K (four scale blocks): codes of the 128 A
+//     rows and 256 B rows plus their 32-bit scale words, all copied straight
+//     from global memory into LDS (global_load_lds, 16-byte pieces for codes,
+//     4-byte pieces for scale words); three stages rotate, so the loads of
+//     stage k+2 are in flight while stage k feeds the matrix cores;
+//   - LDS reads are issued explicitly (ds_read_b128) one MFMA group ahead and
+//     waited for with lgkmcnt just before use; one barrier per stage.
 //
 // Operand layout of the scaled MFMA (measured on gfx950): lane l holds row
 // l % 32 (A) or column l % 32 (B) and the 16-byte K pieces [16 h, 16 h + 16)
-// and [32 + 16 h, 32 + 16 h + 16) with h = l / 32; the E8M0 scale in byte 0 of
-// lane l's scale register applies to 32-block h of that row or column.  A lane
-// therefore reads 16-byte chunks c0 + h and c0 + 2 + h of its LDS row and
-// passes the scale of block c0 / 2 + h.  Each lane keeps one 32-bit word of
-// scales (four consecutive blocks, the whole K step) per operand row it feeds,
-// loaded one K step ahead.
+// and [32 + 16 h, 32 + 16 h + 16) of a 64-byte K step, h = l / 32; the E8M0
+// scale in byte 0 of lane l's scale operand applies to 32-block h of that row
+// or column.  A lane therefore reads 16-byte chunks c0 + h and c0 + 2 + h of
+// its LDS row and passes byte (2 s + h) of the row's scale word for K step s.
 //
 // Epilogues go through LDS (one 32 x 32 accumulator at a time per wavefront)
 // so each lane finishes 16 consecutive columns of one row: the SwiGLU GEMM
@@ -44,22 +54,47 @@ struct MxArgs {
     uint16_t* stash;         // SwiGLU, optional: bf16 g | u [rows][2 n_out]
 };
 
+constexpr int kMxBM = 128;   // rows per tile
+constexpr int kMxBN = 256;   // B rows per tile
+constexpr int kMxStages = 3;
+
+__device__ __forceinline__ void mx_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint4 mx_ds_read16(uint32_t addr) {
+    uint4 v;
+    __asm__ volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ uint32_t mx_ds_read4(uint32_t addr) {
+    uint32_t v;
+    __asm__ volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
 template <bool SWIGLU>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
-    constexpr int BKB = 128;               // K bytes per stage
-    constexpr int CH = BKB / 16;           // 16-byte chunks per LDS row
-    constexpr int RPL = 64 / CH;           // rows per wave-wide load
-    constexpr int LOADS = 64 / RPL;        // loads per wave per operand per stage
-    constexpr int STAGE = kTile * BKB;     // bytes of one operand stage
+    constexpr int BKB = 128;                       // K bytes per stage
+    constexpr int CH = BKB / 16;                   // 16-byte chunks per LDS row
+    constexpr int RPL = 64 / CH;                   // rows per wave-wide code load
+    constexpr int A_LOADS = kMxBM / 4 / RPL;       // 4: each wave loads 32 A rows
+    constexpr int B_LOADS = kMxBN / 4 / RPL;       // 8: each wave loads 64 B rows
+    constexpr int LPS = A_LOADS + B_LOADS + 2;     // loads per wave per stage (+ two scale loads)
+    constexpr int A_BYTES = kMxBM * BKB;           // 16 KiB
+    constexpr int B_BYTES = kMxBN * BKB;           // 32 KiB
+    constexpr int AS_OFF = A_BYTES + B_BYTES;      // scale words of the A rows
+    constexpr int BS_OFF = AS_OFF + kMxBM * 4;     // scale words of the B rows
+    constexpr int ST_BYTES = BS_OFF + kMxBN * 4;   // 50688
+    static_assert(LPS == 14, "wait counts below");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kMxStages * ST_BYTES];
     __shared__ int32_t pre[kMaxExperts + 1];
     __shared__ int scan_tmp[kThreads / 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid >> 1, wn = wid & 1, half = lane >> 5;
-    const int total_m = build_tile_prefix(p.offsets, p.E, kTile, pre, scan_tmp);
-    const int cols_per_tile = SWIGLU ? kTile / 2 : kTile;
+    const int total_m = build_tile_prefix(p.offsets, p.E, kMxBM, pre, scan_tmp);
+    const int cols_per_tile = SWIGLU ? kMxBN / 2 : kMxBN;
     const int n_tiles = (p.n_out + cols_per_tile - 1) / cols_per_tile;
     const int total = total_m * n_tiles;
     const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
@@ -70,20 +105,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     const int nk = K / BKB;
     const int lrow = lane / CH, lslot = lane % CH;
 
-    int arow[4], brow[4];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
+    // LDS rows of this lane's MFMA operands (2 x 4 accumulators of 32 x 32 per wave)
+    int arow[2], brow[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) arow[mi] = wm * 128 + mi * 32 + (lane & 31);
+    for (int mi = 0; mi < 2; ++mi) arow[mi] = wm * 64 + mi * 32 + (lane & 31);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
         brow[ni] = SWIGLU ? (ni < 2 ? 0 : 128) + wn * 64 + (ni & 1) * 32 + (lane & 31)
                           : wn * 128 + ni * 32 + (lane & 31);
+    uint32_t ra[2], rb[4];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) ra[mi] = lds_base + arow[mi] * BKB;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) rb[ni] = lds_base + A_BYTES + brow[ni] * BKB;
 
     for (int t = t_begin + lb; t < t_end; t += per_xcd) {
         int mt, nt;
         tile_coords(t, total_m, n_tiles, 4, &mt, &nt);
         const int e = find_expert(pre, p.E, mt);
         const int row_end = min(p.offsets[e + 1], p.rows);
-        const int row0 = p.offsets[e] + (mt - pre[e]) * kTile;
+        const int row0 = p.offsets[e] + (mt - pre[e]) * kMxBM;
         if (row0 < 0 || row0 >= row_end) continue;  // only for inconsistent offsets
 
         auto b_row_of = [&](int r) __attribute__((always_inline)) {
@@ -91,110 +133,136 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
                 const int f = min(nt * 128 + (r & 127), p.n_out - 1);
                 return r < 128 ? f : p.n_out + f;
             }
-            return min(nt * kTile + r, p.n_out - 1);
+            return min(nt * kMxBN + r, p.n_out - 1);
         };
-        uint32_t aoff[LOADS], boff[LOADS];
+        // per-lane global byte offsets of the code loads (K offset 0); the
+        // 16-byte chunk a lane fetches is permuted so that LDS holds chunk
+        // c of row r at position c ^ (r & 7) (conflict-free fragment reads)
+        uint32_t aoff[A_LOADS], boff[B_LOADS];
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
+        for (int i = 0; i < A_LOADS; ++i) {
+            const int r = wid * 32 + i * RPL + lrow;
+            aoff[i] = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K + ((lslot ^ (r & 7)) * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i) {
             const int r = wid * 64 + i * RPL + lrow;
-            const int chunk = lslot ^ swz<0>(r);
-            aoff[i] = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K + chunk * 16);
-            boff[i] = (uint32_t)((size_t)b_row_of(r) * K + chunk * 16);
+            boff[i] = (uint32_t)((size_t)b_row_of(r) * K + ((lslot ^ (r & 7)) * 16));
         }
         const uint8_t* acodes = p.A + (size_t)row0 * K;  // A offsets are tile-relative
         const uint8_t* bcodes = p.B + (size_t)e * p.b_rows * K;
-        const uint8_t* bscales = p.Bs + (size_t)e * p.b_rows * KS;
-        // scale rows of this lane's MFMA operands
-        const uint8_t* asr[4];
-        const uint8_t* bsr[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) asr[mi] = p.As + (size_t)min(row0 + arow[mi], row_end - 1) * KS;
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) bsr[ni] = bscales + (size_t)b_row_of(brow[ni]) * KS;
+        // scale words: A rows wid*32 + lane (lanes 0..31), B rows wid*64 + lane
+        const uint8_t* asrow = p.As + (size_t)min(row0 + wid * 32 + (lane & 31), row_end - 1) * KS;
+        const uint8_t* bsrow = p.Bs + ((size_t)e * p.b_rows + b_row_of(wid * 64 + lane)) * KS;
 
-        f32x16 acc[4][4];
+        f32x16 acc[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-#define GM_LOAD(kt, stage)                                                                               \
-    _Pragma("unroll") for (int i = 0; i < LOADS; ++i) {                                                  \
-        __builtin_amdgcn_global_load_lds((glb_void*)(acodes + aoff[i] + (size_t)(kt) * BKB),                  \
-                                         (lds_void*)&lds[stage][0][(wid * 64 + i * RPL) * BKB], 16, 0, 0); \
-        __builtin_amdgcn_global_load_lds((glb_void*)(bcodes + boff[i] + (size_t)(kt) * BKB),               \
-                                         (lds_void*)&lds[stage][1][(wid * 64 + i * RPL) * BKB], 16, 0, 0); \
+#define MX_ISSUE(kt)                                                                                     \
+    {                                                                                                    \
+        uint8_t* st_ = lds + ((kt) % kMxStages) * ST_BYTES;                                              \
+        _Pragma("unroll") for (int i = 0; i < A_LOADS; ++i)                                              \
+            __builtin_amdgcn_global_load_lds((glb_void*)(acodes + aoff[i] + (size_t)(kt) * BKB),         \
+                                             (lds_void*)(st_ + (wid * 32 + i * RPL) * BKB), 16, 0, 0);  \
+        _Pragma("unroll") for (int i = 0; i < B_LOADS; ++i)                                              \
+            __builtin_amdgcn_global_load_lds((glb_void*)(bcodes + boff[i] + (size_t)(kt) * BKB),         \
+                                             (lds_void*)(st_ + A_BYTES + (wid * 64 + i * RPL) * BKB), 16, 0, 0); \
+        if (lane < 32)                                                                                   \
+            __builtin_amdgcn_global_load_lds((glb_void*)(asrow + (kt) * 4),                              \
+                                             (lds_void*)(st_ + AS_OFF + wid * 32 * 4), 4, 0, 0);         \
+        __builtin_amdgcn_global_load_lds((glb_void*)(bsrow + (kt) * 4),                                  \
+                                         (lds_void*)(st_ + BS_OFF + wid * 64 * 4), 4, 0, 0);             \
     }
-#define GM_SCALES(kt, SA, SB)                                                                            \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                      \
-        SA[i] = *(const uint32_t*)(asr[i] + (kt) * 4);                                                    \
-        SB[i] = *(const uint32_t*)(bsr[i] + (kt) * 4);                                                    \
+        // fragments of K step `sub` (64 bytes) of stage kt: chunks 4 sub + h and 4 sub + 2 + h
+#define MX_READ(kt, sub, FA, FB)                                                                         \
+    {                                                                                                    \
+        const uint32_t so_ = ((kt) % kMxStages) * ST_BYTES;                                              \
+        _Pragma("unroll") for (int mi = 0; mi < 2; ++mi) {                                               \
+            const uint4 lo = mx_ds_read16(ra[mi] + so_ + ((((sub) * 4 + half) ^ (arow[mi] & 7)) << 4));   \
+            const uint4 hi = mx_ds_read16(ra[mi] + so_ + ((((sub) * 4 + 2 + half) ^ (arow[mi] & 7)) << 4)); \
+            FA[mi] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w}; \
+        }                                                                                                \
+        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) {                                               \
+            const uint4 lo = mx_ds_read16(rb[ni] + so_ + ((((sub) * 4 + half) ^ (brow[ni] & 7)) << 4));   \
+            const uint4 hi = mx_ds_read16(rb[ni] + so_ + ((((sub) * 4 + 2 + half) ^ (brow[ni] & 7)) << 4)); \
+            FB[ni] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w}; \
+        }                                                                                                \
     }
-        uint32_t sa[4], sb[4], sa_n[4], sb_n[4];
-        GM_LOAD(0, 0);
-        GM_SCALES(0, sa, sb);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int st = kt & 1;
-            const bool more = kt + 1 < nk;
-            if (more) {
-                GM_LOAD(kt + 1, st ^ 1);
-                GM_SCALES(kt + 1, sa_n, sb_n);
-            }
-#pragma unroll
-            for (int s = 0; s < BKB / 64; ++s) {
-                const int c0 = 4 * s;
-                i32x8 fa[4], fb[4];
-                int xa[4], xb[4];
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
-                    const int r = arow[mi];
-                    const uint4 lo = *(const uint4*)&lds[st][0][r * BKB + (((c0 + half) ^ swz<0>(r)) << 4)];
-                    const uint4 hi = *(const uint4*)&lds[st][0][r * BKB + (((c0 + 2 + half) ^ swz<0>(r)) << 4)];
-                    fa[mi] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    xa[mi] = (int)((sa[mi] >> (8 * (2 * s + half))) & 0xffu);
-                }
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const int r = brow[ni];
-                    const uint4 lo = *(const uint4*)&lds[st][1][r * BKB + (((c0 + half) ^ swz<0>(r)) << 4)];
-                    const uint4 hi = *(const uint4*)&lds[st][1][r * BKB + (((c0 + 2 + half) ^ swz<0>(r)) << 4)];
-                    fb[ni] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    xb[ni] = (int)((sb[ni] >> (8 * (2 * s + half))) & 0xffu);
-                }
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fa[mi], fb[ni], acc[mi][ni], 0, 0, 0, xa[mi], 0, xb[ni]);
-            }
-            if (more) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sa[i] = sa_n[i];
-                    sb[i] = sb_n[i];
-                }
-            }
-            __syncthreads();  // next stage landed (vmcnt 0); this stage fully read
-        }
-#undef GM_LOAD
-#undef GM_SCALES
+#define MX_READ_SCALES(kt, SA, SB)                                                                       \
+    {                                                                                                    \
+        const uint32_t so_ = lds_base + ((kt) % kMxStages) * ST_BYTES;                                   \
+        _Pragma("unroll") for (int mi = 0; mi < 2; ++mi) SA[mi] = mx_ds_read4(so_ + AS_OFF + arow[mi] * 4); \
+        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) SB[ni] = mx_ds_read4(so_ + BS_OFF + brow[ni] * 4); \
+    }
+#define MX_WAIT(FA, FB, SA, SB)                                                                          \
+    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
+                     : "+v"(FA[0]), "+v"(FA[1]), "+v"(FB[0]), "+v"(FB[1]), "+v"(FB[2]), "+v"(FB[3]),     \
+                       "+v"(SA[0]), "+v"(SA[1]), "+v"(SB[0]), "+v"(SB[1]), "+v"(SB[2]), "+v"(SB[3])::"memory")
+#define MX_MFMAS(FA, FB, SA, SB, sub)                                                                    \
+    _Pragma("unroll") for (int mi = 0; mi < 2; ++mi) _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)   \
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                    \
+            FA[mi], FB[ni], acc[mi][ni], 0, 0, 0, (int)((SA[mi] >> (8 * (2 * (sub) + half))) & 0xffu), 0, \
+            (int)((SB[ni] >> (8 * (2 * (sub) + half))) & 0xffu));
 
-        // epilogue through LDS: lane -> row rr, columns c0 .. c0+15 of a 32x32 tile
-        float* wb = (float*)&lds[0][0][0] + wid * 2 * (32 * 33 + 32);
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous tile's stores retired
+        MX_ISSUE(0);
+        if (nk > 1) MX_ISSUE(1);
+        if (nk > 1) __asm__ volatile("s_waitcnt vmcnt(14)" ::: "memory");  // stage 0 landed
+        else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        mx_barrier();
+        i32x8 f0a[2], f0b[4], f1a[2], f1b[4];
+        uint32_t s0a[2], s0b[4], s1a[2], s1b[4];
+        MX_READ(0, 0, f0a, f0b);
+        MX_READ_SCALES(0, s0a, s0b);
+        MX_WAIT(f0a, f0b, s0a, s0b);
+        for (int kt = 0; kt < nk; ++kt) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 2 < nk) MX_ISSUE(kt + 2);  // into the buffer of stage kt-1, free since the last barrier
+            MX_READ(kt, 1, f1a, f1b);
+            __builtin_amdgcn_sched_barrier(0);
+            MX_MFMAS(f0a, f0b, s0a, s0b, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            MX_WAIT(f1a, f1b, s0a, s0b);  // this wave has read all of stage kt
+            if (kt + 2 < nk) __asm__ volatile("s_waitcnt vmcnt(14)" ::: "memory");  // stage kt+1 landed
+            else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            mx_barrier();  // ... for every wave, and every wave is done with stage kt
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) {
+                MX_READ(kt + 1, 0, f0a, f0b);
+                MX_READ_SCALES(kt + 1, s1a, s1b);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            MX_MFMAS(f1a, f1b, s0a, s0b, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) {
+                MX_WAIT(f0a, f0b, s1a, s1b);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) s0a[i] = s1a[i];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s0b[i] = s1b[i];
+            }
+        }
+#undef MX_ISSUE
+#undef MX_READ
+#undef MX_READ_SCALES
+#undef MX_WAIT
+#undef MX_MFMAS
+        // every wave passed the last barrier after reading its last stage: LDS is free
+
+        // epilogue through LDS: lane -> row rr, columns cc .. cc+15 of a 32x32 tile
+        float* wb = (float*)lds + wid * 2 * (32 * 33 + 32);
         float* wb2 = wb + 32 * 33 + 32;
         const int rr = lane >> 1, cc = (lane & 1) * 16;
-#define GM_STAGE_TILE(BUF, MI, NI)                                                                       \
-    _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                      \
-        BUF[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * 33 + (lane & 31)] = acc[MI][NI][q];
         if (SWIGLU) {
 #define GM_EPI_SW(MI, NI)                                                                                \
     {                                                                                                    \
-        GM_STAGE_TILE(wb, MI, NI)                                                                        \
-        GM_STAGE_TILE(wb2, MI, (NI) + 2)                                                                 \
+        GE_STAGE_TILE(wb, acc[MI][NI])                                                                   \
+        GE_STAGE_TILE(wb2, acc[MI][(NI) + 2])                                                            \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
         float hv[16], gv[16], uv[16];                                                                    \
         float amax = 0.f;                                                                                \
@@ -206,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         }                                                                                                \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
         amax = fmaxf(amax, __shfl_xor(amax, 1, 64));                                                     \
-        const int r = row0 + wm * 128 + (MI) * 32 + rr;                                                  \
+        const int r = row0 + wm * 64 + (MI) * 32 + rr;                                                   \
         const int f = nt * 128 + wn * 64 + (NI) * 32 + cc;                                               \
         if (r < row_end && f < p.n_out) {                                                                \
             const int se = mx_shared_exp(amax);                                                          \
@@ -222,41 +290,33 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
                 uint4* gs = (uint4*)(p.stash + (size_t)r * 2 * p.n_out + f);                             \
                 uint4* us = (uint4*)(p.stash + (size_t)r * 2 * p.n_out + p.n_out + f);                   \
                 _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                         \
-                    gs[j] = make_uint4(pack_bf16x2(gv[8 * j], gv[8 * j + 1]), pack_bf16x2(gv[8 * j + 2], gv[8 * j + 3]), \
-                                       pack_bf16x2(gv[8 * j + 4], gv[8 * j + 5]), pack_bf16x2(gv[8 * j + 6], gv[8 * j + 7])); \
-                    us[j] = make_uint4(pack_bf16x2(uv[8 * j], uv[8 * j + 1]), pack_bf16x2(uv[8 * j + 2], uv[8 * j + 3]), \
-                                       pack_bf16x2(uv[8 * j + 4], uv[8 * j + 5]), pack_bf16x2(uv[8 * j + 6], uv[8 * j + 7])); \
+                    gs[j] = GE_PACK8(gv, 8 * j);                                                         \
+                    us[j] = GE_PACK8(uv, 8 * j);                                                         \
                 }                                                                                        \
             }                                                                                            \
         }                                                                                                \
     }
             GM_EPI_SW(0, 0) GM_EPI_SW(0, 1) GM_EPI_SW(1, 0) GM_EPI_SW(1, 1)
-            GM_EPI_SW(2, 0) GM_EPI_SW(2, 1) GM_EPI_SW(3, 0) GM_EPI_SW(3, 1)
 #undef GM_EPI_SW
         } else {
 #define GM_EPI_DN(MI, NI)                                                                                \
     {                                                                                                    \
-        GM_STAGE_TILE(wb, MI, NI)                                                                        \
+        GE_STAGE_TILE(wb, acc[MI][NI])                                                                   \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
         float v[16];                                                                                     \
         _Pragma("unroll") for (int j = 0; j < 16; ++j) v[j] = wb[rr * 33 + cc + j];                      \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
-        const int r = row0 + wm * 128 + (MI) * 32 + rr;                                                  \
-        const int n = nt * kTile + wn * 128 + (NI) * 32 + cc;                                            \
+        const int r = row0 + wm * 64 + (MI) * 32 + rr;                                                   \
+        const int n = nt * kMxBN + wn * 128 + (NI) * 32 + cc;                                            \
         if (r < row_end && n < p.n_out) {                                                                \
             uint4* dst = (uint4*)(p.Cb + (size_t)r * p.n_out + n);                                       \
-            _Pragma("unroll") for (int j = 0; j < 2; ++j)                                               \
-                dst[j] = make_uint4(pack_bf16x2(v[8 * j], v[8 * j + 1]), pack_bf16x2(v[8 * j + 2], v[8 * j + 3]), \
-                                    pack_bf16x2(v[8 * j + 4], v[8 * j + 5]), pack_bf16x2(v[8 * j + 6], v[8 * j + 7])); \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j) dst[j] = GE_PACK8(v, 8 * j);                  \
         }                                                                                                \
     }
             GM_EPI_DN(0, 0) GM_EPI_DN(0, 1) GM_EPI_DN(0, 2) GM_EPI_DN(0, 3)
             GM_EPI_DN(1, 0) GM_EPI_DN(1, 1) GM_EPI_DN(1, 2) GM_EPI_DN(1, 3)
-            GM_EPI_DN(2, 0) GM_EPI_DN(2, 1) GM_EPI_DN(2, 2) GM_EPI_DN(2, 3)
-            GM_EPI_DN(3, 0) GM_EPI_DN(3, 1) GM_EPI_DN(3, 2) GM_EPI_DN(3, 3)
 #undef GM_EPI_DN
         }
-#undef GM_STAGE_TILE
         __syncthreads();  // LDS reused by the next tile's loads
     }
 }

@@ -59,7 +59,7 @@ hipError_t launch_swiglu_gemm_mxfp8(const moe_config& c, const uint8_t* xp, cons
                                     const uint8_t* w1, const uint8_t* w1_scale, const int32_t* offsets, uint8_t* h,
                                     uint8_t* h_scale, uint16_t* stash, hipStream_t s) {
     const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
-    const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.F + 127) / 128);
+    const int64_t max_tiles = (R_cap / gemm::kMxBM + c.E) * ((c.F + 127) / 128);
     if (max_tiles == 0) return hipSuccess;
     gemm::MxArgs a{xp, xp_scale, w1, w1_scale, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, h_scale, nullptr, stash};
     gemm::grouped_gemm_mxfp8<true><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
@@ -69,7 +69,7 @@ hipError_t launch_swiglu_gemm_mxfp8(const moe_config& c, const uint8_t* xp, cons
 hipError_t launch_down_gemm_mxfp8(const moe_config& c, const uint8_t* h, const uint8_t* h_scale, const uint8_t* w2,
                                   const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, hipStream_t s) {
     const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
-    const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.H + gemm::kTile - 1) / gemm::kTile);
+    const int64_t max_tiles = (R_cap / gemm::kMxBM + c.E) * ((c.H + gemm::kMxBN - 1) / gemm::kMxBN);
     if (max_tiles == 0) return hipSuccess;
     gemm::MxArgs a{h, h_scale, w2, w2_scale, offsets, c.E, c.F, (int)R_cap, c.H, c.H, nullptr, nullptr, yp, nullptr};
     gemm::grouped_gemm_mxfp8<false><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
