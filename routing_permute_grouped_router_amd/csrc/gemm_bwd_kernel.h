@@ -16,13 +16,24 @@
 //           both operands row-major over the rows r.
 //
 // Tiles are 256 x 256 x 64 on 4 wavefronts of 128 x 128 (4 x 4 MFMA 32x32
-// accumulators), two LDS stages of 64 KiB with the same XOR-swizzled
-// K-contiguous layout as the forward kernel.  Operands go global -> registers
-// -> LDS: the next stage's loads are in flight during the current stage's
-// MFMAs.  A K-contiguous operand is copied in 16-byte chunks; a K-strided one
-// is loaded as 8 x 8 bf16 blocks (eight 16-byte rows along the contiguous
-// axis) and transposed in registers so that LDS again holds 8 consecutive K
-// values per 16 bytes.  Out-of-range rows and columns load zeros.
+// accumulators), two LDS stages of 64 KiB filled straight from global memory
+// (global_load_lds, 16-byte pieces; the next stage is in flight while the
+// current one feeds the matrix cores).  A K-contiguous operand (the rows of a
+// DGRAD) is kept as in the forward kernel: 128-byte rows of 64 K values, the
+// 16-byte chunks XOR-permuted by (row & 7).  A strided operand (the weights of
+// a DGRAD; both operands of a WGRAD) is kept as it lies in memory: 64 K rows of
+// 256 columns (512 bytes each), 16-byte chunk c of K row k stored at chunk
+// position c ^ 4 (k & 3), and its MFMA fragments are read with the CDNA4 LDS
+// transpose read ds_read_b64_tr_b16.  Measured lane rule of that instruction:
+// within each group of 16 lanes, lane i receives element i % 4 of the four
+// 16-bit values addressed by lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12.
+// Lane a of a group therefore addresses K row kb + a / 4, columns c + 4 (a % 4)
+// and receives column c + a at K rows kb .. kb + 3; two such reads give the
+// eight K values of one MFMA operand lane.  The 4 (k & 3) chunk permutation
+// puts the four K rows of one read in different LDS banks.
+// Rows past a WGRAD unit's end load a clamped valid row and the A copy of
+// those rows is overwritten with zeros before use; rows and columns past a
+// DGRAD's output are never stored.
 #pragma once
 
 #include "gemm_bf16_kernel.h"
@@ -53,29 +64,6 @@ struct BwdArgs {
     int S;
     int slots;
 };
-
-// 8 x 8 bf16 transpose: in[i] holds row i (8 values along the contiguous axis);
-// out[j] holds column j (the 8 row values, row 0 lowest).
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-    uint32_t w[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        w[i][0] = in[i].x;
-        w[i][1] = in[i].y;
-        w[i][2] = in[i].z;
-        w[i][3] = in[i].w;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint32_t o[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t x = w[2 * p][j >> 1], y = w[2 * p + 1][j >> 1];
-            o[p] = (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-        }
-        out[j] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-}
 
 // Epilogue of 16 consecutive output columns n..n+15 of row r (values v).
 template <int MODE>
@@ -128,18 +116,50 @@ __device__ __forceinline__ void bwd_store16(const BwdArgs& p, const float (&v)[1
     }
 }
 
+// Byte offset, within a [64][256] strided stage region, that lane `lane`
+// addresses for the 32-column block starting at colbase (K base 0).
+__device__ __forceinline__ uint32_t tr_lane_off(int colbase, int lane) {
+    const int a = lane & 15, g = (lane >> 4) & 1;
+    const int col = colbase + 16 * g + 4 * (a & 3);
+    const int krow = a >> 2;  // K row within a group of four (K base is a multiple of 4)
+    return (uint32_t)(krow * 512 + (((col >> 3) ^ (krow << 2)) << 4) + (col & 7) * 2);
+}
+
+// LDS reads issued as inline asm: the compiler then does not order them
+// behind the direct-to-LDS loads still in flight into the other stage (it
+// cannot tell the two stages apart); waits are explicit (bwd_wait).
+__device__ __forceinline__ uint4 bwd_ds_read16(uint32_t addr) {
+    uint4 v;
+    __asm__ volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+__device__ __forceinline__ uint2 bwd_ds_read_tr(uint32_t addr) {
+    uint2 v;
+    __asm__ volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+// eight K values of one operand lane from two transpose reads, 2048 bytes apart
+__device__ __forceinline__ bf16x8 bwd_tr_frag(uint32_t addr) {
+    const uint2 lo = bwd_ds_read_tr(addr), hi = bwd_ds_read_tr(addr + 4 * 512);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+#define BWD_WAIT(FA, FB)                                                                                  \
+    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                               \
+                     : "+v"(FA[0]), "+v"(FA[1]), "+v"(FA[2]), "+v"(FA[3]), "+v"(FB[0]), "+v"(FB[1]),     \
+                       "+v"(FB[2]), "+v"(FB[3])::"memory")
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
     constexpr int BK = 64;
     constexpr bool WG = MODE == kWgrad;
-    constexpr int STAGE = kTile * BK;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][STAGE];
+    constexpr int OPB = kTile * BK * 2;  // bytes of one operand in one stage
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][OPB];
     __shared__ int32_t pre[kMaxExperts + 1];
     __shared__ int32_t spre[WG ? kMaxExperts + 1 : 1];
     __shared__ int scan_tmp[kThreads / 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wm = wid >> 1, wn = wid & 1;
+    const int wm = wid >> 1, wn = wid & 1, half = lane >> 5;
     const int n_tiles = (p.N + kTile - 1) / kTile;
     int total, m_tiles = 0;
     if (WG) {
@@ -167,15 +187,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
         t_end = (int)((int64_t)total * (xcd + 1) / kXcds);
     }
 
-    int arow[4], brow[4];
+    // fragment addressing: K-contiguous A rows (DGRAD) and strided blocks
+    int arow[4];
+    uint32_t a_tr[4], b_tr[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) arow[mi] = wm * 128 + mi * 32 + (lane & 31);
+    for (int mi = 0; mi < 4; ++mi) {
+        arow[mi] = wm * 128 + mi * 32 + (lane & 31);
+        a_tr[mi] = tr_lane_off(wm * 128 + mi * 32, lane);
+    }
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) brow[ni] = wn * 128 + ni * 32 + (lane & 31);
+    for (int ni = 0; ni < 4; ++ni) b_tr[ni] = tr_lane_off(wn * 128 + ni * 32, lane);
+    // loaders: K-contiguous rows r = wid*64 + 8i + lane/8, chunk lane%8 (permuted by r & 7);
+    // strided K rows kr = 16 wid + 2i + lane/32, chunk position lane%32 (holds chunk pos ^ 4 (kr & 3))
+    const int c_lrow = lane >> 3, c_slot = lane & 7;
+    const int s_kr = lane >> 5, s_pos = lane & 31;
 
-    // strided-operand loader: thread -> 8 x 8 block (k block tid / 32, column block tid % 32)
-    const int sb_k = tid >> 5, sb_c = tid & 31;
-    // contiguous-operand loader: 8 chunks of 16 B per thread, chunk q = tid + 256 i
     for (int t = t_begin + lb; t < t_end; t += per_xcd) {
         int e, m0, n0, k_begin, k_end, row0 = 0, row_end = 0;
         float* cw = nullptr;
@@ -210,56 +236,45 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
             k_end = p.K;
         }
         const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
-        const uint16_t* Be = WG ? p.B : p.B + (size_t)e * p.K * p.N;
-        const int a_cols = WG ? p.M : 0;
 
-        uint4 ra[8], rb[8];
-        // global -> registers for K step kt
-#define GB_LOAD(kt)                                                                                       \
-    {                                                                                                     \
-        const int k0 = k_begin + (kt) * BK;                                                               \
-        if (WG) {                                                                                         \
-            _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                               \
-                const int k = k0 + sb_k * 8 + i, m = m0 + sb_c * 8;                                       \
-                ra[i] = (k < k_end && m < a_cols) ? *(const uint4*)(p.A + (size_t)k * a_cols + m)         \
-                                                  : make_uint4(0, 0, 0, 0);                               \
-            }                                                                                             \
-        } else {                                                                                          \
-            _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                               \
-                const int q = tid + 256 * i, r = q >> 3, c = q & 7;                                       \
-                const int row = m0 + r;                                                                   \
-                ra[i] = row < row_end ? *(const uint4*)(p.A + (size_t)row * p.K + k0 + c * 8)             \
-                                      : make_uint4(0, 0, 0, 0);                                           \
-            }                                                                                             \
-        }                                                                                                 \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                   \
-            const int k = k0 + sb_k * 8 + i, n = n0 + sb_c * 8;                                           \
-            rb[i] = (k < k_end && n < p.N) ? *(const uint4*)(Be + (size_t)k * p.N + n)                    \
-                                           : make_uint4(0, 0, 0, 0);                                      \
-        }                                                                                                 \
-    }
-        // registers -> LDS stage st (K-contiguous swizzled rows)
-#define GB_STORE(st)                                                                                      \
-    {                                                                                                     \
-        uint4 tr[8];                                                                                      \
-        if (WG) {                                                                                         \
-            transpose8x8(ra, tr);                                                                         \
-            _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                               \
-                const int r = sb_c * 8 + j;                                                               \
-                *(uint4*)&lds[st][0][r * BK + ((sb_k ^ swz<0>(r)) << 3)] = tr[j];                         \
-            }                                                                                             \
-        } else {                                                                                          \
-            _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                               \
-                const int q = tid + 256 * i, r = q >> 3, c = q & 7;                                       \
-                *(uint4*)&lds[st][0][r * BK + ((c ^ swz<0>(r)) << 3)] = ra[i];                            \
-            }                                                                                             \
-        }                                                                                                 \
-        transpose8x8(rb, tr);                                                                             \
-        _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                   \
-            const int r = sb_c * 8 + j;                                                                   \
-            *(uint4*)&lds[st][1][r * BK + ((sb_k ^ swz<0>(r)) << 3)] = tr[j];                             \
-        }                                                                                                 \
-    }
+        // per-lane byte offsets of the 8 loads of each operand, for K step 0
+        //   A: DGRAD rows of p.A [rows][K]; WGRAD K rows of p.A [rows][M] (columns m0..)
+        //   B: DGRAD K rows of B_e [K][N] (columns n0..); WGRAD K rows of p.B [rows][N]
+        const char* abase;
+        const char* bbase;
+        size_t a_kstep, b_kstep;  // bytes per K step of 64
+        uint32_t aoff[8], boff[8];
+        const int ncols_b = p.N;
+        if (WG) {
+            abase = (const char*)(p.A + (size_t)k_begin * p.M);
+            bbase = (const char*)(p.B + (size_t)k_begin * p.N);
+            a_kstep = (size_t)BK * p.M * 2;
+            b_kstep = (size_t)BK * p.N * 2;
+        } else {
+            abase = (const char*)(p.A + (size_t)row0 * p.K);
+            bbase = (const char*)(p.B + (size_t)e * p.K * p.N);
+            a_kstep = BK * 2;
+            b_kstep = (size_t)BK * p.N * 2;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kr = 16 * wid + 2 * i + s_kr;                   // strided: K row within the stage
+            const int sch = s_pos ^ ((kr & 3) << 2);                   // global chunk this lane fetches
+            const int ncol = min(n0 + 8 * sch, ncols_b - 8);           // clamp to a valid chunk
+            if (WG) {
+                const int mcol = min(m0 + 8 * sch, p.M - 8);
+                aoff[i] = (uint32_t)(((size_t)kr * p.M + mcol) * 2);
+                boff[i] = (uint32_t)(((size_t)kr * p.N + ncol) * 2);
+            } else {
+                const int r = wid * 64 + 8 * i + c_lrow;                // K-contiguous: tile row
+                const int ar = min(row0 + r, row_end - 1);
+                aoff[i] = (uint32_t)(((size_t)(ar - row0) * p.K + 8 * (c_slot ^ (r & 7))) * 2);
+                boff[i] = (uint32_t)(((size_t)kr * p.N + ncol) * 2);
+            }
+        }
+        // WGRAD: K rows past the unit's end load row k_end-1 instead (zeroed in A below)
+        int a_rowcap = 0;
+        if (WG) a_rowcap = k_end - k_begin - 1;
 
         f32x16 acc[4][4];
 #pragma unroll
@@ -269,38 +284,92 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
+#define GB_LOAD(kt, st)                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                       \
+        size_t ao = aoff[i] + (size_t)(kt) * a_kstep, bo = boff[i] + (size_t)(kt) * b_kstep;              \
+        if (WG) {                                                                                         \
+            const int kr = (kt) * BK + 16 * wid + 2 * i + s_kr;                                           \
+            if (kr > a_rowcap) {                                                                          \
+                const size_t back = (size_t)(kr - a_rowcap);                                              \
+                ao -= back * p.M * 2;                                                                     \
+                bo -= back * p.N * 2;                                                                     \
+            }                                                                                             \
+        }                                                                                                 \
+        __builtin_amdgcn_global_load_lds((glb_void*)(abase + ao),                                         \
+                                         (lds_void*)&lds[st][0][(WG ? (16 * wid + 2 * i) * 512            \
+                                                                    : (wid * 64 + 8 * i) * 128)], 16, 0, 0); \
+        __builtin_amdgcn_global_load_lds((glb_void*)(bbase + bo),                                         \
+                                         (lds_void*)&lds[st][1][(16 * wid + 2 * i) * 512], 16, 0, 0);     \
+    }
+        // WGRAD tail: zero the A copy of K rows past the unit's end (this wave's own rows, after its loads landed)
+#define GB_ZERO_TAIL(kt, st)                                                                              \
+    if (WG && (kt) * BK + BK - 1 > a_rowcap) {                                                            \
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");                                             \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                   \
+            const int kr = 16 * wid + 2 * i + s_kr;                                                       \
+            if ((kt) * BK + kr > a_rowcap) *(uint4*)&lds[st][0][kr * 512 + s_pos * 16] = make_uint4(0, 0, 0, 0); \
+        }                                                                                                 \
+    }
+
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0][0];
+        // fragments of K sub-step kk (16 values) of the stage in buffer st
+#define GB_READ(st, kk, FA, FB)                                                                           \
+    {                                                                                                     \
+        const uint32_t sa_ = lds_base + (st) * 2 * OPB, sb_ = sa_ + OPB;                                  \
+        _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                                \
+            if (WG) FA[mi] = bwd_tr_frag(sa_ + a_tr[mi] + (16 * (kk) + 8 * half) * 512);                  \
+            else FA[mi] = __builtin_bit_cast(bf16x8, bwd_ds_read16(sa_ + arow[mi] * 128 +                 \
+                                                                   ((((kk) * 2 + half) ^ (arow[mi] & 7)) << 4))); \
+        }                                                                                                 \
+        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                                  \
+            FB[ni] = bwd_tr_frag(sb_ + b_tr[ni] + (16 * (kk) + 8 * half) * 512);                          \
+    }
+#define GB_MFMAS(FA, FB)                                                                                  \
+    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)     \
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0);
+
+        bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
         if (nk > 0) {
-            GB_LOAD(0);
-            GB_STORE(0);
-            __syncthreads();
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous tile's stores retired
+            GB_LOAD(0, 0);
+            GB_ZERO_TAIL(0, 0);
+            __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            GB_READ(0, 0, f0a, f0b);
+            BWD_WAIT(f0a, f0b);
         }
         for (int kt = 0; kt < nk; ++kt) {
             const int st = kt & 1;
-            if (kt + 1 < nk) GB_LOAD(kt + 1);
-#pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                const int c = kk * 2 + (lane >> 5);
-                bf16x8 fa[4], fb[4];
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    fa[mi] = __builtin_bit_cast(
-                        bf16x8, *(const uint4*)&lds[st][0][arow[mi] * BK + ((c ^ swz<0>(arow[mi])) << 3)]);
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    fb[ni] = __builtin_bit_cast(
-                        bf16x8, *(const uint4*)&lds[st][1][brow[ni] * BK + ((c ^ swz<0>(brow[ni])) << 3)]);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-            }
-            if (kt + 1 < nk) GB_STORE(st ^ 1);
-            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) GB_LOAD(kt + 1, st ^ 1);  // into the buffer freed by the last barrier
+            GB_READ(st, 1, f1a, f1b);
+            __builtin_amdgcn_sched_barrier(0);
+            GB_MFMAS(f0a, f0b);
+            __builtin_amdgcn_sched_barrier(0);
+            BWD_WAIT(f1a, f1b);
+            GB_READ(st, 2, f0a, f0b);
+            __builtin_amdgcn_sched_barrier(0);
+            GB_MFMAS(f1a, f1b);
+            __builtin_amdgcn_sched_barrier(0);
+            BWD_WAIT(f0a, f0b);
+            GB_READ(st, 3, f1a, f1b);
+            __builtin_amdgcn_sched_barrier(0);
+            GB_MFMAS(f0a, f0b);
+            __builtin_amdgcn_sched_barrier(0);
+            BWD_WAIT(f1a, f1b);  // this wave has read all of stage kt
+            if (kt + 1 < nk) GB_ZERO_TAIL(kt + 1, st ^ 1);
+            // next stage landed for every wave; every wave is done with stage kt
+            __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) GB_READ(st ^ 1, 0, f0a, f0b);
+            __builtin_amdgcn_sched_barrier(0);
+            GB_MFMAS(f1a, f1b);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) BWD_WAIT(f0a, f0b);
         }
-
+#undef GB_READ
+#undef GB_MFMAS
 #undef GB_LOAD
-#undef GB_STORE
+#undef GB_ZERO_TAIL
         // epilogue: each 32x32 accumulator goes through this wave's 4 KiB of LDS
         // (row stride 33 floats) and comes back as 16 consecutive columns of
         // one row per lane, for 32/64-byte stores.  The stage buffers are free:
