@@ -122,8 +122,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
 
     for (int t = t_begin + lb; t < t_end; t += per_xcd) {
         int mt, nt;
-        tile_coords(t, total_m, n_tiles, 4, &mt, &nt);
-        const int e = find_expert(pre, p.E, mt);
+        // Tiles are ordered expert by expert, and within an expert N-tile by
+        // N-tile with its M-tiles adjacent: the blocks of one XCD that run at
+        // the same time then cover few experts, so each weight panel is
+        // fetched from HBM once and shared in L2 by all of the expert's M-tiles.
+        const int e = find_expert(pre, p.E, t / n_tiles);
+        {
+            const int m_e = pre[e + 1] - pre[e], li = t - pre[e] * n_tiles;
+            nt = li / m_e;
+            mt = pre[e] + li % m_e;
+        }
         const int row_end = min(p.offsets[e + 1], p.rows);
         const int row0 = p.offsets[e] + (mt - pre[e]) * kMxBM;
         if (row0 < 0 || row0 >= row_end) continue;  // only for inconsistent offsets
