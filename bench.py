@@ -217,7 +217,7 @@ def main():
         moe.moe_combine(cfg, buf["yp"], buf["row_map"], buf["w"], buf["y"])
         ev[5].record(stream)
         if s.backward:
-            moe.moe_combine_bwd(cfg, dy, buf["src_map"], buf["offsets"], buf["w"], bwd["dyp"])
+            moe.moe_combine_bwd(cfg, dy, buf["row_map"], buf["src_map"], buf["offsets"], buf["w"], bwd["dyp"])
             ev[6].record(stream)
             moe.moe_grouped_down_bwd(cfg, bwd["dyp"], w2, buf["h"], buf["gu_stash"], buf["offsets"], bwd["dgu"],
                                      bwd["dw2"], bwd["ws"])

@@ -192,10 +192,14 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
 /* weights are constants here (their gradient is not part of this path).     */
 /* ---------------------------------------------------------------------- */
 
-/* dYp[r] = round(w[s] * dy[s/k]) for real rows (s = src_map[r]) and 0 for
- * padding rows, r in [0, offsets[E]).  dy [T,H], dyp [R_cap,H], output dtype. */
-moe_status moe_combine_bwd(const moe_config* cfg, const void* dy, const int32_t* src_map, const int32_t* offsets,
-                           const float* w, void* dyp, void* stream);
+/* dYp[row_map[t,j]] = round(w[t,j] * dy[t]) for every route (t,j) whose
+ * row_map entry is a row in [0, R_cap); dYp[r] = 0 for every row r in
+ * [0, offsets[E]) whose src_map entry is not a route index in [0, T*k) (the
+ * padding rows).  row_map and src_map are the two directions of one
+ * permutation, as moe_permute writes them.  dy [T,H], dyp [R_cap,H], output
+ * dtype. */
+moe_status moe_combine_bwd(const moe_config* cfg, const void* dy, const int32_t* row_map, const int32_t* src_map,
+                           const int32_t* offsets, const float* w, void* dyp, void* stream);
 
 /* Down-projection backward fused with the SwiGLU backward, per expert rows:
  *   dH[r][f] = sum_o dYp[r][o] * w2[e][o][f]

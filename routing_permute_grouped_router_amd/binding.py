@@ -101,7 +101,7 @@ _SIGS = {
     "moe_grouped_down_gemm": (ctypes.c_int, [CFG, P, P, P, P, P, P, P]),
     "moe_combine": (ctypes.c_int, [CFG, P, P, P, P, P]),
     "moe_forward": (ctypes.c_int, [CFG] + [P] * 22 + [ctypes.c_size_t, P]),
-    "moe_combine_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P]),
+    "moe_combine_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P]),
     "moe_grouped_down_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_grouped_swiglu_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_permute_bwd": (ctypes.c_int, [CFG, P, P, P, P]),
@@ -272,10 +272,11 @@ def moe_forward(cfg: MoEConfig, logits, x, w1, w2, buf: dict, x_scale=None, w1_s
         _ptr(buf.get("err"), "err", torch.int32, (1,), optional=True), wp, wb, _stream(stream)))
 
 
-def moe_combine_bwd(cfg: MoEConfig, dy, src_map, offsets, w, dyp, stream=None):
+def moe_combine_bwd(cfg: MoEConfig, dy, row_map, src_map, offsets, w, dyp, stream=None):
     c = cfg.c()
     _check(load_library().moe_combine_bwd(
         ctypes.byref(c), _ptr(dy, "dy", cfg.out_dtype, (cfg.T, cfg.H)),
+        _ptr(row_map, "row_map", torch.int32, (cfg.T, cfg.k)),
         _ptr(src_map, "src_map", torch.int32, (cfg.R_cap,)), _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)),
         _ptr(w, "w", torch.float32, (cfg.T, cfg.k)), _ptr(dyp, "dyp", cfg.out_dtype, (cfg.R_cap, cfg.H)),
         _stream(stream)))

@@ -240,8 +240,8 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
     return moe_combine(cfg, yp, row_map, w, y, stream);
 }
 
-moe_status moe_combine_bwd(const moe_config* cfg, const void* dy, const int32_t* src_map, const int32_t* offsets,
-                           const float* w, void* dyp, void* stream) {
+moe_status moe_combine_bwd(const moe_config* cfg, const void* dy, const int32_t* row_map, const int32_t* src_map,
+                           const int32_t* offsets, const float* w, void* dyp, void* stream) {
     moe_status st = check_config(cfg);
     if (st) return st;
     if (cfg->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "the backward takes F32 or BF16 storage");
@@ -249,11 +249,12 @@ moe_status moe_combine_bwd(const moe_config* cfg, const void* dy, const int32_t*
     REQUIRE(offsets);
     if (rows_capacity(*cfg) > 0) {
         REQUIRE(dy);
+        REQUIRE(row_map);
         REQUIRE(src_map);
         REQUIRE(w);
         REQUIRE(dyp);
     }
-    return hip_status(launch_combine_bwd(*cfg, dy, src_map, offsets, w, dyp, as_stream(stream)), "moe_combine_bwd");
+    return hip_status(launch_combine_bwd(*cfg, dy, row_map, src_map, offsets, w, dyp, as_stream(stream)), "moe_combine_bwd");
 }
 
 moe_status moe_grouped_down_bwd(const moe_config* cfg, const void* dyp, const void* w2, const void* h,
@@ -315,7 +316,7 @@ moe_status moe_backward(const moe_config* cfg, const void* dy, const float* w, c
                         const void* h, const void* gu_stash, void* dyp, void* dgu, void* dxp, void* dx, float* dw1,
                         float* dw2, void* ws, size_t ws_bytes, void* stream) {
     moe_status st;
-    if ((st = moe_combine_bwd(cfg, dy, src_map, offsets, w, dyp, stream))) return st;
+    if ((st = moe_combine_bwd(cfg, dy, row_map, src_map, offsets, w, dyp, stream))) return st;
     if ((st = moe_grouped_down_bwd(cfg, dyp, w2, h, gu_stash, offsets, dgu, dw2, ws, ws_bytes, stream))) return st;
     if ((st = moe_grouped_swiglu_bwd(cfg, dgu, w1, xp, offsets, dxp, dw1, ws, ws_bytes, stream))) return st;
     return moe_permute_bwd(cfg, dxp, row_map, dx, stream);

@@ -4,9 +4,11 @@
 // expert-parallel Python API surface, PyTorch reference, and tests" (Summary)
 // and the TransformerEngine page "[JAX] Expert Parallelism: JAX primitives +
 // VJPs" (expert outputs summed across the top-k; padded or unused rows are
-// never multiplied in, since NaN * 0 would still be NaN).  All three kernels
-// are HBM-bound row gathers: one block per token (or per destination row),
-// 16-byte vector loads and stores, float32 accumulation, one rounding.
+// never multiplied in, since NaN * 0 would still be NaN).  All kernels here
+// are HBM-bound row moves with 16-byte vector loads and stores: the combine
+// and the permute backward gather a token's k rows (one block per token,
+// float32 accumulation, one rounding); the combine backward reads each token's
+// gradient row once and scatters it to the token's k rows.
 #include "moe_internal.h"
 
 namespace moe {
@@ -18,8 +20,16 @@ struct Vec;
 template <>
 struct Vec<false> {
     static constexpr int N = 8;
+    template <bool NT = false>
     __device__ static void load(const void* p, int64_t i, float* v) {
-        const uint4 q = ((const uint4*)p)[i];
+        uint4 q;
+        if (NT) {
+            const uint32_t* a = (const uint32_t*)((const uint4*)p + i);
+            q = make_uint4(__builtin_nontemporal_load(a), __builtin_nontemporal_load(a + 1),
+                           __builtin_nontemporal_load(a + 2), __builtin_nontemporal_load(a + 3));
+        } else {
+            q = ((const uint4*)p)[i];
+        }
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
@@ -27,18 +37,28 @@ struct Vec<false> {
             v[2 * a + 1] = __uint_as_float(w[a] & 0xffff0000u);
         }
     }
+    template <bool NT = false>
     __device__ static void store(void* p, int64_t i, const float* v) {
         uint4 q;
         q.x = pack_bf16x2(v[0], v[1]);
         q.y = pack_bf16x2(v[2], v[3]);
         q.z = pack_bf16x2(v[4], v[5]);
         q.w = pack_bf16x2(v[6], v[7]);
-        ((uint4*)p)[i] = q;
+        if (NT) {
+            uint32_t* a = (uint32_t*)((uint4*)p + i);
+            __builtin_nontemporal_store(q.x, a);
+            __builtin_nontemporal_store(q.y, a + 1);
+            __builtin_nontemporal_store(q.z, a + 2);
+            __builtin_nontemporal_store(q.w, a + 3);
+        } else {
+            ((uint4*)p)[i] = q;
+        }
     }
 };
 template <>
 struct Vec<true> {
     static constexpr int N = 4;
+    template <bool NT = false>
     __device__ static void load(const void* p, int64_t i, float* v) {
         const float4 q = ((const float4*)p)[i];
         v[0] = q.x;
@@ -46,13 +66,31 @@ struct Vec<true> {
         v[2] = q.z;
         v[3] = q.w;
     }
+    template <bool NT = false>
     __device__ static void store(void* p, int64_t i, const float* v) {
         ((float4*)p)[i] = make_float4(v[0], v[1], v[2], v[3]);
     }
 };
 
+// Gathers read the routes of a token in groups of G (the smallest of 1, 2, 4,
+// 8 that covers k, 8 for larger k): the group's row indices first, then all
+// of its row loads, unconditionally (a route without a valid row reads row 0
+// and is masked out), then the accumulation in ascending j.  Each lane then has
+// G 16-byte loads in flight instead of one.
+template <int G>
+__device__ __forceinline__ void gather_rows(const int32_t* __restrict__ row_map, int64_t t, int k, int j0,
+                                            int64_t n_rows, int32_t (&r)[G], bool (&ok)[G]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int j = j0 + g;
+        r[g] = j < k ? row_map[t * k + j] : -1;
+        ok[g] = r[g] >= 0 && r[g] < n_rows;
+        if (!ok[g]) r[g] = 0;
+    }
+}
+
 // y[t] = round(sum_j w[t,j] * Yp[row_map[t,j]]); one block per token.
-template <bool F32>
+template <bool F32, int G>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yp, const int32_t* __restrict__ row_map,
                                                       const float* __restrict__ w, int k, int vec_per_row,
                                                       int64_t n_rows, void* __restrict__ y) {
@@ -62,48 +100,81 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
         float acc[V::N];
 #pragma unroll
         for (int a = 0; a < V::N; ++a) acc[a] = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const int32_t r = row_map[t * k + j];
-            if (r < 0 || r >= n_rows) continue;
-            const float wt = w[t * k + j];
-            float v[V::N];
-            V::load(yp, (int64_t)r * vec_per_row + c, v);
+        for (int j0 = 0; j0 < k; j0 += G) {
+            int32_t r[G];
+            bool ok[G];
+            float v[G][V::N];
+            gather_rows<G>(row_map, t, k, j0, n_rows, r, ok);
 #pragma unroll
-            for (int a = 0; a < V::N; ++a) acc[a] = fmaf(wt, v[a], acc[a]);
+            for (int g = 0; g < G; ++g) V::template load<true>(yp, (int64_t)r[g] * vec_per_row + c, v[g]);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float wt = ok[g] ? w[t * k + j0 + g] : 0.f;
+#pragma unroll
+                for (int a = 0; a < V::N; ++a) acc[a] = ok[g] ? fmaf(wt, v[g][a], acc[a]) : acc[a];
+            }
         }
         V::store(y, t * vec_per_row + c, acc);
     }
 }
 
-// dYp[r] = round(w[s] * dy[s / k]) for a real row, 0 for a padding row.
+// dYp[row_map[t,j]] = round(w[t,j] * dy[t]): each token's gradient row is read
+// once and written to its k rows; tpb tokens per block when a row is shorter
+// than the block.
 template <bool F32>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const void* __restrict__ dy,
-                                                          const int32_t* __restrict__ src_map,
-                                                          const int32_t* __restrict__ offsets, int E,
-                                                          const float* __restrict__ w, int k, int vec_per_row,
-                                                          int64_t n_routes, void* __restrict__ dyp) {
+                                                          const int32_t* __restrict__ row_map,
+                                                          const float* __restrict__ w, int T, int k,
+                                                          int vec_per_row, int tpb, int64_t n_rows,
+                                                          void* __restrict__ dyp) {
     using V = Vec<F32>;
-    const int64_t r = blockIdx.x;
-    if (r >= offsets[E]) return;
-    int32_t s = src_map[r];  // -1 or a route index t*k+j (< T*k)
-    if (s >= n_routes) s = -1;
-    const float wt = s >= 0 ? w[s] : 0.f;
-    for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
-        float v[V::N];
-        if (s >= 0) {
-            V::load(dy, (int64_t)(s / k) * vec_per_row + c, v);
+    const int t0 = blockIdx.x * tpb;
+    const int n = min(tpb, T - t0) * vec_per_row;
+    for (int q = threadIdx.x; q < n; q += blockDim.x) {
+        const int t = t0 + q / vec_per_row;
+        const int c = q % vec_per_row;
+        float v[V::N], o[V::N];
+        V::load(dy, (int64_t)t * vec_per_row + c, v);
+        for (int j = 0; j < k; ++j) {
+            const int32_t r = row_map[(int64_t)t * k + j];
+            if (r < 0 || r >= n_rows) continue;
+            const float wt = w[(int64_t)t * k + j];
 #pragma unroll
-            for (int a = 0; a < V::N; ++a) v[a] *= wt;
-        } else {
-#pragma unroll
-            for (int a = 0; a < V::N; ++a) v[a] = 0.f;
+            for (int a = 0; a < V::N; ++a) o[a] = v[a] * wt;
+            V::template store<true>(dyp, (int64_t)r * vec_per_row + c, o);
         }
-        V::store(dyp, r * vec_per_row + c, v);
     }
 }
 
-// dx[t] = round(sum_j dXp[row_map[t,j]]).
+// Rows r < offsets[E] that carry no route (src_map[r] outside [0, n_routes):
+// the padding of a group) get dYp[r] = 0.  A block checks 256 rows, one per
+// thread, and then clears its padding rows (usually none) together.
 template <bool F32>
+__global__ __launch_bounds__(256) void zero_unrouted_rows_kernel(const int32_t* __restrict__ src_map,
+                                                                 const int32_t* __restrict__ offsets, int E,
+                                                                 int64_t n_routes, int vec_per_row, int64_t n_rows,
+                                                                 void* __restrict__ dyp) {
+    using V = Vec<F32>;
+    __shared__ int32_t pad[256];
+    __shared__ int n_pad;
+    if (threadIdx.x == 0) n_pad = 0;
+    __syncthreads();
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r < min((int64_t)offsets[E], n_rows)) {
+        const int32_t s = src_map[r];
+        if (s < 0 || s >= n_routes) pad[atomicAdd(&n_pad, 1)] = (int32_t)(r - (int64_t)blockIdx.x * 256);
+    }
+    __syncthreads();
+    float z[V::N];
+#pragma unroll
+    for (int a = 0; a < V::N; ++a) z[a] = 0.f;
+    const int n = n_pad * vec_per_row;
+    for (int q = threadIdx.x; q < n; q += 256)
+        V::store(dyp, ((int64_t)blockIdx.x * 256 + pad[q / vec_per_row]) * vec_per_row + q % vec_per_row, z);
+}
+
+// dx[t] = round(sum_j dXp[row_map[t,j]]).
+template <bool F32, int G>
 __global__ __launch_bounds__(256) void permute_bwd_kernel(const void* __restrict__ dxp,
                                                           const int32_t* __restrict__ row_map, int k,
                                                           int vec_per_row, int64_t n_rows, void* __restrict__ dx) {
@@ -113,17 +184,30 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const void* __restrict
         float acc[V::N];
 #pragma unroll
         for (int a = 0; a < V::N; ++a) acc[a] = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const int32_t r = row_map[t * k + j];
-            if (r < 0 || r >= n_rows) continue;
-            float v[V::N];
-            V::load(dxp, (int64_t)r * vec_per_row + c, v);
+        for (int j0 = 0; j0 < k; j0 += G) {
+            int32_t r[G];
+            bool ok[G];
+            float v[G][V::N];
+            gather_rows<G>(row_map, t, k, j0, n_rows, r, ok);
 #pragma unroll
-            for (int a = 0; a < V::N; ++a) acc[a] += v[a];
+            for (int g = 0; g < G; ++g) V::template load<true>(dxp, (int64_t)r[g] * vec_per_row + c, v[g]);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int a = 0; a < V::N; ++a) acc[a] = ok[g] ? acc[a] + v[g][a] : acc[a];
         }
         V::store(dx, t * vec_per_row + c, acc);
     }
 }
+
+// Launch a gather kernel template K<F32, G> with G chosen from k.
+#define MOE_GATHER_LAUNCH(KERNEL, F32, k, grid, block, s, ...)                                            \
+    do {                                                                                                 \
+        if ((k) <= 1) KERNEL<F32, 1><<<grid, block, 0, s>>>(__VA_ARGS__);                                \
+        else if ((k) <= 2) KERNEL<F32, 2><<<grid, block, 0, s>>>(__VA_ARGS__);                           \
+        else if ((k) <= 4) KERNEL<F32, 4><<<grid, block, 0, s>>>(__VA_ARGS__);                           \
+        else KERNEL<F32, 8><<<grid, block, 0, s>>>(__VA_ARGS__);                                         \
+    } while (0)
 
 int block_for(int vec_per_row) {
     int b = 64;
@@ -140,22 +224,30 @@ hipError_t launch_combine(const moe_config& c, const void* yp, const int32_t* ro
     const bool f32 = c.dtype == MOE_F32;
     const int vpr = c.H / (f32 ? 4 : 8);
     if (f32)
-        combine_kernel<true><<<c.T, block_for(vpr), 0, s>>>(yp, row_map, w, c.k, vpr, R_cap, y);
+        MOE_GATHER_LAUNCH(combine_kernel, true, c.k, c.T, block_for(vpr), s, yp, row_map, w, c.k, vpr, R_cap, y);
     else
-        combine_kernel<false><<<c.T, block_for(vpr), 0, s>>>(yp, row_map, w, c.k, vpr, R_cap, y);
+        MOE_GATHER_LAUNCH(combine_kernel, false, c.k, c.T, block_for(vpr), s, yp, row_map, w, c.k, vpr, R_cap, y);
     return hipGetLastError();
 }
 
-hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const int32_t* src_map, const int32_t* offsets,
-                              const float* w, void* dyp, hipStream_t s) {
+hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const int32_t* row_map, const int32_t* src_map,
+                              const int32_t* offsets, const float* w, void* dyp, hipStream_t s) {
     const int64_t rows = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     if (rows == 0) return hipSuccess;
     const bool f32 = c.dtype == MOE_F32;
     const int vpr = c.H / (f32 ? 4 : 8);
-    if (f32)
-        combine_bwd_kernel<true><<<rows, block_for(vpr), 0, s>>>(dy, src_map, offsets, c.E, w, c.k, vpr, (int64_t)c.T * c.k, dyp);
-    else
-        combine_bwd_kernel<false><<<rows, block_for(vpr), 0, s>>>(dy, src_map, offsets, c.E, w, c.k, vpr, (int64_t)c.T * c.k, dyp);
+    const int tpb = vpr >= 256 ? 1 : (256 + vpr - 1) / vpr;
+    const int64_t n_routes = (int64_t)c.T * c.k;
+    const unsigned zgrid = (unsigned)((rows + 255) / 256);
+    if (f32) {
+        zero_unrouted_rows_kernel<true><<<zgrid, 256, 0, s>>>(src_map, offsets, c.E, n_routes, vpr, rows, dyp);
+        if (c.T > 0)
+            combine_bwd_kernel<true><<<(c.T + tpb - 1) / tpb, 256, 0, s>>>(dy, row_map, w, c.T, c.k, vpr, tpb, rows, dyp);
+    } else {
+        zero_unrouted_rows_kernel<false><<<zgrid, 256, 0, s>>>(src_map, offsets, c.E, n_routes, vpr, rows, dyp);
+        if (c.T > 0)
+            combine_bwd_kernel<false><<<(c.T + tpb - 1) / tpb, 256, 0, s>>>(dy, row_map, w, c.T, c.k, vpr, tpb, rows, dyp);
+    }
     return hipGetLastError();
 }
 
@@ -166,9 +258,9 @@ hipError_t launch_permute_bwd(const moe_config& c, const void* dxp, const int32_
     const bool f32 = c.dtype == MOE_F32;
     const int vpr = c.H / (f32 ? 4 : 8);
     if (f32)
-        permute_bwd_kernel<true><<<c.T, block_for(vpr), 0, s>>>(dxp, row_map, c.k, vpr, R_cap, dx);
+        MOE_GATHER_LAUNCH(permute_bwd_kernel, true, c.k, c.T, block_for(vpr), s, dxp, row_map, c.k, vpr, R_cap, dx);
     else
-        permute_bwd_kernel<false><<<c.T, block_for(vpr), 0, s>>>(dxp, row_map, c.k, vpr, R_cap, dx);
+        MOE_GATHER_LAUNCH(permute_bwd_kernel, false, c.k, c.T, block_for(vpr), s, dxp, row_map, c.k, vpr, R_cap, dx);
     return hipGetLastError();
 }
 

@@ -54,8 +54,8 @@ hipError_t launch_permute_rows(const moe_config& c, const void* x, const uint8_t
 
 hipError_t launch_combine(const moe_config& c, const void* yp, const int32_t* row_map, const float* w, void* y,
                           hipStream_t s);
-hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const int32_t* src_map, const int32_t* offsets,
-                              const float* w, void* dyp, hipStream_t s);
+hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const int32_t* row_map, const int32_t* src_map,
+                              const int32_t* offsets, const float* w, void* dyp, hipStream_t s);
 hipError_t launch_permute_bwd(const moe_config& c, const void* dxp, const int32_t* row_map, void* dx,
                               hipStream_t s);
 

@@ -2,7 +2,8 @@
 fused with the SwiGLU backward, gate/up backward, permute backward) against
 the CPU oracle, through the C ABI.
 
-Small skewed shape: every gradient compared in full.  Full-size skewed workload
+Small shapes (skewed routing; 16-row group alignment): every gradient compared
+in full.  Full-size skewed workload
 (T=16384, H=2048, F=768, E=128, top-8, Zipf-biased routing): dX on a seeded
 token sample, dW1/dW2 on sampled entries of moderately loaded experts, and
 dW of every empty expert exactly zero (it starts as NaN)."""
@@ -30,8 +31,11 @@ def _run_backward(inp, fwd):
     return bwd
 
 
-def test_backward_small_skewed_full_parity():
-    s = [x for x in wl.small_shapes() if x.name == "small_skewed_bf16"][0]
+@pytest.mark.parametrize("name", ["small_skewed_bf16", "small_bf16_sigmoid_align"])
+def test_backward_small_full_parity(name):
+    """Skewed routing (empty experts) and a 16-row group alignment (padding
+    rows, which the combine backward must zero)."""
+    s = [x for x in wl.small_shapes() if x.name == name][0]
     inp = Inputs(s, want_dy=True)
     fwd = run_forward(inp, training=True)
     bwd = _run_backward(inp, fwd)
@@ -54,8 +58,13 @@ def test_backward_small_skewed_full_parity():
     assert np.all(np.isfinite(dw1)) and np.all(np.isfinite(dw2))
     assert rel_err(dw1, g["dw1"]) < TOL["bf16"]
     assert rel_err(dw2, g["dw2"]) < TOL["bf16"]
+    if s.align > 1:
+        pad = src_map[:n] < 0
+        assert pad.any(), "the alignment should leave padding rows"
+        assert np.all(to_host(bwd["dyp"])[:n][pad] == 0)
     empty = np.where(counts == 0)[0]
-    assert len(empty) > 0, "the skewed routing should leave some experts empty"
+    if name == "small_skewed_bf16":
+        assert len(empty) > 0, "the skewed routing should leave some experts empty"
     assert np.all(dw1[empty] == 0) and np.all(dw2[empty] == 0)
 
 
