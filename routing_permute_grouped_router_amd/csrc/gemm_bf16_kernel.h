@@ -75,6 +75,44 @@ __device__ __forceinline__ int swz(int row) {
     make_uint4(pack_bf16x2((V)[(O)], (V)[(O) + 1]), pack_bf16x2((V)[(O) + 2], (V)[(O) + 3]),            \
                pack_bf16x2((V)[(O) + 4], (V)[(O) + 5]), pack_bf16x2((V)[(O) + 6], (V)[(O) + 7]))
 
+// Direct epilogue helpers.  A 32 x 32 fp32 accumulator tile holds, in lane l
+// and slot q, row 8 (q / 4) + 4 (l / 32) + q % 4 of column l % 32.  pair_bf16
+// rounds it to bf16 (nearest even) and regroups it with the neighbouring lane
+// (l ^ 1, a DPP quad permute) so that word p of lane l holds the two adjacent
+// columns (l % 32) & ~1 and +1 of row pair_row(p, l).
+// An accumulator element read out of its AGPR where it is used, so the
+// compiler does not copy every accumulator to VGPRs as the K loop ends.
+__device__ __forceinline__ float agpr_read(float a) {
+    float v;
+    __asm__ volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+__device__ __forceinline__ float swap_lane1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ int pair_row(int p, int lane) {
+    return 8 * (p >> 1) + 4 * (lane >> 5) + 2 * (p & 1) + (lane & 1);
+}
+__device__ __forceinline__ void pair_bf16(const float (&v)[16], int lane, uint32_t (&out)[8]) {
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const float recv = swap_lane1(odd ? v[2 * p] : v[2 * p + 1]);
+        const float lo = odd ? recv : v[2 * p], hi = odd ? v[2 * p + 1] : recv;
+        out[p] = pack_bf16x2(lo, hi);
+    }
+}
+
+// The same regrouping without rounding: float32 pairs.
+__device__ __forceinline__ void pair_f32(const float (&v)[16], int lane, float2 (&out)[8]) {
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const float recv = swap_lane1(odd ? v[2 * p] : v[2 * p + 1]);
+        out[p] = make_float2(odd ? recv : v[2 * p], odd ? v[2 * p + 1] : recv);
+    }
+}
+
 template <bool SWIGLU, int SWZ, int GM, int EARLY = 0>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     constexpr int BK = 64;                  // K depth of one stage
@@ -229,69 +267,88 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #undef GG_ISSUE
         __syncthreads();  // every wave done with both stages before the next tile's loads
 
-        // Epilogue through LDS, one 32 x 32 accumulator tile at a time per
-        // wavefront: the MFMA layout (lane = column, 16 rows per lane) is
-        // turned into 16 consecutive columns of one row per lane, so every
-        // store is 16 bytes wide.
-        float* wb = (float*)&lds[0][0][0] + wid * 2 * (32 * 33 + 32);
-        float* wb2 = wb + 32 * 33 + 32;
-        const int rr = lane >> 1, cc = (lane & 1) * 16;
+        // Epilogue straight from the accumulators: each 32 x 32 tile becomes 8
+        // bf16 pairs per lane (two adjacent columns of one row, one DPP lane
+        // swap per pair), stored as 4-byte words; 32 lanes cover 128
+        // contiguous bytes of a row.  No LDS, so no barrier before the next tile.
+        // Opaque copies of the tile's first row and of the lane index: the
+        // address arithmetic below then stays after the K loop (it is not
+        // hoisted out of the tile loop, where it would hold registers).
+        int rbase = row0, ln = lane;
+        __asm__ volatile("" : "+v"(rbase), "+v"(ln));
+        const int c2 = (ln & 31) & ~1;                // even column of this lane's pairs
+        const int prow = 4 * (ln >> 5) + (ln & 1);    // row of this lane's pair 0 in a 32-row block
+        const int rlim = row_end - rbase;  // rows of the tile that exist
+        const uint32_t ldw = (uint32_t)p.n_out / 2;  // 4-byte words per output row
+        // Store the 8 pairs of a 32-row block whose first row (tile-relative) is
+        // RB0 from word pointer DST (this lane's pair-0 address), LDW words per
+        // row; the rows are checked only when the block runs past the group's end.
+#define GB_STORE_PAIRS(DST, LDW, RB0, VP)                                                                \
+    if ((RB0) + 32 <= rlim) {                                                                            \
+        _Pragma("unroll") for (int q = 0; q < 8; ++q)                                                    \
+            (DST)[(8 * (q >> 1) + 2 * (q & 1)) * (LDW)] = (VP)[q];                                       \
+    } else {                                                                                             \
+        _Pragma("unroll") for (int q = 0; q < 8; ++q)                                                    \
+            if ((RB0) + prow + 8 * (q >> 1) + 2 * (q & 1) < rlim)                                        \
+                (DST)[(8 * (q >> 1) + 2 * (q & 1)) * (LDW)] = (VP)[q];                                   \
+    }
         if (SWIGLU) {
+            uint16_t* const cbase = p.C + (size_t)rbase * p.n_out;
+            uint16_t* const sbase = p.stash ? p.stash + (size_t)rbase * 2 * p.n_out : nullptr;
 #define GB_EPI_SW(MI, NI)                                                                                \
     {                                                                                                    \
-        GE_STAGE_TILE(wb, acc[MI][NI])                                                                   \
-        GE_STAGE_TILE(wb2, acc[MI][(NI) + 2])                                                            \
-        __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
+        const int f = nt * 128 + wn * 64 + (NI) * 32 + c2;                                               \
+        const int rb0 = wm * 128 + (MI) * 32;                                                            \
+        float hv[16];                                                                                    \
         float gv[16], uv[16];                                                                            \
-        _Pragma("unroll") for (int j = 0; j < 16; ++j) {                                                 \
-            gv[j] = wb[rr * 33 + cc + j];                                                                \
-            uv[j] = wb2[rr * 33 + cc + j];                                                               \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                                 \
+            gv[q] = agpr_read(acc[MI][NI][q]);                                                           \
+            uv[q] = agpr_read(acc[MI][(NI) + 2][q]);                                                     \
+            hv[q] = silu(gv[q]) * uv[q];                                                                 \
         }                                                                                                \
-        __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
-        const int r = row0 + wm * 128 + (MI) * 32 + rr;                                                  \
-        const int f = nt * 128 + wn * 64 + (NI) * 32 + cc;                                               \
-        if (r < row_end && f < p.n_out) {                                                                \
-            uint4* dst = (uint4*)(p.C + (size_t)r * p.n_out + f);                                        \
-            _Pragma("unroll") for (int j = 0; j < 2; ++j) dst[j] = make_uint4(                          \
-                pack_bf16x2(silu(gv[8 * j]) * uv[8 * j], silu(gv[8 * j + 1]) * uv[8 * j + 1]),           \
-                pack_bf16x2(silu(gv[8 * j + 2]) * uv[8 * j + 2], silu(gv[8 * j + 3]) * uv[8 * j + 3]),   \
-                pack_bf16x2(silu(gv[8 * j + 4]) * uv[8 * j + 4], silu(gv[8 * j + 5]) * uv[8 * j + 5]),   \
-                pack_bf16x2(silu(gv[8 * j + 6]) * uv[8 * j + 6], silu(gv[8 * j + 7]) * uv[8 * j + 7]));  \
-            if (p.stash) {                                                                               \
-                uint4* gs = (uint4*)(p.stash + (size_t)r * 2 * p.n_out + f);                             \
-                uint4* us = (uint4*)(p.stash + (size_t)r * 2 * p.n_out + p.n_out + f);                   \
-                _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                         \
-                    gs[j] = GE_PACK8(gv, 8 * j);                                                         \
-                    us[j] = GE_PACK8(uv, 8 * j);                                                         \
-                }                                                                                        \
+        uint32_t hp[8];                                                                                  \
+        pair_bf16(hv, lane, hp);                                                                         \
+        if (f < p.n_out) {                                                                               \
+            uint32_t* dst = (uint32_t*)(cbase + (uint32_t)((rb0 + prow) * p.n_out + f));                 \
+            GB_STORE_PAIRS(dst, ldw, rb0, hp)                                                                 \
+            if (sbase) {                                                                                 \
+                uint32_t gp[8], up[8];                                                                   \
+                pair_bf16(gv, lane, gp);                                                                 \
+                pair_bf16(uv, lane, up);                                                                 \
+                uint32_t* gd = (uint32_t*)(sbase + (uint32_t)((rb0 + prow) * 2 * p.n_out + f));          \
+                GB_STORE_PAIRS(gd, 2 * ldw, rb0, gp)                                                              \
+                uint32_t* ud = gd + ldw;                                                                 \
+                GB_STORE_PAIRS(ud, 2 * ldw, rb0, up)                                                              \
             }                                                                                            \
         }                                                                                                \
-    }
+    }                                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);
             GB_EPI_SW(0, 0) GB_EPI_SW(0, 1) GB_EPI_SW(1, 0) GB_EPI_SW(1, 1)
             GB_EPI_SW(2, 0) GB_EPI_SW(2, 1) GB_EPI_SW(3, 0) GB_EPI_SW(3, 1)
 #undef GB_EPI_SW
         } else {
+            uint16_t* const cbase = p.C + (size_t)rbase * p.n_out;
 #define GB_EPI_DN(MI, NI)                                                                                \
     {                                                                                                    \
-        GE_STAGE_TILE(wb, acc[MI][NI])                                                                   \
-        __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
+        const int n = nt * kTile + wn * 128 + (NI) * 32 + c2;                                            \
+        const int rb0 = wm * 128 + (MI) * 32;                                                            \
         float v[16];                                                                                     \
-        _Pragma("unroll") for (int j = 0; j < 16; ++j) v[j] = wb[rr * 33 + cc + j];                      \
-        __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
-        const int r = row0 + wm * 128 + (MI) * 32 + rr;                                                  \
-        const int n = nt * kTile + wn * 128 + (NI) * 32 + cc;                                            \
-        if (r < row_end && n < p.n_out) {                                                                \
-            uint4* dst = (uint4*)(p.C + (size_t)r * p.n_out + n);                                        \
-            _Pragma("unroll") for (int j = 0; j < 2; ++j) dst[j] = GE_PACK8(v, 8 * j);                  \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
+        uint32_t vp[8];                                                                                  \
+        pair_bf16(v, lane, vp);                                                                          \
+        if (n < p.n_out) {                                                                               \
+            uint32_t* dst = (uint32_t*)(cbase + (uint32_t)((rb0 + prow) * p.n_out + n));                 \
+            GB_STORE_PAIRS(dst, ldw, rb0, vp)                                                                 \
         }                                                                                                \
-    }
+    }                                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);
             GB_EPI_DN(0, 0) GB_EPI_DN(0, 1) GB_EPI_DN(0, 2) GB_EPI_DN(0, 3)
             GB_EPI_DN(1, 0) GB_EPI_DN(1, 1) GB_EPI_DN(1, 2) GB_EPI_DN(1, 3)
             GB_EPI_DN(2, 0) GB_EPI_DN(2, 1) GB_EPI_DN(2, 2) GB_EPI_DN(2, 3)
             GB_EPI_DN(3, 0) GB_EPI_DN(3, 1) GB_EPI_DN(3, 2) GB_EPI_DN(3, 3)
 #undef GB_EPI_DN
         }
-        __syncthreads();  // LDS reused by the next tile's loads
+#undef GB_STORE_PAIRS
     }
 }
 

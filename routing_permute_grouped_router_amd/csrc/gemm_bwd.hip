@@ -36,8 +36,19 @@ int64_t wgrad_slots(const moe_config& c, int64_t M, int64_t N) {
 }
 
 size_t wgrad_ws_bytes(const moe_config& c, int64_t M, int64_t N) {
-    // partial sums, then E (units, first slot) pairs
+    // partial sums, then E (units, first slot) pairs, then 2 x 8 tile counters
     return (size_t)(wgrad_slots(c, M, N) * M * N * 4) + (size_t)c.E * sizeof(int2) + 256;
+}
+
+// The tile counters of a DGRAD launch (8) and of the WGRAD launch after it (8).
+int* tile_counters(const moe_config& c, int64_t M, int64_t N, void* ws) {
+    return (int*)((char*)ws + wgrad_slots(c, M, N) * M * N * 4 + (size_t)c.E * sizeof(int2));
+}
+
+// Zeroes the 16 tile counters (a kernel rather than a memset node, so the
+// calls stay safe to capture in a graph).
+__global__ void zero_counters_kernel(int* cnt) {
+    if (threadIdx.x < 2 * gemm::kXcds) cnt[threadIdx.x] = 0;
 }
 
 // dW[e] = sum over the expert's units, in unit order, of the partial sums,
@@ -72,6 +83,7 @@ hipError_t launch(const gemm::BwdArgs& a, int64_t max_tiles, hipStream_t s) {
 
 hipError_t launch_wgrad(const moe_config& c, gemm::BwdArgs w, void* ws, hipStream_t s) {
     const int64_t M = w.M, N = w.N;
+    w.sched = tile_counters(c, M, N, ws) + gemm::kXcds;
     const int64_t slots = wgrad_slots(c, M, N);
     w.S = wgrad_split_rows(c, M, N);
     w.slots = (int)slots;
@@ -98,12 +110,14 @@ hipError_t launch_down_bwd(const moe_config& c, const void* dyp, const void* w2,
                            const int32_t* offsets, void* dgu, float* dw2, void* ws, hipStream_t s) {
     if (c.dtype != MOE_BF16) return hipErrorNotSupported;
     const int64_t R = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
+    int* cnt = tile_counters(c, c.H, c.F, ws);
+    zero_counters_kernel<<<1, 64, 0, s>>>(cnt);
     gemm::BwdArgs d{(const uint16_t*)dyp, (const uint16_t*)w2, offsets, c.E, (int)R, 0, c.F, c.H,
-                    (uint16_t*)dgu, nullptr, (const uint16_t*)stash, nullptr, nullptr, 0, 0};
+                    (uint16_t*)dgu, nullptr, (const uint16_t*)stash, nullptr, nullptr, 0, 0, cnt};
     hipError_t e = launch<gemm::kDgradDswiglu>(d, (R / gemm::kTile + c.E) * cdiv(c.F, gemm::kTile), s);
     if (e != hipSuccess) return e;
     gemm::BwdArgs w{(const uint16_t*)dyp, (const uint16_t*)h, offsets, c.E, (int)R, c.H, c.F, 0,
-                    nullptr, dw2, nullptr, nullptr, nullptr, 0, 0};
+                    nullptr, dw2, nullptr, nullptr, nullptr, 0, 0, nullptr};
     return launch_wgrad(c, w, ws, s);
 }
 
@@ -111,12 +125,14 @@ hipError_t launch_swiglu_bwd(const moe_config& c, const void* dgu, const void* w
                              const int32_t* offsets, void* dxp, float* dw1, void* ws, hipStream_t s) {
     if (c.dtype != MOE_BF16) return hipErrorNotSupported;
     const int64_t R = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
+    int* cnt = tile_counters(c, 2 * (int64_t)c.F, c.H, ws);
+    zero_counters_kernel<<<1, 64, 0, s>>>(cnt);
     gemm::BwdArgs d{(const uint16_t*)dgu, (const uint16_t*)w1, offsets, c.E, (int)R, 0, c.H, 2 * c.F,
-                    (uint16_t*)dxp, nullptr, nullptr, nullptr, nullptr, 0, 0};
+                    (uint16_t*)dxp, nullptr, nullptr, nullptr, nullptr, 0, 0, cnt};
     hipError_t e = launch<gemm::kDgrad>(d, (R / gemm::kTile + c.E) * cdiv(c.H, gemm::kTile), s);
     if (e != hipSuccess) return e;
     gemm::BwdArgs w{(const uint16_t*)dgu, (const uint16_t*)xp, offsets, c.E, (int)R, 2 * c.F, c.H, 0,
-                    nullptr, dw1, nullptr, nullptr, nullptr, 0, 0};
+                    nullptr, dw1, nullptr, nullptr, nullptr, 0, 0, nullptr};
     return launch_wgrad(c, w, ws, s);
 }
 

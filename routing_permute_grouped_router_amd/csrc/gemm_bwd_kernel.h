@@ -63,57 +63,19 @@ struct BwdArgs {
     int2* meta;
     int S;
     int slots;
+    // Tile counters, one per XCD, zero at launch: the blocks of an XCD take
+    // their next tile from the XCD's list with an atomic increment.
+    int* sched;
 };
 
-// Epilogue of 16 consecutive output columns n..n+15 of row r (values v).
-template <int MODE>
-__device__ __forceinline__ void bwd_store16(const BwdArgs& p, const float (&v)[16], float* cw, int r, int n,
-                                            int row_end) {
-    if (n >= p.N) return;
-    if (MODE == kWgrad) {
-        if (r >= p.M) return;
-        float4* dst = (float4*)(cw + (size_t)r * p.N + n);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
-        return;
-    }
-    if (r >= row_end) return;
-    if (MODE == kDgrad) {
-        uint4* dst = (uint4*)(p.C + (size_t)r * p.N + n);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            dst[j] = make_uint4(pack_bf16x2(v[8 * j], v[8 * j + 1]), pack_bf16x2(v[8 * j + 2], v[8 * j + 3]),
-                                pack_bf16x2(v[8 * j + 4], v[8 * j + 5]), pack_bf16x2(v[8 * j + 6], v[8 * j + 7]));
-        return;
-    }
-    // SwiGLU backward: v = dH[r, n..]; g, u from the bf16 stash
-    const uint4* gs = (const uint4*)(p.stash + (size_t)r * 2 * p.N + n);
-    const uint4* us = (const uint4*)(p.stash + (size_t)r * 2 * p.N + p.N + n);
-    uint4* dg = (uint4*)(p.C + (size_t)r * 2 * p.N + n);
-    uint4* du = (uint4*)(p.C + (size_t)r * 2 * p.N + p.N + n);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const uint4 gq = gs[j], uq = us[j];
-        const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w}, uw[4] = {uq.x, uq.y, uq.z, uq.w};
-        uint32_t og[4], ou[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            float rg[2], ru[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float g = __uint_as_float(h ? (gw[w] & 0xffff0000u) : (gw[w] << 16));
-                const float u = __uint_as_float(h ? (uw[w] & 0xffff0000u) : (uw[w] << 16));
-                const float dh = v[8 * j + 2 * w + h];
-                const float sg = 1.0f / (1.0f + __expf(-g));
-                rg[h] = dh * u * sg * (1.0f + g * (1.0f - sg));
-                ru[h] = dh * g * sg;
-            }
-            og[w] = pack_bf16x2(rg[0], rg[1]);
-            ou[w] = pack_bf16x2(ru[0], ru[1]);
-        }
-        dg[j] = make_uint4(og[0], og[1], og[2], og[3]);
-        du[j] = make_uint4(ou[0], ou[1], ou[2], ou[3]);
-    }
+constexpr int kMaxUnits = 2048;  // weight-gradient units dealt by size (beyond: by index)
+
+// Hand the tile index that thread 0 fetched (nxt) to the whole block.
+__device__ __forceinline__ int bwd_next_tile(int* s_next, int& sb, int nxt) {
+    if (threadIdx.x == 0) s_next[sb ^ 1] = nxt;
+    __syncthreads();
+    sb ^= 1;
+    return s_next[sb];
 }
 
 // Byte offset, within a [64][256] strided stage region, that lane `lane`
@@ -171,21 +133,56 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
     } else {
         total = build_tile_prefix(p.offsets, p.E, kTile, pre, scan_tmp) * n_tiles;
     }
-    const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
-    const int lb = blockIdx.x / kXcds;
-    // Row-indexed GEMMs: every tile costs the same, so each XCD takes a
-    // contiguous range.  Weight gradients: units differ in rows (hot experts
-    // come first in expert order), so units are dealt to the XCDs round robin
-    // (unit u to XCD u % 8) and each XCD walks the tiles of its own units.
-    int t_begin, t_end;
+    const int xcd = blockIdx.x % kXcds;
+    // Row-indexed GEMMs: every tile costs the same; each XCD owns a
+    // contiguous range of the tile sequence.  Weight gradients: units differ
+    // in rows, so they are ranked by rows (longest first) and dealt to the
+    // XCDs in snake order (ranks 0..7 to XCDs 0..7, ranks 8..15 to XCDs
+    // 7..0, ...), which evens out the XCDs' loads; an XCD lists its units in
+    // rank order.  In both cases the blocks of an XCD take tiles from the
+    // XCD's list through its counter, so a block that finishes early takes
+    // the next tile.
+    __shared__ int32_t ukey[WG ? kMaxUnits : 1];
+    __shared__ int32_t uorder[WG ? kMaxUnits / kXcds + 1 : 1];
+    __shared__ int s_next[2];
+    int t_begin, t_end, nj = 0;
+    const int mn = m_tiles * n_tiles;
+    const bool dealt = WG && total / max(mn, 1) <= kMaxUnits;
     if (WG) {
-        const int units = total / (m_tiles * n_tiles);
+        const int units = total / mn;
+        if (dealt) {
+            for (int u = tid; u < units; u += kThreads) {
+                const int e = find_expert(pre, p.E, u);
+                const int r_begin = max(0, p.offsets[e]), r_end = min(p.offsets[e + 1], p.rows);
+                const int kb = min(r_begin + (u - pre[e]) * p.S, r_end);
+                ukey[u] = min(kb + p.S, r_end) - kb;
+            }
+            __syncthreads();
+            for (int u = tid; u < units; u += kThreads) {
+                const int ku = ukey[u];
+                int rank = 0;
+                for (int i = 0; i < units; ++i) {
+                    const int ki = ukey[i];
+                    rank += ki > ku || (ki == ku && i < u);
+                }
+                const int round = rank / kXcds, pos = rank % kXcds;
+                if (((round & 1) ? kXcds - 1 - pos : pos) == xcd) uorder[round] = u;
+            }
+            const int full = units / kXcds, rest = units % kXcds;
+            nj = full + (((full & 1) ? kXcds - 1 - xcd : xcd) < rest ? 1 : 0);
+        } else {
+            nj = units > xcd ? (units - xcd + kXcds - 1) / kXcds : 0;
+        }
         t_begin = 0;
-        t_end = (units > xcd ? (units - xcd + kXcds - 1) / kXcds : 0) * m_tiles * n_tiles;
+        t_end = nj * mn;
     } else {
         t_begin = (int)((int64_t)total * xcd / kXcds);
         t_end = (int)((int64_t)total * (xcd + 1) / kXcds);
     }
+    int sb = 0, nxt = 0;
+    if (tid == 0) s_next[0] = atomicAdd(p.sched + xcd, 1);
+    __syncthreads();
+    const int t_first = t_begin + s_next[0];
 
     // fragment addressing: K-contiguous A rows (DGRAD) and strided blocks
     int arow[4];
@@ -202,13 +199,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
     const int c_lrow = lane >> 3, c_slot = lane & 7;
     const int s_kr = lane >> 5, s_pos = lane & 31;
 
-    for (int t = t_begin + lb; t < t_end; t += per_xcd) {
+    for (int t = t_first; t < t_end; t = t_begin + bwd_next_tile(s_next, sb, nxt)) {
+        if (tid == 0) nxt = atomicAdd(p.sched + xcd, 1);  // the tile after this one; read at its end
         int e, m0, n0, k_begin, k_end, row0 = 0, row_end = 0;
         float* cw = nullptr;
         if (WG) {
-            const int j = t / (m_tiles * n_tiles);
-            const int rem = t - j * m_tiles * n_tiles;
-            const int u = xcd + kXcds * j;
+            const int jl = t / mn;
+            const int rem = t - jl * mn;
+            const int u = dealt ? uorder[jl] : xcd + kXcds * jl;
             e = find_expert(pre, p.E, u);
             const int s = u - pre[e], units = pre[e + 1] - pre[e];
             m0 = (rem / n_tiles) * kTile;
@@ -370,28 +368,124 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
 #undef GB_MFMAS
 #undef GB_LOAD
 #undef GB_ZERO_TAIL
-        // epilogue: each 32x32 accumulator goes through this wave's 4 KiB of LDS
-        // (row stride 33 floats) and comes back as 16 consecutive columns of
-        // one row per lane, for 32/64-byte stores.  The stage buffers are free:
-        // the K loop ended with a barrier.
-        float* wbuf = (float*)&lds[0][0][0] + wid * (32 * 33 + 32);
-        const int rr = lane >> 1, c0 = (lane & 1) * 16;
-#define GB_EPI(MI, NI)                                                                                   \
+        // Epilogue straight from the accumulators (no LDS): each 32 x 32 tile
+        // becomes 8 pairs of adjacent columns of one row per lane (a DPP swap
+        // with lane ^ 1), stored as 8-byte float32 pairs (weight gradients) or
+        // 4-byte bf16 pairs.  The SwiGLU backward loads the matching (g, u)
+        // pairs of the stash a 32-row block ahead of their use.
+        // Opaque copies of the tile's first row and of the lane index: the
+        // address arithmetic below then stays after the K loop (it is not
+        // hoisted out of the tile loop, where it would hold registers).
+        int mbase = m0, ln = lane;
+        __asm__ volatile("" : "+v"(mbase), "+v"(ln));
+        const int c2 = (ln & 31) & ~1;
+        const int prow = 4 * (ln >> 5) + (ln & 1);
+        if (WG) {
+            const int mlim = p.M - mbase;
+#define GB_EPI_WG(MI, NI)                                                                                \
     {                                                                                                    \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                  \
-            wbuf[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * 33 + (lane & 31)] = acc[MI][NI][q];        \
-        __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): the wave's writes are in LDS */              \
+        const int n = n0 + wn * 128 + (NI) * 32 + c2;                                                    \
+        const int rb0 = wm * 128 + (MI) * 32;                                                            \
         float v[16];                                                                                     \
-        _Pragma("unroll") for (int j = 0; j < 16; ++j) v[j] = wbuf[rr * 33 + c0 + j];                    \
-        __builtin_amdgcn_s_waitcnt(0xC07F); /* reads done before the next tile overwrites */            \
-        bwd_store16<MODE>(p, v, cw, m0 + wm * 128 + (MI) * 32 + rr, n0 + wn * 128 + (NI) * 32 + c0, row_end); \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
+        float2 vp[8];                                                                                    \
+        pair_f32(v, lane, vp);                                                                           \
+        if (n < p.N) {                                                                                   \
+            float2* dst = (float2*)(cw + (size_t)(mbase + rb0 + prow) * p.N + n);                        \
+            const uint32_t ld2 = (uint32_t)p.N / 2;                                                      \
+            _Pragma("unroll") for (int q = 0; q < 8; ++q)                                                \
+                if (rb0 + prow + 8 * (q >> 1) + 2 * (q & 1) < mlim)                                      \
+                    dst[(8 * (q >> 1) + 2 * (q & 1)) * ld2] = vp[q];                                     \
+        }                                                                                                \
+    }                                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);
+            GB_EPI_WG(0, 0) GB_EPI_WG(0, 1) GB_EPI_WG(0, 2) GB_EPI_WG(0, 3)
+            GB_EPI_WG(1, 0) GB_EPI_WG(1, 1) GB_EPI_WG(1, 2) GB_EPI_WG(1, 3)
+            GB_EPI_WG(2, 0) GB_EPI_WG(2, 1) GB_EPI_WG(2, 2) GB_EPI_WG(2, 3)
+            GB_EPI_WG(3, 0) GB_EPI_WG(3, 1) GB_EPI_WG(3, 2) GB_EPI_WG(3, 3)
+#undef GB_EPI_WG
+        } else if (MODE == kDgrad) {
+            const int rlim = row_end - mbase;
+            uint16_t* const cbase = p.C + (size_t)mbase * p.N;
+            const uint32_t ldw = (uint32_t)p.N / 2;
+#define GB_EPI_DG(MI, NI)                                                                                \
+    {                                                                                                    \
+        const int n = n0 + wn * 128 + (NI) * 32 + c2;                                                    \
+        const int rb0 = wm * 128 + (MI) * 32;                                                            \
+        float v[16];                                                                                     \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
+        uint32_t vp[8];                                                                                  \
+        pair_bf16(v, lane, vp);                                                                          \
+        if (n < p.N) {                                                                                   \
+            uint32_t* dst = (uint32_t*)(cbase + (uint32_t)((rb0 + prow) * p.N + n));                     \
+            _Pragma("unroll") for (int q = 0; q < 8; ++q)                                                \
+                if (rb0 + prow + 8 * (q >> 1) + 2 * (q & 1) < rlim)                                      \
+                    dst[(8 * (q >> 1) + 2 * (q & 1)) * ldw] = vp[q];                                     \
+        }                                                                                                \
+    }                                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);
+            GB_EPI_DG(0, 0) GB_EPI_DG(0, 1) GB_EPI_DG(0, 2) GB_EPI_DG(0, 3)
+            GB_EPI_DG(1, 0) GB_EPI_DG(1, 1) GB_EPI_DG(1, 2) GB_EPI_DG(1, 3)
+            GB_EPI_DG(2, 0) GB_EPI_DG(2, 1) GB_EPI_DG(2, 2) GB_EPI_DG(2, 3)
+            GB_EPI_DG(3, 0) GB_EPI_DG(3, 1) GB_EPI_DG(3, 2) GB_EPI_DG(3, 3)
+#undef GB_EPI_DG
+        } else {
+            // C = [dG | dU] with rows of 2N bf16; the stash holds [g | u] alike
+            const int rlim = row_end - mbase;
+            const uint32_t ldw = (uint32_t)p.N;  // words per 2N-wide row
+            uint32_t* const cbase = (uint32_t*)(p.C + (size_t)mbase * 2 * p.N);
+            const uint32_t* const sbase = (const uint32_t*)(p.stash + (size_t)mbase * 2 * p.N);
+            uint32_t gs[4][8], us[4][8];
+#define GB_LOAD_STASH(MI)                                                                                \
+    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) {                                                   \
+        const int n = min(n0 + wn * 128 + ni * 32 + c2, p.N - 2);                                        \
+        _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                                  \
+            const int r = min(wm * 128 + (MI) * 32 + prow + 8 * (q >> 1) + 2 * (q & 1), rlim - 1);       \
+            const uint32_t o = (uint32_t)r * ldw + (uint32_t)n / 2;                                      \
+            gs[ni][q] = sbase[o];                                                                        \
+            us[ni][q] = sbase[o + ldw / 2];                                                              \
+        }                                                                                                \
     }
-        GB_EPI(0, 0) GB_EPI(0, 1) GB_EPI(0, 2) GB_EPI(0, 3)
-        GB_EPI(1, 0) GB_EPI(1, 1) GB_EPI(1, 2) GB_EPI(1, 3)
-        GB_EPI(2, 0) GB_EPI(2, 1) GB_EPI(2, 2) GB_EPI(2, 3)
-        GB_EPI(3, 0) GB_EPI(3, 1) GB_EPI(3, 2) GB_EPI(3, 3)
-#undef GB_EPI
-        __syncthreads();  // LDS reused by the next tile's loads
+#define GB_EPI_SG(MI, NI)                                                                                \
+    {                                                                                                    \
+        const int n = n0 + wn * 128 + (NI) * 32 + c2;                                                    \
+        const int rb0 = wm * 128 + (MI) * 32;                                                            \
+        float v[16];                                                                                     \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
+        float2 dh[8];                                                                                    \
+        pair_f32(v, lane, dh);                                                                           \
+        if (n < p.N) {                                                                                   \
+            _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                              \
+                const int r = rb0 + prow + 8 * (q >> 1) + 2 * (q & 1);                                   \
+                float rg[2], ru[2];                                                                      \
+                const float dhv[2] = {dh[q].x, dh[q].y};                                                 \
+                _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                          \
+                    const float g = __uint_as_float(h ? (gs[NI][q] & 0xffff0000u) : (gs[NI][q] << 16));  \
+                    const float u = __uint_as_float(h ? (us[NI][q] & 0xffff0000u) : (us[NI][q] << 16));  \
+                    const float sg = sigmoid_fast(g);                                                    \
+                    rg[h] = dhv[h] * u * sg * (1.0f + g * (1.0f - sg));                                  \
+                    ru[h] = dhv[h] * g * sg;                                                             \
+                }                                                                                        \
+                if (r < rlim) {                                                                          \
+                    uint32_t* dst = cbase + (uint32_t)r * ldw + (uint32_t)n / 2;                          \
+                    dst[0] = pack_bf16x2(rg[0], rg[1]);                                                  \
+                    dst[ldw / 2] = pack_bf16x2(ru[0], ru[1]);                                            \
+                }                                                                                        \
+            }                                                                                            \
+        }                                                                                                \
+    }                                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);
+            GB_LOAD_STASH(0)
+            GB_EPI_SG(0, 0) GB_EPI_SG(0, 1) GB_EPI_SG(0, 2) GB_EPI_SG(0, 3)
+            GB_LOAD_STASH(1)
+            GB_EPI_SG(1, 0) GB_EPI_SG(1, 1) GB_EPI_SG(1, 2) GB_EPI_SG(1, 3)
+            GB_LOAD_STASH(2)
+            GB_EPI_SG(2, 0) GB_EPI_SG(2, 1) GB_EPI_SG(2, 2) GB_EPI_SG(2, 3)
+            GB_LOAD_STASH(3)
+            GB_EPI_SG(3, 0) GB_EPI_SG(3, 1) GB_EPI_SG(3, 2) GB_EPI_SG(3, 3)
+#undef GB_LOAD_STASH
+#undef GB_EPI_SG
+        }
     }
 }
 

