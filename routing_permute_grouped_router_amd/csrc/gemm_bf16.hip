@@ -17,7 +17,7 @@ namespace moe {
 namespace {
 
 // Tuned on MI355X with the Mixtral-shaped and fine-grained layers.
-constexpr int kSwizzle = 0, kGroupM = 4, kEarlyLoads = 1;
+constexpr int kSwizzle = 0, kGroupM = 4;
 
 int g_num_cus = 0;
 
@@ -49,7 +49,7 @@ hipError_t launch_swiglu_gemm_bf16(const moe_config& c, const uint16_t* xp, cons
     const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.F + 127) / 128);
     if (max_tiles == 0) return hipSuccess;
     gemm::Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash};
-    gemm::grouped_gemm_bf16<true, kSwizzle, kGroupM, kEarlyLoads>
+    gemm::grouped_gemm_bf16<true, kSwizzle, kGroupM>
         <<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -60,7 +60,7 @@ hipError_t launch_down_gemm_bf16(const moe_config& c, const uint16_t* h, const u
     const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.H + gemm::kTile - 1) / gemm::kTile);
     if (max_tiles == 0) return hipSuccess;
     gemm::Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr};
-    gemm::grouped_gemm_bf16<false, kSwizzle, kGroupM, kEarlyLoads>
+    gemm::grouped_gemm_bf16<false, kSwizzle, kGroupM>
         <<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
     return hipGetLastError();
 }

@@ -113,21 +113,56 @@ __device__ __forceinline__ void pair_f32(const float (&v)[16], int lane, float2 
     }
 }
 
-template <bool SWIGLU, int SWZ, int GM, int EARLY = 0>
+// One 16-byte MFMA operand fragment from LDS.  Issued as inline assembly so
+// the compiler neither reorders it nor makes it wait for the direct-to-LDS
+// loads into the other stage buffer (it cannot prove that they do not
+// alias); the kernel waits for its reads itself (lgkmcnt) before the
+// fragments are used.
+// Direct global-to-LDS copies.  Lane l copies 16 (or 4) bytes from
+// sbase + voff to LDS address lds + 16 l (4 l).  The LDS address is uniform and
+// goes through M0 with one scalar move; the global address is a uniform 64-bit
+// base plus a 32-bit lane offset.  Any vector arithmetic on the address path
+// (64-bit adds, readfirstlane into M0) would sit between the MFMAs of the
+// K loop and stall their issue; this form needs none.  Issued as inline
+// assembly: the kernel counts these loads itself (vmcnt).
+__device__ __forceinline__ void dma_lds16(uint32_t lds, uint32_t voff, const void* sbase) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                     : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds4(uint32_t lds, uint32_t voff, const void* sbase) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                     : "memory", "m0");
+}
+
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
+    uint4 v;
+    __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <bool SWIGLU, int SWZ, int GM>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     constexpr int BK = 64;                  // K depth of one stage
     constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
     constexpr int RPL = 64 / CH;            // rows per wave-wide load
     constexpr int LOADS = 64 / RPL;         // loads per wave per operand per stage
     constexpr int STAGE_ELEMS = kTile * BK; // one operand of one stage
+    // byte offsets of B fragments 1..3 from fragment 0: SwiGLU tiles hold
+    // gate rows 0..127 and up rows 128..255 (fragments 2, 3 are the up rows
+    // of fragments 0, 1); other tiles 32 consecutive rows per fragment
+    constexpr int B1 = 32 * BK * 2, B2 = (SWIGLU ? 128 : 64) * BK * 2, B3 = (SWIGLU ? 160 : 96) * BK * 2;
 
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][STAGE_ELEMS];
     __shared__ int32_t pre[kMaxExperts + 1];
+    __shared__ int32_t offs[kMaxExperts + 1];  // the group offsets, read once per block
+    __shared__ uint32_t pf_sink[64];           // landing slot of the L2 prefetches (never read)
     __shared__ int scan_tmp[kThreads / 64];
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
-    const int total_m = build_tile_prefix(p.offsets, p.E, kTile, pre, scan_tmp);
+    for (int e = tid; e <= p.E; e += kThreads) offs[e] = p.offsets[e];
+    const int total_m = build_tile_prefix(p.offsets, p.E, kTile, pre, scan_tmp);  // ends with a barrier
     const int cols_per_tile = SWIGLU ? kTile / 2 : kTile;
     const int n_tiles = (p.n_out + cols_per_tile - 1) / cols_per_tile;  // last N tile may be partial
     const int total = total_m * n_tiles;
@@ -140,22 +175,35 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     const int nk = K / BK;
     const int lrow = lane / CH, lslot = lane % CH;
 
-    // LDS rows of this lane's MFMA operands
-    int arow[4], brow[4];
+    // LDS byte address of this lane's first A and B fragment (stage 0, K
+    // chunk 0) and the byte offset of its chunk in each 16-deep K sub-step:
+    // lane l reads row l % 32 of each 32-row fragment at 16-byte chunk
+    // 2 kk + l / 32, stored at chunk position (2 kk + l / 32) ^ swz(row).
+    // Fragments start at multiples of 32 rows, so swz(row) depends only on l
+    // and, for the row ^ (row / 8) permutation, on the fragment's parity.
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0][0];
+    constexpr uint32_t kStageBytes = 2 * STAGE_ELEMS * 2;
+    // LDS rows this wave's loads fill: wid * 64 .. +63 of each operand
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(wid * 64 * BK * 2));
+    const uint32_t pf_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)pf_sink);
+    const uint32_t a_rd = lds_base + (uint32_t)((wm * 128 + (lane & 31)) * BK * 2);
+    const uint32_t b_rd = lds_base + (uint32_t)(STAGE_ELEMS * 2 + (SWIGLU ? wn * 64 : wn * 128) * BK * 2 +
+                                                (lane & 31) * BK * 2);
+    uint32_t koff[4][2];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) arow[mi] = wm * 128 + mi * 32 + (lane & 31);
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-        brow[ni] = SWIGLU ? (ni < 2 ? 0 : 128) + wn * 64 + (ni & 1) * 32 + (lane & 31)
-                          : wn * 128 + ni * 32 + (lane & 31);
-
+        for (int par = 0; par < 2; ++par)
+            koff[kk][par] = (uint32_t)(((2 * kk + (lane >> 5)) ^ swz<SWZ>(par * 32 + (lane & 31))) << 4);
     for (int t = t_begin + lb; t < t_end; t += per_xcd) {
         int mt, nt;
         tile_coords(t, total_m, n_tiles, GM, &mt, &nt);
-        const int e = find_expert(pre, p.E, mt);
-        const int row_end = min(p.offsets[e + 1], p.rows);
-        const int row0 = p.offsets[e] + (mt - pre[e]) * kTile;
+        const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, p.E, mt));
+        const int row_end = __builtin_amdgcn_readfirstlane(min(offs[e + 1], p.rows));
+        const int row0 = __builtin_amdgcn_readfirstlane(offs[e] + (mt - pre[e]) * kTile);
         if (row0 < 0 || row0 >= row_end) continue;  // only for inconsistent offsets
+        // first B row of the tile (SwiGLU: first gate row; the up rows are F rows further)
+        const int brow0 = SWIGLU ? nt * 128 : nt * kTile;
 
         // Per-lane byte offsets of the A and B loads (K offset 0) against the
         // uniform bases: 32-bit, so the loads take few registers.
@@ -173,10 +221,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             } else {
                 br = min(nt * kTile + r, p.n_out - 1);
             }
-            boff[i] = (uint32_t)(((size_t)br * K + chunk * 8) * 2);
+            boff[i] = (uint32_t)(((size_t)(br - brow0) * K + chunk * 8) * 2);
         }
         const char* abase = (const char*)(p.A + (size_t)row0 * K);  // A offsets are tile-relative
-        const char* bbase = (const char*)(p.B + (size_t)e * p.b_rows * K);
+        const char* bbase = (const char*)(p.B + ((size_t)e * p.b_rows + brow0) * K);  // tile-relative too
+        // L2 prefetch: lane l of wave w touches the K segment of a stage in
+        // tile row w * 64 + l of A and of B (the rows this wave loads).
+        uint32_t apf, bpf;
+        {
+            const int r = wid * 64 + lane;
+            apf = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K * 2);
+            int br;
+            if (SWIGLU) {
+                const int f = min(nt * 128 + (r & 127), p.n_out - 1);
+                br = r < 128 ? f : p.n_out + f;
+            } else {
+                br = min(nt * kTile + r, p.n_out - 1);
+            }
+            bpf = (uint32_t)((size_t)(br - brow0) * K * 2);
+        }
 
         f32x16 acc[4][4];
 #pragma unroll
@@ -187,85 +250,170 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
 #define GG_LOAD_A(kt, stage, i)                                                                          \
-    __builtin_amdgcn_global_load_lds((glb_void*)(abase + aoff[i] + (size_t)(kt) * (BK * 2)),              \
-                                     (lds_void*)&lds[stage][0][(wid * 64 + (i) * RPL) * BK], 16, 0, 0)
+    dma_lds16(lds_wave + (uint32_t)(stage) * kStageBytes + (i) * RPL * BK * 2, aoff[i], abase + (size_t)(kt) * (BK * 2))
 #define GG_LOAD_B(kt, stage, i)                                                                          \
-    __builtin_amdgcn_global_load_lds((glb_void*)(bbase + boff[i] + (size_t)(kt) * (BK * 2)),              \
-                                     (lds_void*)&lds[stage][1][(wid * 64 + (i) * RPL) * BK], 16, 0, 0)
-#define GG_READ(stage, kk, FA, FB)                                                                       \
-    {                                                                                                    \
-        const int c_ = (kk) * 2 + (lane >> 5);                                                            \
-        _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) FA[mi] = __builtin_bit_cast(                    \
-            bf16x8, *(const uint4*)(&lds[stage][0][arow[mi] * BK + ((c_ ^ swz<SWZ>(arow[mi])) << 3)]));    \
-        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) FB[ni] = __builtin_bit_cast(                    \
-            bf16x8, *(const uint4*)(&lds[stage][1][brow[ni] * BK + ((c_ ^ swz<SWZ>(brow[ni])) << 3)]));    \
-    }
-#define GG_MFMAS(FA, FB)                                                                                 \
-    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)    \
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0);
+    dma_lds16(lds_wave + (uint32_t)(stage) * kStageBytes + STAGE_ELEMS * 2 + (i) * RPL * BK * 2, boff[i],         \
+              bbase + (size_t)(kt) * (BK * 2))
 #define GG_ISSUE(kt, stage)                                                                              \
     _Pragma("unroll") for (int i = 0; i < LOADS; ++i) {                                                  \
         GG_LOAD_A(kt, stage, i);                                                                         \
         GG_LOAD_B(kt, stage, i);                                                                         \
     }
+// Pull the 128-byte K segment of stage kt of this wave's 64 A rows (B rows)
+// into L2: 4 bytes per lane, one row per lane, into a sink slot of LDS that
+// nothing reads.  The loads of that stage, issued a stage and a half later,
+// then hit in L2.
+#define GG_PREFETCH_A(kt) dma_lds4(pf_lds, apf, abase + (size_t)(kt) * (BK * 2))
+#define GG_PREFETCH_B(kt) dma_lds4(pf_lds, bpf, bbase + (size_t)(kt) * (BK * 2))
+// Wait until every LDS read issued so far has landed; the fragment registers
+// are tied to the wait so no MFMA that uses them moves above it.
+#define GG_WAIT_FRAGS(FA, FB)                                                                            \
+    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
+                     : "+v"(FA[0]), "+v"(FA[1]), "+v"(FA[2]), "+v"(FA[3]), "+v"(FB[0]), "+v"(FB[1]),     \
+                       "+v"(FB[2]), "+v"(FB[3])::"memory")
+#define GG_MFMA(FA, FB, mi, ni)                                                                          \
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0)
+// The 8 fragments of one K sub-step: A fragment mi at mi * 32 rows, B
+// fragment ni at B1..B3 bytes past fragment 0; AD/BD[par] are the lane's
+// addresses for fragments of parity par (the chunk permutation differs).
+#define GG_RD_A(GA, AD, mi) GA[mi] = lds_frag<(mi) * 32 * BK * 2>(AD[(mi) & 1])
+#define GG_RD_B(GB, BD, ni) GB[ni] = lds_frag<(ni) == 0 ? 0 : (ni) == 1 ? B1 : (ni) == 2 ? B2 : B3>(BD[(ni) & 1])
+#define GG_SB __builtin_amdgcn_sched_barrier(0)
+// One MFMA of a K sub-step, preceded by PRE (a load of a later stage, or
+// nothing) and followed by RD (one fragment read of the next sub-step, or
+// nothing); sched_barrier pins the order, so the matrix core has its next
+// MFMA ready while the loads and reads are in flight.
+#define GG_STEP(FA, FB, mi, ni, PRE, RD)                                                                 \
+    PRE;                                                                                                 \
+    GG_MFMA(FA, FB, mi, ni);                                                                             \
+    RD;                                                                                                  \
+    GG_SB;
+// One K sub-step: 16 MFMAs on FA/FB; the 8 fragment reads of the next
+// sub-step into GA/GB (addresses AD/BD) follow the first 8 of them, and
+// L0..L7 (loads of a later stage, or nothing) precede every other MFMA: one
+// 1 KiB load per two MFMAs per wave is what the CU's address unit sustains
+// (about one such load per 16 cycles for the four wavefronts together).
+#define GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, L0, L1, L2, L3, L4, L5, L6, L7)                             \
+    GG_WAIT_FRAGS(FA, FB);                                                                               \
+    GG_SB;                                                                                               \
+    GG_STEP(FA, FB, 0, 0, L0, GG_RD_A(GA, AD, 0))                                                        \
+    GG_STEP(FA, FB, 0, 1, (void)0, GG_RD_A(GA, AD, 1))                                                   \
+    GG_STEP(FA, FB, 0, 2, L1, GG_RD_A(GA, AD, 2))                                                        \
+    GG_STEP(FA, FB, 0, 3, (void)0, GG_RD_A(GA, AD, 3))                                                   \
+    GG_STEP(FA, FB, 1, 0, L2, GG_RD_B(GB, BD, 0))                                                        \
+    GG_STEP(FA, FB, 1, 1, (void)0, GG_RD_B(GB, BD, 1))                                                   \
+    GG_STEP(FA, FB, 1, 2, L3, GG_RD_B(GB, BD, 2))                                                        \
+    GG_STEP(FA, FB, 1, 3, (void)0, GG_RD_B(GB, BD, 3))                                                   \
+    GG_STEP(FA, FB, 2, 0, L4, (void)0)                                                                   \
+    GG_STEP(FA, FB, 2, 1, (void)0, (void)0)                                                              \
+    GG_STEP(FA, FB, 2, 2, L5, (void)0)                                                                   \
+    GG_STEP(FA, FB, 2, 3, (void)0, (void)0)                                                              \
+    GG_STEP(FA, FB, 3, 0, L6, (void)0)                                                                   \
+    GG_STEP(FA, FB, 3, 1, (void)0, (void)0)                                                              \
+    GG_STEP(FA, FB, 3, 2, L7, (void)0)                                                                   \
+    GG_STEP(FA, FB, 3, 3, (void)0, (void)0)
+#define GG_N_ (void)0
+#define GG_SUBSTEP(FA, FB, GA, GB, AD, BD)                                                               \
+    GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_)
+// ... with the 8 A (B) loads of stage LKT into stage buffer LST
+#define GG_SUBSTEP_LA(FA, FB, GA, GB, AD, BD, LKT, LST)                                                  \
+    GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_LOAD_A(LKT, LST, 0), GG_LOAD_A(LKT, LST, 1),                 \
+                 GG_LOAD_A(LKT, LST, 2), GG_LOAD_A(LKT, LST, 3), GG_LOAD_A(LKT, LST, 4),                 \
+                 GG_LOAD_A(LKT, LST, 5), GG_LOAD_A(LKT, LST, 6), GG_LOAD_A(LKT, LST, 7))
+#define GG_SUBSTEP_LB(FA, FB, GA, GB, AD, BD, LKT, LST)                                                  \
+    GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_LOAD_B(LKT, LST, 0), GG_LOAD_B(LKT, LST, 1),                 \
+                 GG_LOAD_B(LKT, LST, 2), GG_LOAD_B(LKT, LST, 3), GG_LOAD_B(LKT, LST, 4),                 \
+                 GG_LOAD_B(LKT, LST, 5), GG_LOAD_B(LKT, LST, 6), GG_LOAD_B(LKT, LST, 7))
+// ... with the L2 prefetch of stage PKT
+#define GG_SUBSTEP_PF(FA, FB, GA, GB, AD, BD, PKT)                                                       \
+    GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_PREFETCH_A(PKT), GG_PREFETCH_B(PKT), GG_N_, GG_N_, GG_N_,    \
+                 GG_N_, GG_N_, GG_N_)
 
-        // Two LDS stages.  Within a stage the four 16-deep K sub-steps alternate
-        // two fragment register sets, so the LDS reads of sub-step j+1 and a
-        // quarter of the next stage's global loads are in flight while the
-        // 16 MFMAs of sub-step j run.
+        // Two LDS stages, software-pipelined across the stage boundary.  A stage
+        // is four 16-deep K sub-steps of 16 MFMAs each; the fragments of
+        // sub-step j+1 are read from LDS while the MFMAs of sub-step j issue.
+        // The one barrier per stage sits before the last sub-step: by then
+        // this wave has read all of stage kt and its loads of stage kt+1 have
+        // landed; once every wave is past it the buffer of stage kt is free.
+        // The loads of stage kt+2 go into it, the A half during the last
+        // sub-step of stage kt and the B half during the first sub-step of
+        // stage kt+1 (so the address unit is never oversubscribed), and the
+        // L2 prefetch of stage kt+3 rides on the second sub-step.  Loads past
+        // the end of K repeat the last stage into the free buffer, so the loop
+        // has no branch; a wave's loads complete in issue order, so they land
+        // before the next tile's loads of the same rows.
         bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous tile's stores retired
+        GG_SB;
+        GG_ISSUE(0, 0);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            GG_LOAD_A(0, 0, i);
-            GG_LOAD_B(0, 0, i);
+        for (int i = 0; i < LOADS; ++i) GG_LOAD_A(min(1, nk - 1), 1, i);
+        GG_PREFETCH_A(min(2, nk - 1));
+        GG_PREFETCH_B(min(2, nk - 1));
+        __asm__ volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");  // stage 0 landed everywhere
+        GG_SB;
+        {
+            const uint32_t ad[2] = {a_rd + koff[0][0], a_rd + koff[0][1]};
+            const uint32_t bd[2] = {b_rd + koff[0][0], b_rd + koff[0][1]};
+            GG_RD_A(fa0, ad, 0);
+            GG_RD_A(fa0, ad, 1);
+            GG_RD_A(fa0, ad, 2);
+            GG_RD_A(fa0, ad, 3);
+            GG_RD_B(fb0, bd, 0);
+            GG_RD_B(fb0, bd, 1);
+            GG_RD_B(fb0, bd, 2);
+            GG_RD_B(fb0, bd, 3);
         }
-        __syncthreads();
-        GG_READ(0, 0, fa0, fb0);
         for (int kt = 0; kt < nk; ++kt) {
             const int st = kt & 1;
-            const bool more = kt + 1 < nk;
-            GG_READ(st, 1, fa1, fb1);
-            if (more) {
-#pragma unroll
-                for (int i = 0; i < LOADS / 2; ++i) GG_LOAD_A(kt + 1, st ^ 1, i);
-                if (EARLY) {
-#pragma unroll
-                    for (int i = 0; i < LOADS / 2; ++i) GG_LOAD_B(kt + 1, st ^ 1, i);
-                }
+            const uint32_t so = (uint32_t)st * kStageBytes;
+            GG_SB;
+            {
+                const uint32_t ad[2] = {a_rd + so + koff[1][0], a_rd + so + koff[1][1]};
+                const uint32_t bd[2] = {b_rd + so + koff[1][0], b_rd + so + koff[1][1]};
+                GG_SUBSTEP_LB(fa0, fb0, fa1, fb1, ad, bd, min(kt + 1, nk - 1), st ^ 1)
             }
-            GG_MFMAS(fa0, fb0);
-            GG_READ(st, 2, fa0, fb0);
-            if (more) {
-#pragma unroll
-                for (int i = LOADS / 2; i < LOADS; ++i) GG_LOAD_A(kt + 1, st ^ 1, i);
-                if (EARLY) {
-#pragma unroll
-                    for (int i = LOADS / 2; i < LOADS; ++i) GG_LOAD_B(kt + 1, st ^ 1, i);
-                }
+            {
+                const uint32_t ad[2] = {a_rd + so + koff[2][0], a_rd + so + koff[2][1]};
+                const uint32_t bd[2] = {b_rd + so + koff[2][0], b_rd + so + koff[2][1]};
+                GG_SUBSTEP_PF(fa1, fb1, fa0, fb0, ad, bd, min(kt + 3, nk - 1))
             }
-            GG_MFMAS(fa1, fb1);
-            GG_READ(st, 3, fa1, fb1);
-            if (more && !EARLY) {
-#pragma unroll
-                for (int i = 0; i < LOADS / 2; ++i) GG_LOAD_B(kt + 1, st ^ 1, i);
+            {
+                const uint32_t ad[2] = {a_rd + so + koff[3][0], a_rd + so + koff[3][1]};
+                const uint32_t bd[2] = {b_rd + so + koff[3][0], b_rd + so + koff[3][1]};
+                GG_SUBSTEP(fa0, fb0, fa1, fb1, ad, bd)
             }
-            GG_MFMAS(fa0, fb0);
-            if (more && !EARLY) {
-#pragma unroll
-                for (int i = LOADS / 2; i < LOADS; ++i) GG_LOAD_B(kt + 1, st ^ 1, i);
-            }
-            GG_MFMAS(fa1, fb1);
-            if (more) {
-                __syncthreads();  // next stage landed (vmcnt 0); this stage fully read by every wave
-                GG_READ(st ^ 1, 0, fa0, fb0);
+            // this wave has read all of stage kt and its loads of stage kt+1
+            // landed (only the two prefetches may still be in flight); past
+            // the barrier, the same holds for every wave
+            __asm__ volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            GG_SB;
+            {
+                const uint32_t nso = so ^ kStageBytes;
+                const uint32_t ad[2] = {a_rd + nso + koff[0][0], a_rd + nso + koff[0][1]};
+                const uint32_t bd[2] = {b_rd + nso + koff[0][0], b_rd + nso + koff[0][1]};
+                GG_SUBSTEP_LA(fa1, fb1, fa0, fb0, ad, bd, min(kt + 2, nk - 1), st)
             }
         }
+        GG_SB;
 #undef GG_LOAD_A
 #undef GG_LOAD_B
-#undef GG_READ
-#undef GG_MFMAS
 #undef GG_ISSUE
-        __syncthreads();  // every wave done with both stages before the next tile's loads
+#undef GG_PREFETCH_A
+#undef GG_PREFETCH_B
+#undef GG_WAIT_FRAGS
+#undef GG_MFMA
+#undef GG_RD_A
+#undef GG_RD_B
+#undef GG_SB
+#undef GG_STEP
+#undef GG_SUBSTEP_X
+#undef GG_N_
+#undef GG_SUBSTEP
+#undef GG_SUBSTEP_LA
+#undef GG_SUBSTEP_LB
+#undef GG_SUBSTEP_PF
+
 
         // Epilogue straight from the accumulators: each 32 x 32 tile becomes 8
         // bf16 pairs per lane (two adjacent columns of one row, one DPP lane
