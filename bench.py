@@ -207,11 +207,11 @@ def main():
                         buf["src_map"], buf["ws"], x_scale=g.get("x_scale"), xp_scale=buf.get("xp_scale"),
                         err=buf["err"])
         ev[2].record(stream)
-        moe.moe_grouped_swiglu_gemm(cfg, buf["xp"], w1, buf["offsets"], buf["h"], xp_scale=buf.get("xp_scale"),
+        moe.moe_grouped_swiglu_gemm(cfg, buf["xp"], w1, buf["offsets"], buf["h"], buf["ws"], xp_scale=buf.get("xp_scale"),
                                     w1_scale=g.get("w1_scale"), h_scale=buf.get("h_scale"),
                                     gu_stash=buf.get("gu_stash"))
         ev[3].record(stream)
-        moe.moe_grouped_down_gemm(cfg, buf["h"], w2, buf["offsets"], buf["yp"], h_scale=buf.get("h_scale"),
+        moe.moe_grouped_down_gemm(cfg, buf["h"], w2, buf["offsets"], buf["yp"], buf["ws"], h_scale=buf.get("h_scale"),
                                   w2_scale=g.get("w2_scale"))
         ev[4].record(stream)
         moe.moe_combine(cfg, buf["yp"], buf["row_map"], buf["w"], buf["y"])

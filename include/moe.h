@@ -102,8 +102,10 @@ typedef struct moe_config {
 /* Rows of the permuted buffers: T*k + E*(align-1).  Host only. */
 int64_t moe_rows_capacity(const moe_config* cfg);
 
-/* Bytes of scratch moe_permute and moe_forward need for this config (0 is
- * possible).  Host only; no device access. */
+/* Bytes of scratch moe_permute, the grouped GEMMs and moe_forward need for
+ * this config (0 is possible; for bf16 storage about 64 MiB: the GEMMs'
+ * work-queue counters and the float32 partial sums of tiles cut along K).
+ * Host only; no device access. */
 size_t moe_workspace_size(const moe_config* cfg);
 
 /* Bytes of scratch moe_grouped_down_bwd, moe_grouped_swiglu_bwd and
@@ -149,17 +151,21 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const uint8_t* x_sc
  * Group sizes are read from `offsets` on the device; empty experts cost no
  * tiles.  gu_stash (optional, [R_cap,2F] in the output dtype) receives g in
  * columns [0,F) and u in [F,2F) for the backward ([CUDNN] fc1 stash).
- * xp_scale / w1_scale / h_scale: MXFP8 only, NULL otherwise. */
+ * xp_scale / w1_scale / h_scale: MXFP8 only, NULL otherwise.
+ * ws: moe_workspace_size(cfg) bytes (the same scratch moe_permute takes; the
+ * bf16 GEMMs keep their work-queue counters and the partial sums of tiles cut
+ * along K there, so calls sharing one workspace must not overlap). */
 moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const uint8_t* xp_scale, const void* w1,
                                    const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
-                                   void* gu_stash, void* stream);
+                                   void* gu_stash, void* ws, size_t ws_bytes, void* stream);
 
 /* Step 4, grouped down GEMM ([BLOCK] down projection).  For every expert e
  * and row r in [offsets[e], offsets[e+1]):
  *   Yp[r][o] = h[r] . w2[e][o][:]   (float32 sum, stored in the output dtype).
- * h_scale / w2_scale: MXFP8 only. */
+ * h_scale / w2_scale: MXFP8 only.  ws: as for moe_grouped_swiglu_gemm. */
 moe_status moe_grouped_down_gemm(const moe_config* cfg, const void* h, const uint8_t* h_scale, const void* w2,
-                                 const uint8_t* w2_scale, const int32_t* offsets, void* yp, void* stream);
+                                 const uint8_t* w2_scale, const int32_t* offsets, void* yp, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* Step 5, top-k weighted combine ([CUDNN] per-top-k combine; [TE-EP] expert
  * outputs summed across the top-k).

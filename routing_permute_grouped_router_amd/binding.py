@@ -97,8 +97,8 @@ _SIGS = {
     "moe_backward_workspace_size": (ctypes.c_size_t, [CFG]),
     "moe_route": (ctypes.c_int, [CFG, P, P, P, P]),
     "moe_permute": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
-    "moe_grouped_swiglu_gemm": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P]),
-    "moe_grouped_down_gemm": (ctypes.c_int, [CFG, P, P, P, P, P, P, P]),
+    "moe_grouped_swiglu_gemm": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+    "moe_grouped_down_gemm": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_combine": (ctypes.c_int, [CFG, P, P, P, P, P]),
     "moe_forward": (ctypes.c_int, [CFG] + [P] * 22 + [ctypes.c_size_t, P]),
     "moe_combine_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P]),
@@ -214,10 +214,11 @@ def moe_permute(cfg: MoEConfig, x, idx, xp, counts, offsets, row_map, src_map, w
         _ptr(err, "err", torch.int32, (1,), optional=True), wp, wb, _stream(stream)))
 
 
-def moe_grouped_swiglu_gemm(cfg: MoEConfig, xp, w1, offsets, h, xp_scale=None, w1_scale=None, h_scale=None,
+def moe_grouped_swiglu_gemm(cfg: MoEConfig, xp, w1, offsets, h, ws, xp_scale=None, w1_scale=None, h_scale=None,
                             gu_stash=None, stream=None):
     c = cfg.c()
     mx = cfg.dtype == "mxfp8"
+    wp, wb = _ws(ws)
     _check(load_library().moe_grouped_swiglu_gemm(
         ctypes.byref(c), _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.H)),
         _ptr(xp_scale, "xp_scale", torch.uint8, (cfg.R_cap, cfg.H // 32), optional=not mx),
@@ -225,19 +226,21 @@ def moe_grouped_swiglu_gemm(cfg: MoEConfig, xp, w1, offsets, h, xp_scale=None, w
         _ptr(w1_scale, "w1_scale", torch.uint8, (cfg.E, 2 * cfg.F, cfg.H // 32), optional=not mx),
         _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
         _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx),
-        _ptr(gu_stash, "gu_stash", cfg.out_dtype, (cfg.R_cap, 2 * cfg.F), optional=True), _stream(stream)))
+        _ptr(gu_stash, "gu_stash", cfg.out_dtype, (cfg.R_cap, 2 * cfg.F), optional=True), wp, wb,
+        _stream(stream)))
 
 
-def moe_grouped_down_gemm(cfg: MoEConfig, h, w2, offsets, yp, h_scale=None, w2_scale=None, stream=None):
+def moe_grouped_down_gemm(cfg: MoEConfig, h, w2, offsets, yp, ws, h_scale=None, w2_scale=None, stream=None):
     c = cfg.c()
     mx = cfg.dtype == "mxfp8"
+    wp, wb = _ws(ws)
     _check(load_library().moe_grouped_down_gemm(
         ctypes.byref(c), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
         _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx),
         _ptr(w2, "w2", cfg.store_dtype, (cfg.E, cfg.H, cfg.F)),
         _ptr(w2_scale, "w2_scale", torch.uint8, (cfg.E, cfg.H, cfg.F // 32), optional=not mx),
         _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(yp, "yp", cfg.out_dtype, (cfg.R_cap, cfg.H)),
-        _stream(stream)))
+        wp, wb, _stream(stream)))
 
 
 def moe_combine(cfg: MoEConfig, yp, row_map, w, y, stream=None):

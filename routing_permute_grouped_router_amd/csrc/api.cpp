@@ -82,6 +82,12 @@ hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Forward workspace: the grouping's per-chunk counts, then the GEMMs' region
+// (work-queue counters and split-tile partial sums; used in stream order by
+// the gate/up GEMM and then the down GEMM).
+size_t group_ws_bytes(const moe_config& c) { return round256((size_t)group_n_chunks(c.T, c.E) * c.E * sizeof(int32_t)); }
+void* gemm_ws(const moe_config& c, void* ws) { return (char*)ws + group_ws_bytes(c); }
+
 }  // namespace
 
 extern "C" {
@@ -94,7 +100,7 @@ int64_t moe_rows_capacity(const moe_config* cfg) {
 size_t moe_workspace_size(const moe_config* cfg) {
     if (check_config(cfg) != MOE_OK) return 0;
     const moe_config& c = *cfg;
-    return round256((size_t)group_n_chunks(c.T, c.E) * c.E * sizeof(int32_t));
+    return group_ws_bytes(c) + round256(gemm_bf16_ws_bytes(c));
 }
 
 size_t moe_backward_workspace_size(const moe_config* cfg) {
@@ -142,7 +148,7 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const uint8_t* x_sc
 
 moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const uint8_t* xp_scale, const void* w1,
                                    const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
-                                   void* gu_stash, void* stream) {
+                                   void* gu_stash, void* ws, size_t ws_bytes, void* stream) {
     moe_status st = check_config(cfg);
     if (st) return st;
     const moe_config& c = *cfg;
@@ -152,11 +158,12 @@ moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const 
     REQUIRE(w1);
     REQUIRE(offsets);
     REQUIRE(h);
+    if ((st = check_ws(c, ws, ws_bytes))) return st;
     hipStream_t s = as_stream(stream);
     switch (c.dtype) {
     case MOE_BF16:
         return hip_status(launch_swiglu_gemm_bf16(c, (const uint16_t*)xp, (const uint16_t*)w1, offsets, (uint16_t*)h,
-                                                  (uint16_t*)gu_stash, s),
+                                                  (uint16_t*)gu_stash, gemm_ws(c, ws), s),
                           "moe_grouped_swiglu_gemm");
     case MOE_F32:
         return hip_status(
@@ -173,7 +180,8 @@ moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const 
 }
 
 moe_status moe_grouped_down_gemm(const moe_config* cfg, const void* h, const uint8_t* h_scale, const void* w2,
-                                 const uint8_t* w2_scale, const int32_t* offsets, void* yp, void* stream) {
+                                 const uint8_t* w2_scale, const int32_t* offsets, void* yp, void* ws, size_t ws_bytes,
+                                 void* stream) {
     moe_status st = check_config(cfg);
     if (st) return st;
     const moe_config& c = *cfg;
@@ -183,11 +191,12 @@ moe_status moe_grouped_down_gemm(const moe_config* cfg, const void* h, const uin
     REQUIRE(w2);
     REQUIRE(offsets);
     REQUIRE(yp);
+    if ((st = check_ws(c, ws, ws_bytes))) return st;
     hipStream_t s = as_stream(stream);
     switch (c.dtype) {
     case MOE_BF16:
         return hip_status(
-            launch_down_gemm_bf16(c, (const uint16_t*)h, (const uint16_t*)w2, offsets, (uint16_t*)yp, s),
+            launch_down_gemm_bf16(c, (const uint16_t*)h, (const uint16_t*)w2, offsets, (uint16_t*)yp, gemm_ws(c, ws), s),
             "moe_grouped_down_gemm");
     case MOE_F32:
         return hip_status(launch_down_gemm_f32(c, (const float*)h, (const float*)w2, offsets, (float*)yp, s),
@@ -234,9 +243,10 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
     if ((st = moe_permute(cfg, x, x_scale, idx, xp, xp_scale, counts, offsets, row_map, src_map, err, ws, ws_bytes,
                           stream)))
         return st;
-    if ((st = moe_grouped_swiglu_gemm(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, gu_stash, stream)))
+    if ((st = moe_grouped_swiglu_gemm(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, gu_stash, ws, ws_bytes,
+                                      stream)))
         return st;
-    if ((st = moe_grouped_down_gemm(cfg, h, h_scale, w2, w2_scale, offsets, yp, stream))) return st;
+    if ((st = moe_grouped_down_gemm(cfg, h, h_scale, w2, w2_scale, offsets, yp, ws, ws_bytes, stream))) return st;
     return moe_combine(cfg, yp, row_map, w, y, stream);
 }
 

@@ -43,26 +43,111 @@ int gemm_persistent_grid(int64_t max_tiles) {
     return (int)std::min<int64_t>(g, std::max<int64_t>(need, gemm::kXcds));
 }
 
-hipError_t launch_swiglu_gemm_bf16(const moe_config& c, const uint16_t* xp, const uint16_t* w1,
-                                   const int32_t* offsets, uint16_t* h, uint16_t* stash, hipStream_t s) {
-    const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
-    const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.F + 127) / 128);
-    if (max_tiles == 0) return hipSuccess;
-    gemm::Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash};
-    gemm::grouped_gemm_bf16<true, kSwizzle, kGroupM>
-        <<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+size_t gemm_bf16_ws_bytes(const moe_config& c) {
+    if (c.dtype != MOE_BF16) return 0;
+    return 256 + (size_t)gemm::kXcds * gemm::kSlotsPerXcd * gemm::kTile * gemm::kTile * sizeof(float);
+}
+
+namespace {
+
+// Zeroes the work-queue counters (a kernel rather than a memset node, so the
+// calls stay safe to capture in a graph).
+__global__ void zero_sched_kernel(int* sched) {
+    if (threadIdx.x < gemm::kXcds) sched[threadIdx.x] = 0;
+}
+
+// Split tile j of XCD blockIdx.y (j = blockIdx.x): the float32 partial sums
+// of its S K-parts are added in part order, then the epilogue of the grouped
+// GEMM is applied (SwiGLU: h = silu(g) * u rounded to bf16, plus the g | u
+// stash; down: rounding to bf16).  The queue layout is recomputed from the
+// same offsets and block count as the GEMM launch.
+template <bool SWIGLU, int GM>
+__global__ __launch_bounds__(256) void split_reduce_bf16(gemm::Args p, int nb) {
+    __shared__ int32_t pre[kMaxExperts + 1];
+    __shared__ int scan_tmp[256 / 64];
+    const int x = blockIdx.y, j = blockIdx.x;
+    const int nk = p.K / 64;
+    const int total_m = build_tile_prefix(p.offsets, p.E, gemm::kTile, pre, scan_tmp);
+    const int cols_per_tile = SWIGLU ? gemm::kTile / 2 : gemm::kTile;
+    const int n_tiles = (p.n_out + cols_per_tile - 1) / cols_per_tile;
+    const gemm::Queue q = gemm::xcd_queue(total_m * n_tiles, x, nb, nk);
+    if (q.S < 2 || j >= (q.units - q.whole) / q.S) return;
+    int mt, nt;
+    tile_coords(q.tb + q.whole + j, total_m, n_tiles, GM, &mt, &nt);
+    const int e = find_expert(pre, p.E, mt);
+    const int row_end = min(p.offsets[e + 1], p.rows);
+    const int row0 = p.offsets[e] + (mt - pre[e]) * gemm::kTile;
+    if (row0 < 0 || row0 >= row_end) return;
+    const int rows = min(gemm::kTile, row_end - row0);
+    constexpr int kPart = gemm::kTile * gemm::kTile;
+    const float* part = p.part + (size_t)(x * gemm::kSlotsPerXcd + j * q.S) * kPart;
+    if (SWIGLU) {
+        // 128 gate columns (partial columns 0..127) and their up columns (128..255)
+        for (int i = threadIdx.x; i < rows * 32; i += blockDim.x) {
+            const int r = i >> 5, c = (i & 31) * 4;
+            const int f = nt * 128 + c;
+            if (f >= p.n_out) continue;
+            float4 g = *(const float4*)(part + r * gemm::kTile + c);
+            float4 u = *(const float4*)(part + r * gemm::kTile + 128 + c);
+            for (int s = 1; s < q.S; ++s) {
+                const float4 g2 = *(const float4*)(part + (size_t)s * kPart + r * gemm::kTile + c);
+                const float4 u2 = *(const float4*)(part + (size_t)s * kPart + r * gemm::kTile + 128 + c);
+                g.x += g2.x; g.y += g2.y; g.z += g2.z; g.w += g2.w;
+                u.x += u2.x; u.y += u2.y; u.z += u2.z; u.w += u2.w;
+            }
+            const size_t row = (size_t)(row0 + r);
+            *(uint2*)(p.C + row * p.n_out + f) = make_uint2(pack_bf16x2(silu(g.x) * u.x, silu(g.y) * u.y),
+                                                            pack_bf16x2(silu(g.z) * u.z, silu(g.w) * u.w));
+            if (p.stash) {
+                *(uint2*)(p.stash + row * 2 * p.n_out + f) = make_uint2(pack_bf16x2(g.x, g.y), pack_bf16x2(g.z, g.w));
+                *(uint2*)(p.stash + row * 2 * p.n_out + p.n_out + f) =
+                    make_uint2(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w));
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < rows * 64; i += blockDim.x) {
+            const int r = i >> 6, c = (i & 63) * 4;
+            const int n = nt * gemm::kTile + c;
+            if (n >= p.n_out) continue;
+            float4 v = *(const float4*)(part + r * gemm::kTile + c);
+            for (int s = 1; s < q.S; ++s) {
+                const float4 v2 = *(const float4*)(part + (size_t)s * kPart + r * gemm::kTile + c);
+                v.x += v2.x; v.y += v2.y; v.z += v2.z; v.w += v2.w;
+            }
+            *(uint2*)(p.C + (size_t)(row0 + r) * p.n_out + n) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        }
+    }
+}
+
+template <bool SWIGLU>
+hipError_t launch_bf16(gemm::Args a, int64_t max_tiles, void* ws, hipStream_t s) {
+    const int grid = gemm_persistent_grid(max_tiles);
+    a.sched = (int*)ws;
+    a.part = (float*)((char*)ws + 256);
+    zero_sched_kernel<<<1, 64, 0, s>>>(a.sched);
+    gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM><<<grid, gemm::kThreads, 0, s>>>(a);
+    split_reduce_bf16<SWIGLU, kGroupM><<<dim3(gemm::kSlotsPerXcd, gemm::kXcds), 256, 0, s>>>(a, grid / gemm::kXcds);
     return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_swiglu_gemm_bf16(const moe_config& c, const uint16_t* xp, const uint16_t* w1,
+                                   const int32_t* offsets, uint16_t* h, uint16_t* stash, void* ws, hipStream_t s) {
+    const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
+    const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.F + 127) / 128);
+    if (max_tiles == 0) return hipSuccess;
+    gemm::Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash, nullptr, nullptr};
+    return launch_bf16<true>(a, max_tiles, ws, s);
+}
+
 hipError_t launch_down_gemm_bf16(const moe_config& c, const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
-                                 uint16_t* yp, hipStream_t s) {
+                                 uint16_t* yp, void* ws, hipStream_t s) {
     const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.H + gemm::kTile - 1) / gemm::kTile);
     if (max_tiles == 0) return hipSuccess;
-    gemm::Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr};
-    gemm::grouped_gemm_bf16<false, kSwizzle, kGroupM>
-        <<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
-    return hipGetLastError();
+    gemm::Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr, nullptr, nullptr};
+    return launch_bf16<false>(a, max_tiles, ws, s);
 }
 
 }  // namespace moe

@@ -52,7 +52,56 @@ struct Args {
     int b_rows;             // rows of B per expert (2F or H)
     uint16_t* C;            // [rows, n_out]
     uint16_t* stash;        // SwiGLU only: [rows, 2F] or null
+    int* sched;             // [kXcds] work-queue counters, zero at launch
+    float* part;            // [kXcds * kSlotsPerXcd][kTile][kTile] partial sums of split tiles
 };
+
+// Work queues.  The tiles are cut into kXcds contiguous ranges, one per XCD
+// (block b runs on XCD b % kXcds).  The blocks of an XCD take work units from
+// their range in order through an atomic counter, so a block that finishes
+// early takes more, and once the range is used up they take units from the
+// other XCDs' ranges.  When the tiles of a range do not fill the last round of
+// the XCD's blocks, its last r tiles are cut along K into S parts each (parts
+// of at least kMinSplitStages stages), so the last round is made of shorter
+// units; their float32 partial sums go to `part` and split_reduce_bf16 adds
+// them in part order and applies the epilogue.
+constexpr int kSlotsPerXcd = 32;
+constexpr int kMaxSplit = 8;
+constexpr int kMinSplitStages = 32;
+
+struct Queue {
+    int tb;     // first tile of the range
+    int whole;  // units that are whole tiles (the first `whole` tiles)
+    int S;      // parts per split tile (1: no split)
+    int units;  // whole + split tiles * S
+};
+
+// The queue of XCD x: total tiles, nb blocks per XCD, nk K stages per tile.
+__device__ __forceinline__ Queue xcd_queue(int total, int x, int nb, int nk) {
+    Queue q;
+    q.tb = (int)((int64_t)total * x / kXcds);
+    const int n = (int)((int64_t)total * (x + 1) / kXcds) - q.tb;
+    const int r = n % nb;
+    int best = 1;
+    if (r > 0) {
+        // The last round's work, in tiles, if its r tiles are cut in S parts
+        // and the XCD's blocks take them in step: ceil(r S / nb) / S.  Compared
+        // exactly (integers), so the reduction kernel makes the same choice.
+        int best_rounds = 1;  // ceil(r / nb) for S = 1
+        const int smax = min(min(kMaxSplit, nk / kMinSplitStages), kSlotsPerXcd / r);
+        for (int S = 2; S <= smax; ++S) {
+            const int rounds = (r * S + nb - 1) / nb;
+            if (rounds * best < best_rounds * S) {
+                best_rounds = rounds;
+                best = S;
+            }
+        }
+    }
+    q.S = best;
+    q.whole = best > 1 ? n - r : n;
+    q.units = q.whole + (best > 1 ? r * best : 0);
+    return q;
+}
 
 // XOR mask applied to a row's 16-byte K chunk index in LDS (CH chunks per
 // row).  128-byte rows: mode 0 spreads any 8 consecutive rows over distinct
@@ -158,6 +207,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     __shared__ int32_t offs[kMaxExperts + 1];  // the group offsets, read once per block
     __shared__ uint32_t pf_sink[64];           // landing slot of the L2 prefetches (never read)
     __shared__ int scan_tmp[kThreads / 64];
+    __shared__ Queue queues[kXcds];
+    __shared__ int s_unit2[2];                 // the block's next work unit (thread 0 claims it)
 
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
@@ -167,12 +218,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     const int n_tiles = (p.n_out + cols_per_tile - 1) / cols_per_tile;  // last N tile may be partial
     const int total = total_m * n_tiles;
 
-    const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
-    const int lb = blockIdx.x / kXcds;
-    const int t_begin = (int)((int64_t)total * xcd / kXcds), t_end = (int)((int64_t)total * (xcd + 1) / kXcds);
-
     const int K = p.K;
     const int nk = K / BK;
+    const int xcd = blockIdx.x % kXcds, nb = gridDim.x / kXcds;
+    if (tid < kXcds) queues[tid] = xcd_queue(total, tid, nb, nk);
+    // Thread 0 claims units: the own XCD's queue first, then the others'
+    // (a unit is (queue << 20) | index; -1 when every queue is used up).
+    // `dry` remembers the queues found empty, so each costs one atomic.
+    uint32_t dry = 0;
+    auto claim = [&]() -> int {
+        for (int d = 0; d < kXcds; ++d) {
+            const int x = (xcd + d) % kXcds;
+            if (dry >> x & 1) continue;
+            const int u = atomicAdd(p.sched + x, 1);
+            if (u < queues[x].units) return (x << 20) | u;
+            dry |= 1u << x;
+        }
+        return -1;
+    };
+    __syncthreads();
+    int hb = 0;
+    if (tid == 0) s_unit2[0] = claim();
+    __syncthreads();
+    int unit = s_unit2[0];
     const int lrow = lane / CH, lslot = lane % CH;
 
     // LDS byte address of this lane's first A and B fragment (stage 0, K
@@ -195,13 +263,36 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #pragma unroll
         for (int par = 0; par < 2; ++par)
             koff[kk][par] = (uint32_t)(((2 * kk + (lane >> 5)) ^ swz<SWZ>(par * 32 + (lane & 31))) << 4);
-    for (int t = t_begin + lb; t < t_end; t += per_xcd) {
+    while (unit >= 0) {
+        int next = -1;
+        if (tid == 0) next = claim();  // the unit after this one, handed over at its end
+        // decode the unit: tile, K stages [kb, ke), partial-sum slot (-1: whole tile)
+        const int ux = __builtin_amdgcn_readfirstlane(unit >> 20), uu = __builtin_amdgcn_readfirstlane(unit & 0xFFFFF);
+        const Queue q = queues[ux];
+        int t, kb = 0, ke = nk, slot = -1;
+        if (uu < q.whole) {
+            t = q.tb + uu;
+        } else {
+            const int j = uu - q.whole;
+            t = q.tb + q.whole + j / q.S;
+            const int part = j % q.S;
+            kb = part * nk / q.S;
+            ke = (part + 1) * nk / q.S;
+            slot = ux * kSlotsPerXcd + j;
+        }
+        t = __builtin_amdgcn_readfirstlane(t);
+        kb = __builtin_amdgcn_readfirstlane(kb);
+        ke = __builtin_amdgcn_readfirstlane(ke);
+        slot = __builtin_amdgcn_readfirstlane(slot);
         int mt, nt;
         tile_coords(t, total_m, n_tiles, GM, &mt, &nt);
         const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, p.E, mt));
         const int row_end = __builtin_amdgcn_readfirstlane(min(offs[e + 1], p.rows));
         const int row0 = __builtin_amdgcn_readfirstlane(offs[e] + (mt - pre[e]) * kTile);
-        if (row0 < 0 || row0 >= row_end) continue;  // only for inconsistent offsets
+        // (row0 outside [0, row_end) only happens for inconsistent offsets: the
+        // unit is then skipped, its partial sums, if any, left unwritten)
+        const bool skip = row0 < 0 || row0 >= row_end;
+        if (!skip) {
         // first B row of the tile (SwiGLU: first gate row; the up rows are F rows further)
         const int brow0 = SWIGLU ? nt * 128 : nt * kTile;
 
@@ -345,11 +436,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous tile's stores retired
         GG_SB;
-        GG_ISSUE(0, 0);
+        GG_ISSUE(kb, 0);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) GG_LOAD_A(min(1, nk - 1), 1, i);
-        GG_PREFETCH_A(min(2, nk - 1));
-        GG_PREFETCH_B(min(2, nk - 1));
+        for (int i = 0; i < LOADS; ++i) GG_LOAD_A(min(kb + 1, ke - 1), 1, i);
+        GG_PREFETCH_A(min(kb + 2, ke - 1));
+        GG_PREFETCH_B(min(kb + 2, ke - 1));
         __asm__ volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");  // stage 0 landed everywhere
         GG_SB;
         {
@@ -364,19 +455,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             GG_RD_B(fb0, bd, 2);
             GG_RD_B(fb0, bd, 3);
         }
-        for (int kt = 0; kt < nk; ++kt) {
-            const int st = kt & 1;
+        for (int kt = kb; kt < ke; ++kt) {
+            const int st = (kt - kb) & 1;
             const uint32_t so = (uint32_t)st * kStageBytes;
             GG_SB;
             {
                 const uint32_t ad[2] = {a_rd + so + koff[1][0], a_rd + so + koff[1][1]};
                 const uint32_t bd[2] = {b_rd + so + koff[1][0], b_rd + so + koff[1][1]};
-                GG_SUBSTEP_LB(fa0, fb0, fa1, fb1, ad, bd, min(kt + 1, nk - 1), st ^ 1)
+                GG_SUBSTEP_LB(fa0, fb0, fa1, fb1, ad, bd, min(kt + 1, ke - 1), st ^ 1)
             }
             {
                 const uint32_t ad[2] = {a_rd + so + koff[2][0], a_rd + so + koff[2][1]};
                 const uint32_t bd[2] = {b_rd + so + koff[2][0], b_rd + so + koff[2][1]};
-                GG_SUBSTEP_PF(fa1, fb1, fa0, fb0, ad, bd, min(kt + 3, nk - 1))
+                GG_SUBSTEP_PF(fa1, fb1, fa0, fb0, ad, bd, min(kt + 3, ke - 1))
             }
             {
                 const uint32_t ad[2] = {a_rd + so + koff[3][0], a_rd + so + koff[3][1]};
@@ -392,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
                 const uint32_t nso = so ^ kStageBytes;
                 const uint32_t ad[2] = {a_rd + nso + koff[0][0], a_rd + nso + koff[0][1]};
                 const uint32_t bd[2] = {b_rd + nso + koff[0][0], b_rd + nso + koff[0][1]};
-                GG_SUBSTEP_LA(fa1, fb1, fa0, fb0, ad, bd, min(kt + 2, nk - 1), st)
+                GG_SUBSTEP_LA(fa1, fb1, fa0, fb0, ad, bd, min(kt + 2, ke - 1), st)
             }
         }
         GG_SB;
@@ -440,7 +531,31 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             if ((RB0) + prow + 8 * (q >> 1) + 2 * (q & 1) < rlim)                                        \
                 (DST)[(8 * (q >> 1) + 2 * (q & 1)) * (LDW)] = (VP)[q];                                   \
     }
-        if (SWIGLU) {
+
+        if (slot >= 0) {
+            // a K part of a split tile: its float32 partial sums, all 256 x 256
+            // (rows past the group's end and columns past the output width
+            // included; the reduction skips them), in [row][column] order with
+            // SwiGLU gate columns 0..127 and up columns 128..255
+            float* const pb = p.part + (size_t)slot * kTile * kTile;
+#define GB_EPI_PART(MI, NI)                                                                              \
+    {                                                                                                    \
+        const int col = (SWIGLU ? ((NI) < 2 ? 0 : 128) + wn * 64 + ((NI) & 1) * 32 : wn * 128 + (NI) * 32) + c2; \
+        const int rb0 = wm * 128 + (MI) * 32;                                                            \
+        float v[16];                                                                                     \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
+        float2 vp[8];                                                                                    \
+        pair_f32(v, lane, vp);                                                                           \
+        float2* dst = (float2*)(pb + (size_t)(rb0 + prow) * kTile + col);                               \
+        _Pragma("unroll") for (int q = 0; q < 8; ++q) dst[(8 * (q >> 1) + 2 * (q & 1)) * (kTile / 2)] = vp[q]; \
+    }                                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);
+            GB_EPI_PART(0, 0) GB_EPI_PART(0, 1) GB_EPI_PART(0, 2) GB_EPI_PART(0, 3)
+            GB_EPI_PART(1, 0) GB_EPI_PART(1, 1) GB_EPI_PART(1, 2) GB_EPI_PART(1, 3)
+            GB_EPI_PART(2, 0) GB_EPI_PART(2, 1) GB_EPI_PART(2, 2) GB_EPI_PART(2, 3)
+            GB_EPI_PART(3, 0) GB_EPI_PART(3, 1) GB_EPI_PART(3, 2) GB_EPI_PART(3, 3)
+#undef GB_EPI_PART
+        } else if (SWIGLU) {
             uint16_t* const cbase = p.C + (size_t)rbase * p.n_out;
             uint16_t* const sbase = p.stash ? p.stash + (size_t)rbase * 2 * p.n_out : nullptr;
 #define GB_EPI_SW(MI, NI)                                                                                \
@@ -497,6 +612,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #undef GB_EPI_DN
         }
 #undef GB_STORE_PAIRS
+        }  // !skip
+        // hand the claimed unit to every wave (double-buffered slot: a wave
+        // still reading the previous one cannot see it overwritten)
+        if (tid == 0) s_unit2[hb ^ 1] = next;
+        __syncthreads();
+        hb ^= 1;
+        unit = s_unit2[hb];
     }
 }
 

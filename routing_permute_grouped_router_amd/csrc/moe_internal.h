@@ -63,10 +63,13 @@ hipError_t launch_permute_bwd(const moe_config& c, const void* dxp, const int32_
                               hipStream_t s);
 
 // Grouped GEMMs.
+// ws: gemm_bf16_ws_bytes(c) bytes (work-queue counters and the partial sums
+// of K-split tiles).
+size_t gemm_bf16_ws_bytes(const moe_config& c);
 hipError_t launch_swiglu_gemm_bf16(const moe_config& c, const uint16_t* xp, const uint16_t* w1,
-                                   const int32_t* offsets, uint16_t* h, uint16_t* stash, hipStream_t s);
+                                   const int32_t* offsets, uint16_t* h, uint16_t* stash, void* ws, hipStream_t s);
 hipError_t launch_down_gemm_bf16(const moe_config& c, const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
-                                 uint16_t* yp, hipStream_t s);
+                                 uint16_t* yp, void* ws, hipStream_t s);
 hipError_t launch_swiglu_gemm_f32(const moe_config& c, const float* xp, const float* w1, const int32_t* offsets,
                                   float* h, float* stash, hipStream_t s);
 hipError_t launch_down_gemm_f32(const moe_config& c, const float* h, const float* w2, const int32_t* offsets,

@@ -65,15 +65,15 @@ def test_null_pointers_rejected():
 def test_unsupported_shapes():
     lib = moe.load_library()
     c = _cfg(H=96)
-    assert lib.moe_grouped_swiglu_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, None, None) == \
+    assert lib.moe_grouped_swiglu_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, None, None, 0, None) == \
         b.MOE_ERR_UNSUPPORTED
     c = _cfg(F=40)
-    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, 0, None) == b.MOE_ERR_UNSUPPORTED
     c = _cfg(F=192, dtype=b.MOE_MXFP8)  # MXFP8 tiles F by 128
-    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, 1, 1, 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, 1, 1, 1, 1, 1, None, 0, None) == b.MOE_ERR_UNSUPPORTED
     assert b"128" in lib.moe_last_error()
     c = _cfg(H=32768, F=16384)  # one expert's weights must stay below 2^32 bytes
-    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, 0, None) == b.MOE_ERR_UNSUPPORTED
 
 
 def test_workspace_checks():
@@ -86,6 +86,11 @@ def test_workspace_checks():
     assert lib.moe_rows_capacity(ctypes.byref(c)) == 5000 * 8
     c2 = _cfg(T=5000, E=128, k=8, align=128)
     assert lib.moe_rows_capacity(ctypes.byref(c2)) == 5000 * 8 + 128 * 127
+    # the grouped GEMMs take the same workspace
+    st = lib.moe_grouped_swiglu_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, None, 1, need - 1, None)
+    assert st == b.MOE_ERR_WORKSPACE
+    st = lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, 0, None)
+    assert st == b.MOE_ERR_WORKSPACE
 
 
 def test_backward_workspace_bounds():
@@ -94,7 +99,9 @@ def test_backward_workspace_bounds():
     c = _cfg(T=16384, H=2048, F=768, E=128, k=8)
     need = lib.moe_backward_workspace_size(ctypes.byref(c))
     assert 0 < need <= (1 << 30) + (1 << 20)
-    assert lib.moe_workspace_size(ctypes.byref(c)) < (1 << 20)  # the forward needs only the grouping scratch
+    # the bf16 forward: grouping scratch plus the GEMMs' queue counters and split-tile partial sums
+    assert (64 << 20) < lib.moe_workspace_size(ctypes.byref(c)) < (65 << 20)
+    assert lib.moe_workspace_size(ctypes.byref(_cfg(T=16384, H=2048, F=768, E=128, k=8, dtype=b.MOE_F32))) < (1 << 20)
     # too few rows to split an expert: only the per-expert table
     c = _cfg(T=64, H=128, F=64, E=8, k=2)
     assert lib.moe_backward_workspace_size(ctypes.byref(c)) < 4096

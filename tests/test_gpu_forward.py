@@ -94,6 +94,64 @@ def test_forward_full_size(shape):
         print(f"{s.name}: {int((counts == 0).sum())} empty experts, max count {int(counts.max())}")
 
 
+# Shapes whose contraction (H for the gate/up GEMM, F for the down GEMM) is
+# long enough that the GEMMs cut tiles along K: the gate/up GEMM (with the
+# g | u stash) in the first, the down GEMM in the second.
+SPLIT_K = [
+    wl.MoEShape("split_k_gateup_bf16", 1024, 4096, 128, 8, 2, "softmax", False, "bf16", seed=2006),
+    wl.MoEShape("split_k_down_bf16", 1024, 256, 4096, 8, 2, "softmax", False, "bf16", seed=2007),
+]
+
+
+def _split_tiles(offsets, rows_cap, E, K, n_out, cols_per_tile, cus):
+    """Tiles the grouped bf16 GEMM cuts along K for these group offsets: the
+    launch's work-queue layout (8 XCD ranges, the last partial round of each
+    split when that shortens it), restated so the test can require that its
+    shape takes the split path."""
+    n_tiles = -(-n_out // cols_per_tile)
+    max_tiles = (rows_cap // 256 + E) * n_tiles
+    grid = min(cus // 8 * 8, max(-(-max_tiles // 8) * 8, 8))
+    nb, nk = grid // 8, K // 64
+    total = sum(-(-int(offsets[e + 1] - offsets[e]) // 256) for e in range(E)) * n_tiles
+    split = 0
+    for x in range(8):
+        n = total * (x + 1) // 8 - total * x // 8
+        r = n % nb
+        if r == 0:
+            continue
+        best, best_rounds = 1, 1
+        for S in range(2, min(8, nk // 32, 32 // r) + 1):
+            rounds = -(-r * S // nb)
+            if rounds * best < best_rounds * S:
+                best, best_rounds = S, rounds
+        split += r if best > 1 else 0
+    return split
+
+
+@pytest.mark.parametrize("shape", SPLIT_K, ids=lambda s: s.name)
+def test_forward_split_k_tiles(shape):
+    """Tiles cut along K (partial sums added by the reduction kernel, which also
+    applies the SwiGLU epilogue and writes the stash) against the oracle, in full."""
+    inp = Inputs(shape)
+    buf = run_forward(inp, training=True)
+    s = shape
+    idx, w, counts, offsets, row_map, src_map = _check_routing(inp, buf)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    R = s.T * s.k
+    gate_up = _split_tiles(offsets, R, s.E, s.H, s.F, 128, cus)
+    down = _split_tiles(offsets, R, s.E, s.F, s.H, 256, cus)
+    assert (gate_up if s.H > s.F else down) > 0, "the shape no longer exercises the K-split path"
+    ref = orc.forward_tokens(s, np.arange(s.T), inp.x, inp.w1, inp.w2, idx, w, want_stash=True)
+    rm = row_map.ravel()
+    h, yp, st = to_host(buf["h"]), to_host(buf["yp"]), to_host(buf["gu_stash"])
+    assert rel_err(decode("bf16", h[rm]), decode("bf16", ref["h"].reshape(-1, s.F))) < TOL["bf16"]
+    assert rel_err(decode("bf16", st[rm]), decode("bf16", ref["stash"].reshape(-1, 2 * s.F))) < TOL["bf16"]
+    assert rel_err(decode("bf16", yp[rm]), decode("bf16", ref["yp"].reshape(-1, s.H))) < TOL["bf16"]
+    y = decode("bf16", to_host(buf["y"]))
+    assert np.all(np.isfinite(y))
+    assert rel_err(y, decode("bf16", ref["y"])) < TOL["bf16"]
+
+
 def test_route_edge_cases():
     # ties, signed zeros and uniform logits (every token picks experts 0..k-1)
     T, E, k = 130, 16, 4
