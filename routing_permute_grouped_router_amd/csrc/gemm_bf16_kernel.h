@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     __shared__ uint32_t pf_sink[64];           // landing slot of the L2 prefetches (never read)
     __shared__ int scan_tmp[kThreads / 64];
     __shared__ Queue queues[kXcds];
-    __shared__ int s_unit2[2];                 // the block's next work unit (thread 0 claims it)
+    __shared__ int s_unit;                     // the block's next work unit (thread 0 claims it)
 
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1;
@@ -222,12 +222,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     const int nk = K / BK;
     const int xcd = blockIdx.x % kXcds, nb = gridDim.x / kXcds;
     if (tid < kXcds) queues[tid] = xcd_queue(total, tid, nb, nk);
-    // Thread 0 claims units: the own XCD's queue first, then the others'
-    // (a unit is (queue << 20) | index; -1 when every queue is used up).
-    // `dry` remembers the queues found empty, so each costs one atomic.
+    // Thread 0 claims units: tickets from the own XCD's queue, then units of
+    // the other XCDs' queues once it is used up (a unit is (queue << 20) |
+    // index; -1 when every queue is used up).  `dry` remembers the queues
+    // found empty, so each costs one atomic.  A ticket is taken one unit ahead
+    // and looked at only after the next full memory wait, so no wave waits on
+    // the atomic; stealing (only at the end) waits.
     uint32_t dry = 0;
-    auto claim = [&]() -> int {
-        for (int d = 0; d < kXcds; ++d) {
+    auto ticket = [&]() -> int { return (dry >> xcd & 1) ? -1 : atomicAdd(p.sched + xcd, 1); };
+    auto take = [&](int r) -> int {
+        if (!(dry >> xcd & 1)) {
+            if (r >= 0 && r < queues[xcd].units) return (xcd << 20) | r;
+            dry |= 1u << xcd;
+        }
+        for (int d = 1; d < kXcds; ++d) {
             const int x = (xcd + d) % kXcds;
             if (dry >> x & 1) continue;
             const int u = atomicAdd(p.sched + x, 1);
@@ -237,10 +245,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         return -1;
     };
     __syncthreads();
-    int hb = 0;
-    if (tid == 0) s_unit2[0] = claim();
+    int tick = -1;
+    if (tid == 0) {
+        s_unit = take(ticket());
+        tick = ticket();
+    }
     __syncthreads();
-    int unit = s_unit2[0];
+    int unit = s_unit;
     const int lrow = lane / CH, lslot = lane % CH;
 
     // LDS byte address of this lane's first A and B fragment (stage 0, K
@@ -263,83 +274,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #pragma unroll
         for (int par = 0; par < 2; ++par)
             koff[kk][par] = (uint32_t)(((2 * kk + (lane >> 5)) ^ swz<SWZ>(par * 32 + (lane & 31))) << 4);
-    while (unit >= 0) {
-        int next = -1;
-        if (tid == 0) next = claim();  // the unit after this one, handed over at its end
-        // decode the unit: tile, K stages [kb, ke), partial-sum slot (-1: whole tile)
-        const int ux = __builtin_amdgcn_readfirstlane(unit >> 20), uu = __builtin_amdgcn_readfirstlane(unit & 0xFFFFF);
-        const Queue q = queues[ux];
-        int t, kb = 0, ke = nk, slot = -1;
-        if (uu < q.whole) {
-            t = q.tb + uu;
-        } else {
-            const int j = uu - q.whole;
-            t = q.tb + q.whole + j / q.S;
-            const int part = j % q.S;
-            kb = part * nk / q.S;
-            ke = (part + 1) * nk / q.S;
-            slot = ux * kSlotsPerXcd + j;
-        }
-        t = __builtin_amdgcn_readfirstlane(t);
-        kb = __builtin_amdgcn_readfirstlane(kb);
-        ke = __builtin_amdgcn_readfirstlane(ke);
-        slot = __builtin_amdgcn_readfirstlane(slot);
-        int mt, nt;
-        tile_coords(t, total_m, n_tiles, GM, &mt, &nt);
-        const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, p.E, mt));
-        const int row_end = __builtin_amdgcn_readfirstlane(min(offs[e + 1], p.rows));
-        const int row0 = __builtin_amdgcn_readfirstlane(offs[e] + (mt - pre[e]) * kTile);
-        // (row0 outside [0, row_end) only happens for inconsistent offsets: the
-        // unit is then skipped, its partial sums, if any, left unwritten)
-        const bool skip = row0 < 0 || row0 >= row_end;
-        if (!skip) {
-        // first B row of the tile (SwiGLU: first gate row; the up rows are F rows further)
-        const int brow0 = SWIGLU ? nt * 128 : nt * kTile;
-
-        // Per-lane byte offsets of the A and B loads (K offset 0) against the
-        // uniform bases: 32-bit, so the loads take few registers.
-        uint32_t aoff[LOADS], boff[LOADS];
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int r = wid * 64 + i * RPL + lrow;  // tile row 0..255
-            const int chunk = lslot ^ swz<SWZ>(r);
-            const int ar = min(row0 + r, row_end - 1);
-            aoff[i] = (uint32_t)(((size_t)(ar - row0) * K + chunk * 8) * 2);
-            int br;
-            if (SWIGLU) {
-                const int f = min(nt * 128 + (r & 127), p.n_out - 1);
-                br = r < 128 ? f : p.n_out + f;
-            } else {
-                br = min(nt * kTile + r, p.n_out - 1);
-            }
-            boff[i] = (uint32_t)(((size_t)(br - brow0) * K + chunk * 8) * 2);
-        }
-        const char* abase = (const char*)(p.A + (size_t)row0 * K);  // A offsets are tile-relative
-        const char* bbase = (const char*)(p.B + ((size_t)e * p.b_rows + brow0) * K);  // tile-relative too
-        // L2 prefetch: lane l of wave w touches the K segment of a stage in
-        // tile row w * 64 + l of A and of B (the rows this wave loads).
-        uint32_t apf, bpf;
-        {
-            const int r = wid * 64 + lane;
-            apf = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K * 2);
-            int br;
-            if (SWIGLU) {
-                const int f = min(nt * 128 + (r & 127), p.n_out - 1);
-                br = r < 128 ? f : p.n_out + f;
-            } else {
-                br = min(nt * kTile + r, p.n_out - 1);
-            }
-            bpf = (uint32_t)((size_t)(br - brow0) * K * 2);
-        }
-
-        f32x16 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
+    // State of the unit in flight, set by `setup`: its tile, K stages
+    // [kb, ke), partial-sum slot (-1: whole tile), load offsets and bases.
+    int kb = 0, ke = 0, slot = -1, row0 = 0, row_end = 0, nt = 0;
+    bool valid = false;
+    uint32_t aoff[LOADS], boff[LOADS], apf = 0, bpf = 0;
+    const char* abase = (const char*)p.A;
+    const char* bbase = (const char*)p.B;
 #define GG_LOAD_A(kt, stage, i)                                                                          \
     dma_lds16(lds_wave + (uint32_t)(stage) * kStageBytes + (i) * RPL * BK * 2, aoff[i], abase + (size_t)(kt) * (BK * 2))
 #define GG_LOAD_B(kt, stage, i)                                                                          \
@@ -420,6 +361,92 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_PREFETCH_A(PKT), GG_PREFETCH_B(PKT), GG_N_, GG_N_, GG_N_,    \
                  GG_N_, GG_N_, GG_N_)
 
+    // Decode unit u (from `take`), compute its tile's addressing and issue
+    // the loads of its first stage, the A half of its second and the L2
+    // prefetch of its third (stage buffers 0 and 1).  Called right after the
+    // previous unit's K loop, so these loads are in flight while that unit's
+    // epilogue runs.  A wave's loads land in issue order, after the previous
+    // unit's last (repeated) loads of the same rows.
+    auto setup = [&](int u) __attribute__((always_inline)) {
+        const int ux = __builtin_amdgcn_readfirstlane(u >> 20), uu = __builtin_amdgcn_readfirstlane(u & 0xFFFFF);
+        const Queue q = queues[ux];
+        int t;
+        kb = 0;
+        ke = nk;
+        slot = -1;
+        if (uu < q.whole) {
+            t = q.tb + uu;
+        } else {
+            const int j = uu - q.whole;
+            t = q.tb + q.whole + j / q.S;
+            const int part = j % q.S;
+            kb = part * nk / q.S;
+            ke = (part + 1) * nk / q.S;
+            slot = ux * kSlotsPerXcd + j;
+        }
+        t = __builtin_amdgcn_readfirstlane(t);
+        kb = __builtin_amdgcn_readfirstlane(kb);
+        ke = __builtin_amdgcn_readfirstlane(ke);
+        slot = __builtin_amdgcn_readfirstlane(slot);
+        int mt, ntt;
+        tile_coords(t, total_m, n_tiles, GM, &mt, &ntt);
+        nt = __builtin_amdgcn_readfirstlane(ntt);
+        const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, p.E, mt));
+        row_end = __builtin_amdgcn_readfirstlane(min(offs[e + 1], p.rows));
+        row0 = __builtin_amdgcn_readfirstlane(offs[e] + (mt - pre[e]) * kTile);
+        // row0 outside [0, row_end) only happens for inconsistent offsets: the
+        // unit is then skipped (no loads, no K loop, nothing stored)
+        valid = row0 >= 0 && row0 < row_end;
+        if (!valid) {
+            kb = ke = 0;
+            return;
+        }
+        // first B row of the tile (SwiGLU: first gate row; the up rows are F rows further)
+        const int brow0 = SWIGLU ? nt * 128 : nt * kTile;
+        // Per-lane byte offsets of the A and B loads (K offset 0) against the
+        // uniform tile bases: 32-bit, so the loads take few registers.
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int r = wid * 64 + i * RPL + lrow;  // tile row 0..255
+            const int chunk = lslot ^ swz<SWZ>(r);
+            const int ar = min(row0 + r, row_end - 1);
+            aoff[i] = (uint32_t)(((size_t)(ar - row0) * K + chunk * 8) * 2);
+            int br;
+            if (SWIGLU) {
+                const int f = min(nt * 128 + (r & 127), p.n_out - 1);
+                br = r < 128 ? f : p.n_out + f;
+            } else {
+                br = min(nt * kTile + r, p.n_out - 1);
+            }
+            boff[i] = (uint32_t)(((size_t)(br - brow0) * K + chunk * 8) * 2);
+        }
+        abase = (const char*)(p.A + (size_t)row0 * K);
+        bbase = (const char*)(p.B + ((size_t)e * p.b_rows + brow0) * K);
+        // L2 prefetch: lane l of wave w touches the K segment of a stage in
+        // tile row w * 64 + l of A and of B (the rows this wave loads).
+        {
+            const int r = wid * 64 + lane;
+            apf = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K * 2);
+            int br;
+            if (SWIGLU) {
+                const int f = min(nt * 128 + (r & 127), p.n_out - 1);
+                br = r < 128 ? f : p.n_out + f;
+            } else {
+                br = min(nt * kTile + r, p.n_out - 1);
+            }
+            bpf = (uint32_t)((size_t)(br - brow0) * K * 2);
+        }
+        GG_SB;
+        GG_ISSUE(kb, 0);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) GG_LOAD_A(min(kb + 1, ke - 1), 1, i);
+        GG_PREFETCH_A(min(kb + 2, ke - 1));
+        GG_PREFETCH_B(min(kb + 2, ke - 1));
+        GG_SB;
+    };
+
+    setup(unit);
+    while (unit >= 0) {
         // Two LDS stages, software-pipelined across the stage boundary.  A stage
         // is four 16-deep K sub-steps of 16 MFMAs each; the fragments of
         // sub-step j+1 are read from LDS while the MFMAs of sub-step j issue.
@@ -431,18 +458,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         // stage kt+1 (so the address unit is never oversubscribed), and the
         // L2 prefetch of stage kt+3 rides on the second sub-step.  Loads past
         // the end of K repeat the last stage into the free buffer, so the loop
-        // has no branch; a wave's loads complete in issue order, so they land
-        // before the next tile's loads of the same rows.
+        // has no branch.
         bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous tile's stores retired
+        // the unit's first stage landed everywhere; the previous unit's stores retired
+        __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         GG_SB;
-        GG_ISSUE(kb, 0);
+        if (tid == 0) {  // publish the next unit, take a ticket for the one after
+            const int nu = take(tick);
+            s_unit = nu;
+            tick = nu >= 0 ? ticket() : -1;
+        }
+        f32x16 acc[4][4];
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) GG_LOAD_A(min(kb + 1, ke - 1), 1, i);
-        GG_PREFETCH_A(min(kb + 2, ke - 1));
-        GG_PREFETCH_B(min(kb + 2, ke - 1));
-        __asm__ volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");  // stage 0 landed everywhere
-        GG_SB;
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
         {
             const uint32_t ad[2] = {a_rd + koff[0][0], a_rd + koff[0][1]};
             const uint32_t bd[2] = {b_rd + koff[0][0], b_rd + koff[0][1]};
@@ -506,6 +538,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #undef GG_SUBSTEP_PF
 
 
+        // The next unit (published by thread 0 before this unit's K loop; the
+        // barrier makes it visible even when the loop had no stage), its
+        // first loads issued before this unit's epilogue.
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int next_unit = s_unit;
+        const int e_row0 = row0, e_row_end = row_end, e_nt = nt, e_slot = slot;
+        const bool e_valid = valid;
+        if (next_unit >= 0) setup(next_unit);
+        if (e_valid) {
         // Epilogue straight from the accumulators: each 32 x 32 tile becomes 8
         // bf16 pairs per lane (two adjacent columns of one row, one DPP lane
         // swap per pair), stored as 4-byte words; 32 lanes cover 128
@@ -513,11 +554,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         // Opaque copies of the tile's first row and of the lane index: the
         // address arithmetic below then stays after the K loop (it is not
         // hoisted out of the tile loop, where it would hold registers).
-        int rbase = row0, ln = lane;
+        int rbase = e_row0, ln = lane;
         __asm__ volatile("" : "+v"(rbase), "+v"(ln));
         const int c2 = (ln & 31) & ~1;                // even column of this lane's pairs
         const int prow = 4 * (ln >> 5) + (ln & 1);    // row of this lane's pair 0 in a 32-row block
-        const int rlim = row_end - rbase;  // rows of the tile that exist
+        const int rlim = e_row_end - rbase;  // rows of the tile that exist
         const uint32_t ldw = (uint32_t)p.n_out / 2;  // 4-byte words per output row
         // Store the 8 pairs of a 32-row block whose first row (tile-relative) is
         // RB0 from word pointer DST (this lane's pair-0 address), LDW words per
@@ -532,12 +573,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
                 (DST)[(8 * (q >> 1) + 2 * (q & 1)) * (LDW)] = (VP)[q];                                   \
     }
 
-        if (slot >= 0) {
+        if (e_slot >= 0) {
             // a K part of a split tile: its float32 partial sums, all 256 x 256
             // (rows past the group's end and columns past the output width
             // included; the reduction skips them), in [row][column] order with
             // SwiGLU gate columns 0..127 and up columns 128..255
-            float* const pb = p.part + (size_t)slot * kTile * kTile;
+            float* const pb = p.part + (size_t)e_slot * kTile * kTile;
 #define GB_EPI_PART(MI, NI)                                                                              \
     {                                                                                                    \
         const int col = (SWIGLU ? ((NI) < 2 ? 0 : 128) + wn * 64 + ((NI) & 1) * 32 : wn * 128 + (NI) * 32) + c2; \
@@ -560,7 +601,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             uint16_t* const sbase = p.stash ? p.stash + (size_t)rbase * 2 * p.n_out : nullptr;
 #define GB_EPI_SW(MI, NI)                                                                                \
     {                                                                                                    \
-        const int f = nt * 128 + wn * 64 + (NI) * 32 + c2;                                               \
+        const int f = e_nt * 128 + wn * 64 + (NI) * 32 + c2;                                               \
         const int rb0 = wm * 128 + (MI) * 32;                                                            \
         float hv[16];                                                                                    \
         float gv[16], uv[16];                                                                            \
@@ -593,7 +634,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             uint16_t* const cbase = p.C + (size_t)rbase * p.n_out;
 #define GB_EPI_DN(MI, NI)                                                                                \
     {                                                                                                    \
-        const int n = nt * kTile + wn * 128 + (NI) * 32 + c2;                                            \
+        const int n = e_nt * kTile + wn * 128 + (NI) * 32 + c2;                                            \
         const int rb0 = wm * 128 + (MI) * 32;                                                            \
         float v[16];                                                                                     \
         _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
@@ -612,13 +653,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #undef GB_EPI_DN
         }
 #undef GB_STORE_PAIRS
-        }  // !skip
-        // hand the claimed unit to every wave (double-buffered slot: a wave
-        // still reading the previous one cannot see it overwritten)
-        if (tid == 0) s_unit2[hb ^ 1] = next;
-        __syncthreads();
-        hb ^= 1;
-        unit = s_unit2[hb];
+        }  // valid
+        unit = next_unit;
     }
 }
 
