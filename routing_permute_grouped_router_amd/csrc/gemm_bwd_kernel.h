@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
     __shared__ int32_t spre[WG ? kMaxExperts + 1 : 1];
     __shared__ int scan_tmp[kThreads / 64];
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1, half = lane >> 5;
     const int n_tiles = (p.N + kTile - 1) / kTile;
     int total, m_tiles = 0;
@@ -233,6 +233,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
             k_begin = 0;
             k_end = p.K;
         }
+        // the tile's coordinates are uniform: the load bases live in SGPRs
+        e = __builtin_amdgcn_readfirstlane(e);
+        m0 = __builtin_amdgcn_readfirstlane(m0);
+        n0 = __builtin_amdgcn_readfirstlane(n0);
+        k_begin = __builtin_amdgcn_readfirstlane(k_begin);
+        k_end = __builtin_amdgcn_readfirstlane(k_end);
+        row0 = __builtin_amdgcn_readfirstlane(row0);
+        row_end = __builtin_amdgcn_readfirstlane(row_end);
         const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
 
         // per-lane byte offsets of the 8 loads of each operand, for K step 0
@@ -282,92 +290,151 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-#define GB_LOAD(kt, st)                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                       \
-        size_t ao = aoff[i] + (size_t)(kt) * a_kstep, bo = boff[i] + (size_t)(kt) * b_kstep;              \
-        if (WG) {                                                                                         \
-            const int kr = (kt) * BK + 16 * wid + 2 * i + s_kr;                                           \
-            if (kr > a_rowcap) {                                                                          \
-                const size_t back = (size_t)(kr - a_rowcap);                                              \
-                ao -= back * p.M * 2;                                                                     \
-                bo -= back * p.N * 2;                                                                     \
-            }                                                                                             \
+        // Direct-to-LDS loads (dma_lds16: uniform M0 and base, 32-bit lane
+        // offsets).  Stage kt of an operand starts at base + kt * kstep.
+        // A WGRAD unit's last stage may run past its rows: there each lane
+        // clamps its K row to the unit's last row (the only stage that needs
+        // per-lane arithmetic), and the A copy of those rows is zeroed once
+        // they have landed (this wave's own rows).
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0][0];
+        const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(WG ? 16 * wid * 512 : wid * 64 * 128));
+        const uint32_t b_dst = __builtin_amdgcn_readfirstlane(lds_base + OPB + (uint32_t)(16 * wid * 512));
+        // stage kt reaches past the WGRAD unit's rows
+#define GB_TAIL(kt) (WG && (kt) * BK + BK - 1 > a_rowcap)
+#define GB_LOAD_A(kt, st, i)                                                                              \
+    {                                                                                                     \
+        uint32_t o_ = aoff[i];                                                                            \
+        if (GB_TAIL(kt)) {                                                                                \
+            const int kr_ = (kt) * BK + 16 * wid + 2 * (i) + s_kr;                                        \
+            if (kr_ > a_rowcap) o_ -= (uint32_t)(kr_ - a_rowcap) * (uint32_t)p.M * 2u;                    \
         }                                                                                                 \
-        __builtin_amdgcn_global_load_lds((glb_void*)(abase + ao),                                         \
-                                         (lds_void*)&lds[st][0][(WG ? (16 * wid + 2 * i) * 512            \
-                                                                    : (wid * 64 + 8 * i) * 128)], 16, 0, 0); \
-        __builtin_amdgcn_global_load_lds((glb_void*)(bbase + bo),                                         \
-                                         (lds_void*)&lds[st][1][(16 * wid + 2 * i) * 512], 16, 0, 0);     \
+        dma_lds16(a_dst + (uint32_t)(st) * 2 * OPB + (i) * (WG ? 2 * 512 : 8 * 128), o_,                  \
+                  abase + (size_t)(kt) * a_kstep);                                                        \
     }
-        // WGRAD tail: zero the A copy of K rows past the unit's end (this wave's own rows, after its loads landed)
+#define GB_LOAD_B(kt, st, i)                                                                              \
+    {                                                                                                     \
+        uint32_t o_ = boff[i];                                                                            \
+        if (GB_TAIL(kt)) {                                                                                \
+            const int kr_ = (kt) * BK + 16 * wid + 2 * (i) + s_kr;                                        \
+            if (kr_ > a_rowcap) o_ -= (uint32_t)(kr_ - a_rowcap) * (uint32_t)p.N * 2u;                    \
+        }                                                                                                 \
+        dma_lds16(b_dst + (uint32_t)(st) * 2 * OPB + (i) * 2 * 512, o_, bbase + (size_t)(kt) * b_kstep);  \
+    }
+        // WGRAD tail: zero the A copy of K rows past the unit's end (this wave's
+        // own rows; every load of this wave has landed)
 #define GB_ZERO_TAIL(kt, st)                                                                              \
-    if (WG && (kt) * BK + BK - 1 > a_rowcap) {                                                            \
+    if (GB_TAIL(kt)) {                                                                                    \
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");                                             \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                   \
             const int kr = 16 * wid + 2 * i + s_kr;                                                       \
             if ((kt) * BK + kr > a_rowcap) *(uint4*)&lds[st][0][kr * 512 + s_pos * 16] = make_uint4(0, 0, 0, 0); \
         }                                                                                                 \
     }
+        // fragment reads of K sub-step kk of the stage in buffer st: A
+        // fragment mi (one 16-byte read, or two transpose reads for a strided
+        // A), B fragment ni (two transpose reads)
+#define GB_RD_A(FA, st, kk, mi)                                                                           \
+    FA[mi] = WG ? bwd_tr_frag(lds_base + (st) * 2 * OPB + a_tr[mi] + (16 * (kk) + 8 * half) * 512)        \
+                : __builtin_bit_cast(bf16x8, bwd_ds_read16(lds_base + (st) * 2 * OPB + arow[mi] * 128 +   \
+                                                           ((((kk) * 2 + half) ^ (arow[mi] & 7)) << 4)))
+#define GB_RD_B(FB, st, kk, ni) FB[ni] = bwd_tr_frag(lds_base + (st) * 2 * OPB + OPB + b_tr[ni] + (16 * (kk) + 8 * half) * 512)
+#define GB_MFMA(FA, FB, mi, ni) acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0)
+#define GB_SB __builtin_amdgcn_sched_barrier(0)
+#define GB_STEP(FA, FB, mi, ni, PRE, RD)                                                                  \
+    PRE;                                                                                                  \
+    GB_MFMA(FA, FB, mi, ni);                                                                              \
+    RD;                                                                                                   \
+    GB_SB;
+        // One K sub-step: 16 MFMAs on FA/FB; the 8 fragment reads of sub-step
+        // KK (buffer ST) into GA/GB follow the first 8 of them, and L0..L7 (loads
+        // of a later stage, or nothing) precede every other MFMA: one 1 KiB
+        // load per two MFMAs per wave is what the CU's address unit sustains.
+#define GB_SUBSTEP_X(FA, FB, GA, GB, ST, KK, L0, L1, L2, L3, L4, L5, L6, L7)                              \
+    BWD_WAIT(FA, FB);                                                                                     \
+    GB_SB;                                                                                                \
+    GB_STEP(FA, FB, 0, 0, L0, GB_RD_A(GA, ST, KK, 0))                                                     \
+    GB_STEP(FA, FB, 0, 1, (void)0, GB_RD_A(GA, ST, KK, 1))                                                \
+    GB_STEP(FA, FB, 0, 2, L1, GB_RD_A(GA, ST, KK, 2))                                                     \
+    GB_STEP(FA, FB, 0, 3, (void)0, GB_RD_A(GA, ST, KK, 3))                                                \
+    GB_STEP(FA, FB, 1, 0, L2, GB_RD_B(GB, ST, KK, 0))                                                     \
+    GB_STEP(FA, FB, 1, 1, (void)0, GB_RD_B(GB, ST, KK, 1))                                                \
+    GB_STEP(FA, FB, 1, 2, L3, GB_RD_B(GB, ST, KK, 2))                                                     \
+    GB_STEP(FA, FB, 1, 3, (void)0, GB_RD_B(GB, ST, KK, 3))                                                \
+    GB_STEP(FA, FB, 2, 0, L4, (void)0)                                                                    \
+    GB_STEP(FA, FB, 2, 1, (void)0, (void)0)                                                               \
+    GB_STEP(FA, FB, 2, 2, L5, (void)0)                                                                    \
+    GB_STEP(FA, FB, 2, 3, (void)0, (void)0)                                                               \
+    GB_STEP(FA, FB, 3, 0, L6, (void)0)                                                                    \
+    GB_STEP(FA, FB, 3, 1, (void)0, (void)0)                                                               \
+    GB_STEP(FA, FB, 3, 2, L7, (void)0)                                                                    \
+    GB_STEP(FA, FB, 3, 3, (void)0, (void)0)
+#define GB_N_ (void)0
+#define GB_SUBSTEP(FA, FB, GA, GB, ST, KK)                                                                \
+    GB_SUBSTEP_X(FA, FB, GA, GB, ST, KK, GB_N_, GB_N_, GB_N_, GB_N_, GB_N_, GB_N_, GB_N_, GB_N_)
+#define GB_SUBSTEP_LA(FA, FB, GA, GB, ST, KK, LKT, LST)                                                   \
+    GB_SUBSTEP_X(FA, FB, GA, GB, ST, KK, GB_LOAD_A(LKT, LST, 0), GB_LOAD_A(LKT, LST, 1), GB_LOAD_A(LKT, LST, 2), \
+                 GB_LOAD_A(LKT, LST, 3), GB_LOAD_A(LKT, LST, 4), GB_LOAD_A(LKT, LST, 5), GB_LOAD_A(LKT, LST, 6), \
+                 GB_LOAD_A(LKT, LST, 7))
+#define GB_SUBSTEP_LB(FA, FB, GA, GB, ST, KK, LKT, LST)                                                   \
+    GB_SUBSTEP_X(FA, FB, GA, GB, ST, KK, GB_LOAD_B(LKT, LST, 0), GB_LOAD_B(LKT, LST, 1), GB_LOAD_B(LKT, LST, 2), \
+                 GB_LOAD_B(LKT, LST, 3), GB_LOAD_B(LKT, LST, 4), GB_LOAD_B(LKT, LST, 5), GB_LOAD_B(LKT, LST, 6), \
+                 GB_LOAD_B(LKT, LST, 7))
 
-        const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0][0];
-        // fragments of K sub-step kk (16 values) of the stage in buffer st
-#define GB_READ(st, kk, FA, FB)                                                                           \
-    {                                                                                                     \
-        const uint32_t sa_ = lds_base + (st) * 2 * OPB, sb_ = sa_ + OPB;                                  \
-        _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) {                                                \
-            if (WG) FA[mi] = bwd_tr_frag(sa_ + a_tr[mi] + (16 * (kk) + 8 * half) * 512);                  \
-            else FA[mi] = __builtin_bit_cast(bf16x8, bwd_ds_read16(sa_ + arow[mi] * 128 +                 \
-                                                                   ((((kk) * 2 + half) ^ (arow[mi] & 7)) << 4))); \
-        }                                                                                                 \
-        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)                                                  \
-            FB[ni] = bwd_tr_frag(sb_ + b_tr[ni] + (16 * (kk) + 8 * half) * 512);                          \
-    }
-#define GB_MFMAS(FA, FB)                                                                                  \
-    _Pragma("unroll") for (int mi = 0; mi < 4; ++mi) _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)     \
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0);
-
+        // Two LDS stages, software-pipelined as in the forward kernel: the
+        // barrier of stage kt sits before its last sub-step (stage kt read by
+        // every wave, stage kt+1 landed); after it the A half of stage kt+2
+        // goes into the freed buffer under the last sub-step's MFMAs and the B
+        // half under the first sub-step of stage kt+1, while the fragments of
+        // the next sub-step are read under the MFMAs of the current one.
+        // Loads past the last stage repeat it into the free buffer.
         bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
         if (nk > 0) {
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous tile's stores retired
-            GB_LOAD(0, 0);
+            GB_SB;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                GB_LOAD_A(0, 0, i);
+                GB_LOAD_B(0, 0, i);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) GB_LOAD_A(min(1, nk - 1), 1, i);
+            __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0 landed (this wave)
             GB_ZERO_TAIL(0, 0);
-            __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            GB_READ(0, 0, f0a, f0b);
-            BWD_WAIT(f0a, f0b);
+            __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            GB_SB;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) GB_RD_A(f0a, 0, 0, mi);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) GB_RD_B(f0b, 0, 0, ni);
         }
         for (int kt = 0; kt < nk; ++kt) {
             const int st = kt & 1;
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + 1 < nk) GB_LOAD(kt + 1, st ^ 1);  // into the buffer freed by the last barrier
-            GB_READ(st, 1, f1a, f1b);
-            __builtin_amdgcn_sched_barrier(0);
-            GB_MFMAS(f0a, f0b);
-            __builtin_amdgcn_sched_barrier(0);
-            BWD_WAIT(f1a, f1b);
-            GB_READ(st, 2, f0a, f0b);
-            __builtin_amdgcn_sched_barrier(0);
-            GB_MFMAS(f1a, f1b);
-            __builtin_amdgcn_sched_barrier(0);
-            BWD_WAIT(f0a, f0b);
-            GB_READ(st, 3, f1a, f1b);
-            __builtin_amdgcn_sched_barrier(0);
-            GB_MFMAS(f0a, f0b);
-            __builtin_amdgcn_sched_barrier(0);
-            BWD_WAIT(f1a, f1b);  // this wave has read all of stage kt
+            GB_SB;
+            GB_SUBSTEP_LB(f0a, f0b, f1a, f1b, st, 1, min(kt + 1, nk - 1), st ^ 1)
+            GB_SUBSTEP(f1a, f1b, f0a, f0b, st, 2)
+            GB_SUBSTEP(f0a, f0b, f1a, f1b, st, 3)
             if (kt + 1 < nk) GB_ZERO_TAIL(kt + 1, st ^ 1);
-            // next stage landed for every wave; every wave is done with stage kt
+            // this wave read all of stage kt and its loads of stage kt+1
+            // landed; past the barrier, the same holds for every wave
             __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + 1 < nk) GB_READ(st ^ 1, 0, f0a, f0b);
-            __builtin_amdgcn_sched_barrier(0);
-            GB_MFMAS(f1a, f1b);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + 1 < nk) BWD_WAIT(f0a, f0b);
+            GB_SB;
+            GB_SUBSTEP_LA(f1a, f1b, f0a, f0b, st ^ 1, 0, min(kt + 2, nk - 1), st)
         }
-#undef GB_READ
-#undef GB_MFMAS
-#undef GB_LOAD
+        GB_SB;
+#undef GB_TAIL
+#undef GB_LOAD_A
+#undef GB_LOAD_B
 #undef GB_ZERO_TAIL
+#undef GB_RD_A
+#undef GB_RD_B
+#undef GB_MFMA
+#undef GB_SB
+#undef GB_STEP
+#undef GB_SUBSTEP_X
+#undef GB_N_
+#undef GB_SUBSTEP
+#undef GB_SUBSTEP_LA
+#undef GB_SUBSTEP_LB
         // Epilogue straight from the accumulators (no LDS): each 32 x 32 tile
         // becomes 8 pairs of adjacent columns of one row per lane (a DPP swap
         // with lane ^ 1), stored as 8-byte float32 pairs (weight gradients) or
