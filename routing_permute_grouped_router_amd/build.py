@@ -4,6 +4,7 @@ from __future__ import annotations
 import concurrent.futures as cf
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -24,13 +25,30 @@ def sources() -> list:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+# The grouped GEMM kernels count their own memory operations (s_waitcnt
+# vmcnt with fixed counts against inline-asm loads); scratch spills would add
+# memory operations the counts do not know about, so they must have none.
+_USAGE = re.compile(r"remark: Function Name: (\S+)|remark:\s+ScratchSize \[bytes/lane\]: (\d+)")
+
+
+def _check_scratch(src: str, text: str) -> None:
+    fn = None
+    for m in _USAGE.finditer(text):
+        if m.group(1):
+            fn = m.group(1)
+        elif fn and "grouped_gemm" in fn and int(m.group(2)) > 0:
+            raise RuntimeError(f"{src}: kernel {fn} spills to scratch ({m.group(2)} bytes per lane)")
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", src, "-o", obj, "-Rpass-analysis=kernel-resource-usage"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+    _check_scratch(src, r.stdout + r.stderr)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{out}")
     if out.strip() and verbose:

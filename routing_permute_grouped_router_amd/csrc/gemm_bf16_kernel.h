@@ -345,6 +345,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     GG_STEP(FA, FB, 3, 2, L7, (void)0)                                                                   \
     GG_STEP(FA, FB, 3, 3, (void)0, (void)0)
 #define GG_N_ (void)0
+// The 16 MFMAs of a sub-step with nothing riding along.
+#define GG_SUBSTEP_NR(FA, FB)                                                                            \
+    GG_WAIT_FRAGS(FA, FB);                                                                               \
+    GG_SB;                                                                                               \
+    GG_STEP(FA, FB, 0, 0, (void)0, (void)0) GG_STEP(FA, FB, 0, 1, (void)0, (void)0)                      \
+    GG_STEP(FA, FB, 0, 2, (void)0, (void)0) GG_STEP(FA, FB, 0, 3, (void)0, (void)0)                      \
+    GG_STEP(FA, FB, 1, 0, (void)0, (void)0) GG_STEP(FA, FB, 1, 1, (void)0, (void)0)                      \
+    GG_STEP(FA, FB, 1, 2, (void)0, (void)0) GG_STEP(FA, FB, 1, 3, (void)0, (void)0)                      \
+    GG_STEP(FA, FB, 2, 0, (void)0, (void)0) GG_STEP(FA, FB, 2, 1, (void)0, (void)0)                      \
+    GG_STEP(FA, FB, 2, 2, (void)0, (void)0) GG_STEP(FA, FB, 2, 3, (void)0, (void)0)                      \
+    GG_STEP(FA, FB, 3, 0, (void)0, (void)0) GG_STEP(FA, FB, 3, 1, (void)0, (void)0)                      \
+    GG_STEP(FA, FB, 3, 2, (void)0, (void)0) GG_STEP(FA, FB, 3, 3, (void)0, (void)0)
 #define GG_SUBSTEP(FA, FB, GA, GB, AD, BD)                                                               \
     GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_)
 // ... with the 8 A (B) loads of stage LKT into stage buffer LST
@@ -517,6 +529,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
                 const uint32_t bd[2] = {b_rd + nso + koff[0][0], b_rd + nso + koff[0][1]};
                 GG_SUBSTEP_LA(fa1, fb1, fa0, fb0, ad, bd, min(kt + 2, ke - 1), st)
             }
+            // the next stage's first fragments landed (they had the last 8
+            // MFMAs to do so); waiting here rather than at the top of the next
+            // iteration leaves no LDS read in flight when the loop ends
+            GG_WAIT_FRAGS(fa0, fb0);
         }
         GG_SB;
 #undef GG_LOAD_A
@@ -536,6 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #undef GG_SUBSTEP_LA
 #undef GG_SUBSTEP_LB
 #undef GG_SUBSTEP_PF
+#undef GG_SUBSTEP_NR
 
 
         // The next unit (published by thread 0 before this unit's K loop; the

@@ -369,6 +369,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
     GB_STEP(FA, FB, 3, 2, L7, (void)0)                                                                    \
     GB_STEP(FA, FB, 3, 3, (void)0, (void)0)
 #define GB_N_ (void)0
+#define GB_SUBSTEP_NR(FA, FB)                                                                             \
+    BWD_WAIT(FA, FB);                                                                                     \
+    GB_SB;                                                                                                \
+    GB_STEP(FA, FB, 0, 0, (void)0, (void)0) GB_STEP(FA, FB, 0, 1, (void)0, (void)0)                       \
+    GB_STEP(FA, FB, 0, 2, (void)0, (void)0) GB_STEP(FA, FB, 0, 3, (void)0, (void)0)                       \
+    GB_STEP(FA, FB, 1, 0, (void)0, (void)0) GB_STEP(FA, FB, 1, 1, (void)0, (void)0)                       \
+    GB_STEP(FA, FB, 1, 2, (void)0, (void)0) GB_STEP(FA, FB, 1, 3, (void)0, (void)0)                       \
+    GB_STEP(FA, FB, 2, 0, (void)0, (void)0) GB_STEP(FA, FB, 2, 1, (void)0, (void)0)                       \
+    GB_STEP(FA, FB, 2, 2, (void)0, (void)0) GB_STEP(FA, FB, 2, 3, (void)0, (void)0)                       \
+    GB_STEP(FA, FB, 3, 0, (void)0, (void)0) GB_STEP(FA, FB, 3, 1, (void)0, (void)0)                       \
+    GB_STEP(FA, FB, 3, 2, (void)0, (void)0) GB_STEP(FA, FB, 3, 3, (void)0, (void)0)
 #define GB_SUBSTEP(FA, FB, GA, GB, ST, KK)                                                                \
     GB_SUBSTEP_X(FA, FB, GA, GB, ST, KK, GB_N_, GB_N_, GB_N_, GB_N_, GB_N_, GB_N_, GB_N_, GB_N_)
 #define GB_SUBSTEP_LA(FA, FB, GA, GB, ST, KK, LKT, LST)                                                   \
@@ -419,6 +430,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
             __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
             GB_SB;
             GB_SUBSTEP_LA(f1a, f1b, f0a, f0b, st ^ 1, 0, min(kt + 2, nk - 1), st)
+            // wait for the next stage's first fragments here (they had 8 MFMAs
+            // to land), so no LDS read is in flight when the loop ends
+            BWD_WAIT(f0a, f0b);
         }
         GB_SB;
 #undef GB_TAIL
@@ -435,6 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
 #undef GB_SUBSTEP
 #undef GB_SUBSTEP_LA
 #undef GB_SUBSTEP_LB
+#undef GB_SUBSTEP_NR
         // Epilogue straight from the accumulators (no LDS): each 32 x 32 tile
         // becomes 8 pairs of adjacent columns of one row per lane (a DPP swap
         // with lane ^ 1), stored as 8-byte float32 pairs (weight gradients) or

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     __shared__ int32_t pre[kMaxExperts + 1];
     __shared__ int scan_tmp[kThreads / 64];
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1, half = lane >> 5;
     const int total_m = build_tile_prefix(p.offsets, p.E, kMxBM, pre, scan_tmp);
     const int cols_per_tile = SWIGLU ? kMxBN / 2 : kMxBN;
@@ -114,11 +114,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     for (int ni = 0; ni < 4; ++ni)
         brow[ni] = SWIGLU ? (ni < 2 ? 0 : 128) + wn * 64 + (ni & 1) * 32 + (lane & 31)
                           : wn * 128 + ni * 32 + (lane & 31);
-    uint32_t ra[2], rb[4];
+    // LDS byte address of fragment 0 of A and of B (stage 0), the row offsets
+    // of B fragments 1..3, and the lane's chunk offsets for K step sub, half hl
+    const uint32_t ra0 = lds_base + (uint32_t)arow[0] * BKB, rb0 = lds_base + A_BYTES + (uint32_t)brow[0] * BKB;
+    constexpr int kBRow[4] = {0, 32, SWIGLU ? 128 : 64, SWIGLU ? 160 : 96};
+    uint32_t kc[2][2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) ra[mi] = lds_base + arow[mi] * BKB;
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) rb[ni] = lds_base + A_BYTES + brow[ni] * BKB;
+        for (int hl = 0; hl < 2; ++hl) kc[sub][hl] = (uint32_t)((((sub * 4 + hl * 2 + half) ^ (lane & 7))) << 4);
 
     for (int t = t_begin + lb; t < t_end; t += per_xcd) {
         int mt, nt;
@@ -126,14 +130,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         // N-tile with its M-tiles adjacent: the blocks of one XCD that run at
         // the same time then cover few experts, so each weight panel is
         // fetched from HBM once and shared in L2 by all of the expert's M-tiles.
-        const int e = find_expert(pre, p.E, t / n_tiles);
+        const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, p.E, t / n_tiles));
         {
             const int m_e = pre[e + 1] - pre[e], li = t - pre[e] * n_tiles;
             nt = li / m_e;
             mt = pre[e] + li % m_e;
         }
-        const int row_end = min(p.offsets[e + 1], p.rows);
-        const int row0 = p.offsets[e] + (mt - pre[e]) * kMxBM;
+        nt = __builtin_amdgcn_readfirstlane(nt);
+        const int row_end = __builtin_amdgcn_readfirstlane(min(p.offsets[e + 1], p.rows));
+        const int row0 = __builtin_amdgcn_readfirstlane(p.offsets[e] + (mt - pre[e]) * kMxBM);
         if (row0 < 0 || row0 >= row_end) continue;  // only for inconsistent offsets
 
         auto b_row_of = [&](int r) __attribute__((always_inline)) {
@@ -159,9 +164,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         }
         const uint8_t* acodes = p.A + (size_t)row0 * K;  // A offsets are tile-relative
         const uint8_t* bcodes = p.B + (size_t)e * p.b_rows * K;
-        // scale words: A rows wid*32 + lane (lanes 0..31), B rows wid*64 + lane
-        const uint8_t* asrow = p.As + (size_t)min(row0 + wid * 32 + (lane & 31), row_end - 1) * KS;
-        const uint8_t* bsrow = p.Bs + ((size_t)e * p.b_rows + b_row_of(wid * 64 + lane)) * KS;
+        // scale words: A rows wid*32 + lane (lanes 0..31), B rows wid*64 + lane,
+        // as uniform bases plus 32-bit lane offsets
+        const uint8_t* asbase = p.As + (size_t)row0 * KS;
+        const uint8_t* bsbase = p.Bs + (size_t)e * p.b_rows * KS;
+        const uint32_t asoff = (uint32_t)((min(row0 + wid * 32 + (lane & 31), row_end - 1) - row0) * KS);
+        const uint32_t bsoff = (uint32_t)(b_row_of(wid * 64 + lane) * KS);
 
         f32x16 acc[2][4];
 #pragma unroll
@@ -171,95 +179,140 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
+        // Loads of stage kt into stage buffer slot % 3 (dma_lds16 / dma_lds4:
+        // uniform M0 and base, 32-bit lane offsets): the codes of this wave's
+        // 32 A rows (4 loads) and 64 B rows (8 loads), and the 32-bit scale
+        // words of those rows (one load each).  MX_LD(slot, kt, j) is load j
+        // of 14; slot = kt except past the end of K, where the last stage is
+        // loaded again into the free buffer.
+#define MX_LD(slot, kt, j)                                                                               \
+    {                                                                                                    \
+        const uint32_t st_ = lds_base + (uint32_t)((slot) % kMxStages) * ST_BYTES;                       \
+        if ((j) < A_LOADS)                                                                               \
+            dma_lds16(__builtin_amdgcn_readfirstlane(st_ + (wid * 32 + (j) * RPL) * BKB), aoff[(j) % A_LOADS], \
+                      acodes + (size_t)(kt) * BKB);                                                      \
+        else if ((j) < A_LOADS + B_LOADS)                                                                \
+            dma_lds16(__builtin_amdgcn_readfirstlane(st_ + A_BYTES + (wid * 64 + ((j) - A_LOADS) * RPL) * BKB), \
+                      boff[((j) - A_LOADS) % B_LOADS], bcodes + (size_t)(kt) * BKB);                      \
+        else if ((j) == A_LOADS + B_LOADS) {                                                             \
+            if (lane < 32)                                                                               \
+                dma_lds4(__builtin_amdgcn_readfirstlane(st_ + AS_OFF + wid * 32 * 4), asoff, asbase + (size_t)(kt) * 4); \
+        } else                                                                                           \
+            dma_lds4(__builtin_amdgcn_readfirstlane(st_ + BS_OFF + wid * 64 * 4), bsoff, bsbase + (size_t)(kt) * 4); \
+    }
 #define MX_ISSUE(kt)                                                                                     \
+    _Pragma("unroll") for (int j_ = 0; j_ < LPS; ++j_) MX_LD(kt, kt, j_)
+        // Fragment reads of K step `sub` (64 bytes) of the stage at byte offset
+        // so_: A fragment mi / B fragment ni from 16-byte chunks 4 sub + h and
+        // 4 sub + 2 + h of the lane's row (h = lane / 32), stored at chunk
+        // position c ^ (row & 7); row & 7 = lane & 7 for every fragment.
+#define MX_RD_A(FA, so_, sub, mi)                                                                        \
     {                                                                                                    \
-        uint8_t* st_ = lds + ((kt) % kMxStages) * ST_BYTES;                                              \
-        _Pragma("unroll") for (int i = 0; i < A_LOADS; ++i)                                              \
-            __builtin_amdgcn_global_load_lds((glb_void*)(acodes + aoff[i] + (size_t)(kt) * BKB),         \
-                                             (lds_void*)(st_ + (wid * 32 + i * RPL) * BKB), 16, 0, 0);  \
-        _Pragma("unroll") for (int i = 0; i < B_LOADS; ++i)                                              \
-            __builtin_amdgcn_global_load_lds((glb_void*)(bcodes + boff[i] + (size_t)(kt) * BKB),         \
-                                             (lds_void*)(st_ + A_BYTES + (wid * 64 + i * RPL) * BKB), 16, 0, 0); \
-        if (lane < 32)                                                                                   \
-            __builtin_amdgcn_global_load_lds((glb_void*)(asrow + (kt) * 4),                              \
-                                             (lds_void*)(st_ + AS_OFF + wid * 32 * 4), 4, 0, 0);         \
-        __builtin_amdgcn_global_load_lds((glb_void*)(bsrow + (kt) * 4),                                  \
-                                         (lds_void*)(st_ + BS_OFF + wid * 64 * 4), 4, 0, 0);             \
+        const uint4 lo_ = mx_ds_read16(ra0 + (so_) + kc[sub][0] + (mi) * 32 * BKB);                      \
+        const uint4 hi_ = mx_ds_read16(ra0 + (so_) + kc[sub][1] + (mi) * 32 * BKB);                      \
+        FA[mi] = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
     }
-        // fragments of K step `sub` (64 bytes) of stage kt: chunks 4 sub + h and 4 sub + 2 + h
-#define MX_READ(kt, sub, FA, FB)                                                                         \
+#define MX_RD_B(FB, so_, sub, ni)                                                                        \
     {                                                                                                    \
-        const uint32_t so_ = ((kt) % kMxStages) * ST_BYTES;                                              \
-        _Pragma("unroll") for (int mi = 0; mi < 2; ++mi) {                                               \
-            const uint4 lo = mx_ds_read16(ra[mi] + so_ + ((((sub) * 4 + half) ^ (arow[mi] & 7)) << 4));   \
-            const uint4 hi = mx_ds_read16(ra[mi] + so_ + ((((sub) * 4 + 2 + half) ^ (arow[mi] & 7)) << 4)); \
-            FA[mi] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w}; \
-        }                                                                                                \
-        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) {                                               \
-            const uint4 lo = mx_ds_read16(rb[ni] + so_ + ((((sub) * 4 + half) ^ (brow[ni] & 7)) << 4));   \
-            const uint4 hi = mx_ds_read16(rb[ni] + so_ + ((((sub) * 4 + 2 + half) ^ (brow[ni] & 7)) << 4)); \
-            FB[ni] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w}; \
-        }                                                                                                \
+        const uint4 lo_ = mx_ds_read16(rb0 + (so_) + kc[sub][0] + kBRow[ni] * BKB);                      \
+        const uint4 hi_ = mx_ds_read16(rb0 + (so_) + kc[sub][1] + kBRow[ni] * BKB);                      \
+        FB[ni] = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
     }
-#define MX_READ_SCALES(kt, SA, SB)                                                                       \
+        // the 32-bit scale words (one byte per 32 K values of the stage) of the lane's rows
+#define MX_RD_S(SA, SB, so_)                                                                             \
     {                                                                                                    \
-        const uint32_t so_ = lds_base + ((kt) % kMxStages) * ST_BYTES;                                   \
-        _Pragma("unroll") for (int mi = 0; mi < 2; ++mi) SA[mi] = mx_ds_read4(so_ + AS_OFF + arow[mi] * 4); \
-        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) SB[ni] = mx_ds_read4(so_ + BS_OFF + brow[ni] * 4); \
+        _Pragma("unroll") for (int mi = 0; mi < 2; ++mi) SA[mi] = mx_ds_read4(lds_base + (so_) + AS_OFF + arow[mi] * 4); \
+        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) SB[ni] = mx_ds_read4(lds_base + (so_) + BS_OFF + brow[ni] * 4); \
     }
-#define MX_WAIT(FA, FB, SA, SB)                                                                          \
+#define MX_WAIT(FA, FB)                                                                                  \
     __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
-                     : "+v"(FA[0]), "+v"(FA[1]), "+v"(FB[0]), "+v"(FB[1]), "+v"(FB[2]), "+v"(FB[3]),     \
-                       "+v"(SA[0]), "+v"(SA[1]), "+v"(SB[0]), "+v"(SB[1]), "+v"(SB[2]), "+v"(SB[3])::"memory")
-#define MX_MFMAS(FA, FB, SA, SB, sub)                                                                    \
-    _Pragma("unroll") for (int mi = 0; mi < 2; ++mi) _Pragma("unroll") for (int ni = 0; ni < 4; ++ni)   \
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                    \
-            FA[mi], FB[ni], acc[mi][ni], 0, 0, 0, (int)((SA[mi] >> (8 * (2 * (sub) + half))) & 0xffu), 0, \
-            (int)((SB[ni] >> (8 * (2 * (sub) + half))) & 0xffu));
+                     : "+v"(FA[0]), "+v"(FA[1]), "+v"(FB[0]), "+v"(FB[1]), "+v"(FB[2]), "+v"(FB[3])::"memory")
+#define MX_WAIT_S(SA, SB)                                                                                \
+    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
+                     : "+v"(SA[0]), "+v"(SA[1]), "+v"(SB[0]), "+v"(SB[1]), "+v"(SB[2]), "+v"(SB[3])::"memory")
+        // One MFMA of K step SUB: the scale words were shifted right by 8 h, so
+        // the byte of 32-block 2 SUB + h is byte 2 SUB for every lane (opsel).
+#define MX_MFMA(FA, FB, SA, SB, SUB, mi, ni)                                                             \
+    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(FA[mi], FB[ni], acc[mi][ni], 0, 0, 2 * (SUB), \
+                                                                  (int)SA[mi], 2 * (SUB), (int)SB[ni])
+#define MX_SB __builtin_amdgcn_sched_barrier(0)
+#define MX_STEP(PRE, MF, RD)                                                                             \
+    PRE;                                                                                                 \
+    MF;                                                                                                  \
+    RD;                                                                                                  \
+    MX_SB;
 
+        const int KT_ = nk;  // stages
+        // prologue: stages 0 and 1 in flight, stage 0 landed everywhere
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous tile's stores retired
+        MX_SB;
         MX_ISSUE(0);
-        if (nk > 1) MX_ISSUE(1);
-        if (nk > 1) __asm__ volatile("s_waitcnt vmcnt(14)" ::: "memory");  // stage 0 landed
-        else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        mx_barrier();
+        _Pragma("unroll") for (int j_ = 0; j_ < LPS; ++j_) MX_LD(1, min(1, KT_ - 1), j_)
+        __asm__ volatile("s_waitcnt vmcnt(14)\n\ts_barrier" ::: "memory");
+        MX_SB;
         i32x8 f0a[2], f0b[4], f1a[2], f1b[4];
         uint32_t s0a[2], s0b[4], s1a[2], s1b[4];
-        MX_READ(0, 0, f0a, f0b);
-        MX_READ_SCALES(0, s0a, s0b);
-        MX_WAIT(f0a, f0b, s0a, s0b);
-        for (int kt = 0; kt < nk; ++kt) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + 2 < nk) MX_ISSUE(kt + 2);  // into the buffer of stage kt-1, free since the last barrier
-            MX_READ(kt, 1, f1a, f1b);
-            __builtin_amdgcn_sched_barrier(0);
-            MX_MFMAS(f0a, f0b, s0a, s0b, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            MX_WAIT(f1a, f1b, s0a, s0b);  // this wave has read all of stage kt
-            if (kt + 2 < nk) __asm__ volatile("s_waitcnt vmcnt(14)" ::: "memory");  // stage kt+1 landed
-            else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            mx_barrier();  // ... for every wave, and every wave is done with stage kt
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + 1 < nk) {
-                MX_READ(kt + 1, 0, f0a, f0b);
-                MX_READ_SCALES(kt + 1, s1a, s1b);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            MX_MFMAS(f1a, f1b, s0a, s0b, 1);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + 1 < nk) {
-                MX_WAIT(f0a, f0b, s1a, s1b);
+        MX_RD_A(f0a, 0u, 0, 0) MX_RD_A(f0a, 0u, 0, 1)
+        MX_RD_B(f0b, 0u, 0, 0) MX_RD_B(f0b, 0u, 0, 1) MX_RD_B(f0b, 0u, 0, 2) MX_RD_B(f0b, 0u, 0, 3)
+        MX_RD_S(s1a, s1b, 0u)
+        for (int kt = 0; kt < KT_; ++kt) {
+            const uint32_t so = (uint32_t)(kt % kMxStages) * ST_BYTES;
+            const uint32_t sn = (uint32_t)((kt + 1) % kMxStages) * ST_BYTES;
+            const int kl = min(kt + 2, KT_ - 1);  // loads of stage kt+2 (past the end: the last stage again)
+            MX_SB;
+            // this stage's scale words, shifted so byte 2 s holds 32-block 2 s + h
+            MX_WAIT_S(s1a, s1b);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) s0a[i] = s1a[i];
+            for (int i = 0; i < 2; ++i) s0a[i] = s1a[i] >> (8 * half);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s0b[i] = s1b[i];
-            }
+            for (int i = 0; i < 4; ++i) s0b[i] = s1b[i] >> (8 * half);
+            MX_WAIT(f0a, f0b);
+            MX_SB;
+            // K step 0: 8 MFMAs; the fragments of step 1 and loads 0..6 of stage kt+2 ride along
+            MX_STEP(MX_LD(kt + 2, kl, 0), MX_MFMA(f0a, f0b, s0a, s0b, 0, 0, 0), MX_RD_A(f1a, so, 1, 0))
+            MX_STEP(MX_LD(kt + 2, kl, 1), MX_MFMA(f0a, f0b, s0a, s0b, 0, 0, 1), MX_RD_A(f1a, so, 1, 1))
+            MX_STEP(MX_LD(kt + 2, kl, 2), MX_MFMA(f0a, f0b, s0a, s0b, 0, 0, 2), MX_RD_B(f1b, so, 1, 0))
+            MX_STEP(MX_LD(kt + 2, kl, 3), MX_MFMA(f0a, f0b, s0a, s0b, 0, 0, 3), MX_RD_B(f1b, so, 1, 1))
+            MX_STEP(MX_LD(kt + 2, kl, 4), MX_MFMA(f0a, f0b, s0a, s0b, 0, 1, 0), MX_RD_B(f1b, so, 1, 2))
+            MX_STEP(MX_LD(kt + 2, kl, 5), MX_MFMA(f0a, f0b, s0a, s0b, 0, 1, 1), MX_RD_B(f1b, so, 1, 3))
+            MX_STEP(MX_LD(kt + 2, kl, 6), MX_MFMA(f0a, f0b, s0a, s0b, 0, 1, 2), (void)0)
+            MX_STEP((void)0, MX_MFMA(f0a, f0b, s0a, s0b, 0, 1, 3), (void)0)
+            MX_WAIT(f1a, f1b);  // this wave has read all of stage kt
+            // stage kt+1 landed (only the 7 loads of stage kt+2 just issued may
+            // be in flight); past the barrier the same holds for every wave and
+            // the buffer of stage kt is free
+            __asm__ volatile("s_waitcnt vmcnt(7)\n\ts_barrier" ::: "memory");
+            MX_SB;
+            // K step 1: 8 MFMAs; step 0 and the scale words of stage kt+1 and
+            // loads 7..13 of stage kt+2 ride along
+            MX_STEP(MX_LD(kt + 2, kl, 7), MX_MFMA(f1a, f1b, s0a, s0b, 1, 0, 0), MX_RD_A(f0a, sn, 0, 0))
+            MX_STEP(MX_LD(kt + 2, kl, 8), MX_MFMA(f1a, f1b, s0a, s0b, 1, 0, 1), MX_RD_A(f0a, sn, 0, 1))
+            MX_STEP(MX_LD(kt + 2, kl, 9), MX_MFMA(f1a, f1b, s0a, s0b, 1, 0, 2), MX_RD_B(f0b, sn, 0, 0))
+            MX_STEP(MX_LD(kt + 2, kl, 10), MX_MFMA(f1a, f1b, s0a, s0b, 1, 0, 3), MX_RD_B(f0b, sn, 0, 1))
+            MX_STEP(MX_LD(kt + 2, kl, 11), MX_MFMA(f1a, f1b, s0a, s0b, 1, 1, 0), MX_RD_B(f0b, sn, 0, 2))
+            MX_STEP(MX_LD(kt + 2, kl, 12), MX_MFMA(f1a, f1b, s0a, s0b, 1, 1, 1), MX_RD_B(f0b, sn, 0, 3))
+            MX_STEP(MX_LD(kt + 2, kl, 13), MX_MFMA(f1a, f1b, s0a, s0b, 1, 1, 2), MX_RD_S(s1a, s1b, sn))
+            MX_STEP((void)0, MX_MFMA(f1a, f1b, s0a, s0b, 1, 1, 3), (void)0)
+            // wait for the next stage's step-0 fragments and scale words here
+            // (they had the last MFMAs to land), so no LDS read is in flight
+            // when the loop ends
+            MX_WAIT(f0a, f0b);
+            MX_WAIT_S(s1a, s1b);
         }
+        MX_SB;
+        // every wave passed the last barrier after reading its last stage, and
+        // its last loads (repeats of the last stage) went to the free buffer
+        __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // LDS free for the epilogue
+#undef MX_LD
 #undef MX_ISSUE
-#undef MX_READ
-#undef MX_READ_SCALES
+#undef MX_RD_A
+#undef MX_RD_B
+#undef MX_RD_S
 #undef MX_WAIT
-#undef MX_MFMAS
+#undef MX_WAIT_S
+#undef MX_MFMA
+#undef MX_SB
+#undef MX_STEP
         // every wave passed the last barrier after reading its last stage: LDS is free
 
         // epilogue through LDS: lane -> row rr, columns cc .. cc+15 of a 32x32 tile
