@@ -56,16 +56,19 @@ __global__ void zero_sched_kernel(int* sched) {
     if (threadIdx.x < gemm::kXcds) sched[threadIdx.x] = 0;
 }
 
-// Split tile j of XCD blockIdx.y (j = blockIdx.x): the float32 partial sums
-// of its S K-parts are added in part order, then the epilogue of the grouped
-// GEMM is applied (SwiGLU: h = silu(g) * u rounded to bf16, plus the g | u
-// stash; down: rounding to bf16).  The queue layout is recomputed from the
-// same offsets and block count as the GEMM launch.
+// Rows [32 c, 32 c + 32) of split tile j of XCD blockIdx.y (blockIdx.x =
+// 8 j + c): the float32 partial sums of its S K-parts are added in part
+// order, then the epilogue of the grouped GEMM is applied (SwiGLU: h =
+// silu(g) * u rounded to bf16, plus the g | u stash; down: rounding to bf16).
+// The queue layout is recomputed from the same offsets and block count as the
+// GEMM launch.
+constexpr int kReduceRows = 32;
 template <bool SWIGLU, int GM>
 __global__ __launch_bounds__(256) void split_reduce_bf16(gemm::Args p, int nb) {
     __shared__ int32_t pre[kMaxExperts + 1];
     __shared__ int scan_tmp[256 / 64];
-    const int x = blockIdx.y, j = blockIdx.x;
+    constexpr int kChunks = gemm::kTile / kReduceRows;
+    const int x = blockIdx.y, j = blockIdx.x / kChunks, c = blockIdx.x % kChunks;
     const int nk = p.K / 64;
     const int total_m = build_tile_prefix(p.offsets, p.E, gemm::kTile, pre, scan_tmp);
     const int cols_per_tile = SWIGLU ? gemm::kTile / 2 : gemm::kTile;
@@ -78,43 +81,43 @@ __global__ __launch_bounds__(256) void split_reduce_bf16(gemm::Args p, int nb) {
     const int row_end = min(p.offsets[e + 1], p.rows);
     const int row0 = p.offsets[e] + (mt - pre[e]) * gemm::kTile;
     if (row0 < 0 || row0 >= row_end) return;
-    const int rows = min(gemm::kTile, row_end - row0);
+    const int r_lo = c * kReduceRows, r_hi = min(r_lo + kReduceRows, row_end - row0);
+    if (r_lo >= r_hi) return;
     constexpr int kPart = gemm::kTile * gemm::kTile;
     const float* part = p.part + (size_t)(x * gemm::kSlotsPerXcd + j * q.S) * kPart;
-    if (SWIGLU) {
-        // 128 gate columns (partial columns 0..127) and their up columns (128..255)
-        for (int i = threadIdx.x; i < rows * 32; i += blockDim.x) {
-            const int r = i >> 5, c = (i & 31) * 4;
-            const int f = nt * 128 + c;
-            if (f >= p.n_out) continue;
-            float4 g = *(const float4*)(part + r * gemm::kTile + c);
-            float4 u = *(const float4*)(part + r * gemm::kTile + 128 + c);
-            for (int s = 1; s < q.S; ++s) {
-                const float4 g2 = *(const float4*)(part + (size_t)s * kPart + r * gemm::kTile + c);
-                const float4 u2 = *(const float4*)(part + (size_t)s * kPart + r * gemm::kTile + 128 + c);
-                g.x += g2.x; g.y += g2.y; g.z += g2.z; g.w += g2.w;
-                u.x += u2.x; u.y += u2.y; u.z += u2.z; u.w += u2.w;
-            }
-            const size_t row = (size_t)(row0 + r);
-            *(uint2*)(p.C + row * p.n_out + f) = make_uint2(pack_bf16x2(silu(g.x) * u.x, silu(g.y) * u.y),
-                                                            pack_bf16x2(silu(g.z) * u.z, silu(g.w) * u.w));
-            if (p.stash) {
-                *(uint2*)(p.stash + row * 2 * p.n_out + f) = make_uint2(pack_bf16x2(g.x, g.y), pack_bf16x2(g.z, g.w));
-                *(uint2*)(p.stash + row * 2 * p.n_out + p.n_out + f) =
-                    make_uint2(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w));
+    constexpr int kQuads = SWIGLU ? 32 : 64;  // float4 columns per row handled here
+    for (int i = threadIdx.x; i < (r_hi - r_lo) * kQuads; i += blockDim.x) {
+        const int r = r_lo + i / kQuads, col = (i % kQuads) * 4;
+        const int n = nt * cols_per_tile + col;
+        if (n >= p.n_out) continue;
+        // all parts' loads first, then the sums in part order
+        float4 v[gemm::kMaxSplit], w[gemm::kMaxSplit];
+#pragma unroll
+        for (int s = 0; s < gemm::kMaxSplit; ++s) {
+            if (s < q.S) {
+                v[s] = *(const float4*)(part + (size_t)s * kPart + r * gemm::kTile + col);
+                if (SWIGLU) w[s] = *(const float4*)(part + (size_t)s * kPart + r * gemm::kTile + 128 + col);
             }
         }
-    } else {
-        for (int i = threadIdx.x; i < rows * 64; i += blockDim.x) {
-            const int r = i >> 6, c = (i & 63) * 4;
-            const int n = nt * gemm::kTile + c;
-            if (n >= p.n_out) continue;
-            float4 v = *(const float4*)(part + r * gemm::kTile + c);
-            for (int s = 1; s < q.S; ++s) {
-                const float4 v2 = *(const float4*)(part + (size_t)s * kPart + r * gemm::kTile + c);
-                v.x += v2.x; v.y += v2.y; v.z += v2.z; v.w += v2.w;
+        float4 g = v[0], u = SWIGLU ? w[0] : v[0];
+#pragma unroll
+        for (int s = 1; s < gemm::kMaxSplit; ++s) {
+            if (s < q.S) {
+                g.x += v[s].x; g.y += v[s].y; g.z += v[s].z; g.w += v[s].w;
+                if (SWIGLU) { u.x += w[s].x; u.y += w[s].y; u.z += w[s].z; u.w += w[s].w; }
             }
-            *(uint2*)(p.C + (size_t)(row0 + r) * p.n_out + n) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        }
+        const size_t row = (size_t)(row0 + r);
+        if (SWIGLU) {
+            *(uint2*)(p.C + row * p.n_out + n) = make_uint2(pack_bf16x2(silu(g.x) * u.x, silu(g.y) * u.y),
+                                                            pack_bf16x2(silu(g.z) * u.z, silu(g.w) * u.w));
+            if (p.stash) {
+                *(uint2*)(p.stash + row * 2 * p.n_out + n) = make_uint2(pack_bf16x2(g.x, g.y), pack_bf16x2(g.z, g.w));
+                *(uint2*)(p.stash + row * 2 * p.n_out + p.n_out + n) =
+                    make_uint2(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w));
+            }
+        } else {
+            *(uint2*)(p.C + row * p.n_out + n) = make_uint2(pack_bf16x2(g.x, g.y), pack_bf16x2(g.z, g.w));
         }
     }
 }
@@ -126,7 +129,8 @@ hipError_t launch_bf16(gemm::Args a, int64_t max_tiles, void* ws, hipStream_t s)
     a.part = (float*)((char*)ws + 256);
     zero_sched_kernel<<<1, 64, 0, s>>>(a.sched);
     gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM><<<grid, gemm::kThreads, 0, s>>>(a);
-    split_reduce_bf16<SWIGLU, kGroupM><<<dim3(gemm::kSlotsPerXcd, gemm::kXcds), 256, 0, s>>>(a, grid / gemm::kXcds);
+    split_reduce_bf16<SWIGLU, kGroupM><<<dim3(gemm::kSlotsPerXcd * (gemm::kTile / kReduceRows), gemm::kXcds), 256, 0, s>>>(
+        a, grid / gemm::kXcds);
     return hipGetLastError();
 }
 
