@@ -16,8 +16,9 @@
 namespace moe {
 namespace {
 
-// Tuned on MI355X with the Mixtral-shaped and fine-grained layers.
-constexpr int kSwizzle = 0, kGroupM = 4;
+// Tuned on MI355X with the Mixtral-shaped and fine-grained layers (kGroupM = 0:
+// tiles expert by expert, each weight panel streamed once).
+constexpr int kSwizzle = 0, kGroupM = 0;
 
 int g_num_cus = 0;
 
@@ -75,9 +76,8 @@ __global__ __launch_bounds__(256) void split_reduce_bf16(gemm::Args p, int nb) {
     const int n_tiles = (p.n_out + cols_per_tile - 1) / cols_per_tile;
     const gemm::Queue q = gemm::xcd_queue(total_m * n_tiles, x, nb, nk);
     if (q.S < 2 || j >= (q.units - q.whole) / q.S) return;
-    int mt, nt;
-    tile_coords(q.tb + q.whole + j, total_m, n_tiles, GM, &mt, &nt);
-    const int e = find_expert(pre, p.E, mt);
+    int mt, nt, e;
+    tile_of(q.tb + q.whole + j, pre, p.E, total_m, n_tiles, GM, &e, &mt, &nt);
     const int row_end = min(p.offsets[e + 1], p.rows);
     const int row0 = p.offsets[e] + (mt - pre[e]) * gemm::kTile;
     if (row0 < 0 || row0 >= row_end) return;

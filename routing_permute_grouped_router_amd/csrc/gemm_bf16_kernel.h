@@ -205,7 +205,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][STAGE_ELEMS];
     __shared__ int32_t pre[kMaxExperts + 1];
     __shared__ int32_t offs[kMaxExperts + 1];  // the group offsets, read once per block
-    __shared__ uint32_t pf_sink[64];           // landing slot of the L2 prefetches (never read)
     __shared__ int scan_tmp[kThreads / 64];
     __shared__ Queue queues[kXcds];
     __shared__ int s_unit;                     // the block's next work unit (thread 0 claims it)
@@ -264,7 +263,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     constexpr uint32_t kStageBytes = 2 * STAGE_ELEMS * 2;
     // LDS rows this wave's loads fill: wid * 64 .. +63 of each operand
     const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(wid * 64 * BK * 2));
-    const uint32_t pf_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)pf_sink);
     const uint32_t a_rd = lds_base + (uint32_t)((wm * 128 + (lane & 31)) * BK * 2);
     const uint32_t b_rd = lds_base + (uint32_t)(STAGE_ELEMS * 2 + (SWIGLU ? wn * 64 : wn * 128) * BK * 2 +
                                                 (lane & 31) * BK * 2);
@@ -278,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     // [kb, ke), partial-sum slot (-1: whole tile), load offsets and bases.
     int kb = 0, ke = 0, slot = -1, row0 = 0, row_end = 0, nt = 0;
     bool valid = false;
-    uint32_t aoff[LOADS], boff[LOADS], apf = 0, bpf = 0;
+    uint32_t aoff[LOADS], boff[LOADS];
     const char* abase = (const char*)p.A;
     const char* bbase = (const char*)p.B;
 #define GG_LOAD_A(kt, stage, i)                                                                          \
@@ -291,12 +289,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         GG_LOAD_A(kt, stage, i);                                                                         \
         GG_LOAD_B(kt, stage, i);                                                                         \
     }
-// Pull the 128-byte K segment of stage kt of this wave's 64 A rows (B rows)
-// into L2: 4 bytes per lane, one row per lane, into a sink slot of LDS that
-// nothing reads.  The loads of that stage, issued a stage and a half later,
-// then hit in L2.
-#define GG_PREFETCH_A(kt) dma_lds4(pf_lds, apf, abase + (size_t)(kt) * (BK * 2))
-#define GG_PREFETCH_B(kt) dma_lds4(pf_lds, bpf, bbase + (size_t)(kt) * (BK * 2))
 // Wait until every LDS read issued so far has landed; the fragment registers
 // are tied to the wait so no MFMA that uses them moves above it.
 #define GG_WAIT_FRAGS(FA, FB)                                                                            \
@@ -345,18 +337,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     GG_STEP(FA, FB, 3, 2, L7, (void)0)                                                                   \
     GG_STEP(FA, FB, 3, 3, (void)0, (void)0)
 #define GG_N_ (void)0
-// The 16 MFMAs of a sub-step with nothing riding along.
-#define GG_SUBSTEP_NR(FA, FB)                                                                            \
-    GG_WAIT_FRAGS(FA, FB);                                                                               \
-    GG_SB;                                                                                               \
-    GG_STEP(FA, FB, 0, 0, (void)0, (void)0) GG_STEP(FA, FB, 0, 1, (void)0, (void)0)                      \
-    GG_STEP(FA, FB, 0, 2, (void)0, (void)0) GG_STEP(FA, FB, 0, 3, (void)0, (void)0)                      \
-    GG_STEP(FA, FB, 1, 0, (void)0, (void)0) GG_STEP(FA, FB, 1, 1, (void)0, (void)0)                      \
-    GG_STEP(FA, FB, 1, 2, (void)0, (void)0) GG_STEP(FA, FB, 1, 3, (void)0, (void)0)                      \
-    GG_STEP(FA, FB, 2, 0, (void)0, (void)0) GG_STEP(FA, FB, 2, 1, (void)0, (void)0)                      \
-    GG_STEP(FA, FB, 2, 2, (void)0, (void)0) GG_STEP(FA, FB, 2, 3, (void)0, (void)0)                      \
-    GG_STEP(FA, FB, 3, 0, (void)0, (void)0) GG_STEP(FA, FB, 3, 1, (void)0, (void)0)                      \
-    GG_STEP(FA, FB, 3, 2, (void)0, (void)0) GG_STEP(FA, FB, 3, 3, (void)0, (void)0)
 #define GG_SUBSTEP(FA, FB, GA, GB, AD, BD)                                                               \
     GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_)
 // ... with the 8 A (B) loads of stage LKT into stage buffer LST
@@ -368,18 +348,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_LOAD_B(LKT, LST, 0), GG_LOAD_B(LKT, LST, 1),                 \
                  GG_LOAD_B(LKT, LST, 2), GG_LOAD_B(LKT, LST, 3), GG_LOAD_B(LKT, LST, 4),                 \
                  GG_LOAD_B(LKT, LST, 5), GG_LOAD_B(LKT, LST, 6), GG_LOAD_B(LKT, LST, 7))
-// ... with the L2 prefetch of stage PKT
-#define GG_SUBSTEP_PF(FA, FB, GA, GB, AD, BD, PKT)                                                       \
-    GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_PREFETCH_A(PKT), GG_PREFETCH_B(PKT), GG_N_, GG_N_, GG_N_,    \
-                 GG_N_, GG_N_, GG_N_)
 
     // Decode unit u (from `take`), compute its tile's addressing and issue
-    // the loads of its first stage, the A half of its second and the L2
-    // prefetch of its third (stage buffers 0 and 1).  Called right after the
+    // the loads of its first stage and the A half of its second (stage
+    // buffers 0 and 1).  Called right after the
     // previous unit's K loop, so these loads are in flight while that unit's
     // epilogue runs.  A wave's loads land in issue order, after the previous
     // unit's last (repeated) loads of the same rows.
     auto setup = [&](int u) __attribute__((always_inline)) {
+        u = __builtin_amdgcn_readfirstlane(u);
+        if (u < 0) {  // no unit (every queue used up): nothing to decode or load
+            valid = false;
+            kb = ke = 0;
+            return;
+        }
         const int ux = __builtin_amdgcn_readfirstlane(u >> 20), uu = __builtin_amdgcn_readfirstlane(u & 0xFFFFF);
         const Queue q = queues[ux];
         int t;
@@ -400,10 +382,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         kb = __builtin_amdgcn_readfirstlane(kb);
         ke = __builtin_amdgcn_readfirstlane(ke);
         slot = __builtin_amdgcn_readfirstlane(slot);
-        int mt, ntt;
-        tile_coords(t, total_m, n_tiles, GM, &mt, &ntt);
+        int mt, ntt, ee;
+        tile_of(t, pre, p.E, total_m, n_tiles, GM, &ee, &mt, &ntt);
         nt = __builtin_amdgcn_readfirstlane(ntt);
-        const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, p.E, mt));
+        mt = __builtin_amdgcn_readfirstlane(mt);
+        const int e = __builtin_amdgcn_readfirstlane(ee);
         row_end = __builtin_amdgcn_readfirstlane(min(offs[e + 1], p.rows));
         row0 = __builtin_amdgcn_readfirstlane(offs[e] + (mt - pre[e]) * kTile);
         // row0 outside [0, row_end) only happens for inconsistent offsets: the
@@ -434,26 +417,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         }
         abase = (const char*)(p.A + (size_t)row0 * K);
         bbase = (const char*)(p.B + ((size_t)e * p.b_rows + brow0) * K);
-        // L2 prefetch: lane l of wave w touches the K segment of a stage in
-        // tile row w * 64 + l of A and of B (the rows this wave loads).
-        {
-            const int r = wid * 64 + lane;
-            apf = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K * 2);
-            int br;
-            if (SWIGLU) {
-                const int f = min(nt * 128 + (r & 127), p.n_out - 1);
-                br = r < 128 ? f : p.n_out + f;
-            } else {
-                br = min(nt * kTile + r, p.n_out - 1);
-            }
-            bpf = (uint32_t)((size_t)(br - brow0) * K * 2);
-        }
         GG_SB;
         GG_ISSUE(kb, 0);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) GG_LOAD_A(min(kb + 1, ke - 1), 1, i);
-        GG_PREFETCH_A(min(kb + 2, ke - 1));
-        GG_PREFETCH_B(min(kb + 2, ke - 1));
         GG_SB;
     };
 
@@ -467,10 +434,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         // landed; once every wave is past it the buffer of stage kt is free.
         // The loads of stage kt+2 go into it, the A half during the last
         // sub-step of stage kt and the B half during the first sub-step of
-        // stage kt+1 (so the address unit is never oversubscribed), and the
-        // L2 prefetch of stage kt+3 rides on the second sub-step.  Loads past
-        // the end of K repeat the last stage into the free buffer, so the loop
-        // has no branch.
+        // stage kt+1 (so the address unit is never oversubscribed).  Loads
+        // past the end of K repeat the last stage into the free buffer, so
+        // the loop has no branch.  (An L2 prefetch of later stages, one
+        // 4-byte load per row, cost more address-unit time than it saved.)
         bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
         // the unit's first stage landed everywhere; the previous unit's stores retired
         __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -511,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             {
                 const uint32_t ad[2] = {a_rd + so + koff[2][0], a_rd + so + koff[2][1]};
                 const uint32_t bd[2] = {b_rd + so + koff[2][0], b_rd + so + koff[2][1]};
-                GG_SUBSTEP_PF(fa1, fb1, fa0, fb0, ad, bd, min(kt + 3, ke - 1))
+                GG_SUBSTEP(fa1, fb1, fa0, fb0, ad, bd)
             }
             {
                 const uint32_t ad[2] = {a_rd + so + koff[3][0], a_rd + so + koff[3][1]};
@@ -519,9 +486,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
                 GG_SUBSTEP(fa0, fb0, fa1, fb1, ad, bd)
             }
             // this wave has read all of stage kt and its loads of stage kt+1
-            // landed (only the two prefetches may still be in flight); past
-            // the barrier, the same holds for every wave
-            __asm__ volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            // landed; past the barrier, the same holds for every wave
+            __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
             GG_SB;
             {
                 const uint32_t nso = so ^ kStageBytes;
@@ -538,8 +504,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #undef GG_LOAD_A
 #undef GG_LOAD_B
 #undef GG_ISSUE
-#undef GG_PREFETCH_A
-#undef GG_PREFETCH_B
 #undef GG_WAIT_FRAGS
 #undef GG_MFMA
 #undef GG_RD_A
@@ -551,8 +515,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #undef GG_SUBSTEP
 #undef GG_SUBSTEP_LA
 #undef GG_SUBSTEP_LB
-#undef GG_SUBSTEP_PF
-#undef GG_SUBSTEP_NR
 
 
         // The next unit (published by thread 0 before this unit's K loop; the

@@ -101,6 +101,14 @@ __device__ __forceinline__ int find_expert(const int32_t* pre, int E, int mt) {
     return lo;
 }
 
+// Tile t of a grouped GEMM: its expert e, M-tile mt (global index) and
+// N-tile nt.  GM > 0: runs of GM consecutive M-tiles sweep all N-tiles, so
+// blocks running together share both A rows and B columns in L2.  GM == 0:
+// expert by expert, and within an expert N-tile by N-tile with the expert's
+// M-tiles adjacent, so the blocks running together cover few experts and each
+// weight panel is streamed from HBM once per expert.
+__device__ __forceinline__ void tile_of(int t, const int32_t* pre, int E, int total_m, int n_tiles, int GM, int* e,
+                                        int* mt, int* nt);
 // Grouped launch order: runs of GM consecutive M-tiles sweep all N-tiles, so
 // blocks running together share both A rows and B columns in L2.
 __device__ __forceinline__ void tile_coords(int t, int total_m, int n_tiles, int GM, int* mt, int* nt) {
@@ -109,6 +117,20 @@ __device__ __forceinline__ void tile_coords(int t, int total_m, int n_tiles, int
     const int gm = min(GM, total_m - sr * GM);
     *nt = rem / gm;
     *mt = sr * GM + rem % gm;
+}
+
+__device__ __forceinline__ void tile_of(int t, const int32_t* pre, int E, int total_m, int n_tiles, int GM, int* e,
+                                        int* mt, int* nt) {
+    if (GM > 0) {
+        tile_coords(t, total_m, n_tiles, GM, mt, nt);
+        *e = find_expert(pre, E, *mt);
+    } else {
+        const int x = find_expert(pre, E, t / n_tiles);
+        const int m_e = pre[x + 1] - pre[x], li = t - pre[x] * n_tiles;
+        *e = x;
+        *nt = li / m_e;
+        *mt = pre[x] + li % m_e;
+    }
 }
 
 }  // namespace moe
