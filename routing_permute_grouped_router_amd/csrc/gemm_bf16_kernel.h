@@ -162,6 +162,18 @@ __device__ __forceinline__ void pair_f32(const float (&v)[16], int lane, float2 
     }
 }
 
+// Output column of B row r of a forward tile (tile-relative).  A wavefront
+// reads B fragment ni of its column half wn from LDS rows wn 128 + 32 ni + c
+// (c = 0..31), and MFMA lane l holds column c = l % 32 of every fragment; with
+// row wn 128 + 32 ni + c carrying output column wn 128 + 4 c + ni, lane l ends
+// up with the four adjacent columns 4 c .. 4 c + 3 of each of its rows, one
+// from each fragment, and stores them as one 8-byte word with no lane
+// exchange.  SwiGLU tiles (gate rows 0..127, up rows 128..255; fragments 0, 1
+// of half wn at rows wn 64 + 32 ni + c): h column wn 64 + 2 c + ni, so each
+// lane holds two adjacent h columns.
+__device__ __forceinline__ int out_col(int r) { return (r & 128) + 4 * (r & 31) + ((r >> 5) & 3); }
+__device__ __forceinline__ int out_col_swiglu(int h) { return (h & 64) + 2 * (h & 31) + ((h >> 5) & 1); }
+
 // One 16-byte MFMA operand fragment from LDS.  Issued as inline assembly so
 // the compiler neither reorders it nor makes it wait for the direct-to-LDS
 // loads into the other stage buffer (it cannot prove that they do not
@@ -408,10 +420,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             aoff[i] = (uint32_t)(((size_t)(ar - row0) * K + chunk * 8) * 2);
             int br;
             if (SWIGLU) {
-                const int f = min(nt * 128 + (r & 127), p.n_out - 1);
+                const int f = min(nt * 128 + out_col_swiglu(r & 127), p.n_out - 1);
                 br = r < 128 ? f : p.n_out + f;
             } else {
-                br = min(nt * kTile + r, p.n_out - 1);
+                br = min(nt * kTile + out_col(r), p.n_out - 1);
             }
             boff[i] = (uint32_t)(((size_t)(br - brow0) * K + chunk * 8) * 2);
         }
@@ -526,30 +538,32 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         const bool e_valid = valid;
         if (next_unit >= 0) setup(next_unit);
         if (e_valid) {
-        // Epilogue straight from the accumulators: each 32 x 32 tile becomes 8
-        // bf16 pairs per lane (two adjacent columns of one row, one DPP lane
-        // swap per pair), stored as 4-byte words; 32 lanes cover 128
-        // contiguous bytes of a row.  No LDS, so no barrier before the next tile.
-        // Opaque copies of the tile's first row and of the lane index: the
-        // address arithmetic below then stays after the K loop (it is not
-        // hoisted out of the tile loop, where it would hold registers).
+        // Epilogue straight from the accumulators (no LDS, so no barrier
+        // before the next tile).  With the column order of the B rows above,
+        // lane l holds, for each of its 16 rows of a 32-row block, adjacent
+        // output columns in its four (SwiGLU: two) fragments: one 8-byte word
+        // of four bf16 (SwiGLU: a 4-byte pair of h), so 32 lanes cover 256
+        // (128) contiguous bytes of a row.  Opaque copies of the tile's first
+        // row and of the lane index: the address arithmetic below then stays
+        // after the K loop (it is not hoisted out of the tile loop, where it
+        // would hold registers).
         int rbase = e_row0, ln = lane;
         __asm__ volatile("" : "+v"(rbase), "+v"(ln));
-        const int c2 = (ln & 31) & ~1;                // even column of this lane's pairs
-        const int prow = 4 * (ln >> 5) + (ln & 1);    // row of this lane's pair 0 in a 32-row block
+        const int lc = ln & 31;             // this lane's column group
+        const int lr = 4 * (ln >> 5);       // this lane's first row in a 32-row block
         const int rlim = e_row_end - rbase;  // rows of the tile that exist
-        const uint32_t ldw = (uint32_t)p.n_out / 2;  // 4-byte words per output row
-        // Store the 8 pairs of a 32-row block whose first row (tile-relative) is
-        // RB0 from word pointer DST (this lane's pair-0 address), LDW words per
-        // row; the rows are checked only when the block runs past the group's end.
-#define GB_STORE_PAIRS(DST, LDW, RB0, VP)                                                                \
+        // Store W[q] (type T) to row 8 (q / 4) + q % 4 past DST (LD elements
+        // per row) for q = 0..15: the lane's rows of the 32-row block starting
+        // at tile row RB0; rows are checked only when the block runs past the
+        // group's end.
+#define GB_STORE_ROWS(T, DST, LD, RB0, W)                                                                \
     if ((RB0) + 32 <= rlim) {                                                                            \
-        _Pragma("unroll") for (int q = 0; q < 8; ++q)                                                    \
-            (DST)[(8 * (q >> 1) + 2 * (q & 1)) * (LDW)] = (VP)[q];                                       \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
+            *(T*)((DST) + (size_t)(8 * (q >> 2) + (q & 3)) * (LD)) = (W)[q];                             \
     } else {                                                                                             \
-        _Pragma("unroll") for (int q = 0; q < 8; ++q)                                                    \
-            if ((RB0) + prow + 8 * (q >> 1) + 2 * (q & 1) < rlim)                                        \
-                (DST)[(8 * (q >> 1) + 2 * (q & 1)) * (LDW)] = (VP)[q];                                   \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
+            if ((RB0) + lr + 8 * (q >> 2) + (q & 3) < rlim)                                              \
+                *(T*)((DST) + (size_t)(8 * (q >> 2) + (q & 3)) * (LD)) = (W)[q];                         \
     }
 
         if (e_slot >= 0) {
@@ -558,80 +572,85 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             // included; the reduction skips them), in [row][column] order with
             // SwiGLU gate columns 0..127 and up columns 128..255
             float* const pb = p.part + (size_t)e_slot * kTile * kTile;
-#define GB_EPI_PART(MI, NI)                                                                              \
+#define GB_EPI_PART(MI)                                                                                  \
     {                                                                                                    \
-        const int col = (SWIGLU ? ((NI) < 2 ? 0 : 128) + wn * 64 + ((NI) & 1) * 32 : wn * 128 + (NI) * 32) + c2; \
         const int rb0 = wm * 128 + (MI) * 32;                                                            \
-        float v[16];                                                                                     \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
-        float2 vp[8];                                                                                    \
-        pair_f32(v, lane, vp);                                                                           \
-        float2* dst = (float2*)(pb + (size_t)(rb0 + prow) * kTile + col);                               \
-        _Pragma("unroll") for (int q = 0; q < 8; ++q) dst[(8 * (q >> 1) + 2 * (q & 1)) * (kTile / 2)] = vp[q]; \
+        float* const prow = pb + (size_t)(rb0 + lr) * kTile;                                             \
+        if (SWIGLU) {                                                                                    \
+            float2 gw[16], uw[16];                                                                       \
+            _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                             \
+                gw[q] = make_float2(agpr_read(acc[MI][0][q]), agpr_read(acc[MI][1][q]));                 \
+                uw[q] = make_float2(agpr_read(acc[MI][2][q]), agpr_read(acc[MI][3][q]));                 \
+            }                                                                                            \
+            _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                             \
+                float* const d = prow + (size_t)(8 * (q >> 2) + (q & 3)) * kTile + wn * 64 + 2 * lc;     \
+                *(float2*)d = gw[q];                                                                     \
+                *(float2*)(d + 128) = uw[q];                                                             \
+            }                                                                                            \
+        } else {                                                                                         \
+            float4 w[16];                                                                                \
+            _Pragma("unroll") for (int q = 0; q < 16; ++q)                                               \
+                w[q] = make_float4(agpr_read(acc[MI][0][q]), agpr_read(acc[MI][1][q]),                   \
+                                   agpr_read(acc[MI][2][q]), agpr_read(acc[MI][3][q]));                  \
+            _Pragma("unroll") for (int q = 0; q < 16; ++q)                                               \
+                *(float4*)(prow + (size_t)(8 * (q >> 2) + (q & 3)) * kTile + wn * 128 + 4 * lc) = w[q];  \
+        }                                                                                                \
     }                                                                                                    \
     __builtin_amdgcn_sched_barrier(0);
-            GB_EPI_PART(0, 0) GB_EPI_PART(0, 1) GB_EPI_PART(0, 2) GB_EPI_PART(0, 3)
-            GB_EPI_PART(1, 0) GB_EPI_PART(1, 1) GB_EPI_PART(1, 2) GB_EPI_PART(1, 3)
-            GB_EPI_PART(2, 0) GB_EPI_PART(2, 1) GB_EPI_PART(2, 2) GB_EPI_PART(2, 3)
-            GB_EPI_PART(3, 0) GB_EPI_PART(3, 1) GB_EPI_PART(3, 2) GB_EPI_PART(3, 3)
+            GB_EPI_PART(0) GB_EPI_PART(1) GB_EPI_PART(2) GB_EPI_PART(3)
 #undef GB_EPI_PART
         } else if (SWIGLU) {
             uint16_t* const cbase = p.C + (size_t)rbase * p.n_out;
             uint16_t* const sbase = p.stash ? p.stash + (size_t)rbase * 2 * p.n_out : nullptr;
-#define GB_EPI_SW(MI, NI)                                                                                \
+            const int f = e_nt * 128 + wn * 64 + 2 * lc;  // this lane's h columns f, f + 1
+#define GB_EPI_SW(MI)                                                                                    \
     {                                                                                                    \
-        const int f = e_nt * 128 + wn * 64 + (NI) * 32 + c2;                                               \
         const int rb0 = wm * 128 + (MI) * 32;                                                            \
-        float hv[16];                                                                                    \
-        float gv[16], uv[16];                                                                            \
+        uint32_t hw[16];                                                                                 \
         _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                                 \
-            gv[q] = agpr_read(acc[MI][NI][q]);                                                           \
-            uv[q] = agpr_read(acc[MI][(NI) + 2][q]);                                                     \
-            hv[q] = silu(gv[q]) * uv[q];                                                                 \
+            const float g0 = agpr_read(acc[MI][0][q]), g1 = agpr_read(acc[MI][1][q]);                    \
+            const float u0 = agpr_read(acc[MI][2][q]), u1 = agpr_read(acc[MI][3][q]);                    \
+            hw[q] = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);                                           \
         }                                                                                                \
-        uint32_t hp[8];                                                                                  \
-        pair_bf16(hv, lane, hp);                                                                         \
         if (f < p.n_out) {                                                                               \
-            uint32_t* dst = (uint32_t*)(cbase + (uint32_t)((rb0 + prow) * p.n_out + f));                 \
-            GB_STORE_PAIRS(dst, ldw, rb0, hp)                                                                 \
+            uint16_t* const dst = cbase + (size_t)(rb0 + lr) * p.n_out + f;                              \
+            GB_STORE_ROWS(uint32_t, dst, p.n_out, rb0, hw)                                               \
             if (sbase) {                                                                                 \
-                uint32_t gp[8], up[8];                                                                   \
-                pair_bf16(gv, lane, gp);                                                                 \
-                pair_bf16(uv, lane, up);                                                                 \
-                uint32_t* gd = (uint32_t*)(sbase + (uint32_t)((rb0 + prow) * 2 * p.n_out + f));          \
-                GB_STORE_PAIRS(gd, 2 * ldw, rb0, gp)                                                              \
-                uint32_t* ud = gd + ldw;                                                                 \
-                GB_STORE_PAIRS(ud, 2 * ldw, rb0, up)                                                              \
+                uint32_t gw[16], uw[16];                                                                 \
+                _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                         \
+                    gw[q] = pack_bf16x2(agpr_read(acc[MI][0][q]), agpr_read(acc[MI][1][q]));             \
+                    uw[q] = pack_bf16x2(agpr_read(acc[MI][2][q]), agpr_read(acc[MI][3][q]));             \
+                }                                                                                        \
+                uint16_t* const gd = sbase + (size_t)(rb0 + lr) * 2 * p.n_out + f;                       \
+                GB_STORE_ROWS(uint32_t, gd, 2 * p.n_out, rb0, gw)                                        \
+                uint16_t* const ud = gd + p.n_out;                                                       \
+                GB_STORE_ROWS(uint32_t, ud, 2 * p.n_out, rb0, uw)                                        \
             }                                                                                            \
         }                                                                                                \
     }                                                                                                    \
     __builtin_amdgcn_sched_barrier(0);
-            GB_EPI_SW(0, 0) GB_EPI_SW(0, 1) GB_EPI_SW(1, 0) GB_EPI_SW(1, 1)
-            GB_EPI_SW(2, 0) GB_EPI_SW(2, 1) GB_EPI_SW(3, 0) GB_EPI_SW(3, 1)
+            GB_EPI_SW(0) GB_EPI_SW(1) GB_EPI_SW(2) GB_EPI_SW(3)
 #undef GB_EPI_SW
         } else {
             uint16_t* const cbase = p.C + (size_t)rbase * p.n_out;
-#define GB_EPI_DN(MI, NI)                                                                                \
+            const int n = e_nt * kTile + wn * 128 + 4 * lc;  // this lane's columns n .. n + 3
+#define GB_EPI_DN(MI)                                                                                    \
     {                                                                                                    \
-        const int n = e_nt * kTile + wn * 128 + (NI) * 32 + c2;                                            \
         const int rb0 = wm * 128 + (MI) * 32;                                                            \
-        float v[16];                                                                                     \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
-        uint32_t vp[8];                                                                                  \
-        pair_bf16(v, lane, vp);                                                                          \
+        uint2 w[16];                                                                                     \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
+            w[q] = make_uint2(pack_bf16x2(agpr_read(acc[MI][0][q]), agpr_read(acc[MI][1][q])),           \
+                              pack_bf16x2(agpr_read(acc[MI][2][q]), agpr_read(acc[MI][3][q])));          \
         if (n < p.n_out) {                                                                               \
-            uint32_t* dst = (uint32_t*)(cbase + (uint32_t)((rb0 + prow) * p.n_out + n));                 \
-            GB_STORE_PAIRS(dst, ldw, rb0, vp)                                                                 \
+            uint16_t* const dst = cbase + (size_t)(rb0 + lr) * p.n_out + n;                              \
+            GB_STORE_ROWS(uint2, dst, p.n_out, rb0, w)                                                   \
         }                                                                                                \
     }                                                                                                    \
     __builtin_amdgcn_sched_barrier(0);
-            GB_EPI_DN(0, 0) GB_EPI_DN(0, 1) GB_EPI_DN(0, 2) GB_EPI_DN(0, 3)
-            GB_EPI_DN(1, 0) GB_EPI_DN(1, 1) GB_EPI_DN(1, 2) GB_EPI_DN(1, 3)
-            GB_EPI_DN(2, 0) GB_EPI_DN(2, 1) GB_EPI_DN(2, 2) GB_EPI_DN(2, 3)
-            GB_EPI_DN(3, 0) GB_EPI_DN(3, 1) GB_EPI_DN(3, 2) GB_EPI_DN(3, 3)
+            GB_EPI_DN(0) GB_EPI_DN(1) GB_EPI_DN(2) GB_EPI_DN(3)
 #undef GB_EPI_DN
         }
-#undef GB_STORE_PAIRS
+#undef GB_STORE_ROWS
         }  // valid
         unit = next_unit;
     }
