@@ -53,24 +53,50 @@ __global__ void zero_counters_kernel(int* cnt) {
 
 // dW[e] = sum over the expert's units, in unit order, of the partial sums,
 // for experts with two or more units (the others were written directly).
-__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const int2* __restrict__ meta,
+// Every block lists those experts (in expert order) in LDS, then the grid
+// covers each listed expert's matrix in turn; a thread issues the loads of up
+// to 8 units before adding them, so each lane has several loads in flight.
+constexpr int kReduceBatch = 8;
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const int2* __restrict__ meta, int E,
                                                            const float4* __restrict__ part, int64_t n4, int slots,
                                                            float4* __restrict__ dw) {
-    const int e = blockIdx.y;
-    const int2 m = meta[e];
-    if (m.x < 2 || m.y < 0 || m.y + m.x > slots) return;  // the last test only fails for inconsistent offsets
-    const float4* src = part + (size_t)m.y * n4;
-    float4* dst = dw + (size_t)e * n4;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-        float4 a = src[i];
-        for (int u = 1; u < m.x; ++u) {
-            const float4 b = src[(size_t)u * n4 + i];
-            a.x += b.x;
-            a.y += b.y;
-            a.z += b.z;
-            a.w += b.w;
+    __shared__ int list[kMaxExperts];
+    __shared__ int scan_tmp[256 / 64];
+    const int per = (E + blockDim.x - 1) / blockDim.x;
+    const int e0 = threadIdx.x * per, e1 = min(E, e0 + per);
+    int mine = 0;
+    for (int e = e0; e < e1; ++e) mine += meta[e].x >= 2;
+    int count;
+    int at = block_exclusive_scan(mine, scan_tmp, &count);
+    for (int e = e0; e < e1; ++e)
+        if (meta[e].x >= 2) list[at++] = e;
+    __syncthreads();
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int li = 0; li < count; ++li) {
+        const int e = list[li];
+        const int2 m = meta[e];
+        if (m.y < 0 || m.y + m.x > slots) continue;  // only for inconsistent offsets
+        const float4* src = part + (size_t)m.y * n4;
+        float4* dst = dw + (size_t)e * n4;
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+            float4 a = src[i];
+            for (int u0 = 1; u0 < m.x; u0 += kReduceBatch) {
+                float4 b[kReduceBatch];
+#pragma unroll
+                for (int j = 0; j < kReduceBatch; ++j)
+                    if (u0 + j < m.x) b[j] = src[(size_t)(u0 + j) * n4 + i];
+#pragma unroll
+                for (int j = 0; j < kReduceBatch; ++j) {
+                    if (u0 + j < m.x) {
+                        a.x += b[j].x;
+                        a.y += b[j].y;
+                        a.z += b[j].z;
+                        a.w += b[j].w;
+                    }
+                }
+            }
+            dst[i] = a;
         }
-        dst[i] = a;
     }
 }
 
@@ -94,8 +120,8 @@ hipError_t launch_wgrad(const moe_config& c, gemm::BwdArgs w, void* ws, hipStrea
     hipError_t e = launch<gemm::kWgrad>(w, max_units * cdiv(M, gemm::kTile) * cdiv(N, gemm::kTile), s);
     if (e != hipSuccess || slots == 0) return e;
     const int64_t n4 = M * N / 4;
-    const int bx = (int)std::min<int64_t>(cdiv(n4, 256 * 4), 512);
-    wgrad_reduce_kernel<<<dim3(bx, c.E), 256, 0, s>>>(w.meta, (const float4*)w.part, n4, w.slots, (float4*)w.Cw);
+    const int bx = (int)std::min<int64_t>(cdiv(n4, 256), 2048);
+    wgrad_reduce_kernel<<<bx, 256, 0, s>>>(w.meta, c.E, (const float4*)w.part, n4, w.slots, (float4*)w.Cw);
     return hipGetLastError();
 }
 

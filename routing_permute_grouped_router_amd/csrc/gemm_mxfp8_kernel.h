@@ -118,11 +118,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     // of B fragments 1..3, and the lane's chunk offsets for K step sub, half hl
     const uint32_t ra0 = lds_base + (uint32_t)arow[0] * BKB, rb0 = lds_base + A_BYTES + (uint32_t)brow[0] * BKB;
     constexpr int kBRow[4] = {0, 32, SWIGLU ? 128 : 64, SWIGLU ? 160 : 96};
-    uint32_t kc[2][2];
+    // (LDS holds chunk c of row r at position c ^ swz<1>(r): any 16
+    // consecutive rows of a fragment then cover all 64 banks, so a
+    // ds_read_b128 is conflict-free; fragments start at multiples of 32 rows,
+    // so swz<1> of a fragment row depends only on the lane and the fragment's
+    // parity par)
+    uint32_t kc[2][2][2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int hl = 0; hl < 2; ++hl) kc[sub][hl] = (uint32_t)((((sub * 4 + hl * 2 + half) ^ (lane & 7))) << 4);
+        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int par = 0; par < 2; ++par)
+                kc[sub][hl][par] = (uint32_t)(((sub * 4 + hl * 2 + half) ^ swz<1>(par * 32 + (lane & 31))) << 4);
 
     for (int t = t_begin + lb; t < t_end; t += per_xcd) {
         int mt, nt;
@@ -150,17 +158,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         };
         // per-lane global byte offsets of the code loads (K offset 0); the
         // 16-byte chunk a lane fetches is permuted so that LDS holds chunk
-        // c of row r at position c ^ (r & 7) (conflict-free fragment reads)
+        // c of row r at position c ^ swz<1>(r) (conflict-free fragment reads)
         uint32_t aoff[A_LOADS], boff[B_LOADS];
 #pragma unroll
         for (int i = 0; i < A_LOADS; ++i) {
             const int r = wid * 32 + i * RPL + lrow;
-            aoff[i] = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K + ((lslot ^ (r & 7)) * 16));
+            aoff[i] = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K + ((lslot ^ swz<1>(r)) * 16));
         }
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i) {
             const int r = wid * 64 + i * RPL + lrow;
-            boff[i] = (uint32_t)((size_t)b_row_of(r) * K + ((lslot ^ (r & 7)) * 16));
+            boff[i] = (uint32_t)((size_t)b_row_of(r) * K + ((lslot ^ swz<1>(r)) * 16));
         }
         const uint8_t* acodes = p.A + (size_t)row0 * K;  // A offsets are tile-relative
         const uint8_t* bcodes = p.B + (size_t)e * p.b_rows * K;
@@ -205,17 +213,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         // Fragment reads of K step `sub` (64 bytes) of the stage at byte offset
         // so_: A fragment mi / B fragment ni from 16-byte chunks 4 sub + h and
         // 4 sub + 2 + h of the lane's row (h = lane / 32), stored at chunk
-        // position c ^ (row & 7); row & 7 = lane & 7 for every fragment.
+        // position c ^ swz<1>(row) (kc, by the fragment's parity).
 #define MX_RD_A(FA, so_, sub, mi)                                                                        \
     {                                                                                                    \
-        const uint4 lo_ = mx_ds_read16(ra0 + (so_) + kc[sub][0] + (mi) * 32 * BKB);                      \
-        const uint4 hi_ = mx_ds_read16(ra0 + (so_) + kc[sub][1] + (mi) * 32 * BKB);                      \
+        const uint4 lo_ = mx_ds_read16(ra0 + (so_) + kc[sub][0][(mi) & 1] + (mi) * 32 * BKB);                      \
+        const uint4 hi_ = mx_ds_read16(ra0 + (so_) + kc[sub][1][(mi) & 1] + (mi) * 32 * BKB);                      \
         FA[mi] = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
     }
 #define MX_RD_B(FB, so_, sub, ni)                                                                        \
     {                                                                                                    \
-        const uint4 lo_ = mx_ds_read16(rb0 + (so_) + kc[sub][0] + kBRow[ni] * BKB);                      \
-        const uint4 hi_ = mx_ds_read16(rb0 + (so_) + kc[sub][1] + kBRow[ni] * BKB);                      \
+        const uint4 lo_ = mx_ds_read16(rb0 + (so_) + kc[sub][0][(ni) & 1] + kBRow[ni] * BKB);                      \
+        const uint4 hi_ = mx_ds_read16(rb0 + (so_) + kc[sub][1][(ni) & 1] + kBRow[ni] * BKB);                      \
         FB[ni] = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
     }
         // the 32-bit scale words (one byte per 32 K values of the stage) of the lane's rows
