@@ -153,8 +153,9 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const uint8_t* x_sc
  * columns [0,F) and u in [F,2F) for the backward ([CUDNN] fc1 stash).
  * xp_scale / w1_scale / h_scale: MXFP8 only, NULL otherwise.
  * ws: moe_workspace_size(cfg) bytes (the same scratch moe_permute takes; the
- * bf16 GEMMs keep their work-queue counters and the partial sums of tiles cut
- * along K there, so calls sharing one workspace must not overlap). */
+ * bf16 and MXFP8 GEMMs keep their work-queue counters there, the bf16 ones
+ * also the partial sums of tiles cut along K, so calls sharing one workspace
+ * must not overlap). */
 moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const uint8_t* xp_scale, const void* w1,
                                    const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
                                    void* gu_stash, void* ws, size_t ws_bytes, void* stream);

@@ -100,7 +100,7 @@ int64_t moe_rows_capacity(const moe_config* cfg) {
 size_t moe_workspace_size(const moe_config* cfg) {
     if (check_config(cfg) != MOE_OK) return 0;
     const moe_config& c = *cfg;
-    return group_ws_bytes(c) + round256(gemm_bf16_ws_bytes(c));
+    return group_ws_bytes(c) + round256(gemm_bf16_ws_bytes(c) + gemm_mxfp8_ws_bytes(c));
 }
 
 size_t moe_backward_workspace_size(const moe_config* cfg) {
@@ -174,7 +174,7 @@ moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const 
         REQUIRE(w1_scale);
         REQUIRE(h_scale);
         return hip_status(launch_swiglu_gemm_mxfp8(c, (const uint8_t*)xp, xp_scale, (const uint8_t*)w1, w1_scale,
-                                                   offsets, (uint8_t*)h, h_scale, (uint16_t*)gu_stash, s),
+                                                   offsets, (uint8_t*)h, h_scale, (uint16_t*)gu_stash, gemm_ws(c, ws), s),
                           "moe_grouped_swiglu_gemm");
     }
 }
@@ -205,7 +205,7 @@ moe_status moe_grouped_down_gemm(const moe_config* cfg, const void* h, const uin
         REQUIRE(h_scale);
         REQUIRE(w2_scale);
         return hip_status(launch_down_gemm_mxfp8(c, (const uint8_t*)h, h_scale, (const uint8_t*)w2, w2_scale, offsets,
-                                                 (uint16_t*)yp, s),
+                                                 (uint16_t*)yp, gemm_ws(c, ws), s),
                           "moe_grouped_down_gemm");
     }
 }

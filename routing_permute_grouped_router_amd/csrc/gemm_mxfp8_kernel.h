@@ -6,31 +6,12 @@
 // page "Add MoE + expert-parallel Python API surface, PyTorch reference, and
 // tests" (BlockScaledTensor, block 32) with OCP E4M3 elements.
 //
-// These GEMMs stream their weights from HBM (each expert's weights serve only
-// its own few hundred rows), so the design favours bytes in flight over
-// on-chip reuse:
-//   - tiles are 128 rows x 256 columns (SwiGLU: 128 gate + 128 up rows of W1),
-//     so an expert with a few hundred rows wastes at most one partial 128-row
-//     tile;
-//   - one LDS stage is 128 bytes of K (four scale blocks): codes of the 128 A
-//     rows and 256 B rows plus their 32-bit scale words, all copied straight
-//     from global memory into LDS (global_load_lds, 16-byte pieces for codes,
-//     4-byte pieces for scale words); three stages rotate, so the loads of
-//     stage k+2 are in flight while stage k feeds the matrix cores;
-//   - LDS reads are issued explicitly (ds_read_b128) one MFMA group ahead and
-//     waited for with lgkmcnt just before use; one barrier per stage.
-//
 // Operand layout of the scaled MFMA (measured on gfx950): lane l holds row
 // l % 32 (A) or column l % 32 (B) and the 16-byte K pieces [16 h, 16 h + 16)
 // and [32 + 16 h, 32 + 16 h + 16) of a 64-byte K step, h = l / 32; the E8M0
 // scale in byte 0 of lane l's scale operand applies to 32-block h of that row
-// or column.  A lane therefore reads 16-byte chunks c0 + h and c0 + 2 + h of
+// or column.  A lane therefore reads 16-byte chunks 4 s + h and 4 s + 2 + h of
 // its LDS row and passes byte (2 s + h) of the row's scale word for K step s.
-//
-// Epilogues go through LDS (one 32 x 32 accumulator at a time per wavefront)
-// so each lane finishes 16 consecutive columns of one row: the SwiGLU GEMM
-// forms silu(g) * u and requantises h to MXFP8 (blocks of 32 along F; the two
-// lanes of a block exchange their partial max), the down GEMM stores bf16.
 #pragma once
 
 #include "gemm_bf16_kernel.h"
@@ -52,342 +33,506 @@ struct MxArgs {
     uint8_t* Cs;             // SwiGLU: h scales [rows][n_out/32]
     uint16_t* Cb;            // down: Yp bf16 [rows][n_out]
     uint16_t* stash;         // SwiGLU, optional: bf16 g | u [rows][2 n_out]
+    int* sched;              // 8 work-queue counters, zero at launch
 };
 
-constexpr int kMxBM = 128;   // rows per tile
-constexpr int kMxBN = 256;   // B rows per tile
-constexpr int kMxStages = 3;
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles.  Each wavefront owns a 128 x 128 sub-tile (4 x 4 scaled
+// MFMAs), so every operand fragment read from LDS feeds two MFMAs (a 64 x 128
+// wavefront tile feeds 1.33 and needs ~100 bytes of fragment reads per MFMA
+// cycle and CU, near what LDS serves; here 64).
+// Two stages of 128 K-bytes of E4M3 codes rotate through LDS; a stage is two
+// K steps of 16 MFMAs each (2048 cycles, as long as a stage of the bf16
+// kernel).  The one barrier per stage sits after the first K step: there
+// this wavefront has read all of stage kt and stage kt+1 has landed.  The 16
+// code loads of stage kt+2 then go into the freed buffer under the 16 MFMAs
+// of the second K step, so each has at least one K step to land before the
+// next barrier, while the fragments of stage kt+1's first K step and its
+// scale words are read.  Scale words (one 32-bit word of four E8M0 bytes per
+// row and stage) sit in two slots of their own: with K a multiple of 512, a
+// 16-byte load per row brings the words of four stages (a row's scales are
+// 224 bytes apart at K = 7168, so each 4-byte load touched its own cache
+// line: as many L2 requests as all the code loads); else one word per stage.  Scheduling as in the bf16 kernel: per-XCD work queues
+// with stealing, the next unit's first stage and a half issued before the
+// epilogue (no K split: its partial sums would need the requantising
+// epilogue in a second kernel).
+//
+// Epilogues.  Down GEMM: bf16 straight from the accumulators with the
+// column order of the B rows chosen so that each lane stores 8-byte words of
+// four adjacent columns (out_col).  SwiGLU GEMM: h = silu(g) u is formed in
+// registers and each 32 x 32 h tile goes through a wavefront-private LDS tile
+// so that each lane finishes 16 consecutive columns of one row: the two
+// lanes of a 32-block exchange their partial maxima, quantise to E4M3
+// (OCP rule) and store 16 bytes of codes plus the scale byte.  The LDS tile
+// of wavefront w is the part of stage buffer 1 that only w's own loads write
+// (its 64 B-code rows): the next unit's B half of that buffer is issued only
+// after the epilogue, once w's reads of the tile are done.
 
-__device__ __forceinline__ void mx_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
-
-__device__ __forceinline__ uint4 mx_ds_read16(uint32_t addr) {
-    uint4 v;
-    __asm__ volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-    return v;
+// One operand fragment of a 64-byte K step: two 16-byte chunks (lo, hi).
+template <int OFF>
+__device__ __forceinline__ i32x8 mx_frag(uint32_t lo, uint32_t hi) {
+    uint4 a, b;
+    __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a) : "v"(lo), "i"(OFF) : "memory");
+    __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(b) : "v"(hi), "i"(OFF) : "memory");
+    return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
-
-__device__ __forceinline__ uint32_t mx_ds_read4(uint32_t addr) {
+template <int OFF>
+__device__ __forceinline__ uint32_t mx_word(uint32_t addr) {
     uint32_t v;
-    __asm__ volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    __asm__ volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
     return v;
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, int G>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
-    constexpr int BKB = 128;                       // K bytes per stage
-    constexpr int CH = BKB / 16;                   // 16-byte chunks per LDS row
-    constexpr int RPL = 64 / CH;                   // rows per wave-wide code load
-    constexpr int A_LOADS = kMxBM / 4 / RPL;       // 4: each wave loads 32 A rows
-    constexpr int B_LOADS = kMxBN / 4 / RPL;       // 8: each wave loads 64 B rows
-    constexpr int LPS = A_LOADS + B_LOADS + 2;     // loads per wave per stage (+ two scale loads)
-    constexpr int A_BYTES = kMxBM * BKB;           // 16 KiB
-    constexpr int B_BYTES = kMxBN * BKB;           // 32 KiB
-    constexpr int AS_OFF = A_BYTES + B_BYTES;      // scale words of the A rows
-    constexpr int BS_OFF = AS_OFF + kMxBM * 4;     // scale words of the B rows
-    constexpr int ST_BYTES = BS_OFF + kMxBN * 4;   // 50688
-    static_assert(LPS == 14, "wait counts below");
+    constexpr int BKB = 128;                 // K bytes (E4M3 values) per stage: four scale blocks
+    constexpr int CH = BKB / 16;             // 16-byte chunks per LDS row
+    constexpr int RPL = 64 / CH;             // rows per wave-wide code load
+    constexpr int LOADS = 64 / RPL;          // code loads per wave per operand per stage
+    constexpr int OPB = kTile * BKB;         // codes of one operand in one stage (32 KiB)
+    constexpr uint32_t STB = 2 * OPB;        // one stage: A codes | B codes
+    // Scale words: G stages per load (G = 4: 16 bytes per row, one cache line
+    // per row every four stages instead of every stage), in two slots of
+    // [A rows | B rows] x 4 G bytes after the two stages; stage kt's word of
+    // row r is at slot (kt / G) % 2, byte 4 (kt % G) of the row's entry.
+    static_assert(G == 1 || G == 4, "scale group");
+    constexpr int SW_ROW = 4 * G, SC_OP = kTile * SW_ROW, SC_SLOT = 2 * SC_OP;
+    constexpr uint32_t SC_BASE = 2 * STB;
+    // byte offsets of B fragments 1..3 from fragment 0 (SwiGLU: fragments 2, 3
+    // are the up rows of fragments 0, 1)
+    constexpr int B1 = 32 * BKB, B2 = (SWIGLU ? 128 : 64) * BKB, B3 = (SWIGLU ? 160 : 96) * BKB;
+    constexpr int W1 = 32 * SW_ROW, W2 = (SWIGLU ? 128 : 64) * SW_ROW, W3 = (SWIGLU ? 160 : 96) * SW_ROW;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kMxStages * ST_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STB + 2 * SC_SLOT];
     __shared__ int32_t pre[kMaxExperts + 1];
+    __shared__ int32_t offs[kMaxExperts + 1];
     __shared__ int scan_tmp[kThreads / 64];
+    __shared__ Queue queues[kXcds];
+    __shared__ int s_unit;
 
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid >> 1, wn = wid & 1, half = lane >> 5;
-    const int total_m = build_tile_prefix(p.offsets, p.E, kMxBM, pre, scan_tmp);
-    const int cols_per_tile = SWIGLU ? kMxBN / 2 : kMxBN;
+    for (int e = tid; e <= p.E; e += kThreads) offs[e] = p.offsets[e];
+    const int total_m = build_tile_prefix(p.offsets, p.E, kTile, pre, scan_tmp);  // ends with a barrier
+    const int cols_per_tile = SWIGLU ? kTile / 2 : kTile;
     const int n_tiles = (p.n_out + cols_per_tile - 1) / cols_per_tile;
     const int total = total_m * n_tiles;
-    const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
-    const int lb = blockIdx.x / kXcds;
-    const int t_begin = (int)((int64_t)total * xcd / kXcds), t_end = (int)((int64_t)total * (xcd + 1) / kXcds);
-
-    const int K = p.K, KS = K / 32;  // bytes per row, scale bytes per row
-    const int nk = K / BKB;
+    const int K = p.K, KS = K / 32, nk = K / BKB;
+    const int xcd = blockIdx.x % kXcds, nb = gridDim.x / kXcds;
+    if (tid < kXcds) queues[tid] = xcd_queue(total, tid, nb, 0);  // whole tiles only
+    uint32_t dry = 0;
+    auto ticket = [&]() -> int { return (dry >> xcd & 1) ? -1 : atomicAdd(p.sched + xcd, 1); };
+    auto take = [&](int r) -> int {
+        if (!(dry >> xcd & 1)) {
+            if (r >= 0 && r < queues[xcd].units) return (xcd << 20) | r;
+            dry |= 1u << xcd;
+        }
+        for (int d = 1; d < kXcds; ++d) {
+            const int x = (xcd + d) % kXcds;
+            if (dry >> x & 1) continue;
+            const int u = atomicAdd(p.sched + x, 1);
+            if (u < queues[x].units) return (x << 20) | u;
+            dry |= 1u << x;
+        }
+        return -1;
+    };
+    __syncthreads();
+    int tick = -1;
+    if (tid == 0) {
+        s_unit = take(ticket());
+        tick = ticket();
+    }
+    __syncthreads();
+    int unit = s_unit;
     const int lrow = lane / CH, lslot = lane % CH;
 
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
-    // LDS rows of this lane's MFMA operands (2 x 4 accumulators of 32 x 32 per wave)
-    int arow[2], brow[4];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) arow[mi] = wm * 64 + mi * 32 + (lane & 31);
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-        brow[ni] = SWIGLU ? (ni < 2 ? 0 : 128) + wn * 64 + (ni & 1) * 32 + (lane & 31)
-                          : wn * 128 + ni * 32 + (lane & 31);
-    // LDS byte address of fragment 0 of A and of B (stage 0), the row offsets
-    // of B fragments 1..3, and the lane's chunk offsets for K step sub, half hl
-    const uint32_t ra0 = lds_base + (uint32_t)arow[0] * BKB, rb0 = lds_base + A_BYTES + (uint32_t)brow[0] * BKB;
-    constexpr int kBRow[4] = {0, 32, SWIGLU ? 128 : 64, SWIGLU ? 160 : 96};
-    // (LDS holds chunk c of row r at position c ^ swz<1>(r): any 16
-    // consecutive rows of a fragment then cover all 64 banks, so a
-    // ds_read_b128 is conflict-free; fragments start at multiples of 32 rows,
-    // so swz<1> of a fragment row depends only on the lane and the fragment's
-    // parity par)
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)&lds[0];
+    // LDS rows this wave's loads fill: wid * 64 .. +63 of each operand
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(wid * 64 * BKB));
+    const uint32_t lds_wsc = __builtin_amdgcn_readfirstlane(lds_base + SC_BASE + (uint32_t)(wid * 64 * SW_ROW));
+    const int bfr = SWIGLU ? wn * 64 : wn * 128;  // first B row of this wave's fragments
+    const uint32_t a_rd = lds_base + (uint32_t)((wm * 128 + (lane & 31)) * BKB);
+    const uint32_t b_rd = lds_base + (uint32_t)(OPB + (bfr + (lane & 31)) * BKB);
+    const uint32_t as_rd = lds_base + SC_BASE + (uint32_t)((wm * 128 + (lane & 31)) * SW_ROW);
+    const uint32_t bs_rd = lds_base + SC_BASE + (uint32_t)(SC_OP + (bfr + (lane & 31)) * SW_ROW);
+    // chunk offsets [K step][lo, hi][fragment parity]: lane l reads 16-byte
+    // chunks 4 s + h and 4 s + 2 + h (h = l / 32) of row l % 32 of a
+    // fragment, stored at position c ^ swz<1>(row)
     uint32_t kc[2][2][2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
             for (int par = 0; par < 2; ++par)
-                kc[sub][hl][par] = (uint32_t)(((sub * 4 + hl * 2 + half) ^ swz<1>(par * 32 + (lane & 31))) << 4);
+                kc[s][hl][par] = (uint32_t)(((4 * s + 2 * hl + half) ^ swz<1>(par * 32 + (lane & 31))) << 4);
 
-    for (int t = t_begin + lb; t < t_end; t += per_xcd) {
-        int mt, nt;
-        // Tiles are ordered expert by expert, and within an expert N-tile by
-        // N-tile with its M-tiles adjacent: the blocks of one XCD that run at
-        // the same time then cover few experts, so each weight panel is
-        // fetched from HBM once and shared in L2 by all of the expert's M-tiles.
-        const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, p.E, t / n_tiles));
-        {
-            const int m_e = pre[e + 1] - pre[e], li = t - pre[e] * n_tiles;
-            nt = li / m_e;
-            mt = pre[e] + li % m_e;
+    int kb = 0, ke = 0, row0 = 0, row_end = 0, nt = 0;
+    bool valid = false;
+    uint32_t aoff[LOADS], boff[LOADS], asoff = 0, bsoff = 0;
+    const uint8_t* acodes = p.A;
+    const uint8_t* bcodes = p.B;
+    const uint8_t* ascale = p.As;
+    const uint8_t* bscale = p.Bs;
+#define MX_LOAD_A(kt, stage, i)                                                                          \
+    dma_lds16(lds_wave + (uint32_t)(stage) * STB + (i) * RPL * BKB, aoff[i], acodes + (size_t)(kt) * BKB)
+#define MX_LOAD_B(kt, stage, i)                                                                          \
+    dma_lds16(lds_wave + (uint32_t)(stage) * STB + OPB + (i) * RPL * BKB, boff[i], bcodes + (size_t)(kt) * BKB)
+// scale words of load group grp (G stages) into slot `slot`
+#define MX_LOAD_SC(OP, SOFF, SBASE, grp, slot)                                                           \
+    {                                                                                                    \
+        if constexpr (G == 4)                                                                            \
+            dma_lds16(lds_wsc + (uint32_t)(slot) * SC_SLOT + (OP) * SC_OP, SOFF, SBASE + (size_t)(grp) * 16); \
+        else                                                                                             \
+            dma_lds4(lds_wsc + (uint32_t)(slot) * SC_SLOT + (OP) * SC_OP, SOFF, SBASE + (size_t)(grp) * 4); \
+    }
+#define MX_LOAD_AS(grp, slot) MX_LOAD_SC(0, asoff, ascale, grp, slot)
+#define MX_LOAD_BS(grp, slot) MX_LOAD_SC(1, bsoff, bscale, grp, slot)
+// LDS byte offset of stage kt's scale words within the scale slots
+#define MX_SC_OFF(kt) ((uint32_t)(((kt) / G) & 1) * SC_SLOT + (uint32_t)((kt) % G) * 4)
+#define MX_SB __builtin_amdgcn_sched_barrier(0)
+// fragment reads of K step S of the stage at byte offset SO
+#define MX_RD_A(F, SO, S, mi)                                                                            \
+    F[mi] = mx_frag<(mi) * 32 * BKB>(a_rd + (SO) + kc[S][0][(mi) & 1], a_rd + (SO) + kc[S][1][(mi) & 1])
+#define MX_RD_B(G, SO, S, ni)                                                                            \
+    G[ni] = mx_frag<(ni) == 0 ? 0 : (ni) == 1 ? B1 : (ni) == 2 ? B2 : B3>(b_rd + (SO) + kc[S][0][(ni) & 1], \
+                                                                          b_rd + (SO) + kc[S][1][(ni) & 1])
+// the scale words of a stage (SO = MX_SC_OFF of the stage): A rows of fragments 0..3, then B
+#define MX_RD_S(SW, SO)                                                                                  \
+    {                                                                                                    \
+        SW[0] = mx_word<0>(as_rd + (SO));                                                                \
+        SW[1] = mx_word<32 * SW_ROW>(as_rd + (SO));                                                      \
+        SW[2] = mx_word<64 * SW_ROW>(as_rd + (SO));                                                      \
+        SW[3] = mx_word<96 * SW_ROW>(as_rd + (SO));                                                      \
+        SW[4] = mx_word<0>(bs_rd + (SO));                                                                \
+        SW[5] = mx_word<W1>(bs_rd + (SO));                                                               \
+        SW[6] = mx_word<W2>(bs_rd + (SO));                                                               \
+        SW[7] = mx_word<W3>(bs_rd + (SO));                                                               \
+    }
+#define MX_WAIT_F(F, G)                                                                                  \
+    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
+                     : "+v"(F[0]), "+v"(F[1]), "+v"(F[2]), "+v"(F[3]), "+v"(G[0]), "+v"(G[1]), "+v"(G[2]), \
+                       "+v"(G[3])::"memory")
+#define MX_WAIT_W(SW)                                                                                    \
+    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
+                     : "+v"(SW[0]), "+v"(SW[1]), "+v"(SW[2]), "+v"(SW[3]), "+v"(SW[4]), "+v"(SW[5]),     \
+                       "+v"(SW[6]), "+v"(SW[7])::"memory")
+// One MFMA of K step S: the scale words were shifted right by 8 h (h = lane
+// / 32), so byte 2 S holds the scale of 32-block 2 S + h for every lane.
+#define MX_MFMA(F, G, SS, S, mi, ni)                                                                     \
+    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F[mi], G[ni], acc[mi][ni], 0, 0, 2 * (S), \
+                                                                  (int)SS[mi], 2 * (S), (int)SS[4 + (ni)])
+#define MX_STEP(F, G, SS, S, mi, ni, PRE, RD)                                                            \
+    PRE;                                                                                                 \
+    MX_MFMA(F, G, SS, S, mi, ni);                                                                        \
+    RD;                                                                                                  \
+    MX_SB;
+
+    // Decode unit u, compute its tile's addressing and issue the loads of its
+    // first stage and the A half of its second (stage buffers 0 and 1).
+    auto setup = [&](int u) __attribute__((always_inline)) {
+        u = __builtin_amdgcn_readfirstlane(u);
+        if (u < 0) {  // no unit (every queue used up): nothing to decode or load
+            valid = false;
+            kb = ke = 0;
+            return;
         }
-        nt = __builtin_amdgcn_readfirstlane(nt);
-        const int row_end = __builtin_amdgcn_readfirstlane(min(p.offsets[e + 1], p.rows));
-        const int row0 = __builtin_amdgcn_readfirstlane(p.offsets[e] + (mt - pre[e]) * kMxBM);
-        if (row0 < 0 || row0 >= row_end) continue;  // only for inconsistent offsets
-
-        auto b_row_of = [&](int r) __attribute__((always_inline)) {
+        const int ux = __builtin_amdgcn_readfirstlane(u >> 20), uu = __builtin_amdgcn_readfirstlane(u & 0xFFFFF);
+        const int t = __builtin_amdgcn_readfirstlane(queues[ux].tb + uu);
+        kb = 0;
+        ke = nk;
+        int mt, ntt, ee;
+        tile_of(t, pre, p.E, total_m, n_tiles, 0, &ee, &mt, &ntt);
+        nt = __builtin_amdgcn_readfirstlane(ntt);
+        mt = __builtin_amdgcn_readfirstlane(mt);
+        const int e = __builtin_amdgcn_readfirstlane(ee);
+        row_end = __builtin_amdgcn_readfirstlane(min(offs[e + 1], p.rows));
+        row0 = __builtin_amdgcn_readfirstlane(offs[e] + (mt - pre[e]) * kTile);
+        valid = row0 >= 0 && row0 < row_end;  // false only for inconsistent offsets
+        if (!valid) {
+            kb = ke = 0;
+            return;
+        }
+        const int brow0 = SWIGLU ? nt * 128 : nt * kTile;
+        // B row (of the expert's matrix) that tile row r of B holds
+        auto b_row = [&](int r) -> int {
             if (SWIGLU) {
                 const int f = min(nt * 128 + (r & 127), p.n_out - 1);
                 return r < 128 ? f : p.n_out + f;
             }
-            return min(nt * kMxBN + r, p.n_out - 1);
+            return min(nt * kTile + out_col(r), p.n_out - 1);
         };
-        // per-lane global byte offsets of the code loads (K offset 0); the
-        // 16-byte chunk a lane fetches is permuted so that LDS holds chunk
-        // c of row r at position c ^ swz<1>(r) (conflict-free fragment reads)
-        uint32_t aoff[A_LOADS], boff[B_LOADS];
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
-            const int r = wid * 32 + i * RPL + lrow;
-            aoff[i] = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K + ((lslot ^ swz<1>(r)) * 16));
+        for (int i = 0; i < LOADS; ++i) {
+            const int r = wid * 64 + i * RPL + lrow;  // tile row 0..255
+            const int chunk = lslot ^ swz<1>(r);
+            aoff[i] = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K + chunk * 16);
+            boff[i] = (uint32_t)((size_t)(b_row(r) - brow0) * K + chunk * 16);
         }
+        {
+            const int r = wid * 64 + lane;  // tile row of this lane's scale words
+            asoff = (uint32_t)((min(row0 + r, row_end - 1) - row0) * KS);
+            bsoff = (uint32_t)((b_row(r) - brow0) * KS);
+        }
+        acodes = p.A + (size_t)row0 * K;
+        bcodes = p.B + ((size_t)e * p.b_rows + brow0) * K;
+        ascale = p.As + (size_t)row0 * KS;
+        bscale = p.Bs + ((size_t)e * p.b_rows + brow0) * KS;
+        MX_SB;
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) {
-            const int r = wid * 64 + i * RPL + lrow;
-            boff[i] = (uint32_t)((size_t)b_row_of(r) * K + ((lslot ^ swz<1>(r)) * 16));
+        for (int i = 0; i < LOADS; ++i) {
+            MX_LOAD_A(kb, 0, i);
+            MX_LOAD_B(kb, 0, i);
         }
-        const uint8_t* acodes = p.A + (size_t)row0 * K;  // A offsets are tile-relative
-        const uint8_t* bcodes = p.B + (size_t)e * p.b_rows * K;
-        // scale words: A rows wid*32 + lane (lanes 0..31), B rows wid*64 + lane,
-        // as uniform bases plus 32-bit lane offsets
-        const uint8_t* asbase = p.As + (size_t)row0 * KS;
-        const uint8_t* bsbase = p.Bs + (size_t)e * p.b_rows * KS;
-        const uint32_t asoff = (uint32_t)((min(row0 + wid * 32 + (lane & 31), row_end - 1) - row0) * KS);
-        const uint32_t bsoff = (uint32_t)(b_row_of(wid * 64 + lane) * KS);
+        // (no K split here: kb = 0, so stage kt's buffer is kt % 2)
+        MX_LOAD_AS(0, 0);
+        MX_LOAD_BS(0, 0);
+        const int k1 = min(kb + 1, ke - 1);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) MX_LOAD_A(k1, 1, i);
+        if constexpr (G == 1) MX_LOAD_AS(k1, 1);
+        MX_SB;
+    };
+    // The B half of the unit's second stage (into stage buffer 1).
+    auto load_b_half = [&]() __attribute__((always_inline)) {
+        if (!valid) return;
+        const int k1 = min(kb + 1, ke - 1);
+        MX_SB;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) MX_LOAD_B(k1, 1, i);
+        if constexpr (G == 1) MX_LOAD_BS(k1, 1);
+        MX_SB;
+    };
 
-        f32x16 acc[2][4];
+    setup(unit);
+    load_b_half();
+    while (unit >= 0) {
+        i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
+        uint32_t sw[8], ss[8];
+        // the unit's first two stages landed everywhere; the previous unit's stores retired
+        __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        MX_SB;
+        if (tid == 0) {  // publish the next unit, take a ticket for the one after
+            const int nu = take(tick);
+            s_unit = nu;
+            tick = nu >= 0 ? ticket() : -1;
+        }
+        f32x16 acc[4][4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-        // Loads of stage kt into stage buffer slot % 3 (dma_lds16 / dma_lds4:
-        // uniform M0 and base, 32-bit lane offsets): the codes of this wave's
-        // 32 A rows (4 loads) and 64 B rows (8 loads), and the 32-bit scale
-        // words of those rows (one load each).  MX_LD(slot, kt, j) is load j
-        // of 14; slot = kt except past the end of K, where the last stage is
-        // loaded again into the free buffer.
-#define MX_LD(slot, kt, j)                                                                               \
+        MX_RD_A(fa0, 0u, 0, 0);
+        MX_RD_A(fa0, 0u, 0, 1);
+        MX_RD_A(fa0, 0u, 0, 2);
+        MX_RD_A(fa0, 0u, 0, 3);
+        MX_RD_B(fb0, 0u, 0, 0);
+        MX_RD_B(fb0, 0u, 0, 1);
+        MX_RD_B(fb0, 0u, 0, 2);
+        MX_RD_B(fb0, 0u, 0, 3);
+        MX_RD_S(sw, MX_SC_OFF(kb));
+        MX_WAIT_F(fa0, fb0);
+        MX_WAIT_W(sw);
+// One stage KT in stage buffer ST (0 or 1); SCL (a literal): whether its
+// second K step issues scale-word loads.  G = 1: those of stage kl, into the
+// freed slot ST; G = 4 (every fourth stage): the next group of four stages,
+// into the other slot.
+#define MX_STAGE(KT, ST, SCL)                                                                            \
     {                                                                                                    \
-        const uint32_t st_ = lds_base + (uint32_t)((slot) % kMxStages) * ST_BYTES;                       \
-        if ((j) < A_LOADS)                                                                               \
-            dma_lds16(__builtin_amdgcn_readfirstlane(st_ + (wid * 32 + (j) * RPL) * BKB), aoff[(j) % A_LOADS], \
-                      acodes + (size_t)(kt) * BKB);                                                      \
-        else if ((j) < A_LOADS + B_LOADS)                                                                \
-            dma_lds16(__builtin_amdgcn_readfirstlane(st_ + A_BYTES + (wid * 64 + ((j) - A_LOADS) * RPL) * BKB), \
-                      boff[((j) - A_LOADS) % B_LOADS], bcodes + (size_t)(kt) * BKB);                      \
-        else if ((j) == A_LOADS + B_LOADS) {                                                             \
-            if (lane < 32)                                                                               \
-                dma_lds4(__builtin_amdgcn_readfirstlane(st_ + AS_OFF + wid * 32 * 4), asoff, asbase + (size_t)(kt) * 4); \
-        } else                                                                                           \
-            dma_lds4(__builtin_amdgcn_readfirstlane(st_ + BS_OFF + wid * 64 * 4), bsoff, bsbase + (size_t)(kt) * 4); \
+        const int kt_ = (KT), st_ = (ST);                                                                \
+        const uint32_t so = st_ ? STB : 0u, nso = st_ ? 0u : STB;                                        \
+        const int kl = min(kt_ + 2, ke - 1); /* loads of stage kt+2 (past the end: the last stage) */   \
+        const int sg = G == 1 ? kl : min(kt_ / G + 1, (ke - 1) / G);                                     \
+        const int sslot = G == 1 ? st_ : ((kt_ / G) + 1) & 1;                                            \
+        const uint32_t nsc = MX_SC_OFF(kt_ + 1);                                                         \
+        MX_SB;                                                                                           \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ss[i] = sw[i] >> (8 * half);                       \
+        MX_SB;                                                                                           \
+        /* K step 0 on fa0/fb0; the fragments of K step 1 are read under the first 8 MFMAs */           \
+        MX_STEP(fa0, fb0, ss, 0, 0, 0, (void)0, MX_RD_A(fa1, so, 1, 0))                                  \
+        MX_STEP(fa0, fb0, ss, 0, 0, 1, (void)0, MX_RD_A(fa1, so, 1, 1))                                  \
+        MX_STEP(fa0, fb0, ss, 0, 0, 2, (void)0, MX_RD_A(fa1, so, 1, 2))                                  \
+        MX_STEP(fa0, fb0, ss, 0, 0, 3, (void)0, MX_RD_A(fa1, so, 1, 3))                                  \
+        MX_STEP(fa0, fb0, ss, 0, 1, 0, (void)0, MX_RD_B(fb1, so, 1, 0))                                  \
+        MX_STEP(fa0, fb0, ss, 0, 1, 1, (void)0, MX_RD_B(fb1, so, 1, 1))                                  \
+        MX_STEP(fa0, fb0, ss, 0, 1, 2, (void)0, MX_RD_B(fb1, so, 1, 2))                                  \
+        MX_STEP(fa0, fb0, ss, 0, 1, 3, (void)0, MX_RD_B(fb1, so, 1, 3))                                  \
+        MX_STEP(fa0, fb0, ss, 0, 2, 0, (void)0, (void)0)                                                 \
+        MX_STEP(fa0, fb0, ss, 0, 2, 1, (void)0, (void)0)                                                 \
+        MX_STEP(fa0, fb0, ss, 0, 2, 2, (void)0, (void)0)                                                 \
+        MX_STEP(fa0, fb0, ss, 0, 2, 3, (void)0, (void)0)                                                 \
+        MX_STEP(fa0, fb0, ss, 0, 3, 0, (void)0, (void)0)                                                 \
+        MX_STEP(fa0, fb0, ss, 0, 3, 1, (void)0, (void)0)                                                 \
+        MX_STEP(fa0, fb0, ss, 0, 3, 2, (void)0, (void)0)                                                 \
+        MX_STEP(fa0, fb0, ss, 0, 3, 3, (void)0, (void)0)                                                 \
+        MX_WAIT_F(fa1, fb1);                                                                             \
+        /* this wave has read all of stage kt and its loads of stage kt+1 landed; */                    \
+        /* past the barrier the same holds for every wave */                                             \
+        __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");                     \
+        MX_SB;                                                                                           \
+        /* K step 1 on fa1/fb1; stage kt+1's first fragments and scale words are */                     \
+        /* read, and the loads of stage kt+2 go into buffer ST */                                        \
+        MX_STEP(fa1, fb1, ss, 1, 0, 0, MX_LOAD_A(kl, st_, 0), MX_RD_A(fa0, nso, 0, 0))                   \
+        MX_STEP(fa1, fb1, ss, 1, 0, 1, MX_LOAD_B(kl, st_, 0), MX_RD_A(fa0, nso, 0, 1))                   \
+        MX_STEP(fa1, fb1, ss, 1, 0, 2, MX_LOAD_A(kl, st_, 1), MX_RD_A(fa0, nso, 0, 2))                   \
+        MX_STEP(fa1, fb1, ss, 1, 0, 3, MX_LOAD_B(kl, st_, 1), MX_RD_A(fa0, nso, 0, 3))                   \
+        MX_STEP(fa1, fb1, ss, 1, 1, 0, MX_LOAD_A(kl, st_, 2), MX_RD_B(fb0, nso, 0, 0))                   \
+        MX_STEP(fa1, fb1, ss, 1, 1, 1, MX_LOAD_B(kl, st_, 2), MX_RD_B(fb0, nso, 0, 1))                   \
+        MX_STEP(fa1, fb1, ss, 1, 1, 2, MX_LOAD_A(kl, st_, 3), MX_RD_B(fb0, nso, 0, 2))                   \
+        MX_STEP(fa1, fb1, ss, 1, 1, 3, MX_LOAD_B(kl, st_, 3), MX_RD_B(fb0, nso, 0, 3))                   \
+        MX_STEP(fa1, fb1, ss, 1, 2, 0, MX_LOAD_A(kl, st_, 4); if (SCL) MX_LOAD_AS(sg, sslot), MX_RD_S(sw, nsc)) \
+        MX_STEP(fa1, fb1, ss, 1, 2, 1, MX_LOAD_B(kl, st_, 4), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 2, 2, MX_LOAD_A(kl, st_, 5), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 2, 3, MX_LOAD_B(kl, st_, 5), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 3, 0, MX_LOAD_A(kl, st_, 6), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 3, 1, MX_LOAD_B(kl, st_, 6), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 3, 2, MX_LOAD_A(kl, st_, 7), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 3, 3, MX_LOAD_B(kl, st_, 7); if (SCL) MX_LOAD_BS(sg, sslot), (void)0)   \
+        /* the next stage's first fragments and scale words landed (no LDS read */                      \
+        /* is in flight when the loop ends) */                                                           \
+        MX_WAIT_F(fa0, fb0);                                                                             \
+        MX_WAIT_W(sw);                                                                                   \
     }
-#define MX_ISSUE(kt)                                                                                     \
-    _Pragma("unroll") for (int j_ = 0; j_ < LPS; ++j_) MX_LD(kt, kt, j_)
-        // Fragment reads of K step `sub` (64 bytes) of the stage at byte offset
-        // so_: A fragment mi / B fragment ni from 16-byte chunks 4 sub + h and
-        // 4 sub + 2 + h of the lane's row (h = lane / 32), stored at chunk
-        // position c ^ swz<1>(row) (kc, by the fragment's parity).
-#define MX_RD_A(FA, so_, sub, mi)                                                                        \
-    {                                                                                                    \
-        const uint4 lo_ = mx_ds_read16(ra0 + (so_) + kc[sub][0][(mi) & 1] + (mi) * 32 * BKB);                      \
-        const uint4 hi_ = mx_ds_read16(ra0 + (so_) + kc[sub][1][(mi) & 1] + (mi) * 32 * BKB);                      \
-        FA[mi] = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
-    }
-#define MX_RD_B(FB, so_, sub, ni)                                                                        \
-    {                                                                                                    \
-        const uint4 lo_ = mx_ds_read16(rb0 + (so_) + kc[sub][0][(ni) & 1] + kBRow[ni] * BKB);                      \
-        const uint4 hi_ = mx_ds_read16(rb0 + (so_) + kc[sub][1][(ni) & 1] + kBRow[ni] * BKB);                      \
-        FB[ni] = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
-    }
-        // the 32-bit scale words (one byte per 32 K values of the stage) of the lane's rows
-#define MX_RD_S(SA, SB, so_)                                                                             \
-    {                                                                                                    \
-        _Pragma("unroll") for (int mi = 0; mi < 2; ++mi) SA[mi] = mx_ds_read4(lds_base + (so_) + AS_OFF + arow[mi] * 4); \
-        _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) SB[ni] = mx_ds_read4(lds_base + (so_) + BS_OFF + brow[ni] * 4); \
-    }
-#define MX_WAIT(FA, FB)                                                                                  \
-    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
-                     : "+v"(FA[0]), "+v"(FA[1]), "+v"(FB[0]), "+v"(FB[1]), "+v"(FB[2]), "+v"(FB[3])::"memory")
-#define MX_WAIT_S(SA, SB)                                                                                \
-    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
-                     : "+v"(SA[0]), "+v"(SA[1]), "+v"(SB[0]), "+v"(SB[1]), "+v"(SB[2]), "+v"(SB[3])::"memory")
-        // One MFMA of K step SUB: the scale words were shifted right by 8 h, so
-        // the byte of 32-block 2 SUB + h is byte 2 SUB for every lane (opsel).
-#define MX_MFMA(FA, FB, SA, SB, SUB, mi, ni)                                                             \
-    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(FA[mi], FB[ni], acc[mi][ni], 0, 0, 2 * (SUB), \
-                                                                  (int)SA[mi], 2 * (SUB), (int)SB[ni])
-#define MX_SB __builtin_amdgcn_sched_barrier(0)
-#define MX_STEP(PRE, MF, RD)                                                                             \
-    PRE;                                                                                                 \
-    MF;                                                                                                  \
-    RD;                                                                                                  \
-    MX_SB;
-
-        const int KT_ = nk;  // stages
-        // prologue: stages 0 and 1 in flight, stage 0 landed everywhere
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous tile's stores retired
-        MX_SB;
-        MX_ISSUE(0);
-        _Pragma("unroll") for (int j_ = 0; j_ < LPS; ++j_) MX_LD(1, min(1, KT_ - 1), j_)
-        __asm__ volatile("s_waitcnt vmcnt(14)\n\ts_barrier" ::: "memory");
-        MX_SB;
-        i32x8 f0a[2], f0b[4], f1a[2], f1b[4];
-        uint32_t s0a[2], s0b[4], s1a[2], s1b[4];
-        MX_RD_A(f0a, 0u, 0, 0) MX_RD_A(f0a, 0u, 0, 1)
-        MX_RD_B(f0b, 0u, 0, 0) MX_RD_B(f0b, 0u, 0, 1) MX_RD_B(f0b, 0u, 0, 2) MX_RD_B(f0b, 0u, 0, 3)
-        MX_RD_S(s1a, s1b, 0u)
-        for (int kt = 0; kt < KT_; ++kt) {
-            const uint32_t so = (uint32_t)(kt % kMxStages) * ST_BYTES;
-            const uint32_t sn = (uint32_t)((kt + 1) % kMxStages) * ST_BYTES;
-            const int kl = min(kt + 2, KT_ - 1);  // loads of stage kt+2 (past the end: the last stage again)
-            MX_SB;
-            // this stage's scale words, shifted so byte 2 s holds 32-block 2 s + h
-            MX_WAIT_S(s1a, s1b);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) s0a[i] = s1a[i] >> (8 * half);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s0b[i] = s1b[i] >> (8 * half);
-            MX_WAIT(f0a, f0b);
-            MX_SB;
-            // K step 0: 8 MFMAs; the fragments of step 1 and loads 0..6 of stage kt+2 ride along
-            MX_STEP(MX_LD(kt + 2, kl, 0), MX_MFMA(f0a, f0b, s0a, s0b, 0, 0, 0), MX_RD_A(f1a, so, 1, 0))
-            MX_STEP(MX_LD(kt + 2, kl, 1), MX_MFMA(f0a, f0b, s0a, s0b, 0, 0, 1), MX_RD_A(f1a, so, 1, 1))
-            MX_STEP(MX_LD(kt + 2, kl, 2), MX_MFMA(f0a, f0b, s0a, s0b, 0, 0, 2), MX_RD_B(f1b, so, 1, 0))
-            MX_STEP(MX_LD(kt + 2, kl, 3), MX_MFMA(f0a, f0b, s0a, s0b, 0, 0, 3), MX_RD_B(f1b, so, 1, 1))
-            MX_STEP(MX_LD(kt + 2, kl, 4), MX_MFMA(f0a, f0b, s0a, s0b, 0, 1, 0), MX_RD_B(f1b, so, 1, 2))
-            MX_STEP(MX_LD(kt + 2, kl, 5), MX_MFMA(f0a, f0b, s0a, s0b, 0, 1, 1), MX_RD_B(f1b, so, 1, 3))
-            MX_STEP(MX_LD(kt + 2, kl, 6), MX_MFMA(f0a, f0b, s0a, s0b, 0, 1, 2), (void)0)
-            MX_STEP((void)0, MX_MFMA(f0a, f0b, s0a, s0b, 0, 1, 3), (void)0)
-            MX_WAIT(f1a, f1b);  // this wave has read all of stage kt
-            // stage kt+1 landed (only the 7 loads of stage kt+2 just issued may
-            // be in flight); past the barrier the same holds for every wave and
-            // the buffer of stage kt is free
-            __asm__ volatile("s_waitcnt vmcnt(7)\n\ts_barrier" ::: "memory");
-            MX_SB;
-            // K step 1: 8 MFMAs; step 0 and the scale words of stage kt+1 and
-            // loads 7..13 of stage kt+2 ride along
-            MX_STEP(MX_LD(kt + 2, kl, 7), MX_MFMA(f1a, f1b, s0a, s0b, 1, 0, 0), MX_RD_A(f0a, sn, 0, 0))
-            MX_STEP(MX_LD(kt + 2, kl, 8), MX_MFMA(f1a, f1b, s0a, s0b, 1, 0, 1), MX_RD_A(f0a, sn, 0, 1))
-            MX_STEP(MX_LD(kt + 2, kl, 9), MX_MFMA(f1a, f1b, s0a, s0b, 1, 0, 2), MX_RD_B(f0b, sn, 0, 0))
-            MX_STEP(MX_LD(kt + 2, kl, 10), MX_MFMA(f1a, f1b, s0a, s0b, 1, 0, 3), MX_RD_B(f0b, sn, 0, 1))
-            MX_STEP(MX_LD(kt + 2, kl, 11), MX_MFMA(f1a, f1b, s0a, s0b, 1, 1, 0), MX_RD_B(f0b, sn, 0, 2))
-            MX_STEP(MX_LD(kt + 2, kl, 12), MX_MFMA(f1a, f1b, s0a, s0b, 1, 1, 1), MX_RD_B(f0b, sn, 0, 3))
-            MX_STEP(MX_LD(kt + 2, kl, 13), MX_MFMA(f1a, f1b, s0a, s0b, 1, 1, 2), MX_RD_S(s1a, s1b, sn))
-            MX_STEP((void)0, MX_MFMA(f1a, f1b, s0a, s0b, 1, 1, 3), (void)0)
-            // wait for the next stage's step-0 fragments and scale words here
-            // (they had the last MFMAs to land), so no LDS read is in flight
-            // when the loop ends
-            MX_WAIT(f0a, f0b);
-            MX_WAIT_S(s1a, s1b);
+        if constexpr (G == 1) {
+            for (int kt = kb; kt < ke; ++kt) MX_STAGE(kt, (kt - kb) & 1, 1)
+        } else {
+            // stages in fours (K is a multiple of 4 stages, kb = 0): the scale
+            // group loads sit in the first stage of each four, with no branch
+            for (int kt = kb; kt < ke; kt += 4) {
+                MX_STAGE(kt, 0, 1)
+                MX_STAGE(kt + 1, 1, 0)
+                MX_STAGE(kt + 2, 0, 0)
+                MX_STAGE(kt + 3, 1, 0)
+            }
         }
+#undef MX_STAGE
         MX_SB;
-        // every wave passed the last barrier after reading its last stage, and
-        // its last loads (repeats of the last stage) went to the free buffer
-        __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // LDS free for the epilogue
-#undef MX_LD
-#undef MX_ISSUE
+#undef MX_LOAD_A
+#undef MX_LOAD_B
+#undef MX_LOAD_SC
+#undef MX_LOAD_AS
+#undef MX_LOAD_BS
+#undef MX_SC_OFF
 #undef MX_RD_A
 #undef MX_RD_B
 #undef MX_RD_S
-#undef MX_WAIT
-#undef MX_WAIT_S
+#undef MX_WAIT_F
+#undef MX_WAIT_W
 #undef MX_MFMA
-#undef MX_SB
 #undef MX_STEP
-        // every wave passed the last barrier after reading its last stage: LDS is free
-
-        // epilogue through LDS: lane -> row rr, columns cc .. cc+15 of a 32x32 tile
-        float* wb = (float*)lds + wid * 2 * (32 * 33 + 32);
-        float* wb2 = wb + 32 * 33 + 32;
-        const int rr = lane >> 1, cc = (lane & 1) * 16;
-        if (SWIGLU) {
-#define GM_EPI_SW(MI, NI)                                                                                \
+        // every wave has read its last stage; the next unit (published by
+        // thread 0 before this unit's K loop) gets its first loads now
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int next_unit = s_unit;
+        const int e_row0 = row0, e_row_end = row_end, e_nt = nt;
+        const bool e_valid = valid;
+        if (next_unit >= 0) setup(next_unit);
+        if (e_valid) {
+            int rbase = e_row0, ln = lane;
+            __asm__ volatile("" : "+v"(rbase), "+v"(ln));
+            const int rlim = e_row_end - rbase;  // rows of the tile that exist
+            if (SWIGLU) {
+                // this wave's LDS tile (32 x 33 floats) in its own B rows of
+                // stage buffer 1; the loop's last loads (repeats of the last
+                // stage, possibly into these rows) must have landed first:
+                // they precede the 27 (G = 4: 26) loads of setup (if it issued any)
+                if (next_unit >= 0 && valid) {
+                    if constexpr (G == 1) __asm__ volatile("s_waitcnt vmcnt(27)" ::: "memory");
+                    else __asm__ volatile("s_waitcnt vmcnt(26)" ::: "memory");
+                } else {
+                    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+                float* const wb = (float*)(lds + STB + OPB + wid * 64 * BKB);
+                const int rr = ln >> 1, cc = (ln & 1) * 16;
+#define MX_EPI_SW(MI, NI)                                                                                \
     {                                                                                                    \
-        GE_STAGE_TILE(wb, acc[MI][NI])                                                                   \
-        GE_STAGE_TILE(wb2, acc[MI][(NI) + 2])                                                            \
+        float hv[16];                                                                                    \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
+            hv[q] = silu(agpr_read(acc[MI][NI][q])) * agpr_read(acc[MI][(NI) + 2][q]);                   \
+        GE_STAGE_TILE(wb, hv)                                                                            \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
-        float hv[16], gv[16], uv[16];                                                                    \
+        float v[16];                                                                                     \
         float amax = 0.f;                                                                                \
         _Pragma("unroll") for (int j = 0; j < 16; ++j) {                                                 \
-            gv[j] = wb[rr * 33 + cc + j];                                                                \
-            uv[j] = wb2[rr * 33 + cc + j];                                                               \
-            hv[j] = silu(gv[j]) * uv[j];                                                                 \
-            amax = fmaxf(amax, fabsf(hv[j]));                                                            \
+            v[j] = wb[rr * 33 + cc + j];                                                                 \
+            amax = fmaxf(amax, fabsf(v[j]));                                                             \
         }                                                                                                \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
         amax = fmaxf(amax, __shfl_xor(amax, 1, 64));                                                     \
-        const int r = row0 + wm * 64 + (MI) * 32 + rr;                                                   \
-        const int f = nt * 128 + wn * 64 + (NI) * 32 + cc;                                               \
-        if (r < row_end && f < p.n_out) {                                                                \
+        const int r = wm * 128 + (MI) * 32 + rr;                                                         \
+        const int f = e_nt * 128 + wn * 64 + (NI) * 32 + cc;                                             \
+        if (r < rlim && f < p.n_out) {                                                                   \
             const int se = mx_shared_exp(amax);                                                          \
             uint32_t w4[4];                                                                              \
-            _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
-                w4[j] = (uint32_t)e4m3_rne(ldexpf(hv[4 * j], -se)) |                                     \
-                        ((uint32_t)e4m3_rne(ldexpf(hv[4 * j + 1], -se)) << 8) |                          \
-                        ((uint32_t)e4m3_rne(ldexpf(hv[4 * j + 2], -se)) << 16) |                         \
-                        ((uint32_t)e4m3_rne(ldexpf(hv[4 * j + 3], -se)) << 24);                          \
-            *(uint4*)(p.C + (size_t)r * p.n_out + f) = make_uint4(w4[0], w4[1], w4[2], w4[3]);           \
-            if ((lane & 1) == 0) p.Cs[(size_t)r * (p.n_out / 32) + f / 32] = (uint8_t)(se + 127);        \
-            if (p.stash) {                                                                               \
-                uint4* gs = (uint4*)(p.stash + (size_t)r * 2 * p.n_out + f);                             \
-                uint4* us = (uint4*)(p.stash + (size_t)r * 2 * p.n_out + p.n_out + f);                   \
-                _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                         \
-                    gs[j] = GE_PACK8(gv, 8 * j);                                                         \
-                    us[j] = GE_PACK8(uv, 8 * j);                                                         \
+            _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                \
+                w4[j] = (uint32_t)e4m3_rne(ldexpf(v[4 * j], -se)) |                                      \
+                        ((uint32_t)e4m3_rne(ldexpf(v[4 * j + 1], -se)) << 8) |                           \
+                        ((uint32_t)e4m3_rne(ldexpf(v[4 * j + 2], -se)) << 16) |                          \
+                        ((uint32_t)e4m3_rne(ldexpf(v[4 * j + 3], -se)) << 24);                           \
+            const size_t row = (size_t)(rbase + r);                                                      \
+            *(uint4*)(p.C + row * p.n_out + f) = make_uint4(w4[0], w4[1], w4[2], w4[3]);                 \
+            if ((ln & 1) == 0) p.Cs[row * (p.n_out / 32) + f / 32] = (uint8_t)(se + 127);                \
+        }                                                                                                \
+        if (p.stash) {                                                                                   \
+            _Pragma("unroll") for (int gu = 0; gu < 2; ++gu) {                                           \
+                float tv[16];                                                                            \
+                _Pragma("unroll") for (int q = 0; q < 16; ++q)                                           \
+                    tv[q] = agpr_read(acc[MI][(NI) + 2 * gu][q]);                                        \
+                GE_STAGE_TILE(wb, tv)                                                                    \
+                __builtin_amdgcn_s_waitcnt(0xC07F);                                                      \
+                float sv[16];                                                                            \
+                _Pragma("unroll") for (int j = 0; j < 16; ++j) sv[j] = wb[rr * 33 + cc + j];             \
+                __builtin_amdgcn_s_waitcnt(0xC07F);                                                      \
+                if (r < rlim && f < p.n_out) {                                                           \
+                    uint4* const d = (uint4*)(p.stash + (size_t)(rbase + r) * 2 * p.n_out + gu * p.n_out + f); \
+                    d[0] = GE_PACK8(sv, 0);                                                              \
+                    d[1] = GE_PACK8(sv, 8);                                                              \
                 }                                                                                        \
             }                                                                                            \
         }                                                                                                \
-    }
-            GM_EPI_SW(0, 0) GM_EPI_SW(0, 1) GM_EPI_SW(1, 0) GM_EPI_SW(1, 1)
-#undef GM_EPI_SW
-        } else {
-#define GM_EPI_DN(MI, NI)                                                                                \
+    }                                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);
+                MX_EPI_SW(0, 0) MX_EPI_SW(0, 1) MX_EPI_SW(1, 0) MX_EPI_SW(1, 1)
+                MX_EPI_SW(2, 0) MX_EPI_SW(2, 1) MX_EPI_SW(3, 0) MX_EPI_SW(3, 1)
+#undef MX_EPI_SW
+                // this wave's reads of its LDS tile are done before its loads refill those rows
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+            } else {
+                const int lc = ln & 31, lr = 4 * (ln >> 5);
+                uint16_t* const cbase = p.Cb + (size_t)rbase * p.n_out;
+                const int n = e_nt * kTile + wn * 128 + 4 * lc;  // this lane's columns n .. n + 3
+#define MX_EPI_DN(MI)                                                                                    \
     {                                                                                                    \
-        GE_STAGE_TILE(wb, acc[MI][NI])                                                                   \
-        __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
-        float v[16];                                                                                     \
-        _Pragma("unroll") for (int j = 0; j < 16; ++j) v[j] = wb[rr * 33 + cc + j];                      \
-        __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
-        const int r = row0 + wm * 64 + (MI) * 32 + rr;                                                   \
-        const int n = nt * kMxBN + wn * 128 + (NI) * 32 + cc;                                            \
-        if (r < row_end && n < p.n_out) {                                                                \
-            uint4* dst = (uint4*)(p.Cb + (size_t)r * p.n_out + n);                                       \
-            _Pragma("unroll") for (int j = 0; j < 2; ++j) dst[j] = GE_PACK8(v, 8 * j);                  \
+        const int rb0 = wm * 128 + (MI) * 32;                                                            \
+        uint2 w[16];                                                                                     \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
+            w[q] = make_uint2(pack_bf16x2(agpr_read(acc[MI][0][q]), agpr_read(acc[MI][1][q])),           \
+                              pack_bf16x2(agpr_read(acc[MI][2][q]), agpr_read(acc[MI][3][q])));          \
+        if (n < p.n_out) {                                                                               \
+            uint16_t* const dst = cbase + (size_t)(rb0 + lr) * p.n_out + n;                              \
+            if (rb0 + 32 <= rlim) {                                                                      \
+                _Pragma("unroll") for (int q = 0; q < 16; ++q)                                           \
+                    *(uint2*)(dst + (size_t)(8 * (q >> 2) + (q & 3)) * p.n_out) = w[q];                  \
+            } else {                                                                                     \
+                _Pragma("unroll") for (int q = 0; q < 16; ++q)                                           \
+                    if (rb0 + lr + 8 * (q >> 2) + (q & 3) < rlim)                                        \
+                        *(uint2*)(dst + (size_t)(8 * (q >> 2) + (q & 3)) * p.n_out) = w[q];              \
+            }                                                                                            \
         }                                                                                                \
+    }                                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);
+                MX_EPI_DN(0) MX_EPI_DN(1) MX_EPI_DN(2) MX_EPI_DN(3)
+#undef MX_EPI_DN
+            }
+        }  // valid
+        if (next_unit >= 0) load_b_half();
+        unit = next_unit;
     }
-            GM_EPI_DN(0, 0) GM_EPI_DN(0, 1) GM_EPI_DN(0, 2) GM_EPI_DN(0, 3)
-            GM_EPI_DN(1, 0) GM_EPI_DN(1, 1) GM_EPI_DN(1, 2) GM_EPI_DN(1, 3)
-#undef GM_EPI_DN
-        }
-        __syncthreads();  // LDS reused by the next tile's loads
-    }
+    // no direct-to-LDS load may still be in flight when the wave ends
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef MX_SB
 }
 
 }  // namespace gemm

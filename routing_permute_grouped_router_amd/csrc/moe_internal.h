@@ -78,11 +78,14 @@ hipError_t launch_down_gemm_f32(const moe_config& c, const float* h, const float
 // MXFP8
 hipError_t launch_quantize_mxfp8(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                                  hipStream_t s);
+// Workspace of the MXFP8 GEMMs: their 8 work-queue counters.
+size_t gemm_mxfp8_ws_bytes(const moe_config& c);
 hipError_t launch_swiglu_gemm_mxfp8(const moe_config& c, const uint8_t* xp, const uint8_t* xp_scale,
                                     const uint8_t* w1, const uint8_t* w1_scale, const int32_t* offsets, uint8_t* h,
-                                    uint8_t* h_scale, uint16_t* stash, hipStream_t s);
+                                    uint8_t* h_scale, uint16_t* stash, void* ws, hipStream_t s);
 hipError_t launch_down_gemm_mxfp8(const moe_config& c, const uint8_t* h, const uint8_t* h_scale, const uint8_t* w2,
-                                  const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, hipStream_t s);
+                                  const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, void* ws,
+                                  hipStream_t s);
 
 // Backward GEMMs (bf16 / f32 storage).
 size_t bwd_workspace_bytes(const moe_config& c);

@@ -55,24 +55,51 @@ namespace moe {
 
 int gemm_persistent_grid(int64_t max_tiles);
 
+namespace {
+
+// Zeroes the 8 work-queue counters (a kernel rather than a memset node, so
+// the calls stay safe to capture in a graph).
+__global__ void zero_mx_sched_kernel(int* sched) {
+    if (threadIdx.x < gemm::kXcds) sched[threadIdx.x] = 0;
+}
+
+int64_t rows_cap(const moe_config& c) { return (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1); }
+
+}  // namespace
+
+size_t gemm_mxfp8_ws_bytes(const moe_config& c) { return c.dtype == MOE_MXFP8 ? 256 : 0; }
+
 hipError_t launch_swiglu_gemm_mxfp8(const moe_config& c, const uint8_t* xp, const uint8_t* xp_scale,
                                     const uint8_t* w1, const uint8_t* w1_scale, const int32_t* offsets, uint8_t* h,
-                                    uint8_t* h_scale, uint16_t* stash, hipStream_t s) {
-    const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
-    const int64_t max_tiles = (R_cap / gemm::kMxBM + c.E) * ((c.F + 127) / 128);
+                                    uint8_t* h_scale, uint16_t* stash, void* ws, hipStream_t s) {
+    const int64_t max_tiles = (rows_cap(c) / gemm::kTile + c.E) * ((c.F + 127) / 128);
     if (max_tiles == 0) return hipSuccess;
-    gemm::MxArgs a{xp, xp_scale, w1, w1_scale, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, h_scale, nullptr, stash};
-    gemm::grouped_gemm_mxfp8<true><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+    gemm::MxArgs a{xp, xp_scale, w1, w1_scale, offsets, c.E, c.H, (int)rows_cap(c), c.F, 2 * c.F, h, h_scale,
+                   nullptr, stash, (int*)ws};
+    zero_mx_sched_kernel<<<1, 64, 0, s>>>(a.sched);
+    // scale words loaded four stages at a time when each row's scales are a
+    // whole number of 16-byte pieces (K a multiple of 512)
+    if (a.K % 512 == 0)
+        gemm::grouped_gemm_mxfp8<true, 4><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+    else
+        gemm::grouped_gemm_mxfp8<true, 1><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_down_gemm_mxfp8(const moe_config& c, const uint8_t* h, const uint8_t* h_scale, const uint8_t* w2,
-                                  const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, hipStream_t s) {
-    const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
-    const int64_t max_tiles = (R_cap / gemm::kMxBM + c.E) * ((c.H + gemm::kMxBN - 1) / gemm::kMxBN);
+                                  const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, void* ws,
+                                  hipStream_t s) {
+    const int64_t max_tiles = (rows_cap(c) / gemm::kTile + c.E) * ((c.H + gemm::kTile - 1) / gemm::kTile);
     if (max_tiles == 0) return hipSuccess;
-    gemm::MxArgs a{h, h_scale, w2, w2_scale, offsets, c.E, c.F, (int)R_cap, c.H, c.H, nullptr, nullptr, yp, nullptr};
-    gemm::grouped_gemm_mxfp8<false><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+    gemm::MxArgs a{h, h_scale, w2, w2_scale, offsets, c.E, c.F, (int)rows_cap(c), c.H, c.H, nullptr, nullptr,
+                   yp, nullptr, (int*)ws};
+    zero_mx_sched_kernel<<<1, 64, 0, s>>>(a.sched);
+    // scale words loaded four stages at a time when each row's scales are a
+    // whole number of 16-byte pieces (K a multiple of 512)
+    if (a.K % 512 == 0)
+        gemm::grouped_gemm_mxfp8<false, 4><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+    else
+        gemm::grouped_gemm_mxfp8<false, 1><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

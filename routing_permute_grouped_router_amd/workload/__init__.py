@@ -229,4 +229,6 @@ def small_shapes() -> list:
         MoEShape("small_skewed_bf16", 512, 256, 128, 16, 4, "softmax", True, "bf16", zipf_bias=1.2,
                  backward=True, seed=2004),
         MoEShape("small_mxfp8", 260, 256, 128, 16, 4, "sigmoid", True, "mxfp8", seed=2005),
+        # K = 512 in both GEMMs: the scale words of four stages per load
+        MoEShape("small_mxfp8_k512", 300, 512, 512, 8, 2, "sigmoid", True, "mxfp8", seed=2006),
     ]

@@ -40,23 +40,28 @@ def test_quantize_matches_oracle_bitwise():
     assert np.array_equal(to_host(codes), c_o)
 
 
-def _forward_mx(s, x_f32, w1_f32, w2_f32, logits):
+def _forward_mx(s, x_f32, w1_f32, w2_f32, logits, training=False):
     cfg = cfg_of(s)
     xq, xs = _gpu_quantize(x_f32)
     w1q, w1s = _gpu_quantize(w1_f32)
     w2q, w2s = _gpu_quantize(w2_f32)
-    buf = moe.alloc_forward(cfg)
+    buf = moe.alloc_forward(cfg, training=training)
     buf["y"].fill_(float("nan"))
+    if training:
+        buf["gu_stash"].fill_(float("nan"))
     moe.moe_forward(cfg, to_dev(logits, "f32"), xq, w1q, w2q, buf, x_scale=xs, w1_scale=w1s, w2_scale=w2s)
     torch.cuda.synchronize()
     return buf, (xq, xs)
 
 
-def test_forward_mxfp8_small_full_parity():
-    s = [x for x in wl.small_shapes() if x.dtype == "mxfp8"][0]
+@pytest.mark.parametrize("name", ["small_mxfp8", "small_mxfp8_k512"])
+def test_forward_mxfp8_small_full_parity(name):
+    """Every output of a small MXFP8 layer in full: K = 256 / 128 (one
+    scale word per stage) and K = 512 (scale words of four stages per load)."""
+    s = [x for x in wl.small_shapes() if x.name == name][0]
     w = wl.Workload(s)
     x, w1, w2, lg = w.x(), w.w1(), w.w2(), w.logits()
-    buf, (xq, xs) = _forward_mx(s, x, w1, w2, lg)
+    buf, (xq, xs) = _forward_mx(s, x, w1, w2, lg, training=True)
     xq_o, xs_o = orc.mx_quantize(x)
     w1q_o, w1s_o = orc.mx_quantize(w1)
     w2q_o, w2s_o = orc.mx_quantize(w2)
@@ -68,8 +73,11 @@ def test_forward_mxfp8_small_full_parity():
     n = int(offsets[-1])
     assert np.array_equal(to_host(buf["xp"])[:n], orc.permute(xq_o, row_map, n))
     assert np.array_equal(to_host(buf["xp_scale"])[:n], orc.permute(xs_o, row_map, n))
-    ref = orc.forward_tokens(s, np.arange(s.T), xq_o, w1q_o, w2q_o, idx, wt, xs_o, w1s_o, w2s_o)
+    ref = orc.forward_tokens(s, np.arange(s.T), xq_o, w1q_o, w2q_o, idx, wt, xs_o, w1s_o, w2s_o, want_stash=True)
     rm = row_map.ravel()
+    # the optional bf16 g | u stash of the SwiGLU GEMM
+    st = decode("bf16", to_host(buf["gu_stash"])[rm])
+    assert rel_err(st, decode("bf16", ref["stash"].reshape(-1, 2 * s.F))) < TOL["bf16"]
     h = orc.mx_dequantize(to_host(buf["h"])[rm], to_host(buf["h_scale"])[rm])
     h_ref = orc.mx_dequantize(ref["h"].reshape(-1, s.F), ref["h_scale"].reshape(-1, s.F // 32))
     assert rel_err(h, h_ref) < TOL["mxfp8"]
