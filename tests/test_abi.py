@@ -122,3 +122,23 @@ def test_python_layer_type_errors():
     cfg = moe.MoEConfig(4, 128, 64, 8, 2)
     with pytest.raises(ValueError):  # CPU tensors are refused before any call
         moe.moe_route(cfg, torch.zeros(4, 8), torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2))
+
+
+def test_device_e4m3_rounding_matches_oracle(tmp_path):
+    """The E4M3 rounding the MXFP8 kernels use (compiled for the host) against
+    the oracle's encoder on every float in [2^-10, 2^10) of both signs: the
+    range the quantiser and the SwiGLU epilogue feed it after the block scale
+    (below 2^-10 everything rounds to 0 and is sampled)."""
+    import subprocess
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    lib = root / "oracle" / "liboracle.so"
+    if not lib.exists():
+        pytest.skip("oracle library not built")
+    exe = tmp_path / "e4m3_check"
+    subprocess.run(["/opt/rocm/bin/hipcc", "-O2", "-std=c++17", "--offload-arch=gfx950", "-x", "hip",
+                    "-I", str(root / "include"), "-I", str(root / "routing_permute_grouped_router_amd" / "csrc"),
+                    str(root / "tests" / "e4m3_check.cpp"), "-x", "none", str(lib), "-Wl,-rpath," + str(lib.parent),
+                    "-o", str(exe)], check=True, capture_output=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]
