@@ -512,61 +512,93 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
             GB_EPI_DG(3, 0) GB_EPI_DG(3, 1) GB_EPI_DG(3, 2) GB_EPI_DG(3, 3)
 #undef GB_EPI_DG
         } else {
-            // C = [dG | dU] with rows of 2N bf16; the stash holds [g | u] alike
+            // C = [dG | dU] with rows of 2N bf16; the stash holds [g | u] alike.
+            // dH goes through LDS so that each lane handles 8 consecutive
+            // columns of a row: 16-byte stash loads and 16-byte dG / dU
+            // stores (a quarter of the memory instructions of pairs).  Each
+            // wavefront stages its 128 x 128 float32 sub-tile in two halves of
+            // 64 rows in its own 32 KiB of the stage buffers (free once every
+            // wave's last loads landed; the barrier at the next tile's claim
+            // keeps the next loads out until every wave is done).  A half is
+            // [64 rows][32 chunks of 4 floats], chunk c of row r at position
+            // c ^ ((c >> 4) & 1) ^ (((r >> 2) & 1) << 3): the MFMA-layout
+            // writes (rows r and r + 4 per instruction) and the 8-column reads
+            // are both free of bank conflicts.
+            __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
             const int rlim = row_end - mbase;
-            const uint32_t ldw = (uint32_t)p.N;  // words per 2N-wide row
-            uint32_t* const cbase = (uint32_t*)(p.C + (size_t)mbase * 2 * p.N);
-            const uint32_t* const sbase = (const uint32_t*)(p.stash + (size_t)mbase * 2 * p.N);
-            uint32_t gs[4][8], us[4][8];
-#define GB_LOAD_STASH(MI)                                                                                \
-    _Pragma("unroll") for (int ni = 0; ni < 4; ++ni) {                                                   \
-        const int n = min(n0 + wn * 128 + ni * 32 + c2, p.N - 2);                                        \
-        _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                                  \
-            const int r = min(wm * 128 + (MI) * 32 + prow + 8 * (q >> 1) + 2 * (q & 1), rlim - 1);       \
-            const uint32_t o = (uint32_t)r * ldw + (uint32_t)n / 2;                                      \
-            gs[ni][q] = sbase[o];                                                                        \
-            us[ni][q] = sbase[o + ldw / 2];                                                              \
+            const int N = p.N;
+            uint8_t* const stg = &lds[0][0][0] + wid * 32768;
+            const int hh = ln >> 5, ca = (ln & 31) >> 2;
+            uint8_t* wa[4];  // this lane's write address for fragment ni (row 0 of the half)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                wa[ni] = stg + hh * 2048 + ((((ni ^ hh) << 3) | (ca ^ ((ni >> 1) & 1))) << 4) + (ln & 3) * 4;
+            const int kc8 = ln & 15, rq = ln >> 4;  // this lane's column group (8 columns) and row in a pass
+            const uint8_t* ra[2][2];                // read addresses [pass parity][lo, hi chunk]
+#pragma unroll
+            for (int par = 0; par < 2; ++par)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+                    ra[par][hl] = stg + rq * 512 + ((((2 * kc8 + hl) ^ (kc8 >> 3)) ^ (par << 3)) << 4);
+            const int ncol = n0 + wn * 128 + 8 * kc8;  // this lane's first column
+            const bool col_ok = ncol < N;
+            const uint16_t* const sbase = p.stash + (size_t)mbase * 2 * N + ncol;
+            uint16_t* const cbase = p.C + (size_t)mbase * 2 * N + ncol;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                // stash rows of the half's 16 passes (4 rows each) through a
+                // ring of 8: passes 0..7 are loaded before the staging, pass
+                // p + 8 right after pass p is consumed, so loads stay in flight
+                uint4 gq[8], uq[8];
+#define GB_LOAD_STASH(PS)                                                                                \
+    {                                                                                                    \
+        const int r_ = wm * 128 + hf * 64 + 4 * (PS) + rq;                                               \
+        if (col_ok && r_ < rlim) {                                                                       \
+            gq[(PS) & 7] = *(const uint4*)(sbase + (size_t)r_ * 2 * N);                                  \
+            uq[(PS) & 7] = *(const uint4*)(sbase + (size_t)r_ * 2 * N + N);                              \
         }                                                                                                \
     }
-#define GB_EPI_SG(MI, NI)                                                                                \
-    {                                                                                                    \
-        const int n = n0 + wn * 128 + (NI) * 32 + c2;                                                    \
-        const int rb0 = wm * 128 + (MI) * 32;                                                            \
-        float v[16];                                                                                     \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
-        float2 dh[8];                                                                                    \
-        pair_f32(v, lane, dh);                                                                           \
-        if (n < p.N) {                                                                                   \
-            _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                              \
-                const int r = rb0 + prow + 8 * (q >> 1) + 2 * (q & 1);                                   \
-                float rg[2], ru[2];                                                                      \
-                const float dhv[2] = {dh[q].x, dh[q].y};                                                 \
-                _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                          \
-                    const float g = __uint_as_float(h ? (gs[NI][q] & 0xffff0000u) : (gs[NI][q] << 16));  \
-                    const float u = __uint_as_float(h ? (us[NI][q] & 0xffff0000u) : (us[NI][q] << 16));  \
-                    const float sg = sigmoid_fast(g);                                                    \
-                    rg[h] = dhv[h] * u * sg * (1.0f + g * (1.0f - sg));                                  \
-                    ru[h] = dhv[h] * g * sg;                                                             \
-                }                                                                                        \
-                if (r < rlim) {                                                                          \
-                    uint32_t* dst = cbase + (uint32_t)r * ldw + (uint32_t)n / 2;                          \
-                    dst[0] = pack_bf16x2(rg[0], rg[1]);                                                  \
-                    dst[ldw / 2] = pack_bf16x2(ru[0], ru[1]);                                            \
-                }                                                                                        \
-            }                                                                                            \
-        }                                                                                                \
-    }                                                                                                    \
-    __builtin_amdgcn_sched_barrier(0);
-            GB_LOAD_STASH(0)
-            GB_EPI_SG(0, 0) GB_EPI_SG(0, 1) GB_EPI_SG(0, 2) GB_EPI_SG(0, 3)
-            GB_LOAD_STASH(1)
-            GB_EPI_SG(1, 0) GB_EPI_SG(1, 1) GB_EPI_SG(1, 2) GB_EPI_SG(1, 3)
-            GB_LOAD_STASH(2)
-            GB_EPI_SG(2, 0) GB_EPI_SG(2, 1) GB_EPI_SG(2, 2) GB_EPI_SG(2, 3)
-            GB_LOAD_STASH(3)
-            GB_EPI_SG(3, 0) GB_EPI_SG(3, 1) GB_EPI_SG(3, 2) GB_EPI_SG(3, 3)
+#pragma unroll
+                for (int ps = 0; ps < 8; ++ps) GB_LOAD_STASH(ps)
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q)
+                            *(float*)(wa[ni] + (32 * m2 + 8 * (q >> 2) + (q & 3)) * 512) =
+                                agpr_read(acc[2 * hf + m2][ni][q]);
+#pragma unroll
+                for (int ps = 0; ps < 16; ++ps) {
+                    const int r = wm * 128 + hf * 64 + 4 * ps + rq;
+                    const float4 lo = *(const float4*)(ra[ps & 1][0] + ps * 2048);
+                    const float4 hi = *(const float4*)(ra[ps & 1][1] + ps * 2048);
+                    const float dh[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    const uint32_t gw[4] = {gq[ps & 7].x, gq[ps & 7].y, gq[ps & 7].z, gq[ps & 7].w};
+                    const uint32_t uw[4] = {uq[ps & 7].x, uq[ps & 7].y, uq[ps & 7].z, uq[ps & 7].w};
+                    if (ps < 8) GB_LOAD_STASH(ps + 8)
+                    uint32_t dg[4], du[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float rg[2], ru[2];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const float g = __uint_as_float(h ? (gw[j] & 0xffff0000u) : (gw[j] << 16));
+                            const float u = __uint_as_float(h ? (uw[j] & 0xffff0000u) : (uw[j] << 16));
+                            const float sg = sigmoid_fast(g);
+                            rg[h] = dh[2 * j + h] * u * sg * (1.0f + g * (1.0f - sg));
+                            ru[h] = dh[2 * j + h] * g * sg;
+                        }
+                        dg[j] = pack_bf16x2(rg[0], rg[1]);
+                        du[j] = pack_bf16x2(ru[0], ru[1]);
+                    }
+                    if (col_ok && r < rlim) {
+                        *(uint4*)(cbase + (size_t)r * 2 * N) = make_uint4(dg[0], dg[1], dg[2], dg[3]);
+                        *(uint4*)(cbase + (size_t)r * 2 * N + N) = make_uint4(du[0], du[1], du[2], du[3]);
+                    }
+                }
 #undef GB_LOAD_STASH
-#undef GB_EPI_SG
+            }
         }
     }
 }
