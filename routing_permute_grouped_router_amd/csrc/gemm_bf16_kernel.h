@@ -22,9 +22,9 @@
 // the epilogue forms silu(g) * u in registers.
 //
 // The grid is persistent (one block per CU); block b runs on XCD b % 8 and
-// the tile sequence is cut into 8 contiguous ranges, one per XCD, walked in a
-// grouped order (GM M-tiles sweep the N-tiles) so the blocks of an XCD share A
-// rows and B columns in its L2.
+// the tile sequence (expert by expert; tile_of) is cut into 8 contiguous
+// ranges, one per XCD, so the blocks of an XCD share A rows and B columns in
+// its L2; the blocks take their units through per-XCD work queues (below).
 #pragma once
 
 #include "moe_internal.h"
@@ -124,42 +124,14 @@ __device__ __forceinline__ int swz(int row) {
     make_uint4(pack_bf16x2((V)[(O)], (V)[(O) + 1]), pack_bf16x2((V)[(O) + 2], (V)[(O) + 3]),            \
                pack_bf16x2((V)[(O) + 4], (V)[(O) + 5]), pack_bf16x2((V)[(O) + 6], (V)[(O) + 7]))
 
-// Direct epilogue helpers.  A 32 x 32 fp32 accumulator tile holds, in lane l
-// and slot q, row 8 (q / 4) + 4 (l / 32) + q % 4 of column l % 32.  pair_bf16
-// rounds it to bf16 (nearest even) and regroups it with the neighbouring lane
-// (l ^ 1, a DPP quad permute) so that word p of lane l holds the two adjacent
-// columns (l % 32) & ~1 and +1 of row pair_row(p, l).
-// An accumulator element read out of its AGPR where it is used, so the
-// compiler does not copy every accumulator to VGPRs as the K loop ends.
+// A 32 x 32 fp32 accumulator tile holds, in lane l and slot q, row
+// 8 (q / 4) + 4 (l / 32) + q % 4 of column l % 32.  agpr_read reads one
+// element out of its AGPR where it is used, so the compiler does not copy
+// every accumulator to VGPRs as the K loop ends.
 __device__ __forceinline__ float agpr_read(float a) {
     float v;
     __asm__ volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
     return v;
-}
-__device__ __forceinline__ float swap_lane1(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ int pair_row(int p, int lane) {
-    return 8 * (p >> 1) + 4 * (lane >> 5) + 2 * (p & 1) + (lane & 1);
-}
-__device__ __forceinline__ void pair_bf16(const float (&v)[16], int lane, uint32_t (&out)[8]) {
-    const bool odd = lane & 1;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const float recv = swap_lane1(odd ? v[2 * p] : v[2 * p + 1]);
-        const float lo = odd ? recv : v[2 * p], hi = odd ? v[2 * p + 1] : recv;
-        out[p] = pack_bf16x2(lo, hi);
-    }
-}
-
-// The same regrouping without rounding: float32 pairs.
-__device__ __forceinline__ void pair_f32(const float (&v)[16], int lane, float2 (&out)[8]) {
-    const bool odd = lane & 1;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const float recv = swap_lane1(odd ? v[2 * p] : v[2 * p + 1]);
-        out[p] = make_float2(odd ? recv : v[2 * p], odd ? v[2 * p + 1] : recv);
-    }
 }
 
 // Output column of B row r of a forward tile (tile-relative).  A wavefront

@@ -450,129 +450,92 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
 #undef GB_SUBSTEP_LA
 #undef GB_SUBSTEP_LB
 #undef GB_SUBSTEP_NR
-        // Epilogue straight from the accumulators (no LDS): each 32 x 32 tile
-        // becomes 8 pairs of adjacent columns of one row per lane (a DPP swap
-        // with lane ^ 1), stored as 8-byte float32 pairs (weight gradients) or
-        // 4-byte bf16 pairs.  The SwiGLU backward loads the matching (g, u)
-        // pairs of the stash a 32-row block ahead of their use.
+        // Epilogue through LDS, so that each lane handles 8 consecutive
+        // columns of a row: 16-byte bf16 stores (dgrad), two 16-byte float32
+        // stores (weight gradients), 16-byte stash loads and dG / dU stores
+        // (dgrad + dSwiGLU), a quarter (half for float32) of the memory
+        // instructions of lane pairs.  Each wavefront stages its 128 x 128
+        // float32 sub-tile in two halves of 64 rows in its own 32 KiB of the
+        // stage buffers (free once every wave's last loads landed; the barrier
+        // at the next tile's claim keeps the next loads out until every wave
+        // is done).  A half is [64 rows][32 chunks of 4 floats], chunk c of row
+        // r at position c ^ ((c >> 4) & 1) ^ (((r >> 2) & 1) << 3): the
+        // MFMA-layout writes (rows r and r + 4 per instruction) and the
+        // 8-column reads are both free of bank conflicts.
         // Opaque copies of the tile's first row and of the lane index: the
         // address arithmetic below then stays after the K loop (it is not
         // hoisted out of the tile loop, where it would hold registers).
         int mbase = m0, ln = lane;
         __asm__ volatile("" : "+v"(mbase), "+v"(ln));
-        const int c2 = (ln & 31) & ~1;
-        const int prow = 4 * (ln >> 5) + (ln & 1);
-        if (WG) {
-            const int mlim = p.M - mbase;
-#define GB_EPI_WG(MI, NI)                                                                                \
-    {                                                                                                    \
-        const int n = n0 + wn * 128 + (NI) * 32 + c2;                                                    \
-        const int rb0 = wm * 128 + (MI) * 32;                                                            \
-        float v[16];                                                                                     \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
-        float2 vp[8];                                                                                    \
-        pair_f32(v, lane, vp);                                                                           \
-        if (n < p.N) {                                                                                   \
-            float2* dst = (float2*)(cw + (size_t)(mbase + rb0 + prow) * p.N + n);                        \
-            const uint32_t ld2 = (uint32_t)p.N / 2;                                                      \
-            _Pragma("unroll") for (int q = 0; q < 8; ++q)                                                \
-                if (rb0 + prow + 8 * (q >> 1) + 2 * (q & 1) < mlim)                                      \
-                    dst[(8 * (q >> 1) + 2 * (q & 1)) * ld2] = vp[q];                                     \
-        }                                                                                                \
-    }                                                                                                    \
-    __builtin_amdgcn_sched_barrier(0);
-            GB_EPI_WG(0, 0) GB_EPI_WG(0, 1) GB_EPI_WG(0, 2) GB_EPI_WG(0, 3)
-            GB_EPI_WG(1, 0) GB_EPI_WG(1, 1) GB_EPI_WG(1, 2) GB_EPI_WG(1, 3)
-            GB_EPI_WG(2, 0) GB_EPI_WG(2, 1) GB_EPI_WG(2, 2) GB_EPI_WG(2, 3)
-            GB_EPI_WG(3, 0) GB_EPI_WG(3, 1) GB_EPI_WG(3, 2) GB_EPI_WG(3, 3)
-#undef GB_EPI_WG
-        } else if (MODE == kDgrad) {
-            const int rlim = row_end - mbase;
-            uint16_t* const cbase = p.C + (size_t)mbase * p.N;
-            const uint32_t ldw = (uint32_t)p.N / 2;
-#define GB_EPI_DG(MI, NI)                                                                                \
-    {                                                                                                    \
-        const int n = n0 + wn * 128 + (NI) * 32 + c2;                                                    \
-        const int rb0 = wm * 128 + (MI) * 32;                                                            \
-        float v[16];                                                                                     \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q) v[q] = agpr_read(acc[MI][NI][q]);                 \
-        uint32_t vp[8];                                                                                  \
-        pair_bf16(v, lane, vp);                                                                          \
-        if (n < p.N) {                                                                                   \
-            uint32_t* dst = (uint32_t*)(cbase + (uint32_t)((rb0 + prow) * p.N + n));                     \
-            _Pragma("unroll") for (int q = 0; q < 8; ++q)                                                \
-                if (rb0 + prow + 8 * (q >> 1) + 2 * (q & 1) < rlim)                                      \
-                    dst[(8 * (q >> 1) + 2 * (q & 1)) * ldw] = vp[q];                                     \
-        }                                                                                                \
-    }                                                                                                    \
-    __builtin_amdgcn_sched_barrier(0);
-            GB_EPI_DG(0, 0) GB_EPI_DG(0, 1) GB_EPI_DG(0, 2) GB_EPI_DG(0, 3)
-            GB_EPI_DG(1, 0) GB_EPI_DG(1, 1) GB_EPI_DG(1, 2) GB_EPI_DG(1, 3)
-            GB_EPI_DG(2, 0) GB_EPI_DG(2, 1) GB_EPI_DG(2, 2) GB_EPI_DG(2, 3)
-            GB_EPI_DG(3, 0) GB_EPI_DG(3, 1) GB_EPI_DG(3, 2) GB_EPI_DG(3, 3)
-#undef GB_EPI_DG
-        } else {
-            // C = [dG | dU] with rows of 2N bf16; the stash holds [g | u] alike.
-            // dH goes through LDS so that each lane handles 8 consecutive
-            // columns of a row: 16-byte stash loads and 16-byte dG / dU
-            // stores (a quarter of the memory instructions of pairs).  Each
-            // wavefront stages its 128 x 128 float32 sub-tile in two halves of
-            // 64 rows in its own 32 KiB of the stage buffers (free once every
-            // wave's last loads landed; the barrier at the next tile's claim
-            // keeps the next loads out until every wave is done).  A half is
-            // [64 rows][32 chunks of 4 floats], chunk c of row r at position
-            // c ^ ((c >> 4) & 1) ^ (((r >> 2) & 1) << 3): the MFMA-layout
-            // writes (rows r and r + 4 per instruction) and the 8-column reads
-            // are both free of bank conflicts.
-            __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-            const int rlim = row_end - mbase;
-            const int N = p.N;
-            uint8_t* const stg = &lds[0][0][0] + wid * 32768;
-            const int hh = ln >> 5, ca = (ln & 31) >> 2;
-            uint8_t* wa[4];  // this lane's write address for fragment ni (row 0 of the half)
+        __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        const int N = p.N;
+        const int rlim = WG ? p.M - mbase : row_end - mbase;  // rows of the tile that exist
+        uint8_t* const stg = &lds[0][0][0] + wid * 32768;
+        const int hh = ln >> 5, ca = (ln & 31) >> 2;
+        uint8_t* wa[4];  // this lane's write address for fragment ni (row 0 of the half)
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                wa[ni] = stg + hh * 2048 + ((((ni ^ hh) << 3) | (ca ^ ((ni >> 1) & 1))) << 4) + (ln & 3) * 4;
-            const int kc8 = ln & 15, rq = ln >> 4;  // this lane's column group (8 columns) and row in a pass
-            const uint8_t* ra[2][2];                // read addresses [pass parity][lo, hi chunk]
+        for (int ni = 0; ni < 4; ++ni)
+            wa[ni] = stg + hh * 2048 + ((((ni ^ hh) << 3) | (ca ^ ((ni >> 1) & 1))) << 4) + (ln & 3) * 4;
+        const int kc8 = ln & 15, rq = ln >> 4;  // this lane's column group (8 columns) and row in a pass
+        const uint8_t* ra[2][2];                // read addresses [pass parity][lo, hi chunk]
 #pragma unroll
-            for (int par = 0; par < 2; ++par)
+        for (int par = 0; par < 2; ++par)
 #pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-                    ra[par][hl] = stg + rq * 512 + ((((2 * kc8 + hl) ^ (kc8 >> 3)) ^ (par << 3)) << 4);
-            const int ncol = n0 + wn * 128 + 8 * kc8;  // this lane's first column
-            const bool col_ok = ncol < N;
-            const uint16_t* const sbase = p.stash + (size_t)mbase * 2 * N + ncol;
-            uint16_t* const cbase = p.C + (size_t)mbase * 2 * N + ncol;
+            for (int hl = 0; hl < 2; ++hl)
+                ra[par][hl] = stg + rq * 512 + ((((2 * kc8 + hl) ^ (kc8 >> 3)) ^ (par << 3)) << 4);
+        const int ncol = n0 + wn * 128 + 8 * kc8;  // this lane's first column
+        const bool col_ok = ncol < N;
+        // row 0 of the tile at this lane's columns: weight gradient (float32,
+        // N per row), dgrad (bf16, N per row), dgrad + dSwiGLU (bf16, 2N per
+        // row, stash alike)
+        const int ldc = MODE == kDgradDswiglu ? 2 * N : N;
+        float* const wbase = WG ? cw + (size_t)mbase * N + ncol : nullptr;
+        uint16_t* const cbase = WG ? nullptr : p.C + (size_t)mbase * ldc + ncol;
+        const uint16_t* const sbase = MODE == kDgradDswiglu ? p.stash + (size_t)mbase * ldc + ncol : nullptr;
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                // stash rows of the half's 16 passes (4 rows each) through a
-                // ring of 8: passes 0..7 are loaded before the staging, pass
-                // p + 8 right after pass p is consumed, so loads stay in flight
-                uint4 gq[8], uq[8];
+        for (int hf = 0; hf < 2; ++hf) {
+            // dgrad + dSwiGLU: stash rows of the half's 16 passes (4 rows each)
+            // through a ring of 8: passes 0..7 are loaded before the staging,
+            // pass p + 8 right after pass p is consumed
+            uint4 gq[8], uq[8];
 #define GB_LOAD_STASH(PS)                                                                                \
     {                                                                                                    \
         const int r_ = wm * 128 + hf * 64 + 4 * (PS) + rq;                                               \
         if (col_ok && r_ < rlim) {                                                                       \
-            gq[(PS) & 7] = *(const uint4*)(sbase + (size_t)r_ * 2 * N);                                  \
-            uq[(PS) & 7] = *(const uint4*)(sbase + (size_t)r_ * 2 * N + N);                              \
+            gq[(PS) & 7] = *(const uint4*)(sbase + (size_t)r_ * ldc);                                    \
+            uq[(PS) & 7] = *(const uint4*)(sbase + (size_t)r_ * ldc + N);                                \
         }                                                                                                \
     }
+            if (MODE == kDgradDswiglu) {
 #pragma unroll
                 for (int ps = 0; ps < 8; ++ps) GB_LOAD_STASH(ps)
+            }
 #pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2)
+            for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
+                for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-                        for (int q = 0; q < 16; ++q)
-                            *(float*)(wa[ni] + (32 * m2 + 8 * (q >> 2) + (q & 3)) * 512) =
-                                agpr_read(acc[2 * hf + m2][ni][q]);
+                    for (int q = 0; q < 16; ++q)
+                        *(float*)(wa[ni] + (32 * m2 + 8 * (q >> 2) + (q & 3)) * 512) =
+                            agpr_read(acc[2 * hf + m2][ni][q]);
 #pragma unroll
-                for (int ps = 0; ps < 16; ++ps) {
-                    const int r = wm * 128 + hf * 64 + 4 * ps + rq;
-                    const float4 lo = *(const float4*)(ra[ps & 1][0] + ps * 2048);
-                    const float4 hi = *(const float4*)(ra[ps & 1][1] + ps * 2048);
+            for (int ps = 0; ps < 16; ++ps) {
+                const int r = wm * 128 + hf * 64 + 4 * ps + rq;
+                const bool ok = col_ok && r < rlim;
+                const float4 lo = *(const float4*)(ra[ps & 1][0] + ps * 2048);
+                const float4 hi = *(const float4*)(ra[ps & 1][1] + ps * 2048);
+                if (WG) {
+                    if (ok) {
+                        float4* const d = (float4*)(wbase + (size_t)r * N);
+                        d[0] = lo;
+                        d[1] = hi;
+                    }
+                } else if (MODE == kDgrad) {
+                    if (ok)
+                        *(uint4*)(cbase + (size_t)r * ldc) = make_uint4(
+                            pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w), pack_bf16x2(hi.x, hi.y),
+                            pack_bf16x2(hi.z, hi.w));
+                } else {
                     const float dh[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                     const uint32_t gw[4] = {gq[ps & 7].x, gq[ps & 7].y, gq[ps & 7].z, gq[ps & 7].w};
                     const uint32_t uw[4] = {uq[ps & 7].x, uq[ps & 7].y, uq[ps & 7].z, uq[ps & 7].w};
@@ -592,13 +555,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
                         dg[j] = pack_bf16x2(rg[0], rg[1]);
                         du[j] = pack_bf16x2(ru[0], ru[1]);
                     }
-                    if (col_ok && r < rlim) {
-                        *(uint4*)(cbase + (size_t)r * 2 * N) = make_uint4(dg[0], dg[1], dg[2], dg[3]);
-                        *(uint4*)(cbase + (size_t)r * 2 * N + N) = make_uint4(du[0], du[1], du[2], du[3]);
+                    if (ok) {
+                        *(uint4*)(cbase + (size_t)r * ldc) = make_uint4(dg[0], dg[1], dg[2], dg[3]);
+                        *(uint4*)(cbase + (size_t)r * ldc + N) = make_uint4(du[0], du[1], du[2], du[3]);
                     }
                 }
-#undef GB_LOAD_STASH
             }
+#undef GB_LOAD_STASH
         }
     }
 }
