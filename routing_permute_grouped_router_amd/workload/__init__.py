@@ -231,4 +231,7 @@ def small_shapes() -> list:
         MoEShape("small_mxfp8", 260, 256, 128, 16, 4, "sigmoid", True, "mxfp8", seed=2005),
         # K = 512 in both GEMMs: the scale words of four stages per load
         MoEShape("small_mxfp8_k512", 300, 512, 512, 8, 2, "sigmoid", True, "mxfp8", seed=2006),
+        # skewed routing (empty experts) and 16-row groups (zero padding rows)
+        MoEShape("small_mxfp8_skew_align", 300, 512, 256, 16, 4, "softmax", True, "mxfp8", align=16,
+                 zipf_bias=1.2, seed=2007),
     ]

@@ -54,10 +54,11 @@ def _forward_mx(s, x_f32, w1_f32, w2_f32, logits, training=False):
     return buf, (xq, xs)
 
 
-@pytest.mark.parametrize("name", ["small_mxfp8", "small_mxfp8_k512"])
+@pytest.mark.parametrize("name", ["small_mxfp8", "small_mxfp8_k512", "small_mxfp8_skew_align"])
 def test_forward_mxfp8_small_full_parity(name):
     """Every output of a small MXFP8 layer in full: K = 256 / 128 (one
-    scale word per stage) and K = 512 (scale words of four stages per load)."""
+    scale word per stage), K = 512 (scale words of four stages per load), and
+    skewed routing with 16-row groups (empty experts, zero padding rows)."""
     s = [x for x in wl.small_shapes() if x.name == name][0]
     w = wl.Workload(s)
     x, w1, w2, lg = w.x(), w.w1(), w.w2(), w.logits()
@@ -83,6 +84,12 @@ def test_forward_mxfp8_small_full_parity(name):
     assert rel_err(h, h_ref) < TOL["mxfp8"]
     assert rel_err(decode("bf16", to_host(buf["yp"])[rm]), decode("bf16", ref["yp"].reshape(-1, s.H))) < TOL["mxfp8"]
     assert rel_err(decode("bf16", to_host(buf["y"])), decode("bf16", ref["y"])) < TOL["mxfp8"]
+    if s.align > 1:  # padding rows of Xp are zero codes with zero scales
+        pad = src_map[:n] < 0
+        assert pad.any(), "the alignment should leave padding rows"
+        assert not to_host(buf["xp"])[:n][pad].any() and not to_host(buf["xp_scale"])[:n][pad].any()
+    if s.zipf_bias:
+        assert (counts == 0).any(), "the skewed routing should leave some experts empty"
 
 
 def test_forward_mxfp8_full_size():
