@@ -161,6 +161,64 @@ def route(logits, k: int, score: str = "softmax", renorm: bool = False):
     return idx, w
 
 
+def route_bwd(logits, idx, row_map, dy, yp, fmt: str, score: str = "softmax", renorm: bool = False,
+              tokens=None):
+    """Routing backward, float64.
+
+    The forward gives route (t, j) the weight w[t, j] of its expert idx[t, j]
+    as or_route computes it: the softmax over all E logits p, either as is or
+    renormalised over the k chosen (p / (sum of the chosen p + 1e-20)), or the
+    sigmoid of the chosen logits normalised over the k chosen (s / (sum s +
+    1e-20)); the combine forms y[t] = sum_j w[t, j] Yp[row_map[t, j]].  For an
+    upstream gradient dy of y:
+        dw[t, j]      = <dy[t], Yp[row_map[t, j]]>   (0 for a dropped route, row -1)
+        dlogits[t, e] = sum_j dw[t, j] * d w[t, j] / d logits[t, e]
+    written out by the chain rule through the normalisation above; the top-k
+    choice is piecewise constant and contributes nothing.
+
+    dy [T, H] and yp [R, H] are stored arrays of format fmt; tokens (optional)
+    selects the rows of the result.  Returns (dw [n, k], dlogits [n, E])."""
+    lg = np.asarray(logits, np.float32)
+    T, E = lg.shape
+    k = idx.shape[1]
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    n = len(tok)
+    rm = np.asarray(row_map).reshape(T, k)[tok]
+    sel = np.asarray(idx)[tok].astype(np.int64)
+    dyv = decode(fmt, np.asarray(dy)[tok])
+    dw = np.zeros((n, k))
+    for j in range(k):
+        ok = rm[:, j] >= 0
+        if ok.any():
+            dw[ok, j] = np.einsum("th,th->t", dyv[ok], decode(fmt, np.asarray(yp)[rm[ok, j]]))
+    l = lg[tok].astype(np.float64)
+    ok_sel = (sel >= 0) & (sel < E)
+    sel_c = np.where(ok_sel, sel, 0)
+    dl = np.zeros((n, E))
+    rows = np.arange(n)[:, None]
+    if score == "softmax":
+        m = l.max(axis=1, keepdims=True)
+        a = np.exp(l - m)
+        p = a / a.sum(axis=1, keepdims=True)
+        sc = np.where(ok_sel, p[rows, sel_c], 0.0)          # p of the chosen experts
+        if renorm:
+            S = sc.sum(axis=1, keepdims=True) + 1e-20
+            dsc = dw / S - (dw * sc).sum(axis=1, keepdims=True) / S ** 2
+        else:
+            dsc = dw
+        dsc = np.where(ok_sel, dsc, 0.0)
+        # d p_c / d l_e = p_c (delta_ce - p_e)
+        np.add.at(dl, (np.broadcast_to(rows, sel_c.shape), sel_c), dsc * sc)
+        dl -= p * (dsc * sc).sum(axis=1, keepdims=True)
+    else:
+        s = np.where(ok_sel, 1.0 / (1.0 + np.exp(-l[rows, sel_c])), 0.0)
+        S = s.sum(axis=1, keepdims=True) + 1e-20
+        ds = dw / S - (dw * s).sum(axis=1, keepdims=True) / S ** 2
+        ds = np.where(ok_sel, ds, 0.0)
+        np.add.at(dl, (np.broadcast_to(rows, sel_c.shape), sel_c), ds * s * (1.0 - s))
+    return dw, dl
+
+
 def group(idx, E: int, align: int = 1, R_cap: int | None = None):
     idx = _c(idx, np.int32)
     T, k = idx.shape
