@@ -244,6 +244,20 @@ def main():
         for i, n in enumerate(names):
             acc[n] += ev[i].elapsed_time(ev[i + 1])
     kern_ms = {n: acc[n] / args.steps for n in names}
+    if s.backward:
+        # the routing backward (gradients of the top-k weights and router
+        # logits): timed on its own, outside the step
+        dlog = torch.empty(s.T, s.E, dtype=torch.float32, device=dev)
+        dwr = torch.empty(s.T, s.k, dtype=torch.float32, device=dev)
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        moe.moe_route_bwd(cfg, dy, buf["yp"], logits, buf["idx"], buf["row_map"], dlog, dw=dwr)
+        r0.record(stream)
+        for _ in range(args.steps):
+            moe.moe_route_bwd(cfg, dy, buf["yp"], logits, buf["idx"], buf["row_map"], dlog, dw=dwr)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        kern_ms["route_bwd"] = r0.elapsed_time(r1) / args.steps
+        names.append("route_bwd")
 
     R, T, H, F, E, k = s.R, s.T, s.H, s.F, s.E, s.k
     esz = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32}[s.dtype]
@@ -256,6 +270,13 @@ def main():
         "combine": R * H * osz + T * H * osz + T * k * 8,
         "swiglu_gemm": R * H * esz + E * 2 * F * H * esz + R * F * esz,
         "down_gemm": R * F * esz + E * H * F * esz + R * H * osz,
+        # backward bandwidth kernels: dY read, dYp rows written (padding rows
+        # zeroed too), w and maps; dXp rows read, dX written, map
+        "combine_bwd": T * H * osz + s.R_cap * H * osz + T * k * 8 + s.R_cap * 4,
+        "permute_bwd": R * H * osz + T * H * osz + T * k * 4,
+        # routing backward: dY and the routed Yp rows read, logits read,
+        # dlogits and dw written, idx and row_map read
+        "route_bwd": T * H * osz + R * H * osz + 2 * T * E * 4 + T * k * 12,
     }
     peak_mm = {"f32": PEAK_FP32_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "mxfp8": PEAK_FP8_TFLOPS}[s.dtype]
     kern = {}

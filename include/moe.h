@@ -196,8 +196,24 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
 /* [TE-EP]: weight gradients of experts with no rows are zero; d_x keeps x's */
 /* dtype.  [CUDNN]: the backward re-dispatches the output gradient along the */
 /* forward routes and recomputes SwiGLU from the saved stash.  The routing   */
-/* weights are constants here (their gradient is not part of this path).     */
+/* weights are constants here; moe_route_bwd gives their gradient.           */
 /* ---------------------------------------------------------------------- */
+
+/* Routing backward ([TE-EP] router commits; [CUDNN] per-top-k combine): for
+ * an upstream gradient dy of the combine's output y[t] = sum_j w[t,j] Yp[...],
+ *   dw[t][j]      = sum_c dy[t][c] * Yp[row_map[t,j]][c]   (float32; 0 for a
+ *                   dropped route, row -1)
+ *   dlogits[t][e] = sum_j dw[t][j] * d w[t][j] / d logits[t][e]
+ * through moe_route's normalisation (softmax over all E; softmax renormalised
+ * over the k selected; sigmoid normalised over the k selected); the top-k
+ * choice itself has no gradient, so with renormalisation or the sigmoid only
+ * the selected experts' logits get a nonzero gradient.  dy [T,H] and yp
+ * [R_cap,H] in the output dtype (bf16 for BF16 and MXFP8 storage, float for
+ * F32); logits [T,E] float (moe_route's input); idx [T,k] and row_map [T,k]
+ * from moe_route / moe_permute; dw (optional, NULL to skip) [T,k] float;
+ * dlogits [T,E] float, every entry written. */
+moe_status moe_route_bwd(const moe_config* cfg, const void* dy, const void* yp, const float* logits,
+                         const int32_t* idx, const int32_t* row_map, float* dw, float* dlogits, void* stream);
 
 /* dYp[row_map[t,j]] = round(w[t,j] * dy[t]) for every route (t,j) whose
  * row_map entry is a row in [0, R_cap); dYp[r] = 0 for every row r in

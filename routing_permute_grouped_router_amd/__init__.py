@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     moe_backward,
     moe_combine,
     moe_combine_bwd,
+    moe_route_bwd,
     moe_forward,
     moe_grouped_down_bwd,
     moe_grouped_down_gemm,

@@ -101,6 +101,7 @@ _SIGS = {
     "moe_grouped_down_gemm": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_combine": (ctypes.c_int, [CFG, P, P, P, P, P]),
     "moe_forward": (ctypes.c_int, [CFG] + [P] * 22 + [ctypes.c_size_t, P]),
+    "moe_route_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P]),
     "moe_combine_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P]),
     "moe_grouped_down_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_grouped_swiglu_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -273,6 +274,17 @@ def moe_forward(cfg: MoEConfig, logits, x, w1, w2, buf: dict, x_scale=None, w1_s
         _ptr(buf["yp"], "yp", od, (R, H)),
         _ptr(buf.get("gu_stash"), "gu_stash", od, (R, 2 * F), optional=True),
         _ptr(buf.get("err"), "err", torch.int32, (1,), optional=True), wp, wb, _stream(stream)))
+
+
+def moe_route_bwd(cfg: MoEConfig, dy, yp, logits, idx, row_map, dlogits, dw=None, stream=None):
+    """Gradients of the top-k weights (dw, optional) and of the router logits."""
+    c = cfg.c()
+    _check(load_library().moe_route_bwd(
+        ctypes.byref(c), _ptr(dy, "dy", cfg.out_dtype, (cfg.T, cfg.H)),
+        _ptr(yp, "yp", cfg.out_dtype, (cfg.R_cap, cfg.H)), _ptr(logits, "logits", torch.float32, (cfg.T, cfg.E)),
+        _ptr(idx, "idx", torch.int32, (cfg.T, cfg.k)), _ptr(row_map, "row_map", torch.int32, (cfg.T, cfg.k)),
+        _ptr(dw, "dw", torch.float32, (cfg.T, cfg.k), optional=True),
+        _ptr(dlogits, "dlogits", torch.float32, (cfg.T, cfg.E)), _stream(stream)))
 
 
 def moe_combine_bwd(cfg: MoEConfig, dy, row_map, src_map, offsets, w, dyp, stream=None):

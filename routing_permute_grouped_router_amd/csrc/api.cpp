@@ -250,6 +250,22 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
     return moe_combine(cfg, yp, row_map, w, y, stream);
 }
 
+moe_status moe_route_bwd(const moe_config* cfg, const void* dy, const void* yp, const float* logits,
+                         const int32_t* idx, const int32_t* row_map, float* dw, float* dlogits, void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    if ((st = check_shapes(*cfg))) return st;
+    if (cfg->T == 0) return MOE_OK;
+    REQUIRE(dy);
+    REQUIRE(yp);
+    REQUIRE(logits);
+    REQUIRE(idx);
+    REQUIRE(row_map);
+    REQUIRE(dlogits);
+    return hip_status(launch_route_bwd(*cfg, dy, yp, logits, idx, row_map, dw, dlogits, as_stream(stream)),
+                      "moe_route_bwd");
+}
+
 moe_status moe_combine_bwd(const moe_config* cfg, const void* dy, const int32_t* row_map, const int32_t* src_map,
                            const int32_t* offsets, const float* w, void* dyp, void* stream) {
     moe_status st = check_config(cfg);

@@ -61,6 +61,8 @@ hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const int32_t
                               const int32_t* offsets, const float* w, void* dyp, hipStream_t s);
 hipError_t launch_permute_bwd(const moe_config& c, const void* dxp, const int32_t* row_map, void* dx,
                               hipStream_t s);
+hipError_t launch_route_bwd(const moe_config& c, const void* dy, const void* yp, const float* logits,
+                            const int32_t* idx, const int32_t* row_map, float* dw, float* dlogits, hipStream_t s);
 
 // Grouped GEMMs.
 // ws: gemm_bf16_ws_bytes(c) bytes (work-queue counters and the partial sums
