@@ -60,6 +60,12 @@ def test_null_pointers_rejected():
     assert b"logits" in lib.moe_last_error()
     assert lib.moe_combine(ctypes.byref(c), 1, None, 1, 1, None) == b.MOE_ERR_INVALID_ARG
     assert lib.moe_route(None, 1, 1, 1, None) == b.MOE_ERR_INVALID_ARG
+    # routing backward: every input and dlogits required, dw optional
+    assert lib.moe_route_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, None, None, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_bwd(ctypes.byref(c), 1, None, 1, 1, 1, None, 1, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_bwd(None, 1, 1, 1, 1, 1, None, 1, None) == b.MOE_ERR_INVALID_ARG
+    # T = 0 is a no-op that touches nothing
+    assert lib.moe_route_bwd(ctypes.byref(_cfg(T=0)), None, None, None, None, None, None, None, None) == b.MOE_OK
 
 
 def test_unsupported_shapes():
