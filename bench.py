@@ -259,6 +259,35 @@ def main():
         kern_ms["route_bwd"] = r0.elapsed_time(r1) / args.steps
         names.append("route_bwd")
 
+    variants = None
+    if not s.backward:
+        # The gather form of the forward (no materialised Xp: the gate/up GEMM
+        # reads x[src_map[r] / k] itself), timed as whole steps and as the
+        # gather GEMM alone; reported beside the step, which stays the
+        # materialised path.
+        bg = dict(buf, xp=None, xp_scale=None)
+
+        def gstep():
+            moe.moe_forward(cfg, logits, x, w1, w2, bg, **scales)
+
+        for _ in range(2):
+            gstep()
+        g0, g1, g2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(args.steps):
+            gstep()
+        g1.record(stream)
+        for _ in range(args.steps):
+            moe.moe_grouped_swiglu_gemm_gather(cfg, x, buf["src_map"], buf["counts"], w1, buf["offsets"], buf["h"],
+                                               buf["ws"], x_scale=g.get("x_scale"), w1_scale=g.get("w1_scale"),
+                                               h_scale=buf.get("h_scale"))
+        g2.record(stream)
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        variants = {"gather_forward": {"ms_per_step": round(gms, 4), "tokens_per_s": round(s.T / (gms * 1e-3), 1),
+                                       "swiglu_gemm_gather_ms": round(g1.elapsed_time(g2) / args.steps, 4)}}
+
     R, T, H, F, E, k = s.R, s.T, s.H, s.F, s.E, s.k
     esz = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32}[s.dtype]
     osz = 4 if s.dtype == "f32" else 2
@@ -369,6 +398,7 @@ def main():
         "kernels": kern,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "variants": variants,
         "wall_s_timed": round(t_wall, 3),
         "setup_s": round(t_gen, 1),
     }

@@ -137,7 +137,9 @@ moe_status moe_route(const moe_config* cfg, const float* logits, int32_t* idx, f
  * Within an expert, routes are in ascending (t, j) order, so every output is
  * deterministic.  MXFP8: x_scale rows travel with x into xp_scale (both NULL
  * otherwise).  err (optional, may be NULL) is incremented once per id
- * outside [-1, E).  ws: moe_workspace_size(cfg) bytes. */
+ * outside [-1, E).  xp NULL: the grouping only (counts .. src_map), for the
+ * gather form of the gate/up GEMM below; x, x_scale, xp_scale are then not
+ * read.  ws: moe_workspace_size(cfg) bytes. */
 moe_status moe_permute(const moe_config* cfg, const void* x, const uint8_t* x_scale, const int32_t* idx, void* xp,
                        uint8_t* xp_scale, int32_t* counts, int32_t* offsets, int32_t* row_map, int32_t* src_map,
                        int32_t* err, void* ws, size_t ws_bytes, void* stream);
@@ -159,6 +161,23 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const uint8_t* x_sc
 moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const uint8_t* xp_scale, const void* w1,
                                    const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
                                    void* gu_stash, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 3 with step 2's permutation folded into the operand loads, so that
+ * no Xp is materialised ([BLOCK] Diagram shows dispatch and the grouped GEMM
+ * as two steps; this variant computes their composition): as
+ * moe_grouped_swiglu_gemm, with row r of the grouped operand read as
+ * x[src_map[r] / k] (the token routed to row r) for the first counts[e] rows
+ * of expert e, and the padding rows of its group computed as zero rows.  h
+ * (+ h_scale) equals, bit for bit, what moe_grouped_swiglu_gemm writes from
+ * the Xp of moe_permute.  x [T,H] (+ x_scale [T,H/32] for MXFP8); src_map,
+ * counts, offsets from moe_permute (which may skip Xp: xp NULL).  No stash
+ * (a training forward keeps Xp for the weight gradient).  Needs
+ * T*H*element size < 4 GiB (MOE_ERR_UNSUPPORTED otherwise).  ws: as for
+ * moe_grouped_swiglu_gemm. */
+moe_status moe_grouped_swiglu_gemm_gather(const moe_config* cfg, const void* x, const uint8_t* x_scale,
+                                          const int32_t* src_map, const int32_t* counts, const void* w1,
+                                          const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
+                                          void* ws, size_t ws_bytes, void* stream);
 
 /* Step 4, grouped down GEMM ([BLOCK] down projection).  For every expert e
  * and row r in [offsets[e], offsets[e+1]):
@@ -183,7 +202,10 @@ moe_status moe_combine(const moe_config* cfg, const void* yp, const int32_t* row
  * yp, the output y [T,H], and gu_stash (NULL unless the backward will run).
  * Buffers another call would read later (idx .. src_map, xp, h, gu_stash) are
  * the routing state and saved tensors of the backward ([TE-EP]: no second
- * routing pass in the backward). */
+ * routing pass in the backward).  xp NULL (with xp_scale NULL and gu_stash
+ * NULL: inference): the permutation is fused into the gate/up GEMM
+ * (moe_grouped_swiglu_gemm_gather) and Xp is never written; the outputs are
+ * the same bit for bit. */
 moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x, const uint8_t* x_scale,
                        const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, void* y,
                        int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* row_map,

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     moe_combine,
     moe_combine_bwd,
     moe_route_bwd,
+    moe_grouped_swiglu_gemm_gather,
     moe_forward,
     moe_grouped_down_bwd,
     moe_grouped_down_gemm,

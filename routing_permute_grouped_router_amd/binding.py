@@ -102,6 +102,7 @@ _SIGS = {
     "moe_combine": (ctypes.c_int, [CFG, P, P, P, P, P]),
     "moe_forward": (ctypes.c_int, [CFG] + [P] * 22 + [ctypes.c_size_t, P]),
     "moe_route_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P]),
+    "moe_grouped_swiglu_gemm_gather": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_combine_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P]),
     "moe_grouped_down_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_grouped_swiglu_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -208,8 +209,9 @@ def moe_permute(cfg: MoEConfig, x, idx, xp, counts, offsets, row_map, src_map, w
     _check(load_library().moe_permute(
         ctypes.byref(c), _ptr(x, "x", cfg.store_dtype, (cfg.T, cfg.H)),
         _ptr(x_scale, "x_scale", torch.uint8, (cfg.T, cfg.H // 32), optional=not mx),
-        _ptr(idx, "idx", torch.int32, (cfg.T, cfg.k)), _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.H)),
-        _ptr(xp_scale, "xp_scale", torch.uint8, (cfg.R_cap, cfg.H // 32), optional=not mx),
+        _ptr(idx, "idx", torch.int32, (cfg.T, cfg.k)),
+        _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.H), optional=True),
+        _ptr(xp_scale, "xp_scale", torch.uint8, (cfg.R_cap, cfg.H // 32), optional=not mx or xp is None),
         _ptr(counts, "counts", torch.int32, (cfg.E,)), _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)),
         _ptr(row_map, "row_map", torch.int32, (cfg.T, cfg.k)), _ptr(src_map, "src_map", torch.int32, (cfg.R_cap,)),
         _ptr(err, "err", torch.int32, (1,), optional=True), wp, wb, _stream(stream)))
@@ -229,6 +231,22 @@ def moe_grouped_swiglu_gemm(cfg: MoEConfig, xp, w1, offsets, h, ws, xp_scale=Non
         _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx),
         _ptr(gu_stash, "gu_stash", cfg.out_dtype, (cfg.R_cap, 2 * cfg.F), optional=True), wp, wb,
         _stream(stream)))
+
+
+def moe_grouped_swiglu_gemm_gather(cfg: MoEConfig, x, src_map, counts, w1, offsets, h, ws, x_scale=None,
+                                   w1_scale=None, h_scale=None, stream=None):
+    """The gate/up GEMM reading x[src_map[r] / k] for row r (no materialised Xp)."""
+    c = cfg.c()
+    mx = cfg.dtype == "mxfp8"
+    wp, wb = _ws(ws)
+    _check(load_library().moe_grouped_swiglu_gemm_gather(
+        ctypes.byref(c), _ptr(x, "x", cfg.store_dtype, (cfg.T, cfg.H)),
+        _ptr(x_scale, "x_scale", torch.uint8, (cfg.T, cfg.H // 32), optional=not mx),
+        _ptr(src_map, "src_map", torch.int32, (cfg.R_cap,)), _ptr(counts, "counts", torch.int32, (cfg.E,)),
+        _ptr(w1, "w1", cfg.store_dtype, (cfg.E, 2 * cfg.F, cfg.H)),
+        _ptr(w1_scale, "w1_scale", torch.uint8, (cfg.E, 2 * cfg.F, cfg.H // 32), optional=not mx),
+        _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
+        _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx), wp, wb, _stream(stream)))
 
 
 def moe_grouped_down_gemm(cfg: MoEConfig, h, w2, offsets, yp, ws, h_scale=None, w2_scale=None, stream=None):
@@ -268,8 +286,9 @@ def moe_forward(cfg: MoEConfig, logits, x, w1, w2, buf: dict, x_scale=None, w1_s
         _ptr(buf["y"], "y", od, (T, H)), _ptr(buf["idx"], "idx", torch.int32, (T, k)),
         _ptr(buf["w"], "w", torch.float32, (T, k)), _ptr(buf["counts"], "counts", torch.int32, (E,)),
         _ptr(buf["offsets"], "offsets", torch.int32, (E + 1,)), _ptr(buf["row_map"], "row_map", torch.int32, (T, k)),
-        _ptr(buf["src_map"], "src_map", torch.int32, (R,)), _ptr(buf["xp"], "xp", sd, (R, H)),
-        _ptr(buf.get("xp_scale"), "xp_scale", torch.uint8, (R, H // 32), optional=not mx),
+        _ptr(buf["src_map"], "src_map", torch.int32, (R,)),
+        _ptr(buf.get("xp"), "xp", sd, (R, H), optional=True),
+        _ptr(buf.get("xp_scale"), "xp_scale", torch.uint8, (R, H // 32), optional=not mx or buf.get("xp") is None),
         _ptr(buf["h"], "h", sd, (R, F)), _ptr(buf.get("h_scale"), "h_scale", torch.uint8, (R, F // 32), optional=not mx),
         _ptr(buf["yp"], "yp", od, (R, H)),
         _ptr(buf.get("gu_stash"), "gu_stash", od, (R, 2 * F), optional=True),

@@ -130,19 +130,21 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const uint8_t* x_sc
     REQUIRE(offsets);
     if (rows_capacity(c) > 0) REQUIRE(src_map);
     if (c.T > 0) {
-        REQUIRE(x);
         REQUIRE(idx);
-        REQUIRE(xp);
         REQUIRE(row_map);
-        if (c.dtype == MOE_MXFP8) {
-            REQUIRE(x_scale);
-            REQUIRE(xp_scale);
+        if (xp) {  // xp NULL: the grouping only (for the gather form of the gate/up GEMM)
+            REQUIRE(x);
+            if (c.dtype == MOE_MXFP8) {
+                REQUIRE(x_scale);
+                REQUIRE(xp_scale);
+            }
         }
     }
     if ((st = check_ws(c, ws, ws_bytes))) return st;
     hipStream_t s = as_stream(stream);
     if ((st = hip_status(launch_group(c, idx, counts, offsets, row_map, src_map, err, (int32_t*)ws, s), "moe_permute")))
         return st;
+    if (!xp) return MOE_OK;
     return hip_status(launch_permute_rows(c, x, x_scale, row_map, counts, offsets, xp, xp_scale, s), "moe_permute");
 }
 
@@ -163,19 +165,61 @@ moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const 
     switch (c.dtype) {
     case MOE_BF16:
         return hip_status(launch_swiglu_gemm_bf16(c, (const uint16_t*)xp, (const uint16_t*)w1, offsets, (uint16_t*)h,
-                                                  (uint16_t*)gu_stash, gemm_ws(c, ws), s),
+                                                  (uint16_t*)gu_stash, nullptr, nullptr, gemm_ws(c, ws), s),
                           "moe_grouped_swiglu_gemm");
     case MOE_F32:
         return hip_status(
-            launch_swiglu_gemm_f32(c, (const float*)xp, (const float*)w1, offsets, (float*)h, (float*)gu_stash, s),
+            launch_swiglu_gemm_f32(c, (const float*)xp, (const float*)w1, offsets, (float*)h, (float*)gu_stash,
+                                   nullptr, nullptr, s),
             "moe_grouped_swiglu_gemm");
     default:
         REQUIRE(xp_scale);
         REQUIRE(w1_scale);
         REQUIRE(h_scale);
         return hip_status(launch_swiglu_gemm_mxfp8(c, (const uint8_t*)xp, xp_scale, (const uint8_t*)w1, w1_scale,
-                                                   offsets, (uint8_t*)h, h_scale, (uint16_t*)gu_stash, gemm_ws(c, ws), s),
+                                                   offsets, (uint8_t*)h, h_scale, (uint16_t*)gu_stash, nullptr,
+                                                   nullptr, gemm_ws(c, ws), s),
                           "moe_grouped_swiglu_gemm");
+    }
+}
+
+moe_status moe_grouped_swiglu_gemm_gather(const moe_config* cfg, const void* x, const uint8_t* x_scale,
+                                          const int32_t* src_map, const int32_t* counts, const void* w1,
+                                          const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
+                                          void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    const moe_config& c = *cfg;
+    if ((st = check_shapes(c))) return st;
+    if (rows_capacity(c) == 0) return MOE_OK;
+    // the kernels address a row of x with a 32-bit byte offset
+    if ((int64_t)c.T * c.H * (c.dtype == MOE_F32 ? 4 : c.dtype == MOE_BF16 ? 2 : 1) >= ((int64_t)1 << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "the gather form needs T*H*element size < 4 GiB");
+    REQUIRE(x);
+    REQUIRE(src_map);
+    REQUIRE(counts);
+    REQUIRE(w1);
+    REQUIRE(offsets);
+    REQUIRE(h);
+    if ((st = check_ws(c, ws, ws_bytes))) return st;
+    hipStream_t s = as_stream(stream);
+    switch (c.dtype) {
+    case MOE_BF16:
+        return hip_status(launch_swiglu_gemm_bf16(c, (const uint16_t*)x, (const uint16_t*)w1, offsets, (uint16_t*)h,
+                                                  nullptr, src_map, counts, gemm_ws(c, ws), s),
+                          "moe_grouped_swiglu_gemm_gather");
+    case MOE_F32:
+        return hip_status(launch_swiglu_gemm_f32(c, (const float*)x, (const float*)w1, offsets, (float*)h, nullptr,
+                                                 src_map, counts, s),
+                          "moe_grouped_swiglu_gemm_gather");
+    default:
+        REQUIRE(x_scale);
+        REQUIRE(w1_scale);
+        REQUIRE(h_scale);
+        return hip_status(launch_swiglu_gemm_mxfp8(c, (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale,
+                                                   offsets, (uint8_t*)h, h_scale, nullptr, src_map, counts,
+                                                   gemm_ws(c, ws), s),
+                          "moe_grouped_swiglu_gemm_gather");
     }
 }
 
@@ -239,13 +283,19 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
         REQUIRE(w1_scale);
         REQUIRE(w2_scale);
     }
+    if (!xp && gu_stash) return fail(MOE_ERR_INVALID_ARG, "a training forward (gu_stash) needs xp");
     if ((st = moe_route(cfg, logits, idx, w, stream))) return st;
     if ((st = moe_permute(cfg, x, x_scale, idx, xp, xp_scale, counts, offsets, row_map, src_map, err, ws, ws_bytes,
                           stream)))
         return st;
-    if ((st = moe_grouped_swiglu_gemm(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, gu_stash, ws, ws_bytes,
-                                      stream)))
+    if (xp) {
+        if ((st = moe_grouped_swiglu_gemm(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, gu_stash, ws,
+                                          ws_bytes, stream)))
+            return st;
+    } else if ((st = moe_grouped_swiglu_gemm_gather(cfg, x, x_scale, src_map, counts, w1, w1_scale, offsets, h,
+                                                    h_scale, ws, ws_bytes, stream))) {
         return st;
+    }
     if ((st = moe_grouped_down_gemm(cfg, h, h_scale, w2, w2_scale, offsets, yp, ws, ws_bytes, stream))) return st;
     return moe_combine(cfg, yp, row_map, w, y, stream);
 }

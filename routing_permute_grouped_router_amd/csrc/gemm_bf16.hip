@@ -83,6 +83,8 @@ __global__ __launch_bounds__(256) void split_reduce_bf16(gemm::Args p, int nb) {
     if (row0 < 0 || row0 >= row_end) return;
     const int r_lo = c * kReduceRows, r_hi = min(r_lo + kReduceRows, row_end - row0);
     if (r_lo >= r_hi) return;
+    // gather: rows from a_end on are padding rows, stored as zeros
+    const int a_end = p.src_map ? min(p.offsets[e] + p.counts[e], row_end) : row_end;
     constexpr int kPart = gemm::kTile * gemm::kTile;
     const float* part = p.part + (size_t)(x * gemm::kSlotsPerXcd + j * q.S) * kPart;
     constexpr int kQuads = SWIGLU ? 32 : 64;  // float4 columns per row handled here
@@ -109,8 +111,10 @@ __global__ __launch_bounds__(256) void split_reduce_bf16(gemm::Args p, int nb) {
         }
         const size_t row = (size_t)(row0 + r);
         if (SWIGLU) {
-            *(uint2*)(p.C + row * p.n_out + n) = make_uint2(pack_bf16x2(silu(g.x) * u.x, silu(g.y) * u.y),
-                                                            pack_bf16x2(silu(g.z) * u.z, silu(g.w) * u.w));
+            *(uint2*)(p.C + row * p.n_out + n) =
+                row0 + r < a_end ? make_uint2(pack_bf16x2(silu(g.x) * u.x, silu(g.y) * u.y),
+                                              pack_bf16x2(silu(g.z) * u.z, silu(g.w) * u.w))
+                                 : make_uint2(0u, 0u);
             if (p.stash) {
                 *(uint2*)(p.stash + row * 2 * p.n_out + n) = make_uint2(pack_bf16x2(g.x, g.y), pack_bf16x2(g.z, g.w));
                 *(uint2*)(p.stash + row * 2 * p.n_out + p.n_out + n) =
@@ -137,11 +141,13 @@ hipError_t launch_bf16(gemm::Args a, int64_t max_tiles, void* ws, hipStream_t s)
 }  // namespace
 
 hipError_t launch_swiglu_gemm_bf16(const moe_config& c, const uint16_t* xp, const uint16_t* w1,
-                                   const int32_t* offsets, uint16_t* h, uint16_t* stash, void* ws, hipStream_t s) {
+                                   const int32_t* offsets, uint16_t* h, uint16_t* stash, const int32_t* src_map,
+                                   const int32_t* counts, void* ws, hipStream_t s) {
     const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.F + 127) / 128);
     if (max_tiles == 0) return hipSuccess;
-    gemm::Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash, nullptr, nullptr};
+    gemm::Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash, nullptr, nullptr,
+                 src_map, counts, c.k};
     return launch_bf16<true>(a, max_tiles, ws, s);
 }
 

@@ -54,6 +54,13 @@ struct Args {
     uint16_t* stash;        // SwiGLU only: [rows, 2F] or null
     int* sched;             // [kXcds] work-queue counters, zero at launch
     float* part;            // [kXcds * kSlotsPerXcd][kTile][kTile] partial sums of split tiles
+    // Gather (gate/up GEMM only; src_map null otherwise): A is x [T, K] and row
+    // r of the grouped operand is x[src_map[r] / gk]; the first counts[e] rows
+    // of expert e are routed, the rest of its group are padding rows, whose
+    // outputs are stored as zeros (as for the zero rows of a materialised Xp).
+    const int32_t* src_map;
+    const int32_t* counts;
+    int gk;
 };
 
 // Work queues.  The tiles are cut into kXcds contiguous ranges, one per XCD
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             koff[kk][par] = (uint32_t)(((2 * kk + (lane >> 5)) ^ swz<SWZ>(par * 32 + (lane & 31))) << 4);
     // State of the unit in flight, set by `setup`: its tile, K stages
     // [kb, ke), partial-sum slot (-1: whole tile), load offsets and bases.
-    int kb = 0, ke = 0, slot = -1, row0 = 0, row_end = 0, nt = 0;
+    int kb = 0, ke = 0, slot = -1, row0 = 0, row_end = 0, a_end = 0, nt = 0;
     bool valid = false;
     uint32_t aoff[LOADS], boff[LOADS];
     const char* abase = (const char*)p.A;
@@ -380,6 +387,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             kb = ke = 0;
             return;
         }
+        // rows with an A row of their own: all, or (gather) the routed rows
+        a_end = p.src_map ? __builtin_amdgcn_readfirstlane(min(offs[e] + p.counts[e], row_end)) : row_end;
         // first B row of the tile (SwiGLU: first gate row; the up rows are F rows further)
         const int brow0 = SWIGLU ? nt * 128 : nt * kTile;
         // Per-lane byte offsets of the A and B loads (K offset 0) against the
@@ -388,8 +397,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         for (int i = 0; i < LOADS; ++i) {
             const int r = wid * 64 + i * RPL + lrow;  // tile row 0..255
             const int chunk = lslot ^ swz<SWZ>(r);
-            const int ar = min(row0 + r, row_end - 1);
-            aoff[i] = (uint32_t)(((size_t)(ar - row0) * K + chunk * 8) * 2);
+            const int ar = min(row0 + r, a_end - 1);
+            aoff[i] = p.src_map ? (uint32_t)(((size_t)(p.src_map[ar] / p.gk) * K + chunk * 8) * 2)
+                                : (uint32_t)(((size_t)(ar - row0) * K + chunk * 8) * 2);
             int br;
             if (SWIGLU) {
                 const int f = min(nt * 128 + out_col_swiglu(r & 127), p.n_out - 1);
@@ -399,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             }
             boff[i] = (uint32_t)(((size_t)(br - brow0) * K + chunk * 8) * 2);
         }
-        abase = (const char*)(p.A + (size_t)row0 * K);
+        abase = p.src_map ? (const char*)p.A : (const char*)(p.A + (size_t)row0 * K);
         bbase = (const char*)(p.B + ((size_t)e * p.b_rows + brow0) * K);
         GG_SB;
         GG_ISSUE(kb, 0);
@@ -506,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         // first loads issued before this unit's epilogue.
         __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const int next_unit = s_unit;
-        const int e_row0 = row0, e_row_end = row_end, e_nt = nt, e_slot = slot;
+        const int e_row0 = row0, e_row_end = row_end, e_a_end = a_end, e_nt = nt, e_slot = slot;
         const bool e_valid = valid;
         if (next_unit >= 0) setup(next_unit);
         if (e_valid) {
@@ -524,6 +534,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         const int lc = ln & 31;             // this lane's column group
         const int lr = 4 * (ln >> 5);       // this lane's first row in a 32-row block
         const int rlim = e_row_end - rbase;  // rows of the tile that exist
+        const int alim = e_a_end - rbase;    // rows of the tile that are not padding (gather)
         // Store W[q] (type T) to row 8 (q / 4) + q % 4 past DST (LD elements
         // per row) for q = 0..15: the lane's rows of the 32-row block starting
         // at tile row RB0; rows are checked only when the block runs past the
@@ -583,6 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             const float g0 = agpr_read(acc[MI][0][q]), g1 = agpr_read(acc[MI][1][q]);                    \
             const float u0 = agpr_read(acc[MI][2][q]), u1 = agpr_read(acc[MI][3][q]);                    \
             hw[q] = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);                                           \
+            if (rb0 + lr + 8 * (q >> 2) + (q & 3) >= alim) hw[q] = 0; /* gather: padding rows */         \
         }                                                                                                \
         if (f < p.n_out) {                                                                               \
             uint16_t* const dst = cbase + (size_t)(rb0 + lr) * p.n_out + f;                              \

@@ -22,6 +22,12 @@ struct F32Args {
     int E, K, rows, n_out, b_rows;
     float* C;
     float* stash;
+    // gather (gate/up only): A is x [T, K], row r of the grouped operand is
+    // x[src_map[r] / gk]; the first counts[e] rows of expert e are routed, the
+    // rest are padding rows (zero A rows, as in a materialised Xp)
+    const int32_t* src_map;
+    const int32_t* counts;
+    int gk;
 };
 
 template <bool SWIGLU>
@@ -45,14 +51,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(F32Args p, int n_
     // load mapping: one float4 of A and one of B per thread per K slice
     const int lr = tid >> 2, lk = (tid & 3) * 4;
     const int a_row = row0 + lr;
+    const int a_end = p.src_map ? min(p.offsets[e] + p.counts[e], row_end) : row_end;
+    const float* const a_src =
+        a_row < a_end ? (p.src_map ? p.A + (size_t)(p.src_map[a_row] / p.gk) * p.K : p.A + (size_t)a_row * p.K)
+                      : nullptr;
     int b_row;
     if (SWIGLU) b_row = lr < 32 ? nt * 32 + lr : p.n_out + nt * 32 + (lr - 32);
     else b_row = nt * TN + lr;
 
     float acc[4][4] = {};
     for (int k0 = 0; k0 < p.K; k0 += TK) {
-        const float4 av = a_row < row_end ? *(const float4*)(p.A + (size_t)a_row * p.K + k0 + lk)
-                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 av = a_src ? *(const float4*)(a_src + k0 + lk) : make_float4(0.f, 0.f, 0.f, 0.f);
         const float4 bv = *(const float4*)(Be + (size_t)b_row * p.K + k0 + lk);
         As[lk + 0][lr] = av.x;
         As[lk + 1][lr] = av.y;
@@ -109,12 +118,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(F32Args p, int n_
 }  // namespace
 
 hipError_t launch_swiglu_gemm_f32(const moe_config& c, const float* xp, const float* w1, const int32_t* offsets,
-                                  float* h, float* stash, hipStream_t s) {
+                                  float* h, float* stash, const int32_t* src_map, const int32_t* counts,
+                                  hipStream_t s) {
     const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     const int n_tiles = c.F / 32;
     const int64_t blocks = (R_cap / TM + c.E) * n_tiles;
     if (blocks == 0) return hipSuccess;
-    F32Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash};
+    F32Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash, src_map, counts, c.k};
     grouped_gemm_f32_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(a, n_tiles);
     return hipGetLastError();
 }
@@ -125,7 +135,7 @@ hipError_t launch_down_gemm_f32(const moe_config& c, const float* h, const float
     const int n_tiles = c.H / TN;
     const int64_t blocks = (R_cap / TM + c.E) * n_tiles;
     if (blocks == 0) return hipSuccess;
-    F32Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr};
+    F32Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr, nullptr, nullptr, 1};
     grouped_gemm_f32_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(a, n_tiles);
     return hipGetLastError();
 }

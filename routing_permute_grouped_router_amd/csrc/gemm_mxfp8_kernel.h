@@ -34,6 +34,13 @@ struct MxArgs {
     uint16_t* Cb;            // down: Yp bf16 [rows][n_out]
     uint16_t* stash;         // SwiGLU, optional: bf16 g | u [rows][2 n_out]
     int* sched;              // 8 work-queue counters, zero at launch
+    // gather (SwiGLU only; src_map null otherwise): A / As are x codes / scales
+    // [T, K], row r of the grouped operand is x[src_map[r] / gk]; the first
+    // counts[e] rows of expert e are routed, the rest are padding rows, whose h
+    // is stored as zeros (codes 0, scale code 0, as for zero rows of Xp)
+    const int32_t* src_map;
+    const int32_t* counts;
+    int gk;
 };
 
 // ---------------------------------------------------------------------------
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
             for (int par = 0; par < 2; ++par)
                 kc[s][hl][par] = (uint32_t)(((4 * s + 2 * hl + half) ^ swz<1>(par * 32 + (lane & 31))) << 4);
 
-    int kb = 0, ke = 0, row0 = 0, row_end = 0, nt = 0;
+    int kb = 0, ke = 0, row0 = 0, row_end = 0, a_end = 0, nt = 0;
     bool valid = false;
     uint32_t aoff[LOADS], boff[LOADS], asoff = 0, bsoff = 0;
     const uint8_t* acodes = p.A;
@@ -253,7 +260,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
             kb = ke = 0;
             return;
         }
+        // rows with an A row of their own: all, or (gather) the routed rows
+        a_end = p.src_map ? __builtin_amdgcn_readfirstlane(min(offs[e] + p.counts[e], row_end)) : row_end;
         const int brow0 = SWIGLU ? nt * 128 : nt * kTile;
+        // row of A (tile-relative, or of x when gathering) that tile row r reads
+        auto a_row = [&](int r) -> int {
+            const int ar = min(row0 + r, a_end - 1);
+            return p.src_map ? p.src_map[ar] / p.gk : ar - row0;
+        };
         // B row (of the expert's matrix) that tile row r of B holds
         auto b_row = [&](int r) -> int {
             if (SWIGLU) {
@@ -266,17 +280,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         for (int i = 0; i < LOADS; ++i) {
             const int r = wid * 64 + i * RPL + lrow;  // tile row 0..255
             const int chunk = lslot ^ swz<1>(r);
-            aoff[i] = (uint32_t)((size_t)(min(row0 + r, row_end - 1) - row0) * K + chunk * 16);
+            aoff[i] = (uint32_t)((size_t)a_row(r) * K + chunk * 16);
             boff[i] = (uint32_t)((size_t)(b_row(r) - brow0) * K + chunk * 16);
         }
         {
             const int r = wid * 64 + lane;  // tile row of this lane's scale words
-            asoff = (uint32_t)((min(row0 + r, row_end - 1) - row0) * KS);
+            asoff = (uint32_t)(a_row(r) * KS);
             bsoff = (uint32_t)((b_row(r) - brow0) * KS);
         }
-        acodes = p.A + (size_t)row0 * K;
+        acodes = p.src_map ? p.A : p.A + (size_t)row0 * K;
         bcodes = p.B + ((size_t)e * p.b_rows + brow0) * K;
-        ascale = p.As + (size_t)row0 * KS;
+        ascale = p.src_map ? p.As : p.As + (size_t)row0 * KS;
         bscale = p.Bs + ((size_t)e * p.b_rows + brow0) * KS;
         MX_SB;
 #pragma unroll
@@ -426,13 +440,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         // thread 0 before this unit's K loop) gets its first loads now
         __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const int next_unit = s_unit;
-        const int e_row0 = row0, e_row_end = row_end, e_nt = nt;
+        const int e_row0 = row0, e_row_end = row_end, e_a_end = a_end, e_nt = nt;
         const bool e_valid = valid;
         if (next_unit >= 0) setup(next_unit);
         if (e_valid) {
             int rbase = e_row0, ln = lane;
             __asm__ volatile("" : "+v"(rbase), "+v"(ln));
             const int rlim = e_row_end - rbase;  // rows of the tile that exist
+            const int alim = e_a_end - rbase;    // rows of the tile that are not padding (gather)
             if (SWIGLU) {
                 // this wave's LDS tile (32 x 33 floats) in its own B rows of
                 // stage buffer 1; the loop's last loads (repeats of the last
@@ -455,8 +470,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
         float v[16];                                                                                     \
         float amax = 0.f;                                                                                \
+        const bool pad = wm * 128 + (MI) * 32 + rr >= alim; /* gather: padding rows are zeros */        \
         _Pragma("unroll") for (int j = 0; j < 16; ++j) {                                                 \
-            v[j] = wb[rr * 33 + cc + j];                                                                 \
+            v[j] = pad ? 0.f : wb[rr * 33 + cc + j];                                                     \
             amax = fmaxf(amax, fabsf(v[j]));                                                             \
         }                                                                                                \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \

@@ -68,12 +68,16 @@ hipError_t launch_route_bwd(const moe_config& c, const void* dy, const void* yp,
 // ws: gemm_bf16_ws_bytes(c) bytes (work-queue counters and the partial sums
 // of K-split tiles).
 size_t gemm_bf16_ws_bytes(const moe_config& c);
+// Gate/up GEMMs: with src_map and counts non-null, xp is x [T,H] (+ x_scale)
+// and row r of the grouped operand is x[src_map[r] / k] (the gather form).
 hipError_t launch_swiglu_gemm_bf16(const moe_config& c, const uint16_t* xp, const uint16_t* w1,
-                                   const int32_t* offsets, uint16_t* h, uint16_t* stash, void* ws, hipStream_t s);
+                                   const int32_t* offsets, uint16_t* h, uint16_t* stash, const int32_t* src_map,
+                                   const int32_t* counts, void* ws, hipStream_t s);
 hipError_t launch_down_gemm_bf16(const moe_config& c, const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
                                  uint16_t* yp, void* ws, hipStream_t s);
 hipError_t launch_swiglu_gemm_f32(const moe_config& c, const float* xp, const float* w1, const int32_t* offsets,
-                                  float* h, float* stash, hipStream_t s);
+                                  float* h, float* stash, const int32_t* src_map, const int32_t* counts,
+                                  hipStream_t s);
 hipError_t launch_down_gemm_f32(const moe_config& c, const float* h, const float* w2, const int32_t* offsets,
                                 float* yp, hipStream_t s);
 
@@ -84,7 +88,8 @@ hipError_t launch_quantize_mxfp8(const float* in, int64_t rows, int64_t cols, ui
 size_t gemm_mxfp8_ws_bytes(const moe_config& c);
 hipError_t launch_swiglu_gemm_mxfp8(const moe_config& c, const uint8_t* xp, const uint8_t* xp_scale,
                                     const uint8_t* w1, const uint8_t* w1_scale, const int32_t* offsets, uint8_t* h,
-                                    uint8_t* h_scale, uint16_t* stash, void* ws, hipStream_t s);
+                                    uint8_t* h_scale, uint16_t* stash, const int32_t* src_map,
+                                    const int32_t* counts, void* ws, hipStream_t s);
 hipError_t launch_down_gemm_mxfp8(const moe_config& c, const uint8_t* h, const uint8_t* h_scale, const uint8_t* w2,
                                   const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, void* ws,
                                   hipStream_t s);

@@ -71,11 +71,12 @@ size_t gemm_mxfp8_ws_bytes(const moe_config& c) { return c.dtype == MOE_MXFP8 ? 
 
 hipError_t launch_swiglu_gemm_mxfp8(const moe_config& c, const uint8_t* xp, const uint8_t* xp_scale,
                                     const uint8_t* w1, const uint8_t* w1_scale, const int32_t* offsets, uint8_t* h,
-                                    uint8_t* h_scale, uint16_t* stash, void* ws, hipStream_t s) {
+                                    uint8_t* h_scale, uint16_t* stash, const int32_t* src_map,
+                                    const int32_t* counts, void* ws, hipStream_t s) {
     const int64_t max_tiles = (rows_cap(c) / gemm::kTile + c.E) * ((c.F + 127) / 128);
     if (max_tiles == 0) return hipSuccess;
     gemm::MxArgs a{xp, xp_scale, w1, w1_scale, offsets, c.E, c.H, (int)rows_cap(c), c.F, 2 * c.F, h, h_scale,
-                   nullptr, stash, (int*)ws};
+                   nullptr, stash, (int*)ws, src_map, counts, c.k};
     zero_mx_sched_kernel<<<1, 64, 0, s>>>(a.sched);
     // scale words loaded four stages at a time when each row's scales are a
     // whole number of 16-byte pieces (K a multiple of 512)
@@ -92,7 +93,7 @@ hipError_t launch_down_gemm_mxfp8(const moe_config& c, const uint8_t* h, const u
     const int64_t max_tiles = (rows_cap(c) / gemm::kTile + c.E) * ((c.H + gemm::kTile - 1) / gemm::kTile);
     if (max_tiles == 0) return hipSuccess;
     gemm::MxArgs a{h, h_scale, w2, w2_scale, offsets, c.E, c.F, (int)rows_cap(c), c.H, c.H, nullptr, nullptr,
-                   yp, nullptr, (int*)ws};
+                   yp, nullptr, (int*)ws, nullptr, nullptr, 1};
     zero_mx_sched_kernel<<<1, 64, 0, s>>>(a.sched);
     // scale words loaded four stages at a time when each row's scales are a
     // whole number of 16-byte pieces (K a multiple of 512)
