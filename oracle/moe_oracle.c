@@ -44,6 +44,9 @@ enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
 
 #define OR_MX_BLOCK 32
 
+/* Where the routing weight is applied (its own numbering). */
+enum { OR_AT_COMBINE = 0, OR_AT_FC1 = 1, OR_AT_FC2 = 2 };
+
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                           */
 /* ------------------------------------------------------------------------ */
@@ -379,13 +382,22 @@ void or_permute(int T, int k, int64_t n_rows, int64_t row_bytes, const uint8_t* 
  * Yp_o = store_out( sum_f h_f * W2s[e][o][f] )   (uses the stored h)
  * stash = store_stash(g), store_stash(u)     (backward's saved activations)
  *
+ * Placement of the routing weight w of the row ([CUDNN] Summary: the router
+ * weight is applied in the FC1 or the FC2 epilogue; [TE-EP] commits: the
+ * weights may be applied early, before the combine).  site OR_AT_COMBINE
+ * leaves the row unweighted (the combine applies w).  OR_AT_FC1 scales the
+ * SwiGLU output before it is stored, h_f = store_h( w * silu(g_f) * u_f ).
+ * OR_AT_FC2 scales the down projection before it is stored,
+ * Yp_o = store_out( w * sum_f h_f W2s[e][o][f] ).  In exact arithmetic all
+ * three give the same combined y; only the rounding points differ.
+ *
  * fmt is the storage format of x and the weights, h_fmt that of h (F32, BF16 or
  * MXFP8 with blocks along F), y_fmt that of Yp and y (F32 or BF16), s_fmt that
  * of the stash (F32 or BF16).  Any output pointer may be NULL.
  */
 void or_expert_row(int H, int F, int fmt, const void* x_row, const uint8_t* x_scale_row, const void* w1_e,
                    const uint8_t* w1s_e, const void* w2_e, const uint8_t* w2s_e, int h_fmt, int y_fmt, int s_fmt,
-                   void* h_out, uint8_t* h_scale_out, void* yp_out, void* stash_out) {
+                   int site, double row_w, void* h_out, uint8_t* h_scale_out, void* yp_out, void* stash_out) {
     const size_t eb = or_elem_bytes(fmt);
     double* xv = (double*)malloc(sizeof(double) * (size_t)H);
     double* hv = (double*)malloc(sizeof(double) * (size_t)F);
@@ -401,6 +413,7 @@ void or_expert_row(int H, int F, int fmt, const void* x_row, const uint8_t* x_sc
     for (int f = 0; f < F; ++f) {
         double g = gu[f], u = gu[F + f];
         hv[f] = (g / (1.0 + exp(-g))) * u;
+        if (site == OR_AT_FC1) hv[f] *= row_w;
     }
     if (stash_out) or_store_row(s_fmt, gu, 2 * F, stash_out, NULL);
     if (h_out) or_store_row(h_fmt, hv, F, h_out, h_scale_out);
@@ -412,7 +425,7 @@ void or_expert_row(int H, int F, int fmt, const void* x_row, const uint8_t* x_sc
             const uint8_t* wsrow = fmt == OR_MXFP8 ? w2s_e + (size_t)o * (F / OR_MX_BLOCK) : NULL;
             double acc = 0.0;
             for (int f = 0; f < F; ++f) acc += hv[f] * or_load(fmt, wrow, wsrow, f);
-            yv[o] = acc;
+            yv[o] = site == OR_AT_FC2 ? row_w * acc : acc;
         }
         or_store_row(y_fmt, yv, H, yp_out, NULL);
         free(yv);
@@ -437,10 +450,12 @@ static inline size_t or_row_bytes(int fmt, int64_t n) { return (size_t)n * or_el
  *   stash_out[i*k+j] (2F elements, s_fmt)
  * and the combine ([CUDNN] Summary, per-top-k combine; [TE-EP] expert outputs
  * summed across the top-k):
- *   y_out[i] = store_y( sum_{j ascending, idx != -1} w[t, j] * Yp(t, j) )
- * accumulated in double from the stored Yp.  Any output may be NULL.
+ *   y_out[i] = store_y( sum_{j ascending, idx != -1} c(t, j) * Yp(t, j) )
+ * accumulated in double from the stored Yp, with c = w[t, j] for site
+ * OR_AT_COMBINE and c = 1 when the weight was applied in an epilogue (the row
+ * of (t, j) then carries w[t, j], see or_expert_row).  Any output may be NULL.
  */
-int or_forward_tokens(int H, int F, int k, int fmt, int h_fmt, int y_fmt, int s_fmt, int n_tok,
+int or_forward_tokens(int H, int F, int k, int fmt, int h_fmt, int y_fmt, int s_fmt, int site, int n_tok,
                       const int32_t* tokens, const void* x, const uint8_t* x_scale, const void* w1,
                       const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, const int32_t* idx,
                       const float* w, void* h_out, uint8_t* h_scale_out, void* yp_out, void* stash_out,
@@ -463,7 +478,8 @@ int or_forward_tokens(int H, int F, int k, int fmt, int h_fmt, int y_fmt, int s_
         const uint8_t* xs = fmt == OR_MXFP8 ? x_scale + (size_t)t * (H / OR_MX_BLOCK) : NULL;
         or_expert_row(H, F, fmt, xr, xs, (const uint8_t*)w1 + e * w1_expert,
                       fmt == OR_MXFP8 ? w1_scale + e * w1s_expert : NULL, (const uint8_t*)w2 + e * w2_expert,
-                      fmt == OR_MXFP8 ? w2_scale + e * w2s_expert : NULL, h_fmt, y_fmt, s_fmt,
+                      fmt == OR_MXFP8 ? w2_scale + e * w2s_expert : NULL, h_fmt, y_fmt, s_fmt, site,
+                      (double)w[t * k + j],
                       h_out ? (uint8_t*)h_out + ij * hb : NULL, h_scale_out ? h_scale_out + ij * hsb : NULL,
                       (uint8_t*)yp_out + ij * yb, stash_out ? (uint8_t*)stash_out + ij * sb : NULL);
     }
@@ -476,7 +492,7 @@ int or_forward_tokens(int H, int F, int k, int fmt, int h_fmt, int y_fmt, int s_
             for (int j = 0; j < k; ++j) {
                 if (idx[t * k + j] < 0) continue;
                 const void* yr = (const uint8_t*)yp_out + (i * k + j) * yb;
-                const double wt = (double)w[t * k + j];
+                const double wt = site == OR_AT_COMBINE ? (double)w[t * k + j] : 1.0;
                 for (int o = 0; o < H; ++o) acc[o] += wt * or_load(y_fmt, yr, NULL, o);
             }
             or_store_row(y_fmt, acc, H, (uint8_t*)y_out + i * H * ob, NULL);
@@ -488,7 +504,8 @@ int or_forward_tokens(int H, int F, int k, int fmt, int h_fmt, int y_fmt, int s_
 
 /* Combine of already-permuted expert outputs ([CUDNN] per-top-k combine):
  * y[t] = store_y( sum_{j ascending} w[t,j] * Yp[row_map[t*k+j]] ), skipping
- * dropped routes.  Rows that no route maps are never read. */
+ * dropped routes.  Rows that no route maps are never read.  w NULL: the
+ * weights were applied in an expert epilogue and the routes are summed. */
 void or_combine(int T, int H, int k, int y_fmt, const void* yp, const int32_t* row_map, const float* w, void* y) {
     const size_t ob = or_elem_bytes(y_fmt);
 #pragma omp parallel for schedule(static)
@@ -498,7 +515,8 @@ void or_combine(int T, int H, int k, int y_fmt, const void* yp, const int32_t* r
             int32_t row = row_map[(int64_t)t * k + j];
             if (row < 0) continue;
             const void* yr = (const uint8_t*)yp + (size_t)row * H * ob;
-            for (int o = 0; o < H; ++o) acc[o] += (double)w[(int64_t)t * k + j] * or_load(y_fmt, yr, NULL, o);
+            const double wt = w ? (double)w[(int64_t)t * k + j] : 1.0;
+            for (int o = 0; o < H; ++o) acc[o] += wt * or_load(y_fmt, yr, NULL, o);
         }
         or_store_row(y_fmt, acc, H, (uint8_t*)y + (size_t)t * H * ob, NULL);
         free(acc);

@@ -57,8 +57,8 @@ def _load():
         "or_route": (I32, [I32, I32, I32, I32, I32, P, P, P]),
         "or_group": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P]),
         "or_permute": (None, [I32, I32, I64, I64, P, P, P]),
-        "or_forward_tokens": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P,
-                                    P, P]),
+        "or_forward_tokens": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P,
+                                    P, P, P]),
         "or_combine": (None, [I32, I32, I32, I32, P, P, P, P]),
         "or_backward": (I32, [I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, I32, P, I32, P, P, P, P,
                               P, P, P]),
@@ -247,9 +247,16 @@ def permute(x, row_map, n_rows: int):
     return xp
 
 
+SITES = {"combine": 0, "fc1": 1, "fc2": 2}
+
+
 def forward_tokens(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=None, w2_scale=None,
-                   want_stash: bool = False):
+                   want_stash: bool = False, site: str = "combine"):
     """Per-token evaluation of the expert FFN and the combine.
+
+    site: where the routing weight is applied ([CUDNN] Summary: router weight in
+    the FC1 or FC2 epilogue): "combine" (default), "fc1" (h scaled before it is
+    stored) or "fc2" (Yp scaled before it is stored; the combine then sums).
 
     x, w1, w2 are stored arrays of format shape.dtype (w1 [E, 2F, H], w2 [E, H, F]).
     Returns dict with h [n, k, F] (+ h_scale for MXFP8), yp [n, k, H], y [n, H]
@@ -275,7 +282,8 @@ def forward_tokens(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=None
     xs = None if x_scale is None else np.ascontiguousarray(x_scale)
     w1s = None if w1_scale is None else np.ascontiguousarray(w1_scale)
     w2s = None if w2_scale is None else np.ascontiguousarray(w2_scale)
-    rc = _load().or_forward_tokens(s.H, s.F, k, FMT[fmt], FMT[h_fmt], FMT[y_fmt], FMT[s_fmt], n, tokens.ctypes.data,
+    rc = _load().or_forward_tokens(s.H, s.F, k, FMT[fmt], FMT[h_fmt], FMT[y_fmt], FMT[s_fmt], SITES[site], n,
+                                   tokens.ctypes.data,
                                    x.ctypes.data, _p(xs), w1.ctypes.data, _p(w1s), w2.ctypes.data, _p(w2s),
                                    idx.ctypes.data, w.ctypes.data, h.ctypes.data, _p(h_scale), yp.ctypes.data,
                                    _p(stash), y.ctypes.data)
@@ -290,13 +298,14 @@ def forward_tokens(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=None
 
 
 def combine(yp, row_map, w, y_fmt: str):
+    """y[t] = sum_j w[t, j] Yp[row_map[t, j]]; w None sums the routes unweighted."""
     yp = np.ascontiguousarray(yp)
     row_map = _c(row_map, np.int32)
-    w = _c(w, np.float32)
+    w = None if w is None else _c(w, np.float32)
     T, k = row_map.shape
     H = yp.shape[1]
     y = np.empty((T, H), _NP[y_fmt])
-    _load().or_combine(T, H, k, FMT[y_fmt], yp.ctypes.data, row_map.ctypes.data, w.ctypes.data, y.ctypes.data)
+    _load().or_combine(T, H, k, FMT[y_fmt], yp.ctypes.data, row_map.ctypes.data, _p(w), y.ctypes.data)
     return y
 
 
