@@ -14,6 +14,7 @@ grouped gate/up GEMM) and the CPU oracle timed on a bounded token sample.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -32,7 +33,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # the clocks settle over the first ~100 steps: fewer warm-up steps
+    # measured the fine-grained step ~7 % slower
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="mixtral_bf16")
     p.add_argument("--cpu-sample", type=int, default=256, help="tokens of the oracle CPU baseline (0 = skip)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -287,6 +290,20 @@ def main():
         gms = g0.elapsed_time(g1) / args.steps
         variants = {"gather_forward": {"ms_per_step": round(gms, 4), "tokens_per_s": round(s.T / (gms * 1e-3), 1),
                                        "swiglu_gemm_gather_ms": round(g1.elapsed_time(g2) / args.steps, 4)}}
+        # The routing weight applied in the gate/up (FC1) or down (FC2)
+        # epilogue instead of the combine, on the materialised step.
+        for site in ("fc1", "fc2"):
+            cw = dataclasses.replace(cfg, weight_site=site)
+            for _ in range(2):
+                moe.moe_forward(cw, logits, x, w1, w2, buf, **scales)
+            torch.cuda.synchronize()
+            g0.record(stream)
+            for _ in range(args.steps):
+                moe.moe_forward(cw, logits, x, w1, w2, buf, **scales)
+            g1.record(stream)
+            torch.cuda.synchronize()
+            wms = g0.elapsed_time(g1) / args.steps
+            variants[f"weight_{site}"] = {"ms_per_step": round(wms, 4), "tokens_per_s": round(s.T / (wms * 1e-3), 1)}
 
     R, T, H, F, E, k = s.R, s.T, s.H, s.F, s.E, s.k
     esz = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32}[s.dtype]

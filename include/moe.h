@@ -85,6 +85,16 @@ typedef enum moe_status {
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
 typedef enum moe_score { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
+/* Where moe_forward applies the routing weights ([CUDNN] Summary: the router
+ * weight in the FC1 or the FC2 epilogue; [TE-EP] commits: the weights may be
+ * applied before the combine).  In exact arithmetic the three give the same
+ * y; they differ in where the weight meets a rounding.
+ *   MOE_WEIGHT_AT_COMBINE: y[t] = sum_j w[t,j] Yp[row]          (default)
+ *   MOE_WEIGHT_AT_FC1:     h[row] = store(w[t,j] silu(g) u), y[t] = sum_j Yp[row]
+ *   MOE_WEIGHT_AT_FC2:     Yp[row] = store(w[t,j] h W2^T),  y[t] = sum_j Yp[row]
+ * The backward calls (moe_combine_bwd, moe_backward, moe_route_bwd) are built
+ * for MOE_WEIGHT_AT_COMBINE and return MOE_ERR_UNSUPPORTED otherwise. */
+typedef enum moe_weight_site { MOE_WEIGHT_AT_COMBINE = 0, MOE_WEIGHT_AT_FC1 = 1, MOE_WEIGHT_AT_FC2 = 2 } moe_weight_site;
 
 typedef struct moe_config {
     int32_t T;      /* tokens (>= 0)                                         */
@@ -97,6 +107,7 @@ typedef struct moe_config {
     int32_t renorm; /* softmax: 1 = renormalise over the k selected;
                        sigmoid: always normalised over the k selected        */
     int32_t dtype;  /* moe_dtype of x / weights / Xp / h                     */
+    int32_t weight_site; /* moe_weight_site: where moe_forward applies w     */
 } moe_config;
 
 /* Rows of the permuted buffers: T*k + E*(align-1).  Host only. */
@@ -179,6 +190,18 @@ moe_status moe_grouped_swiglu_gemm_gather(const moe_config* cfg, const void* x, 
                                           const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
                                           void* ws, size_t ws_bytes, void* stream);
 
+/* Step 3 with the routing weight in its epilogue ([CUDNN] Summary: router
+ * weight in the FC1 epilogue): as moe_grouped_swiglu_gemm, with
+ *   h[r][f] = store( w[src_map[r]] * silu(g) * u )
+ * (MXFP8: the weighted values are quantised); padding rows (src_map -1) get
+ * weight 0.  src_map [R_cap] and w [T*k] from moe_permute / moe_route.  No
+ * stash.  The per-row weights are written into ws first (part of
+ * moe_workspace_size).  Combine such rows with moe_combine(w = NULL). */
+moe_status moe_grouped_swiglu_gemm_weighted(const moe_config* cfg, const void* xp, const uint8_t* xp_scale,
+                                            const void* w1, const uint8_t* w1_scale, const int32_t* offsets,
+                                            const int32_t* src_map, const float* w, void* h, uint8_t* h_scale,
+                                            void* ws, size_t ws_bytes, void* stream);
+
 /* Step 4, grouped down GEMM ([BLOCK] down projection).  For every expert e
  * and row r in [offsets[e], offsets[e+1]):
  *   Yp[r][o] = h[r] . w2[e][o][:]   (float32 sum, stored in the output dtype).
@@ -187,11 +210,24 @@ moe_status moe_grouped_down_gemm(const moe_config* cfg, const void* h, const uin
                                  const uint8_t* w2_scale, const int32_t* offsets, void* yp, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* Step 4 with the routing weight in its epilogue ([CUDNN] Summary: router
+ * weight in the FC2 epilogue): as moe_grouped_down_gemm, with
+ *   Yp[r][o] = store( w[src_map[r]] * (h[r] . w2[e][o][:]) )
+ * (the float32 sum times the weight, rounded once); padding rows get weight
+ * 0.  src_map, w and ws as for moe_grouped_swiglu_gemm_weighted.  Combine
+ * such rows with moe_combine(w = NULL). */
+moe_status moe_grouped_down_gemm_weighted(const moe_config* cfg, const void* h, const uint8_t* h_scale,
+                                          const void* w2, const uint8_t* w2_scale, const int32_t* offsets,
+                                          const int32_t* src_map, const float* w, void* yp, void* ws,
+                                          size_t ws_bytes, void* stream);
+
 /* Step 5, top-k weighted combine ([CUDNN] per-top-k combine; [TE-EP] expert
  * outputs summed across the top-k).
  *   y[t] = round( sum_{j ascending, row_map[t,j] != -1} w[t,j] * Yp[row_map[t,j]] )
  * summed in float32 and rounded once to the output dtype.  Rows no route maps
- * are never read, so padding and the tail may hold anything. */
+ * are never read, so padding and the tail may hold anything.  w NULL: the
+ * weights were applied in an expert epilogue, and the routes are summed
+ * (y[t] = round(sum_j Yp[row_map[t,j]])). */
 moe_status moe_combine(const moe_config* cfg, const void* yp, const int32_t* row_map, const float* w, void* y,
                        void* stream);
 
@@ -205,7 +241,8 @@ moe_status moe_combine(const moe_config* cfg, const void* yp, const int32_t* row
  * routing pass in the backward).  xp NULL (with xp_scale NULL and gu_stash
  * NULL: inference): the permutation is fused into the gate/up GEMM
  * (moe_grouped_swiglu_gemm_gather) and Xp is never written; the outputs are
- * the same bit for bit. */
+ * the same bit for bit.  cfg->weight_site picks where w is applied: in the
+ * combine, or in the gate/up (FC1) or down (FC2) epilogue (both forms). */
 moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x, const uint8_t* x_scale,
                        const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, void* y,
                        int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* row_map,

@@ -21,6 +21,8 @@ from .binding import (  # noqa: F401
     moe_combine_bwd,
     moe_route_bwd,
     moe_grouped_swiglu_gemm_gather,
+    moe_grouped_swiglu_gemm_weighted,
+    moe_grouped_down_gemm_weighted,
     moe_forward,
     moe_grouped_down_bwd,
     moe_grouped_down_gemm,

@@ -22,6 +22,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
+MOE_WEIGHT_AT_COMBINE, MOE_WEIGHT_AT_FC1, MOE_WEIGHT_AT_FC2 = 0, 1, 2
+WEIGHT_SITES = {"combine": MOE_WEIGHT_AT_COMBINE, "fc1": MOE_WEIGHT_AT_FC1, "fc2": MOE_WEIGHT_AT_FC2}
 SCORES = {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}
 
 
@@ -52,7 +54,8 @@ _EXC = {MOE_ERR_INVALID_ARG: MoEInvalidArgument, MOE_ERR_UNSUPPORTED: MoEUnsuppo
 
 
 class moe_config(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "F", "E", "k", "align", "score", "renorm", "dtype")]
+    _fields_ = [(n, ctypes.c_int32)
+                for n in ("T", "H", "F", "E", "k", "align", "score", "renorm", "dtype", "weight_site")]
 
 
 @dataclass(frozen=True)
@@ -66,6 +69,7 @@ class MoEConfig:
     score: str = "softmax"
     renorm: bool = False
     dtype: str = "bf16"
+    weight_site: str = "combine"  # where moe_forward applies w: "combine", "fc1" or "fc2"
 
     @classmethod
     def from_shape(cls, s) -> "MoEConfig":
@@ -73,7 +77,7 @@ class MoEConfig:
 
     def c(self) -> moe_config:
         return moe_config(self.T, self.H, self.F, self.E, self.k, self.align, SCORES[self.score],
-                          int(self.renorm), DTYPES[self.dtype])
+                          int(self.renorm), DTYPES[self.dtype], WEIGHT_SITES[self.weight_site])
 
     @property
     def R_cap(self) -> int:
@@ -103,6 +107,8 @@ _SIGS = {
     "moe_forward": (ctypes.c_int, [CFG] + [P] * 22 + [ctypes.c_size_t, P]),
     "moe_route_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P]),
     "moe_grouped_swiglu_gemm_gather": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+    "moe_grouped_swiglu_gemm_weighted": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+    "moe_grouped_down_gemm_weighted": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_combine_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P]),
     "moe_grouped_down_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_grouped_swiglu_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -249,6 +255,38 @@ def moe_grouped_swiglu_gemm_gather(cfg: MoEConfig, x, src_map, counts, w1, offse
         _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx), wp, wb, _stream(stream)))
 
 
+def moe_grouped_swiglu_gemm_weighted(cfg: MoEConfig, xp, w1, offsets, src_map, w, h, ws, xp_scale=None,
+                                     w1_scale=None, h_scale=None, stream=None):
+    """The gate/up GEMM with h scaled by each row's routing weight w[src_map[r]]."""
+    c = cfg.c()
+    mx = cfg.dtype == "mxfp8"
+    wp, wb = _ws(ws)
+    _check(load_library().moe_grouped_swiglu_gemm_weighted(
+        ctypes.byref(c), _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.H)),
+        _ptr(xp_scale, "xp_scale", torch.uint8, (cfg.R_cap, cfg.H // 32), optional=not mx),
+        _ptr(w1, "w1", cfg.store_dtype, (cfg.E, 2 * cfg.F, cfg.H)),
+        _ptr(w1_scale, "w1_scale", torch.uint8, (cfg.E, 2 * cfg.F, cfg.H // 32), optional=not mx),
+        _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(src_map, "src_map", torch.int32, (cfg.R_cap,)),
+        _ptr(w, "w", torch.float32, (cfg.T, cfg.k)), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
+        _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx), wp, wb, _stream(stream)))
+
+
+def moe_grouped_down_gemm_weighted(cfg: MoEConfig, h, w2, offsets, src_map, w, yp, ws, h_scale=None, w2_scale=None,
+                                   stream=None):
+    """The down GEMM with Yp scaled by each row's routing weight w[src_map[r]]."""
+    c = cfg.c()
+    mx = cfg.dtype == "mxfp8"
+    wp, wb = _ws(ws)
+    _check(load_library().moe_grouped_down_gemm_weighted(
+        ctypes.byref(c), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
+        _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx),
+        _ptr(w2, "w2", cfg.store_dtype, (cfg.E, cfg.H, cfg.F)),
+        _ptr(w2_scale, "w2_scale", torch.uint8, (cfg.E, cfg.H, cfg.F // 32), optional=not mx),
+        _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(src_map, "src_map", torch.int32, (cfg.R_cap,)),
+        _ptr(w, "w", torch.float32, (cfg.T, cfg.k)), _ptr(yp, "yp", cfg.out_dtype, (cfg.R_cap, cfg.H)),
+        wp, wb, _stream(stream)))
+
+
 def moe_grouped_down_gemm(cfg: MoEConfig, h, w2, offsets, yp, ws, h_scale=None, w2_scale=None, stream=None):
     c = cfg.c()
     mx = cfg.dtype == "mxfp8"
@@ -263,10 +301,12 @@ def moe_grouped_down_gemm(cfg: MoEConfig, h, w2, offsets, yp, ws, h_scale=None, 
 
 
 def moe_combine(cfg: MoEConfig, yp, row_map, w, y, stream=None):
+    """y[t] = sum_j w[t, j] Yp[row_map[t, j]]; w None sums the routes (weights already applied)."""
     c = cfg.c()
     _check(load_library().moe_combine(
         ctypes.byref(c), _ptr(yp, "yp", cfg.out_dtype, (cfg.R_cap, cfg.H)),
-        _ptr(row_map, "row_map", torch.int32, (cfg.T, cfg.k)), _ptr(w, "w", torch.float32, (cfg.T, cfg.k)),
+        _ptr(row_map, "row_map", torch.int32, (cfg.T, cfg.k)),
+        _ptr(w, "w", torch.float32, (cfg.T, cfg.k), optional=True),
         _ptr(y, "y", cfg.out_dtype, (cfg.T, cfg.H)), _stream(stream)))
 
 

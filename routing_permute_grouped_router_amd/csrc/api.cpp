@@ -51,6 +51,10 @@ moe_status check_config(const moe_config* cfg) {
     if (c.renorm != 0 && c.renorm != 1) return fail(MOE_ERR_INVALID_ARG, "renorm must be 0 or 1 (got %d)", c.renorm);
     if (c.dtype != MOE_F32 && c.dtype != MOE_BF16 && c.dtype != MOE_MXFP8)
         return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32, MOE_BF16 or MOE_MXFP8 (got %d)", c.dtype);
+    if (c.weight_site != MOE_WEIGHT_AT_COMBINE && c.weight_site != MOE_WEIGHT_AT_FC1 &&
+        c.weight_site != MOE_WEIGHT_AT_FC2)
+        return fail(MOE_ERR_INVALID_ARG, "weight_site must be MOE_WEIGHT_AT_COMBINE, _FC1 or _FC2 (got %d)",
+                    c.weight_site);
     if (rows_capacity(c) >= (int64_t)1 << 31)
         return fail(MOE_ERR_INVALID_ARG, "T*k + E*(align-1) must be below 2^31");
     if ((int64_t)c.T * c.H >= (int64_t)1 << 40) return fail(MOE_ERR_INVALID_ARG, "T*H too large");
@@ -88,6 +92,102 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 size_t group_ws_bytes(const moe_config& c) { return round256((size_t)group_n_chunks(c.T, c.E) * c.E * sizeof(int32_t)); }
 void* gemm_ws(const moe_config& c, void* ws) { return (char*)ws + group_ws_bytes(c); }
 
+// Per-row copy of the routing weights (epilogue placements), after the
+// forward region of the workspace.
+size_t row_w_ws_bytes(const moe_config& c) { return round256((size_t)(rows_capacity(c) + kRowWeightPad) * sizeof(float)); }
+float* row_w_ws(const moe_config& c, void* ws) {
+    return (float*)((char*)ws + group_ws_bytes(c) + round256(gemm_bf16_ws_bytes(c) + gemm_mxfp8_ws_bytes(c)));
+}
+
+// The gate/up GEMM with all its forms: gsrc/gcounts non-null = gather form
+// (a is x), row_w non-null = h scaled by the row's routing weight.
+moe_status swiglu_checked(const moe_config* cfg, const void* a, const uint8_t* a_scale, const void* w1,
+                          const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale, void* stash,
+                          const int32_t* gsrc, const int32_t* gcounts, const float* row_w, void* ws, size_t ws_bytes,
+                          void* stream, const char* what) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    const moe_config& c = *cfg;
+    if ((st = check_shapes(c))) return st;
+    if (rows_capacity(c) == 0) return MOE_OK;
+    // the gather form addresses a row of x with a 32-bit byte offset
+    if (gsrc && (int64_t)c.T * c.H * (c.dtype == MOE_F32 ? 4 : c.dtype == MOE_BF16 ? 2 : 1) >= ((int64_t)1 << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: the gather form needs T*H*element size < 4 GiB", what);
+    if (!a) return fail(MOE_ERR_INVALID_ARG, "%s: the grouped operand (xp or x) is NULL", what);
+    REQUIRE(w1);
+    REQUIRE(offsets);
+    REQUIRE(h);
+    if ((st = check_ws(c, ws, ws_bytes))) return st;
+    hipStream_t s = as_stream(stream);
+    switch (c.dtype) {
+    case MOE_BF16:
+        return hip_status(launch_swiglu_gemm_bf16(c, (const uint16_t*)a, (const uint16_t*)w1, offsets, (uint16_t*)h,
+                                                  (uint16_t*)stash, gsrc, gcounts, row_w, gemm_ws(c, ws), s),
+                          what);
+    case MOE_F32:
+        return hip_status(launch_swiglu_gemm_f32(c, (const float*)a, (const float*)w1, offsets, (float*)h,
+                                                 (float*)stash, gsrc, gcounts, row_w, s),
+                          what);
+    default:
+        if (!a_scale) return fail(MOE_ERR_INVALID_ARG, "%s: the grouped operand's MXFP8 scales are NULL", what);
+        REQUIRE(w1_scale);
+        REQUIRE(h_scale);
+        return hip_status(launch_swiglu_gemm_mxfp8(c, (const uint8_t*)a, a_scale, (const uint8_t*)w1, w1_scale,
+                                                   offsets, (uint8_t*)h, h_scale, (uint16_t*)stash, gsrc, gcounts,
+                                                   row_w, gemm_ws(c, ws), s),
+                          what);
+    }
+}
+
+// The down GEMM; row_w non-null = Yp scaled by the row's routing weight.
+moe_status down_checked(const moe_config* cfg, const void* h, const uint8_t* h_scale, const void* w2,
+                        const uint8_t* w2_scale, const int32_t* offsets, void* yp, const float* row_w, void* ws,
+                        size_t ws_bytes, void* stream, const char* what) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    const moe_config& c = *cfg;
+    if ((st = check_shapes(c))) return st;
+    if (rows_capacity(c) == 0) return MOE_OK;
+    REQUIRE(h);
+    REQUIRE(w2);
+    REQUIRE(offsets);
+    REQUIRE(yp);
+    if ((st = check_ws(c, ws, ws_bytes))) return st;
+    hipStream_t s = as_stream(stream);
+    switch (c.dtype) {
+    case MOE_BF16:
+        return hip_status(launch_down_gemm_bf16(c, (const uint16_t*)h, (const uint16_t*)w2, offsets, (uint16_t*)yp,
+                                                row_w, gemm_ws(c, ws), s),
+                          what);
+    case MOE_F32:
+        return hip_status(launch_down_gemm_f32(c, (const float*)h, (const float*)w2, offsets, (float*)yp, row_w, s),
+                          what);
+    default:
+        REQUIRE(h_scale);
+        REQUIRE(w2_scale);
+        return hip_status(launch_down_gemm_mxfp8(c, (const uint8_t*)h, h_scale, (const uint8_t*)w2, w2_scale, offsets,
+                                                 (uint16_t*)yp, row_w, gemm_ws(c, ws), s),
+                          what);
+    }
+}
+
+// Writes the per-row routing weights into the workspace; *row_w = their
+// address (left null when there are no rows).
+moe_status row_weights_checked(const moe_config* cfg, const int32_t* src_map, const float* w, void* ws,
+                               size_t ws_bytes, void* stream, const float** row_w) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    const moe_config& c = *cfg;
+    if (rows_capacity(c) == 0) return MOE_OK;
+    REQUIRE(src_map);
+    REQUIRE(w);
+    if ((st = check_ws(c, ws, ws_bytes))) return st;
+    float* rw = row_w_ws(c, ws);
+    if ((st = hip_status(launch_row_weights(c, src_map, w, rw, as_stream(stream)), "row weights"))) return st;
+    *row_w = rw;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -100,7 +200,7 @@ int64_t moe_rows_capacity(const moe_config* cfg) {
 size_t moe_workspace_size(const moe_config* cfg) {
     if (check_config(cfg) != MOE_OK) return 0;
     const moe_config& c = *cfg;
-    return group_ws_bytes(c) + round256(gemm_bf16_ws_bytes(c) + gemm_mxfp8_ws_bytes(c));
+    return group_ws_bytes(c) + round256(gemm_bf16_ws_bytes(c) + gemm_mxfp8_ws_bytes(c)) + row_w_ws_bytes(c);
 }
 
 size_t moe_backward_workspace_size(const moe_config* cfg) {
@@ -151,107 +251,49 @@ moe_status moe_permute(const moe_config* cfg, const void* x, const uint8_t* x_sc
 moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const uint8_t* xp_scale, const void* w1,
                                    const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
                                    void* gu_stash, void* ws, size_t ws_bytes, void* stream) {
-    moe_status st = check_config(cfg);
-    if (st) return st;
-    const moe_config& c = *cfg;
-    if ((st = check_shapes(c))) return st;
-    if (rows_capacity(c) == 0) return MOE_OK;
-    REQUIRE(xp);
-    REQUIRE(w1);
-    REQUIRE(offsets);
-    REQUIRE(h);
-    if ((st = check_ws(c, ws, ws_bytes))) return st;
-    hipStream_t s = as_stream(stream);
-    switch (c.dtype) {
-    case MOE_BF16:
-        return hip_status(launch_swiglu_gemm_bf16(c, (const uint16_t*)xp, (const uint16_t*)w1, offsets, (uint16_t*)h,
-                                                  (uint16_t*)gu_stash, nullptr, nullptr, gemm_ws(c, ws), s),
-                          "moe_grouped_swiglu_gemm");
-    case MOE_F32:
-        return hip_status(
-            launch_swiglu_gemm_f32(c, (const float*)xp, (const float*)w1, offsets, (float*)h, (float*)gu_stash,
-                                   nullptr, nullptr, s),
-            "moe_grouped_swiglu_gemm");
-    default:
-        REQUIRE(xp_scale);
-        REQUIRE(w1_scale);
-        REQUIRE(h_scale);
-        return hip_status(launch_swiglu_gemm_mxfp8(c, (const uint8_t*)xp, xp_scale, (const uint8_t*)w1, w1_scale,
-                                                   offsets, (uint8_t*)h, h_scale, (uint16_t*)gu_stash, nullptr,
-                                                   nullptr, gemm_ws(c, ws), s),
-                          "moe_grouped_swiglu_gemm");
-    }
+    return swiglu_checked(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, gu_stash, nullptr, nullptr, nullptr,
+                          ws, ws_bytes, stream, "moe_grouped_swiglu_gemm");
 }
 
 moe_status moe_grouped_swiglu_gemm_gather(const moe_config* cfg, const void* x, const uint8_t* x_scale,
                                           const int32_t* src_map, const int32_t* counts, const void* w1,
                                           const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
                                           void* ws, size_t ws_bytes, void* stream) {
-    moe_status st = check_config(cfg);
-    if (st) return st;
-    const moe_config& c = *cfg;
-    if ((st = check_shapes(c))) return st;
-    if (rows_capacity(c) == 0) return MOE_OK;
-    // the kernels address a row of x with a 32-bit byte offset
-    if ((int64_t)c.T * c.H * (c.dtype == MOE_F32 ? 4 : c.dtype == MOE_BF16 ? 2 : 1) >= ((int64_t)1 << 32))
-        return fail(MOE_ERR_UNSUPPORTED, "the gather form needs T*H*element size < 4 GiB");
-    REQUIRE(x);
-    REQUIRE(src_map);
-    REQUIRE(counts);
-    REQUIRE(w1);
-    REQUIRE(offsets);
-    REQUIRE(h);
-    if ((st = check_ws(c, ws, ws_bytes))) return st;
-    hipStream_t s = as_stream(stream);
-    switch (c.dtype) {
-    case MOE_BF16:
-        return hip_status(launch_swiglu_gemm_bf16(c, (const uint16_t*)x, (const uint16_t*)w1, offsets, (uint16_t*)h,
-                                                  nullptr, src_map, counts, gemm_ws(c, ws), s),
-                          "moe_grouped_swiglu_gemm_gather");
-    case MOE_F32:
-        return hip_status(launch_swiglu_gemm_f32(c, (const float*)x, (const float*)w1, offsets, (float*)h, nullptr,
-                                                 src_map, counts, s),
-                          "moe_grouped_swiglu_gemm_gather");
-    default:
-        REQUIRE(x_scale);
-        REQUIRE(w1_scale);
-        REQUIRE(h_scale);
-        return hip_status(launch_swiglu_gemm_mxfp8(c, (const uint8_t*)x, x_scale, (const uint8_t*)w1, w1_scale,
-                                                   offsets, (uint8_t*)h, h_scale, nullptr, src_map, counts,
-                                                   gemm_ws(c, ws), s),
-                          "moe_grouped_swiglu_gemm_gather");
+    if (cfg && rows_capacity(*cfg) > 0) {
+        REQUIRE(src_map);
+        REQUIRE(counts);
     }
+    return swiglu_checked(cfg, x, x_scale, w1, w1_scale, offsets, h, h_scale, nullptr, src_map, counts, nullptr, ws,
+                          ws_bytes, stream, "moe_grouped_swiglu_gemm_gather");
+}
+
+moe_status moe_grouped_swiglu_gemm_weighted(const moe_config* cfg, const void* xp, const uint8_t* xp_scale,
+                                            const void* w1, const uint8_t* w1_scale, const int32_t* offsets,
+                                            const int32_t* src_map, const float* w, void* h, uint8_t* h_scale,
+                                            void* ws, size_t ws_bytes, void* stream) {
+    const float* row_w = nullptr;
+    moe_status st = row_weights_checked(cfg, src_map, w, ws, ws_bytes, stream, &row_w);
+    if (st) return st;
+    return swiglu_checked(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, nullptr, nullptr, nullptr, row_w, ws,
+                          ws_bytes, stream, "moe_grouped_swiglu_gemm_weighted");
 }
 
 moe_status moe_grouped_down_gemm(const moe_config* cfg, const void* h, const uint8_t* h_scale, const void* w2,
                                  const uint8_t* w2_scale, const int32_t* offsets, void* yp, void* ws, size_t ws_bytes,
                                  void* stream) {
-    moe_status st = check_config(cfg);
+    return down_checked(cfg, h, h_scale, w2, w2_scale, offsets, yp, nullptr, ws, ws_bytes, stream,
+                        "moe_grouped_down_gemm");
+}
+
+moe_status moe_grouped_down_gemm_weighted(const moe_config* cfg, const void* h, const uint8_t* h_scale,
+                                          const void* w2, const uint8_t* w2_scale, const int32_t* offsets,
+                                          const int32_t* src_map, const float* w, void* yp, void* ws,
+                                          size_t ws_bytes, void* stream) {
+    const float* row_w = nullptr;
+    moe_status st = row_weights_checked(cfg, src_map, w, ws, ws_bytes, stream, &row_w);
     if (st) return st;
-    const moe_config& c = *cfg;
-    if ((st = check_shapes(c))) return st;
-    if (rows_capacity(c) == 0) return MOE_OK;
-    REQUIRE(h);
-    REQUIRE(w2);
-    REQUIRE(offsets);
-    REQUIRE(yp);
-    if ((st = check_ws(c, ws, ws_bytes))) return st;
-    hipStream_t s = as_stream(stream);
-    switch (c.dtype) {
-    case MOE_BF16:
-        return hip_status(
-            launch_down_gemm_bf16(c, (const uint16_t*)h, (const uint16_t*)w2, offsets, (uint16_t*)yp, gemm_ws(c, ws), s),
-            "moe_grouped_down_gemm");
-    case MOE_F32:
-        return hip_status(launch_down_gemm_f32(c, (const float*)h, (const float*)w2, offsets, (float*)yp, s),
-                          "moe_grouped_down_gemm");
-    default:
-        REQUIRE(h_scale);
-        REQUIRE(w2_scale);
-        return hip_status(launch_down_gemm_mxfp8(c, (const uint8_t*)h, h_scale, (const uint8_t*)w2, w2_scale, offsets,
-                                                 (uint16_t*)yp, gemm_ws(c, ws), s),
-                          "moe_grouped_down_gemm");
-    }
+    return down_checked(cfg, h, h_scale, w2, w2_scale, offsets, yp, row_w, ws, ws_bytes, stream,
+                        "moe_grouped_down_gemm_weighted");
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* yp, const int32_t* row_map, const float* w, void* y,
@@ -262,7 +304,6 @@ moe_status moe_combine(const moe_config* cfg, const void* yp, const int32_t* row
     if (cfg->T > 0) {
         REQUIRE(yp);
         REQUIRE(row_map);
-        REQUIRE(w);
         REQUIRE(y);
     }
     return hip_status(launch_combine(*cfg, yp, row_map, w, y, as_stream(stream)), "moe_combine");
@@ -288,16 +329,25 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
     if ((st = moe_permute(cfg, x, x_scale, idx, xp, xp_scale, counts, offsets, row_map, src_map, err, ws, ws_bytes,
                           stream)))
         return st;
-    if (xp) {
-        if ((st = moe_grouped_swiglu_gemm(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, gu_stash, ws,
-                                          ws_bytes, stream)))
-            return st;
-    } else if ((st = moe_grouped_swiglu_gemm_gather(cfg, x, x_scale, src_map, counts, w1, w1_scale, offsets, h,
-                                                    h_scale, ws, ws_bytes, stream))) {
+    // the routing weights applied in an expert epilogue: their per-row copy
+    const float* row_w = nullptr;
+    if (c.weight_site != MOE_WEIGHT_AT_COMBINE &&
+        (st = row_weights_checked(cfg, src_map, w, ws, ws_bytes, stream, &row_w)))
         return st;
+    const float* fc1_w = c.weight_site == MOE_WEIGHT_AT_FC1 ? row_w : nullptr;
+    const float* fc2_w = c.weight_site == MOE_WEIGHT_AT_FC2 ? row_w : nullptr;
+    if (xp) {
+        st = swiglu_checked(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, gu_stash, nullptr, nullptr, fc1_w,
+                            ws, ws_bytes, stream, "moe_forward");
+    } else {
+        if (rows_capacity(c) > 0) REQUIRE(src_map);
+        st = swiglu_checked(cfg, x, x_scale, w1, w1_scale, offsets, h, h_scale, nullptr, src_map, counts, fc1_w, ws,
+                            ws_bytes, stream, "moe_forward");
     }
-    if ((st = moe_grouped_down_gemm(cfg, h, h_scale, w2, w2_scale, offsets, yp, ws, ws_bytes, stream))) return st;
-    return moe_combine(cfg, yp, row_map, w, y, stream);
+    if (st) return st;
+    if ((st = down_checked(cfg, h, h_scale, w2, w2_scale, offsets, yp, fc2_w, ws, ws_bytes, stream, "moe_forward")))
+        return st;
+    return moe_combine(cfg, yp, row_map, c.weight_site == MOE_WEIGHT_AT_COMBINE ? w : nullptr, y, stream);
 }
 
 moe_status moe_route_bwd(const moe_config* cfg, const void* dy, const void* yp, const float* logits,
@@ -305,6 +355,8 @@ moe_status moe_route_bwd(const moe_config* cfg, const void* dy, const void* yp, 
     moe_status st = check_config(cfg);
     if (st) return st;
     if ((st = check_shapes(*cfg))) return st;
+    if (cfg->weight_site != MOE_WEIGHT_AT_COMBINE)
+        return fail(MOE_ERR_UNSUPPORTED, "the routing backward reads unweighted Yp rows (weights applied in the combine)");
     if (cfg->T == 0) return MOE_OK;
     REQUIRE(dy);
     REQUIRE(yp);
@@ -321,6 +373,8 @@ moe_status moe_combine_bwd(const moe_config* cfg, const void* dy, const int32_t*
     moe_status st = check_config(cfg);
     if (st) return st;
     if (cfg->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "the backward takes F32 or BF16 storage");
+    if (cfg->weight_site != MOE_WEIGHT_AT_COMBINE)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward is built for the weights applied in the combine");
     if ((st = check_shapes(*cfg))) return st;
     REQUIRE(offsets);
     if (rows_capacity(*cfg) > 0) {

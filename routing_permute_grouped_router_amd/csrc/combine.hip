@@ -89,7 +89,8 @@ __device__ __forceinline__ void gather_rows(const int32_t* __restrict__ row_map,
     }
 }
 
-// y[t] = round(sum_j w[t,j] * Yp[row_map[t,j]]); one block per token.
+// y[t] = round(sum_j w[t,j] * Yp[row_map[t,j]]); one block per token.  w null:
+// the weights were applied in an expert epilogue, the routes are summed.
 template <bool F32, int G>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yp, const int32_t* __restrict__ row_map,
                                                       const float* __restrict__ w, int k, int vec_per_row,
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
             for (int g = 0; g < G; ++g) V::template load<true>(yp, (int64_t)r[g] * vec_per_row + c, v[g]);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float wt = ok[g] ? w[t * k + j0 + g] : 0.f;
+                const float wt = ok[g] ? (w ? w[t * k + j0 + g] : 1.f) : 0.f;
 #pragma unroll
                 for (int a = 0; a < V::N; ++a) acc[a] = ok[g] ? fmaf(wt, v[g][a], acc[a]) : acc[a];
             }
@@ -216,6 +217,27 @@ int block_for(int vec_per_row) {
 }
 
 }  // namespace
+
+namespace {
+// row_w[r] = w[src_map[r]] (the routing weight of the route in row r), 0 for
+// rows no route fills; rows [R_cap, n_alloc) are set to 0 as well.
+__global__ __launch_bounds__(256) void row_weights_kernel(const int32_t* __restrict__ src_map,
+                                                          const float* __restrict__ w, int64_t n_rows,
+                                                          int64_t n_alloc, int64_t n_routes, float* __restrict__ row_w) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= n_alloc) return;
+    const int32_t s = r < n_rows ? src_map[r] : -1;
+    row_w[r] = (s >= 0 && s < n_routes) ? w[s] : 0.f;
+}
+}  // namespace
+
+hipError_t launch_row_weights(const moe_config& c, const int32_t* src_map, const float* w, float* row_w,
+                              hipStream_t s) {
+    const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
+    const int64_t n = R_cap + kRowWeightPad;
+    row_weights_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(src_map, w, R_cap, n, (int64_t)c.T * c.k, row_w);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const moe_config& c, const void* yp, const int32_t* row_map, const float* w, void* y,
                           hipStream_t s) {

@@ -110,10 +110,11 @@ __global__ __launch_bounds__(256) void split_reduce_bf16(gemm::Args p, int nb) {
             }
         }
         const size_t row = (size_t)(row0 + r);
+        const float rw = p.row_w ? p.row_w[row] : 1.f;
         if (SWIGLU) {
             *(uint2*)(p.C + row * p.n_out + n) =
-                row0 + r < a_end ? make_uint2(pack_bf16x2(silu(g.x) * u.x, silu(g.y) * u.y),
-                                              pack_bf16x2(silu(g.z) * u.z, silu(g.w) * u.w))
+                row0 + r < a_end ? make_uint2(pack_bf16x2(silu(g.x) * u.x * rw, silu(g.y) * u.y * rw),
+                                              pack_bf16x2(silu(g.z) * u.z * rw, silu(g.w) * u.w * rw))
                                  : make_uint2(0u, 0u);
             if (p.stash) {
                 *(uint2*)(p.stash + row * 2 * p.n_out + n) = make_uint2(pack_bf16x2(g.x, g.y), pack_bf16x2(g.z, g.w));
@@ -121,7 +122,8 @@ __global__ __launch_bounds__(256) void split_reduce_bf16(gemm::Args p, int nb) {
                     make_uint2(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w));
             }
         } else {
-            *(uint2*)(p.C + row * p.n_out + n) = make_uint2(pack_bf16x2(g.x, g.y), pack_bf16x2(g.z, g.w));
+            *(uint2*)(p.C + row * p.n_out + n) =
+                make_uint2(pack_bf16x2(g.x * rw, g.y * rw), pack_bf16x2(g.z * rw, g.w * rw));
         }
     }
 }
@@ -132,7 +134,10 @@ hipError_t launch_bf16(gemm::Args a, int64_t max_tiles, void* ws, hipStream_t s)
     a.sched = (int*)ws;
     a.part = (float*)((char*)ws + 256);
     zero_sched_kernel<<<1, 64, 0, s>>>(a.sched);
-    gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM><<<grid, gemm::kThreads, 0, s>>>(a);
+    if (a.row_w)
+        gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM, true><<<grid, gemm::kThreads, 0, s>>>(a);
+    else
+        gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM, false><<<grid, gemm::kThreads, 0, s>>>(a);
     split_reduce_bf16<SWIGLU, kGroupM><<<dim3(gemm::kSlotsPerXcd * (gemm::kTile / kReduceRows), gemm::kXcds), 256, 0, s>>>(
         a, grid / gemm::kXcds);
     return hipGetLastError();
@@ -142,21 +147,22 @@ hipError_t launch_bf16(gemm::Args a, int64_t max_tiles, void* ws, hipStream_t s)
 
 hipError_t launch_swiglu_gemm_bf16(const moe_config& c, const uint16_t* xp, const uint16_t* w1,
                                    const int32_t* offsets, uint16_t* h, uint16_t* stash, const int32_t* src_map,
-                                   const int32_t* counts, void* ws, hipStream_t s) {
+                                   const int32_t* counts, const float* row_w, void* ws, hipStream_t s) {
     const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.F + 127) / 128);
     if (max_tiles == 0) return hipSuccess;
     gemm::Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash, nullptr, nullptr,
-                 src_map, counts, c.k};
+                 src_map, counts, c.k, row_w};
     return launch_bf16<true>(a, max_tiles, ws, s);
 }
 
 hipError_t launch_down_gemm_bf16(const moe_config& c, const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
-                                 uint16_t* yp, void* ws, hipStream_t s) {
+                                 uint16_t* yp, const float* row_w, void* ws, hipStream_t s) {
     const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.H + gemm::kTile - 1) / gemm::kTile);
     if (max_tiles == 0) return hipSuccess;
-    gemm::Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr, nullptr, nullptr};
+    gemm::Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr, nullptr, nullptr,
+                 nullptr, nullptr, 1, row_w};
     return launch_bf16<false>(a, max_tiles, ws, s);
 }
 

@@ -61,6 +61,10 @@ struct Args {
     const int32_t* src_map;
     const int32_t* counts;
     int gk;
+    // Optional per-row routing weights (the epilogue placements of the
+    // weight): output row r is scaled by row_w[r] before it is stored.  The
+    // array holds 256 rows past `rows`, so a tile reads without a bound.
+    const float* row_w;
 };
 
 // Work queues.  The tiles are cut into kXcds contiguous ranges, one per XCD
@@ -181,7 +185,9 @@ __device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-template <bool SWIGLU, int SWZ, int GM>
+// RW: the outputs are scaled by p.row_w (built separately, so the plain
+// kernel carries none of it).
+template <bool SWIGLU, int SWZ, int GM, bool RW>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     constexpr int BK = 64;                  // K depth of one stage
     constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
@@ -518,6 +524,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         const int next_unit = s_unit;
         const int e_row0 = row0, e_row_end = row_end, e_a_end = a_end, e_nt = nt, e_slot = slot;
         const bool e_valid = valid;
+        // Routing weights of this wave's 128 rows, two per lane (rows 2 lane
+        // and 2 lane + 1 of the band), loaded and waited for before setup
+        // issues the next unit's loads: the wait then covers only these.
+        float rwa = 1.f, rwb = 1.f;
+        if constexpr (RW) {
+            if (e_valid) {
+                const float* const rwp = p.row_w + e_row0 + wm * 128 + 2 * lane;
+                rwa = rwp[0];
+                rwb = rwp[1];
+            }
+            __asm__ volatile("" : "+v"(rwa), "+v"(rwb));
+        }
         if (next_unit >= 0) setup(next_unit);
         if (e_valid) {
         // Epilogue straight from the accumulators (no LDS, so no barrier
@@ -539,6 +557,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         // per row) for q = 0..15: the lane's rows of the 32-row block starting
         // at tile row RB0; rows are checked only when the block runs past the
         // group's end.
+        // RW[q]: the routing weight of the lane's row 8 (q / 4) + q % 4 of
+        // 32-row block MI (1 without weights); row i of the wave's band sits
+        // in lane i / 2, as rwa (even i) or rwb (odd i).
+#define GB_ROW_WEIGHTS(MI, W_)                                                                           \
+    if constexpr (RW) {                                                                                  \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
+            W_[q] = __shfl((q & 1) ? rwb : rwa, ((MI) * 32 + lr + 8 * (q >> 2) + (q & 3)) >> 1, 64);     \
+    } else {                                                                                             \
+        _Pragma("unroll") for (int q = 0; q < 16; ++q) W_[q] = 1.f;                                      \
+    }
 #define GB_STORE_ROWS(T, DST, LD, RB0, W)                                                                \
     if ((RB0) + 32 <= rlim) {                                                                            \
         _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
@@ -590,10 +618,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     {                                                                                                    \
         const int rb0 = wm * 128 + (MI) * 32;                                                            \
         uint32_t hw[16];                                                                                 \
+        float rw[16];                                                                                    \
+        GB_ROW_WEIGHTS(MI, rw)                                                                           \
         _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                                 \
             const float g0 = agpr_read(acc[MI][0][q]), g1 = agpr_read(acc[MI][1][q]);                    \
             const float u0 = agpr_read(acc[MI][2][q]), u1 = agpr_read(acc[MI][3][q]);                    \
-            hw[q] = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);                                           \
+            hw[q] = pack_bf16x2(silu(g0) * u0 * rw[q], silu(g1) * u1 * rw[q]);                           \
             if (rb0 + lr + 8 * (q >> 2) + (q & 3) >= alim) hw[q] = 0; /* gather: padding rows */         \
         }                                                                                                \
         if (f < p.n_out) {                                                                               \
@@ -622,9 +652,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     {                                                                                                    \
         const int rb0 = wm * 128 + (MI) * 32;                                                            \
         uint2 w[16];                                                                                     \
+        float rw[16];                                                                                    \
+        GB_ROW_WEIGHTS(MI, rw)                                                                           \
         _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
-            w[q] = make_uint2(pack_bf16x2(agpr_read(acc[MI][0][q]), agpr_read(acc[MI][1][q])),           \
-                              pack_bf16x2(agpr_read(acc[MI][2][q]), agpr_read(acc[MI][3][q])));          \
+            w[q] = make_uint2(pack_bf16x2(agpr_read(acc[MI][0][q]) * rw[q], agpr_read(acc[MI][1][q]) * rw[q]), \
+                              pack_bf16x2(agpr_read(acc[MI][2][q]) * rw[q], agpr_read(acc[MI][3][q]) * rw[q])); \
         if (n < p.n_out) {                                                                               \
             uint16_t* const dst = cbase + (size_t)(rb0 + lr) * p.n_out + n;                              \
             GB_STORE_ROWS(uint2, dst, p.n_out, rb0, w)                                                   \
@@ -635,6 +667,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
 #undef GB_EPI_DN
         }
 #undef GB_STORE_ROWS
+#undef GB_ROW_WEIGHTS
         }  // valid
         unit = next_unit;
     }

@@ -28,6 +28,7 @@ struct F32Args {
     const int32_t* src_map;
     const int32_t* counts;
     int gk;
+    const float* row_w;  // optional: output row r scaled by row_w[r] before it is stored
 };
 
 template <bool SWIGLU>
@@ -97,12 +98,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(F32Args p, int n_
     for (int i = 0; i < 4; ++i) {
         const int r = row0 + ty * 4 + i;
         if (r >= row_end) continue;
+        const float rw = p.row_w ? p.row_w[r] : 1.f;
         if (SWIGLU) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int f = nt * 32 + tx * 2 + j;
                 const float g = acc[i][j], u = acc[i][2 + j];
-                p.C[(size_t)r * p.n_out + f] = (g / (1.0f + expf(-g))) * u;
+                p.C[(size_t)r * p.n_out + f] = (g / (1.0f + expf(-g))) * u * rw;
                 if (p.stash) {
                     p.stash[(size_t)r * 2 * p.n_out + f] = g;
                     p.stash[(size_t)r * 2 * p.n_out + p.n_out + f] = u;
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(F32Args p, int n_
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) p.C[(size_t)r * p.n_out + nt * TN + tx * 4 + j] = acc[i][j];
+            for (int j = 0; j < 4; ++j) p.C[(size_t)r * p.n_out + nt * TN + tx * 4 + j] = acc[i][j] * rw;
         }
     }
 }
@@ -119,23 +121,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(F32Args p, int n_
 
 hipError_t launch_swiglu_gemm_f32(const moe_config& c, const float* xp, const float* w1, const int32_t* offsets,
                                   float* h, float* stash, const int32_t* src_map, const int32_t* counts,
-                                  hipStream_t s) {
+                                  const float* row_w, hipStream_t s) {
     const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     const int n_tiles = c.F / 32;
     const int64_t blocks = (R_cap / TM + c.E) * n_tiles;
     if (blocks == 0) return hipSuccess;
-    F32Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash, src_map, counts, c.k};
+    F32Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash, src_map, counts, c.k, row_w};
     grouped_gemm_f32_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(a, n_tiles);
     return hipGetLastError();
 }
 
 hipError_t launch_down_gemm_f32(const moe_config& c, const float* h, const float* w2, const int32_t* offsets,
-                                float* yp, hipStream_t s) {
+                                float* yp, const float* row_w, hipStream_t s) {
     const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     const int n_tiles = c.H / TN;
     const int64_t blocks = (R_cap / TM + c.E) * n_tiles;
     if (blocks == 0) return hipSuccess;
-    F32Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr, nullptr, nullptr, 1};
+    F32Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr, nullptr, nullptr, 1, row_w};
     grouped_gemm_f32_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(a, n_tiles);
     return hipGetLastError();
 }

@@ -41,6 +41,10 @@ struct MxArgs {
     const int32_t* src_map;
     const int32_t* counts;
     int gk;
+    // optional per-row routing weights (the epilogue placements of the
+    // weight): output row r is scaled by row_w[r] before it is stored (h
+    // before its quantisation); 256 rows past `rows` are readable
+    const float* row_w;
 };
 
 // ---------------------------------------------------------------------------
@@ -90,7 +94,9 @@ __device__ __forceinline__ uint32_t mx_word(uint32_t addr) {
     return v;
 }
 
-template <bool SWIGLU, int G>
+// RW: the outputs are scaled by p.row_w (built separately, so the plain
+// kernel carries none of it).
+template <bool SWIGLU, int G, bool RW>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     constexpr int BKB = 128;                 // K bytes (E4M3 values) per stage: four scale blocks
     constexpr int CH = BKB / 16;             // 16-byte chunks per LDS row
@@ -442,6 +448,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         const int next_unit = s_unit;
         const int e_row0 = row0, e_row_end = row_end, e_a_end = a_end, e_nt = nt;
         const bool e_valid = valid;
+        // routing weights of this wave's 128 rows, two per lane (rows 2 lane
+        // and 2 lane + 1 of the band), loaded and waited for before setup
+        // issues the next unit's loads
+        float rwa = 1.f, rwb = 1.f;
+        if constexpr (RW) {
+            if (e_valid) {
+                const float* const rwp = p.row_w + e_row0 + wm * 128 + 2 * lane;
+                rwa = rwp[0];
+                rwb = rwp[1];
+            }
+            __asm__ volatile("" : "+v"(rwa), "+v"(rwb));
+        }
         if (next_unit >= 0) setup(next_unit);
         if (e_valid) {
             int rbase = e_row0, ln = lane;
@@ -471,8 +489,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         float v[16];                                                                                     \
         float amax = 0.f;                                                                                \
         const bool pad = wm * 128 + (MI) * 32 + rr >= alim; /* gather: padding rows are zeros */        \
+        float rw = 1.f;                                                                                  \
+        if constexpr (RW) {                                                                              \
+            const float wa_ = __shfl(rwa, ((MI) * 32 + rr) >> 1, 64);                                    \
+            const float wb_ = __shfl(rwb, ((MI) * 32 + rr) >> 1, 64);                                    \
+            rw = (rr & 1) ? wb_ : wa_;                                                                   \
+        }                                                                                                \
         _Pragma("unroll") for (int j = 0; j < 16; ++j) {                                                 \
-            v[j] = pad ? 0.f : wb[rr * 33 + cc + j];                                                     \
+            v[j] = pad ? 0.f : wb[rr * 33 + cc + j] * rw;                                                \
             amax = fmaxf(amax, fabsf(v[j]));                                                             \
         }                                                                                                \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
@@ -523,9 +547,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     {                                                                                                    \
         const int rb0 = wm * 128 + (MI) * 32;                                                            \
         uint2 w[16];                                                                                     \
+        float rw[16];                                                                                    \
+        if constexpr (RW) {                                                                              \
+            _Pragma("unroll") for (int q = 0; q < 16; ++q)                                               \
+                rw[q] = __shfl((q & 1) ? rwb : rwa, ((MI) * 32 + lr + 8 * (q >> 2) + (q & 3)) >> 1, 64); \
+        } else {                                                                                         \
+            _Pragma("unroll") for (int q = 0; q < 16; ++q) rw[q] = 1.f;                                  \
+        }                                                                                                \
         _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
-            w[q] = make_uint2(pack_bf16x2(agpr_read(acc[MI][0][q]), agpr_read(acc[MI][1][q])),           \
-                              pack_bf16x2(agpr_read(acc[MI][2][q]), agpr_read(acc[MI][3][q])));          \
+            w[q] = make_uint2(pack_bf16x2(agpr_read(acc[MI][0][q]) * rw[q], agpr_read(acc[MI][1][q]) * rw[q]), \
+                              pack_bf16x2(agpr_read(acc[MI][2][q]) * rw[q], agpr_read(acc[MI][3][q]) * rw[q])); \
         if (n < p.n_out) {                                                                               \
             uint16_t* const dst = cbase + (size_t)(rb0 + lr) * p.n_out + n;                              \
             if (rb0 + 32 <= rlim) {                                                                      \

@@ -61,6 +61,12 @@ hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const int32_t
                               const int32_t* offsets, const float* w, void* dyp, hipStream_t s);
 hipError_t launch_permute_bwd(const moe_config& c, const void* dxp, const int32_t* row_map, void* dx,
                               hipStream_t s);
+// Per-row routing weights for the epilogue placements: row_w[r] =
+// w[src_map[r]] for r < R_cap, 0 for unfilled rows and for the kRowWeightPad
+// rows after R_cap (a 256-row tile reads its rows' weights without a bound).
+constexpr int kRowWeightPad = 256;
+hipError_t launch_row_weights(const moe_config& c, const int32_t* src_map, const float* w, float* row_w,
+                              hipStream_t s);
 hipError_t launch_route_bwd(const moe_config& c, const void* dy, const void* yp, const float* logits,
                             const int32_t* idx, const int32_t* row_map, float* dw, float* dlogits, hipStream_t s);
 
@@ -70,16 +76,18 @@ hipError_t launch_route_bwd(const moe_config& c, const void* dy, const void* yp,
 size_t gemm_bf16_ws_bytes(const moe_config& c);
 // Gate/up GEMMs: with src_map and counts non-null, xp is x [T,H] (+ x_scale)
 // and row r of the grouped operand is x[src_map[r] / k] (the gather form).
+// row_w (optional, from launch_row_weights): each output row r is scaled by
+// row_w[r] before it is stored (h for the gate/up GEMMs, Yp for the down).
 hipError_t launch_swiglu_gemm_bf16(const moe_config& c, const uint16_t* xp, const uint16_t* w1,
                                    const int32_t* offsets, uint16_t* h, uint16_t* stash, const int32_t* src_map,
-                                   const int32_t* counts, void* ws, hipStream_t s);
+                                   const int32_t* counts, const float* row_w, void* ws, hipStream_t s);
 hipError_t launch_down_gemm_bf16(const moe_config& c, const uint16_t* h, const uint16_t* w2, const int32_t* offsets,
-                                 uint16_t* yp, void* ws, hipStream_t s);
+                                 uint16_t* yp, const float* row_w, void* ws, hipStream_t s);
 hipError_t launch_swiglu_gemm_f32(const moe_config& c, const float* xp, const float* w1, const int32_t* offsets,
                                   float* h, float* stash, const int32_t* src_map, const int32_t* counts,
-                                  hipStream_t s);
+                                  const float* row_w, hipStream_t s);
 hipError_t launch_down_gemm_f32(const moe_config& c, const float* h, const float* w2, const int32_t* offsets,
-                                float* yp, hipStream_t s);
+                                float* yp, const float* row_w, hipStream_t s);
 
 // MXFP8
 hipError_t launch_quantize_mxfp8(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
@@ -89,10 +97,10 @@ size_t gemm_mxfp8_ws_bytes(const moe_config& c);
 hipError_t launch_swiglu_gemm_mxfp8(const moe_config& c, const uint8_t* xp, const uint8_t* xp_scale,
                                     const uint8_t* w1, const uint8_t* w1_scale, const int32_t* offsets, uint8_t* h,
                                     uint8_t* h_scale, uint16_t* stash, const int32_t* src_map,
-                                    const int32_t* counts, void* ws, hipStream_t s);
+                                    const int32_t* counts, const float* row_w, void* ws, hipStream_t s);
 hipError_t launch_down_gemm_mxfp8(const moe_config& c, const uint8_t* h, const uint8_t* h_scale, const uint8_t* w2,
-                                  const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, void* ws,
-                                  hipStream_t s);
+                                  const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, const float* row_w,
+                                  void* ws, hipStream_t s);
 
 // Backward GEMMs (bf16 / f32 storage).
 size_t bwd_workspace_bytes(const moe_config& c);

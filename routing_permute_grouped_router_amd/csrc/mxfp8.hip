@@ -67,40 +67,46 @@ int64_t rows_cap(const moe_config& c) { return (int64_t)c.T * c.k + (int64_t)c.E
 
 }  // namespace
 
+// The weighted (a.row_w set) or the plain instance of a GEMM kernel.
+template <typename K>
+void mx_launch(K weighted, K plain, const gemm::MxArgs& a, int64_t max_tiles, hipStream_t s) {
+    (a.row_w ? weighted : plain)<<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+}
+
 size_t gemm_mxfp8_ws_bytes(const moe_config& c) { return c.dtype == MOE_MXFP8 ? 256 : 0; }
 
 hipError_t launch_swiglu_gemm_mxfp8(const moe_config& c, const uint8_t* xp, const uint8_t* xp_scale,
                                     const uint8_t* w1, const uint8_t* w1_scale, const int32_t* offsets, uint8_t* h,
                                     uint8_t* h_scale, uint16_t* stash, const int32_t* src_map,
-                                    const int32_t* counts, void* ws, hipStream_t s) {
+                                    const int32_t* counts, const float* row_w, void* ws, hipStream_t s) {
     const int64_t max_tiles = (rows_cap(c) / gemm::kTile + c.E) * ((c.F + 127) / 128);
     if (max_tiles == 0) return hipSuccess;
     gemm::MxArgs a{xp, xp_scale, w1, w1_scale, offsets, c.E, c.H, (int)rows_cap(c), c.F, 2 * c.F, h, h_scale,
-                   nullptr, stash, (int*)ws, src_map, counts, c.k};
+                   nullptr, stash, (int*)ws, src_map, counts, c.k, row_w};
     zero_mx_sched_kernel<<<1, 64, 0, s>>>(a.sched);
     // scale words loaded four stages at a time when each row's scales are a
     // whole number of 16-byte pieces (K a multiple of 512)
     if (a.K % 512 == 0)
-        gemm::grouped_gemm_mxfp8<true, 4><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+        mx_launch(gemm::grouped_gemm_mxfp8<true, 4, true>, gemm::grouped_gemm_mxfp8<true, 4, false>, a, max_tiles, s);
     else
-        gemm::grouped_gemm_mxfp8<true, 1><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+        mx_launch(gemm::grouped_gemm_mxfp8<true, 1, true>, gemm::grouped_gemm_mxfp8<true, 1, false>, a, max_tiles, s);
     return hipGetLastError();
 }
 
 hipError_t launch_down_gemm_mxfp8(const moe_config& c, const uint8_t* h, const uint8_t* h_scale, const uint8_t* w2,
-                                  const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, void* ws,
-                                  hipStream_t s) {
+                                  const uint8_t* w2_scale, const int32_t* offsets, uint16_t* yp, const float* row_w,
+                                  void* ws, hipStream_t s) {
     const int64_t max_tiles = (rows_cap(c) / gemm::kTile + c.E) * ((c.H + gemm::kTile - 1) / gemm::kTile);
     if (max_tiles == 0) return hipSuccess;
     gemm::MxArgs a{h, h_scale, w2, w2_scale, offsets, c.E, c.F, (int)rows_cap(c), c.H, c.H, nullptr, nullptr,
-                   yp, nullptr, (int*)ws, nullptr, nullptr, 1};
+                   yp, nullptr, (int*)ws, nullptr, nullptr, 1, row_w};
     zero_mx_sched_kernel<<<1, 64, 0, s>>>(a.sched);
     // scale words loaded four stages at a time when each row's scales are a
     // whole number of 16-byte pieces (K a multiple of 512)
     if (a.K % 512 == 0)
-        gemm::grouped_gemm_mxfp8<false, 4><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+        mx_launch(gemm::grouped_gemm_mxfp8<false, 4, true>, gemm::grouped_gemm_mxfp8<false, 4, false>, a, max_tiles, s);
     else
-        gemm::grouped_gemm_mxfp8<false, 1><<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+        mx_launch(gemm::grouped_gemm_mxfp8<false, 1, true>, gemm::grouped_gemm_mxfp8<false, 1, false>, a, max_tiles, s);
     return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def _cfg(**kw):
-    base = dict(T=64, H=128, F=64, E=8, k=2, align=1, score=0, renorm=0, dtype=1)
+    base = dict(T=64, H=128, F=64, E=8, k=2, align=1, score=0, renorm=0, dtype=1, weight_site=0)
     base.update(kw)
     return b.moe_config(*[base[n] for n, _ in b.moe_config._fields_])
 
@@ -44,6 +44,7 @@ def _cfg(**kw):
     (dict(align=0), b.MOE_ERR_INVALID_ARG),
     (dict(score=5), b.MOE_ERR_INVALID_ARG),
     (dict(dtype=7), b.MOE_ERR_INVALID_ARG),
+    (dict(weight_site=3), b.MOE_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected_on_host(kw, status):
     lib = moe.load_library()
@@ -148,3 +149,23 @@ def test_device_e4m3_rounding_matches_oracle(tmp_path):
                     "-o", str(exe)], check=True, capture_output=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-2000:]
+
+
+def test_weighted_gemms_and_placement_checked_on_host():
+    lib = moe.load_library()
+    c = _cfg(weight_site=b.MOE_WEIGHT_AT_FC2)
+    need = lib.moe_workspace_size(ctypes.byref(c))
+    # the per-row weights need src_map and w
+    st = lib.moe_grouped_down_gemm_weighted(ctypes.byref(c), 1, None, 1, None, 1, None, 1, 1, 1, need, None)
+    assert st == b.MOE_ERR_INVALID_ARG and b"src_map" in lib.moe_last_error()
+    st = lib.moe_grouped_swiglu_gemm_weighted(ctypes.byref(c), 1, None, 1, None, 1, 1, None, 1, None, 1, need, None)
+    assert st == b.MOE_ERR_INVALID_ARG and b"w" in lib.moe_last_error()
+    # the workspace holds the per-row weights as well
+    c0 = _cfg()
+    assert need == lib.moe_workspace_size(ctypes.byref(c0))
+    assert need >= 4 * (64 * 2 + 256)
+    # the backward is built for the weights applied in the combine
+    assert lib.moe_combine_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+    # an unweighted combine takes w = NULL (T = 0: nothing to launch)
+    assert lib.moe_combine(ctypes.byref(_cfg(T=0)), None, None, None, None, None) == b.MOE_OK
