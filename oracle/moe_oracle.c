@@ -44,6 +44,40 @@ enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
 
 #define OR_MX_BLOCK 32
 
+/*
+ * Optional SwiGLU clamp ([CUDNN] Summary: local SwiGLU experts with an
+ * optional DeepSeek-style clamp; the pages state no bounds).  With a limit
+ * L > 0 the gate is clamped from above and the up projection to [-L, L]
+ * before the activation:
+ *   h = silu(min(g, L)) * clamp(u, -L, L)
+ * and the gradient of each clamp passes where its bound is not exceeded (the
+ * bounds themselves included).  L = 0: no clamp.  The limit is set per call
+ * by the Python wrapper (or_set_swiglu_limit) before the function using it.
+ */
+static double or_limit = 0.0;
+void or_set_swiglu_limit(double limit) { or_limit = limit; }
+
+static double or_swiglu(double g, double u) {
+    if (or_limit > 0.0) {
+        g = g > or_limit ? or_limit : g;
+        u = u > or_limit ? or_limit : (u < -or_limit ? -or_limit : u);
+    }
+    return (g / (1.0 + exp(-g))) * u;
+}
+
+/* Partial derivatives dh/dg and dh/du of or_swiglu at the unclamped (g, u). */
+static void or_swiglu_grad(double g, double u, double* dg, double* du) {
+    double mg = 1.0, mu = 1.0;
+    if (or_limit > 0.0) {
+        if (g > or_limit) { g = or_limit; mg = 0.0; }
+        if (u > or_limit) { u = or_limit; mu = 0.0; }
+        if (u < -or_limit) { u = -or_limit; mu = 0.0; }
+    }
+    const double sig = 1.0 / (1.0 + exp(-g));
+    *dg = mg * u * sig * (1.0 + g * (1.0 - sig));
+    *du = mu * g * sig;
+}
+
 /* Where the routing weight is applied (its own numbering). */
 enum { OR_AT_COMBINE = 0, OR_AT_FC1 = 1, OR_AT_FC2 = 2 };
 
@@ -412,7 +446,7 @@ void or_expert_row(int H, int F, int fmt, const void* x_row, const uint8_t* x_sc
     }
     for (int f = 0; f < F; ++f) {
         double g = gu[f], u = gu[F + f];
-        hv[f] = (g / (1.0 + exp(-g))) * u;
+        hv[f] = or_swiglu(g, u);
         if (site == OR_AT_FC1) hv[f] *= row_w;
     }
     if (stash_out) or_store_row(s_fmt, gu, 2 * F, stash_out, NULL);
@@ -588,10 +622,10 @@ int or_backward(int T, int H, int F, int E, int k, int fmt, int g_fmt, const voi
         }
         const void* sr = (const uint8_t*)stash + r * sb;
         for (int f = 0; f < F; ++f) {
-            double g = or_load(s_fmt, sr, NULL, f), u = or_load(s_fmt, sr, NULL, F + f);
-            double sig = 1.0 / (1.0 + exp(-g));
-            d[f] = dh[f] * u * sig * (1.0 + g * (1.0 - sig));
-            d[F + f] = dh[f] * g * sig;
+            double g = or_load(s_fmt, sr, NULL, f), u = or_load(s_fmt, sr, NULL, F + f), dg, du;
+            or_swiglu_grad(g, u, &dg, &du);
+            d[f] = dh[f] * dg;
+            d[F + f] = dh[f] * du;
         }
         void* dgr = (uint8_t*)dgu + r * 2 * F * gb;
         or_store_row(g_fmt, d, 2 * F, dgr, NULL);
@@ -667,7 +701,7 @@ static void or_route_gu(int H, int F, int fmt, int s_fmt, int h_fmt, const void*
         for (int c = 0; c < H; ++c) acc += xv[c] * or_load(fmt, wrow, NULL, c);
         gu[n] = acc;
     }
-    for (int f = 0; f < F; ++f) h[f] = (gu[f] / (1.0 + exp(-gu[f]))) * gu[F + f];
+    for (int f = 0; f < F; ++f) h[f] = or_swiglu(gu[f], gu[F + f]);
     or_round_trip_row(h_fmt, h, F);
     or_round_trip_row(s_fmt, gu, 2 * F);
     for (int f = 0; f < F; ++f) { g[f] = gu[f]; u[f] = gu[F + f]; }
@@ -709,9 +743,10 @@ int or_backward_dx_tokens(int H, int F, int k, int fmt, int g_fmt, int h_fmt, in
                 for (int f = 0; f < F; ++f) dh[f] += dyp[o] * or_load(fmt, wrow, NULL, f);
             }
             for (int f = 0; f < F; ++f) {
-                double sig = 1.0 / (1.0 + exp(-g[f]));
-                d[f] = dh[f] * u[f] * sig * (1.0 + g[f] * (1.0 - sig));
-                d[F + f] = dh[f] * g[f] * sig;
+                double dg, du;
+                or_swiglu_grad(g[f], u[f], &dg, &du);
+                d[f] = dh[f] * dg;
+                d[F + f] = dh[f] * du;
             }
             or_round_trip_row(g_fmt, d, 2 * F);
             for (int c = 0; c < H; ++c) dxr[c] = 0.0;
@@ -767,8 +802,9 @@ int or_backward_dw_entries(int H, int F, int k, int fmt, int g_fmt, int h_fmt, i
             const int n = n1i[i], f = n % F;
             double dh = 0.0;
             for (int o = 0; o < H; ++o) dh += dyp[o] * or_load(fmt, w2e + (size_t)o * F * eb, NULL, f);
-            double sig = 1.0 / (1.0 + exp(-g[f]));
-            double d = n < F ? dh * u[f] * sig * (1.0 + g[f] * (1.0 - sig)) : dh * g[f] * sig;
+            double dg, du;
+            or_swiglu_grad(g[f], u[f], &dg, &du);
+            double d = n < F ? dh * dg : dh * du;
             d = g_fmt == OR_F32 ? (double)(float)d : or_double_from_bf16(or_bf16_from_double(d));
             cc1[q * n1 + i] = d * or_load(fmt, xr, NULL, c1[i]);
         }

@@ -60,6 +60,7 @@ def _load():
         "or_forward_tokens": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P,
                                     P, P, P]),
         "or_combine": (None, [I32, I32, I32, I32, P, P, P, P]),
+        "or_set_swiglu_limit": (None, [ctypes.c_double]),
         "or_backward": (I32, [I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, I32, P, I32, P, P, P, P,
                               P, P, P]),
         "or_backward_dx_tokens": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]),
@@ -251,9 +252,10 @@ SITES = {"combine": 0, "fc1": 1, "fc2": 2}
 
 
 def forward_tokens(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=None, w2_scale=None,
-                   want_stash: bool = False, site: str = "combine"):
+                   want_stash: bool = False, site: str = "combine", limit: float = 0.0):
     """Per-token evaluation of the expert FFN and the combine.
 
+    limit: the optional SwiGLU clamp (0 = none): h = silu(min(g, L)) clamp(u, -L, L).
     site: where the routing weight is applied ([CUDNN] Summary: router weight in
     the FC1 or FC2 epilogue): "combine" (default), "fc1" (h scaled before it is
     stored) or "fc2" (Yp scaled before it is stored; the combine then sums).
@@ -282,6 +284,7 @@ def forward_tokens(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=None
     xs = None if x_scale is None else np.ascontiguousarray(x_scale)
     w1s = None if w1_scale is None else np.ascontiguousarray(w1_scale)
     w2s = None if w2_scale is None else np.ascontiguousarray(w2_scale)
+    _load().or_set_swiglu_limit(float(limit))
     rc = _load().or_forward_tokens(s.H, s.F, k, FMT[fmt], FMT[h_fmt], FMT[y_fmt], FMT[s_fmt], SITES[site], n,
                                    tokens.ctypes.data,
                                    x.ctypes.data, _p(xs), w1.ctypes.data, _p(w1s), w2.ctypes.data, _p(w2s),
@@ -309,7 +312,7 @@ def combine(yp, row_map, w, y_fmt: str):
     return y
 
 
-def backward(shape, x, w1, w2, w, row_map, src_map, offsets, h_rows, stash_rows, dy):
+def backward(shape, x, w1, w2, w, row_map, src_map, offsets, h_rows, stash_rows, dy, limit: float = 0.0):
     """Full backward (small shapes).  h_rows [R_cap, F] / stash_rows [R_cap, 2F]
     are the forward's stored h and stash arranged by permuted row."""
     s = shape
@@ -331,6 +334,7 @@ def backward(shape, x, w1, w2, w, row_map, src_map, offsets, h_rows, stash_rows,
     h_rows = np.ascontiguousarray(h_rows)
     stash_rows = np.ascontiguousarray(stash_rows)
     dy = np.ascontiguousarray(dy)
+    _load().or_set_swiglu_limit(float(limit))
     rc = _load().or_backward(s.T, s.H, s.F, s.E, s.k, FMT[fmt], FMT[g_fmt], args[0].ctypes.data, args[1].ctypes.data,
                              args[2].ctypes.data, w.ctypes.data, row_map.ctypes.data, src_map.ctypes.data,
                              offsets.ctypes.data, h_rows.ctypes.data, FMT[fmt], stash_rows.ctypes.data,
@@ -341,13 +345,14 @@ def backward(shape, x, w1, w2, w, row_map, src_map, offsets, h_rows, stash_rows,
     return {"dyp": dyp, "dgu": dgu, "dxp": dxp, "dx": dx, "dw1": dw1, "dw2": dw2}
 
 
-def backward_dx_tokens(shape, tokens, x, w1, w2, idx, w, dy):
+def backward_dx_tokens(shape, tokens, x, w1, w2, idx, w, dy, limit: float = 0.0):
     s = shape
     fmt = s.dtype
     g_fmt = "f32" if fmt == "f32" else "bf16"
     tokens = _c(np.asarray(tokens, np.int32), np.int32)
     dx = np.empty((tokens.size, s.H), _NP[g_fmt])
     a = [np.ascontiguousarray(v) for v in (x, w1, w2, dy)]
+    _load().or_set_swiglu_limit(float(limit))
     rc = _load().or_backward_dx_tokens(s.H, s.F, s.k, FMT[fmt], FMT[g_fmt], FMT[fmt], FMT[g_fmt], tokens.size,
                                        tokens.ctypes.data, a[0].ctypes.data, a[1].ctypes.data, a[2].ctypes.data,
                                        _c(idx, np.int32).ctypes.data, _c(w, np.float32).ctypes.data,
@@ -357,7 +362,7 @@ def backward_dx_tokens(shape, tokens, x, w1, w2, idx, w, dy):
     return dx
 
 
-def backward_dw_entries(shape, e, x, w1, w2, w, src_map, offsets, dy, dw2_idx, dw1_idx):
+def backward_dw_entries(shape, e, x, w1, w2, w, src_map, offsets, dy, dw2_idx, dw1_idx, limit: float = 0.0):
     """dW2s[e][o, f] for (o, f) in dw2_idx and dW1s[e][n, c] for (n, c) in dw1_idx (float64)."""
     s = shape
     fmt = s.dtype
@@ -371,6 +376,7 @@ def backward_dw_entries(shape, e, x, w1, w2, w, src_map, offsets, dy, dw2_idx, d
     out2 = np.empty(len(o2), np.float64)
     out1 = np.empty(len(n1), np.float64)
     a = [np.ascontiguousarray(v) for v in (x, w1, w2, dy)]
+    _load().or_set_swiglu_limit(float(limit))
     rc = _load().or_backward_dw_entries(s.H, s.F, s.k, FMT[fmt], FMT[g_fmt], FMT[fmt], FMT[g_fmt], int(e),
                                         a[0].ctypes.data, a[1].ctypes.data, a[2].ctypes.data,
                                         _c(w, np.float32).ctypes.data, _c(src_map, np.int32).ctypes.data,
