@@ -291,9 +291,11 @@ def main():
         variants = {"gather_forward": {"ms_per_step": round(gms, 4), "tokens_per_s": round(s.T / (gms * 1e-3), 1),
                                        "swiglu_gemm_gather_ms": round(g1.elapsed_time(g2) / args.steps, 4)}}
         # The routing weight applied in the gate/up (FC1) or down (FC2)
-        # epilogue instead of the combine, on the materialised step.
-        for site in ("fc1", "fc2"):
-            cw = dataclasses.replace(cfg, weight_site=site)
+        # epilogue instead of the combine, and the SwiGLU clamp (its cost does
+        # not depend on the limit), each on the materialised step.
+        for vname, change in (("weight_fc1", dict(weight_site="fc1")), ("weight_fc2", dict(weight_site="fc2")),
+                              ("swiglu_clamp", dict(swiglu_limit=7.0))):
+            cw = dataclasses.replace(cfg, **change)
             for _ in range(2):
                 moe.moe_forward(cw, logits, x, w1, w2, buf, **scales)
             torch.cuda.synchronize()
@@ -303,7 +305,7 @@ def main():
             g1.record(stream)
             torch.cuda.synchronize()
             wms = g0.elapsed_time(g1) / args.steps
-            variants[f"weight_{site}"] = {"ms_per_step": round(wms, 4), "tokens_per_s": round(s.T / (wms * 1e-3), 1)}
+            variants[vname] = {"ms_per_step": round(wms, 4), "tokens_per_s": round(s.T / (wms * 1e-3), 1)}
 
     R, T, H, F, E, k = s.R, s.T, s.H, s.F, s.E, s.k
     esz = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32}[s.dtype]

@@ -108,6 +108,13 @@ typedef struct moe_config {
                        sigmoid: always normalised over the k selected        */
     int32_t dtype;  /* moe_dtype of x / weights / Xp / h                     */
     int32_t weight_site; /* moe_weight_site: where moe_forward applies w     */
+    float swiglu_limit;  /* optional SwiGLU clamp ([CUDNN] Summary: optional
+                            DeepSeek-style clamp; no bounds on the pages):
+                            L > 0: h = silu(min(g, L)) * clamp(u, -L, L) in
+                            every gate/up GEMM, and the backward passes the
+                            gradient only where the bound is not exceeded
+                            (bounds included); 0: no clamp.  The stash keeps
+                            the unclamped g and u.  Must be finite, >= 0.    */
 } moe_config;
 
 /* Rows of the permuted buffers: T*k + E*(align-1).  Host only. */

@@ -55,7 +55,8 @@ _EXC = {MOE_ERR_INVALID_ARG: MoEInvalidArgument, MOE_ERR_UNSUPPORTED: MoEUnsuppo
 
 class moe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32)
-                for n in ("T", "H", "F", "E", "k", "align", "score", "renorm", "dtype", "weight_site")]
+                for n in ("T", "H", "F", "E", "k", "align", "score", "renorm", "dtype", "weight_site")] + [
+                    ("swiglu_limit", ctypes.c_float)]
 
 
 @dataclass(frozen=True)
@@ -70,6 +71,7 @@ class MoEConfig:
     renorm: bool = False
     dtype: str = "bf16"
     weight_site: str = "combine"  # where moe_forward applies w: "combine", "fc1" or "fc2"
+    swiglu_limit: float = 0.0     # SwiGLU clamp: h = silu(min(g, L)) clamp(u, -L, L); 0 = none
 
     @classmethod
     def from_shape(cls, s) -> "MoEConfig":
@@ -77,7 +79,8 @@ class MoEConfig:
 
     def c(self) -> moe_config:
         return moe_config(self.T, self.H, self.F, self.E, self.k, self.align, SCORES[self.score],
-                          int(self.renorm), DTYPES[self.dtype], WEIGHT_SITES[self.weight_site])
+                          int(self.renorm), DTYPES[self.dtype], WEIGHT_SITES[self.weight_site],
+                          float(self.swiglu_limit))
 
     @property
     def R_cap(self) -> int:

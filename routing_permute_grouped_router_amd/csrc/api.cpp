@@ -55,6 +55,8 @@ moe_status check_config(const moe_config* cfg) {
         c.weight_site != MOE_WEIGHT_AT_FC2)
         return fail(MOE_ERR_INVALID_ARG, "weight_site must be MOE_WEIGHT_AT_COMBINE, _FC1 or _FC2 (got %d)",
                     c.weight_site);
+    if (!(c.swiglu_limit >= 0.f) || c.swiglu_limit == INFINITY)
+        return fail(MOE_ERR_INVALID_ARG, "swiglu_limit must be finite and >= 0 (got %g)", (double)c.swiglu_limit);
     if (rows_capacity(c) >= (int64_t)1 << 31)
         return fail(MOE_ERR_INVALID_ARG, "T*k + E*(align-1) must be below 2^31");
     if ((int64_t)c.T * c.H >= (int64_t)1 << 40) return fail(MOE_ERR_INVALID_ARG, "T*H too large");

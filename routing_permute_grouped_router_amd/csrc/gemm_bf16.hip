@@ -111,10 +111,17 @@ __global__ __launch_bounds__(256) void split_reduce_bf16(gemm::Args p, int nb) {
         }
         const size_t row = (size_t)(row0 + r);
         const float rw = p.row_w ? p.row_w[row] : 1.f;
+        // the SwiGLU inputs, clamped when a limit is set (the stash keeps g, u)
+        float4 gc = g, uc = u;
+        if (SWIGLU && p.lim < INFINITY) {
+            gc.x = fminf(g.x, p.lim); gc.y = fminf(g.y, p.lim); gc.z = fminf(g.z, p.lim); gc.w = fminf(g.w, p.lim);
+            uc.x = fminf(fmaxf(u.x, -p.lim), p.lim); uc.y = fminf(fmaxf(u.y, -p.lim), p.lim);
+            uc.z = fminf(fmaxf(u.z, -p.lim), p.lim); uc.w = fminf(fmaxf(u.w, -p.lim), p.lim);
+        }
         if (SWIGLU) {
             *(uint2*)(p.C + row * p.n_out + n) =
-                row0 + r < a_end ? make_uint2(pack_bf16x2(silu(g.x) * u.x * rw, silu(g.y) * u.y * rw),
-                                              pack_bf16x2(silu(g.z) * u.z * rw, silu(g.w) * u.w * rw))
+                row0 + r < a_end ? make_uint2(pack_bf16x2(silu(gc.x) * uc.x * rw, silu(gc.y) * uc.y * rw),
+                                              pack_bf16x2(silu(gc.z) * uc.z * rw, silu(gc.w) * uc.w * rw))
                                  : make_uint2(0u, 0u);
             if (p.stash) {
                 *(uint2*)(p.stash + row * 2 * p.n_out + n) = make_uint2(pack_bf16x2(g.x, g.y), pack_bf16x2(g.z, g.w));
@@ -134,10 +141,14 @@ hipError_t launch_bf16(gemm::Args a, int64_t max_tiles, void* ws, hipStream_t s)
     a.sched = (int*)ws;
     a.part = (float*)((char*)ws + 256);
     zero_sched_kernel<<<1, 64, 0, s>>>(a.sched);
-    if (a.row_w)
-        gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM, true><<<grid, gemm::kThreads, 0, s>>>(a);
-    else
-        gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM, false><<<grid, gemm::kThreads, 0, s>>>(a);
+    // epilogue variant: row weights (bit 1), SwiGLU clamp (bit 2)
+    const int ep = (a.row_w ? 1 : 0) | (SWIGLU && a.lim < INFINITY ? 2 : 0);
+    if (ep == 0) gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM, 0><<<grid, gemm::kThreads, 0, s>>>(a);
+    else if (ep == 1) gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM, 1><<<grid, gemm::kThreads, 0, s>>>(a);
+    else if constexpr (SWIGLU) {
+        if (ep == 2) gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM, 2><<<grid, gemm::kThreads, 0, s>>>(a);
+        else gemm::grouped_gemm_bf16<SWIGLU, kSwizzle, kGroupM, 3><<<grid, gemm::kThreads, 0, s>>>(a);
+    }
     split_reduce_bf16<SWIGLU, kGroupM><<<dim3(gemm::kSlotsPerXcd * (gemm::kTile / kReduceRows), gemm::kXcds), 256, 0, s>>>(
         a, grid / gemm::kXcds);
     return hipGetLastError();
@@ -152,7 +163,7 @@ hipError_t launch_swiglu_gemm_bf16(const moe_config& c, const uint16_t* xp, cons
     const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.F + 127) / 128);
     if (max_tiles == 0) return hipSuccess;
     gemm::Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash, nullptr, nullptr,
-                 src_map, counts, c.k, row_w};
+                 src_map, counts, c.k, row_w, c.swiglu_limit > 0.f ? c.swiglu_limit : INFINITY};
     return launch_bf16<true>(a, max_tiles, ws, s);
 }
 
@@ -162,7 +173,7 @@ hipError_t launch_down_gemm_bf16(const moe_config& c, const uint16_t* h, const u
     const int64_t max_tiles = (R_cap / gemm::kTile + c.E) * ((c.H + gemm::kTile - 1) / gemm::kTile);
     if (max_tiles == 0) return hipSuccess;
     gemm::Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr, nullptr, nullptr,
-                 nullptr, nullptr, 1, row_w};
+                 nullptr, nullptr, 1, row_w, INFINITY};
     return launch_bf16<false>(a, max_tiles, ws, s);
 }
 

@@ -65,6 +65,9 @@ struct Args {
     // weight): output row r is scaled by row_w[r] before it is stored.  The
     // array holds 256 rows past `rows`, so a tile reads without a bound.
     const float* row_w;
+    // SwiGLU clamp limit (the clamped variant only): g <- min(g, lim),
+    // u <- clamp(u, -lim, lim) before the activation; +inf when off
+    float lim;
 };
 
 // Work queues.  The tiles are cut into kXcds contiguous ranges, one per XCD
@@ -185,9 +188,10 @@ __device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// RW: the outputs are scaled by p.row_w (built separately, so the plain
-// kernel carries none of it).
-template <bool SWIGLU, int SWZ, int GM, bool RW>
+// EP, epilogue variant bits (built separately, so the plain kernel carries
+// none of it): 1 = the outputs are scaled by p.row_w, 2 = the SwiGLU inputs
+// are clamped to p.lim.
+template <bool SWIGLU, int SWZ, int GM, int EP>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     constexpr int BK = 64;                  // K depth of one stage
     constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         // and 2 lane + 1 of the band), loaded and waited for before setup
         // issues the next unit's loads: the wait then covers only these.
         float rwa = 1.f, rwb = 1.f;
-        if constexpr (RW) {
+        if constexpr ((EP & 1) != 0) {
             if (e_valid) {
                 const float* const rwp = p.row_w + e_row0 + wm * 128 + 2 * lane;
                 rwa = rwp[0];
@@ -561,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         // 32-row block MI (1 without weights); row i of the wave's band sits
         // in lane i / 2, as rwa (even i) or rwb (odd i).
 #define GB_ROW_WEIGHTS(MI, W_)                                                                           \
-    if constexpr (RW) {                                                                                  \
+    if constexpr ((EP & 1) != 0) {                                                                       \
         _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
             W_[q] = __shfl((q & 1) ? rwb : rwa, ((MI) * 32 + lr + 8 * (q >> 2) + (q & 3)) >> 1, 64);     \
     } else {                                                                                             \
@@ -621,8 +625,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         float rw[16];                                                                                    \
         GB_ROW_WEIGHTS(MI, rw)                                                                           \
         _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                                 \
-            const float g0 = agpr_read(acc[MI][0][q]), g1 = agpr_read(acc[MI][1][q]);                    \
-            const float u0 = agpr_read(acc[MI][2][q]), u1 = agpr_read(acc[MI][3][q]);                    \
+            float g0 = agpr_read(acc[MI][0][q]), g1 = agpr_read(acc[MI][1][q]);                          \
+            float u0 = agpr_read(acc[MI][2][q]), u1 = agpr_read(acc[MI][3][q]);                          \
+            if constexpr ((EP & 2) != 0) {                                                               \
+                g0 = fminf(g0, p.lim);                                                                   \
+                g1 = fminf(g1, p.lim);                                                                   \
+                u0 = fminf(fmaxf(u0, -p.lim), p.lim);                                                    \
+                u1 = fminf(fmaxf(u1, -p.lim), p.lim);                                                    \
+            }                                                                                            \
             hw[q] = pack_bf16x2(silu(g0) * u0 * rw[q], silu(g1) * u1 * rw[q]);                           \
             if (rb0 + lr + 8 * (q >> 2) + (q & 3) >= alim) hw[q] = 0; /* gather: padding rows */         \
         }                                                                                                \

@@ -66,6 +66,9 @@ struct BwdArgs {
     // Tile counters, one per XCD, zero at launch: the blocks of an XCD take
     // their next tile from the XCD's list with an atomic increment.
     int* sched;
+    // kDgradDswiglu: the forward's SwiGLU clamp limit (+inf: none); the
+    // gradient of a clamped gate or up value is 0, values on a bound pass
+    float lim;
 };
 
 constexpr int kMaxUnits = 2048;  // weight-gradient units dealt by size (beyond: by index)
@@ -506,6 +509,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
             uq[(PS) & 7] = *(const uint4*)(sbase + (size_t)r_ * ldc + N);                                \
         }                                                                                                \
     }
+            const bool clamp = MODE == kDgradDswiglu && p.lim < INFINITY;  // uniform
             if (MODE == kDgradDswiglu) {
 #pragma unroll
                 for (int ps = 0; ps < 8; ++ps) GB_LOAD_STASH(ps)
@@ -546,11 +550,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
                         float rg[2], ru[2];
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
-                            const float g = __uint_as_float(h ? (gw[j] & 0xffff0000u) : (gw[j] << 16));
-                            const float u = __uint_as_float(h ? (uw[j] & 0xffff0000u) : (uw[j] << 16));
+                            float g = __uint_as_float(h ? (gw[j] & 0xffff0000u) : (gw[j] << 16));
+                            float u = __uint_as_float(h ? (uw[j] & 0xffff0000u) : (uw[j] << 16));
+                            float mg = 1.f, mu = 1.f;
+                            if (clamp) {
+                                mg = g > p.lim ? 0.f : 1.f;
+                                mu = (u > p.lim || u < -p.lim) ? 0.f : 1.f;
+                                g = fminf(g, p.lim);
+                                u = fminf(fmaxf(u, -p.lim), p.lim);
+                            }
                             const float sg = sigmoid_fast(g);
-                            rg[h] = dh[2 * j + h] * u * sg * (1.0f + g * (1.0f - sg));
-                            ru[h] = dh[2 * j + h] * g * sg;
+                            rg[h] = dh[2 * j + h] * u * sg * (1.0f + g * (1.0f - sg)) * mg;
+                            ru[h] = dh[2 * j + h] * g * sg * mu;
                         }
                         dg[j] = pack_bf16x2(rg[0], rg[1]);
                         du[j] = pack_bf16x2(ru[0], ru[1]);

@@ -29,6 +29,7 @@ struct F32Args {
     const int32_t* counts;
     int gk;
     const float* row_w;  // optional: output row r scaled by row_w[r] before it is stored
+    float lim;           // SwiGLU clamp limit (+inf: none)
 };
 
 template <bool SWIGLU>
@@ -104,7 +105,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(F32Args p, int n_
             for (int j = 0; j < 2; ++j) {
                 const int f = nt * 32 + tx * 2 + j;
                 const float g = acc[i][j], u = acc[i][2 + j];
-                p.C[(size_t)r * p.n_out + f] = (g / (1.0f + expf(-g))) * u * rw;
+                const float gc = p.lim < INFINITY ? fminf(g, p.lim) : g;
+                const float uc = p.lim < INFINITY ? fminf(fmaxf(u, -p.lim), p.lim) : u;
+                p.C[(size_t)r * p.n_out + f] = (gc / (1.0f + expf(-gc))) * uc * rw;
                 if (p.stash) {
                     p.stash[(size_t)r * 2 * p.n_out + f] = g;
                     p.stash[(size_t)r * 2 * p.n_out + p.n_out + f] = u;
@@ -126,7 +129,8 @@ hipError_t launch_swiglu_gemm_f32(const moe_config& c, const float* xp, const fl
     const int n_tiles = c.F / 32;
     const int64_t blocks = (R_cap / TM + c.E) * n_tiles;
     if (blocks == 0) return hipSuccess;
-    F32Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash, src_map, counts, c.k, row_w};
+    F32Args a{xp, w1, offsets, c.E, c.H, (int)R_cap, c.F, 2 * c.F, h, stash, src_map, counts, c.k, row_w,
+              c.swiglu_limit > 0.f ? c.swiglu_limit : INFINITY};
     grouped_gemm_f32_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(a, n_tiles);
     return hipGetLastError();
 }
@@ -137,7 +141,7 @@ hipError_t launch_down_gemm_f32(const moe_config& c, const float* h, const float
     const int n_tiles = c.H / TN;
     const int64_t blocks = (R_cap / TM + c.E) * n_tiles;
     if (blocks == 0) return hipSuccess;
-    F32Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr, nullptr, nullptr, 1, row_w};
+    F32Args a{h, w2, offsets, c.E, c.F, (int)R_cap, c.H, c.H, yp, nullptr, nullptr, nullptr, 1, row_w, INFINITY};
     grouped_gemm_f32_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(a, n_tiles);
     return hipGetLastError();
 }

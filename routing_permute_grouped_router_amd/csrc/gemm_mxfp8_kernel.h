@@ -45,6 +45,9 @@ struct MxArgs {
     // weight): output row r is scaled by row_w[r] before it is stored (h
     // before its quantisation); 256 rows past `rows` are readable
     const float* row_w;
+    // SwiGLU clamp limit (the clamped variant only): g <- min(g, lim),
+    // u <- clamp(u, -lim, lim) before the activation; +inf when off
+    float lim;
 };
 
 // ---------------------------------------------------------------------------
@@ -94,9 +97,10 @@ __device__ __forceinline__ uint32_t mx_word(uint32_t addr) {
     return v;
 }
 
-// RW: the outputs are scaled by p.row_w (built separately, so the plain
-// kernel carries none of it).
-template <bool SWIGLU, int G, bool RW>
+// EP, epilogue variant bits (built separately, so the plain kernel carries
+// none of it): 1 = the outputs are scaled by p.row_w, 2 = the SwiGLU inputs
+// are clamped to p.lim.
+template <bool SWIGLU, int G, int EP>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     constexpr int BKB = 128;                 // K bytes (E4M3 values) per stage: four scale blocks
     constexpr int CH = BKB / 16;             // 16-byte chunks per LDS row
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         // and 2 lane + 1 of the band), loaded and waited for before setup
         // issues the next unit's loads
         float rwa = 1.f, rwb = 1.f;
-        if constexpr (RW) {
+        if constexpr ((EP & 1) != 0) {
             if (e_valid) {
                 const float* const rwp = p.row_w + e_row0 + wm * 128 + 2 * lane;
                 rwa = rwp[0];
@@ -483,14 +487,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     {                                                                                                    \
         float hv[16];                                                                                    \
         _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
-            hv[q] = silu(agpr_read(acc[MI][NI][q])) * agpr_read(acc[MI][(NI) + 2][q]);                   \
+            hv[q] = (EP & 2) != 0 ? silu(fminf(agpr_read(acc[MI][NI][q]), p.lim)) *                      \
+                                        fminf(fmaxf(agpr_read(acc[MI][(NI) + 2][q]), -p.lim), p.lim)     \
+                                  : silu(agpr_read(acc[MI][NI][q])) * agpr_read(acc[MI][(NI) + 2][q]);   \
         GE_STAGE_TILE(wb, hv)                                                                            \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
         float v[16];                                                                                     \
         float amax = 0.f;                                                                                \
         const bool pad = wm * 128 + (MI) * 32 + rr >= alim; /* gather: padding rows are zeros */        \
         float rw = 1.f;                                                                                  \
-        if constexpr (RW) {                                                                              \
+        if constexpr ((EP & 1) != 0) {                                                                              \
             const float wa_ = __shfl(rwa, ((MI) * 32 + rr) >> 1, 64);                                    \
             const float wb_ = __shfl(rwb, ((MI) * 32 + rr) >> 1, 64);                                    \
             rw = (rr & 1) ? wb_ : wa_;                                                                   \
@@ -548,7 +554,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         const int rb0 = wm * 128 + (MI) * 32;                                                            \
         uint2 w[16];                                                                                     \
         float rw[16];                                                                                    \
-        if constexpr (RW) {                                                                              \
+        if constexpr ((EP & 1) != 0) {                                                                              \
             _Pragma("unroll") for (int q = 0; q < 16; ++q)                                               \
                 rw[q] = __shfl((q & 1) ? rwb : rwa, ((MI) * 32 + lr + 8 * (q >> 2) + (q & 3)) >> 1, 64); \
         } else {                                                                                         \

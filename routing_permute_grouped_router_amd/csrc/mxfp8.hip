@@ -67,10 +67,18 @@ int64_t rows_cap(const moe_config& c) { return (int64_t)c.T * c.k + (int64_t)c.E
 
 }  // namespace
 
-// The weighted (a.row_w set) or the plain instance of a GEMM kernel.
-template <typename K>
-void mx_launch(K weighted, K plain, const gemm::MxArgs& a, int64_t max_tiles, hipStream_t s) {
-    (a.row_w ? weighted : plain)<<<gemm_persistent_grid(max_tiles), gemm::kThreads, 0, s>>>(a);
+// The instance of a GEMM kernel for the epilogue variant the arguments ask
+// for: row weights (bit 1), SwiGLU clamp (bit 2).
+template <bool SWIGLU, int G>
+void mx_launch(const gemm::MxArgs& a, int64_t max_tiles, hipStream_t s) {
+    const int ep = (a.row_w ? 1 : 0) | (SWIGLU && a.lim < INFINITY ? 2 : 0);
+    const unsigned grid = gemm_persistent_grid(max_tiles);
+    if (ep == 0) gemm::grouped_gemm_mxfp8<SWIGLU, G, 0><<<grid, gemm::kThreads, 0, s>>>(a);
+    else if (ep == 1) gemm::grouped_gemm_mxfp8<SWIGLU, G, 1><<<grid, gemm::kThreads, 0, s>>>(a);
+    else if constexpr (SWIGLU) {
+        if (ep == 2) gemm::grouped_gemm_mxfp8<SWIGLU, G, 2><<<grid, gemm::kThreads, 0, s>>>(a);
+        else gemm::grouped_gemm_mxfp8<SWIGLU, G, 3><<<grid, gemm::kThreads, 0, s>>>(a);
+    }
 }
 
 size_t gemm_mxfp8_ws_bytes(const moe_config& c) { return c.dtype == MOE_MXFP8 ? 256 : 0; }
@@ -82,14 +90,15 @@ hipError_t launch_swiglu_gemm_mxfp8(const moe_config& c, const uint8_t* xp, cons
     const int64_t max_tiles = (rows_cap(c) / gemm::kTile + c.E) * ((c.F + 127) / 128);
     if (max_tiles == 0) return hipSuccess;
     gemm::MxArgs a{xp, xp_scale, w1, w1_scale, offsets, c.E, c.H, (int)rows_cap(c), c.F, 2 * c.F, h, h_scale,
-                   nullptr, stash, (int*)ws, src_map, counts, c.k, row_w};
+                   nullptr, stash, (int*)ws, src_map, counts, c.k, row_w,
+                   c.swiglu_limit > 0.f ? c.swiglu_limit : INFINITY};
     zero_mx_sched_kernel<<<1, 64, 0, s>>>(a.sched);
     // scale words loaded four stages at a time when each row's scales are a
     // whole number of 16-byte pieces (K a multiple of 512)
     if (a.K % 512 == 0)
-        mx_launch(gemm::grouped_gemm_mxfp8<true, 4, true>, gemm::grouped_gemm_mxfp8<true, 4, false>, a, max_tiles, s);
+        mx_launch<true, 4>(a, max_tiles, s);
     else
-        mx_launch(gemm::grouped_gemm_mxfp8<true, 1, true>, gemm::grouped_gemm_mxfp8<true, 1, false>, a, max_tiles, s);
+        mx_launch<true, 1>(a, max_tiles, s);
     return hipGetLastError();
 }
 
@@ -99,14 +108,14 @@ hipError_t launch_down_gemm_mxfp8(const moe_config& c, const uint8_t* h, const u
     const int64_t max_tiles = (rows_cap(c) / gemm::kTile + c.E) * ((c.H + gemm::kTile - 1) / gemm::kTile);
     if (max_tiles == 0) return hipSuccess;
     gemm::MxArgs a{h, h_scale, w2, w2_scale, offsets, c.E, c.F, (int)rows_cap(c), c.H, c.H, nullptr, nullptr,
-                   yp, nullptr, (int*)ws, nullptr, nullptr, 1, row_w};
+                   yp, nullptr, (int*)ws, nullptr, nullptr, 1, row_w, INFINITY};
     zero_mx_sched_kernel<<<1, 64, 0, s>>>(a.sched);
     // scale words loaded four stages at a time when each row's scales are a
     // whole number of 16-byte pieces (K a multiple of 512)
     if (a.K % 512 == 0)
-        mx_launch(gemm::grouped_gemm_mxfp8<false, 4, true>, gemm::grouped_gemm_mxfp8<false, 4, false>, a, max_tiles, s);
+        mx_launch<false, 4>(a, max_tiles, s);
     else
-        mx_launch(gemm::grouped_gemm_mxfp8<false, 1, true>, gemm::grouped_gemm_mxfp8<false, 1, false>, a, max_tiles, s);
+        mx_launch<false, 1>(a, max_tiles, s);
     return hipGetLastError();
 }
 

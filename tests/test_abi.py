@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def _cfg(**kw):
-    base = dict(T=64, H=128, F=64, E=8, k=2, align=1, score=0, renorm=0, dtype=1, weight_site=0)
+    base = dict(T=64, H=128, F=64, E=8, k=2, align=1, score=0, renorm=0, dtype=1, weight_site=0, swiglu_limit=0.0)
     base.update(kw)
     return b.moe_config(*[base[n] for n, _ in b.moe_config._fields_])
 
@@ -45,6 +45,9 @@ def _cfg(**kw):
     (dict(score=5), b.MOE_ERR_INVALID_ARG),
     (dict(dtype=7), b.MOE_ERR_INVALID_ARG),
     (dict(weight_site=3), b.MOE_ERR_INVALID_ARG),
+    (dict(swiglu_limit=-1.0), b.MOE_ERR_INVALID_ARG),
+    (dict(swiglu_limit=float("nan")), b.MOE_ERR_INVALID_ARG),
+    (dict(swiglu_limit=float("inf")), b.MOE_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected_on_host(kw, status):
     lib = moe.load_library()

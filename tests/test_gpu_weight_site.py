@@ -29,7 +29,7 @@ def _host(t):
     return None if t is None else to_host(t)
 
 
-def _check(s, site, args, buf, toks=None):
+def _check(s, site, args, buf, toks=None, limit=0.0):
     logits, x, w1, w2, scales = args
     idx, w = orc.route(to_host(logits), s.k, s.score, s.renorm)
     counts, offsets, row_map, src_map, _ = orc.group(idx, s.E, s.align)
@@ -47,7 +47,7 @@ def _check(s, site, args, buf, toks=None):
                     if e >= 0:
                         hw[k][e] = to_host(t[int(e)])
     ref = orc.forward_tokens(s, toks, _host(x), hw["w1"], hw["w2"], idx, w, _host(scales.get("x_scale")),
-                             hw.get("w1_scale"), hw.get("w2_scale"), site=site)
+                             hw.get("w1_scale"), hw.get("w2_scale"), site=site, limit=limit)
     f = s.dtype
     rows = row_map[toks].ravel()
     ok = rows >= 0
@@ -60,7 +60,15 @@ def _check(s, site, args, buf, toks=None):
         hr = decode(f, h_ref, ref["h_scale"].reshape(-1, s.F // 32)[ok])
     else:
         hd, hr = decode(f, h), decode(f, h_ref)
-    assert rel_err(hd, hr) < TOL[f], "h"
+    if f == "mxfp8" and limit > 0:
+        # The clamp piles values onto silu(L) L, the tensor's maximum.  Where
+        # the two sides' float values straddle an E4M3 rounding boundary, a
+        # code moves by one step (at most 2^-3 of the element, 3 mantissa
+        # bits), undiluted at the maximum.  The bar: one step, in few places.
+        assert rel_err(hd, hr) <= 2.0 ** -3 + 1e-3, "h"
+        assert np.mean(hd != hr) < 0.02, "h codes"
+    else:
+        assert rel_err(hd, hr) < TOL[f], "h"
     yp = decode(s.out_dtype, to_host(buf["yp"][ridx]))
     assert rel_err(yp, decode(s.out_dtype, ref["yp"].reshape(-1, s.H)[ok])) < TOL[f], "yp"
     y = decode(s.out_dtype, to_host(buf["y"])[toks])
