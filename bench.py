@@ -37,6 +37,8 @@ def parse():
     # measured the fine-grained step ~7 % slower
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="mixtral_bf16")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the variant timings (gather form, weight placements, clamp): counter passes")
     p.add_argument("--cpu-sample", type=int, default=256, help="tokens of the oracle CPU baseline (0 = skip)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="HBM bytes per dispatch measured with rocprofv3 counters (optional)")
@@ -263,7 +265,7 @@ def main():
         names.append("route_bwd")
 
     variants = None
-    if not s.backward:
+    if not s.backward and not args.no_variants:
         # The gather form of the forward (no materialised Xp: the gate/up GEMM
         # reads x[src_map[r] / k] itself), timed as whole steps and as the
         # gather GEMM alone; reported beside the step, which stays the
