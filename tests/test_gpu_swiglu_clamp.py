@@ -92,3 +92,39 @@ def test_clamp_backward_small(name):
     sv = decode("bf16", st)
     assert np.all(dgu[:, : s.F][sv[:, : s.F] > LIMIT] == 0)
     assert np.all(dgu[:, s.F:][np.abs(sv[:, s.F:]) > LIMIT] == 0)
+
+
+@pytest.mark.parametrize("name", ["small_bf16_sigmoid_align", "small_mxfp8_skew_align"])
+def test_variant_forward_graph_capture_replays(name):
+    """The gather form with the weight in the FC2 epilogue and the clamp
+    (per-row weights written by a kernel into the workspace) captures into a
+    HIP graph; replays, with eager work between them, give the eager bytes."""
+    s = next(x for x in wl.small_shapes() if x.name == name)
+    logits, x, w1, w2, sc = _inputs(s)
+    cfg = dataclasses.replace(cfg_of(s), swiglu_limit=LIMIT, weight_site="fc2")
+    buf = moe.alloc_forward(cfg)
+    buf["xp"] = None
+    buf["xp_scale"] = None
+    moe.moe_forward(cfg, logits, x, w1, w2, buf, **sc)
+    torch.cuda.synchronize()
+    keys = [k for k, v in buf.items() if v is not None and k not in ("ws", "err")]
+    eager = {k: to_host(buf[k]).copy() for k in keys}
+    n = int(eager["offsets"][-1])
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            moe.moe_forward(cfg, logits, x, w1, w2, buf, **sc)
+    for rep in range(3):
+        buf["y"].fill_(float("nan"))
+        buf["yp"].fill_(float("nan"))
+        buf["h"].fill_(0x5A if buf["h"].dtype == torch.uint8 else float("nan"))
+        buf["ws"].fill_(0x77)  # the per-row weights must be rewritten on every replay
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (logits * 2).sum().item()  # unrelated eager work between replays
+        for k in keys:
+            got, v = to_host(buf[k]), eager[k]
+            if k in ("h", "h_scale", "yp", "src_map"):
+                got, v = got[:n], v[:n]
+            assert np.array_equal(got.view(np.uint8), v.view(np.uint8)), f"replay {rep}: {k} differs"
