@@ -106,7 +106,7 @@ float* row_w_ws(const moe_config& c, void* ws) {
 moe_status swiglu_checked(const moe_config* cfg, const void* a, const uint8_t* a_scale, const void* w1,
                           const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale, void* stash,
                           const int32_t* gsrc, const int32_t* gcounts, const float* row_w, void* ws, size_t ws_bytes,
-                          void* stream, const char* what) {
+                          void* stream, const char* what, bool launch = true) {
     moe_status st = check_config(cfg);
     if (st) return st;
     const moe_config& c = *cfg;
@@ -120,6 +120,12 @@ moe_status swiglu_checked(const moe_config* cfg, const void* a, const uint8_t* a
     REQUIRE(offsets);
     REQUIRE(h);
     if ((st = check_ws(c, ws, ws_bytes))) return st;
+    if (c.dtype == MOE_MXFP8) {
+        if (!a_scale) return fail(MOE_ERR_INVALID_ARG, "%s: the grouped operand's MXFP8 scales are NULL", what);
+        REQUIRE(w1_scale);
+        REQUIRE(h_scale);
+    }
+    if (!launch) return MOE_OK;  // arguments checked, nothing enqueued
     hipStream_t s = as_stream(stream);
     switch (c.dtype) {
     case MOE_BF16:
@@ -144,7 +150,7 @@ moe_status swiglu_checked(const moe_config* cfg, const void* a, const uint8_t* a
 // The down GEMM; row_w non-null = Yp scaled by the row's routing weight.
 moe_status down_checked(const moe_config* cfg, const void* h, const uint8_t* h_scale, const void* w2,
                         const uint8_t* w2_scale, const int32_t* offsets, void* yp, const float* row_w, void* ws,
-                        size_t ws_bytes, void* stream, const char* what) {
+                        size_t ws_bytes, void* stream, const char* what, bool launch = true) {
     moe_status st = check_config(cfg);
     if (st) return st;
     const moe_config& c = *cfg;
@@ -155,6 +161,11 @@ moe_status down_checked(const moe_config* cfg, const void* h, const uint8_t* h_s
     REQUIRE(offsets);
     REQUIRE(yp);
     if ((st = check_ws(c, ws, ws_bytes))) return st;
+    if (c.dtype == MOE_MXFP8) {
+        REQUIRE(h_scale);
+        REQUIRE(w2_scale);
+    }
+    if (!launch) return MOE_OK;  // arguments checked, nothing enqueued
     hipStream_t s = as_stream(stream);
     switch (c.dtype) {
     case MOE_BF16:
@@ -273,9 +284,12 @@ moe_status moe_grouped_swiglu_gemm_weighted(const moe_config* cfg, const void* x
                                             const void* w1, const uint8_t* w1_scale, const int32_t* offsets,
                                             const int32_t* src_map, const float* w, void* h, uint8_t* h_scale,
                                             void* ws, size_t ws_bytes, void* stream) {
-    const float* row_w = nullptr;
-    moe_status st = row_weights_checked(cfg, src_map, w, ws, ws_bytes, stream, &row_w);
+    // every argument is checked before the per-row weights are launched
+    moe_status st = swiglu_checked(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, nullptr, nullptr, nullptr,
+                                   nullptr, ws, ws_bytes, stream, "moe_grouped_swiglu_gemm_weighted", false);
     if (st) return st;
+    const float* row_w = nullptr;
+    if ((st = row_weights_checked(cfg, src_map, w, ws, ws_bytes, stream, &row_w))) return st;
     return swiglu_checked(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, nullptr, nullptr, nullptr, row_w, ws,
                           ws_bytes, stream, "moe_grouped_swiglu_gemm_weighted");
 }
@@ -291,9 +305,12 @@ moe_status moe_grouped_down_gemm_weighted(const moe_config* cfg, const void* h, 
                                           const void* w2, const uint8_t* w2_scale, const int32_t* offsets,
                                           const int32_t* src_map, const float* w, void* yp, void* ws,
                                           size_t ws_bytes, void* stream) {
-    const float* row_w = nullptr;
-    moe_status st = row_weights_checked(cfg, src_map, w, ws, ws_bytes, stream, &row_w);
+    // every argument is checked before the per-row weights are launched
+    moe_status st = down_checked(cfg, h, h_scale, w2, w2_scale, offsets, yp, nullptr, ws, ws_bytes, stream,
+                                 "moe_grouped_down_gemm_weighted", false);
     if (st) return st;
+    const float* row_w = nullptr;
+    if ((st = row_weights_checked(cfg, src_map, w, ws, ws_bytes, stream, &row_w))) return st;
     return down_checked(cfg, h, h_scale, w2, w2_scale, offsets, yp, row_w, ws, ws_bytes, stream,
                         "moe_grouped_down_gemm_weighted");
 }

@@ -172,3 +172,31 @@ def test_weighted_gemms_and_placement_checked_on_host():
     assert lib.moe_route_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
     # an unweighted combine takes w = NULL (T = 0: nothing to launch)
     assert lib.moe_combine(ctypes.byref(_cfg(T=0)), None, None, None, None, None) == b.MOE_OK
+
+
+def test_new_entry_points_host_edge_cases():
+    lib = moe.load_library()
+    c0 = _cfg(T=0)  # no rows: every GEMM entry point is a no-op, nothing is dereferenced
+    n0 = lib.moe_workspace_size(ctypes.byref(c0))
+    assert lib.moe_grouped_swiglu_gemm_weighted(ctypes.byref(c0), None, None, None, None, None, None, None, None,
+                                                None, None, 0, None) == b.MOE_OK
+    assert lib.moe_grouped_down_gemm_weighted(ctypes.byref(c0), None, None, None, None, None, None, None, None,
+                                              None, 0, None) == b.MOE_OK
+    assert lib.moe_grouped_swiglu_gemm_gather(ctypes.byref(c0), None, None, None, None, None, None, None, None,
+                                              None, None, n0, None) == b.MOE_OK
+    c = _cfg(weight_site=b.MOE_WEIGHT_AT_FC1)
+    need = lib.moe_workspace_size(ctypes.byref(c))
+    # a missing output is rejected before anything is launched
+    st = lib.moe_grouped_swiglu_gemm_weighted(ctypes.byref(c), 1, None, 1, None, 1, 1, 1, None, None, 1, need, None)
+    assert st == b.MOE_ERR_INVALID_ARG and b"h" in lib.moe_last_error()
+    st = lib.moe_grouped_down_gemm_weighted(ctypes.byref(c), 1, None, 1, None, 1, 1, 1, None, 1, need, None)
+    assert st == b.MOE_ERR_INVALID_ARG and b"yp" in lib.moe_last_error()
+    # too small a workspace (the per-row weights live there)
+    st = lib.moe_grouped_down_gemm_weighted(ctypes.byref(c), 1, None, 1, None, 1, 1, 1, 1, 1, need - 256, None)
+    assert st == b.MOE_ERR_WORKSPACE
+    # the gather form needs the routing maps
+    st = lib.moe_grouped_swiglu_gemm_gather(ctypes.byref(c), 1, None, None, 1, 1, None, 1, 1, None, 1, need, None)
+    assert st == b.MOE_ERR_INVALID_ARG and b"src_map" in lib.moe_last_error()
+    # a clamp limit is accepted by every call that takes the config
+    cl = _cfg(swiglu_limit=7.0)
+    assert lib.moe_workspace_size(ctypes.byref(cl)) == lib.moe_workspace_size(ctypes.byref(_cfg()))
