@@ -40,12 +40,15 @@
  *   calls are safe under HIP graph capture.  Data-dependent sizes (per-expert
  *   counts and offsets) live in device buffers; grids are sized from host-known
  *   bounds (T, k, E, align).
- * - Errors.  A call returns MOE_OK or an error status without launching
- *   anything; moe_last_error() then holds a message (per thread).  Host-side
- *   checks: null required pointers, sizes, dtype combinations, workspace size.
- *   MOE_ERR_HIP reports a failed kernel launch.  Expert ids outside [-1, E) in
- *   a routing table can only be seen on the device: such routes are dropped
- *   and counted in the optional device counter `err`.
+ * - Errors.  A call returns MOE_OK or an error status; moe_last_error() then
+ *   holds a message (per thread).  Every host-side check (null required
+ *   pointers, sizes, dtype combinations, workspace size) runs before the
+ *   first launch, the fused calls included, so MOE_ERR_INVALID_ARG,
+ *   MOE_ERR_UNSUPPORTED and MOE_ERR_WORKSPACE mean nothing was enqueued.
+ *   MOE_ERR_HIP reports a failed kernel launch (the kernels of the same call
+ *   enqueued before it stay enqueued).  Expert ids outside [-1, E) in a
+ *   routing table can only be seen on the device: such routes are dropped and
+ *   counted in the optional device counter `err`.
  * - Layouts (row-major, innermost last).  x [T,H]; logits [T,E] float32;
  *   idx [T,k] int32; w [T,k] float32.  Expert weights are stored with the
  *   contraction dimension contiguous: w1 [E][2F][H] holds the logical fc1
@@ -257,8 +260,10 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
                        void* gu_stash, int32_t* err, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------- */
-/* Backward of the expert FFN and the combine.  Built for BF16 storage;    */
-/* F32 and MXFP8 configs return MOE_ERR_UNSUPPORTED.                       */
+/* Backward of the expert FFN and the combine.  Built for BF16 storage    */
+/* with the routing weights applied in the combine: every call below except */
+/* moe_route_bwd (which also takes F32 and MXFP8 layers) returns           */
+/* MOE_ERR_UNSUPPORTED for F32 or MXFP8 configs or an epilogue weight site. */
 /* [TE-EP]: weight gradients of experts with no rows are zero; d_x keeps x's */
 /* dtype.  [CUDNN]: the backward re-dispatches the output gradient along the */
 /* forward routes and recomputes SwiGLU from the saved stash.  The routing   */

@@ -819,6 +819,69 @@ int or_backward_dw_entries(int H, int F, int k, int fmt, int g_fmt, int h_fmt, i
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Bulk forms of the per-element steps, for the expert-major front end of   */
+/* oracle.py (whose sums over H and F are float64 matrix products).  Each   */
+/* applies the single definition above to every element or row.            */
+/* ------------------------------------------------------------------------ */
+/* h[r][f] = or_swiglu(gu[r][f], gu[r][F + f]) * (rw ? rw[r] : 1), the FC1
+ * placement of the routing weight included (see or_expert_row). */
+void or_swiglu_rows(const double* gu, int64_t rows, int F, const double* rw, double* h) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int f = 0; f < F; ++f) {
+            double v = or_swiglu(gu[r * 2 * F + f], gu[r * 2 * F + F + f]);
+            h[r * F + f] = rw ? v * rw[r] : v;
+        }
+}
+
+/* dgu[r] = dh[r] * dh/dg | dh[r] * dh/du at the stored (g, u) of row r. */
+void or_swiglu_grad_rows(const double* gu, const double* dh, int64_t rows, int F, double* dgu) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int f = 0; f < F; ++f) {
+            double dg, du;
+            or_swiglu_grad(gu[r * 2 * F + f], gu[r * 2 * F + F + f], &dg, &du);
+            dgu[r * 2 * F + f] = dh[r * F + f] * dg;
+            dgu[r * 2 * F + F + f] = dh[r * F + f] * du;
+        }
+}
+
+/* Rows of n doubles stored in a format (or_store_row per row). */
+void or_store_rows(int fmt, const double* v, int64_t rows, int64_t n, void* out, uint8_t* scale_out) {
+    const size_t rb = (size_t)n * or_elem_bytes(fmt);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        or_store_row(fmt, v + r * n, n, (uint8_t*)out + r * rb,
+                     fmt == OR_MXFP8 ? scale_out + r * (n / OR_MX_BLOCK) : NULL);
+}
+
+/* Rows of n stored values decoded to double: or_load per element, with the
+ * E4M3 decoder tabulated over its 256 codes first for MXFP8. */
+void or_decode_rows(int fmt, const void* in, const uint8_t* scale_in, int64_t rows, int64_t n, double* out) {
+    const size_t rb = (size_t)n * or_elem_bytes(fmt);
+    if (fmt == OR_MXFP8) {
+        double tab[256];
+        for (int c = 0; c < 256; ++c) tab[c] = or_double_from_e4m3((uint8_t)c);
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < rows; ++r) {
+            const uint8_t* row = (const uint8_t*)in + r * rb;
+            const uint8_t* srow = scale_in + r * (n / OR_MX_BLOCK);
+            for (int64_t b = 0; b < n / OR_MX_BLOCK; ++b) {
+                const double sc = or_double_from_e8m0(srow[b]);
+                for (int i = 0; i < OR_MX_BLOCK; ++i)
+                    out[r * n + b * OR_MX_BLOCK + i] = tab[row[b * OR_MX_BLOCK + i]] * sc;
+            }
+        }
+        return;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const void* row = (const uint8_t*)in + r * rb;
+        for (int64_t i = 0; i < n; ++i) out[r * n + i] = or_load(fmt, row, NULL, i);
+    }
+}
+
 int or_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -67,6 +67,10 @@ def _load():
         "or_backward_dw_entries": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, I32, P, P,
                                          P, I32, P, P, P]),
         "or_num_threads": (I32, []),
+        "or_swiglu_rows": (None, [P, I64, I32, P, P]),
+        "or_swiglu_grad_rows": (None, [P, P, I64, I32, P]),
+        "or_store_rows": (None, [I32, P, I64, I64, P, P]),
+        "or_decode_rows": (None, [I32, P, P, I64, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -137,9 +141,17 @@ def mx_quantize(v) -> tuple:
 
 
 def mx_dequantize(codes, scales) -> np.ndarray:
-    d = f64_from_e4m3(codes)
-    s = f64_from_e8m0(scales)
-    return d * np.repeat(s, 32, axis=-1)
+    """E4M3 codes [..., n] with E8M0 scales [..., n/32] -> float64 values."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    n = codes.shape[-1]
+    rows = codes.size // n if n else 0
+    if scales.shape != codes.shape[:-1] + (n // 32,):
+        raise ValueError("scales must hold one code per 32 elements of the last axis")
+    out = np.empty(codes.shape, np.float64)
+    if codes.size:
+        _load().or_decode_rows(FMT["mxfp8"], codes.ctypes.data, scales.ctypes.data, rows, n, out.ctypes.data)
+    return out
 
 
 def decode(fmt: str, data, scale=None) -> np.ndarray:
@@ -386,3 +398,134 @@ def backward_dw_entries(shape, e, x, w1, w2, w, src_map, offsets, dy, dw2_idx, d
     if rc:
         raise ValueError("unsupported")
     return out2, out1
+
+
+# ------------------------------------------------ expert-major float64 front end
+# The same definitions as forward_tokens / backward (moe_oracle.c), evaluated
+# expert by expert so that the sums over H and F are float64 matrix products
+# (numpy's BLAS, a library primitive) instead of ascending loops: fast enough
+# to compare full-size layers in full or on thousands of tokens.  The
+# per-element steps (SwiGLU and its gradient, the clamp, storage rounding and
+# MX quantisation) are the C oracle's own functions.  Only the order of the
+# float64 additions differs from the loop form; the tests pin this front end
+# to it bit for bit on small shapes.
+def _store_rows(fmt: str, v: np.ndarray):
+    """float64 [rows, n] -> stored rows (MXFP8: (codes, scales))."""
+    v = np.ascontiguousarray(v, np.float64)
+    rows, n = v.shape
+    out = np.empty((rows, n), _NP[fmt])
+    sc = np.empty((rows, n // 32), np.uint8) if fmt == "mxfp8" else None
+    _load().or_store_rows(FMT[fmt], v.ctypes.data, rows, n, out.ctypes.data, _p(sc))
+    return (out, sc) if fmt == "mxfp8" else out
+
+
+def _swiglu_rows(gu: np.ndarray, F: int, rw=None) -> np.ndarray:
+    gu = np.ascontiguousarray(gu, np.float64)
+    h = np.empty((gu.shape[0], F))
+    rw = None if rw is None else np.ascontiguousarray(rw, np.float64)
+    _load().or_swiglu_rows(gu.ctypes.data, gu.shape[0], F, _p(rw), h.ctypes.data)
+    return h
+
+
+def _swiglu_grad_rows(gu: np.ndarray, dh: np.ndarray, F: int) -> np.ndarray:
+    gu = np.ascontiguousarray(gu, np.float64)
+    dh = np.ascontiguousarray(dh, np.float64)
+    d = np.empty((gu.shape[0], 2 * F))
+    _load().or_swiglu_grad_rows(gu.ctypes.data, dh.ctypes.data, gu.shape[0], F, d.ctypes.data)
+    return d
+
+
+def _weights_f64(fmt: str, wt, wscale, e: int) -> np.ndarray:
+    return decode(fmt, wt[e], None if wscale is None else wscale[e])
+
+
+def forward_experts(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=None, w2_scale=None,
+                    want_stash: bool = False, site: str = "combine", limit: float = 0.0):
+    """forward_tokens evaluated expert by expert (same arguments and outputs).
+
+    For each expert e, the routes (i, j) of the listed tokens with idx = e form
+    X_e (their x rows, decoded); GU = X_e W1s[e]^T, h = store_h(SwiGLU(GU)),
+    Yp = store_out(h W2s[e]^T), all sums in float64; then the combine
+    y[i] = store_out(sum_{j ascending} c(t, j) Yp(i, j)) as in forward_tokens."""
+    s = shape
+    fmt = s.dtype
+    y_fmt = s_fmt = "f32" if fmt == "f32" else "bf16"
+    h_fmt = fmt
+    tokens = np.asarray(tokens, np.int64)
+    n, k = tokens.size, s.k
+    idx = np.asarray(idx, np.int32)
+    w = np.asarray(w, np.float32)
+    sel = idx[tokens]                                   # [n, k]
+    h = np.zeros((n, k, s.F), _NP[h_fmt])
+    h_sc = np.zeros((n, k, s.F // 32), np.uint8) if h_fmt == "mxfp8" else None
+    yp = np.zeros((n, k, s.H), _NP[y_fmt])
+    stash = np.zeros((n, k, 2 * s.F), _NP[s_fmt]) if want_stash else None
+    _load().or_set_swiglu_limit(float(limit))
+    for e in np.unique(sel[sel >= 0]):
+        ii, jj = np.nonzero(sel == e)
+        t = tokens[ii]
+        xe = decode(fmt, np.asarray(x)[t], None if x_scale is None else np.asarray(x_scale)[t])
+        gu = xe @ _weights_f64(fmt, w1, w1_scale, e).T
+        rw = w[t, jj].astype(np.float64)
+        hv = _swiglu_rows(gu, s.F, rw if site == "fc1" else None)
+        if want_stash:
+            stash[ii, jj] = _store_rows(s_fmt, gu)
+        hs = _store_rows(h_fmt, hv)
+        if h_fmt == "mxfp8":
+            h[ii, jj], h_sc[ii, jj] = hs
+            hq = decode("mxfp8", hs[0], hs[1])
+        else:
+            h[ii, jj] = hs
+            hq = decode(h_fmt, hs)
+        ye = hq @ _weights_f64(fmt, w2, w2_scale, e).T
+        if site == "fc2":
+            ye *= rw[:, None]
+        yp[ii, jj] = _store_rows(y_fmt, ye)
+    acc = np.zeros((n, s.H))
+    for j in range(k):
+        live = sel[:, j] >= 0
+        c = np.ones(n) if site != "combine" else w[tokens, j].astype(np.float64)
+        acc[live] += c[live, None] * decode(y_fmt, yp[live, j])
+    out = {"h": h, "yp": yp, "y": _store_rows(y_fmt, acc)}
+    if h_sc is not None:
+        out["h_scale"] = h_sc
+    if want_stash:
+        out["stash"] = stash
+    return out
+
+
+def backward_expert(shape, e: int, x, w1, w2, w, src_map, offsets, dy, limit: float = 0.0):
+    """Backward of one expert's rows, as or_backward defines it, with the
+    forward's stored h and stash recomputed from x (forward_experts' steps):
+    dYp = store_g(w dY[t]), dH = dYp W2s[e], dGU = store_g(dSwiGLU(stash, dH)),
+    dW2s[e] = dYp^T h, dXp = store_g(dGU W1s[e]), dW1s[e] = dGU^T Xp; weight
+    gradients float32 (exactly 0 for an expert with no rows).  Sums in float64.
+    Returns dict with dw1 [2F, H] f32, dw2 [H, F] f32 and, for the expert's
+    real rows (in row order, `rows`), dyp, dgu, dxp in storage form."""
+    s = shape
+    fmt = s.dtype
+    g_fmt = "f32" if fmt == "f32" else "bf16"
+    rows = np.arange(int(offsets[e]), int(offsets[e + 1]))
+    src = np.asarray(src_map)[rows]
+    rows = rows[src >= 0]
+    src = src[src >= 0].astype(np.int64)
+    t = src // s.k
+    if rows.size == 0:
+        return {"dw1": np.zeros((2 * s.F, s.H), np.float32), "dw2": np.zeros((s.H, s.F), np.float32),
+                "rows": rows}
+    _load().or_set_swiglu_limit(float(limit))
+    xe = decode(fmt, np.asarray(x)[t])
+    w1e = decode(fmt, np.asarray(w1)[e])
+    w2e = decode(fmt, np.asarray(w2)[e])
+    gu = xe @ w1e.T
+    st = decode(g_fmt, _store_rows(g_fmt, gu))                       # the stash as stored
+    hq = decode(fmt, _store_rows(fmt, _swiglu_rows(gu, s.F)))         # h as stored
+    wr = np.asarray(w, np.float32).ravel()[src].astype(np.float64)
+    dyp = _store_rows(g_fmt, wr[:, None] * decode(g_fmt, np.asarray(dy)[t]))
+    dypd = decode(g_fmt, dyp)
+    dh = dypd @ w2e
+    dgu = _store_rows(g_fmt, _swiglu_grad_rows(st, dh, s.F))
+    dgud = decode(g_fmt, dgu)
+    dxp = _store_rows(g_fmt, dgud @ w1e)
+    return {"dw2": (dypd.T @ hq).astype(np.float32), "dw1": (dgud.T @ xe).astype(np.float32),
+            "rows": rows, "dyp": dyp, "dgu": dgu, "dxp": dxp}

@@ -187,7 +187,7 @@ moe_status down_checked(const moe_config* cfg, const void* h, const uint8_t* h_s
 // Writes the per-row routing weights into the workspace; *row_w = their
 // address (left null when there are no rows).
 moe_status row_weights_checked(const moe_config* cfg, const int32_t* src_map, const float* w, void* ws,
-                               size_t ws_bytes, void* stream, const float** row_w) {
+                               size_t ws_bytes, void* stream, const float** row_w, bool launch = true) {
     moe_status st = check_config(cfg);
     if (st) return st;
     const moe_config& c = *cfg;
@@ -195,10 +195,148 @@ moe_status row_weights_checked(const moe_config* cfg, const int32_t* src_map, co
     REQUIRE(src_map);
     REQUIRE(w);
     if ((st = check_ws(c, ws, ws_bytes))) return st;
+    if (!launch) return MOE_OK;
     float* rw = row_w_ws(c, ws);
     if ((st = hip_status(launch_row_weights(c, src_map, w, rw, as_stream(stream)), "row weights"))) return st;
     *row_w = rw;
     return MOE_OK;
+}
+
+moe_status route_checked(const moe_config* cfg, const float* logits, int32_t* idx, float* w, void* stream,
+                         bool launch) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    if (cfg->T > 0) {
+        REQUIRE(logits);
+        REQUIRE(idx);
+        REQUIRE(w);
+    }
+    if (!launch) return MOE_OK;
+    return hip_status(launch_route(*cfg, logits, idx, w, as_stream(stream)), "moe_route");
+}
+
+moe_status permute_checked(const moe_config* cfg, const void* x, const uint8_t* x_scale, const int32_t* idx,
+                           void* xp, uint8_t* xp_scale, int32_t* counts, int32_t* offsets, int32_t* row_map,
+                           int32_t* src_map, int32_t* err, void* ws, size_t ws_bytes, void* stream, bool launch) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    const moe_config& c = *cfg;
+    if (c.dtype == MOE_MXFP8 && c.H % kMxBlock) return fail(MOE_ERR_UNSUPPORTED, "MXFP8 needs H % 32 == 0");
+    REQUIRE(counts);
+    REQUIRE(offsets);
+    if (rows_capacity(c) > 0) REQUIRE(src_map);
+    if (c.T > 0) {
+        REQUIRE(idx);
+        REQUIRE(row_map);
+        if (xp) {  // xp NULL: the grouping only (for the gather form of the gate/up GEMM)
+            REQUIRE(x);
+            if (c.dtype == MOE_MXFP8) {
+                REQUIRE(x_scale);
+                REQUIRE(xp_scale);
+            }
+        }
+    }
+    if ((st = check_ws(c, ws, ws_bytes))) return st;
+    if (!launch) return MOE_OK;
+    hipStream_t s = as_stream(stream);
+    if ((st = hip_status(launch_group(c, idx, counts, offsets, row_map, src_map, err, (int32_t*)ws, s), "moe_permute")))
+        return st;
+    if (!xp) return MOE_OK;
+    return hip_status(launch_permute_rows(c, x, x_scale, row_map, counts, offsets, xp, xp_scale, s), "moe_permute");
+}
+
+moe_status combine_checked(const moe_config* cfg, const void* yp, const int32_t* row_map, const float* w, void* y,
+                           void* stream, bool launch) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    if ((st = check_shapes(*cfg))) return st;
+    if (cfg->T > 0) {
+        REQUIRE(yp);
+        REQUIRE(row_map);
+        REQUIRE(y);
+    }
+    if (!launch) return MOE_OK;
+    return hip_status(launch_combine(*cfg, yp, row_map, w, y, as_stream(stream)), "moe_combine");
+}
+
+// The backward is built for bf16 storage with the routing weights applied in
+// the combine.
+moe_status check_backward(const moe_config* cfg) {
+    moe_status st = check_config(cfg);
+    if (st) return st;
+    if (cfg->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward is built for BF16 storage");
+    if (cfg->weight_site != MOE_WEIGHT_AT_COMBINE)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward is built for the weights applied in the combine");
+    return check_shapes(*cfg);
+}
+
+moe_status combine_bwd_checked(const moe_config* cfg, const void* dy, const int32_t* row_map, const int32_t* src_map,
+                               const int32_t* offsets, const float* w, void* dyp, void* stream, bool launch) {
+    moe_status st = check_backward(cfg);
+    if (st) return st;
+    REQUIRE(offsets);
+    if (rows_capacity(*cfg) > 0) {
+        REQUIRE(dy);
+        REQUIRE(row_map);
+        REQUIRE(src_map);
+        REQUIRE(w);
+        REQUIRE(dyp);
+    }
+    if (!launch) return MOE_OK;
+    return hip_status(launch_combine_bwd(*cfg, dy, row_map, src_map, offsets, w, dyp, as_stream(stream)),
+                      "moe_combine_bwd");
+}
+
+moe_status down_bwd_checked(const moe_config* cfg, const void* dyp, const void* w2, const void* h,
+                            const void* gu_stash, const int32_t* offsets, void* dgu, float* dw2, void* ws,
+                            size_t ws_bytes, void* stream, bool launch) {
+    moe_status st = check_backward(cfg);
+    if (st) return st;
+    REQUIRE(w2);
+    REQUIRE(dw2);
+    REQUIRE(offsets);
+    if ((st = check_ws(*cfg, ws, ws_bytes, true))) return st;
+    if (rows_capacity(*cfg) > 0) {
+        REQUIRE(dyp);
+        REQUIRE(h);
+        REQUIRE(gu_stash);
+        REQUIRE(dgu);
+    }
+    if (!launch) return MOE_OK;
+    return hip_status(launch_down_bwd(*cfg, dyp, w2, h, gu_stash, offsets, dgu, dw2, ws, as_stream(stream)),
+                      "moe_grouped_down_bwd");
+}
+
+moe_status swiglu_bwd_checked(const moe_config* cfg, const void* dgu, const void* w1, const void* xp,
+                              const int32_t* offsets, void* dxp, float* dw1, void* ws, size_t ws_bytes, void* stream,
+                              bool launch) {
+    moe_status st = check_backward(cfg);
+    if (st) return st;
+    REQUIRE(w1);
+    REQUIRE(dw1);
+    REQUIRE(offsets);
+    if ((st = check_ws(*cfg, ws, ws_bytes, true))) return st;
+    if (rows_capacity(*cfg) > 0) {
+        REQUIRE(dgu);
+        REQUIRE(xp);
+        REQUIRE(dxp);
+    }
+    if (!launch) return MOE_OK;
+    return hip_status(launch_swiglu_bwd(*cfg, dgu, w1, xp, offsets, dxp, dw1, ws, as_stream(stream)),
+                      "moe_grouped_swiglu_bwd");
+}
+
+moe_status permute_bwd_checked(const moe_config* cfg, const void* dxp, const int32_t* row_map, void* dx,
+                               void* stream, bool launch) {
+    moe_status st = check_backward(cfg);
+    if (st) return st;
+    if (cfg->T > 0) {
+        REQUIRE(dxp);
+        REQUIRE(row_map);
+        REQUIRE(dx);
+    }
+    if (!launch) return MOE_OK;
+    return hip_status(launch_permute_bwd(*cfg, dxp, row_map, dx, as_stream(stream)), "moe_permute_bwd");
 }
 
 }  // namespace
@@ -222,43 +360,18 @@ size_t moe_backward_workspace_size(const moe_config* cfg) {
 }
 
 moe_status moe_route(const moe_config* cfg, const float* logits, int32_t* idx, float* w, void* stream) {
-    moe_status st = check_config(cfg);
-    if (st) return st;
-    if (cfg->T > 0) {
-        REQUIRE(logits);
-        REQUIRE(idx);
-        REQUIRE(w);
-    }
-    return hip_status(launch_route(*cfg, logits, idx, w, as_stream(stream)), "moe_route");
+    return route_checked(cfg, logits, idx, w, stream, true);
 }
 
 moe_status moe_permute(const moe_config* cfg, const void* x, const uint8_t* x_scale, const int32_t* idx, void* xp,
                        uint8_t* xp_scale, int32_t* counts, int32_t* offsets, int32_t* row_map, int32_t* src_map,
                        int32_t* err, void* ws, size_t ws_bytes, void* stream) {
-    moe_status st = check_config(cfg);
+    // checked in full before the grouping is launched
+    moe_status st = permute_checked(cfg, x, x_scale, idx, xp, xp_scale, counts, offsets, row_map, src_map, err, ws,
+                                    ws_bytes, stream, false);
     if (st) return st;
-    const moe_config& c = *cfg;
-    if (c.dtype == MOE_MXFP8 && c.H % kMxBlock) return fail(MOE_ERR_UNSUPPORTED, "MXFP8 needs H % 32 == 0");
-    REQUIRE(counts);
-    REQUIRE(offsets);
-    if (rows_capacity(c) > 0) REQUIRE(src_map);
-    if (c.T > 0) {
-        REQUIRE(idx);
-        REQUIRE(row_map);
-        if (xp) {  // xp NULL: the grouping only (for the gather form of the gate/up GEMM)
-            REQUIRE(x);
-            if (c.dtype == MOE_MXFP8) {
-                REQUIRE(x_scale);
-                REQUIRE(xp_scale);
-            }
-        }
-    }
-    if ((st = check_ws(c, ws, ws_bytes))) return st;
-    hipStream_t s = as_stream(stream);
-    if ((st = hip_status(launch_group(c, idx, counts, offsets, row_map, src_map, err, (int32_t*)ws, s), "moe_permute")))
-        return st;
-    if (!xp) return MOE_OK;
-    return hip_status(launch_permute_rows(c, x, x_scale, row_map, counts, offsets, xp, xp_scale, s), "moe_permute");
+    return permute_checked(cfg, x, x_scale, idx, xp, xp_scale, counts, offsets, row_map, src_map, err, ws, ws_bytes,
+                           stream, true);
 }
 
 moe_status moe_grouped_swiglu_gemm(const moe_config* cfg, const void* xp, const uint8_t* xp_scale, const void* w1,
@@ -317,17 +430,11 @@ moe_status moe_grouped_down_gemm_weighted(const moe_config* cfg, const void* h, 
 
 moe_status moe_combine(const moe_config* cfg, const void* yp, const int32_t* row_map, const float* w, void* y,
                        void* stream) {
-    moe_status st = check_config(cfg);
-    if (st) return st;
-    if ((st = check_shapes(*cfg))) return st;
-    if (cfg->T > 0) {
-        REQUIRE(yp);
-        REQUIRE(row_map);
-        REQUIRE(y);
-    }
-    return hip_status(launch_combine(*cfg, yp, row_map, w, y, as_stream(stream)), "moe_combine");
+    return combine_checked(cfg, yp, row_map, w, y, stream, true);
 }
 
+// Both fused calls check every step's arguments (pass 0) before the first
+// launch (pass 1), so a host-checkable problem enqueues nothing.
 moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x, const uint8_t* x_scale,
                        const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, void* y,
                        int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* row_map,
@@ -344,29 +451,33 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
         REQUIRE(w2_scale);
     }
     if (!xp && gu_stash) return fail(MOE_ERR_INVALID_ARG, "a training forward (gu_stash) needs xp");
-    if ((st = moe_route(cfg, logits, idx, w, stream))) return st;
-    if ((st = moe_permute(cfg, x, x_scale, idx, xp, xp_scale, counts, offsets, row_map, src_map, err, ws, ws_bytes,
-                          stream)))
-        return st;
-    // the routing weights applied in an expert epilogue: their per-row copy
-    const float* row_w = nullptr;
-    if (c.weight_site != MOE_WEIGHT_AT_COMBINE &&
-        (st = row_weights_checked(cfg, src_map, w, ws, ws_bytes, stream, &row_w)))
-        return st;
-    const float* fc1_w = c.weight_site == MOE_WEIGHT_AT_FC1 ? row_w : nullptr;
-    const float* fc2_w = c.weight_site == MOE_WEIGHT_AT_FC2 ? row_w : nullptr;
-    if (xp) {
-        st = swiglu_checked(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, gu_stash, nullptr, nullptr, fc1_w,
-                            ws, ws_bytes, stream, "moe_forward");
-    } else {
-        if (rows_capacity(c) > 0) REQUIRE(src_map);
-        st = swiglu_checked(cfg, x, x_scale, w1, w1_scale, offsets, h, h_scale, nullptr, src_map, counts, fc1_w, ws,
-                            ws_bytes, stream, "moe_forward");
+    if (!xp && rows_capacity(c) > 0) REQUIRE(src_map);
+    const bool at_combine = c.weight_site == MOE_WEIGHT_AT_COMBINE;
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool launch = pass == 1;
+        if ((st = route_checked(cfg, logits, idx, w, stream, launch))) return st;
+        if ((st = permute_checked(cfg, x, x_scale, idx, xp, xp_scale, counts, offsets, row_map, src_map, err, ws,
+                                  ws_bytes, stream, launch)))
+            return st;
+        // the routing weights applied in an expert epilogue: their per-row copy
+        const float* row_w = nullptr;
+        if (!at_combine && (st = row_weights_checked(cfg, src_map, w, ws, ws_bytes, stream, &row_w, launch)))
+            return st;
+        const float* fc1_w = c.weight_site == MOE_WEIGHT_AT_FC1 ? row_w : nullptr;
+        const float* fc2_w = c.weight_site == MOE_WEIGHT_AT_FC2 ? row_w : nullptr;
+        if (xp)
+            st = swiglu_checked(cfg, xp, xp_scale, w1, w1_scale, offsets, h, h_scale, gu_stash, nullptr, nullptr,
+                                fc1_w, ws, ws_bytes, stream, "moe_forward", launch);
+        else
+            st = swiglu_checked(cfg, x, x_scale, w1, w1_scale, offsets, h, h_scale, nullptr, src_map, counts, fc1_w,
+                                ws, ws_bytes, stream, "moe_forward", launch);
+        if (st) return st;
+        if ((st = down_checked(cfg, h, h_scale, w2, w2_scale, offsets, yp, fc2_w, ws, ws_bytes, stream, "moe_forward",
+                               launch)))
+            return st;
+        if ((st = combine_checked(cfg, yp, row_map, at_combine ? w : nullptr, y, stream, launch))) return st;
     }
-    if (st) return st;
-    if ((st = down_checked(cfg, h, h_scale, w2, w2_scale, offsets, yp, fc2_w, ws, ws_bytes, stream, "moe_forward")))
-        return st;
-    return moe_combine(cfg, yp, row_map, c.weight_site == MOE_WEIGHT_AT_COMBINE ? w : nullptr, y, stream);
+    return MOE_OK;
 }
 
 moe_status moe_route_bwd(const moe_config* cfg, const void* dy, const void* yp, const float* logits,
@@ -389,75 +500,23 @@ moe_status moe_route_bwd(const moe_config* cfg, const void* dy, const void* yp, 
 
 moe_status moe_combine_bwd(const moe_config* cfg, const void* dy, const int32_t* row_map, const int32_t* src_map,
                            const int32_t* offsets, const float* w, void* dyp, void* stream) {
-    moe_status st = check_config(cfg);
-    if (st) return st;
-    if (cfg->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "the backward takes F32 or BF16 storage");
-    if (cfg->weight_site != MOE_WEIGHT_AT_COMBINE)
-        return fail(MOE_ERR_UNSUPPORTED, "the backward is built for the weights applied in the combine");
-    if ((st = check_shapes(*cfg))) return st;
-    REQUIRE(offsets);
-    if (rows_capacity(*cfg) > 0) {
-        REQUIRE(dy);
-        REQUIRE(row_map);
-        REQUIRE(src_map);
-        REQUIRE(w);
-        REQUIRE(dyp);
-    }
-    return hip_status(launch_combine_bwd(*cfg, dy, row_map, src_map, offsets, w, dyp, as_stream(stream)), "moe_combine_bwd");
+    return combine_bwd_checked(cfg, dy, row_map, src_map, offsets, w, dyp, stream, true);
 }
 
 moe_status moe_grouped_down_bwd(const moe_config* cfg, const void* dyp, const void* w2, const void* h,
                                 const void* gu_stash, const int32_t* offsets, void* dgu, float* dw2, void* ws,
                                 size_t ws_bytes, void* stream) {
-    moe_status st = check_config(cfg);
-    if (st) return st;
-    if (cfg->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "the backward takes F32 or BF16 storage");
-    if ((st = check_shapes(*cfg))) return st;
-    REQUIRE(w2);
-    REQUIRE(dw2);
-    REQUIRE(offsets);
-    if ((st = check_ws(*cfg, ws, ws_bytes, true))) return st;
-    if (rows_capacity(*cfg) > 0) {
-        REQUIRE(dyp);
-        REQUIRE(h);
-        REQUIRE(gu_stash);
-        REQUIRE(dgu);
-    }
-    return hip_status(launch_down_bwd(*cfg, dyp, w2, h, gu_stash, offsets, dgu, dw2, ws, as_stream(stream)),
-                      "moe_grouped_down_bwd");
+    return down_bwd_checked(cfg, dyp, w2, h, gu_stash, offsets, dgu, dw2, ws, ws_bytes, stream, true);
 }
 
 moe_status moe_grouped_swiglu_bwd(const moe_config* cfg, const void* dgu, const void* w1, const void* xp,
                                   const int32_t* offsets, void* dxp, float* dw1, void* ws, size_t ws_bytes,
                                   void* stream) {
-    moe_status st = check_config(cfg);
-    if (st) return st;
-    if (cfg->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "the backward takes F32 or BF16 storage");
-    if ((st = check_shapes(*cfg))) return st;
-    REQUIRE(w1);
-    REQUIRE(dw1);
-    REQUIRE(offsets);
-    if ((st = check_ws(*cfg, ws, ws_bytes, true))) return st;
-    if (rows_capacity(*cfg) > 0) {
-        REQUIRE(dgu);
-        REQUIRE(xp);
-        REQUIRE(dxp);
-    }
-    return hip_status(launch_swiglu_bwd(*cfg, dgu, w1, xp, offsets, dxp, dw1, ws, as_stream(stream)),
-                      "moe_grouped_swiglu_bwd");
+    return swiglu_bwd_checked(cfg, dgu, w1, xp, offsets, dxp, dw1, ws, ws_bytes, stream, true);
 }
 
 moe_status moe_permute_bwd(const moe_config* cfg, const void* dxp, const int32_t* row_map, void* dx, void* stream) {
-    moe_status st = check_config(cfg);
-    if (st) return st;
-    if (cfg->dtype == MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "the backward takes F32 or BF16 storage");
-    if ((st = check_shapes(*cfg))) return st;
-    if (cfg->T > 0) {
-        REQUIRE(dxp);
-        REQUIRE(row_map);
-        REQUIRE(dx);
-    }
-    return hip_status(launch_permute_bwd(*cfg, dxp, row_map, dx, as_stream(stream)), "moe_permute_bwd");
+    return permute_bwd_checked(cfg, dxp, row_map, dx, stream, true);
 }
 
 moe_status moe_backward(const moe_config* cfg, const void* dy, const float* w, const void* w1, const void* w2,
@@ -465,10 +524,15 @@ moe_status moe_backward(const moe_config* cfg, const void* dy, const float* w, c
                         const void* h, const void* gu_stash, void* dyp, void* dgu, void* dxp, void* dx, float* dw1,
                         float* dw2, void* ws, size_t ws_bytes, void* stream) {
     moe_status st;
-    if ((st = moe_combine_bwd(cfg, dy, row_map, src_map, offsets, w, dyp, stream))) return st;
-    if ((st = moe_grouped_down_bwd(cfg, dyp, w2, h, gu_stash, offsets, dgu, dw2, ws, ws_bytes, stream))) return st;
-    if ((st = moe_grouped_swiglu_bwd(cfg, dgu, w1, xp, offsets, dxp, dw1, ws, ws_bytes, stream))) return st;
-    return moe_permute_bwd(cfg, dxp, row_map, dx, stream);
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool launch = pass == 1;
+        if ((st = combine_bwd_checked(cfg, dy, row_map, src_map, offsets, w, dyp, stream, launch))) return st;
+        if ((st = down_bwd_checked(cfg, dyp, w2, h, gu_stash, offsets, dgu, dw2, ws, ws_bytes, stream, launch)))
+            return st;
+        if ((st = swiglu_bwd_checked(cfg, dgu, w1, xp, offsets, dxp, dw1, ws, ws_bytes, stream, launch))) return st;
+        if ((st = permute_bwd_checked(cfg, dxp, row_map, dx, stream, launch))) return st;
+    }
+    return MOE_OK;
 }
 
 moe_status moe_quantize_mxfp8(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,

@@ -19,8 +19,10 @@
 //                         c, 0 elsewhere (w is the softmax of the chosen logits)
 //   normalised sigmoid:   dl_c = s_c (1 - s_c) (dw_c - sum_j dw_j w_j) / sum_j s_j
 //                         for the chosen c, 0 elsewhere
-// (the 1e-20 of the forward's normalising sums changes none of these in
-// float32).
+// The normalising sum S carries the forward's + 1e-20 here too: when every
+// chosen sigmoid underflows to 0 (chosen logits below about -88), S is 0, the
+// forward's weights are 0, and so are these gradients (without the 1e-20 they
+// would be 0/0).
 //
 // Lane layout as in route.hip: lane l holds the logits of experts l + 64 i.
 // The dot products stream the token's dY row and its k Yp rows in 16-byte
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const T_* __restrict__ d
         } else {  // normalised sigmoid
             a = my_ok ? 1.0f / (1.0f + __expf(-my_l)) : 0.f;
         }
-        S = wave_sum(a);
+        S = wave_sum(a) + 1e-20f;
         const float my_w = a / S;
         const float B = wave_sum(my_dw * my_w);
         // gradient of route j's logit

@@ -234,4 +234,8 @@ def small_shapes() -> list:
         # skewed routing (empty experts) and 16-row groups (zero padding rows)
         MoEShape("small_mxfp8_skew_align", 300, 512, 256, 16, 4, "softmax", True, "mxfp8", align=16,
                  zipf_bias=1.2, seed=2007),
+        # 128-row groups (the alignment of the TransformerEngine layout): most
+        # rows of Xp, h and Yp are padding
+        MoEShape("small_bf16_align128", 300, 256, 128, 8, 2, "softmax", True, "bf16", align=128, seed=2008),
+        MoEShape("small_mxfp8_align128", 260, 256, 128, 8, 2, "sigmoid", True, "mxfp8", align=128, seed=2009),
     ]

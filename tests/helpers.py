@@ -24,6 +24,62 @@ def rel_err(a, b) -> float:
     return num / den
 
 
+# Per-element bounds |a - b| <= rtol |b| + atol max|b| (b the oracle), next to
+# the normwise bar.  rtol is one step of the storage format at |b| (bf16 keeps
+# 8 significant bits: a step is at most 2^-7 |b|; E4M3 keeps 4: 2^-3 |b|),
+# which is what two roundings of values that differ by less than a step can
+# give; atol covers elements near 0, where the float32 accumulation error of
+# the kernel (relative to the row's magnitude, not the element's) decides.
+#   f32acc: float32 outputs of a float32 sum over bf16 operands (the weight
+#   gradients): sqrt(n) 2^-24 accumulation error plus bf16 flips in the
+#   operands, diluted by the sum, stay far below 2^-10 |b| + 2^-12 max|b|.
+#   e4m3_out: bf16 outputs of a product over a requantised MXFP8 h.  Where the
+#   kernel's float32 and the oracle's float64 put an h value on opposite sides
+#   of an E4M3 rounding boundary, that term of the sum moves by one step,
+#   2^-3 of the value; over a sum of F terms of random sign that is about
+#   2^-3 / sqrt(F) of the result, 2^-6.5 for the smallest F here (128).
+ELEM_BOUNDS = {"f32": (2.0 ** -16, 2.0 ** -17), "bf16": (2.0 ** -7, 2.0 ** -9),
+               "e4m3": (2.0 ** -3, 2.0 ** -9), "e4m3_out": (2.0 ** -5, 2.0 ** -8),
+               "f32acc": (2.0 ** -10, 2.0 ** -12)}
+# normwise bars max|a-b| / max|b| of the same kinds (1e-5 fp32, 2e-2 bf16,
+# 6e-2 MXFP8; float32 weight gradients over bf16 operands take the bf16 bar)
+NORM_TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2, "e4m3_out": 6e-2, "f32acc": 2e-2}
+ELEM_FRAC = 0.999  # share of elements that must meet the per-element bound
+
+
+def elem_stats(a, b, kind: str) -> dict:
+    """Share of elements within the per-element bound of `kind`, and the worst
+    element (the largest |a-b| / (rtol |b| + atol max|b|))."""
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    rtol, atol = ELEM_BOUNDS[kind]
+    if b.size == 0:
+        return {"frac": 1.0, "worst": 0.0, "at": -1, "a": 0.0, "b": 0.0, "n": 0}
+    lim = rtol * np.abs(b) + atol * float(np.max(np.abs(b)))
+    lim = np.where(lim > 0, lim, np.finfo(np.float64).tiny)
+    r = np.abs(a - b) / lim
+    r = np.where(np.isnan(r), np.inf, r)
+    i = int(np.argmax(r))
+    return {"frac": float(np.mean(r <= 1.0)), "worst": float(r[i]), "at": i, "a": float(a[i]), "b": float(b[i]),
+            "n": int(b.size)}
+
+
+def close_elementwise(a, b, kind: str, label: str = "", frac: float = ELEM_FRAC) -> bool:
+    """At least `frac` of the elements meet the per-element bound of `kind`;
+    prints the share and the worst element either way."""
+    st = elem_stats(a, b, kind)
+    print(f"{label}: {st['frac'] * 100:.4f} % of {st['n']} elements within the {kind} bound; worst "
+          f"element {st['at']}: got {st['a']:.6g}, oracle {st['b']:.6g} ({st['worst']:.3g} x the bound)")
+    return st["frac"] >= frac
+
+
+def assert_parity(got, ref, kind: str, label: str = "") -> None:
+    """The normwise bar of `kind` and, next to it, the per-element bound."""
+    e = rel_err(got, ref)
+    assert e < NORM_TOL[kind], f"{label}: normwise relative error {e:.3g} >= {NORM_TOL[kind]}"
+    assert close_elementwise(got, ref, kind, label), f"{label}: fewer than {ELEM_FRAC:.1%} of elements in bound"
+
+
 def to_dev(a: np.ndarray, fmt: str, device="cuda") -> torch.Tensor:
     """Stored numpy array -> torch tensor of the same bytes on the GPU."""
     if fmt == "bf16":

@@ -200,3 +200,67 @@ def test_new_entry_points_host_edge_cases():
     # a clamp limit is accepted by every call that takes the config
     cl = _cfg(swiglu_limit=7.0)
     assert lib.moe_workspace_size(ctypes.byref(cl)) == lib.moe_workspace_size(ctypes.byref(_cfg()))
+
+
+# moe_forward's pointer arguments after cfg, in order (ws_bytes and stream follow)
+_FWD = ("logits", "x", "x_scale", "w1", "w1_scale", "w2", "w2_scale", "y", "idx", "w", "counts", "offsets",
+        "row_map", "src_map", "xp", "xp_scale", "h", "h_scale", "yp", "gu_stash", "err", "ws")
+_BWD = ("dy", "w", "w1", "w2", "offsets", "row_map", "src_map", "xp", "h", "gu_stash", "dyp", "dgu", "dxp", "dx",
+        "dw1", "dw2", "ws")
+
+
+def _forward(lib, c, ws_bytes=None, **override):
+    args = {n: 1 for n in _FWD}
+    args.update({"x_scale": None, "w1_scale": None, "w2_scale": None, "xp_scale": None, "h_scale": None,
+                 "gu_stash": None, "err": None})
+    args.update(override)
+    nb = lib.moe_workspace_size(ctypes.byref(c)) if ws_bytes is None else ws_bytes
+    return lib.moe_forward(ctypes.byref(c), *[args[n] for n in _FWD], nb, None)
+
+
+def _backward(lib, c, ws_bytes=None, **override):
+    args = {n: 1 for n in _BWD}
+    args.update(override)
+    nb = lib.moe_backward_workspace_size(ctypes.byref(c)) if ws_bytes is None else ws_bytes
+    return lib.moe_backward(ctypes.byref(c), *[args[n] for n in _BWD], nb, None)
+
+
+def test_fused_calls_check_everything_before_launching():
+    """Without a GPU any launch fails with MOE_ERR_HIP, so a call that returns
+    the specific status of a later step's argument checked every step before
+    its first launch."""
+    lib = moe.load_library()
+    c = _cfg()
+    need = lib.moe_workspace_size(ctypes.byref(c))
+    assert _forward(lib, c, ws_bytes=need - 1) == b.MOE_ERR_WORKSPACE
+    for name in ("h", "yp", "y", "x", "row_map", "w1", "w2"):
+        assert _forward(lib, c, **{name: None}) == b.MOE_ERR_INVALID_ARG, name
+        assert name.encode() in lib.moe_last_error(), name
+    # MXFP8: the scales of every operand and of h
+    cm = _cfg(dtype=b.MOE_MXFP8, F=128)
+    mx = dict(x_scale=1, w1_scale=1, w2_scale=1, xp_scale=1, h_scale=1)
+    for name in ("h_scale", "xp_scale", "x_scale"):
+        assert _forward(lib, cm, **{**mx, name: None}) == b.MOE_ERR_INVALID_ARG, name
+    # the gather form (xp NULL) refuses a stash and needs src_map
+    assert _forward(lib, c, xp=None, gu_stash=1) == b.MOE_ERR_INVALID_ARG
+    assert _forward(lib, c, xp=None, src_map=None) == b.MOE_ERR_INVALID_ARG
+    # an epilogue weight site checks the per-row weights' inputs first
+    assert _forward(lib, _cfg(weight_site=b.MOE_WEIGHT_AT_FC2), w=None) == b.MOE_ERR_INVALID_ARG
+    # backward: a short workspace and a missing last output are found before the first step runs
+    cb = _cfg()
+    assert _backward(lib, cb, ws_bytes=lib.moe_backward_workspace_size(ctypes.byref(cb)) - 1) == b.MOE_ERR_WORKSPACE
+    for name in ("dx", "dxp", "dw1", "gu_stash", "xp"):
+        assert _backward(lib, cb, **{name: None}) == b.MOE_ERR_INVALID_ARG, name
+
+
+def test_backward_takes_bf16_storage_only():
+    lib = moe.load_library()
+    for dt in (b.MOE_F32, b.MOE_MXFP8):
+        c = _cfg(dtype=dt, F=128)
+        assert _backward(lib, c, ws_bytes=1 << 20) == b.MOE_ERR_UNSUPPORTED
+        assert lib.moe_combine_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+        assert lib.moe_permute_bwd(ctypes.byref(c), 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+        assert lib.moe_grouped_down_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20, None) == \
+            b.MOE_ERR_UNSUPPORTED
+        assert lib.moe_grouped_swiglu_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, 1, 1 << 20, None) == \
+            b.MOE_ERR_UNSUPPORTED

@@ -224,3 +224,185 @@ def test_sampled_backward_helpers_agree_with_full_backward():
     d2, d1 = orc.backward_dw_entries(s, e, x, w1, w2, w, src_map, offsets, dy, i2, i1)
     np.testing.assert_allclose(d2.astype(np.float32), g["dw2"][e][i2[:, 0], i2[:, 1]], rtol=1e-6, atol=1e-7)
     np.testing.assert_allclose(d1.astype(np.float32), g["dw1"][e][i1[:, 0], i1[:, 1]], rtol=1e-6, atol=1e-7)
+
+
+# ---- the expert-major float64 front end (forward_experts, backward_expert)
+# It evaluates the same definitions with the sums over H and F as float64
+# matrix products; only the order of the float64 additions differs, which
+# moves a stored value only when a sum lies within ~1e-16 of a rounding
+# boundary of its storage format.  On these shapes every stored byte agrees.
+def _small_mx(T, H, F, E, k, seed):
+    rng = np.random.default_rng(seed)
+    s = MoEShape("rand_mx", T, H, F, E, k, "sigmoid", True, "mxfp8")
+    q = lambda a: orc.mx_quantize(a.astype(np.float32))
+    x, xs = q(rng.standard_normal((T, H)))
+    w1, w1s = q(rng.standard_normal((E, 2 * F, H)) / np.sqrt(H))
+    w2, w2s = q(rng.standard_normal((E, H, F)) / np.sqrt(F))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    return s, (x, xs), (w1, w1s), (w2, w2s), lg
+
+
+@pytest.mark.parametrize("fmt,site,limit", [("f32", "combine", 0.0), ("bf16", "combine", 0.0),
+                                            ("bf16", "fc1", 0.0), ("bf16", "fc2", 0.0), ("bf16", "combine", 0.6)])
+def test_expert_major_forward_equals_token_loops(fmt, site, limit):
+    s, x, w1, w2, lg = _rand_problem(61, 64, 96, 6, 3, 11, fmt=fmt, renorm=True)
+    idx, w = orc.route(lg, s.k, s.score, s.renorm)
+    idx[::9, 1] = -1  # dropped routes
+    toks = np.arange(s.T)
+    a = orc.forward_tokens(s, toks, x, w1, w2, idx, w, want_stash=True, site=site, limit=limit)
+    b = orc.forward_experts(s, toks, x, w1, w2, idx, w, want_stash=True, site=site, limit=limit)
+    live = idx >= 0
+    for key in ("h", "yp", "stash"):
+        assert np.array_equal(a[key][live].view(np.uint8), b[key][live].view(np.uint8)), key
+    assert np.array_equal(a["y"].view(np.uint8), b["y"].view(np.uint8))
+    # a sample of tokens gives the sample's rows of the full evaluation
+    sub = np.array([3, 17, 40, 60])
+    c = orc.forward_experts(s, sub, x, w1, w2, idx, w, site=site, limit=limit)
+    assert np.array_equal(c["y"].view(np.uint8), b["y"][sub].view(np.uint8))
+
+
+def test_expert_major_forward_equals_token_loops_mxfp8():
+    s, (x, xs), (w1, w1s), (w2, w2s), lg = _small_mx(45, 64, 96, 5, 2, 12)
+    idx, w = orc.route(lg, s.k, s.score, s.renorm)
+    toks = np.arange(s.T)
+    a = orc.forward_tokens(s, toks, x, w1, w2, idx, w, xs, w1s, w2s, want_stash=True)
+    b = orc.forward_experts(s, toks, x, w1, w2, idx, w, xs, w1s, w2s, want_stash=True)
+    for key in ("h", "h_scale", "yp", "stash", "y"):
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+
+
+@pytest.mark.parametrize("limit", [0.0, 0.7])
+def test_expert_major_backward_equals_row_loops(limit):
+    s, x, w1, w2, lg = _rand_problem(80, 64, 48, 5, 2, 13, fmt="bf16", renorm=True)
+    s = MoEShape("rand_bwd", s.T, s.H, s.F, s.E, s.k, s.score, s.renorm, "bf16", align=4)
+    lg[:, 4] -= 50.0  # expert 4 gets no rows
+    idx, w = orc.route(lg, s.k, s.score, s.renorm)
+    counts, offsets, row_map, src_map, _ = orc.group(idx, s.E, s.align)
+    assert counts[4] == 0
+    dy = orc.bf16_from_f64(np.random.default_rng(14).standard_normal((s.T, s.H)))
+    ref = orc.forward_tokens(s, np.arange(s.T), x, w1, w2, idx, w, want_stash=True, limit=limit)
+    R = src_map.shape[0]
+    h_rows = np.zeros((R, s.F), np.uint16)
+    st_rows = np.zeros((R, 2 * s.F), np.uint16)
+    h_rows[row_map.ravel()] = ref["h"].reshape(-1, s.F)
+    st_rows[row_map.ravel()] = ref["stash"].reshape(-1, 2 * s.F)
+    g = orc.backward(s, x, w1, w2, w, row_map, src_map, offsets, h_rows, st_rows, dy, limit=limit)
+    for e in range(s.E):
+        b = orc.backward_expert(s, e, x, w1, w2, w, src_map, offsets, dy, limit=limit)
+        assert np.array_equal(b["dw1"].view(np.uint32), g["dw1"][e].view(np.uint32)), f"dW1 of expert {e}"
+        assert np.array_equal(b["dw2"].view(np.uint32), g["dw2"][e].view(np.uint32)), f"dW2 of expert {e}"
+        r = b["rows"]
+        if r.size:
+            for key in ("dyp", "dgu", "dxp"):
+                assert np.array_equal(b[key], g[key][r]), f"{key} of expert {e}"
+
+
+def _rne_bf16(v):
+    """float64 -> the nearest bfloat16 value (8 significant bits, ties to even),
+    as float64: frexp splits v = m 2^e with 0.5 <= |m| < 1, and numpy's round
+    is half-to-even on m 2^8.  Independent of the oracle's bit-level rounding;
+    valid in bf16's normal range, which these values stay in."""
+    m, e = np.frexp(np.asarray(v, np.float64))
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
+def _ulp_diff_bf16(a_bits, b_f64):
+    """Difference in bf16 units between stored bf16 bits and a float64 value
+    that is itself a bf16 value (same sign assumed for nonzero pairs)."""
+    a = (np.asarray(a_bits, np.uint16).astype(np.int32))
+    b = (orc.bf16_from_f64(b_f64).astype(np.int32))
+    return np.abs(a - b)
+
+
+def test_bf16_backward_rounding_points():
+    """Every bf16 rounding point of the backward, recomputed with torch float64
+    products, torch autograd for the SwiGLU derivative and an independent
+    round-to-nearest-even: dYp = bf16(w dY), dH = dYp W2 (not rounded),
+    dGU = bf16(dH * dSwiGLU(stash)), dXp = bf16(dGU W1), dX = bf16(sum_j dXp),
+    dW2 = f32(dYp^T h) with the rounded dYp and the stored h, dW1 = f32(dGU^T Xp)
+    with the rounded dGU.  A misplaced rounding point (dW1 from the unrounded
+    dGU, dYp unrounded before the products) moves many values by far more than
+    the one bf16 unit, or the float32 rounding, that float64 summation order
+    can account for."""
+    T, H, F, E, k = 40, 64, 48, 5, 2
+    s, x, w1, w2, lg = _rand_problem(T, H, F, E, k, 15, fmt="bf16")
+    idx, w = orc.route(lg, k, s.score, s.renorm)
+    counts, offsets, row_map, src_map, h_rows, st_rows, _ = _forward_rows(s, x, w1, w2, idx, w)
+    dy = orc.bf16_from_f64(np.random.default_rng(16).standard_normal((T, H)))
+    g = orc.backward(s, x, w1, w2, w, row_map, src_map, offsets, h_rows, st_rows, dy)
+    f = lambda a: torch.from_numpy(orc.f64_from_bf16(a))
+    xd, w1d, w2d, dyd = f(x), f(w1), f(w2), f(dy)
+    n = int(offsets[-1])
+    dyp = torch.zeros(n, H, dtype=torch.float64)
+    for r in range(n):
+        sidx = int(src_map[r])
+        dyp[r] = torch.from_numpy(_rne_bf16((float(w.ravel()[sidx]) * dyd[sidx // k]).numpy()))
+    assert np.all(_ulp_diff_bf16(g["dyp"][:n], dyp.numpy()) == 0)
+    dgu = torch.zeros(n, 2 * F, dtype=torch.float64)
+    dxp = torch.zeros(n, H, dtype=torch.float64)
+    dw1 = np.zeros((E, 2 * F, H))
+    dw2 = np.zeros((E, H, F))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        dh = dyp[r0:r1] @ w2d[e]                                  # [rows, F], not rounded
+        st = f(st_rows[r0:r1])
+        gg = st[:, :F].clone().requires_grad_(True)
+        uu = st[:, F:].clone().requires_grad_(True)
+        (tF.silu(gg) * uu).backward(dh)
+        dgu[r0:r1] = torch.from_numpy(_rne_bf16(torch.cat([gg.grad, uu.grad], 1).numpy()))
+        dxp[r0:r1] = torch.from_numpy(_rne_bf16((dgu[r0:r1] @ w1d[e]).numpy()))
+        xp = xd[torch.from_numpy(src_map[r0:r1] // k).long()]
+        dw1[e] = (dgu[r0:r1].T @ xp).numpy()
+        dw2[e] = (dyp[r0:r1].T @ f(h_rows[r0:r1])).numpy()
+    # float64 summation order may move a value across a rounding boundary:
+    # at most one bf16 unit, in a small share of the values
+    for key, ref in (("dgu", dgu), ("dxp", dxp)):
+        d = _ulp_diff_bf16(g[key][:n], ref.numpy())
+        assert d.max() <= 1 and d.mean() < 1e-3, key
+    dx = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            dx[t] += dxp[int(row_map[t, j])].numpy()
+    d = _ulp_diff_bf16(g["dx"], _rne_bf16(dx))
+    assert d.max() <= 1 and d.mean() < 1e-3
+    for key, ref in (("dw1", dw1), ("dw2", dw2)):
+        got = g[key].astype(np.float64)
+        ref32 = ref.astype(np.float32).astype(np.float64)
+        ulp = np.spacing(np.abs(ref32).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - ref32) <= ulp), key
+    # the misplacements named above are caught: dW1 from the unrounded dGU and
+    # dW2 from an unrounded dYp differ from the oracle by far more
+    e = int(np.argmax(counts))
+    r0, r1 = int(offsets[e]), int(offsets[e + 1])
+    dyp_raw = torch.stack([float(w.ravel()[int(src_map[r])]) * dyd[int(src_map[r]) // k] for r in range(r0, r1)])
+    bad2 = (dyp_raw.T @ f(h_rows[r0:r1])).numpy()
+    assert np.max(np.abs(bad2 - g["dw2"][e])) > 100 * np.max(np.abs(dw2[e] - g["dw2"][e]))
+
+
+def test_bf16_backward_within_rounding_of_torch_autograd():
+    """The bf16 layer's gradients against torch float64 autograd of the
+    unrounded layer on the same stored inputs: the storage roundings of h, Yp,
+    the stash, dYp, dGU, dXp and dX (each at most 2^-8 relative) bound the
+    difference; 2^-6 normwise."""
+    T, H, F, E, k = 31, 64, 48, 5, 2
+    s, x, w1, w2, lg = _rand_problem(T, H, F, E, k, 17, fmt="bf16")
+    idx, w = orc.route(lg, k, s.score, s.renorm)
+    counts, offsets, row_map, src_map, h_rows, st_rows, _ = _forward_rows(s, x, w1, w2, idx, w)
+    dy = orc.bf16_from_f64(np.random.default_rng(18).standard_normal((T, H)))
+    g = orc.backward(s, x, w1, w2, w, row_map, src_map, offsets, h_rows, st_rows, dy)
+    f = lambda a: torch.from_numpy(orc.f64_from_bf16(a))
+    xt, w1t, w2t = (f(a).requires_grad_(True) for a in (x, w1, w2))
+    rows = []
+    for t in range(T):
+        acc = torch.zeros(H, dtype=torch.float64)
+        for j in range(k):
+            e = int(idx[t, j])
+            gu = tF.linear(xt[t], w1t[e])
+            acc = acc + float(w[t, j]) * tF.linear(tF.silu(gu[:F]) * gu[F:], w2t[e])
+        rows.append(acc)
+    (torch.stack(rows) * f(dy)).sum().backward()
+    assert _rel(orc.f64_from_bf16(g["dx"]), xt.grad.numpy()) < 2 ** -6
+    assert _rel(g["dw1"], w1t.grad.numpy()) < 2 ** -6
+    assert _rel(g["dw2"], w2t.grad.numpy()) < 2 ** -6
