@@ -90,14 +90,14 @@ def test_route_bwd_sigmoid_underflow():
     gives those tokens w = 0 through the + 1e-20 of the normaliser, and the
     backward must give finite gradients that match the float64 oracle (which
     keeps the same + 1e-20), not 0/0."""
-    T, H, E, k = 96, 64, 16, 4
+    T, H, E, k = 96, 128, 16, 4
     rng = np.random.default_rng(4242)
     lg = rng.standard_normal((T, E)).astype(np.float32)
     lg[::3] = -100.0 - 10.0 * rng.random((len(lg[::3]), E)).astype(np.float32)  # all experts underflow
     lg[1::3, :] -= 80.0                                                            # tiny, not zero
-    cfg = moe.MoEConfig(T, H, 32, E, k, 1, "sigmoid", True, "bf16")
+    cfg = moe.MoEConfig(T, H, 64, E, k, 1, "sigmoid", True, "bf16")
     idx_o, w_o = orc.route(lg, k, "sigmoid", True)
-    assert np.all(w_o[::3] == 0)
+    assert np.all(w_o[::3] < 1e-20)  # float64 sigmoids ~1e-44 over 1e-20; float32 underflows to 0
     _, _, row_map, _, _ = orc.group(idx_o, E, 1)
     yp = orc.bf16_from_f64(rng.standard_normal((T * k, H)))
     dy = orc.bf16_from_f64(rng.standard_normal((T, H)))
@@ -106,6 +106,6 @@ def test_route_bwd_sigmoid_underflow():
     dw_o, dl_o = orc.route_bwd(lg, idx_o, row_map, dy, yp, "bf16", "sigmoid", True)
     dl_h, dw_h = to_host(dl), to_host(dw)
     assert np.all(np.isfinite(dl_h)) and np.all(np.isfinite(dw_h))
-    assert np.all(dl_h[::3] == 0) and np.all(dl_o[::3] == 0)
+    assert np.all(dl_h[::3] == 0) and np.all(np.abs(dl_o[::3]) < 1e-20)
     assert rel_err(dw_h, dw_o) < TOL_RB
     assert rel_err(dl_h, dl_o) < TOL_RB
