@@ -259,6 +259,22 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
                        int32_t* src_map, void* xp, uint8_t* xp_scale, void* h, uint8_t* h_scale, void* yp,
                        void* gu_stash, int32_t* err, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments (ws and ws_bytes dropped), same
+ * kernels and the same results bit for bit.  Its scratch space is a static
+ * device array of the library, 68 MiB on every device the library is loaded
+ * on, held until the process ends; a config whose moe_workspace_size exceeds
+ * 68 MiB returns MOE_ERR_WORKSPACE.  The call allocates nothing.  The array
+ * is shared by every call on a device and keeps the last call's contents:
+ * calls that overlap on one device (other streams, other host threads) race,
+ * so the caller orders them. */
+moe_status moe_forward_noalloc(const moe_config* cfg, const float* logits, const void* x, const uint8_t* x_scale,
+                               const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale,
+                               void* y, int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* row_map,
+                               int32_t* src_map, void* xp, uint8_t* xp_scale, void* h, uint8_t* h_scale, void* yp,
+                               void* gu_stash, int32_t* err, void* stream);
+
 /* ---------------------------------------------------------------------- */
 /* Backward of the expert FFN and the combine.  Built for BF16 storage    */
 /* with the routing weights applied in the combine: every call below except */

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     moe_grouped_swiglu_gemm_weighted,
     moe_grouped_down_gemm_weighted,
     moe_forward,
+    moe_forward_noalloc,
     moe_grouped_down_bwd,
     moe_grouped_down_gemm,
     moe_grouped_swiglu_bwd,

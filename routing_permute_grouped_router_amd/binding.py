@@ -108,6 +108,7 @@ _SIGS = {
     "moe_grouped_down_gemm": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_combine": (ctypes.c_int, [CFG, P, P, P, P, P]),
     "moe_forward": (ctypes.c_int, [CFG] + [P] * 22 + [ctypes.c_size_t, P]),
+    "moe_forward_noalloc": (ctypes.c_int, [CFG] + [P] * 21 + [P]),
     "moe_route_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P]),
     "moe_grouped_swiglu_gemm_gather": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_grouped_swiglu_gemm_weighted": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -316,12 +317,24 @@ def moe_combine(cfg: MoEConfig, yp, row_map, w, y, stream=None):
 def moe_forward(cfg: MoEConfig, logits, x, w1, w2, buf: dict, x_scale=None, w1_scale=None, w2_scale=None,
                 stream=None):
     """buf: the caller's buffers, as made by alloc_forward()."""
+    _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stream, noalloc=False)
+
+
+def moe_forward_noalloc(cfg: MoEConfig, logits, x, w1, w2, buf: dict, x_scale=None, w1_scale=None, w2_scale=None,
+                        stream=None):
+    """moe_forward with the library's static scratch array instead of buf["ws"]
+    (which is not used)."""
+    _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stream, noalloc=True)
+
+
+def _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stream, noalloc):
     c = cfg.c()
     mx = cfg.dtype == "mxfp8"
-    wp, wb = _ws(buf["ws"])
+    ws_args = () if noalloc else _ws(buf["ws"])
+    fn = load_library().moe_forward_noalloc if noalloc else load_library().moe_forward
     R, T, H, F, E, k = cfg.R_cap, cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
     sd, od = cfg.store_dtype, cfg.out_dtype
-    _check(load_library().moe_forward(
+    _check(fn(
         ctypes.byref(c), _ptr(logits, "logits", torch.float32, (T, E)), _ptr(x, "x", sd, (T, H)),
         _ptr(x_scale, "x_scale", torch.uint8, (T, H // 32), optional=not mx),
         _ptr(w1, "w1", sd, (E, 2 * F, H)), _ptr(w1_scale, "w1_scale", torch.uint8, (E, 2 * F, H // 32), optional=not mx),
@@ -335,7 +348,7 @@ def moe_forward(cfg: MoEConfig, logits, x, w1, w2, buf: dict, x_scale=None, w1_s
         _ptr(buf["h"], "h", sd, (R, F)), _ptr(buf.get("h_scale"), "h_scale", torch.uint8, (R, F // 32), optional=not mx),
         _ptr(buf["yp"], "yp", od, (R, H)),
         _ptr(buf.get("gu_stash"), "gu_stash", od, (R, 2 * F), optional=True),
-        _ptr(buf.get("err"), "err", torch.int32, (1,), optional=True), wp, wb, _stream(stream)))
+        _ptr(buf.get("err"), "err", torch.int32, (1,), optional=True), *ws_args, _stream(stream)))
 
 
 def moe_route_bwd(cfg: MoEConfig, dy, yp, logits, idx, row_map, dlogits, dw=None, stream=None):

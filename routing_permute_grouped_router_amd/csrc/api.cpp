@@ -341,6 +341,14 @@ moe_status permute_bwd_checked(const moe_config* cfg, const void* dxp, const int
 
 }  // namespace
 
+moe_status moe::set_error(moe_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
 extern "C" {
 
 int64_t moe_rows_capacity(const moe_config* cfg) {

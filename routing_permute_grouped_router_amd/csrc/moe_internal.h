@@ -40,6 +40,10 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// --------------------------------------------------------- errors
+// Sets the calling thread's moe_last_error() message and returns s.
+moe_status set_error(moe_status s, const char* fmt, ...);
+
 // --------------------------------------------------------- host launchers
 // Each returns hipSuccess or the launch error; arguments were validated by
 // the API layer.

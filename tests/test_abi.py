@@ -264,3 +264,15 @@ def test_backward_takes_bf16_storage_only():
             b.MOE_ERR_UNSUPPORTED
         assert lib.moe_grouped_swiglu_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, 1, 1 << 20, None) == \
             b.MOE_ERR_UNSUPPORTED
+
+
+def test_noalloc_forward_limit_checked_on_host():
+    """moe_forward_noalloc refuses a config whose scratch exceeds its static
+    array before touching the device, and reports a bad config like moe_forward."""
+    lib = moe.load_library()
+    big = _cfg(T=400000, H=2048, F=768, E=128, k=8)
+    assert lib.moe_workspace_size(ctypes.byref(big)) > 68 << 20
+    args = [1] * 21
+    assert lib.moe_forward_noalloc(ctypes.byref(big), *args, None) == b.MOE_ERR_WORKSPACE
+    assert b"68" in lib.moe_last_error() or b"static" in lib.moe_last_error()
+    assert lib.moe_forward_noalloc(ctypes.byref(_cfg(k=0)), *args, None) == b.MOE_ERR_INVALID_ARG
