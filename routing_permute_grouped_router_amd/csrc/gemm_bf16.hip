@@ -18,7 +18,7 @@ namespace {
 
 // Tuned on MI355X with the Mixtral-shaped and fine-grained layers (kGroupM = 0:
 // tiles expert by expert, each weight panel streamed once).
-constexpr int kSwizzle = 0, kGroupM = 0;
+constexpr int kSwizzle = 2, kGroupM = 0;
 
 int g_num_cus = 0;
 

@@ -1,4 +1,4 @@
-// Grouped bf16 GEMM kernel template for CDNA4 (v_mfma_f32_32x32x16_bf16).
+// Grouped bf16 GEMM kernel template for CDNA4 (v_mfma_f32_16x16x32_bf16).
 //
 // C[r, n] = sum_k A[r, k] * B_e[n, k] for the rows r of expert e, group sizes
 // read from the device `offsets` buffer.  Both operands have K contiguous (rows
@@ -6,19 +6,20 @@
 // every MFMA operand is one 16-byte LDS read.
 //
 // Block: 256 threads = 4 wavefronts in a 2 x 2 grid; tile 256 x 256 x 64; each
-// wavefront owns a 128 x 128 sub-tile held in 4 x 4 MFMA 32x32 accumulators
+// wavefront owns a 128 x 128 sub-tile held in 8 x 8 MFMA 16x16 accumulators
 // (256 accumulator registers per lane).  Operand tiles go from global memory
 // straight into LDS with global_load_lds_dwordx4 (lane i of one load lands at
-// LDS base + 16 i), two stages of 64 KiB, so K step k+1 streams in while step
-// k feeds the matrix cores.  In LDS each row's 16-byte K chunks are XOR-
+// LDS base + 16 i), two stages of 64 KiB, so stage k+2 streams in while stages
+// k and k+1 feed the matrix cores.  In LDS each row's 16-byte K chunks are XOR-
 // permuted by a function of the row (swz) so that the MFMA operand reads of
-// consecutive rows hit distinct banks; the permutation is applied on the global side (a lane fetches
-// the chunk its LDS slot must hold).  Rows past a group's end, and columns past
-// the output width, load a clamped valid row and are never stored.
+// consecutive rows hit distinct banks; the permutation is applied on the global
+// side (a lane fetches the chunk its LDS slot must hold).  Rows past a group's
+// end, and columns past the output width, load a clamped valid row and are
+// never stored.
 //
 // SwiGLU tiles put 128 gate rows (f0..f0+127) and the matching 128 up rows
 // (F+f0..) of W1 in one 256-row B tile; a wavefront's accumulators (mi, ni) and
-// (mi, ni+2) are then gate and up of the same outputs in the same lanes, and
+// (mi, ni+4) are then gate and up of the same outputs in the same lanes, and
 // the epilogue forms silu(g) * u in registers.
 //
 // The grid is persistent (one block per CU); block b runs on XCD b % 8 and
@@ -26,6 +27,8 @@
 // ranges, one per XCD, so the blocks of an XCD share A rows and B columns in
 // its L2; the blocks take their units through per-XCD work queues (below).
 #pragma once
+
+#include <type_traits>
 
 #include "moe_internal.h"
 #include "tiles.h"
@@ -123,7 +126,10 @@ __device__ __forceinline__ Queue xcd_queue(int total, int x, int nb, int nk) {
 // (two per 128 bytes): the same two guarantees with the row pair folded in.
 template <int SWZ, int CH = 8>
 __device__ __forceinline__ int swz(int row) {
-    if (CH == 8) return SWZ == 1 ? ((row ^ (row >> 3)) & 7) : (row & 7);
+    if (CH == 8) {
+        if (SWZ == 2) return (row & 7) ^ ((row >> 3) & 1);
+        return SWZ == 1 ? ((row ^ (row >> 3)) & 7) : (row & 7);
+    }
     return SWZ == 1 ? (((row >> 1) ^ (row >> 3)) & 3) : ((row >> 1) & 3);
 }
 
@@ -188,20 +194,53 @@ __device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// 16x16x32 fragments and accumulators.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order (a loop whose
+// index is a constant expression in its body).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// Output column of B row r of a forward tile for the 16x16x32 layout.  A
+// wavefront reads B fragment ni of its column half wn from LDS rows
+// wn 128 + 16 ni + c (c = 0..15), and MFMA lane l holds column c = l % 16 of
+// every fragment; with that row carrying output column wn 128 + 8 c + ni,
+// lane l holds the eight adjacent columns 8 c .. 8 c + 7 of each of its rows,
+// one per fragment, and stores them as one 16-byte word.  SwiGLU tiles (gate
+// rows 0..127, up rows 128..255; gate fragments 0..3 of half wn at rows
+// wn 64 + 16 ni + c, up fragments 4..7 the same rows + 128): h column
+// wn 64 + 4 c + ni, four adjacent h columns per lane.
+__device__ __forceinline__ int out_col16(int r) { return (r & 128) + 8 * (r & 15) + ((r >> 4) & 7); }
+__device__ __forceinline__ int out_col16_swiglu(int h) { return (h & 64) + 4 * (h & 15) + ((h >> 4) & 3); }
+
 // EP, epilogue variant bits (built separately, so the plain kernel carries
 // none of it): 1 = the outputs are scaled by p.row_w, 2 = the SwiGLU inputs
 // are clamped to p.lim.
+//
+// Block tile 256 x 256 x 64, 4 wavefronts of 128 x 128 in a 2 x 2 grid; a
+// wavefront's sub-tile is 8 x 8 v_mfma_f32_16x16x32_bf16 accumulators (256
+// accumulator registers).  On MI355X this instruction sustains ~16 % more
+// throughput than the 32x32x16 form on Gaussian operands (the part runs at
+// its power limit), for the same LDS bytes per flop.  A 64-deep stage is two
+// 32-deep K sub-steps of 64 MFMAs.  Chunk c of tile row r is stored at
+// position c ^ swz(r); fragments start at multiples of 16 rows, so with
+// SWZ 0 or 2 the permutation depends only on the lane.
 template <bool SWIGLU, int SWZ, int GM, int EP>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
+    static_assert(SWZ == 0 || SWZ == 2, "the fragment addressing needs a swizzle of the row within 16");
     constexpr int BK = 64;                  // K depth of one stage
     constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
     constexpr int RPL = 64 / CH;            // rows per wave-wide load
     constexpr int LOADS = 64 / RPL;         // loads per wave per operand per stage
     constexpr int STAGE_ELEMS = kTile * BK; // one operand of one stage
-    // byte offsets of B fragments 1..3 from fragment 0: SwiGLU tiles hold
-    // gate rows 0..127 and up rows 128..255 (fragments 2, 3 are the up rows
-    // of fragments 0, 1); other tiles 32 consecutive rows per fragment
-    constexpr int B1 = 32 * BK * 2, B2 = (SWIGLU ? 128 : 64) * BK * 2, B3 = (SWIGLU ? 160 : 96) * BK * 2;
+    constexpr uint32_t kRowBytes = BK * 2;
+    constexpr uint32_t kFragBytes = 16 * kRowBytes;  // one 16-row fragment
 
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][STAGE_ELEMS];
     __shared__ int32_t pre[kMaxExperts + 1];
@@ -252,27 +291,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     }
     __syncthreads();
     int unit = s_unit;
-    const int lrow = lane / CH, lslot = lane % CH;
-
-    // LDS byte address of this lane's first A and B fragment (stage 0, K
-    // chunk 0) and the byte offset of its chunk in each 16-deep K sub-step:
-    // lane l reads row l % 32 of each 32-row fragment at 16-byte chunk
-    // 2 kk + l / 32, stored at chunk position (2 kk + l / 32) ^ swz(row).
-    // Fragments start at multiples of 32 rows, so swz(row) depends only on l
-    // and, for the row ^ (row / 8) permutation, on the fragment's parity.
+    // LDS byte addresses of this lane's A and B fragment 0 (stage 0) and the
+    // offsets of its chunk in the two K sub-steps: lane l reads row l % 16 of
+    // a fragment at chunk 4 kk + l / 16, stored at (4 kk + l / 16) ^ swz(row).
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)&lds[0][0][0];
     constexpr uint32_t kStageBytes = 2 * STAGE_ELEMS * 2;
     // LDS rows this wave's loads fill: wid * 64 .. +63 of each operand
-    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(wid * 64 * BK * 2));
-    const uint32_t a_rd = lds_base + (uint32_t)((wm * 128 + (lane & 31)) * BK * 2);
-    const uint32_t b_rd = lds_base + (uint32_t)(STAGE_ELEMS * 2 + (SWIGLU ? wn * 64 : wn * 128) * BK * 2 +
-                                                (lane & 31) * BK * 2);
-    uint32_t koff[4][2];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int par = 0; par < 2; ++par)
-            koff[kk][par] = (uint32_t)(((2 * kk + (lane >> 5)) ^ swz<SWZ>(par * 32 + (lane & 31))) << 4);
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(wid * 64) * kRowBytes);
+    const int fr = lane & 15;
+    const uint32_t a_rd = lds_base + (uint32_t)(wm * 128 + fr) * kRowBytes;
+    const uint32_t b_rd = lds_base + (uint32_t)(STAGE_ELEMS * 2) + (uint32_t)((SWIGLU ? wn * 64 : wn * 128) + fr) * kRowBytes;
+    const uint32_t koff0 = (uint32_t)((((lane >> 4)) ^ swz<SWZ>(fr)) << 4);
+    const uint32_t koff1 = (uint32_t)(((4 + (lane >> 4)) ^ swz<SWZ>(fr)) << 4);
     // State of the unit in flight, set by `setup`: its tile, K stages
     // [kb, ke), partial-sum slot (-1: whole tile), load offsets and bases.
     int kb = 0, ke = 0, slot = -1, row0 = 0, row_end = 0, a_end = 0, nt = 0;
@@ -280,82 +310,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     uint32_t aoff[LOADS], boff[LOADS];
     const char* abase = (const char*)p.A;
     const char* bbase = (const char*)p.B;
-#define GG_LOAD_A(kt, stage, i)                                                                          \
-    dma_lds16(lds_wave + (uint32_t)(stage) * kStageBytes + (i) * RPL * BK * 2, aoff[i], abase + (size_t)(kt) * (BK * 2))
-#define GG_LOAD_B(kt, stage, i)                                                                          \
-    dma_lds16(lds_wave + (uint32_t)(stage) * kStageBytes + STAGE_ELEMS * 2 + (i) * RPL * BK * 2, boff[i],         \
+#define GK_LOAD_A(kt, stage, i)                                                                          \
+    dma_lds16(lds_wave + (uint32_t)(stage) * kStageBytes + (i) * RPL * kRowBytes, aoff[i],               \
+              abase + (size_t)(kt) * (BK * 2))
+#define GK_LOAD_B(kt, stage, i)                                                                          \
+    dma_lds16(lds_wave + (uint32_t)(stage) * kStageBytes + STAGE_ELEMS * 2 + (i) * RPL * kRowBytes, boff[i], \
               bbase + (size_t)(kt) * (BK * 2))
-#define GG_ISSUE(kt, stage)                                                                              \
-    _Pragma("unroll") for (int i = 0; i < LOADS; ++i) {                                                  \
-        GG_LOAD_A(kt, stage, i);                                                                         \
-        GG_LOAD_B(kt, stage, i);                                                                         \
-    }
-// Wait until every LDS read issued so far has landed; the fragment registers
-// are tied to the wait so no MFMA that uses them moves above it.
-#define GG_WAIT_FRAGS(FA, FB)                                                                            \
-    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
-                     : "+v"(FA[0]), "+v"(FA[1]), "+v"(FA[2]), "+v"(FA[3]), "+v"(FB[0]), "+v"(FB[1]),     \
-                       "+v"(FB[2]), "+v"(FB[3])::"memory")
-#define GG_MFMA(FA, FB, mi, ni)                                                                          \
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[mi], FB[ni], acc[mi][ni], 0, 0, 0)
-// The 8 fragments of one K sub-step: A fragment mi at mi * 32 rows, B
-// fragment ni at B1..B3 bytes past fragment 0; AD/BD[par] are the lane's
-// addresses for fragments of parity par (the chunk permutation differs).
-#define GG_RD_A(GA, AD, mi) GA[mi] = lds_frag<(mi) * 32 * BK * 2>(AD[(mi) & 1])
-#define GG_RD_B(GB, BD, ni) GB[ni] = lds_frag<(ni) == 0 ? 0 : (ni) == 1 ? B1 : (ni) == 2 ? B2 : B3>(BD[(ni) & 1])
-#define GG_SB __builtin_amdgcn_sched_barrier(0)
-// One MFMA of a K sub-step, preceded by PRE (a load of a later stage, or
-// nothing) and followed by RD (one fragment read of the next sub-step, or
-// nothing); sched_barrier pins the order, so the matrix core has its next
-// MFMA ready while the loads and reads are in flight.
-#define GG_STEP(FA, FB, mi, ni, PRE, RD)                                                                 \
-    PRE;                                                                                                 \
-    GG_MFMA(FA, FB, mi, ni);                                                                             \
-    RD;                                                                                                  \
-    GG_SB;
-// One K sub-step: 16 MFMAs on FA/FB; the 8 fragment reads of the next
-// sub-step into GA/GB (addresses AD/BD) follow the first 8 of them, and
-// L0..L7 (loads of a later stage, or nothing) precede every other MFMA: one
-// 1 KiB load per two MFMAs per wave is what the CU's address unit sustains
-// (about one such load per 16 cycles for the four wavefronts together).
-#define GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, L0, L1, L2, L3, L4, L5, L6, L7)                             \
-    GG_WAIT_FRAGS(FA, FB);                                                                               \
-    GG_SB;                                                                                               \
-    GG_STEP(FA, FB, 0, 0, L0, GG_RD_A(GA, AD, 0))                                                        \
-    GG_STEP(FA, FB, 0, 1, (void)0, GG_RD_A(GA, AD, 1))                                                   \
-    GG_STEP(FA, FB, 0, 2, L1, GG_RD_A(GA, AD, 2))                                                        \
-    GG_STEP(FA, FB, 0, 3, (void)0, GG_RD_A(GA, AD, 3))                                                   \
-    GG_STEP(FA, FB, 1, 0, L2, GG_RD_B(GB, BD, 0))                                                        \
-    GG_STEP(FA, FB, 1, 1, (void)0, GG_RD_B(GB, BD, 1))                                                   \
-    GG_STEP(FA, FB, 1, 2, L3, GG_RD_B(GB, BD, 2))                                                        \
-    GG_STEP(FA, FB, 1, 3, (void)0, GG_RD_B(GB, BD, 3))                                                   \
-    GG_STEP(FA, FB, 2, 0, L4, (void)0)                                                                   \
-    GG_STEP(FA, FB, 2, 1, (void)0, (void)0)                                                              \
-    GG_STEP(FA, FB, 2, 2, L5, (void)0)                                                                   \
-    GG_STEP(FA, FB, 2, 3, (void)0, (void)0)                                                              \
-    GG_STEP(FA, FB, 3, 0, L6, (void)0)                                                                   \
-    GG_STEP(FA, FB, 3, 1, (void)0, (void)0)                                                              \
-    GG_STEP(FA, FB, 3, 2, L7, (void)0)                                                                   \
-    GG_STEP(FA, FB, 3, 3, (void)0, (void)0)
-#define GG_N_ (void)0
-#define GG_SUBSTEP(FA, FB, GA, GB, AD, BD)                                                               \
-    GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_, GG_N_)
-// ... with the 8 A (B) loads of stage LKT into stage buffer LST
-#define GG_SUBSTEP_LA(FA, FB, GA, GB, AD, BD, LKT, LST)                                                  \
-    GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_LOAD_A(LKT, LST, 0), GG_LOAD_A(LKT, LST, 1),                 \
-                 GG_LOAD_A(LKT, LST, 2), GG_LOAD_A(LKT, LST, 3), GG_LOAD_A(LKT, LST, 4),                 \
-                 GG_LOAD_A(LKT, LST, 5), GG_LOAD_A(LKT, LST, 6), GG_LOAD_A(LKT, LST, 7))
-#define GG_SUBSTEP_LB(FA, FB, GA, GB, AD, BD, LKT, LST)                                                  \
-    GG_SUBSTEP_X(FA, FB, GA, GB, AD, BD, GG_LOAD_B(LKT, LST, 0), GG_LOAD_B(LKT, LST, 1),                 \
-                 GG_LOAD_B(LKT, LST, 2), GG_LOAD_B(LKT, LST, 3), GG_LOAD_B(LKT, LST, 4),                 \
-                 GG_LOAD_B(LKT, LST, 5), GG_LOAD_B(LKT, LST, 6), GG_LOAD_B(LKT, LST, 7))
+// B fragment ni's byte offset from fragment 0 (SwiGLU: up fragments 4..7 are
+// the gate fragments' rows + 128)
+#define GK_BOFF(ni) (SWIGLU ? ((ni) & 3) * kFragBytes + ((ni) >> 2) * 128 * kRowBytes : (ni) * kFragBytes)
+#define GK_SB __builtin_amdgcn_sched_barrier(0)
 
     // Decode unit u (from `take`), compute its tile's addressing and issue
-    // the loads of its first stage and the A half of its second (stage
-    // buffers 0 and 1).  Called right after the
-    // previous unit's K loop, so these loads are in flight while that unit's
-    // epilogue runs.  A wave's loads land in issue order, after the previous
-    // unit's last (repeated) loads of the same rows.
+    // the loads of its first two stages (stage buffers 0 and 1).  Called right
+    // after the previous unit's K loop, so these loads are in flight while
+    // that unit's epilogue runs.
     auto setup = [&](int u) __attribute__((always_inline)) {
         u = __builtin_amdgcn_readfirstlane(u);
         if (u < 0) {  // no unit (every queue used up): nothing to decode or load
@@ -402,124 +371,166 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         // first B row of the tile (SwiGLU: first gate row; the up rows are F rows further)
         const int brow0 = SWIGLU ? nt * 128 : nt * kTile;
         // Per-lane byte offsets of the A and B loads (K offset 0) against the
-        // uniform tile bases: 32-bit, so the loads take few registers.
+        // uniform tile bases: 32-bit, so the loads take few registers.  They
+        // are formed from an opaque copy of the lane index, so the compiler
+        // recomputes them per tile instead of holding per-lane constants
+        // across the K loop.
+        int sl = lane;
+        __asm__ volatile("" : "+v"(sl));
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int r = wid * 64 + i * RPL + lrow;  // tile row 0..255
-            const int chunk = lslot ^ swz<SWZ>(r);
+            const int r = wid * 64 + i * RPL + sl / CH;  // tile row 0..255
+            const int chunk = (sl % CH) ^ swz<SWZ>(r);
             const int ar = min(row0 + r, a_end - 1);
             aoff[i] = p.src_map ? (uint32_t)(((size_t)(p.src_map[ar] / p.gk) * K + chunk * 8) * 2)
                                 : (uint32_t)(((size_t)(ar - row0) * K + chunk * 8) * 2);
             int br;
             if (SWIGLU) {
-                const int f = min(nt * 128 + out_col_swiglu(r & 127), p.n_out - 1);
+                const int f = min(nt * 128 + out_col16_swiglu(r & 127), p.n_out - 1);
                 br = r < 128 ? f : p.n_out + f;
             } else {
-                br = min(nt * kTile + out_col(r), p.n_out - 1);
+                br = min(nt * kTile + out_col16(r), p.n_out - 1);
             }
             boff[i] = (uint32_t)(((size_t)(br - brow0) * K + chunk * 8) * 2);
         }
         abase = p.src_map ? (const char*)p.A : (const char*)(p.A + (size_t)row0 * K);
         bbase = (const char*)(p.B + ((size_t)e * p.b_rows + brow0) * K);
-        GG_SB;
-        GG_ISSUE(kb, 0);
+        GK_SB;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) GG_LOAD_A(min(kb + 1, ke - 1), 1, i);
-        GG_SB;
+        for (int i = 0; i < LOADS; ++i) {
+            GK_LOAD_B(kb, 0, i);
+            GK_LOAD_A(kb, 0, i);
+        }
+        if (kb + 1 < ke) {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                GK_LOAD_B(kb + 1, 1, i);
+                GK_LOAD_A(kb + 1, 1, i);
+            }
+        }
+        GK_SB;
     };
 
     setup(unit);
     while (unit >= 0) {
-        // Two LDS stages, software-pipelined across the stage boundary.  A stage
-        // is four 16-deep K sub-steps of 16 MFMAs each; the fragments of
-        // sub-step j+1 are read from LDS while the MFMAs of sub-step j issue.
-        // The one barrier per stage sits before the last sub-step: by then
-        // this wave has read all of stage kt and its loads of stage kt+1 have
-        // landed; once every wave is past it the buffer of stage kt is free.
-        // The loads of stage kt+2 go into it, the A half during the last
-        // sub-step of stage kt and the B half during the first sub-step of
-        // stage kt+1 (so the address unit is never oversubscribed).  Loads
-        // past the end of K repeat the last stage into the free buffer, so
-        // the loop has no branch.  (An L2 prefetch of later stages, one
-        // 4-byte load per row, cost more address-unit time than it saved.)
-        bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+        // Two LDS stage buffers.  Iteration kt (buffer st holds stage kt, the
+        // other buffer stage kt+1, landed or in flight):
+        //   sub-step 0: 64 MFMAs on the fragments fx (K 0..31 of stage kt),
+        //     the 16 fragment reads of K 32..63 into fy under the first 32;
+        //     then each wave has read all of stage kt and its loads of stage
+        //     kt+1 have landed (waitcnt), and past the barrier that holds for
+        //     every wave: buffer st is free and stage kt+1 readable.  The 16
+        //     loads of stage kt+2 into buffer st start there, B (the weights,
+        //     first touched in HBM) before A, one per four MFMAs;
+        //   sub-step 1: 64 MFMAs on fy, the rest of those loads and the 16
+        //     fragment reads of stage kt+1's K 0..31 into fx.
+        // One load per four MFMAs per wave is about what the CU's address unit
+        // sustains for the four wavefronts.  There are no loads past K.
+        bf16x8 fxa[8], fxb[8], fya[8], fyb[8];
         // the unit's first stage landed everywhere; the previous unit's stores retired
         __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        GG_SB;
+        GK_SB;
         if (tid == 0) {  // publish the next unit, take a ticket for the one after
             const int nu = take(tick);
             s_unit = nu;
             tick = nu >= 0 ? ticket() : -1;
         }
-        f32x16 acc[4][4];
+        // The accumulators live in the accumulator registers for the whole tile:
+        // empty asm statements with "a" constraints (at the zeroing and once
+        // per K iteration) keep the register allocator from moving some of
+        // them to VGPRs and copying them around the MFMAs.
+        f32x4 acc[8][8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-        {
-            const uint32_t ad[2] = {a_rd + koff[0][0], a_rd + koff[0][1]};
-            const uint32_t bd[2] = {b_rd + koff[0][0], b_rd + koff[0][1]};
-            GG_RD_A(fa0, ad, 0);
-            GG_RD_A(fa0, ad, 1);
-            GG_RD_A(fa0, ad, 2);
-            GG_RD_A(fa0, ad, 3);
-            GG_RD_B(fb0, bd, 0);
-            GG_RD_B(fb0, bd, 1);
-            GG_RD_B(fb0, bd, 2);
-            GG_RD_B(fb0, bd, 3);
-        }
-        for (int kt = kb; kt < ke; ++kt) {
+            for (int j = 0; j < 8; ++j) __asm__ volatile("" : "=a"(acc[i][j]) : "0"((f32x4){0.f, 0.f, 0.f, 0.f}));
+#define GK_PIN_ACC(I)                                                                                    \
+    __asm__ volatile("" : "+a"(acc[I][0]), "+a"(acc[I][1]), "+a"(acc[I][2]), "+a"(acc[I][3]),            \
+                     "+a"(acc[I][4]), "+a"(acc[I][5]), "+a"(acc[I][6]), "+a"(acc[I][7]))
+        static_for<8>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            fxa[i] = lds_frag<i * kFragBytes>(a_rd + koff0);
+            fxb[i] = lds_frag<GK_BOFF(i)>(b_rd + koff0);
+        });
+#define GK_WAIT_FRAGS(FA, FB)                                                                            \
+    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
+                     : "+v"(FA[0]), "+v"(FA[1]), "+v"(FA[2]), "+v"(FA[3]), "+v"(FA[4]), "+v"(FA[5]),     \
+                       "+v"(FA[6]), "+v"(FA[7]), "+v"(FB[0]), "+v"(FB[1]), "+v"(FB[2]), "+v"(FB[3]),     \
+                       "+v"(FB[4]), "+v"(FB[5]), "+v"(FB[6]), "+v"(FB[7])::"memory")
+        GK_WAIT_FRAGS(fxa, fxb);
+        // One iteration of the K loop; LD: whether it loads stage kt+2 (the
+        // loop is split so that no branch sits between the MFMAs).
+        auto iteration = [&](int kt, auto ld) __attribute__((always_inline)) {
+            constexpr bool LD = decltype(ld)::value;
             const int st = (kt - kb) & 1;
-            const uint32_t so = (uint32_t)st * kStageBytes;
-            GG_SB;
-            {
-                const uint32_t ad[2] = {a_rd + so + koff[1][0], a_rd + so + koff[1][1]};
-                const uint32_t bd[2] = {b_rd + so + koff[1][0], b_rd + so + koff[1][1]};
-                GG_SUBSTEP_LB(fa0, fb0, fa1, fb1, ad, bd, min(kt + 1, ke - 1), st ^ 1)
-            }
-            {
-                const uint32_t ad[2] = {a_rd + so + koff[2][0], a_rd + so + koff[2][1]};
-                const uint32_t bd[2] = {b_rd + so + koff[2][0], b_rd + so + koff[2][1]};
-                GG_SUBSTEP(fa1, fb1, fa0, fb0, ad, bd)
-            }
-            {
-                const uint32_t ad[2] = {a_rd + so + koff[3][0], a_rd + so + koff[3][1]};
-                const uint32_t bd[2] = {b_rd + so + koff[3][0], b_rd + so + koff[3][1]};
-                GG_SUBSTEP(fa0, fb0, fa1, fb1, ad, bd)
-            }
-            // this wave has read all of stage kt and its loads of stage kt+1
-            // landed; past the barrier, the same holds for every wave
-            __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            GG_SB;
-            {
-                const uint32_t nso = so ^ kStageBytes;
-                const uint32_t ad[2] = {a_rd + nso + koff[0][0], a_rd + nso + koff[0][1]};
-                const uint32_t bd[2] = {b_rd + nso + koff[0][0], b_rd + nso + koff[0][1]};
-                GG_SUBSTEP_LA(fa1, fb1, fa0, fb0, ad, bd, min(kt + 2, ke - 1), st)
-            }
-            // the next stage's first fragments landed (they had the last 8
-            // MFMAs to do so); waiting here rather than at the top of the next
-            // iteration leaves no LDS read in flight when the loop ends
-            GG_WAIT_FRAGS(fa0, fb0);
-        }
-        GG_SB;
-#undef GG_LOAD_A
-#undef GG_LOAD_B
-#undef GG_ISSUE
-#undef GG_WAIT_FRAGS
-#undef GG_MFMA
-#undef GG_RD_A
-#undef GG_RD_B
-#undef GG_SB
-#undef GG_STEP
-#undef GG_SUBSTEP_X
-#undef GG_N_
-#undef GG_SUBSTEP
-#undef GG_SUBSTEP_LA
-#undef GG_SUBSTEP_LB
-
+            const uint32_t so = (uint32_t)st * kStageBytes, nso = so ^ kStageBytes;
+            const int lkt = kt + 2;
+            GK_PIN_ACC(0); GK_PIN_ACC(1); GK_PIN_ACC(2); GK_PIN_ACC(3);
+            GK_PIN_ACC(4); GK_PIN_ACC(5); GK_PIN_ACC(6); GK_PIN_ACC(7);
+            // fragment j (0..15: A 0..7, B 0..7) of the K half at KOFF of the stage at byte offset SO
+#define GK_READ(FA, FB, SO, KOFF, j)                                                                     \
+    if constexpr ((j) < 8) FA[(j)] = lds_frag<(j) * kFragBytes>(a_rd + (SO) + (KOFF));                   \
+    else FB[(j) - 8] = lds_frag<GK_BOFF((j) - 8)>(b_rd + (SO) + (KOFF));
+            // load j (0..15: B 0..7, then A 0..7) of stage kt+2 into buffer st
+#define GK_LOAD(j)                                                                                       \
+    if constexpr (LD) {                                                                                  \
+        if constexpr ((j) < 8) GK_LOAD_B(lkt, st, (j));                                                  \
+        else GK_LOAD_A(lkt, st, (j) - 8);                                                                \
+    }
+            GK_SB;
+            // sub-step 0
+            static_for<64>([&](auto mc) __attribute__((always_inline)) {
+                constexpr int m = decltype(mc)::value;
+                if constexpr (m == 40) {
+                    // own reads of stage kt and own loads of stage kt+1 done; then for every wave
+                    __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier"
+                                     : "+v"(fya[0]), "+v"(fya[1]), "+v"(fya[2]), "+v"(fya[3]), "+v"(fya[4]),
+                                       "+v"(fya[5]), "+v"(fya[6]), "+v"(fya[7]), "+v"(fyb[0]), "+v"(fyb[1]),
+                                       "+v"(fyb[2]), "+v"(fyb[3]), "+v"(fyb[4]), "+v"(fyb[5]), "+v"(fyb[6]),
+                                       "+v"(fyb[7])::"memory");
+                    GK_SB;
+                }
+                if constexpr (m >= 40 && (m & 3) == 0) {
+                    GK_LOAD((m - 40) / 4)
+                }
+                acc[m >> 3][m & 7] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(fxa[m >> 3], fxb[m & 7], acc[m >> 3][m & 7], 0, 0, 0);
+                if constexpr (m < 32 && (m & 1) == 0) {
+                    GK_READ(fya, fyb, so, koff1, m / 2)
+                }
+                GK_SB;
+            });
+            // sub-step 1 (after the last stage the reads of "stage kt+1" fetch
+            // unused bytes of the other buffer)
+            static_for<64>([&](auto mc) __attribute__((always_inline)) {
+                constexpr int m = decltype(mc)::value;
+                if constexpr (m < 40 && (m & 3) == 0) {
+                    GK_LOAD(6 + m / 4)
+                }
+                acc[m >> 3][m & 7] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(fya[m >> 3], fyb[m & 7], acc[m >> 3][m & 7], 0, 0, 0);
+                if constexpr (m < 32 && (m & 1) == 1) {
+                    GK_READ(fxa, fxb, nso, koff0, m / 2)
+                }
+                GK_SB;
+            });
+            // the next stage's first fragments landed (waiting here rather than at
+            // the top of the next iteration leaves no LDS read in flight when the
+            // loop ends)
+            GK_WAIT_FRAGS(fxa, fxb);
+#undef GK_READ
+#undef GK_LOAD
+        };
+        int kt = kb;
+        for (; kt + 2 < ke; ++kt) iteration(kt, std::true_type{});
+        for (; kt < ke; ++kt) iteration(kt, std::false_type{});
+        GK_SB;
+#undef GK_LOAD_A
+#undef GK_LOAD_B
+#undef GK_BOFF
+#undef GK_SB
+#undef GK_WAIT_FRAGS
+#undef GK_PIN_ACC
 
         // The next unit (published by thread 0 before this unit's K loop; the
         // barrier makes it visible even when the loop had no stage), its
@@ -542,43 +553,37 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         }
         if (next_unit >= 0) setup(next_unit);
         if (e_valid) {
-        // Epilogue straight from the accumulators (no LDS, so no barrier
-        // before the next tile).  With the column order of the B rows above,
-        // lane l holds, for each of its 16 rows of a 32-row block, adjacent
-        // output columns in its four (SwiGLU: two) fragments: one 8-byte word
-        // of four bf16 (SwiGLU: a 4-byte pair of h), so 32 lanes cover 256
-        // (128) contiguous bytes of a row.  Opaque copies of the tile's first
-        // row and of the lane index: the address arithmetic below then stays
-        // after the K loop (it is not hoisted out of the tile loop, where it
-        // would hold registers).
+        // Epilogue straight from the accumulators.  Lane l holds, in block mi
+        // (16 rows) and slot q, row 16 mi + 4 (l / 16) + q of column l % 16 of
+        // each fragment; with the B row order above those are 8 adjacent
+        // output columns (SwiGLU: 4 h columns).  Opaque copies of the tile's
+        // first row and of the lane index keep the address arithmetic after
+        // the K loop.
         int rbase = e_row0, ln = lane;
         __asm__ volatile("" : "+v"(rbase), "+v"(ln));
-        const int lc = ln & 31;             // this lane's column group
-        const int lr = 4 * (ln >> 5);       // this lane's first row in a 32-row block
+        const int lc = ln & 15;             // this lane's column group
+        const int lr = 4 * (ln >> 4);       // this lane's first row in a 16-row block
         const int rlim = e_row_end - rbase;  // rows of the tile that exist
         const int alim = e_a_end - rbase;    // rows of the tile that are not padding (gather)
-        // Store W[q] (type T) to row 8 (q / 4) + q % 4 past DST (LD elements
-        // per row) for q = 0..15: the lane's rows of the 32-row block starting
-        // at tile row RB0; rows are checked only when the block runs past the
-        // group's end.
-        // RW[q]: the routing weight of the lane's row 8 (q / 4) + q % 4 of
-        // 32-row block MI (1 without weights); row i of the wave's band sits
-        // in lane i / 2, as rwa (even i) or rwb (odd i).
+        // RW[q]: the routing weight of the lane's row q of block MI (1
+        // without weights); row i of the wave's band sits in lane i / 2, as
+        // rwa (even i) or rwb (odd i).
 #define GB_ROW_WEIGHTS(MI, W_)                                                                           \
     if constexpr ((EP & 1) != 0) {                                                                       \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
-            W_[q] = __shfl((q & 1) ? rwb : rwa, ((MI) * 32 + lr + 8 * (q >> 2) + (q & 3)) >> 1, 64);     \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                    \
+            W_[q] = __shfl((q & 1) ? rwb : rwa, ((MI) * 16 + lr + q) >> 1, 64);                          \
     } else {                                                                                             \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q) W_[q] = 1.f;                                      \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) W_[q] = 1.f;                                       \
     }
+// Store W[q] (type T) to row q past DST (LD elements per row) for q = 0..3:
+// the lane's rows of the 16-row block at tile row RB0; rows are checked only
+// when the block runs past the group's end.
 #define GB_STORE_ROWS(T, DST, LD, RB0, W)                                                                \
-    if ((RB0) + 32 <= rlim) {                                                                            \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
-            *(T*)((DST) + (size_t)(8 * (q >> 2) + (q & 3)) * (LD)) = (W)[q];                             \
+    if ((RB0) + 16 <= rlim) {                                                                            \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) *(T*)((DST) + (size_t)q * (LD)) = (W)[q];          \
     } else {                                                                                             \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
-            if ((RB0) + lr + 8 * (q >> 2) + (q & 3) < rlim)                                              \
-                *(T*)((DST) + (size_t)(8 * (q >> 2) + (q & 3)) * (LD)) = (W)[q];                         \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                    \
+            if ((RB0) + lr + q < rlim) *(T*)((DST) + (size_t)q * (LD)) = (W)[q];                         \
     }
 
         if (e_slot >= 0) {
@@ -587,94 +592,112 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             // included; the reduction skips them), in [row][column] order with
             // SwiGLU gate columns 0..127 and up columns 128..255
             float* const pb = p.part + (size_t)e_slot * kTile * kTile;
-#define GB_EPI_PART(MI)                                                                                  \
-    {                                                                                                    \
-        const int rb0 = wm * 128 + (MI) * 32;                                                            \
-        float* const prow = pb + (size_t)(rb0 + lr) * kTile;                                             \
-        if (SWIGLU) {                                                                                    \
-            float2 gw[16], uw[16];                                                                       \
-            _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                             \
-                gw[q] = make_float2(agpr_read(acc[MI][0][q]), agpr_read(acc[MI][1][q]));                 \
-                uw[q] = make_float2(agpr_read(acc[MI][2][q]), agpr_read(acc[MI][3][q]));                 \
-            }                                                                                            \
-            _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                             \
-                float* const d = prow + (size_t)(8 * (q >> 2) + (q & 3)) * kTile + wn * 64 + 2 * lc;     \
-                *(float2*)d = gw[q];                                                                     \
-                *(float2*)(d + 128) = uw[q];                                                             \
-            }                                                                                            \
-        } else {                                                                                         \
-            float4 w[16];                                                                                \
-            _Pragma("unroll") for (int q = 0; q < 16; ++q)                                               \
-                w[q] = make_float4(agpr_read(acc[MI][0][q]), agpr_read(acc[MI][1][q]),                   \
-                                   agpr_read(acc[MI][2][q]), agpr_read(acc[MI][3][q]));                  \
-            _Pragma("unroll") for (int q = 0; q < 16; ++q)                                               \
-                *(float4*)(prow + (size_t)(8 * (q >> 2) + (q & 3)) * kTile + wn * 128 + 4 * lc) = w[q];  \
-        }                                                                                                \
-    }                                                                                                    \
-    __builtin_amdgcn_sched_barrier(0);
-            GB_EPI_PART(0) GB_EPI_PART(1) GB_EPI_PART(2) GB_EPI_PART(3)
-#undef GB_EPI_PART
-        } else if (SWIGLU) {
+            static_for<8>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int mi = decltype(ic)::value;
+                const int rb0 = wm * 128 + mi * 16;
+                float* const prow = pb + (size_t)(rb0 + lr) * kTile;
+                if constexpr (SWIGLU) {
+                    float4 gw[4], uw[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        gw[q] = make_float4(agpr_read(acc[mi][0][q]), agpr_read(acc[mi][1][q]),
+                                            agpr_read(acc[mi][2][q]), agpr_read(acc[mi][3][q]));
+                        uw[q] = make_float4(agpr_read(acc[mi][4][q]), agpr_read(acc[mi][5][q]),
+                                            agpr_read(acc[mi][6][q]), agpr_read(acc[mi][7][q]));
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float* const d = prow + (size_t)q * kTile + wn * 64 + 4 * lc;
+                        *(float4*)d = gw[q];
+                        *(float4*)(d + 128) = uw[q];
+                    }
+                } else {
+                    float4 w0[4], w1[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        w0[q] = make_float4(agpr_read(acc[mi][0][q]), agpr_read(acc[mi][1][q]),
+                                            agpr_read(acc[mi][2][q]), agpr_read(acc[mi][3][q]));
+                        w1[q] = make_float4(agpr_read(acc[mi][4][q]), agpr_read(acc[mi][5][q]),
+                                            agpr_read(acc[mi][6][q]), agpr_read(acc[mi][7][q]));
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float* const d = prow + (size_t)q * kTile + wn * 128 + 8 * lc;
+                        *(float4*)d = w0[q];
+                        *(float4*)(d + 4) = w1[q];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        } else if constexpr (SWIGLU) {
             uint16_t* const cbase = p.C + (size_t)rbase * p.n_out;
             uint16_t* const sbase = p.stash ? p.stash + (size_t)rbase * 2 * p.n_out : nullptr;
-            const int f = e_nt * 128 + wn * 64 + 2 * lc;  // this lane's h columns f, f + 1
-#define GB_EPI_SW(MI)                                                                                    \
-    {                                                                                                    \
-        const int rb0 = wm * 128 + (MI) * 32;                                                            \
-        uint32_t hw[16];                                                                                 \
-        float rw[16];                                                                                    \
-        GB_ROW_WEIGHTS(MI, rw)                                                                           \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                                 \
-            float g0 = agpr_read(acc[MI][0][q]), g1 = agpr_read(acc[MI][1][q]);                          \
-            float u0 = agpr_read(acc[MI][2][q]), u1 = agpr_read(acc[MI][3][q]);                          \
-            if constexpr ((EP & 2) != 0) {                                                               \
-                g0 = fminf(g0, p.lim);                                                                   \
-                g1 = fminf(g1, p.lim);                                                                   \
-                u0 = fminf(fmaxf(u0, -p.lim), p.lim);                                                    \
-                u1 = fminf(fmaxf(u1, -p.lim), p.lim);                                                    \
-            }                                                                                            \
-            hw[q] = pack_bf16x2(silu(g0) * u0 * rw[q], silu(g1) * u1 * rw[q]);                           \
-            if (rb0 + lr + 8 * (q >> 2) + (q & 3) >= alim) hw[q] = 0; /* gather: padding rows */         \
-        }                                                                                                \
-        if (f < p.n_out) {                                                                               \
-            uint16_t* const dst = cbase + (size_t)(rb0 + lr) * p.n_out + f;                              \
-            GB_STORE_ROWS(uint32_t, dst, p.n_out, rb0, hw)                                               \
-            if (sbase) {                                                                                 \
-                uint32_t gw[16], uw[16];                                                                 \
-                _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                         \
-                    gw[q] = pack_bf16x2(agpr_read(acc[MI][0][q]), agpr_read(acc[MI][1][q]));             \
-                    uw[q] = pack_bf16x2(agpr_read(acc[MI][2][q]), agpr_read(acc[MI][3][q]));             \
-                }                                                                                        \
-                uint16_t* const gd = sbase + (size_t)(rb0 + lr) * 2 * p.n_out + f;                       \
-                GB_STORE_ROWS(uint32_t, gd, 2 * p.n_out, rb0, gw)                                        \
-                uint16_t* const ud = gd + p.n_out;                                                       \
-                GB_STORE_ROWS(uint32_t, ud, 2 * p.n_out, rb0, uw)                                        \
-            }                                                                                            \
-        }                                                                                                \
-    }                                                                                                    \
-    __builtin_amdgcn_sched_barrier(0);
-            GB_EPI_SW(0) GB_EPI_SW(1) GB_EPI_SW(2) GB_EPI_SW(3)
-#undef GB_EPI_SW
+            const int f = e_nt * 128 + wn * 64 + 4 * lc;  // this lane's h columns f .. f + 3
+            static_for<8>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int mi = decltype(ic)::value;
+                const int rb0 = wm * 128 + mi * 16;
+                uint2 hw[4];
+                float rw[4];
+                GB_ROW_WEIGHTS(mi, rw)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float g[4], u[4], hv[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        g[c] = agpr_read(acc[mi][c][q]);
+                        u[c] = agpr_read(acc[mi][4 + c][q]);
+                        if constexpr ((EP & 2) != 0) {
+                            g[c] = fminf(g[c], p.lim);
+                            u[c] = fminf(fmaxf(u[c], -p.lim), p.lim);
+                        }
+                        hv[c] = silu(g[c]) * u[c] * rw[q];
+                    }
+                    hw[q] = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+                    if (rb0 + lr + q >= alim) hw[q] = make_uint2(0u, 0u);  // gather: padding rows
+                }
+                if (f < p.n_out) {
+                    uint16_t* const dst = cbase + (size_t)(rb0 + lr) * p.n_out + f;
+                    GB_STORE_ROWS(uint2, dst, p.n_out, rb0, hw)
+                    if (sbase) {
+                        uint2 gw[4], uw[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            gw[q] = make_uint2(pack_bf16x2(agpr_read(acc[mi][0][q]), agpr_read(acc[mi][1][q])),
+                                               pack_bf16x2(agpr_read(acc[mi][2][q]), agpr_read(acc[mi][3][q])));
+                            uw[q] = make_uint2(pack_bf16x2(agpr_read(acc[mi][4][q]), agpr_read(acc[mi][5][q])),
+                                               pack_bf16x2(agpr_read(acc[mi][6][q]), agpr_read(acc[mi][7][q])));
+                        }
+                        uint16_t* const gd = sbase + (size_t)(rb0 + lr) * 2 * p.n_out + f;
+                        GB_STORE_ROWS(uint2, gd, 2 * p.n_out, rb0, gw)
+                        uint16_t* const ud = gd + p.n_out;
+                        GB_STORE_ROWS(uint2, ud, 2 * p.n_out, rb0, uw)
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
         } else {
             uint16_t* const cbase = p.C + (size_t)rbase * p.n_out;
-            const int n = e_nt * kTile + wn * 128 + 4 * lc;  // this lane's columns n .. n + 3
-#define GB_EPI_DN(MI)                                                                                    \
-    {                                                                                                    \
-        const int rb0 = wm * 128 + (MI) * 32;                                                            \
-        uint2 w[16];                                                                                     \
-        float rw[16];                                                                                    \
-        GB_ROW_WEIGHTS(MI, rw)                                                                           \
-        _Pragma("unroll") for (int q = 0; q < 16; ++q)                                                   \
-            w[q] = make_uint2(pack_bf16x2(agpr_read(acc[MI][0][q]) * rw[q], agpr_read(acc[MI][1][q]) * rw[q]), \
-                              pack_bf16x2(agpr_read(acc[MI][2][q]) * rw[q], agpr_read(acc[MI][3][q]) * rw[q])); \
-        if (n < p.n_out) {                                                                               \
-            uint16_t* const dst = cbase + (size_t)(rb0 + lr) * p.n_out + n;                              \
-            GB_STORE_ROWS(uint2, dst, p.n_out, rb0, w)                                                   \
-        }                                                                                                \
-    }                                                                                                    \
-    __builtin_amdgcn_sched_barrier(0);
-            GB_EPI_DN(0) GB_EPI_DN(1) GB_EPI_DN(2) GB_EPI_DN(3)
-#undef GB_EPI_DN
+            const int n = e_nt * kTile + wn * 128 + 8 * lc;  // this lane's columns n .. n + 7
+            static_for<8>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int mi = decltype(ic)::value;
+                const int rb0 = wm * 128 + mi * 16;
+                uint4 w[4];
+                float rw[4];
+                GB_ROW_WEIGHTS(mi, rw)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v[8];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) v[c] = agpr_read(acc[mi][c][q]) * rw[q];
+                    w[q] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                      pack_bf16x2(v[6], v[7]));
+                }
+                if (n < p.n_out) {
+                    uint16_t* const dst = cbase + (size_t)(rb0 + lr) * p.n_out + n;
+                    GB_STORE_ROWS(uint4, dst, p.n_out, rb0, w)
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
         }
 #undef GB_STORE_ROWS
 #undef GB_ROW_WEIGHTS
