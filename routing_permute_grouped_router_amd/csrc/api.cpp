@@ -238,11 +238,9 @@ moe_status permute_checked(const moe_config* cfg, const void* x, const uint8_t* 
     }
     if ((st = check_ws(c, ws, ws_bytes))) return st;
     if (!launch) return MOE_OK;
-    hipStream_t s = as_stream(stream);
-    if ((st = hip_status(launch_group(c, idx, counts, offsets, row_map, src_map, err, (int32_t*)ws, s), "moe_permute")))
-        return st;
-    if (!xp) return MOE_OK;
-    return hip_status(launch_permute_rows(c, x, x_scale, row_map, counts, offsets, xp, xp_scale, s), "moe_permute");
+    return hip_status(launch_group(c, idx, x, x_scale, xp, xp_scale, counts, offsets, row_map, src_map, err,
+                                   (int32_t*)ws, as_stream(stream)),
+                      "moe_permute");
 }
 
 moe_status combine_checked(const moe_config* cfg, const void* yp, const int32_t* row_map, const float* w, void* y,

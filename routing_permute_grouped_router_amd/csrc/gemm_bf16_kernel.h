@@ -194,6 +194,10 @@ __device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+#ifndef GK_BARRIER_AT
+#define GK_BARRIER_AT 40
+#endif
+
 // 16x16x32 fragments and accumulators.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -241,6 +245,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     constexpr int STAGE_ELEMS = kTile * BK; // one operand of one stage
     constexpr uint32_t kRowBytes = BK * 2;
     constexpr uint32_t kFragBytes = 16 * kRowBytes;  // one 16-row fragment
+    // The stage's barrier sits before MFMA kBar of its first sub-step; the 16
+    // loads of stage k+2 follow it, one per four MFMAs (kLoads0 of them in the
+    // first sub-step, the rest at the start of the second).
+    constexpr int kBar = GK_BARRIER_AT;
+    constexpr int kLoads0 = (64 - kBar + 3) / 4;
 
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][STAGE_ELEMS];
     __shared__ int32_t pre[kMaxExperts + 1];
@@ -481,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             // sub-step 0
             static_for<64>([&](auto mc) __attribute__((always_inline)) {
                 constexpr int m = decltype(mc)::value;
-                if constexpr (m == 40) {
+                if constexpr (m == kBar) {
                     // own reads of stage kt and own loads of stage kt+1 done; then for every wave
                     __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier"
                                      : "+v"(fya[0]), "+v"(fya[1]), "+v"(fya[2]), "+v"(fya[3]), "+v"(fya[4]),
@@ -490,8 +499,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
                                        "+v"(fyb[7])::"memory");
                     GK_SB;
                 }
-                if constexpr (m >= 40 && (m & 3) == 0) {
-                    GK_LOAD((m - 40) / 4)
+                if constexpr (m >= kBar && ((m - kBar) & 3) == 0) {
+                    GK_LOAD((m - kBar) / 4)
                 }
                 acc[m >> 3][m & 7] =
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(fxa[m >> 3], fxb[m & 7], acc[m >> 3][m & 7], 0, 0, 0);
@@ -504,8 +513,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             // unused bytes of the other buffer)
             static_for<64>([&](auto mc) __attribute__((always_inline)) {
                 constexpr int m = decltype(mc)::value;
-                if constexpr (m < 40 && (m & 3) == 0) {
-                    GK_LOAD(6 + m / 4)
+                if constexpr ((m & 3) == 0 && m / 4 < 16 - kLoads0) {
+                    GK_LOAD(kLoads0 + m / 4)
                 }
                 acc[m >> 3][m & 7] =
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(fya[m >> 3], fyb[m & 7], acc[m >> 3][m & 7], 0, 0, 0);

@@ -49,15 +49,12 @@ moe_status set_error(moe_status s, const char* fmt, ...);
 // the API layer.
 hipError_t launch_route(const moe_config& c, const float* logits, int32_t* idx, float* w, hipStream_t s);
 
-// Grouping.  chunk_tokens(T,E) tokens per counting chunk; ws holds
-// n_chunks(T,E) * E int32.
-int group_chunk_tokens(int T, int E);
+// Grouping and permutation (xp null: the grouping only).  ws holds
+// group_n_chunks(T, E) * E int32 (per-chunk expert counts).
 int group_n_chunks(int T, int E);
-hipError_t launch_group(const moe_config& c, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                        int32_t* row_map, int32_t* src_map, int32_t* err, int32_t* ws, hipStream_t s);
-hipError_t launch_permute_rows(const moe_config& c, const void* x, const uint8_t* x_scale, const int32_t* row_map,
-                               const int32_t* counts, const int32_t* offsets, void* xp, uint8_t* xp_scale,
-                               hipStream_t s);
+hipError_t launch_group(const moe_config& c, const int32_t* idx, const void* x, const uint8_t* x_scale, void* xp,
+                        uint8_t* xp_scale, int32_t* counts, int32_t* offsets, int32_t* row_map, int32_t* src_map,
+                        int32_t* err, int32_t* ws, hipStream_t s);
 
 hipError_t launch_combine(const moe_config& c, const void* yp, const int32_t* row_map, const float* w, void* y,
                           hipStream_t s);
