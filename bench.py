@@ -1,15 +1,19 @@
 """Benchmark of the MoE FFN hot path on one MI355X.
 
 One step = one pass of the whole forward hot path (route -> permute -> grouped
-gate/up GEMM + SwiGLU -> grouped down GEMM -> top-k combine, the fused
-moe_forward call) over one batch of seeded synthetic input already resident in
-HBM.  Default workload: the Mixtral-shaped layer (T=8192, H=4096, F=14336,
-E=8, top-2 softmax, bf16 with fp32 accumulation).  With --backward the step
-also runs the FFN backward (skewed workload).
+gate/up GEMM + SwiGLU -> grouped down GEMM -> top-k combine: the calls whose
+kernels moe_forward launches, issued one by one with a HIP event after each)
+over one batch of seeded synthetic input already resident in HBM.  Default
+workload: the Mixtral-shaped layer (T=8192, H=4096, F=14336, E=8, top-2
+softmax, bf16 with fp32 accumulation).  The skewed workload's step also runs
+the FFN backward.
 
-Prints one JSON line: tokens/s of the layer, per-kernel times measured with
-HIP events on the launch stream, the roofline of the dominant kernel (the
-grouped gate/up GEMM) and the CPU oracle timed on a bounded token sample.
+Prints one JSON line: tokens/s of the layer over the K timed steps, each
+kernel's duration in those steps (mean, median, p10, p90; HIP events on the
+launch stream), route / permute / combine again with cold caches (a 512 MiB
+write before each of 50 calls), a route sweep over T, the roofline of the
+dominant kernel (the grouped gate/up GEMM) and the CPU oracle timed on a
+bounded token sample.
 """
 from __future__ import annotations
 
@@ -36,6 +40,8 @@ def parse():
     # the clocks settle over the first ~100 steps: fewer warm-up steps
     # measured the fine-grained step ~7 % slower
     p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--flush-iters", type=int, default=50,
+                   help="calls of each bandwidth kernel timed with cold caches (512 MiB flush before each)")
     p.add_argument("--workload", default="mixtral_bf16")
     p.add_argument("--no-variants", action="store_true",
                    help="skip the variant timings (gather form, weight placements, clamp): counter passes")
@@ -175,63 +181,45 @@ def main():
     bwd = moe.alloc_backward(cfg) if s.backward else None
     dy = up(w.dy(), "bf16" if s.dtype != "f32" else "f32") if s.backward else None
     stream = torch.cuda.current_stream()
+    g = {kk: v for kk, v in scales.items()}
 
-    def step():
-        moe.moe_forward(cfg, logits, x, w1, w2, buf, **scales)
-        if s.backward:
-            moe.moe_backward(cfg, dy, w1, w2, buf, bwd)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.time()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.time() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
-
-    # Per-kernel durations: the same step issued call by call, events between
-    # the calls on the launch stream.
+    # One step: the calls of the forward (and, for the training workload, of
+    # the backward) issued one by one on the launch stream -- the kernels
+    # moe_forward / moe_backward launch -- with a HIP event after each call,
+    # so every kernel's duration is measured inside the timed region.
     names = ["route", "permute", "swiglu_gemm", "down_gemm", "combine"]
     if s.backward:
         names += ["combine_bwd", "down_bwd", "swiglu_bwd", "permute_bwd"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    acc = {n: 0.0 for n in names}
-    g = {k: v for k, v in scales.items()}
 
-    def staged():
-        ev[0].record(stream)
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        rec(0)
         moe.moe_route(cfg, logits, buf["idx"], buf["w"])
-        ev[1].record(stream)
+        rec(1)
         moe.moe_permute(cfg, x, buf["idx"], buf["xp"], buf["counts"], buf["offsets"], buf["row_map"],
                         buf["src_map"], buf["ws"], x_scale=g.get("x_scale"), xp_scale=buf.get("xp_scale"),
                         err=buf["err"])
-        ev[2].record(stream)
+        rec(2)
         moe.moe_grouped_swiglu_gemm(cfg, buf["xp"], w1, buf["offsets"], buf["h"], buf["ws"], xp_scale=buf.get("xp_scale"),
                                     w1_scale=g.get("w1_scale"), h_scale=buf.get("h_scale"),
                                     gu_stash=buf.get("gu_stash"))
-        ev[3].record(stream)
+        rec(3)
         moe.moe_grouped_down_gemm(cfg, buf["h"], w2, buf["offsets"], buf["yp"], buf["ws"], h_scale=buf.get("h_scale"),
                                   w2_scale=g.get("w2_scale"))
-        ev[4].record(stream)
+        rec(4)
         moe.moe_combine(cfg, buf["yp"], buf["row_map"], buf["w"], buf["y"])
-        ev[5].record(stream)
+        rec(5)
         if s.backward:
             moe.moe_combine_bwd(cfg, dy, buf["row_map"], buf["src_map"], buf["offsets"], buf["w"], bwd["dyp"])
-            ev[6].record(stream)
+            rec(6)
             moe.moe_grouped_down_bwd(cfg, bwd["dyp"], w2, buf["h"], buf["gu_stash"], buf["offsets"], bwd["dgu"],
                                      bwd["dw2"], bwd["ws"])
-            ev[7].record(stream)
+            rec(7)
             moe.moe_grouped_swiglu_bwd(cfg, bwd["dgu"], w1, buf["xp"], buf["offsets"], bwd["dxp"], bwd["dw1"],
                                        bwd["ws"])
-            ev[8].record(stream)
+            rec(8)
             moe.moe_permute_bwd(cfg, bwd["dxp"], buf["row_map"], bwd["dx"])
-            ev[9].record(stream)
+            rec(9)
 
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -241,14 +229,73 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    staged()
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    for _ in range(args.steps):
-        staged()
+    t_wall = time.time()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_wall = time.time() - t_wall
+    ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
+    per_step = sorted(e[0].elapsed_time(e[-1]) for e in evs)
+    kern_samples = {n: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, n in enumerate(names)}
+    kern_ms = {n: sum(v) / len(v) for n, v in kern_samples.items()}
+
+    def pct(v, q):
+        return v[min(len(v) - 1, int(q * len(v)))]
+
+    # Bandwidth kernels with cold caches: a 512 MiB write (outside the event
+    # window) evicts L2 and the 256 MiB MALL before each of `flush_iters`
+    # calls, so route, permute and combine read their inputs from HBM.
+    flushbuf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    bw_calls = {
+        "route": lambda: moe.moe_route(cfg, logits, buf["idx"], buf["w"]),
+        "permute": lambda: moe.moe_permute(cfg, x, buf["idx"], buf["xp"], buf["counts"], buf["offsets"],
+                                           buf["row_map"], buf["src_map"], buf["ws"], x_scale=g.get("x_scale"),
+                                           xp_scale=buf.get("xp_scale"), err=buf["err"]),
+        "combine": lambda: moe.moe_combine(cfg, buf["yp"], buf["row_map"], buf["w"], buf["y"]),
+    }
+    cold = {}
+    for n, f in bw_calls.items():
+        samples = []
+        for it in range(args.flush_iters):
+            flushbuf.fill_(it & 255)
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            f()
+            a1.record(stream)
+            samples.append((a0, a1))
         torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
-    kern_ms = {n: acc[n] / args.steps for n in names}
+        cold[n] = sorted(a0.elapsed_time(a1) for a0, a1 in samples)
+
+    # Route at growing T (E and k of this workload; logits N(0,1)): where the
+    # kernel leaves the launch-latency regime and what bandwidth it reaches.
+    route_sweep = []
+    for Ts in (s.T, 65536, 262144, 1048576):
+        cs = dataclasses.replace(cfg, T=Ts)
+        lg = torch.randn(Ts, s.E, device=dev)
+        ix = torch.empty(Ts, s.k, dtype=torch.int32, device=dev)
+        wt = torch.empty(Ts, s.k, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            moe.moe_route(cs, lg, ix, wt)
+        samples = []
+        for it in range(20):
+            flushbuf.fill_(it & 255)
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            moe.moe_route(cs, lg, ix, wt)
+            a1.record(stream)
+            samples.append((a0, a1))
+        torch.cuda.synchronize()
+        v = sorted(a0.elapsed_time(a1) for a0, a1 in samples)
+        nb = Ts * s.E * 4 + Ts * s.k * 8
+        route_sweep.append({"T": Ts, "ms": round(pct(v, 0.5), 4), "gbs": round(nb / (pct(v, 0.5) * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(nb / (pct(v, 0.5) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+        del lg, ix, wt
+    del flushbuf
+
     if s.backward:
         # the routing backward (gradients of the top-k weights and router
         # logits): timed on its own, outside the step
@@ -332,12 +379,20 @@ def main():
     kern = {}
     for n in names:
         d = {"ms": round(kern_ms[n], 4)}
+        if n in kern_samples:  # in-step durations over the K timed steps
+            v = kern_samples[n]
+            d.update(ms_median=round(pct(v, 0.5), 4), ms_p10=round(pct(v, 0.1), 4), ms_p90=round(pct(v, 0.9), 4))
         if n in flops:
             tf = flops[n] / (kern_ms[n] * 1e-3) / 1e12
             d.update(tflops=round(tf, 1), frac_mfma=round(tf / peak_mm, 4))
         if n in bytes_:
             gbs = bytes_[n] / (kern_ms[n] * 1e-3) / 1e9
             d.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        if n in cold:  # caches flushed before each call: inputs from HBM
+            v = cold[n]
+            gc = bytes_[n] / (pct(v, 0.5) * 1e-3) / 1e9
+            d["cold"] = {"iters": len(v), "ms_median": round(pct(v, 0.5), 4), "ms_p10": round(pct(v, 0.1), 4),
+                         "ms_p90": round(pct(v, 0.9), 4), "gbs": round(gc, 1), "frac_hbm": round(gc / PEAK_HBM_GBS, 4)}
         kern[n] = d
 
     traffic = None
@@ -416,7 +471,10 @@ def main():
         "config": {"workload": s.name, "T": T, "H": H, "F": F, "E": E, "k": k, "score": s.score,
                    "renorm": s.renorm, "storage": s.dtype, "accumulate": "f32", "backward": s.backward,
                    "parallelism": "single GPU"},
+        "step_ms": {"median": round(pct(per_step, 0.5), 4), "p10": round(pct(per_step, 0.1), 4),
+                    "p90": round(pct(per_step, 0.9), 4)},
         "kernels": kern,
+        "route_sweep": route_sweep,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "variants": variants,
