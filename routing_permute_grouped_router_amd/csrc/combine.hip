@@ -91,31 +91,43 @@ __device__ __forceinline__ void gather_rows(const int32_t* __restrict__ row_map,
 
 // y[t] = round(sum_j w[t,j] * Yp[row_map[t,j]]); one block per token.  w null:
 // the weights were applied in an expert epilogue, the routes are summed.
-template <bool F32, int G>
+template <bool F32, int G, bool TWO>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yp, const int32_t* __restrict__ row_map,
                                                       const float* __restrict__ w, int k, int vec_per_row,
                                                       int64_t n_rows, void* __restrict__ y) {
     using V = Vec<F32>;
     const int64_t t = blockIdx.x;
-    for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
-        float acc[V::N];
+    // TWO (rows longer than the block): two vectors of the row per thread at
+    // a time (columns c and c + blockDim), so 2 G row loads are in flight per
+    // lane; otherwise one (fewer registers, more blocks resident)
+    for (int c0 = threadIdx.x; c0 < vec_per_row; c0 += (TWO ? 2 : 1) * blockDim.x) {
+        const int c1 = c0 + blockDim.x;
+        const bool two = TWO && c1 < vec_per_row;
+        float acc0[V::N], acc1[V::N];
 #pragma unroll
-        for (int a = 0; a < V::N; ++a) acc[a] = 0.f;
+        for (int a = 0; a < V::N; ++a) acc0[a] = acc1[a] = 0.f;
         for (int j0 = 0; j0 < k; j0 += G) {
             int32_t r[G];
             bool ok[G];
-            float v[G][V::N];
+            float v0[G][V::N], v1[G][V::N];
             gather_rows<G>(row_map, t, k, j0, n_rows, r, ok);
 #pragma unroll
-            for (int g = 0; g < G; ++g) V::template load<true>(yp, (int64_t)r[g] * vec_per_row + c, v[g]);
+            for (int g = 0; g < G; ++g) {
+                V::template load<true>(yp, (int64_t)r[g] * vec_per_row + c0, v0[g]);
+                if (two) V::template load<true>(yp, (int64_t)r[g] * vec_per_row + c1, v1[g]);
+            }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const float wt = ok[g] ? (w ? w[t * k + j0 + g] : 1.f) : 0.f;
 #pragma unroll
-                for (int a = 0; a < V::N; ++a) acc[a] = ok[g] ? fmaf(wt, v[g][a], acc[a]) : acc[a];
+                for (int a = 0; a < V::N; ++a) {
+                    acc0[a] = ok[g] ? fmaf(wt, v0[g][a], acc0[a]) : acc0[a];
+                    acc1[a] = ok[g] ? fmaf(wt, v1[g][a], acc1[a]) : acc1[a];
+                }
             }
         }
-        V::store(y, t * vec_per_row + c, acc);
+        V::store(y, t * vec_per_row + c0, acc0);
+        if (two) V::store(y, t * vec_per_row + c1, acc1);
     }
 }
 
@@ -210,6 +222,16 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const void* __restrict
         else KERNEL<F32, 8><<<grid, block, 0, s>>>(__VA_ARGS__);                                         \
     } while (0)
 
+template <bool F32, bool TWO>
+hipError_t combine_t(int k, int T, int b, hipStream_t s, const void* yp, const int32_t* row_map, const float* w,
+                     int vpr, int64_t R_cap, void* y) {
+    if (k <= 1) combine_kernel<F32, 1, TWO><<<T, b, 0, s>>>(yp, row_map, w, k, vpr, R_cap, y);
+    else if (k <= 2) combine_kernel<F32, 2, TWO><<<T, b, 0, s>>>(yp, row_map, w, k, vpr, R_cap, y);
+    else if (k <= 4) combine_kernel<F32, 4, TWO><<<T, b, 0, s>>>(yp, row_map, w, k, vpr, R_cap, y);
+    else combine_kernel<F32, 8, TWO><<<T, b, 0, s>>>(yp, row_map, w, k, vpr, R_cap, y);
+    return hipGetLastError();
+}
+
 int block_for(int vec_per_row) {
     int b = 64;
     while (b < vec_per_row && b < 256) b *= 2;
@@ -245,11 +267,16 @@ hipError_t launch_combine(const moe_config& c, const void* yp, const int32_t* ro
     const int64_t R_cap = (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1);
     const bool f32 = c.dtype == MOE_F32;
     const int vpr = c.H / (f32 ? 4 : 8);
-    if (f32)
-        MOE_GATHER_LAUNCH(combine_kernel, true, c.k, c.T, block_for(vpr), s, yp, row_map, w, c.k, vpr, R_cap, y);
-    else
-        MOE_GATHER_LAUNCH(combine_kernel, false, c.k, c.T, block_for(vpr), s, yp, row_map, w, c.k, vpr, R_cap, y);
-    return hipGetLastError();
+    const int b = block_for(vpr);
+    // two vectors per thread pay off for short top-k only (with k = 8 the
+    // doubled registers cost more resident blocks than the loads gain)
+    const bool two = vpr > b && c.k <= 4;
+    if (f32) {
+        if (two) return combine_t<true, true>(c.k, c.T, b, s, yp, row_map, w, vpr, R_cap, y);
+        return combine_t<true, false>(c.k, c.T, b, s, yp, row_map, w, vpr, R_cap, y);
+    }
+    if (two) return combine_t<false, true>(c.k, c.T, b, s, yp, row_map, w, vpr, R_cap, y);
+    return combine_t<false, false>(c.k, c.T, b, s, yp, row_map, w, vpr, R_cap, y);
 }
 
 hipError_t launch_combine_bwd(const moe_config& c, const void* dy, const int32_t* row_map, const int32_t* src_map,
