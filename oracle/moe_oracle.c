@@ -277,24 +277,37 @@ static void or_round_trip_row(int fmt, double* v, int64_t n) {
  * Weights: softmax: p = exp(l - max) / sum_e exp(l_e - max) over all E
  * experts; with renorm, w_j = p_j / (sum_j p_j + 1e-20).  sigmoid:
  * s = 1 / (1 + exp(-l)), w_j = s_j / (sum_j s_j + 1e-20) (always normalised).
+ *
+ * Optional selection-only expert bias ([TE-EP] commit messages: the router's
+ * expert routing bias, "use_expert_routing_bias", with a sigmoid config that
+ * uses a strong bias, and a zero bias that collapses to no bias).  The pages
+ * give no formula; here the bias b_e shifts the selection key of expert e to
+ * the float32 sum key_e = fl32(l_e + b_e), and the k picks are the largest
+ * keys (ties to the lower index).  The weights above use the unbiased logits
+ * of the picked experts, so the bias changes which experts are chosen, never
+ * how the chosen ones are weighted.  bias NULL: key = logit.
  * Returns 0, or 1 on bad sizes.
  */
-int or_route(int T, int E, int k, int score, int renorm, const float* logits, int32_t* idx, float* w) {
+int or_route_biased(int T, int E, int k, int score, int renorm, const float* logits, const float* bias,
+                    int32_t* idx, float* w) {
     if (T < 0 || E <= 0 || k <= 0 || k > E) return 1;
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         const float* l = logits + (int64_t)t * E;
         unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+        float* key = (float*)malloc(sizeof(float) * (size_t)E);
+        for (int e = 0; e < E; ++e) key[e] = bias ? (float)(l[e] + bias[e]) : l[e];
         int32_t* sel = idx + (int64_t)t * k;
         for (int j = 0; j < k; ++j) {
             int best = -1;
             for (int e = 0; e < E; ++e) {
                 if (taken[e]) continue;
-                if (best < 0 || l[e] > l[best]) best = e;
+                if (best < 0 || key[e] > key[best]) best = e;
             }
             taken[best] = 1;
             sel[j] = best;
         }
+        free(key);
         free(taken);
         double* sc = (double*)malloc(sizeof(double) * (size_t)k);
         double sum_sel = 0.0;
@@ -319,6 +332,10 @@ int or_route(int T, int E, int k, int score, int renorm, const float* logits, in
         free(sc);
     }
     return 0;
+}
+
+int or_route(int T, int E, int k, int score, int renorm, const float* logits, int32_t* idx, float* w) {
+    return or_route_biased(T, E, k, score, renorm, logits, NULL, idx, w);
 }
 
 /* ------------------------------------------------------------------------ */

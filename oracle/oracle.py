@@ -55,6 +55,7 @@ def _load():
         "or_double_from_e4m3_array": (None, [P, P, I64]),
         "or_mx_quantize_f32": (I32, [P, I64, I64, P, P]),
         "or_route": (I32, [I32, I32, I32, I32, I32, P, P, P]),
+        "or_route_biased": (I32, [I32, I32, I32, I32, I32, P, P, P, P]),
         "or_group": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P]),
         "or_permute": (None, [I32, I32, I64, I64, P, P, P]),
         "or_forward_tokens": (I32, [I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P,
@@ -164,12 +165,17 @@ def decode(fmt: str, data, scale=None) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- the path
-def route(logits, k: int, score: str = "softmax", renorm: bool = False):
+def route(logits, k: int, score: str = "softmax", renorm: bool = False, bias=None):
+    """Top-k routing (or_route_biased): bias (optional, float32 [E]) shifts
+    only the selection key, key = fl32(logit + bias); the weights use the
+    unbiased logits."""
     lg = _c(logits, np.float32)
     T, E = lg.shape
     idx = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float32)
-    if _load().or_route(T, E, k, SCORE[score], int(renorm), lg.ctypes.data, idx.ctypes.data, w.ctypes.data):
+    b = None if bias is None else _c(np.asarray(bias, np.float32).reshape(E), np.float32)
+    if _load().or_route_biased(T, E, k, SCORE[score], int(renorm), lg.ctypes.data, _p(b), idx.ctypes.data,
+                               w.ctypes.data):
         raise ValueError("bad routing sizes")
     return idx, w
 

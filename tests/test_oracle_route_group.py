@@ -155,3 +155,62 @@ def test_permute_then_combine_identity():
         assert np.all(xp[pad] == 0)
         y = orc.combine(xp, row_map, np.ones((T, k), np.float32), fmt)
         assert np.array_equal(orc.decode(fmt, y), k * orc.decode(fmt, x))
+
+
+# ---- selection-only expert bias: key = fl32(logit + bias), weights unbiased
+def _biased_problem(seed, T=300, E=32, scale=1.0):
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[::9, : E // 2] = 0.25  # exact ties
+    bias = (rng.standard_normal(E) * scale).astype(np.float32)
+    return lg, bias
+
+
+@pytest.mark.parametrize("score,renorm", [("softmax", False), ("softmax", True), ("sigmoid", True)])
+def test_zero_bias_gives_the_unbiased_routing_bytes(score, renorm):
+    lg, _ = _biased_problem(41)
+    i0, w0 = orc.route(lg, 4, score, renorm)
+    for zero in (np.zeros(32, np.float32), np.full(32, -0.0, np.float32)):
+        i1, w1 = orc.route(lg, 4, score, renorm, bias=zero)
+        assert np.array_equal(i0, i1) and np.array_equal(w0.view(np.uint32), w1.view(np.uint32))
+
+
+@pytest.mark.parametrize("E,k,scale", [(8, 2, 0.5), (32, 4, 1.0), (128, 8, 3.0), (256, 8, 0.1)])
+def test_biased_topk_matches_stable_sort_of_the_float32_key(E, k, scale):
+    lg, bias = _biased_problem(E + k, E=E, scale=scale)
+    key = lg + bias[None, :]  # numpy float32 + float32: one rounding to nearest even
+    assert key.dtype == np.float32
+    idx, _ = orc.route(lg, k, "sigmoid", True, bias=bias)
+    assert np.array_equal(idx, _brute_topk(key, k))
+
+
+@pytest.mark.parametrize("score,renorm", [("softmax", False), ("softmax", True), ("sigmoid", True)])
+def test_bias_changes_the_choice_not_the_weights(score, renorm):
+    """The weights are the unbiased score function of the chosen experts
+    (scipy, float64), whatever bias chose them."""
+    lg, bias = _biased_problem(43, E=64, scale=2.0)
+    idx, w = orc.route(lg, 6, score, renorm, bias=bias)
+    i0, _ = orc.route(lg, 6, score, renorm)
+    assert not np.array_equal(idx, i0), "the bias should change some choices"
+    l64 = lg.astype(np.float64)
+    if score == "softmax":
+        sel = np.take_along_axis(softmax(l64, axis=1), idx.astype(np.int64), axis=1)
+        if renorm:
+            sel = sel / sel.sum(axis=1, keepdims=True)
+    else:
+        sel = expit(np.take_along_axis(l64, idx.astype(np.int64), axis=1))
+        sel = sel / sel.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(w, sel, rtol=1e-7, atol=0)
+
+
+def test_strong_bias_forces_its_experts():
+    """A bias far above the logits' spread picks the biased experts, in the
+    order of their (biased) keys; the weights are still the unbiased ones."""
+    rng = np.random.default_rng(44)
+    lg = rng.standard_normal((100, 16)).astype(np.float32)
+    bias = np.zeros(16, np.float32)
+    bias[[3, 9, 12]] = [100.0, 200.0, 300.0]
+    idx, w = orc.route(lg, 3, "sigmoid", True, bias=bias)
+    assert np.all(idx == np.array([12, 9, 3], np.int32))
+    s = expit(lg[:, [12, 9, 3]].astype(np.float64))
+    np.testing.assert_allclose(w, s / s.sum(axis=1, keepdims=True), rtol=1e-7, atol=0)
