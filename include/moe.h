@@ -33,7 +33,10 @@
  *   allocates, frees or keeps a pointer after returning.  Scratch space comes
  *   only from the caller's workspace `ws` of `ws_bytes` bytes
  *   (moe_workspace_size for the forward calls, moe_backward_workspace_size for
- *   the backward GEMMs).  Pointers are not checked for residency.
+ *   the backward GEMMs).  Every pointer is 16-byte aligned (hipMalloc and
+ *   torch give 256): a required pointer that is NULL or misaligned, or a
+ *   misaligned optional one, is MOE_ERR_INVALID_ARG.  Pointers are not checked
+ *   for residency.
  * - Streams.  `stream` is a hipStream_t (NULL = the null stream).  Every call
  *   only enqueues kernels on it and returns: no host synchronisation, no
  *   device-to-host copy, no host read of counts or offsets ([ISSUE]), so the
@@ -143,8 +146,16 @@ size_t moe_backward_workspace_size(const moe_config* cfg);
  *   softmax: p = exp(l - max_e l) / sum_e exp(l_e - max_e l) over all E;
  *            w = p, or p / (sum of the k selected p + 1e-20) when renorm;
  *   sigmoid: s = 1 / (1 + exp(-l)); w = s / (sum of the k selected s + 1e-20).
+ * Expert bias ([TE-EP] router commits: optional expert routing bias; a zero
+ * bias behaves as none): bias (optional, NULL for none) [E] f32 shifts only
+ * the selection, which then ranks the key fl32(l[e] + bias[e]) (ties again to
+ * the lower index); the weights above are still formed from the unbiased
+ * logits of the chosen experts.  A zero bias gives the same bytes as NULL.
+ * The bias gets no gradient (the choice is piecewise constant); moe_route_bwd
+ * works unchanged on a biased idx.
  * logits [T,E] f32 (finite) -> idx [T,k] i32, w [T,k] f32. */
-moe_status moe_route(const moe_config* cfg, const float* logits, int32_t* idx, float* w, void* stream);
+moe_status moe_route(const moe_config* cfg, const float* logits, const float* bias, int32_t* idx, float* w,
+                     void* stream);
 
 /* Step 2, grouping and permutation ([TE-EP] expert-major layout with per-expert
  * zero padding; device token counts; [ISSUE] no device-to-host sync;
@@ -241,7 +252,7 @@ moe_status moe_grouped_down_gemm_weighted(const moe_config* cfg, const void* h, 
 moe_status moe_combine(const moe_config* cfg, const void* yp, const int32_t* row_map, const float* w, void* y,
                        void* stream);
 
-/* The whole forward in one call: moe_route, moe_permute,
+/* The whole forward in one call: moe_route (bias as there), moe_permute,
  * moe_grouped_swiglu_gemm, moe_grouped_down_gemm, moe_combine on one stream.
  * Every buffer is the caller's: the routing outputs (idx, w, counts, offsets,
  * row_map, src_map), the permuted activations xp (+ xp_scale), h (+ h_scale),
@@ -253,8 +264,9 @@ moe_status moe_combine(const moe_config* cfg, const void* yp, const int32_t* row
  * (moe_grouped_swiglu_gemm_gather) and Xp is never written; the outputs are
  * the same bit for bit.  cfg->weight_site picks where w is applied: in the
  * combine, or in the gate/up (FC1) or down (FC2) epilogue (both forms). */
-moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x, const uint8_t* x_scale,
-                       const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, void* y,
+moe_status moe_forward(const moe_config* cfg, const float* logits, const float* bias, const void* x,
+                       const uint8_t* x_scale, const void* w1, const uint8_t* w1_scale, const void* w2,
+                       const uint8_t* w2_scale, void* y,
                        int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* row_map,
                        int32_t* src_map, void* xp, uint8_t* xp_scale, void* h, uint8_t* h_scale, void* yp,
                        void* gu_stash, int32_t* err, void* ws, size_t ws_bytes, void* stream);
@@ -269,9 +281,9 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
  * is shared by every call on a device and keeps the last call's contents:
  * calls that overlap on one device (other streams, other host threads) race,
  * so the caller orders them. */
-moe_status moe_forward_noalloc(const moe_config* cfg, const float* logits, const void* x, const uint8_t* x_scale,
-                               const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale,
-                               void* y, int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* row_map,
+moe_status moe_forward_noalloc(const moe_config* cfg, const float* logits, const float* bias, const void* x,
+                               const uint8_t* x_scale, const void* w1, const uint8_t* w1_scale, const void* w2,
+                               const uint8_t* w2_scale, void* y, int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* row_map,
                                int32_t* src_map, void* xp, uint8_t* xp_scale, void* h, uint8_t* h_scale, void* yp,
                                void* gu_stash, int32_t* err, void* stream);
 

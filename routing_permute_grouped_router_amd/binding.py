@@ -102,13 +102,13 @@ _SIGS = {
     "moe_rows_capacity": (ctypes.c_int64, [CFG]),
     "moe_workspace_size": (ctypes.c_size_t, [CFG]),
     "moe_backward_workspace_size": (ctypes.c_size_t, [CFG]),
-    "moe_route": (ctypes.c_int, [CFG, P, P, P, P]),
+    "moe_route": (ctypes.c_int, [CFG, P, P, P, P, P]),
     "moe_permute": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_grouped_swiglu_gemm": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_grouped_down_gemm": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_combine": (ctypes.c_int, [CFG, P, P, P, P, P]),
-    "moe_forward": (ctypes.c_int, [CFG] + [P] * 22 + [ctypes.c_size_t, P]),
-    "moe_forward_noalloc": (ctypes.c_int, [CFG] + [P] * 21 + [P]),
+    "moe_forward": (ctypes.c_int, [CFG] + [P] * 23 + [ctypes.c_size_t, P]),
+    "moe_forward_noalloc": (ctypes.c_int, [CFG] + [P] * 22 + [P]),
     "moe_route_bwd": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P]),
     "moe_grouped_swiglu_gemm_gather": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     "moe_grouped_swiglu_gemm_weighted": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -203,10 +203,12 @@ def _scale_dtype(cfg):
     return torch.uint8
 
 
-def moe_route(cfg: MoEConfig, logits, idx, w, stream=None):
+def moe_route(cfg: MoEConfig, logits, idx, w, stream=None, bias=None):
+    """bias (optional, float32 [E]): shifts only the selection key."""
     c = cfg.c()
     _check(load_library().moe_route(
         ctypes.byref(c), _ptr(logits, "logits", torch.float32, (cfg.T, cfg.E)),
+        _ptr(bias, "bias", torch.float32, (cfg.E,), optional=True),
         _ptr(idx, "idx", torch.int32, (cfg.T, cfg.k)), _ptr(w, "w", torch.float32, (cfg.T, cfg.k)),
         _stream(stream)))
 
@@ -315,19 +317,19 @@ def moe_combine(cfg: MoEConfig, yp, row_map, w, y, stream=None):
 
 
 def moe_forward(cfg: MoEConfig, logits, x, w1, w2, buf: dict, x_scale=None, w1_scale=None, w2_scale=None,
-                stream=None):
-    """buf: the caller's buffers, as made by alloc_forward()."""
-    _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stream, noalloc=False)
+                stream=None, bias=None):
+    """buf: the caller's buffers, as made by alloc_forward(); bias as in moe_route."""
+    _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stream, bias, noalloc=False)
 
 
 def moe_forward_noalloc(cfg: MoEConfig, logits, x, w1, w2, buf: dict, x_scale=None, w1_scale=None, w2_scale=None,
-                        stream=None):
+                        stream=None, bias=None):
     """moe_forward with the library's static scratch array instead of buf["ws"]
     (which is not used)."""
-    _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stream, noalloc=True)
+    _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stream, bias, noalloc=True)
 
 
-def _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stream, noalloc):
+def _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stream, bias, noalloc):
     c = cfg.c()
     mx = cfg.dtype == "mxfp8"
     ws_args = () if noalloc else _ws(buf["ws"])
@@ -335,7 +337,8 @@ def _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stre
     R, T, H, F, E, k = cfg.R_cap, cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
     sd, od = cfg.store_dtype, cfg.out_dtype
     _check(fn(
-        ctypes.byref(c), _ptr(logits, "logits", torch.float32, (T, E)), _ptr(x, "x", sd, (T, H)),
+        ctypes.byref(c), _ptr(logits, "logits", torch.float32, (T, E)),
+        _ptr(bias, "bias", torch.float32, (E,), optional=True), _ptr(x, "x", sd, (T, H)),
         _ptr(x_scale, "x_scale", torch.uint8, (T, H // 32), optional=not mx),
         _ptr(w1, "w1", sd, (E, 2 * F, H)), _ptr(w1_scale, "w1_scale", torch.uint8, (E, 2 * F, H // 32), optional=not mx),
         _ptr(w2, "w2", sd, (E, H, F)), _ptr(w2_scale, "w2_scale", torch.uint8, (E, H, F // 32), optional=not mx),

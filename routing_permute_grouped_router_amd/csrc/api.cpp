@@ -29,9 +29,15 @@ moe_status hip_status(hipError_t e, const char* what) {
     return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Every device array is read and written in 16-byte vectors.
+#define ALIGNED16(ptr)                                                                                  \
+    do {                                                                                                \
+        if ((uintptr_t)(ptr) % 16) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", #ptr); \
+    } while (0)
 #define REQUIRE(ptr)                                                              \
     do {                                                                          \
         if ((ptr) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #ptr); \
+        ALIGNED16(ptr);                                                           \
     } while (0)
 
 int64_t rows_capacity(const moe_config& c) { return (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1); }
@@ -202,17 +208,18 @@ moe_status row_weights_checked(const moe_config* cfg, const int32_t* src_map, co
     return MOE_OK;
 }
 
-moe_status route_checked(const moe_config* cfg, const float* logits, int32_t* idx, float* w, void* stream,
-                         bool launch) {
+moe_status route_checked(const moe_config* cfg, const float* logits, const float* bias, int32_t* idx, float* w,
+                         void* stream, bool launch) {
     moe_status st = check_config(cfg);
     if (st) return st;
     if (cfg->T > 0) {
         REQUIRE(logits);
         REQUIRE(idx);
         REQUIRE(w);
+        ALIGNED16(bias);  // optional
     }
     if (!launch) return MOE_OK;
-    return hip_status(launch_route(*cfg, logits, idx, w, as_stream(stream)), "moe_route");
+    return hip_status(launch_route(*cfg, logits, bias, idx, w, as_stream(stream)), "moe_route");
 }
 
 moe_status permute_checked(const moe_config* cfg, const void* x, const uint8_t* x_scale, const int32_t* idx,
@@ -365,8 +372,9 @@ size_t moe_backward_workspace_size(const moe_config* cfg) {
     return cfg->dtype == MOE_BF16 ? round256(bwd_workspace_bytes(*cfg)) : 0;
 }
 
-moe_status moe_route(const moe_config* cfg, const float* logits, int32_t* idx, float* w, void* stream) {
-    return route_checked(cfg, logits, idx, w, stream, true);
+moe_status moe_route(const moe_config* cfg, const float* logits, const float* bias, int32_t* idx, float* w,
+                     void* stream) {
+    return route_checked(cfg, logits, bias, idx, w, stream, true);
 }
 
 moe_status moe_permute(const moe_config* cfg, const void* x, const uint8_t* x_scale, const int32_t* idx, void* xp,
@@ -441,8 +449,9 @@ moe_status moe_combine(const moe_config* cfg, const void* yp, const int32_t* row
 
 // Both fused calls check every step's arguments (pass 0) before the first
 // launch (pass 1), so a host-checkable problem enqueues nothing.
-moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x, const uint8_t* x_scale,
-                       const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, void* y,
+moe_status moe_forward(const moe_config* cfg, const float* logits, const float* bias, const void* x,
+                       const uint8_t* x_scale, const void* w1, const uint8_t* w1_scale, const void* w2,
+                       const uint8_t* w2_scale, void* y,
                        int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* row_map,
                        int32_t* src_map, void* xp, uint8_t* xp_scale, void* h, uint8_t* h_scale, void* yp,
                        void* gu_stash, int32_t* err, void* ws, size_t ws_bytes, void* stream) {
@@ -461,7 +470,7 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const void* x
     const bool at_combine = c.weight_site == MOE_WEIGHT_AT_COMBINE;
     for (int pass = 0; pass < 2; ++pass) {
         const bool launch = pass == 1;
-        if ((st = route_checked(cfg, logits, idx, w, stream, launch))) return st;
+        if ((st = route_checked(cfg, logits, bias, idx, w, stream, launch))) return st;
         if ((st = permute_checked(cfg, x, x_scale, idx, xp, xp_scale, counts, offsets, row_map, src_map, err, ws,
                                   ws_bytes, stream, launch)))
             return st;

@@ -47,7 +47,8 @@ moe_status set_error(moe_status s, const char* fmt, ...);
 // --------------------------------------------------------- host launchers
 // Each returns hipSuccess or the launch error; arguments were validated by
 // the API layer.
-hipError_t launch_route(const moe_config& c, const float* logits, int32_t* idx, float* w, hipStream_t s);
+hipError_t launch_route(const moe_config& c, const float* logits, const float* bias, int32_t* idx, float* w,
+                        hipStream_t s);
 
 // Grouping and permutation (xp null: the grouping only).  ws holds
 // group_n_chunks(T, E) * E int32 (per-chunk expert counts).

@@ -49,16 +49,16 @@ moe_status scratch_on_current_device(void** out) {
 
 }  // namespace
 
-extern "C" moe_status moe_forward_noalloc(const moe_config* cfg, const float* logits, const void* x,
-                                          const uint8_t* x_scale, const void* w1, const uint8_t* w1_scale,
+extern "C" moe_status moe_forward_noalloc(const moe_config* cfg, const float* logits, const float* bias,
+                                          const void* x, const uint8_t* x_scale, const void* w1, const uint8_t* w1_scale,
                                           const void* w2, const uint8_t* w2_scale, void* y, int32_t* idx, float* w,
                                           int32_t* counts, int32_t* offsets, int32_t* row_map, int32_t* src_map,
                                           void* xp, uint8_t* xp_scale, void* h, uint8_t* h_scale, void* yp,
                                           void* gu_stash, int32_t* err, void* stream) {
     // a bad config: moe_forward reports it (with no workspace, before any device call)
     if (moe_rows_capacity(cfg) < 0)
-        return moe_forward(cfg, logits, x, x_scale, w1, w1_scale, w2, w2_scale, y, idx, w, counts, offsets, row_map,
-                           src_map, xp, xp_scale, h, h_scale, yp, gu_stash, err, nullptr, 0, stream);
+        return moe_forward(cfg, logits, bias, x, x_scale, w1, w1_scale, w2, w2_scale, y, idx, w, counts, offsets,
+                           row_map, src_map, xp, xp_scale, h, h_scale, yp, gu_stash, err, nullptr, 0, stream);
     const size_t need = moe_workspace_size(cfg);
     if (need > kNoAllocScratchBytes)
         return moe::set_error(MOE_ERR_WORKSPACE,
@@ -68,6 +68,6 @@ extern "C" moe_status moe_forward_noalloc(const moe_config* cfg, const float* lo
     void* ws = nullptr;
     moe_status st = scratch_on_current_device(&ws);
     if (st) return st;
-    return moe_forward(cfg, logits, x, x_scale, w1, w1_scale, w2, w2_scale, y, idx, w, counts, offsets, row_map,
-                       src_map, xp, xp_scale, h, h_scale, yp, gu_stash, err, ws, kNoAllocScratchBytes, stream);
+    return moe_forward(cfg, logits, bias, x, x_scale, w1, w1_scale, w2, w2_scale, y, idx, w, counts, offsets,
+                       row_map, src_map, xp, xp_scale, h, h_scale, yp, gu_stash, err, ws, kNoAllocScratchBytes, stream);
 }

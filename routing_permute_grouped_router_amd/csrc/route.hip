@@ -18,6 +18,11 @@
 // sees every pick, keeps it (KMAX slots), and the normalising sums are
 // formed in the same order by all of them.  Lane r writes the picks j with
 // j % L == r.
+//
+// With an expert bias (TransformerEngine page, router commits: an optional
+// expert routing bias with a zero bias matching no bias), the selection runs
+// on the key fl32(logit + bias[e]) and each pick carries its unbiased logit
+// along, from which the weights are formed exactly as without a bias.
 #include "moe_internal.h"
 
 namespace moe {
@@ -27,8 +32,9 @@ __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
     return v > bv || (v == bv && e < be);
 }
 
-template <int L, int VPL, int KMAX>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
+template <int L, int VPL, int KMAX, bool BIAS>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
+                                                    const float* __restrict__ bias, int T, int E, int k,
                                                     int score, int renorm, int32_t* __restrict__ idx,
                                                     float* __restrict__ w) {
     constexpr int TPW = kWave / L;  // tokens per wavefront
@@ -38,7 +44,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     const bool live = t < T;
     const float* row = logits + (live ? t : 0) * (int64_t)E;
 
-    float v[VPL];
+    float v[VPL];   // logits
+    float kv[VPL];  // selection keys: the logits, or fl32(logit + bias)
     uint32_t avail = 0;
     if (E % 4 == 0) {  // rows are 16-byte aligned: whole float4 of experts
 #pragma unroll
@@ -50,6 +57,13 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
             v[i + 1] = q.y;
             v[i + 2] = q.z;
             v[i + 3] = q.w;
+            if (BIAS) {
+                const float4 b = ok ? *(const float4*)(bias + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+                kv[i] = q.x + b.x;
+                kv[i + 1] = q.y + b.y;
+                kv[i + 2] = q.z + b.z;
+                kv[i + 3] = q.w + b.w;
+            }
             avail |= ok ? 0xfu << i : 0u;
         }
     } else {
@@ -58,8 +72,13 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
             const int e = r * VPL + i;
             const bool ok = live && e < E;
             v[i] = ok ? row[e] : -INFINITY;
+            if (BIAS) kv[i] = v[i] + (ok ? bias[e] : 0.f);
             avail |= ok ? 1u << i : 0u;
         }
+    }
+    if (!BIAS) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) kv[i] = v[i];
     }
     // group-wide reductions (the L lanes of a group are consecutive and
     // aligned, so xor offsets below L stay inside it)
@@ -74,40 +93,51 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         return x;
     };
 
-    float pv[KMAX];
+    float pv[KMAX];  // the picks' unbiased logits
     int pe[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         pv[j] = -INFINITY;
         pe[j] = -1;
         if (j >= k) continue;
-        float bv = -INFINITY;
+        float bk = -INFINITY, bu = -INFINITY;  // best key and its logit
         int be = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             const int e = r * VPL + i;
-            if ((avail >> i & 1) && better(v[i], e, bv, be)) {
-                bv = v[i];
+            if ((avail >> i & 1) && better(kv[i], e, bk, be)) {
+                bk = kv[i];
+                bu = v[i];
                 be = e;
             }
         }
 #pragma unroll
         for (int off = L / 2; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
+            const float ok = __shfl_xor(bk, off, kWave);
             const int oe = __shfl_xor(be, off, kWave);
-            if (better(ov, oe, bv, be)) {
-                bv = ov;
+            const float ou = BIAS ? __shfl_xor(bu, off, kWave) : ok;
+            if (better(ok, oe, bk, be)) {
+                bk = ok;
+                bu = ou;
                 be = oe;
             }
         }
         if (be / VPL == r) avail &= ~(1u << (be % VPL));  // the owning lane retires the pick
-        pv[j] = bv;
+        pv[j] = BIAS ? bu : bk;
         pe[j] = be;
     }
 
     float wt[KMAX];
     if (score == MOE_SOFTMAX && !renorm) {
-        const float m = pv[0];  // the first pick is the maximum
+        // the first pick is the largest logit; with a bias it need not be
+        float m = pv[0];
+        if (BIAS) {
+            m = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                if (r * VPL + i < E) m = fmaxf(m, v[i]);
+            m = gmax(m);
+        }
         float z = 0.f;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
@@ -116,17 +146,33 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) wt[j] = j < k ? expf(pv[j] - m) / z : 0.f;
     } else if (score == MOE_SOFTMAX) {
-        // p_j / (sum of the chosen p + 1e-20) with p the softmax over all E:
-        // the softmax's normaliser cancels, and the 1e-20 changes nothing in
-        // float32 (the sum of the chosen p is at least 1 / E >= 2^-10, whose
-        // half ulp 2^-34 exceeds 1e-20), so only the chosen k exponentials
-        // are formed.
-        const float m = pv[0];
+        // p_j / (sum of the chosen p + 1e-20) with p the softmax over all E.
+        // With m the largest chosen logit, a_j = exp(l_j - m) and
+        // Zm = sum over all E of exp(l_e - m), this is a_j / (sum a + 1e-20 Zm)
+        // (numerator and denominator times Z exp(max l - m)).  Without a bias
+        // the chosen are the k largest logits, so sum a >= 1 and 1e-20 Zm <=
+        // 1e-20 E < 2^-24: the term cannot change the float32 sum and only the
+        // k chosen exponentials are formed.  A bias can choose experts whose p
+        // is small enough for the 1e-20 to count, so then Zm is formed too
+        // (a zero bias still gives the same bytes: the term rounds away).
+        float m = pv[0];
+        if (BIAS) {
+#pragma unroll
+            for (int j = 1; j < KMAX; ++j)
+                if (j < k) m = fmaxf(m, pv[j]);
+        }
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             wt[j] = j < k ? expf(pv[j] - m) : 0.f;
             s += wt[j];
+        }
+        if (BIAS) {
+            float zm = 0.f;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                if (r * VPL + i < E) zm += expf(v[i] - m);
+            s += 1e-20f * gsum(zm);
         }
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) wt[j] = wt[j] / s;
@@ -151,26 +197,33 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 }
 
 template <int L, int VPL, int KMAX>
-hipError_t launch_l(const moe_config& c, const float* logits, int32_t* idx, float* w, hipStream_t s) {
+hipError_t launch_l(const moe_config& c, const float* logits, const float* bias, int32_t* idx, float* w,
+                    hipStream_t s) {
     constexpr int tokens_per_block = (256 / kWave) * (kWave / L);
     const dim3 grid((unsigned)((c.T + tokens_per_block - 1) / tokens_per_block)), block(256);
-    route_kernel<L, VPL, KMAX><<<grid, block, 0, s>>>(logits, c.T, c.E, c.k, c.score, c.renorm, idx, w);
+    if (bias)
+        route_kernel<L, VPL, KMAX, true><<<grid, block, 0, s>>>(logits, bias, c.T, c.E, c.k, c.score, c.renorm,
+                                                                idx, w);
+    else
+        route_kernel<L, VPL, KMAX, false><<<grid, block, 0, s>>>(logits, nullptr, c.T, c.E, c.k, c.score,
+                                                                 c.renorm, idx, w);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_route(const moe_config& c, const float* logits, int32_t* idx, float* w, hipStream_t s) {
+hipError_t launch_route(const moe_config& c, const float* logits, const float* bias, int32_t* idx, float* w,
+                        hipStream_t s) {
     if (c.T == 0) return hipSuccess;
-    if (c.k > 8) return launch_l<32, 32, kMaxTopK>(c, logits, idx, w, s);  // E <= 1024
-    if (c.E <= 8) return launch_l<1, 8, 8>(c, logits, idx, w, s);
-    if (c.E <= 16) return launch_l<1, 16, 8>(c, logits, idx, w, s);
-    if (c.E <= 32) return launch_l<1, 32, 8>(c, logits, idx, w, s);
-    if (c.E <= 64) return launch_l<2, 32, 8>(c, logits, idx, w, s);
-    if (c.E <= 128) return launch_l<4, 32, 8>(c, logits, idx, w, s);
-    if (c.E <= 256) return launch_l<8, 32, 8>(c, logits, idx, w, s);
-    if (c.E <= 512) return launch_l<16, 32, 8>(c, logits, idx, w, s);
-    return launch_l<32, 32, 8>(c, logits, idx, w, s);
+    if (c.k > 8) return launch_l<32, 32, kMaxTopK>(c, logits, bias, idx, w, s);  // E <= 1024
+    if (c.E <= 8) return launch_l<1, 8, 8>(c, logits, bias, idx, w, s);
+    if (c.E <= 16) return launch_l<1, 16, 8>(c, logits, bias, idx, w, s);
+    if (c.E <= 32) return launch_l<1, 32, 8>(c, logits, bias, idx, w, s);
+    if (c.E <= 64) return launch_l<2, 32, 8>(c, logits, bias, idx, w, s);
+    if (c.E <= 128) return launch_l<4, 32, 8>(c, logits, bias, idx, w, s);
+    if (c.E <= 256) return launch_l<8, 32, 8>(c, logits, bias, idx, w, s);
+    if (c.E <= 512) return launch_l<16, 32, 8>(c, logits, bias, idx, w, s);
+    return launch_l<32, 32, 8>(c, logits, bias, idx, w, s);
 }
 
 }  // namespace moe

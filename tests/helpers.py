@@ -142,7 +142,8 @@ def cfg_of(shape):
     return MoEConfig.from_shape(shape)
 
 
-def run_forward(inp: Inputs, training: bool = False, poison: bool = True) -> dict:
+def run_forward(inp: Inputs, training: bool = False, poison: bool = True, bias=None) -> dict:
+    """bias: optional float32 [E] host array, the router's selection bias."""
     import routing_permute_grouped_router_amd as moe
     cfg = cfg_of(inp.s)
     buf = moe.alloc_forward(cfg, training=training)
@@ -154,6 +155,7 @@ def run_forward(inp: Inputs, training: bool = False, poison: bool = True) -> dic
             buf[k].fill_(-7)
     d = inp.dev
     moe.moe_forward(cfg, d["logits"], d["x"], d["w1"], d["w2"], buf, x_scale=d.get("x_scale"),
-                    w1_scale=d.get("w1_scale"), w2_scale=d.get("w2_scale"))
+                    w1_scale=d.get("w1_scale"), w2_scale=d.get("w2_scale"),
+                    bias=None if bias is None else to_dev(np.asarray(bias, np.float32), "f32"))
     torch.cuda.synchronize()
     return buf

@@ -52,22 +52,33 @@ def _cfg(**kw):
 def test_bad_config_rejected_on_host(kw, status):
     lib = moe.load_library()
     c = _cfg(**kw)
-    st = lib.moe_route(ctypes.byref(c), 1, 1, 1, None)
+    st = lib.moe_route(ctypes.byref(c), 256, None, 256, 256, None)
     assert st == status
     assert lib.moe_last_error()
+
+
+def test_misaligned_pointers_rejected():
+    lib = moe.load_library()
+    c = _cfg()
+    assert lib.moe_route(ctypes.byref(c), 264, None, 256, 256, None) == b.MOE_ERR_INVALID_ARG
+    assert b"logits" in lib.moe_last_error() and b"aligned" in lib.moe_last_error()
+    assert lib.moe_route(ctypes.byref(c), 256, 260, 256, 256, None) == b.MOE_ERR_INVALID_ARG
+    assert b"bias" in lib.moe_last_error()
+    assert _forward(lib, c, y=512 + 4) == b.MOE_ERR_INVALID_ARG
+    assert b"y" in lib.moe_last_error()
 
 
 def test_null_pointers_rejected():
     lib = moe.load_library()
     c = _cfg()
-    assert lib.moe_route(ctypes.byref(c), None, 1, 1, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(c), None, None, 256, 256, None) == b.MOE_ERR_INVALID_ARG
     assert b"logits" in lib.moe_last_error()
-    assert lib.moe_combine(ctypes.byref(c), 1, None, 1, 1, None) == b.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(None, 1, 1, 1, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(c), 256, None, 256, 256, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, 256, None, 256, 256, None) == b.MOE_ERR_INVALID_ARG
     # routing backward: every input and dlogits required, dw optional
-    assert lib.moe_route_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, None, None, None) == b.MOE_ERR_INVALID_ARG
-    assert lib.moe_route_bwd(ctypes.byref(c), 1, None, 1, 1, 1, None, 1, None) == b.MOE_ERR_INVALID_ARG
-    assert lib.moe_route_bwd(None, 1, 1, 1, 1, 1, None, 1, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_bwd(ctypes.byref(c), 256, 256, 256, 256, 256, None, None, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_bwd(ctypes.byref(c), 256, None, 256, 256, 256, None, 256, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_bwd(None, 256, 256, 256, 256, 256, None, 256, None) == b.MOE_ERR_INVALID_ARG
     # T = 0 is a no-op that touches nothing
     assert lib.moe_route_bwd(ctypes.byref(_cfg(T=0)), None, None, None, None, None, None, None, None) == b.MOE_OK
 
@@ -75,15 +86,15 @@ def test_null_pointers_rejected():
 def test_unsupported_shapes():
     lib = moe.load_library()
     c = _cfg(H=96)
-    assert lib.moe_grouped_swiglu_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, None, None, 0, None) == \
+    assert lib.moe_grouped_swiglu_gemm(ctypes.byref(c), 256, None, 256, None, 256, 256, None, None, None, 0, None) == \
         b.MOE_ERR_UNSUPPORTED
     c = _cfg(F=40)
-    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, 0, None) == b.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 256, None, 256, None, 256, 256, None, 0, None) == b.MOE_ERR_UNSUPPORTED
     c = _cfg(F=192, dtype=b.MOE_MXFP8)  # MXFP8 tiles F by 128
-    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, 1, 1, 1, 1, 1, None, 0, None) == b.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 256, 256, 256, 256, 256, 256, None, 0, None) == b.MOE_ERR_UNSUPPORTED
     assert b"128" in lib.moe_last_error()
     c = _cfg(H=32768, F=16384)  # one expert's weights must stay below 2^32 bytes
-    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, 0, None) == b.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_down_gemm(ctypes.byref(c), 256, None, 256, None, 256, 256, None, 0, None) == b.MOE_ERR_UNSUPPORTED
 
 
 def test_workspace_checks():
@@ -91,15 +102,15 @@ def test_workspace_checks():
     c = _cfg(T=5000, E=128, k=8)
     need = lib.moe_workspace_size(ctypes.byref(c))
     assert need > 0
-    st = lib.moe_permute(ctypes.byref(c), 1, None, 1, 1, None, 1, 1, 1, 1, None, 1, need - 1, None)
+    st = lib.moe_permute(ctypes.byref(c), 256, None, 256, 256, None, 256, 256, 256, 256, None, 256, need - 1, None)
     assert st == b.MOE_ERR_WORKSPACE
     assert lib.moe_rows_capacity(ctypes.byref(c)) == 5000 * 8
     c2 = _cfg(T=5000, E=128, k=8, align=128)
     assert lib.moe_rows_capacity(ctypes.byref(c2)) == 5000 * 8 + 128 * 127
     # the grouped GEMMs take the same workspace
-    st = lib.moe_grouped_swiglu_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, None, 1, need - 1, None)
+    st = lib.moe_grouped_swiglu_gemm(ctypes.byref(c), 256, None, 256, None, 256, 256, None, None, 256, need - 1, None)
     assert st == b.MOE_ERR_WORKSPACE
-    st = lib.moe_grouped_down_gemm(ctypes.byref(c), 1, None, 1, None, 1, 1, None, 0, None)
+    st = lib.moe_grouped_down_gemm(ctypes.byref(c), 256, None, 256, None, 256, 256, None, 0, None)
     assert st == b.MOE_ERR_WORKSPACE
 
 
@@ -117,14 +128,14 @@ def test_backward_workspace_bounds():
     assert lib.moe_backward_workspace_size(ctypes.byref(c)) < 4096
     # the backward is built for bf16 storage only
     assert lib.moe_backward_workspace_size(ctypes.byref(_cfg(dtype=b.MOE_F32))) == 0
-    st = lib.moe_grouped_down_bwd(ctypes.byref(_cfg(T=16384, H=2048, F=768, E=128, k=8)), 1, 1, 1, 1, 1, 1, 1,
-                                  1, need - 1, None)
+    st = lib.moe_grouped_down_bwd(ctypes.byref(_cfg(T=16384, H=2048, F=768, E=128, k=8)), 256, 256, 256, 256, 256,
+                                  256, 256, 256, need - 1, None)
     assert st == b.MOE_ERR_WORKSPACE
 
 
 def test_quantize_rejects_ragged_cols():
     lib = moe.load_library()
-    assert lib.moe_quantize_mxfp8(1, 4, 33, 1, 1, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp8(256, 4, 33, 256, 256, None) == b.MOE_ERR_INVALID_ARG
 
 
 def test_python_layer_type_errors():
@@ -159,17 +170,17 @@ def test_weighted_gemms_and_placement_checked_on_host():
     c = _cfg(weight_site=b.MOE_WEIGHT_AT_FC2)
     need = lib.moe_workspace_size(ctypes.byref(c))
     # the per-row weights need src_map and w
-    st = lib.moe_grouped_down_gemm_weighted(ctypes.byref(c), 1, None, 1, None, 1, None, 1, 1, 1, need, None)
+    st = lib.moe_grouped_down_gemm_weighted(ctypes.byref(c), 256, None, 256, None, 256, None, 256, 256, 256, need, None)
     assert st == b.MOE_ERR_INVALID_ARG and b"src_map" in lib.moe_last_error()
-    st = lib.moe_grouped_swiglu_gemm_weighted(ctypes.byref(c), 1, None, 1, None, 1, 1, None, 1, None, 1, need, None)
+    st = lib.moe_grouped_swiglu_gemm_weighted(ctypes.byref(c), 256, None, 256, None, 256, 256, None, 256, None, 256, need, None)
     assert st == b.MOE_ERR_INVALID_ARG and b"w" in lib.moe_last_error()
     # the workspace holds the per-row weights as well
     c0 = _cfg()
     assert need == lib.moe_workspace_size(ctypes.byref(c0))
     assert need >= 4 * (64 * 2 + 256)
     # the backward is built for the weights applied in the combine
-    assert lib.moe_combine_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
-    assert lib.moe_route_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine_bwd(ctypes.byref(c), 256, 256, 256, 256, 256, 256, None) == b.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_bwd(ctypes.byref(c), 256, 256, 256, 256, 256, 256, 256, None) == b.MOE_ERR_UNSUPPORTED
     # an unweighted combine takes w = NULL (T = 0: nothing to launch)
     assert lib.moe_combine(ctypes.byref(_cfg(T=0)), None, None, None, None, None) == b.MOE_OK
 
@@ -187,15 +198,15 @@ def test_new_entry_points_host_edge_cases():
     c = _cfg(weight_site=b.MOE_WEIGHT_AT_FC1)
     need = lib.moe_workspace_size(ctypes.byref(c))
     # a missing output is rejected before anything is launched
-    st = lib.moe_grouped_swiglu_gemm_weighted(ctypes.byref(c), 1, None, 1, None, 1, 1, 1, None, None, 1, need, None)
+    st = lib.moe_grouped_swiglu_gemm_weighted(ctypes.byref(c), 256, None, 256, None, 256, 256, 256, None, None, 256, need, None)
     assert st == b.MOE_ERR_INVALID_ARG and b"h" in lib.moe_last_error()
-    st = lib.moe_grouped_down_gemm_weighted(ctypes.byref(c), 1, None, 1, None, 1, 1, 1, None, 1, need, None)
+    st = lib.moe_grouped_down_gemm_weighted(ctypes.byref(c), 256, None, 256, None, 256, 256, 256, None, 256, need, None)
     assert st == b.MOE_ERR_INVALID_ARG and b"yp" in lib.moe_last_error()
     # too small a workspace (the per-row weights live there)
-    st = lib.moe_grouped_down_gemm_weighted(ctypes.byref(c), 1, None, 1, None, 1, 1, 1, 1, 1, need - 256, None)
+    st = lib.moe_grouped_down_gemm_weighted(ctypes.byref(c), 256, None, 256, None, 256, 256, 256, 256, 256, need - 256, None)
     assert st == b.MOE_ERR_WORKSPACE
     # the gather form needs the routing maps
-    st = lib.moe_grouped_swiglu_gemm_gather(ctypes.byref(c), 1, None, None, 1, 1, None, 1, 1, None, 1, need, None)
+    st = lib.moe_grouped_swiglu_gemm_gather(ctypes.byref(c), 256, None, None, 256, 256, None, 256, 256, None, 256, need, None)
     assert st == b.MOE_ERR_INVALID_ARG and b"src_map" in lib.moe_last_error()
     # a clamp limit is accepted by every call that takes the config
     cl = _cfg(swiglu_limit=7.0)
@@ -203,15 +214,15 @@ def test_new_entry_points_host_edge_cases():
 
 
 # moe_forward's pointer arguments after cfg, in order (ws_bytes and stream follow)
-_FWD = ("logits", "x", "x_scale", "w1", "w1_scale", "w2", "w2_scale", "y", "idx", "w", "counts", "offsets",
+_FWD = ("logits", "bias", "x", "x_scale", "w1", "w1_scale", "w2", "w2_scale", "y", "idx", "w", "counts", "offsets",
         "row_map", "src_map", "xp", "xp_scale", "h", "h_scale", "yp", "gu_stash", "err", "ws")
 _BWD = ("dy", "w", "w1", "w2", "offsets", "row_map", "src_map", "xp", "h", "gu_stash", "dyp", "dgu", "dxp", "dx",
         "dw1", "dw2", "ws")
 
 
 def _forward(lib, c, ws_bytes=None, **override):
-    args = {n: 1 for n in _FWD}
-    args.update({"x_scale": None, "w1_scale": None, "w2_scale": None, "xp_scale": None, "h_scale": None,
+    args = {n: 256 for n in _FWD}
+    args.update({"bias": None, "x_scale": None, "w1_scale": None, "w2_scale": None, "xp_scale": None, "h_scale": None,
                  "gu_stash": None, "err": None})
     args.update(override)
     nb = lib.moe_workspace_size(ctypes.byref(c)) if ws_bytes is None else ws_bytes
@@ -219,7 +230,7 @@ def _forward(lib, c, ws_bytes=None, **override):
 
 
 def _backward(lib, c, ws_bytes=None, **override):
-    args = {n: 1 for n in _BWD}
+    args = {n: 256 for n in _BWD}
     args.update(override)
     nb = lib.moe_backward_workspace_size(ctypes.byref(c)) if ws_bytes is None else ws_bytes
     return lib.moe_backward(ctypes.byref(c), *[args[n] for n in _BWD], nb, None)
@@ -238,11 +249,11 @@ def test_fused_calls_check_everything_before_launching():
         assert name.encode() in lib.moe_last_error(), name
     # MXFP8: the scales of every operand and of h
     cm = _cfg(dtype=b.MOE_MXFP8, F=128)
-    mx = dict(x_scale=1, w1_scale=1, w2_scale=1, xp_scale=1, h_scale=1)
+    mx = dict(x_scale=256, w1_scale=256, w2_scale=256, xp_scale=256, h_scale=256)
     for name in ("h_scale", "xp_scale", "x_scale"):
         assert _forward(lib, cm, **{**mx, name: None}) == b.MOE_ERR_INVALID_ARG, name
     # the gather form (xp NULL) refuses a stash and needs src_map
-    assert _forward(lib, c, xp=None, gu_stash=1) == b.MOE_ERR_INVALID_ARG
+    assert _forward(lib, c, xp=None, gu_stash=256) == b.MOE_ERR_INVALID_ARG
     assert _forward(lib, c, xp=None, src_map=None) == b.MOE_ERR_INVALID_ARG
     # an epilogue weight site checks the per-row weights' inputs first
     assert _forward(lib, _cfg(weight_site=b.MOE_WEIGHT_AT_FC2), w=None) == b.MOE_ERR_INVALID_ARG
@@ -258,11 +269,11 @@ def test_backward_takes_bf16_storage_only():
     for dt in (b.MOE_F32, b.MOE_MXFP8):
         c = _cfg(dtype=dt, F=128)
         assert _backward(lib, c, ws_bytes=1 << 20) == b.MOE_ERR_UNSUPPORTED
-        assert lib.moe_combine_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
-        assert lib.moe_permute_bwd(ctypes.byref(c), 1, 1, 1, None) == b.MOE_ERR_UNSUPPORTED
-        assert lib.moe_grouped_down_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20, None) == \
+        assert lib.moe_combine_bwd(ctypes.byref(c), 256, 256, 256, 256, 256, 256, None) == b.MOE_ERR_UNSUPPORTED
+        assert lib.moe_permute_bwd(ctypes.byref(c), 256, 256, 256, None) == b.MOE_ERR_UNSUPPORTED
+        assert lib.moe_grouped_down_bwd(ctypes.byref(c), 256, 256, 256, 256, 256, 256, 256, 256, 1 << 20, None) == \
             b.MOE_ERR_UNSUPPORTED
-        assert lib.moe_grouped_swiglu_bwd(ctypes.byref(c), 1, 1, 1, 1, 1, 1, 1, 1 << 20, None) == \
+        assert lib.moe_grouped_swiglu_bwd(ctypes.byref(c), 256, 256, 256, 256, 256, 256, 256, 1 << 20, None) == \
             b.MOE_ERR_UNSUPPORTED
 
 
@@ -272,7 +283,7 @@ def test_noalloc_forward_limit_checked_on_host():
     lib = moe.load_library()
     big = _cfg(T=400000, H=2048, F=768, E=128, k=8)
     assert lib.moe_workspace_size(ctypes.byref(big)) > 68 << 20
-    args = [1] * 21
+    args = [256] * 22
     assert lib.moe_forward_noalloc(ctypes.byref(big), *args, None) == b.MOE_ERR_WORKSPACE
     assert b"68" in lib.moe_last_error() or b"static" in lib.moe_last_error()
     assert lib.moe_forward_noalloc(ctypes.byref(_cfg(k=0)), *args, None) == b.MOE_ERR_INVALID_ARG
