@@ -137,6 +137,9 @@ def main():
 
     s = wl.BY_NAME[args.workload]
     cfg = moe.MoEConfig.from_shape(s)
+
+    def note(msg):  # progress on stderr; the JSON line stays alone on stdout
+        print(f"[bench {s.name}] {msg}", file=sys.stderr, flush=True)
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
 
@@ -176,6 +179,7 @@ def main():
         del a1, a2
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
+    note(f"inputs resident ({t_gen:.1f} s)")
 
     buf = moe.alloc_forward(cfg, training=s.backward)
     bwd = moe.alloc_backward(cfg) if s.backward else None
@@ -231,6 +235,7 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    note(f"{args.warmup} warm-up steps done")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall = time.time()
@@ -242,6 +247,7 @@ def main():
     per_step = sorted(e[0].elapsed_time(e[-1]) for e in evs)
     kern_samples = {n: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, n in enumerate(names)}
     kern_ms = {n: sum(v) / len(v) for n, v in kern_samples.items()}
+    note(f"{args.steps} timed steps: {ms:.4f} ms per step")
 
     def pct(v, q):
         return v[min(len(v) - 1, int(q * len(v)))]
@@ -269,6 +275,7 @@ def main():
             samples.append((a0, a1))
         torch.cuda.synchronize()
         cold[n] = sorted(a0.elapsed_time(a1) for a0, a1 in samples)
+    note("cold-cache bandwidth kernels done")
 
     # Route at growing T (E and k of this workload; logits N(0,1)): where the
     # kernel leaves the launch-latency regime and what bandwidth it reaches.
@@ -295,6 +302,7 @@ def main():
                             "frac_hbm": round(nb / (pct(v, 0.5) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
         del lg, ix, wt
     del flushbuf
+    note("route sweep done")
 
     if s.backward:
         # the routing backward (gradients of the top-k weights and router
@@ -355,6 +363,7 @@ def main():
             torch.cuda.synchronize()
             wms = g0.elapsed_time(g1) / args.steps
             variants[vname] = {"ms_per_step": round(wms, 4), "tokens_per_s": round(s.T / (wms * 1e-3), 1)}
+        note("variants done")
 
     R, T, H, F, E, k = s.R, s.T, s.H, s.F, s.E, s.k
     esz = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32}[s.dtype]
@@ -420,6 +429,8 @@ def main():
     cpu = None
     if args.cpu_sample > 0:
         from oracle import oracle as orc
+
+        note("CPU oracle baseline ...")
 
         lg = w.logits()
         xs = w.x()

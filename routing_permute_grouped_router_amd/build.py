@@ -40,9 +40,9 @@ def _check_scratch(src: str, text: str) -> None:
             raise RuntimeError(f"{src}: kernel {fn} spills to scratch ({m.group(2)} bytes per lane)")
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _compile(src: str, verbose: bool, extra: list) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", src, "-o", obj, "-Rpass-analysis=kernel-resource-usage"]
+    cmd = [HIPCC, *COMMON, *extra, "-x", "hip", "-c", src, "-o", obj, "-Rpass-analysis=kernel-resource-usage"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,14 +56,16 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, extra: tuple = ()) -> str:
+    """extra: further hipcc flags for every compile and the link (host-only
+    sanitizer builds pass -Xarch_host forms here)."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, list(extra)), srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *extra, "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

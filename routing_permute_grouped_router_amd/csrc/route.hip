@@ -19,17 +19,48 @@
 // formed in the same order by all of them.  Lane r writes the picks j with
 // j % L == r.
 //
+// The per-lane scan of a pick is branch-free (compares and selects, two
+// independent chains over the two halves of the lane's slots, so the
+// dependent compare-select latency is halved), and the lane exchanges inside
+// a row of 16 are DPP moves: quad permutes for partners 1 and 2 apart, then
+// the half-row and row mirrors (lane i with 7 - i, 15 - i), which pair whole
+// quads and half-rows once those agree.  Only groups of 32 lanes (E > 512)
+// exchange through ds_bpermute.
+//
 // With an expert bias (TransformerEngine page, router commits: an optional
 // expert routing bias with a zero bias matching no bias), the selection runs
 // on the key fl32(logit + bias[e]) and each pick carries its unbiased logit
 // along, from which the weights are formed exactly as without a bias.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
-    return v > bv || (v == bv && e < be);
+// The value of the partner lane at stage OFF of a group reduction (stages
+// run OFF = 1, 2, 4, ... so each stage pairs lanes whose earlier stages agree).
+template <int OFF>
+__device__ __forceinline__ int partner(int x) {
+    if constexpr (OFF == 1) return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+    else if constexpr (OFF == 2) return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+    else if constexpr (OFF == 4) return __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false); // half-row mirror
+    else if constexpr (OFF == 8) return __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false); // row mirror
+    else return __shfl_xor(x, OFF, kWave);
+}
+template <int OFF>
+__device__ __forceinline__ float partner(float x) {
+    return __int_as_float(partner<OFF>(__float_as_int(x)));
+}
+
+// f(integral_constant<OFF>) for OFF = 1, 2, 4, ... < L
+template <int L, class F>
+__device__ __forceinline__ void for_stages(F&& f) {
+    if constexpr (L > 1) f(std::integral_constant<int, 1>{});
+    if constexpr (L > 2) f(std::integral_constant<int, 2>{});
+    if constexpr (L > 4) f(std::integral_constant<int, 4>{});
+    if constexpr (L > 8) f(std::integral_constant<int, 8>{});
+    if constexpr (L > 16) f(std::integral_constant<int, 16>{});
 }
 
 template <int L, int VPL, int KMAX, bool BIAS>
@@ -81,15 +112,14 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         for (int i = 0; i < VPL; ++i) kv[i] = v[i];
     }
     // group-wide reductions (the L lanes of a group are consecutive and
-    // aligned, so xor offsets below L stay inside it)
+    // aligned, so every partner stays inside it; a + b == b + a, so all lanes
+    // of the group end with the same bits)
     auto gmax = [&](float x) {
-#pragma unroll
-        for (int off = L / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+        for_stages<L>([&](auto o) { x = fmaxf(x, partner<decltype(o)::value>(x)); });
         return x;
     };
     auto gsum = [&](float x) {
-#pragma unroll
-        for (int off = L / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+        for_stages<L>([&](auto o) { x += partner<decltype(o)::value>(x); });
         return x;
     };
 
@@ -100,29 +130,43 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         pv[j] = -INFINITY;
         pe[j] = -1;
         if (j >= k) continue;
-        float bk = -INFINITY, bu = -INFINITY;  // best key and its logit
-        int be = 0x7fffffff;
+        // the lane's best available slot: slots in ascending order, a strictly
+        // larger key replaces, so equal keys keep the lower slot; the first
+        // available slot is always taken (a key of -inf included)
+        constexpr int H2 = VPL / 2;
+        float k0 = -INFINITY, k1 = -INFINITY, u0 = -INFINITY, u1 = -INFINITY;
+        int i0 = -1, i1 = -1;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int e = r * VPL + i;
-            if ((avail >> i & 1) && better(kv[i], e, bk, be)) {
-                bk = kv[i];
-                bu = v[i];
-                be = e;
+        for (int i = 0; i < H2; ++i) {
+            const bool t0 = ((avail >> i) & 1u) & ((kv[i] > k0) | (i0 < 0));
+            const bool t1 = ((avail >> (i + H2)) & 1u) & ((kv[i + H2] > k1) | (i1 < 0));
+            k0 = t0 ? kv[i] : k0;
+            i0 = t0 ? i : i0;
+            k1 = t1 ? kv[i + H2] : k1;
+            i1 = t1 ? i + H2 : i1;
+            if constexpr (BIAS) {
+                u0 = t0 ? v[i] : u0;
+                u1 = t1 ? v[i + H2] : u1;
             }
         }
-#pragma unroll
-        for (int off = L / 2; off > 0; off >>= 1) {
-            const float ok = __shfl_xor(bk, off, kWave);
-            const int oe = __shfl_xor(be, off, kWave);
-            const float ou = BIAS ? __shfl_xor(bu, off, kWave) : ok;
-            if (better(ok, oe, bk, be)) {
-                bk = ok;
-                bu = ou;
-                be = oe;
-            }
-        }
-        if (be / VPL == r) avail &= ~(1u << (be % VPL));  // the owning lane retires the pick
+        const bool hi = (i1 >= 0) & ((k1 > k0) | (i0 < 0));  // ties keep the lower half
+        float bk = hi ? k1 : k0;
+        float bu = BIAS ? (hi ? u1 : u0) : bk;
+        const int bi = hi ? i1 : i0;
+        int be = bi < 0 ? 0x7fffffff : r * VPL + bi;  // no slot left: loses every comparison
+        for_stages<L>([&](auto o) {
+            constexpr int OFF = decltype(o)::value;
+            // every lane reads its partner before any select: a DPP read
+            // under a partial exec mask would see inactive lanes
+            const float ok = partner<OFF>(bk);
+            const int oe = partner<OFF>(be);
+            const float ou = BIAS ? partner<OFF>(bu) : ok;
+            const bool t = (ok > bk) | ((ok == bk) & (oe < be));
+            bu = t ? ou : bu;
+            bk = t ? ok : bk;
+            be = t ? oe : be;
+        });
+        avail &= (be / VPL == r) ? ~(1u << (be % VPL)) : ~0u;  // the owning lane retires the pick
         pv[j] = BIAS ? bu : bk;
         pe[j] = be;
     }
