@@ -38,7 +38,7 @@
 #endif
 
 /* Storage formats understood by the oracle (its own numbering). */
-enum { OR_F32 = 0, OR_BF16 = 1, OR_MXFP8 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_MXFP8 = 2, OR_MXFP4 = 3 };
 /* Score functions. */
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
 
@@ -160,6 +160,38 @@ uint8_t or_e4m3_from_double(double v) {
     return (uint8_t)(sign | ((e + 7) << 3) | m);
 }
 
+/* OCP E2M1 ("FP4"): 1 sign, 2 exponent bits (bias 1), 1 mantissa bit, no
+ * infinities or NaN [OCP-MX, element formats]: magnitudes 0 and 0.5
+ * (subnormal), 1, 1.5, 2, 3, 4, 6.  A code is the low 4 bits of c. */
+double or_double_from_e2m1(uint8_t c) {
+    const int s = (c >> 3) & 1, ex = (c >> 1) & 3, m = c & 1;
+    const double v = ex == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, ex - 1);
+    return s ? -v : v;
+}
+
+/* Round-to-nearest-even to E2M1, saturating to +-6 (the MX conversion clamps
+ * values beyond the element format's largest normal).  The quantum is
+ * 2^(e-1) for |v| in [2^e, 2^(e+1)), e >= 0, and the subnormal 0.5 below 1;
+ * nearbyint's ties to even land on the even mantissa. */
+uint8_t or_e2m1_from_double(double v) {
+    const uint8_t sign = signbit(v) ? 0x8 : 0x0;
+    if (isnan(v)) return (uint8_t)(sign | 0x7);
+    const double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);
+    int e = e2 - 1; /* a in [2^e, 2^(e+1)) */
+    if (e < 0) e = 0;
+    const double quantum = ldexp(1.0, e - 1);
+    double r = nearbyint(a / quantum) * quantum;
+    if (r > 6.0) r = 6.0;
+    if (r < 1.0) return (uint8_t)(sign | (int)(r / 0.5)); /* 0 or 0.5 */
+    frexp(r, &e2);
+    e = e2 - 1;
+    const int m = (int)(r / ldexp(1.0, e - 1)) - 2;
+    return (uint8_t)(sign | ((e + 1) << 1) | m);
+}
+
 /* E8M0 shared scale: code c means 2^(c-127); 255 is NaN. */
 double or_double_from_e8m0(uint8_t c) {
     if (c == 255) return NAN;
@@ -168,10 +200,13 @@ double or_double_from_e8m0(uint8_t c) {
 
 /* MX block quantisation of one block of n (<= 32) values [OCP-MX, conversion
  * to MX formats]: shared_exp = floor(log2(max |v|)) - emax_elem, with
- * emax_elem = 8 for E4M3, clamped to the E8M0 range [-127, 127] (an all-zero
- * block therefore gets code 0); each element is v / 2^shared_exp rounded to
- * E4M3 (RNE, saturating). */
-static void or_mx_block(const double* v, int n, uint8_t* codes, uint8_t* scale) {
+ * emax_elem the exponent of the element format's largest normal (8 for E4M3,
+ * 448 = 1.75 * 2^8; 2 for E2M1, 6 = 1.5 * 2^2), clamped to the E8M0 range
+ * [-127, 127] (an all-zero block therefore gets code 0); each element is
+ * v / 2^shared_exp rounded to the element format (RNE, saturating).  One code
+ * per element (E2M1: in the low 4 bits). */
+static void or_mx_block_fmt(int fmt, const double* v, int n, uint8_t* codes, uint8_t* scale) {
+    const int fp4 = fmt == OR_MXFP4;
     double amax = 0.0;
     for (int i = 0; i < n; ++i) {
         double a = fabs(v[i]);
@@ -183,28 +218,50 @@ static void or_mx_block(const double* v, int n, uint8_t* codes, uint8_t* scale) 
     } else {
         int e2;
         frexp(amax, &e2);   /* floor(log2(amax)) = e2 - 1 */
-        se = (e2 - 1) - 8;
+        se = (e2 - 1) - (fp4 ? 2 : 8);
         if (se < -127) se = -127;
         if (se > 127) se = 127;
     }
     *scale = (uint8_t)(se + 127);
-    for (int i = 0; i < n; ++i) codes[i] = or_e4m3_from_double(ldexp(v[i], -se));
+    for (int i = 0; i < n; ++i)
+        codes[i] = fp4 ? or_e2m1_from_double(ldexp(v[i], -se)) : or_e4m3_from_double(ldexp(v[i], -se));
+}
+static void or_mx_block(const double* v, int n, uint8_t* codes, uint8_t* scale) {
+    or_mx_block_fmt(OR_MXFP8, v, n, codes, scale);
 }
 
-/* Quantise a row-major [rows, cols] float32 matrix to MXFP8 with blocks of 32
- * along the columns.  cols must be a multiple of 32. */
-int or_mx_quantize_f32(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales) {
-    if (cols % OR_MX_BLOCK) return 1;
+/* MXFP4 rows hold two E2M1 codes per byte: element 2i in the low 4 bits of
+ * byte i, element 2i + 1 in the high 4 bits. */
+static inline uint8_t or_fp4_code(const void* row, int64_t i) {
+    const uint8_t b = ((const uint8_t*)row)[i >> 1];
+    return (uint8_t)((i & 1) ? b >> 4 : b & 0xF);
+}
+static void or_fp4_pack(const uint8_t* codes, int64_t n, uint8_t* out) {
+    for (int64_t j = 0; j < n / 2; ++j) out[j] = (uint8_t)((codes[2 * j] & 0xF) | ((codes[2 * j + 1] & 0xF) << 4));
+}
+
+/* Quantise a row-major [rows, cols] float32 matrix to MXFP8 (fmt 2: one code
+ * byte per element) or MXFP4 (fmt 3: packed, cols / 2 bytes per row) with
+ * blocks of 32 along the columns.  cols must be a multiple of 32. */
+int or_mx_quantize_f32_fmt(int fmt, const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales) {
+    if (cols % OR_MX_BLOCK || (fmt != OR_MXFP8 && fmt != OR_MXFP4)) return 1;
     const int64_t nb = cols / OR_MX_BLOCK;
+    const int64_t rb = fmt == OR_MXFP4 ? cols / 2 : cols;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         double buf[OR_MX_BLOCK];
+        uint8_t c[OR_MX_BLOCK];
         for (int64_t b = 0; b < nb; ++b) {
             for (int i = 0; i < OR_MX_BLOCK; ++i) buf[i] = (double)in[r * cols + b * OR_MX_BLOCK + i];
-            or_mx_block(buf, OR_MX_BLOCK, codes + r * cols + b * OR_MX_BLOCK, scales + r * nb + b);
+            or_mx_block_fmt(fmt, buf, OR_MX_BLOCK, c, scales + r * nb + b);
+            if (fmt == OR_MXFP4) or_fp4_pack(c, OR_MX_BLOCK, codes + r * rb + b * (OR_MX_BLOCK / 2));
+            else memcpy(codes + r * rb + b * OR_MX_BLOCK, c, OR_MX_BLOCK);
         }
     }
     return 0;
+}
+int or_mx_quantize_f32(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales) {
+    return or_mx_quantize_f32_fmt(OR_MXFP8, in, rows, cols, codes, scales);
 }
 
 /* Bulk helpers for the tests. */
@@ -217,26 +274,42 @@ void or_e4m3_from_double_array(const double* in, uint8_t* out, int64_t n) {
 void or_double_from_e4m3_array(const uint8_t* in, double* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = or_double_from_e4m3(in[i]);
 }
+void or_e2m1_from_double_array(const double* in, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = or_e2m1_from_double(in[i]);
+}
 
-/* Decode element i of a stored row to double.  For MXFP8 the row's scale
- * array holds one E8M0 code per 32 consecutive elements. */
+/* Decode element i of a stored row to double.  For MXFP8 and MXFP4 the
+ * row's scale array holds one E8M0 code per 32 consecutive elements. */
 static inline double or_load(int fmt, const void* row, const uint8_t* scale_row, int64_t i) {
     switch (fmt) {
     case OR_F32: return (double)((const float*)row)[i];
     case OR_BF16: return or_double_from_bf16(((const uint16_t*)row)[i]);
+    case OR_MXFP4: return or_double_from_e2m1(or_fp4_code(row, i)) * or_double_from_e8m0(scale_row[i / OR_MX_BLOCK]);
     default:
         return or_double_from_e4m3(((const uint8_t*)row)[i]) * or_double_from_e8m0(scale_row[i / OR_MX_BLOCK]);
     }
 }
 
+static inline int or_is_mx(int fmt) { return fmt == OR_MXFP8 || fmt == OR_MXFP4; }
 static inline size_t or_elem_bytes(int fmt) { return fmt == OR_F32 ? 4 : (fmt == OR_BF16 ? 2 : 1); }
+/* Size in bytes of one stored row of n elements (data only; MXFP4 packs two
+ * elements per byte). */
+static inline size_t or_row_bytes(int fmt, int64_t n) {
+    return fmt == OR_MXFP4 ? (size_t)n / 2 : (size_t)n * or_elem_bytes(fmt);
+}
 
-/* Store a row of n doubles in a storage format (MXFP8: n % 32 == 0). */
+/* Store a row of n doubles in a storage format (MX formats: n % 32 == 0). */
 static void or_store_row(int fmt, const double* v, int64_t n, void* row, uint8_t* scale_row) {
     if (fmt == OR_F32) {
         for (int64_t i = 0; i < n; ++i) ((float*)row)[i] = (float)v[i];
     } else if (fmt == OR_BF16) {
         for (int64_t i = 0; i < n; ++i) ((uint16_t*)row)[i] = or_bf16_from_double(v[i]);
+    } else if (fmt == OR_MXFP4) {
+        uint8_t c[OR_MX_BLOCK];
+        for (int64_t b = 0; b < n / OR_MX_BLOCK; ++b) {
+            or_mx_block_fmt(OR_MXFP4, v + b * OR_MX_BLOCK, OR_MX_BLOCK, c, scale_row + b);
+            or_fp4_pack(c, OR_MX_BLOCK, (uint8_t*)row + b * (OR_MX_BLOCK / 2));
+        }
     } else {
         for (int64_t b = 0; b < n / OR_MX_BLOCK; ++b)
             or_mx_block(v + b * OR_MX_BLOCK, OR_MX_BLOCK, (uint8_t*)row + b * OR_MX_BLOCK, scale_row + b);
@@ -252,9 +325,10 @@ static void or_round_trip_row(int fmt, double* v, int64_t n) {
     } else {
         for (int64_t b = 0; b < n / OR_MX_BLOCK; ++b) {
             uint8_t c[OR_MX_BLOCK], s;
-            or_mx_block(v + b * OR_MX_BLOCK, OR_MX_BLOCK, c, &s);
+            or_mx_block_fmt(fmt, v + b * OR_MX_BLOCK, OR_MX_BLOCK, c, &s);
             for (int i = 0; i < OR_MX_BLOCK; ++i)
-                v[b * OR_MX_BLOCK + i] = or_double_from_e4m3(c[i]) * or_double_from_e8m0(s);
+                v[b * OR_MX_BLOCK + i] =
+                    (fmt == OR_MXFP4 ? or_double_from_e2m1(c[i]) : or_double_from_e4m3(c[i])) * or_double_from_e8m0(s);
         }
     }
 }
@@ -449,14 +523,13 @@ void or_permute(int T, int k, int64_t n_rows, int64_t row_bytes, const uint8_t* 
 void or_expert_row(int H, int F, int fmt, const void* x_row, const uint8_t* x_scale_row, const void* w1_e,
                    const uint8_t* w1s_e, const void* w2_e, const uint8_t* w2s_e, int h_fmt, int y_fmt, int s_fmt,
                    int site, double row_w, void* h_out, uint8_t* h_scale_out, void* yp_out, void* stash_out) {
-    const size_t eb = or_elem_bytes(fmt);
     double* xv = (double*)malloc(sizeof(double) * (size_t)H);
     double* hv = (double*)malloc(sizeof(double) * (size_t)F);
     double* gu = (double*)malloc(sizeof(double) * 2 * (size_t)F);
     for (int h = 0; h < H; ++h) xv[h] = or_load(fmt, x_row, x_scale_row, h);
     for (int n = 0; n < 2 * F; ++n) {
-        const void* wrow = (const uint8_t*)w1_e + (size_t)n * H * eb;
-        const uint8_t* wsrow = fmt == OR_MXFP8 ? w1s_e + (size_t)n * (H / OR_MX_BLOCK) : NULL;
+        const void* wrow = (const uint8_t*)w1_e + (size_t)n * or_row_bytes(fmt, H);
+        const uint8_t* wsrow = or_is_mx(fmt) ? w1s_e + (size_t)n * (H / OR_MX_BLOCK) : NULL;
         double acc = 0.0;
         for (int h = 0; h < H; ++h) acc += xv[h] * or_load(fmt, wrow, wsrow, h);
         gu[n] = acc;
@@ -472,8 +545,8 @@ void or_expert_row(int H, int F, int fmt, const void* x_row, const uint8_t* x_sc
     if (yp_out) {
         double* yv = (double*)malloc(sizeof(double) * (size_t)H);
         for (int o = 0; o < H; ++o) {
-            const void* wrow = (const uint8_t*)w2_e + (size_t)o * F * eb;
-            const uint8_t* wsrow = fmt == OR_MXFP8 ? w2s_e + (size_t)o * (F / OR_MX_BLOCK) : NULL;
+            const void* wrow = (const uint8_t*)w2_e + (size_t)o * or_row_bytes(fmt, F);
+            const uint8_t* wsrow = or_is_mx(fmt) ? w2s_e + (size_t)o * (F / OR_MX_BLOCK) : NULL;
             double acc = 0.0;
             for (int f = 0; f < F; ++f) acc += hv[f] * or_load(fmt, wrow, wsrow, f);
             yv[o] = site == OR_AT_FC2 ? row_w * acc : acc;
@@ -486,8 +559,6 @@ void or_expert_row(int H, int F, int fmt, const void* x_row, const uint8_t* x_sc
     free(gu);
 }
 
-/* Size in bytes of one stored row of n elements (data only). */
-static inline size_t or_row_bytes(int fmt, int64_t n) { return (size_t)n * or_elem_bytes(fmt); }
 
 /* ------------------------------------------------------------------------ */
 /* Forward for a list of tokens (per-token evaluation, no permutation).     */
@@ -511,13 +582,12 @@ int or_forward_tokens(int H, int F, int k, int fmt, int h_fmt, int y_fmt, int s_
                       const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, const int32_t* idx,
                       const float* w, void* h_out, uint8_t* h_scale_out, void* yp_out, void* stash_out,
                       void* y_out) {
-    if (fmt == OR_MXFP8 && (H % OR_MX_BLOCK || F % OR_MX_BLOCK)) return 1;
-    if (h_fmt == OR_MXFP8 && F % OR_MX_BLOCK) return 1;
-    const size_t eb = or_elem_bytes(fmt);
-    const size_t w1_expert = (size_t)2 * F * H * eb, w2_expert = (size_t)H * F * eb;
+    if (or_is_mx(fmt) && (H % OR_MX_BLOCK || F % OR_MX_BLOCK)) return 1;
+    if (or_is_mx(h_fmt) && F % OR_MX_BLOCK) return 1;
+    const size_t w1_expert = (size_t)2 * F * or_row_bytes(fmt, H), w2_expert = (size_t)H * or_row_bytes(fmt, F);
     const size_t w1s_expert = (size_t)2 * F * (H / OR_MX_BLOCK), w2s_expert = (size_t)H * (F / OR_MX_BLOCK);
     const size_t hb = or_row_bytes(h_fmt, F), yb = or_row_bytes(y_fmt, H), sb = or_row_bytes(s_fmt, 2 * F);
-    const int64_t hsb = h_fmt == OR_MXFP8 ? F / OR_MX_BLOCK : 0;
+    const int64_t hsb = or_is_mx(h_fmt) ? F / OR_MX_BLOCK : 0;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t ij = 0; ij < (int64_t)n_tok * k; ++ij) {
         const int64_t i = ij / k;
@@ -525,11 +595,11 @@ int or_forward_tokens(int H, int F, int k, int fmt, int h_fmt, int y_fmt, int s_
         const int64_t t = tokens[i];
         const int32_t e = idx[t * k + j];
         if (e < 0) continue;
-        const void* xr = (const uint8_t*)x + (size_t)t * H * eb;
-        const uint8_t* xs = fmt == OR_MXFP8 ? x_scale + (size_t)t * (H / OR_MX_BLOCK) : NULL;
+        const void* xr = (const uint8_t*)x + (size_t)t * or_row_bytes(fmt, H);
+        const uint8_t* xs = or_is_mx(fmt) ? x_scale + (size_t)t * (H / OR_MX_BLOCK) : NULL;
         or_expert_row(H, F, fmt, xr, xs, (const uint8_t*)w1 + e * w1_expert,
-                      fmt == OR_MXFP8 ? w1_scale + e * w1s_expert : NULL, (const uint8_t*)w2 + e * w2_expert,
-                      fmt == OR_MXFP8 ? w2_scale + e * w2s_expert : NULL, h_fmt, y_fmt, s_fmt, site,
+                      or_is_mx(fmt) ? w1_scale + e * w1s_expert : NULL, (const uint8_t*)w2 + e * w2_expert,
+                      or_is_mx(fmt) ? w2_scale + e * w2s_expert : NULL, h_fmt, y_fmt, s_fmt, site,
                       (double)w[t * k + j],
                       h_out ? (uint8_t*)h_out + ij * hb : NULL, h_scale_out ? h_scale_out + ij * hsb : NULL,
                       (uint8_t*)yp_out + ij * yb, stash_out ? (uint8_t*)stash_out + ij * sb : NULL);
@@ -603,7 +673,7 @@ int or_backward(int T, int H, int F, int E, int k, int fmt, int g_fmt, const voi
                 const void* w2, const float* w, const int32_t* row_map, const int32_t* src_map,
                 const int32_t* offsets, const void* h_saved, int h_fmt, const void* stash, int s_fmt,
                 const void* dy, void* dyp, void* dgu, void* dxp, void* dx, float* dw1, float* dw2) {
-    if (fmt == OR_MXFP8 || h_fmt == OR_MXFP8) return 1;
+    if (or_is_mx(fmt) || or_is_mx(h_fmt)) return 1;
     const size_t eb = or_elem_bytes(fmt), gb = or_elem_bytes(g_fmt);
     const size_t hb = or_row_bytes(h_fmt, F), sb = or_row_bytes(s_fmt, 2 * F);
     const int64_t R = offsets[E];
@@ -731,7 +801,7 @@ static void or_route_gu(int H, int F, int fmt, int s_fmt, int h_fmt, const void*
 int or_backward_dx_tokens(int H, int F, int k, int fmt, int g_fmt, int h_fmt, int s_fmt, int n_tok,
                           const int32_t* tokens, const void* x, const void* w1, const void* w2,
                           const int32_t* idx, const float* w, const void* dy, void* dx_out) {
-    if (fmt == OR_MXFP8) return 1;
+    if (or_is_mx(fmt)) return 1;
     const size_t eb = or_elem_bytes(fmt), gb = or_elem_bytes(g_fmt);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < n_tok; ++i) {
@@ -789,7 +859,7 @@ int or_backward_dw_entries(int H, int F, int k, int fmt, int g_fmt, int h_fmt, i
                            const void* x, const void* w1, const void* w2, const float* w, const int32_t* src_map,
                            const int32_t* offsets, const void* dy, int n2, const int32_t* o2, const int32_t* f2,
                            double* dw2_out, int n1, const int32_t* n1i, const int32_t* c1, double* dw1_out) {
-    if (fmt == OR_MXFP8) return 1;
+    if (or_is_mx(fmt)) return 1;
     const size_t eb = or_elem_bytes(fmt), gb = or_elem_bytes(g_fmt);
     const int64_t r0 = offsets[e], r1 = offsets[e + 1];
     const uint8_t* w1e = (const uint8_t*)w1 + (size_t)e * 2 * F * H * eb;
@@ -866,17 +936,17 @@ void or_swiglu_grad_rows(const double* gu, const double* dh, int64_t rows, int F
 
 /* Rows of n doubles stored in a format (or_store_row per row). */
 void or_store_rows(int fmt, const double* v, int64_t rows, int64_t n, void* out, uint8_t* scale_out) {
-    const size_t rb = (size_t)n * or_elem_bytes(fmt);
+    const size_t rb = or_row_bytes(fmt, n);
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
         or_store_row(fmt, v + r * n, n, (uint8_t*)out + r * rb,
-                     fmt == OR_MXFP8 ? scale_out + r * (n / OR_MX_BLOCK) : NULL);
+                     or_is_mx(fmt) ? scale_out + r * (n / OR_MX_BLOCK) : NULL);
 }
 
 /* Rows of n stored values decoded to double: or_load per element, with the
  * E4M3 decoder tabulated over its 256 codes first for MXFP8. */
 void or_decode_rows(int fmt, const void* in, const uint8_t* scale_in, int64_t rows, int64_t n, double* out) {
-    const size_t rb = (size_t)n * or_elem_bytes(fmt);
+    const size_t rb = or_row_bytes(fmt, n);
     if (fmt == OR_MXFP8) {
         double tab[256];
         for (int c = 0; c < 256; ++c) tab[c] = or_double_from_e4m3((uint8_t)c);
@@ -895,7 +965,8 @@ void or_decode_rows(int fmt, const void* in, const uint8_t* scale_in, int64_t ro
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         const void* row = (const uint8_t*)in + r * rb;
-        for (int64_t i = 0; i < n; ++i) out[r * n + i] = or_load(fmt, row, NULL, i);
+        const uint8_t* srow = fmt == OR_MXFP4 ? scale_in + r * (n / OR_MX_BLOCK) : NULL;
+        for (int64_t i = 0; i < n; ++i) out[r * n + i] = or_load(fmt, row, srow, i);
     }
 }
 

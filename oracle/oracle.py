@@ -5,7 +5,9 @@ benchmark's CPU-baseline leg, never by the product path.  It shares no code with
 the HIP library.
 
 Formats: "f32" (float32), "bf16" (uint16 bit patterns), "mxfp8" (uint8 E4M3
-codes plus uint8 E8M0 scales, one per 32 elements along the last axis).
+codes plus uint8 E8M0 scales, one per 32 elements along the last axis),
+"mxfp4" (E2M1 codes packed two per byte, element 2i in the low 4 bits of byte
+i, so a row of n elements is n / 2 bytes; the same E8M0 scales).
 """
 from __future__ import annotations
 
@@ -18,9 +20,15 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "moe_oracle.c")
-FMT = {"f32": 0, "bf16": 1, "mxfp8": 2}
+FMT = {"f32": 0, "bf16": 1, "mxfp8": 2, "mxfp4": 3}
+MX = ("mxfp8", "mxfp4")
 SCORE = {"softmax": 0, "sigmoid": 1}
-_NP = {"f32": np.float32, "bf16": np.uint16, "mxfp8": np.uint8}
+_NP = {"f32": np.float32, "bf16": np.uint16, "mxfp8": np.uint8, "mxfp4": np.uint8}
+
+
+def row_len(fmt: str, n: int) -> int:
+    """Stored entries of a row of n elements (MXFP4: n / 2 bytes)."""
+    return n // 2 if fmt == "mxfp4" else n
 
 
 def build(verbose: bool = False) -> str:
@@ -54,6 +62,10 @@ def _load():
         "or_e4m3_from_double_array": (None, [P, P, I64]),
         "or_double_from_e4m3_array": (None, [P, P, I64]),
         "or_mx_quantize_f32": (I32, [P, I64, I64, P, P]),
+        "or_mx_quantize_f32_fmt": (I32, [I32, P, I64, I64, P, P]),
+        "or_e2m1_from_double": (ctypes.c_uint8, [ctypes.c_double]),
+        "or_double_from_e2m1": (ctypes.c_double, [ctypes.c_uint8]),
+        "or_e2m1_from_double_array": (None, [P, P, I64]),
         "or_route": (I32, [I32, I32, I32, I32, I32, P, P, P]),
         "or_route_biased": (I32, [I32, I32, I32, I32, I32, P, P, P, P]),
         "or_group": (I32, [I32, I32, I32, I32, I64, P, P, P, P, P, P]),
@@ -129,29 +141,46 @@ def f64_from_e8m0(c) -> np.ndarray:
     return np.where(c == 255, np.nan, out)
 
 
-def mx_quantize(v) -> tuple:
-    """float32 [..., n] (n % 32 == 0) -> (E4M3 codes uint8 [..., n], E8M0 uint8 [..., n/32])."""
+def e2m1_from_f64(v) -> np.ndarray:
+    """Round to E2M1 (RNE, saturating at 6): one 4-bit code per uint8."""
+    v = _c(np.asarray(v, np.float64), np.float64)
+    out = np.empty(v.shape, np.uint8)
+    _load().or_e2m1_from_double_array(v.ctypes.data, out.ctypes.data, v.size)
+    return out
+
+
+def f64_from_e2m1(c) -> np.ndarray:
+    """E2M1 codes (low 4 bits of each uint8) to float64."""
+    lib = _load()
+    tab = np.array([lib.or_double_from_e2m1(i) for i in range(16)])
+    return tab[np.asarray(c, np.uint8) & 0xF]
+
+
+def mx_quantize(v, fmt: str = "mxfp8") -> tuple:
+    """float32 [..., n] (n % 32 == 0) -> (codes uint8 [..., n] (E4M3) or [..., n/2]
+    (packed E2M1), E8M0 scales uint8 [..., n/32])."""
     v = _c(v, np.float32)
     cols = v.shape[-1]
     rows = v.size // cols
-    codes = np.empty(v.shape, np.uint8)
+    codes = np.empty(v.shape[:-1] + (row_len(fmt, cols),), np.uint8)
     scales = np.empty(v.shape[:-1] + (cols // 32,), np.uint8)
-    if _load().or_mx_quantize_f32(v.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data):
+    if _load().or_mx_quantize_f32_fmt(FMT[fmt], v.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data):
         raise ValueError("last dimension must be a multiple of 32")
     return codes, scales
 
 
-def mx_dequantize(codes, scales) -> np.ndarray:
-    """E4M3 codes [..., n] with E8M0 scales [..., n/32] -> float64 values."""
+def mx_dequantize(codes, scales, fmt: str = "mxfp8") -> np.ndarray:
+    """Codes [..., n] (E4M3) or [..., n/2] (packed E2M1) with E8M0 scales
+    [..., n/32] -> float64 values [..., n]."""
     codes = _c(codes, np.uint8)
     scales = _c(scales, np.uint8)
-    n = codes.shape[-1]
-    rows = codes.size // n if n else 0
+    n = codes.shape[-1] * (2 if fmt == "mxfp4" else 1)
+    rows = codes.size // codes.shape[-1] if codes.shape[-1] else 0
     if scales.shape != codes.shape[:-1] + (n // 32,):
         raise ValueError("scales must hold one code per 32 elements of the last axis")
-    out = np.empty(codes.shape, np.float64)
+    out = np.empty(codes.shape[:-1] + (n,), np.float64)
     if codes.size:
-        _load().or_decode_rows(FMT["mxfp8"], codes.ctypes.data, scales.ctypes.data, rows, n, out.ctypes.data)
+        _load().or_decode_rows(FMT[fmt], codes.ctypes.data, scales.ctypes.data, rows, n, out.ctypes.data)
     return out
 
 
@@ -161,7 +190,7 @@ def decode(fmt: str, data, scale=None) -> np.ndarray:
         return np.asarray(data, np.float32).astype(np.float64)
     if fmt == "bf16":
         return f64_from_bf16(data)
-    return mx_dequantize(data, scale)
+    return mx_dequantize(data, scale, fmt)
 
 
 # ---------------------------------------------------------------- the path
@@ -289,8 +318,8 @@ def forward_tokens(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=None
     tokens = _c(np.asarray(tokens, np.int32), np.int32)
     n = tokens.size
     k = s.k
-    h = np.empty((n, k, s.F), _NP[h_fmt])
-    h_scale = np.empty((n, k, s.F // 32), np.uint8) if h_fmt == "mxfp8" else None
+    h = np.empty((n, k, row_len(h_fmt, s.F)), _NP[h_fmt])
+    h_scale = np.empty((n, k, s.F // 32), np.uint8) if h_fmt in MX else None
     yp = np.empty((n, k, s.H), _NP[y_fmt])
     y = np.empty((n, s.H), _NP[y_fmt])
     stash = np.empty((n, k, 2 * s.F), _NP[s_fmt]) if want_stash else None
@@ -416,13 +445,13 @@ def backward_dw_entries(shape, e, x, w1, w2, w, src_map, offsets, dy, dw2_idx, d
 # float64 additions differs from the loop form; the tests pin this front end
 # to it bit for bit on small shapes.
 def _store_rows(fmt: str, v: np.ndarray):
-    """float64 [rows, n] -> stored rows (MXFP8: (codes, scales))."""
+    """float64 [rows, n] -> stored rows (MX formats: (codes, scales))."""
     v = np.ascontiguousarray(v, np.float64)
     rows, n = v.shape
-    out = np.empty((rows, n), _NP[fmt])
-    sc = np.empty((rows, n // 32), np.uint8) if fmt == "mxfp8" else None
+    out = np.empty((rows, row_len(fmt, n)), _NP[fmt])
+    sc = np.empty((rows, n // 32), np.uint8) if fmt in MX else None
     _load().or_store_rows(FMT[fmt], v.ctypes.data, rows, n, out.ctypes.data, _p(sc))
-    return (out, sc) if fmt == "mxfp8" else out
+    return (out, sc) if fmt in MX else out
 
 
 def _swiglu_rows(gu: np.ndarray, F: int, rw=None) -> np.ndarray:
@@ -462,8 +491,8 @@ def forward_experts(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=Non
     idx = np.asarray(idx, np.int32)
     w = np.asarray(w, np.float32)
     sel = idx[tokens]                                   # [n, k]
-    h = np.zeros((n, k, s.F), _NP[h_fmt])
-    h_sc = np.zeros((n, k, s.F // 32), np.uint8) if h_fmt == "mxfp8" else None
+    h = np.zeros((n, k, row_len(h_fmt, s.F)), _NP[h_fmt])
+    h_sc = np.zeros((n, k, s.F // 32), np.uint8) if h_fmt in MX else None
     yp = np.zeros((n, k, s.H), _NP[y_fmt])
     stash = np.zeros((n, k, 2 * s.F), _NP[s_fmt]) if want_stash else None
     _load().or_set_swiglu_limit(float(limit))
@@ -477,9 +506,9 @@ def forward_experts(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=Non
         if want_stash:
             stash[ii, jj] = _store_rows(s_fmt, gu)
         hs = _store_rows(h_fmt, hv)
-        if h_fmt == "mxfp8":
+        if h_fmt in MX:
             h[ii, jj], h_sc[ii, jj] = hs
-            hq = decode("mxfp8", hs[0], hs[1])
+            hq = decode(h_fmt, hs[0], hs[1])
         else:
             h[ii, jj] = hs
             hq = decode(h_fmt, hs)
