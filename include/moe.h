@@ -66,9 +66,16 @@
  *   MOE_F32, MOE_BF16 or MOE_MXFP8 (OCP E4M3 codes, one byte each, plus one
  *   E8M0 scale byte per 32 consecutive elements of the contiguous dimension:
  *   x_scale [T,H/32], w1_scale [E][2F][H/32], w2_scale [E][H][F/32],
- *   h_scale [R_cap,F/32]).  Yp and y (and all activation gradients) are float32
- *   when dtype is MOE_F32 and bfloat16 otherwise ([TE-EP]: the output keeps
- *   x's dtype; MXFP8 layers return bfloat16 per [CUDNN]).  Every GEMM
+ *   h_scale [R_cap,F/32]).  MOE_MXFP4 (the MX analogue of [ISSUE]'s and
+ *   [CUDNN]'s NVFP4 recipe, native to CDNA4's scaled matrix cores): OCP E2M1
+ *   codes (1 sign, 2 exponent bits, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5,
+ *   2, 3, 4, 6) packed two per byte, element 2i in the low 4 bits of byte i, so
+ *   a row of n elements is n/2 bytes (x [T,H/2], w1 [E][2F][H/2], w2
+ *   [E][H][F/2], Xp [R_cap,H/2], h [R_cap,F/2]), with the same E8M0 scale
+ *   arrays as MXFP8; H and F must be multiples of 512.  Yp and y (and all
+ *   activation gradients) are float32 when dtype is MOE_F32 and bfloat16
+ *   otherwise ([TE-EP]: the output keeps x's dtype; MX layers return bfloat16
+ *   per [CUDNN]).  Every GEMM
  *   accumulates in float32 and rounds once when it stores.
  */
 #ifndef MOE_H
@@ -89,7 +96,7 @@ typedef enum moe_status {
     MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed    */
 } moe_status;
 
-typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2, MOE_MXFP4 = 3 } moe_dtype;
 typedef enum moe_score { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
 /* Where moe_forward applies the routing weights ([CUDNN] Summary: the router
  * weight in the FC1 or the FC2 epilogue; [TE-EP] commits: the weights may be
@@ -104,8 +111,9 @@ typedef enum moe_weight_site { MOE_WEIGHT_AT_COMBINE = 0, MOE_WEIGHT_AT_FC1 = 1,
 
 typedef struct moe_config {
     int32_t T;      /* tokens (>= 0)                                         */
-    int32_t H;      /* hidden size (multiple of 64; of 128 for MXFP8)        */
-    int32_t F;      /* per-expert FFN width (multiple of 64; of 128 for MXFP8) */
+    int32_t H;      /* hidden size (multiple of 128; of 512 for MXFP4)       */
+    int32_t F;      /* per-expert FFN width (multiple of 64; of 128 for MXFP8;
+                       of 512 for MXFP4)                                     */
     int32_t E;      /* experts (1..1024)                                     */
     int32_t k;      /* routes per token (1..min(E, 64))                      */
     int32_t align;  /* per-expert row alignment (>= 1)                       */
@@ -368,6 +376,16 @@ moe_status moe_backward(const moe_config* cfg, const void* dy, const float* w, c
 /* codes [rows, cols] u8, scales [rows, cols/32] u8 (E8M0).  Finite inputs.  */
 /* ---------------------------------------------------------------------- */
 moe_status moe_quantize_mxfp8(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                              void* stream);
+
+/* MXFP4 quantisation (the same OCP MX v1.0 rule with E2M1 elements): per block
+ * of 32, shared exponent = floor(log2(max|v|)) - 2 clamped to [-127, 127]
+ * (all-zero block -> code 0), elements v / 2^shared rounded to nearest even
+ * E2M1, saturating at +-6; a value that rounds to zero keeps its sign (code
+ * 8 for negative).  in [rows, cols] f32, cols % 32 == 0 -> codes [rows,
+ * cols/2] u8 (element 2i in the low 4 bits of byte i), scales [rows, cols/32]
+ * u8 (E8M0).  Finite inputs. */
+moe_status moe_quantize_mxfp4(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                               void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */

@@ -475,8 +475,9 @@ def _weights_f64(fmt: str, wt, wscale, e: int) -> np.ndarray:
 
 
 def forward_experts(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=None, w2_scale=None,
-                    want_stash: bool = False, site: str = "combine", limit: float = 0.0):
-    """forward_tokens evaluated expert by expert (same arguments and outputs).
+                    want_stash: bool = False, site: str = "combine", limit: float = 0.0, want_h_f64: bool = False):
+    """forward_tokens evaluated expert by expert (same arguments and outputs;
+    want_h_f64 adds "h_f64" [n, k, F], the float64 h before it is stored).
 
     For each expert e, the routes (i, j) of the listed tokens with idx = e form
     X_e (their x rows, decoded); GU = X_e W1s[e]^T, h = store_h(SwiGLU(GU)),
@@ -495,6 +496,7 @@ def forward_experts(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=Non
     h_sc = np.zeros((n, k, s.F // 32), np.uint8) if h_fmt in MX else None
     yp = np.zeros((n, k, s.H), _NP[y_fmt])
     stash = np.zeros((n, k, 2 * s.F), _NP[s_fmt]) if want_stash else None
+    h64 = np.zeros((n, k, s.F)) if want_h_f64 else None
     _load().or_set_swiglu_limit(float(limit))
     for e in np.unique(sel[sel >= 0]):
         ii, jj = np.nonzero(sel == e)
@@ -503,6 +505,8 @@ def forward_experts(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=Non
         gu = xe @ _weights_f64(fmt, w1, w1_scale, e).T
         rw = w[t, jj].astype(np.float64)
         hv = _swiglu_rows(gu, s.F, rw if site == "fc1" else None)
+        if want_h_f64:
+            h64[ii, jj] = hv
         if want_stash:
             stash[ii, jj] = _store_rows(s_fmt, gu)
         hs = _store_rows(h_fmt, hv)
@@ -526,7 +530,30 @@ def forward_experts(shape, tokens, x, w1, w2, idx, w, x_scale=None, w1_scale=Non
         out["h_scale"] = h_sc
     if want_stash:
         out["stash"] = stash
+    if want_h_f64:
+        out["h_f64"] = h64
     return out
+
+
+def down_projection(shape, experts, h, h_scale, w2, w2_scale=None, row_w=None):
+    """The down projection of given stored h rows: for row r of expert
+    experts[r] (-1: a row with no expert, left zero),
+        Yp[r] = store_out( (decode(h[r]) W2s[e]^T) * row_w[r] )
+    with float64 sums (row_w None: no weight), as in forward_experts.  h
+    [rows, F] in shape.dtype's stored form (MX: with h_scale [rows, F/32])."""
+    s = shape
+    fmt = s.dtype
+    y_fmt = "f32" if fmt == "f32" else "bf16"
+    experts = np.asarray(experts)
+    yp = np.zeros((experts.size, s.H), _NP[y_fmt])
+    for e in np.unique(experts[experts >= 0]):
+        r = np.flatnonzero(experts == e)
+        hq = decode(fmt, np.asarray(h)[r], None if h_scale is None else np.asarray(h_scale)[r])
+        ye = hq @ _weights_f64(fmt, w2, w2_scale, int(e)).T
+        if row_w is not None:
+            ye *= np.asarray(row_w, np.float64)[r, None]
+        yp[r] = _store_rows(y_fmt, ye)
+    return yp
 
 
 def backward_expert(shape, e: int, x, w1, w2, w, src_map, offsets, dy, limit: float = 0.0):

@@ -31,6 +31,7 @@ from .binding import (  # noqa: F401
     moe_grouped_swiglu_gemm,
     moe_permute,
     moe_permute_bwd,
+    moe_quantize_mxfp4,
     moe_quantize_mxfp8,
     moe_route,
     rows_capacity,

@@ -19,9 +19,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_MXFP8, MOE_MXFP4 = 0, 1, 2, 3
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8, "mxfp4": MOE_MXFP4}
 MOE_WEIGHT_AT_COMBINE, MOE_WEIGHT_AT_FC1, MOE_WEIGHT_AT_FC2 = 0, 1, 2
 WEIGHT_SITES = {"combine": MOE_WEIGHT_AT_COMBINE, "fc1": MOE_WEIGHT_AT_FC1, "fc2": MOE_WEIGHT_AT_FC2}
 SCORES = {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}
@@ -88,7 +88,15 @@ class MoEConfig:
 
     @property
     def store_dtype(self) -> torch.dtype:
-        return {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8}[self.dtype]
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8, "mxfp4": torch.uint8}[self.dtype]
+
+    @property
+    def is_mx(self) -> bool:
+        return self.dtype in ("mxfp8", "mxfp4")
+
+    def cols(self, n: int) -> int:
+        """Stored entries of a row of n elements (MXFP4 packs two per byte)."""
+        return n // 2 if self.dtype == "mxfp4" else n
 
     @property
     def out_dtype(self) -> torch.dtype:
@@ -119,6 +127,7 @@ _SIGS = {
     "moe_permute_bwd": (ctypes.c_int, [CFG, P, P, P, P]),
     "moe_backward": (ctypes.c_int, [CFG] + [P] * 17 + [ctypes.c_size_t, P]),
     "moe_quantize_mxfp8": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int64, P, P, P]),
+    "moe_quantize_mxfp4": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int64, P, P, P]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_version": (ctypes.c_char_p, []),
@@ -216,13 +225,13 @@ def moe_route(cfg: MoEConfig, logits, idx, w, stream=None, bias=None):
 def moe_permute(cfg: MoEConfig, x, idx, xp, counts, offsets, row_map, src_map, ws, x_scale=None, xp_scale=None,
                 err=None, stream=None):
     c = cfg.c()
-    mx = cfg.dtype == "mxfp8"
+    mx = cfg.is_mx
     wp, wb = _ws(ws)
     _check(load_library().moe_permute(
-        ctypes.byref(c), _ptr(x, "x", cfg.store_dtype, (cfg.T, cfg.H)),
+        ctypes.byref(c), _ptr(x, "x", cfg.store_dtype, (cfg.T, cfg.cols(cfg.H))),
         _ptr(x_scale, "x_scale", torch.uint8, (cfg.T, cfg.H // 32), optional=not mx),
         _ptr(idx, "idx", torch.int32, (cfg.T, cfg.k)),
-        _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.H), optional=True),
+        _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.cols(cfg.H)), optional=True),
         _ptr(xp_scale, "xp_scale", torch.uint8, (cfg.R_cap, cfg.H // 32), optional=not mx or xp is None),
         _ptr(counts, "counts", torch.int32, (cfg.E,)), _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)),
         _ptr(row_map, "row_map", torch.int32, (cfg.T, cfg.k)), _ptr(src_map, "src_map", torch.int32, (cfg.R_cap,)),
@@ -232,14 +241,14 @@ def moe_permute(cfg: MoEConfig, x, idx, xp, counts, offsets, row_map, src_map, w
 def moe_grouped_swiglu_gemm(cfg: MoEConfig, xp, w1, offsets, h, ws, xp_scale=None, w1_scale=None, h_scale=None,
                             gu_stash=None, stream=None):
     c = cfg.c()
-    mx = cfg.dtype == "mxfp8"
+    mx = cfg.is_mx
     wp, wb = _ws(ws)
     _check(load_library().moe_grouped_swiglu_gemm(
-        ctypes.byref(c), _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.H)),
+        ctypes.byref(c), _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.cols(cfg.H))),
         _ptr(xp_scale, "xp_scale", torch.uint8, (cfg.R_cap, cfg.H // 32), optional=not mx),
-        _ptr(w1, "w1", cfg.store_dtype, (cfg.E, 2 * cfg.F, cfg.H)),
+        _ptr(w1, "w1", cfg.store_dtype, (cfg.E, 2 * cfg.F, cfg.cols(cfg.H))),
         _ptr(w1_scale, "w1_scale", torch.uint8, (cfg.E, 2 * cfg.F, cfg.H // 32), optional=not mx),
-        _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
+        _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.cols(cfg.F))),
         _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx),
         _ptr(gu_stash, "gu_stash", cfg.out_dtype, (cfg.R_cap, 2 * cfg.F), optional=True), wp, wb,
         _stream(stream)))
@@ -249,15 +258,15 @@ def moe_grouped_swiglu_gemm_gather(cfg: MoEConfig, x, src_map, counts, w1, offse
                                    w1_scale=None, h_scale=None, stream=None):
     """The gate/up GEMM reading x[src_map[r] / k] for row r (no materialised Xp)."""
     c = cfg.c()
-    mx = cfg.dtype == "mxfp8"
+    mx = cfg.is_mx
     wp, wb = _ws(ws)
     _check(load_library().moe_grouped_swiglu_gemm_gather(
-        ctypes.byref(c), _ptr(x, "x", cfg.store_dtype, (cfg.T, cfg.H)),
+        ctypes.byref(c), _ptr(x, "x", cfg.store_dtype, (cfg.T, cfg.cols(cfg.H))),
         _ptr(x_scale, "x_scale", torch.uint8, (cfg.T, cfg.H // 32), optional=not mx),
         _ptr(src_map, "src_map", torch.int32, (cfg.R_cap,)), _ptr(counts, "counts", torch.int32, (cfg.E,)),
-        _ptr(w1, "w1", cfg.store_dtype, (cfg.E, 2 * cfg.F, cfg.H)),
+        _ptr(w1, "w1", cfg.store_dtype, (cfg.E, 2 * cfg.F, cfg.cols(cfg.H))),
         _ptr(w1_scale, "w1_scale", torch.uint8, (cfg.E, 2 * cfg.F, cfg.H // 32), optional=not mx),
-        _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
+        _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.cols(cfg.F))),
         _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx), wp, wb, _stream(stream)))
 
 
@@ -265,15 +274,15 @@ def moe_grouped_swiglu_gemm_weighted(cfg: MoEConfig, xp, w1, offsets, src_map, w
                                      w1_scale=None, h_scale=None, stream=None):
     """The gate/up GEMM with h scaled by each row's routing weight w[src_map[r]]."""
     c = cfg.c()
-    mx = cfg.dtype == "mxfp8"
+    mx = cfg.is_mx
     wp, wb = _ws(ws)
     _check(load_library().moe_grouped_swiglu_gemm_weighted(
-        ctypes.byref(c), _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.H)),
+        ctypes.byref(c), _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.cols(cfg.H))),
         _ptr(xp_scale, "xp_scale", torch.uint8, (cfg.R_cap, cfg.H // 32), optional=not mx),
-        _ptr(w1, "w1", cfg.store_dtype, (cfg.E, 2 * cfg.F, cfg.H)),
+        _ptr(w1, "w1", cfg.store_dtype, (cfg.E, 2 * cfg.F, cfg.cols(cfg.H))),
         _ptr(w1_scale, "w1_scale", torch.uint8, (cfg.E, 2 * cfg.F, cfg.H // 32), optional=not mx),
         _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(src_map, "src_map", torch.int32, (cfg.R_cap,)),
-        _ptr(w, "w", torch.float32, (cfg.T, cfg.k)), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
+        _ptr(w, "w", torch.float32, (cfg.T, cfg.k)), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.cols(cfg.F))),
         _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx), wp, wb, _stream(stream)))
 
 
@@ -281,12 +290,12 @@ def moe_grouped_down_gemm_weighted(cfg: MoEConfig, h, w2, offsets, src_map, w, y
                                    stream=None):
     """The down GEMM with Yp scaled by each row's routing weight w[src_map[r]]."""
     c = cfg.c()
-    mx = cfg.dtype == "mxfp8"
+    mx = cfg.is_mx
     wp, wb = _ws(ws)
     _check(load_library().moe_grouped_down_gemm_weighted(
-        ctypes.byref(c), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
+        ctypes.byref(c), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.cols(cfg.F))),
         _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx),
-        _ptr(w2, "w2", cfg.store_dtype, (cfg.E, cfg.H, cfg.F)),
+        _ptr(w2, "w2", cfg.store_dtype, (cfg.E, cfg.H, cfg.cols(cfg.F))),
         _ptr(w2_scale, "w2_scale", torch.uint8, (cfg.E, cfg.H, cfg.F // 32), optional=not mx),
         _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(src_map, "src_map", torch.int32, (cfg.R_cap,)),
         _ptr(w, "w", torch.float32, (cfg.T, cfg.k)), _ptr(yp, "yp", cfg.out_dtype, (cfg.R_cap, cfg.H)),
@@ -295,12 +304,12 @@ def moe_grouped_down_gemm_weighted(cfg: MoEConfig, h, w2, offsets, src_map, w, y
 
 def moe_grouped_down_gemm(cfg: MoEConfig, h, w2, offsets, yp, ws, h_scale=None, w2_scale=None, stream=None):
     c = cfg.c()
-    mx = cfg.dtype == "mxfp8"
+    mx = cfg.is_mx
     wp, wb = _ws(ws)
     _check(load_library().moe_grouped_down_gemm(
-        ctypes.byref(c), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
+        ctypes.byref(c), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.cols(cfg.F))),
         _ptr(h_scale, "h_scale", torch.uint8, (cfg.R_cap, cfg.F // 32), optional=not mx),
-        _ptr(w2, "w2", cfg.store_dtype, (cfg.E, cfg.H, cfg.F)),
+        _ptr(w2, "w2", cfg.store_dtype, (cfg.E, cfg.H, cfg.cols(cfg.F))),
         _ptr(w2_scale, "w2_scale", torch.uint8, (cfg.E, cfg.H, cfg.F // 32), optional=not mx),
         _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(yp, "yp", cfg.out_dtype, (cfg.R_cap, cfg.H)),
         wp, wb, _stream(stream)))
@@ -331,24 +340,26 @@ def moe_forward_noalloc(cfg: MoEConfig, logits, x, w1, w2, buf: dict, x_scale=No
 
 def _forward_call(cfg, logits, x, w1, w2, buf, x_scale, w1_scale, w2_scale, stream, bias, noalloc):
     c = cfg.c()
-    mx = cfg.dtype == "mxfp8"
+    mx = cfg.is_mx
     ws_args = () if noalloc else _ws(buf["ws"])
     fn = load_library().moe_forward_noalloc if noalloc else load_library().moe_forward
     R, T, H, F, E, k = cfg.R_cap, cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
     sd, od = cfg.store_dtype, cfg.out_dtype
     _check(fn(
         ctypes.byref(c), _ptr(logits, "logits", torch.float32, (T, E)),
-        _ptr(bias, "bias", torch.float32, (E,), optional=True), _ptr(x, "x", sd, (T, H)),
+        _ptr(bias, "bias", torch.float32, (E,), optional=True), _ptr(x, "x", sd, (T, cfg.cols(H))),
         _ptr(x_scale, "x_scale", torch.uint8, (T, H // 32), optional=not mx),
-        _ptr(w1, "w1", sd, (E, 2 * F, H)), _ptr(w1_scale, "w1_scale", torch.uint8, (E, 2 * F, H // 32), optional=not mx),
-        _ptr(w2, "w2", sd, (E, H, F)), _ptr(w2_scale, "w2_scale", torch.uint8, (E, H, F // 32), optional=not mx),
+        _ptr(w1, "w1", sd, (E, 2 * F, cfg.cols(H))),
+        _ptr(w1_scale, "w1_scale", torch.uint8, (E, 2 * F, H // 32), optional=not mx),
+        _ptr(w2, "w2", sd, (E, H, cfg.cols(F))), _ptr(w2_scale, "w2_scale", torch.uint8, (E, H, F // 32), optional=not mx),
         _ptr(buf["y"], "y", od, (T, H)), _ptr(buf["idx"], "idx", torch.int32, (T, k)),
         _ptr(buf["w"], "w", torch.float32, (T, k)), _ptr(buf["counts"], "counts", torch.int32, (E,)),
         _ptr(buf["offsets"], "offsets", torch.int32, (E + 1,)), _ptr(buf["row_map"], "row_map", torch.int32, (T, k)),
         _ptr(buf["src_map"], "src_map", torch.int32, (R,)),
-        _ptr(buf.get("xp"), "xp", sd, (R, H), optional=True),
+        _ptr(buf.get("xp"), "xp", sd, (R, cfg.cols(H)), optional=True),
         _ptr(buf.get("xp_scale"), "xp_scale", torch.uint8, (R, H // 32), optional=not mx or buf.get("xp") is None),
-        _ptr(buf["h"], "h", sd, (R, F)), _ptr(buf.get("h_scale"), "h_scale", torch.uint8, (R, F // 32), optional=not mx),
+        _ptr(buf["h"], "h", sd, (R, cfg.cols(F))),
+        _ptr(buf.get("h_scale"), "h_scale", torch.uint8, (R, F // 32), optional=not mx),
         _ptr(buf["yp"], "yp", od, (R, H)),
         _ptr(buf.get("gu_stash"), "gu_stash", od, (R, 2 * F), optional=True),
         _ptr(buf.get("err"), "err", torch.int32, (1,), optional=True), *ws_args, _stream(stream)))
@@ -380,7 +391,7 @@ def moe_grouped_down_bwd(cfg: MoEConfig, dyp, w2, h, gu_stash, offsets, dgu, dw2
     wp, wb = _ws(ws)
     _check(load_library().moe_grouped_down_bwd(
         ctypes.byref(c), _ptr(dyp, "dyp", cfg.out_dtype, (cfg.R_cap, cfg.H)),
-        _ptr(w2, "w2", cfg.store_dtype, (cfg.E, cfg.H, cfg.F)), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.F)),
+        _ptr(w2, "w2", cfg.store_dtype, (cfg.E, cfg.H, cfg.cols(cfg.F))), _ptr(h, "h", cfg.store_dtype, (cfg.R_cap, cfg.cols(cfg.F))),
         _ptr(gu_stash, "gu_stash", cfg.out_dtype, (cfg.R_cap, 2 * cfg.F)),
         _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(dgu, "dgu", cfg.out_dtype, (cfg.R_cap, 2 * cfg.F)),
         _ptr(dw2, "dw2", torch.float32, (cfg.E, cfg.H, cfg.F)), wp, wb, _stream(stream)))
@@ -391,7 +402,7 @@ def moe_grouped_swiglu_bwd(cfg: MoEConfig, dgu, w1, xp, offsets, dxp, dw1, ws, s
     wp, wb = _ws(ws)
     _check(load_library().moe_grouped_swiglu_bwd(
         ctypes.byref(c), _ptr(dgu, "dgu", cfg.out_dtype, (cfg.R_cap, 2 * cfg.F)),
-        _ptr(w1, "w1", cfg.store_dtype, (cfg.E, 2 * cfg.F, cfg.H)), _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.H)),
+        _ptr(w1, "w1", cfg.store_dtype, (cfg.E, 2 * cfg.F, cfg.cols(cfg.H))), _ptr(xp, "xp", cfg.store_dtype, (cfg.R_cap, cfg.cols(cfg.H))),
         _ptr(offsets, "offsets", torch.int32, (cfg.E + 1,)), _ptr(dxp, "dxp", cfg.out_dtype, (cfg.R_cap, cfg.H)),
         _ptr(dw1, "dw1", torch.float32, (cfg.E, 2 * cfg.F, cfg.H)), wp, wb, _stream(stream)))
 
@@ -430,6 +441,15 @@ def moe_quantize_mxfp8(x, codes, scales, stream=None):
         _ptr(scales, "scales", torch.uint8, tuple(x.shape[:-1]) + (cols // 32,)), _stream(stream)))
 
 
+def moe_quantize_mxfp4(x, codes, scales, stream=None):
+    """x float32 [..., n] -> codes uint8 [..., n/2] (two E2M1 per byte), scales uint8 [..., n/32]."""
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    _check(load_library().moe_quantize_mxfp4(
+        _ptr(x, "x", torch.float32), rows, cols, _ptr(codes, "codes", torch.uint8, tuple(x.shape[:-1]) + (cols // 2,)),
+        _ptr(scales, "scales", torch.uint8, tuple(x.shape[:-1]) + (cols // 32,)), _stream(stream)))
+
+
 # ------------------------------------------------------------ buffer helpers
 def alloc_forward(cfg: MoEConfig, device="cuda", training: bool = False) -> dict:
     """Caller-side buffers of moe_forward (plain torch allocations)."""
@@ -443,13 +463,13 @@ def alloc_forward(cfg: MoEConfig, device="cuda", training: bool = False) -> dict
         "offsets": torch.empty(E + 1, dtype=torch.int32, device=device),
         "row_map": torch.empty(T, k, dtype=torch.int32, device=device),
         "src_map": torch.empty(R, dtype=torch.int32, device=device),
-        "xp": torch.empty(R, H, dtype=sd, device=device),
-        "h": torch.empty(R, F, dtype=sd, device=device),
+        "xp": torch.empty(R, cfg.cols(H), dtype=sd, device=device),
+        "h": torch.empty(R, cfg.cols(F), dtype=sd, device=device),
         "yp": torch.empty(R, H, dtype=od, device=device),
         "err": torch.zeros(1, dtype=torch.int32, device=device),
         "ws": torch.empty(max(workspace_size(cfg), 1), dtype=torch.uint8, device=device),
     }
-    if cfg.dtype == "mxfp8":
+    if cfg.is_mx:
         b["xp_scale"] = torch.empty(R, H // 32, dtype=torch.uint8, device=device)
         b["h_scale"] = torch.empty(R, F // 32, dtype=torch.uint8, device=device)
     if training:

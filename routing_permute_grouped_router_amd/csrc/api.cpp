@@ -41,6 +41,7 @@ moe_status hip_status(hipError_t e, const char* what) {
     } while (0)
 
 int64_t rows_capacity(const moe_config& c) { return (int64_t)c.T * c.k + (int64_t)c.E * (c.align - 1); }
+bool is_mx(const moe_config& c) { return c.dtype == MOE_MXFP8 || c.dtype == MOE_MXFP4; }
 
 // Sizes and enums; does not look at pointers.
 moe_status check_config(const moe_config* cfg) {
@@ -55,8 +56,8 @@ moe_status check_config(const moe_config* cfg) {
     if (c.score != MOE_SOFTMAX && c.score != MOE_SIGMOID)
         return fail(MOE_ERR_INVALID_ARG, "score must be MOE_SOFTMAX or MOE_SIGMOID (got %d)", c.score);
     if (c.renorm != 0 && c.renorm != 1) return fail(MOE_ERR_INVALID_ARG, "renorm must be 0 or 1 (got %d)", c.renorm);
-    if (c.dtype != MOE_F32 && c.dtype != MOE_BF16 && c.dtype != MOE_MXFP8)
-        return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32, MOE_BF16 or MOE_MXFP8 (got %d)", c.dtype);
+    if (c.dtype != MOE_F32 && c.dtype != MOE_BF16 && c.dtype != MOE_MXFP8 && c.dtype != MOE_MXFP4)
+        return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32, MOE_BF16, MOE_MXFP8 or MOE_MXFP4 (got %d)", c.dtype);
     if (c.weight_site != MOE_WEIGHT_AT_COMBINE && c.weight_site != MOE_WEIGHT_AT_FC1 &&
         c.weight_site != MOE_WEIGHT_AT_FC2)
         return fail(MOE_ERR_INVALID_ARG, "weight_site must be MOE_WEIGHT_AT_COMBINE, _FC1 or _FC2 (got %d)",
@@ -78,6 +79,10 @@ moe_status check_shapes(const moe_config& c) {
         return fail(MOE_ERR_UNSUPPORTED, "F*H must be below 2^29 (got F=%d, H=%d)", c.F, c.H);
     if (c.dtype == MOE_MXFP8 && c.F % 128 != 0)
         return fail(MOE_ERR_UNSUPPORTED, "MXFP8 needs F to be a multiple of 128 (got %d)", c.F);
+    // MXFP4: a 128-byte GEMM stage holds 256 values, and one 16-byte load
+    // brings a row's scales of two stages
+    if (c.dtype == MOE_MXFP4 && (c.H % 512 != 0 || c.F % 512 != 0))
+        return fail(MOE_ERR_UNSUPPORTED, "MXFP4 needs H and F to be multiples of 512 (got H=%d, F=%d)", c.H, c.F);
     return MOE_OK;
 }
 
@@ -119,15 +124,16 @@ moe_status swiglu_checked(const moe_config* cfg, const void* a, const uint8_t* a
     if ((st = check_shapes(c))) return st;
     if (rows_capacity(c) == 0) return MOE_OK;
     // the gather form addresses a row of x with a 32-bit byte offset
-    if (gsrc && (int64_t)c.T * c.H * (c.dtype == MOE_F32 ? 4 : c.dtype == MOE_BF16 ? 2 : 1) >= ((int64_t)1 << 32))
+    if (gsrc && (int64_t)c.T * c.H * (c.dtype == MOE_F32 ? 8 : c.dtype == MOE_BF16 ? 4 : c.dtype == MOE_MXFP8 ? 2 : 1) >=
+                    ((int64_t)1 << 33))
         return fail(MOE_ERR_UNSUPPORTED, "%s: the gather form needs T*H*element size < 4 GiB", what);
     if (!a) return fail(MOE_ERR_INVALID_ARG, "%s: the grouped operand (xp or x) is NULL", what);
     REQUIRE(w1);
     REQUIRE(offsets);
     REQUIRE(h);
     if ((st = check_ws(c, ws, ws_bytes))) return st;
-    if (c.dtype == MOE_MXFP8) {
-        if (!a_scale) return fail(MOE_ERR_INVALID_ARG, "%s: the grouped operand's MXFP8 scales are NULL", what);
+    if (is_mx(c)) {
+        if (!a_scale) return fail(MOE_ERR_INVALID_ARG, "%s: the grouped operand's MX scales are NULL", what);
         REQUIRE(w1_scale);
         REQUIRE(h_scale);
     }
@@ -142,10 +148,7 @@ moe_status swiglu_checked(const moe_config* cfg, const void* a, const uint8_t* a
         return hip_status(launch_swiglu_gemm_f32(c, (const float*)a, (const float*)w1, offsets, (float*)h,
                                                  (float*)stash, gsrc, gcounts, row_w, s),
                           what);
-    default:
-        if (!a_scale) return fail(MOE_ERR_INVALID_ARG, "%s: the grouped operand's MXFP8 scales are NULL", what);
-        REQUIRE(w1_scale);
-        REQUIRE(h_scale);
+    default:  // MXFP8 and MXFP4
         return hip_status(launch_swiglu_gemm_mxfp8(c, (const uint8_t*)a, a_scale, (const uint8_t*)w1, w1_scale,
                                                    offsets, (uint8_t*)h, h_scale, (uint16_t*)stash, gsrc, gcounts,
                                                    row_w, gemm_ws(c, ws), s),
@@ -167,7 +170,7 @@ moe_status down_checked(const moe_config* cfg, const void* h, const uint8_t* h_s
     REQUIRE(offsets);
     REQUIRE(yp);
     if ((st = check_ws(c, ws, ws_bytes))) return st;
-    if (c.dtype == MOE_MXFP8) {
+    if (is_mx(c)) {
         REQUIRE(h_scale);
         REQUIRE(w2_scale);
     }
@@ -181,9 +184,7 @@ moe_status down_checked(const moe_config* cfg, const void* h, const uint8_t* h_s
     case MOE_F32:
         return hip_status(launch_down_gemm_f32(c, (const float*)h, (const float*)w2, offsets, (float*)yp, row_w, s),
                           what);
-    default:
-        REQUIRE(h_scale);
-        REQUIRE(w2_scale);
+    default:  // MXFP8 and MXFP4
         return hip_status(launch_down_gemm_mxfp8(c, (const uint8_t*)h, h_scale, (const uint8_t*)w2, w2_scale, offsets,
                                                  (uint16_t*)yp, row_w, gemm_ws(c, ws), s),
                           what);
@@ -228,7 +229,7 @@ moe_status permute_checked(const moe_config* cfg, const void* x, const uint8_t* 
     moe_status st = check_config(cfg);
     if (st) return st;
     const moe_config& c = *cfg;
-    if (c.dtype == MOE_MXFP8 && c.H % kMxBlock) return fail(MOE_ERR_UNSUPPORTED, "MXFP8 needs H % 32 == 0");
+    if (is_mx(c) && c.H % 128) return fail(MOE_ERR_UNSUPPORTED, "the MX formats need H %% 128 == 0");
     REQUIRE(counts);
     REQUIRE(offsets);
     if (rows_capacity(c) > 0) REQUIRE(src_map);
@@ -237,7 +238,7 @@ moe_status permute_checked(const moe_config* cfg, const void* x, const uint8_t* 
         REQUIRE(row_map);
         if (xp) {  // xp NULL: the grouping only (for the gather form of the gate/up GEMM)
             REQUIRE(x);
-            if (c.dtype == MOE_MXFP8) {
+            if (is_mx(c)) {
                 REQUIRE(x_scale);
                 REQUIRE(xp_scale);
             }
@@ -461,7 +462,7 @@ moe_status moe_forward(const moe_config* cfg, const float* logits, const float* 
     if ((st = check_shapes(c))) return st;
     REQUIRE(w1);
     REQUIRE(w2);
-    if (c.dtype == MOE_MXFP8) {
+    if (is_mx(c)) {
         REQUIRE(w1_scale);
         REQUIRE(w2_scale);
     }
@@ -560,6 +561,18 @@ moe_status moe_quantize_mxfp8(const float* in, int64_t rows, int64_t cols, uint8
         REQUIRE(scales);
     }
     return hip_status(launch_quantize_mxfp8(in, rows, cols, codes, scales, as_stream(stream)), "moe_quantize_mxfp8");
+}
+
+moe_status moe_quantize_mxfp4(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                              void* stream) {
+    if (rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "rows and cols must be >= 0");
+    if (cols % kMxBlock) return fail(MOE_ERR_INVALID_ARG, "cols must be a multiple of 32 (got %lld)", (long long)cols);
+    if (rows * cols > 0) {
+        REQUIRE(in);
+        REQUIRE(codes);
+        REQUIRE(scales);
+    }
+    return hip_status(launch_quantize_mxfp4(in, rows, cols, codes, scales, as_stream(stream)), "moe_quantize_mxfp4");
 }
 
 const char* moe_last_error(void) { return g_err; }

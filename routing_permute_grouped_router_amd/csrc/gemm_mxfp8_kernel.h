@@ -1,5 +1,5 @@
-// Grouped MXFP8 GEMMs on CDNA4 scaled matrix cores
-// (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 operands, E8M0 scales per 32).
+// Grouped MXFP8 and MXFP4 GEMMs on CDNA4 scaled matrix cores
+// (v_mfma_scale_f32_32x32x64_f8f6f4; E4M3 or E2M1 operands, E8M0 scales per 32).
 //
 // Same computation and device-side group handling as the bf16 kernel
 // (gemm_bf16_kernel.h), on the MXFP8 block-scaled format of the cudnn-frontend
@@ -12,6 +12,17 @@
 // scale in byte 0 of lane l's scale operand applies to 32-block h of that row
 // or column.  A lane therefore reads 16-byte chunks 4 s + h and 4 s + 2 + h of
 // its LDS row and passes byte (2 s + h) of the row's scale word for K step s.
+//
+// MXFP4 (F4): the same instruction with E2M1 operands reads 4 registers per
+// lane, all 32 values of one scale block: lane l holds row (column) l % 32
+// and 32-block h = l / 32 of a 64-value K step, and its scale operand gives
+// that block's scale (measured on gfx950).  A 16-byte chunk of a packed row
+// is exactly one block, so the chunks 4 s + h and 4 s + 2 + h that the E4M3
+// form reads as one 64-byte K step are two E2M1 K steps here: one MFMA on
+// the low four registers (block 4 s + h, scale byte 0 after the shift) and
+// one on the high four (block 4 s + 2 + h, scale byte 2).  A 128-byte stage
+// holds 256 values (8 blocks, two scale words per row), so every LDS read
+// feeds twice the MFMA work of the E4M3 form.
 #pragma once
 
 #include "gemm_bf16_kernel.h"
@@ -21,15 +32,23 @@ namespace moe {
 namespace gemm {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The scaled MFMA with 4-register (E2M1) operands: the LLVM intrinsic's
+// 128-bit overload, which the clang builtin (8-register operands only) does
+// not expose.  cbsz / blgp 4 select E2M1 for A / B; opsel picks the scale byte.
+__device__ f32x16 mfma_scale_e2m1(i32x4 a, i32x4 b, f32x16 c, int cbsz, int blgp, int opsel_a, int scale_a,
+                                  int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v4i32.v4i32");
 
 struct MxArgs {
-    const uint8_t* A;        // [rows][K] E4M3 codes
+    const uint8_t* A;        // [rows][K] E4M3 codes (MXFP4: [rows][K/2], two E2M1 per byte)
     const uint8_t* As;       // [rows][K/32] E8M0 scales
     const uint8_t* B;        // [E][b_rows][K]
     const uint8_t* Bs;       // [E][b_rows][K/32]
     const int32_t* offsets;  // [E+1]
-    int E, K, rows, n_out, b_rows;
-    uint8_t* C;              // SwiGLU: h codes [rows][n_out]
+    int E, K, rows, n_out, b_rows;  // K: elements
+    uint8_t* C;              // SwiGLU: h codes [rows][n_out] (MXFP4: [rows][n_out/2])
     uint8_t* Cs;             // SwiGLU: h scales [rows][n_out/32]
     uint16_t* Cb;            // down: Yp bf16 [rows][n_out]
     uint16_t* stash;         // SwiGLU, optional: bf16 g | u [rows][2 n_out]
@@ -96,24 +115,33 @@ __device__ __forceinline__ uint32_t mx_word(uint32_t addr) {
     __asm__ volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
     return v;
 }
+template <int OFF>
+__device__ __forceinline__ uint2 mx_word2(uint32_t addr) {
+    uint2 v;
+    __asm__ volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+    return v;
+}
 
 // EP, epilogue variant bits (built separately, so the plain kernel carries
 // none of it): 1 = the outputs are scaled by p.row_w, 2 = the SwiGLU inputs
-// are clamped to p.lim.
-template <bool SWIGLU, int G, int EP>
+// are clamped to p.lim.  F4: E2M1 operands (and h) instead of E4M3.
+template <bool SWIGLU, int G, int EP, bool F4>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
-    constexpr int BKB = 128;                 // K bytes (E4M3 values) per stage: four scale blocks
+    constexpr int BKB = 128;                 // K bytes per stage: 128 E4M3 values (4 blocks) or 256 E2M1 (8)
     constexpr int CH = BKB / 16;             // 16-byte chunks per LDS row
     constexpr int RPL = 64 / CH;             // rows per wave-wide code load
     constexpr int LOADS = 64 / RPL;          // code loads per wave per operand per stage
     constexpr int OPB = kTile * BKB;         // codes of one operand in one stage (32 KiB)
     constexpr uint32_t STB = 2 * OPB;        // one stage: A codes | B codes
-    // Scale words: G stages per load (G = 4: 16 bytes per row, one cache line
-    // per row every four stages instead of every stage), in two slots of
-    // [A rows | B rows] x 4 G bytes after the two stages; stage kt's word of
-    // row r is at slot (kt / G) % 2, byte 4 (kt % G) of the row's entry.
-    static_assert(G == 1 || G == 4, "scale group");
-    constexpr int SW_ROW = 4 * G, SC_OP = kTile * SW_ROW, SC_SLOT = 2 * SC_OP;
+    // Scale words: G stages per load (16 bytes per row, one cache line per row
+    // every G stages instead of every stage: G = 4 for E4M3, whose stage has
+    // one word per row, and G = 2 for E2M1, two words; G = 1: one 4-byte
+    // E4M3 word per stage), in two slots of [A rows | B rows] x SWB G bytes
+    // after the two stages; stage kt's words of row r are at slot (kt / G) % 2,
+    // byte SWB (kt % G) of the row's entry.
+    constexpr int SWB = F4 ? 8 : 4;  // scale bytes per row and stage
+    static_assert(F4 ? G == 2 : (G == 1 || G == 4), "scale group");
+    constexpr int SW_ROW = SWB * G, SC_OP = kTile * SW_ROW, SC_SLOT = 2 * SC_OP;
     constexpr uint32_t SC_BASE = 2 * STB;
     // byte offsets of B fragments 1..3 from fragment 0 (SwiGLU: fragments 2, 3
     // are the up rows of fragments 0, 1)
@@ -134,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     const int cols_per_tile = SWIGLU ? kTile / 2 : kTile;
     const int n_tiles = (p.n_out + cols_per_tile - 1) / cols_per_tile;
     const int total = total_m * n_tiles;
-    const int K = p.K, KS = K / 32, nk = K / BKB;
+    const int K = p.K, KS = K / 32, KB = F4 ? K / 2 : K, nk = KB / BKB;  // KB: bytes per row
     const int xcd = blockIdx.x % kXcds, nb = gridDim.x / kXcds;
     if (tid < kXcds) queues[tid] = xcd_queue(total, tid, nb, 0);  // whole tiles only
     uint32_t dry = 0;
@@ -198,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
 // scale words of load group grp (G stages) into slot `slot`
 #define MX_LOAD_SC(OP, SOFF, SBASE, grp, slot)                                                           \
     {                                                                                                    \
-        if constexpr (G == 4)                                                                            \
+        if constexpr (G * SWB == 16)                                                                     \
             dma_lds16(lds_wsc + (uint32_t)(slot) * SC_SLOT + (OP) * SC_OP, SOFF, SBASE + (size_t)(grp) * 16); \
         else                                                                                             \
             dma_lds4(lds_wsc + (uint32_t)(slot) * SC_SLOT + (OP) * SC_OP, SOFF, SBASE + (size_t)(grp) * 4); \
@@ -206,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
 #define MX_LOAD_AS(grp, slot) MX_LOAD_SC(0, asoff, ascale, grp, slot)
 #define MX_LOAD_BS(grp, slot) MX_LOAD_SC(1, bsoff, bscale, grp, slot)
 // LDS byte offset of stage kt's scale words within the scale slots
-#define MX_SC_OFF(kt) ((uint32_t)(((kt) / G) & 1) * SC_SLOT + (uint32_t)((kt) % G) * 4)
+#define MX_SC_OFF(kt) ((uint32_t)(((kt) / G) & 1) * SC_SLOT + (uint32_t)((kt) % G) * SWB)
 #define MX_SB __builtin_amdgcn_sched_barrier(0)
 // fragment reads of K step S of the stage at byte offset SO
 #define MX_RD_A(F, SO, S, mi)                                                                            \
@@ -214,31 +242,62 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
 #define MX_RD_B(G, SO, S, ni)                                                                            \
     G[ni] = mx_frag<(ni) == 0 ? 0 : (ni) == 1 ? B1 : (ni) == 2 ? B2 : B3>(b_rd + (SO) + kc[S][0][(ni) & 1], \
                                                                           b_rd + (SO) + kc[S][1][(ni) & 1])
-// the scale words of a stage (SO = MX_SC_OFF of the stage): A rows of fragments 0..3, then B
+// the scale words of a stage (SO = MX_SC_OFF of the stage): A rows of
+// fragments 0..3, then B; E2M1: the two words of fragment row i in sw2[i]
 #define MX_RD_S(SW, SO)                                                                                  \
     {                                                                                                    \
-        SW[0] = mx_word<0>(as_rd + (SO));                                                                \
-        SW[1] = mx_word<32 * SW_ROW>(as_rd + (SO));                                                      \
-        SW[2] = mx_word<64 * SW_ROW>(as_rd + (SO));                                                      \
-        SW[3] = mx_word<96 * SW_ROW>(as_rd + (SO));                                                      \
-        SW[4] = mx_word<0>(bs_rd + (SO));                                                                \
-        SW[5] = mx_word<W1>(bs_rd + (SO));                                                               \
-        SW[6] = mx_word<W2>(bs_rd + (SO));                                                               \
-        SW[7] = mx_word<W3>(bs_rd + (SO));                                                               \
+        if constexpr (F4) {                                                                              \
+            sw2[0] = mx_word2<0>(as_rd + (SO));                                                          \
+            sw2[1] = mx_word2<32 * SW_ROW>(as_rd + (SO));                                                \
+            sw2[2] = mx_word2<64 * SW_ROW>(as_rd + (SO));                                                \
+            sw2[3] = mx_word2<96 * SW_ROW>(as_rd + (SO));                                                \
+            sw2[4] = mx_word2<0>(bs_rd + (SO));                                                          \
+            sw2[5] = mx_word2<W1>(bs_rd + (SO));                                                         \
+            sw2[6] = mx_word2<W2>(bs_rd + (SO));                                                         \
+            sw2[7] = mx_word2<W3>(bs_rd + (SO));                                                         \
+        } else {                                                                                         \
+            SW[0] = mx_word<0>(as_rd + (SO));                                                            \
+            SW[1] = mx_word<32 * SW_ROW>(as_rd + (SO));                                                  \
+            SW[2] = mx_word<64 * SW_ROW>(as_rd + (SO));                                                  \
+            SW[3] = mx_word<96 * SW_ROW>(as_rd + (SO));                                                  \
+            SW[4] = mx_word<0>(bs_rd + (SO));                                                            \
+            SW[5] = mx_word<W1>(bs_rd + (SO));                                                           \
+            SW[6] = mx_word<W2>(bs_rd + (SO));                                                           \
+            SW[7] = mx_word<W3>(bs_rd + (SO));                                                           \
+        }                                                                                                \
     }
+
 #define MX_WAIT_F(F, G)                                                                                  \
     __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
                      : "+v"(F[0]), "+v"(F[1]), "+v"(F[2]), "+v"(F[3]), "+v"(G[0]), "+v"(G[1]), "+v"(G[2]), \
                        "+v"(G[3])::"memory")
 #define MX_WAIT_W(SW)                                                                                    \
-    __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                              \
-                     : "+v"(SW[0]), "+v"(SW[1]), "+v"(SW[2]), "+v"(SW[3]), "+v"(SW[4]), "+v"(SW[5]),     \
-                       "+v"(SW[6]), "+v"(SW[7])::"memory")
+    {                                                                                                    \
+        if constexpr (F4)                                                                                \
+            __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                      \
+                             : "+v"(sw2[0]), "+v"(sw2[1]), "+v"(sw2[2]), "+v"(sw2[3]), "+v"(sw2[4]),    \
+                               "+v"(sw2[5]), "+v"(sw2[6]), "+v"(sw2[7])::"memory");                      \
+        else                                                                                             \
+            __asm__ volatile("s_waitcnt lgkmcnt(0)"                                                      \
+                             : "+v"(SW[0]), "+v"(SW[1]), "+v"(SW[2]), "+v"(SW[3]), "+v"(SW[4]), "+v"(SW[5]), \
+                               "+v"(SW[6]), "+v"(SW[7])::"memory");                                      \
+    }
 // One MFMA of K step S: the scale words were shifted right by 8 h (h = lane
 // / 32), so byte 2 S holds the scale of 32-block 2 S + h for every lane.
+// E2M1: two MFMAs on the fragments' low and high four registers (blocks
+// 4 S + h and 4 S + 2 + h: bytes 0 and 2 of the stage's word S).
 #define MX_MFMA(F, G, SS, S, mi, ni)                                                                     \
-    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F[mi], G[ni], acc[mi][ni], 0, 0, 2 * (S), \
-                                                                  (int)SS[mi], 2 * (S), (int)SS[4 + (ni)])
+    if constexpr (F4) {                                                                                  \
+        acc[mi][ni] = mfma_scale_e2m1(__builtin_shufflevector(F[mi], F[mi], 0, 1, 2, 3),                 \
+                                      __builtin_shufflevector(G[ni], G[ni], 0, 1, 2, 3), acc[mi][ni], 4, 4, 0, \
+                                      (int)SS[2 * (mi) + (S)], 0, (int)SS[2 * (4 + (ni)) + (S)]);        \
+        acc[mi][ni] = mfma_scale_e2m1(__builtin_shufflevector(F[mi], F[mi], 4, 5, 6, 7),                 \
+                                      __builtin_shufflevector(G[ni], G[ni], 4, 5, 6, 7), acc[mi][ni], 4, 4, 2, \
+                                      (int)SS[2 * (mi) + (S)], 2, (int)SS[2 * (4 + (ni)) + (S)]);        \
+    } else {                                                                                             \
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F[mi], G[ni], acc[mi][ni], 0, 0, 2 * (S), \
+                                                                      (int)SS[mi], 2 * (S), (int)SS[4 + (ni)]); \
+    }
 #define MX_STEP(F, G, SS, S, mi, ni, PRE, RD)                                                            \
     PRE;                                                                                                 \
     MX_MFMA(F, G, SS, S, mi, ni);                                                                        \
@@ -290,16 +349,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         for (int i = 0; i < LOADS; ++i) {
             const int r = wid * 64 + i * RPL + lrow;  // tile row 0..255
             const int chunk = lslot ^ swz<1>(r);
-            aoff[i] = (uint32_t)((size_t)a_row(r) * K + chunk * 16);
-            boff[i] = (uint32_t)((size_t)(b_row(r) - brow0) * K + chunk * 16);
+            aoff[i] = (uint32_t)((size_t)a_row(r) * KB + chunk * 16);
+            boff[i] = (uint32_t)((size_t)(b_row(r) - brow0) * KB + chunk * 16);
         }
         {
             const int r = wid * 64 + lane;  // tile row of this lane's scale words
             asoff = (uint32_t)(a_row(r) * KS);
             bsoff = (uint32_t)((b_row(r) - brow0) * KS);
         }
-        acodes = p.src_map ? p.A : p.A + (size_t)row0 * K;
-        bcodes = p.B + ((size_t)e * p.b_rows + brow0) * K;
+        acodes = p.src_map ? p.A : p.A + (size_t)row0 * KB;
+        bcodes = p.B + ((size_t)e * p.b_rows + brow0) * KB;
         ascale = p.src_map ? p.As : p.As + (size_t)row0 * KS;
         bscale = p.Bs + ((size_t)e * p.b_rows + brow0) * KS;
         MX_SB;
@@ -332,7 +391,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     load_b_half();
     while (unit >= 0) {
         i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
-        uint32_t sw[8], ss[8];
+        constexpr int NSW = F4 ? 16 : 8;  // scale words of a stage a lane uses (shifted: ss)
+        uint32_t sw[8], ss[NSW];
+        uint2 sw2[8];  // E2M1: both words of each fragment row
         // the unit's first two stages landed everywhere; the previous unit's stores retired
         __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         MX_SB;
@@ -372,7 +433,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         const int sslot = G == 1 ? st_ : ((kt_ / G) + 1) & 1;                                            \
         const uint32_t nsc = MX_SC_OFF(kt_ + 1);                                                         \
         MX_SB;                                                                                           \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) ss[i] = sw[i] >> (8 * half);                       \
+        if constexpr (F4) {                                                                              \
+            _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                              \
+                ss[2 * i] = sw2[i].x >> (8 * half);                                                      \
+                ss[2 * i + 1] = sw2[i].y >> (8 * half);                                                  \
+            }                                                                                            \
+        } else {                                                                                         \
+            _Pragma("unroll") for (int i = 0; i < 8; ++i) ss[i] = sw[i] >> (8 * half);                   \
+        }                                                                                                \
         MX_SB;                                                                                           \
         /* K step 0 on fa0/fb0; the fragments of K step 1 are read under the first 8 MFMAs */           \
         MX_STEP(fa0, fb0, ss, 0, 0, 0, (void)0, MX_RD_A(fa1, so, 1, 0))                                  \
@@ -421,6 +489,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     }
         if constexpr (G == 1) {
             for (int kt = kb; kt < ke; ++kt) MX_STAGE(kt, (kt - kb) & 1, 1)
+        } else if constexpr (G == 2) {
+            // stages in twos (K is a multiple of 2 stages, kb = 0)
+            for (int kt = kb; kt < ke; kt += 2) {
+                MX_STAGE(kt, 0, 1)
+                MX_STAGE(kt + 1, 1, 0)
+            }
         } else {
             // stages in fours (K is a multiple of 4 stages, kb = 0): the scale
             // group loads sit in the first stage of each four, with no branch
@@ -510,15 +584,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         const int r = wm * 128 + (MI) * 32 + rr;                                                         \
         const int f = e_nt * 128 + wn * 64 + (NI) * 32 + cc;                                             \
         if (r < rlim && f < p.n_out) {                                                                   \
-            const int se = mx_shared_exp(amax);                                                          \
-            uint32_t w4[4];                                                                              \
-            _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                \
-                w4[j] = (uint32_t)e4m3_rne(ldexpf(v[4 * j], -se)) |                                      \
-                        ((uint32_t)e4m3_rne(ldexpf(v[4 * j + 1], -se)) << 8) |                           \
-                        ((uint32_t)e4m3_rne(ldexpf(v[4 * j + 2], -se)) << 16) |                          \
-                        ((uint32_t)e4m3_rne(ldexpf(v[4 * j + 3], -se)) << 24);                           \
             const size_t row = (size_t)(rbase + r);                                                      \
-            *(uint4*)(p.C + row * p.n_out + f) = make_uint4(w4[0], w4[1], w4[2], w4[3]);                 \
+            int se;                                                                                      \
+            if constexpr (F4) {                                                                          \
+                se = mx4_shared_exp(amax);                                                               \
+                uint32_t w2[2] = {0u, 0u};                                                               \
+                _Pragma("unroll") for (int j = 0; j < 16; ++j)                                           \
+                    w2[j >> 3] |= (uint32_t)e2m1_rne(ldexpf(v[j], -se)) << (4 * (j & 7));                \
+                *(uint2*)(p.C + row * (p.n_out / 2) + f / 2) = make_uint2(w2[0], w2[1]);                 \
+            } else {                                                                                     \
+                se = mx_shared_exp(amax);                                                                \
+                uint32_t w4[4];                                                                          \
+                _Pragma("unroll") for (int j = 0; j < 4; ++j)                                            \
+                    w4[j] = (uint32_t)e4m3_rne(ldexpf(v[4 * j], -se)) |                                  \
+                            ((uint32_t)e4m3_rne(ldexpf(v[4 * j + 1], -se)) << 8) |                       \
+                            ((uint32_t)e4m3_rne(ldexpf(v[4 * j + 2], -se)) << 16) |                      \
+                            ((uint32_t)e4m3_rne(ldexpf(v[4 * j + 3], -se)) << 24);                       \
+                *(uint4*)(p.C + row * p.n_out + f) = make_uint4(w4[0], w4[1], w4[2], w4[3]);             \
+            }                                                                                            \
             if ((ln & 1) == 0) p.Cs[row * (p.n_out / 32) + f / 32] = (uint8_t)(se + 127);                \
         }                                                                                                \
         if (p.stash) {                                                                                   \

@@ -71,7 +71,7 @@ struct GroupArgs {
     const void* x;                // [T, vpr] vectors, or null (grouping only)
     void* xp;                     // [R_cap, vpr]
     int vpr;
-    const uint32_t* xs;           // MXFP8 scale rows as 4-byte words [T, svpr], or null
+    const uint32_t* xs;           // MX scale rows as 4-byte words [T, svpr], or null
     uint32_t* xps;
     int svpr;
 };
@@ -288,7 +288,7 @@ hipError_t launch_group(const moe_config& c, const int32_t* idx, const void* x, 
     // enough routes per block to keep their rows in LDS.
     int parts = 1;
     const int64_t esz = c.dtype == MOE_F32 ? 4 : (c.dtype == MOE_BF16 ? 2 : 1);
-    const int64_t row_bytes = (int64_t)c.H * esz;
+    const int64_t row_bytes = c.dtype == MOE_MXFP4 ? (int64_t)c.H / 2 : (int64_t)c.H * esz;  // MXFP4: 2 per byte
     const int64_t vec_bytes = row_bytes % 16 == 0 ? 16 : (row_bytes % 4 == 0 ? 4 : 1);
     if (xp) {
         while (parts < kSub && nch * parts < 1024) parts *= 2;
@@ -302,7 +302,7 @@ hipError_t launch_group(const moe_config& c, const int32_t* idx, const void* x, 
     }
     a.x = x;
     a.xp = xp;
-    if (c.dtype == MOE_MXFP8) {  // H % 128 == 0: scale rows are whole 4-byte words
+    if (c.dtype == MOE_MXFP8 || c.dtype == MOE_MXFP4) {  // H % 128 == 0: scale rows are whole 4-byte words
         a.xs = (const uint32_t*)x_scale;
         a.xps = (uint32_t*)xp_scale;
         a.svpr = c.H / kMxBlock / 4;

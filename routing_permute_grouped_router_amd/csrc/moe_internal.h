@@ -92,6 +92,8 @@ hipError_t launch_down_gemm_f32(const moe_config& c, const float* h, const float
                                 float* yp, const float* row_w, hipStream_t s);
 
 // MXFP8
+hipError_t launch_quantize_mxfp4(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s);
 hipError_t launch_quantize_mxfp8(const float* in, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                                  hipStream_t s);
 // Workspace of the MXFP8 GEMMs: their 8 work-queue counters.

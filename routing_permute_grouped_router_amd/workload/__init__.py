@@ -14,13 +14,16 @@ Workloads (T tokens, hidden H, per-expert FFN width F, E experts, top-k):
   deepseek_mxfp8  T=8192  H=7168 F=2048  E=256 k=8  sigmoid, normalised
                   MXFP8 E4M3 (block-32 E8M0 scales) inputs, bf16 output
 
+and, for the narrower MX format, deepseek_mxfp4: the DeepSeek-shaped layer
+with MXFP4 storage (E2M1 elements packed two per byte, the same scales).
+
 Value recipe: x ~ N(0, 1); router weight W_r (H x E) ~ N(0, 0.02); gate/up
 weights ~ N(0, H^-1/2); down weights ~ N(0, F^-1/2) (N(0, H^-1/2) for the tiny
 workload); output gradient dY ~ N(0, 1).  The second argument is the standard
 deviation.  Values are drawn in float64 by a counter-based generator
 (Philox4x32-10 + Box-Muller, see workload_gen.c) and stored in the workload's
 format: float32, or bfloat16 rounded from the float32 value.  MXFP8 workloads
-hand out float32 values, which each side quantises itself.
+and MXFP4 workloads hand out float32 values, which each side quantises itself.
 
 Router logits = float32( x @ W_r (+ bias) ) computed in float64 on the host from
 the stored x (unquantised float32 x for MXFP8): the router GEMM sits outside the
@@ -103,7 +106,7 @@ class MoEShape:
     k: int
     score: str = "softmax"        # "softmax" | "sigmoid"
     renorm: bool = False          # normalise the selected weights over k
-    dtype: str = "bf16"           # storage of x / weights: "f32" | "bf16" | "mxfp8"
+    dtype: str = "bf16"           # storage of x / weights: "f32" | "bf16" | "mxfp8" | "mxfp4"
     zipf_bias: Optional[float] = None  # Zipf exponent of the per-expert logit bias
     backward: bool = False
     down_std_from_h: bool = False  # down weights ~ N(0, H^-1/2) instead of F^-1/2
@@ -135,7 +138,12 @@ WORKLOADS = [
              backward=True, seed=1003),
     MoEShape("deepseek_mxfp8", 8192, 7168, 2048, 256, 8, "sigmoid", True, "mxfp8", seed=1004),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
+# The DeepSeek-shaped layer on MXFP4 storage (the MX analogue of the NVFP4
+# recipe of the pages; not one of the five).
+EXTRA_WORKLOADS = [
+    MoEShape("deepseek_mxfp4", 8192, 7168, 2048, 256, 8, "sigmoid", True, "mxfp4", seed=1005),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
 
 def zipf_bias(E: int, s: float) -> np.ndarray:
@@ -216,6 +224,18 @@ class Workload:
 def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns (uint16) to float32."""
     return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def mxfp4_shapes() -> list:
+    """MXFP4 parity shapes (H and F multiples of 512): several GEMM tiles,
+    ragged group tails, skewed routing with empty experts and 16-row groups,
+    and a plain-softmax top-2 shape with the down GEMM's K = 1024."""
+    return [
+        MoEShape("small_mxfp4", 260, 512, 512, 16, 4, "sigmoid", True, "mxfp4", seed=2020),
+        MoEShape("small_mxfp4_skew_align", 300, 1024, 512, 16, 4, "softmax", True, "mxfp4", align=16,
+                 zipf_bias=1.2, seed=2021),
+        MoEShape("small_mxfp4_k1024", 517, 512, 1024, 8, 2, "softmax", False, "mxfp4", seed=2022),
+    ]
 
 
 def small_shapes() -> list:

@@ -38,12 +38,16 @@ def rel_err(a, b) -> float:
 #   of an E4M3 rounding boundary, that term of the sum moves by one step,
 #   2^-3 of the value; over a sum of F terms of random sign that is about
 #   2^-3 / sqrt(F) of the result, 2^-6.5 for the smallest F here (128).
+#   e2m1_out: bf16 outputs of a product over a requantised MXFP4 h.  One E2M1
+#   step is up to 2^-1 of the value; in one term of a sum of F >= 512 terms of
+#   random sign that is about 2^-1 / sqrt(512) = 2^-5.5 of the result.
 ELEM_BOUNDS = {"f32": (2.0 ** -16, 2.0 ** -17), "bf16": (2.0 ** -7, 2.0 ** -9),
                "e4m3": (2.0 ** -3, 2.0 ** -9), "e4m3_out": (2.0 ** -5, 2.0 ** -8),
-               "f32acc": (2.0 ** -10, 2.0 ** -12)}
+               "e2m1_out": (2.0 ** -4, 2.0 ** -7), "f32acc": (2.0 ** -10, 2.0 ** -12)}
 # normwise bars max|a-b| / max|b| of the same kinds (1e-5 fp32, 2e-2 bf16,
-# 6e-2 MXFP8; float32 weight gradients over bf16 operands take the bf16 bar)
-NORM_TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2, "e4m3_out": 6e-2, "f32acc": 2e-2}
+# 6e-2 for the MX formats; float32 weight gradients over bf16 operands take
+# the bf16 bar)
+NORM_TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2, "e4m3_out": 6e-2, "e2m1_out": 6e-2, "f32acc": 2e-2}
 ELEM_FRAC = 0.999  # share of elements that must meet the per-element bound
 
 

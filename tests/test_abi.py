@@ -136,6 +136,28 @@ def test_backward_workspace_bounds():
 def test_quantize_rejects_ragged_cols():
     lib = moe.load_library()
     assert lib.moe_quantize_mxfp8(256, 4, 33, 256, 256, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp4(256, 4, 48, 256, 256, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp4(256, -1, 32, 256, 256, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp4(None, 4, 64, 256, 256, None) == b.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_mxfp4(None, 0, 64, None, None, None) == b.MOE_OK  # nothing to do
+
+
+def test_mxfp4_shapes_and_backward_checked_on_host():
+    """MXFP4 needs H and F to be multiples of 512 (a 128-byte GEMM stage holds
+    256 values and a 16-byte load brings a row's scales of two stages), and
+    the backward is built for bf16 storage only."""
+    lib = moe.load_library()
+    for H, F in ((256, 512), (512, 256), (640, 512)):
+        c = _cfg(dtype=b.MOE_MXFP4, H=H, F=F)
+        mx = dict(x_scale=256, w1_scale=256, w2_scale=256, xp_scale=256, h_scale=256)
+        assert _forward(lib, c, **mx) == b.MOE_ERR_UNSUPPORTED, (H, F)
+        assert b"512" in lib.moe_last_error()
+    c = _cfg(dtype=b.MOE_MXFP4, H=512, F=512)
+    assert _backward(lib, c, ws_bytes=1 << 20) == b.MOE_ERR_UNSUPPORTED
+    # the MX scales are required
+    mx = dict(x_scale=256, w1_scale=256, w2_scale=256, xp_scale=256, h_scale=256)
+    for name in ("h_scale", "xp_scale", "x_scale", "w1_scale"):
+        assert _forward(lib, c, **{**mx, name: None}) == b.MOE_ERR_INVALID_ARG, name
 
 
 def test_python_layer_type_errors():
@@ -160,6 +182,26 @@ def test_device_e4m3_rounding_matches_oracle(tmp_path):
     subprocess.run(["/opt/rocm/bin/hipcc", "-O2", "-std=c++17", "--offload-arch=gfx950", "-x", "hip",
                     "-I", str(root / "include"), "-I", str(root / "routing_permute_grouped_router_amd" / "csrc"),
                     str(root / "tests" / "e4m3_check.cpp"), "-x", "none", str(lib), "-Wl,-rpath," + str(lib.parent),
+                    "-o", str(exe)], check=True, capture_output=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
+def test_device_e2m1_rounding_matches_the_oracle(tmp_path):
+    """The E2M1 rounding of the MXFP4 quantiser and epilogue, compiled for the
+    host, against the oracle's encoder on every float in [2^-4, 2^5) of both
+    signs (below, everything rounds to 0; above, everything saturates: both
+    sampled)."""
+    import subprocess
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    lib = root / "oracle" / "liboracle.so"
+    if not lib.exists():
+        pytest.skip("oracle library not built")
+    exe = tmp_path / "e2m1_check"
+    subprocess.run(["/opt/rocm/bin/hipcc", "-O2", "-std=c++17", "--offload-arch=gfx950", "-x", "hip",
+                    "-I", str(root / "include"), "-I", str(root / "routing_permute_grouped_router_amd" / "csrc"),
+                    str(root / "tests" / "e2m1_check.cpp"), "-x", "none", str(lib), "-Wl,-rpath," + str(lib.parent),
                     "-o", str(exe)], check=True, capture_output=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-2000:]

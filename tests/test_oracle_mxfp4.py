@@ -189,3 +189,22 @@ def test_expert_major_forward_equals_token_loops_mxfp4():
     b = orc.forward_experts(s, toks, x, w1, w2, idx, w, xs, w1s, w2s, want_stash=True)
     for key in ("h", "h_scale", "yp", "stash", "y"):
         assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+
+
+def test_down_projection_equals_the_forward_yp():
+    """down_projection on the oracle's own stored h gives the forward's Yp
+    bytes (MXFP4 and bf16 storage)."""
+    s, (x, xs), (w1, w1s), (w2, w2s), lg = _small_mx4(30, 64, 64, 4, 2, 27)
+    idx, w = orc.route(lg, s.k, s.score, s.renorm)
+    a = orc.forward_tokens(s, np.arange(s.T), x, w1, w2, idx, w, xs, w1s, w2s)
+    yp = orc.down_projection(s, idx.ravel(), a["h"].reshape(-1, s.F // 2), a["h_scale"].reshape(-1, s.F // 32),
+                             w2, w2s)
+    assert np.array_equal(yp.view(np.uint16), a["yp"].reshape(-1, s.H).view(np.uint16))
+    rng = np.random.default_rng(28)
+    sb = MoEShape("rand_bf16", 30, 64, 64, 4, 2, "softmax", True, "bf16")
+    xb = orc.bf16_from_f64(rng.standard_normal((30, 64)))
+    w1b = orc.bf16_from_f64(rng.standard_normal((4, 128, 64)) / 8)
+    w2b = orc.bf16_from_f64(rng.standard_normal((4, 64, 64)) / 8)
+    b = orc.forward_tokens(sb, np.arange(30), xb, w1b, w2b, idx, w, site="fc2")
+    yp = orc.down_projection(sb, idx.ravel(), b["h"].reshape(-1, 64), None, w2b, row_w=w.ravel())
+    assert np.array_equal(yp, b["yp"].reshape(-1, 64))
