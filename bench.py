@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
+PEAK_FP4_TFLOPS = 10100.0   # MI355X dense fp4 / MXFP4 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -63,9 +64,11 @@ def parse():
 GEMM1_SOURCES = {
     "bf16": ["gemm_bf16_kernel.h", "gemm_bf16.hip", "tiles.h", "moe_internal.h"],
     "mxfp8": ["gemm_mxfp8_kernel.h", "gemm_bf16_kernel.h", "mxfp8.hip", "mxfp8.h", "tiles.h", "moe_internal.h"],
+    "mxfp4": ["gemm_mxfp8_kernel.h", "gemm_bf16_kernel.h", "mxfp8.hip", "mxfp8.h", "tiles.h", "moe_internal.h"],
     "f32": ["gemm_f32.hip", "tiles.h", "moe_internal.h"],
 }
-GEMM1_KERNEL = {"bf16": "grouped_gemm_bf16<true", "mxfp8": "grouped_gemm_mxfp8<true", "f32": "grouped_gemm_f32<true"}
+GEMM1_KERNEL = {"bf16": "grouped_gemm_bf16<true", "mxfp8": "grouped_gemm_mxfp8<true", "mxfp4": "grouped_gemm_mxfp8<true",
+                "f32": "grouped_gemm_f32<true"}
 
 
 def kernel_source_hash(dtype: str) -> str:
@@ -156,23 +159,24 @@ def main():
     x = up(w.x(), gen_fmt)
     # weights expert by expert (bounded host memory)
     sd = cfg.store_dtype
-    w1 = torch.empty(s.E, 2 * s.F, s.H, dtype=sd, device=dev)
-    w2 = torch.empty(s.E, s.H, s.F, dtype=sd, device=dev)
+    w1 = torch.empty(s.E, 2 * s.F, cfg.cols(s.H), dtype=sd, device=dev)
+    w2 = torch.empty(s.E, s.H, cfg.cols(s.F), dtype=sd, device=dev)
     scales = {}
-    if s.dtype == "mxfp8":
+    quantize = moe.moe_quantize_mxfp4 if s.dtype == "mxfp4" else moe.moe_quantize_mxfp8
+    if cfg.is_mx:
         scales["w1_scale"] = torch.empty(s.E, 2 * s.F, s.H // 32, dtype=torch.uint8, device=dev)
         scales["w2_scale"] = torch.empty(s.E, s.H, s.F // 32, dtype=torch.uint8, device=dev)
-        xq = torch.empty(s.T, s.H, dtype=torch.uint8, device=dev)
+        xq = torch.empty(s.T, cfg.cols(s.H), dtype=torch.uint8, device=dev)
         scales["x_scale"] = torch.empty(s.T, s.H // 32, dtype=torch.uint8, device=dev)
-        moe.moe_quantize_mxfp8(x, xq, scales["x_scale"])
+        quantize(x, xq, scales["x_scale"])
         x = xq
     step_e = max(1, (1 << 28) // (2 * s.F * s.H))
     for e0 in range(0, s.E, step_e):
         e1 = min(s.E, e0 + step_e)
         a1, a2 = up(w.w1(e0, e1), gen_fmt), up(w.w2(e0, e1), gen_fmt)
-        if s.dtype == "mxfp8":
-            moe.moe_quantize_mxfp8(a1, w1[e0:e1], scales["w1_scale"][e0:e1])
-            moe.moe_quantize_mxfp8(a2, w2[e0:e1], scales["w2_scale"][e0:e1])
+        if cfg.is_mx:
+            quantize(a1, w1[e0:e1], scales["w1_scale"][e0:e1])
+            quantize(a2, w2[e0:e1], scales["w2_scale"][e0:e1])
         else:
             w1[e0:e1].copy_(a1)
             w2[e0:e1].copy_(a2)
@@ -366,7 +370,7 @@ def main():
         note("variants done")
 
     R, T, H, F, E, k = s.R, s.T, s.H, s.F, s.E, s.k
-    esz = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32}[s.dtype]
+    esz = {"f32": 4, "bf16": 2, "mxfp8": 1 + 1 / 32, "mxfp4": 0.5 + 1 / 32}[s.dtype]
     osz = 4 if s.dtype == "f32" else 2
     flops = {"swiglu_gemm": 4.0 * R * H * F, "down_gemm": 2.0 * R * H * F}
     # algorithmic bytes (each operand read once, each output written once)
@@ -384,7 +388,8 @@ def main():
         # dlogits and dw written, idx and row_map read
         "route_bwd": T * H * osz + R * H * osz + 2 * T * E * 4 + T * k * 12,
     }
-    peak_mm = {"f32": PEAK_FP32_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "mxfp8": PEAK_FP8_TFLOPS}[s.dtype]
+    peak_mm = {"f32": PEAK_FP32_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "mxfp8": PEAK_FP8_TFLOPS,
+               "mxfp4": PEAK_FP4_TFLOPS}[s.dtype]
     kern = {}
     for n in names:
         d = {"ms": round(kern_ms[n], 4)}
@@ -413,11 +418,12 @@ def main():
     except (OSError, ValueError):
         pass
     tf = flops["swiglu_gemm"] / (kern_ms["swiglu_gemm"] * 1e-3) / 1e12
-    if s.dtype == "mxfp8":
-        # MXFP8 weights are streamed once at ~433 FLOP/B, below the MXFP8 ridge
-        # (5000 TFLOP/s / 8 TB/s = 625 FLOP/B): the kernel is HBM-bound.
+    if cfg.is_mx:
+        # MX weights are streamed once at ~433 FLOP/B (MXFP8; ~840 for MXFP4),
+        # below the ridge (5000 TFLOP/s / 8 TB/s = 625 FLOP/B for MXFP8,
+        # 10100 / 8 = 1262 for MXFP4): the kernel is HBM-bound.
         gbs = bytes_["swiglu_gemm"] / (kern_ms["swiglu_gemm"] * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "kernel": "grouped_gemm_mxfp8_swiglu", "achieved": round(gbs, 1),
+        roofline = {"bound": "hbm", "kernel": f"grouped_gemm_{s.dtype}_swiglu", "achieved": round(gbs, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                     "bytes_per_launch": bytes_["swiglu_gemm"], "tflops": round(tf, 1),
                     "frac_mfma": round(tf / peak_mm, 4)}
@@ -443,19 +449,19 @@ def main():
         t_route = time.time() - t0
         # host weights of the experts the sample uses (the others stay zero pages)
         need = np.unique(idx_o[toks])
-        mx = s.dtype == "mxfp8"
-        wdt = {"f32": np.float32, "bf16": np.uint16, "mxfp8": np.uint8}[s.dtype]
-        w1h = np.zeros((E, 2 * F, H), wdt)
-        w2h = np.zeros((E, H, F), wdt)
+        mx = cfg.is_mx
+        wdt = {"f32": np.float32, "bf16": np.uint16, "mxfp8": np.uint8, "mxfp4": np.uint8}[s.dtype]
+        w1h = np.zeros((E, 2 * F, cfg.cols(H)), wdt)
+        w2h = np.zeros((E, H, cfg.cols(F)), wdt)
         xsc = w1sc = w2sc = None
         if mx:
-            xs, xsc = orc.mx_quantize(xs)
+            xs, xsc = orc.mx_quantize(xs, s.dtype)
             w1sc = np.zeros((E, 2 * F, H // 32), np.uint8)
             w2sc = np.zeros((E, H, F // 32), np.uint8)
         for e in need[need >= 0]:
             a1, a2 = w.w1(int(e), int(e) + 1)[0], w.w2(int(e), int(e) + 1)[0]
             if mx:
-                (w1h[e], w1sc[e]), (w2h[e], w2sc[e]) = orc.mx_quantize(a1), orc.mx_quantize(a2)
+                (w1h[e], w1sc[e]), (w2h[e], w2sc[e]) = orc.mx_quantize(a1, s.dtype), orc.mx_quantize(a2, s.dtype)
             else:
                 w1h[e], w2h[e] = a1, a2
         t0 = time.time()
@@ -477,7 +483,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8-e4m3"}[s.dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "mxfp8": "mxfp8-e4m3", "mxfp4": "mxfp4-e2m1"}[s.dtype],
         "data": "synthetic",
         "config": {"workload": s.name, "T": T, "H": H, "F": F, "E": E, "k": k, "score": s.score,
                    "renorm": s.renorm, "storage": s.dtype, "accumulate": "f32", "backward": s.backward,
