@@ -101,6 +101,14 @@ struct MxArgs {
 // (its 64 B-code rows): the next unit's B half of that buffer is issued only
 // after the epilogue, once w's reads of the tile are done.
 
+// A copy of a wavefront-uniform value that the compiler cannot see through,
+// so that a compare on it is made where it is used (a scalar compare and
+// branch) rather than hoisted out of the loop as a lane mask.
+__device__ __forceinline__ int opaque_s(int v) {
+    __asm__ volatile("" : "+s"(v));
+    return v;
+}
+
 // One operand fragment of a 64-byte K step: two 16-byte chunks (lo, hi).
 template <int OFF>
 __device__ __forceinline__ i32x8 mx_frag(uint32_t lo, uint32_t hi) {
@@ -189,16 +197,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     }
     __syncthreads();
     int unit = s_unit;
-    const int lrow = lane / CH, lslot = lane % CH;
 
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)&lds[0];
     // LDS rows this wave's loads fill: wid * 64 .. +63 of each operand
     const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(wid * 64 * BKB));
     const uint32_t lds_wsc = __builtin_amdgcn_readfirstlane(lds_base + SC_BASE + (uint32_t)(wid * 64 * SW_ROW));
     const int bfr = SWIGLU ? wn * 64 : wn * 128;  // first B row of this wave's fragments
-    const uint32_t a_rd = lds_base + (uint32_t)((wm * 128 + (lane & 31)) * BKB);
+    // the wavefront's A fragment mi is tile rows 32 (2 mi + wm) .. + 31
+    const uint32_t a_rd = lds_base + (uint32_t)((wm * 32 + (lane & 31)) * BKB);
     const uint32_t b_rd = lds_base + (uint32_t)(OPB + (bfr + (lane & 31)) * BKB);
-    const uint32_t as_rd = lds_base + SC_BASE + (uint32_t)((wm * 128 + (lane & 31)) * SW_ROW);
+    const uint32_t as_rd = lds_base + SC_BASE + (uint32_t)((wm * 32 + (lane & 31)) * SW_ROW);
     const uint32_t bs_rd = lds_base + SC_BASE + (uint32_t)(SC_OP + (bfr + (lane & 31)) * SW_ROW);
     // chunk offsets [K step][lo, hi][fragment parity]: lane l reads 16-byte
     // chunks 4 s + h and 4 s + 2 + h (h = l / 32) of row l % 32 of a
@@ -211,8 +219,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
 #pragma unroll
             for (int par = 0; par < 2; ++par)
                 kc[s][hl][par] = (uint32_t)(((4 * s + 2 * hl + half) ^ swz<1>(par * 32 + (lane & 31))) << 4);
+    // the same for the A fragments, all of whose rows have parity wm
+    uint32_t kca[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+            kca[s][hl] = (uint32_t)(((4 * s + 2 * hl + half) ^ swz<1>(wm * 32 + (lane & 31))) << 4);
 
     int kb = 0, ke = 0, row0 = 0, row_end = 0, a_end = 0, nt = 0;
+    // this wavefront's A fragments with rows of the group (nv, 0..4), and its
+    // A code loads per stage that fill rows of the tile's fragments with rows
+    // (na, 0..LOADS)
+    int nv = 4, na = LOADS;
     bool valid = false;
     uint32_t aoff[LOADS], boff[LOADS], asoff = 0, bsoff = 0;
     const uint8_t* acodes = p.A;
@@ -221,6 +240,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     const uint8_t* bscale = p.Bs;
 #define MX_LOAD_A(kt, stage, i)                                                                          \
     dma_lds16(lds_wave + (uint32_t)(stage) * STB + (i) * RPL * BKB, aoff[i], acodes + (size_t)(kt) * BKB)
+// an in-loop A load, skipped when it fills only rows of fragments without rows
+#define MX_LOAD_A_IF(kt, stage, i)                                                                       \
+    if ((i) < opaque_s(na)) MX_LOAD_A(kt, stage, i)
 #define MX_LOAD_B(kt, stage, i)                                                                          \
     dma_lds16(lds_wave + (uint32_t)(stage) * STB + OPB + (i) * RPL * BKB, boff[i], bcodes + (size_t)(kt) * BKB)
 // scale words of load group grp (G stages) into slot `slot`
@@ -238,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
 #define MX_SB __builtin_amdgcn_sched_barrier(0)
 // fragment reads of K step S of the stage at byte offset SO
 #define MX_RD_A(F, SO, S, mi)                                                                            \
-    F[mi] = mx_frag<(mi) * 32 * BKB>(a_rd + (SO) + kc[S][0][(mi) & 1], a_rd + (SO) + kc[S][1][(mi) & 1])
+    F[mi] = mx_frag<(mi) * 64 * BKB>(a_rd + (SO) + kca[S][0], a_rd + (SO) + kca[S][1])
 #define MX_RD_B(G, SO, S, ni)                                                                            \
     G[ni] = mx_frag<(ni) == 0 ? 0 : (ni) == 1 ? B1 : (ni) == 2 ? B2 : B3>(b_rd + (SO) + kc[S][0][(ni) & 1], \
                                                                           b_rd + (SO) + kc[S][1][(ni) & 1])
@@ -248,18 +270,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
     {                                                                                                    \
         if constexpr (F4) {                                                                              \
             sw2[0] = mx_word2<0>(as_rd + (SO));                                                          \
-            sw2[1] = mx_word2<32 * SW_ROW>(as_rd + (SO));                                                \
-            sw2[2] = mx_word2<64 * SW_ROW>(as_rd + (SO));                                                \
-            sw2[3] = mx_word2<96 * SW_ROW>(as_rd + (SO));                                                \
+            sw2[1] = mx_word2<64 * SW_ROW>(as_rd + (SO));                                                \
+            sw2[2] = mx_word2<128 * SW_ROW>(as_rd + (SO));                                               \
+            sw2[3] = mx_word2<192 * SW_ROW>(as_rd + (SO));                                               \
             sw2[4] = mx_word2<0>(bs_rd + (SO));                                                          \
             sw2[5] = mx_word2<W1>(bs_rd + (SO));                                                         \
             sw2[6] = mx_word2<W2>(bs_rd + (SO));                                                         \
             sw2[7] = mx_word2<W3>(bs_rd + (SO));                                                         \
         } else {                                                                                         \
             SW[0] = mx_word<0>(as_rd + (SO));                                                            \
-            SW[1] = mx_word<32 * SW_ROW>(as_rd + (SO));                                                  \
-            SW[2] = mx_word<64 * SW_ROW>(as_rd + (SO));                                                  \
-            SW[3] = mx_word<96 * SW_ROW>(as_rd + (SO));                                                  \
+            SW[1] = mx_word<64 * SW_ROW>(as_rd + (SO));                                                  \
+            SW[2] = mx_word<128 * SW_ROW>(as_rd + (SO));                                                 \
+            SW[3] = mx_word<192 * SW_ROW>(as_rd + (SO));                                                 \
             SW[4] = mx_word<0>(bs_rd + (SO));                                                            \
             SW[5] = mx_word<W1>(bs_rd + (SO));                                                           \
             SW[6] = mx_word<W2>(bs_rd + (SO));                                                           \
@@ -287,7 +309,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
 // E2M1: two MFMAs on the fragments' low and high four registers (blocks
 // 4 S + h and 4 S + 2 + h: bytes 0 and 2 of the stage's word S).
 #define MX_MFMA(F, G, SS, S, mi, ni)                                                                     \
-    if constexpr (F4) {                                                                                  \
+    if ((mi) >= opaque_s(nv)) {                                                                          \
+    } else if constexpr (F4) {                                                                           \
         acc[mi][ni] = mfma_scale_e2m1(__builtin_shufflevector(F[mi], F[mi], 0, 1, 2, 3),                 \
                                       __builtin_shufflevector(G[ni], G[ni], 0, 1, 2, 3), acc[mi][ni], 4, 4, 0, \
                                       (int)SS[2 * (mi) + (S)], 0, (int)SS[2 * (4 + (ni)) + (S)]);        \
@@ -331,6 +354,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         }
         // rows with an A row of their own: all, or (gather) the routed rows
         a_end = p.src_map ? __builtin_amdgcn_readfirstlane(min(offs[e] + p.counts[e], row_end)) : row_end;
+        {
+            const int nfrag = (min(row_end - row0, kTile) + 31) >> 5;  // 32-row fragments with rows: 1..8
+            nv = __builtin_amdgcn_readfirstlane((nfrag - wm + 1) >> 1);
+            na = __builtin_amdgcn_readfirstlane(min(max(nfrag * 32 - wid * 64, 0) / RPL, LOADS));
+        }
         const int brow0 = SWIGLU ? nt * 128 : nt * kTile;
         // row of A (tile-relative, or of x when gathering) that tile row r reads
         auto a_row = [&](int r) -> int {
@@ -345,6 +373,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
             }
             return min(nt * kTile + out_col(r), p.n_out - 1);
         };
+        // Per-lane load offsets from an opaque copy of the lane index, so the
+        // compiler forms them per tile instead of holding per-lane constants
+        // across the K loop.
+        int sl = lane;
+        __asm__ volatile("" : "+v"(sl));
+        const int lrow = sl / CH, lslot = sl % CH;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int r = wid * 64 + i * RPL + lrow;  // tile row 0..255
@@ -353,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
             boff[i] = (uint32_t)((size_t)(b_row(r) - brow0) * KB + chunk * 16);
         }
         {
-            const int r = wid * 64 + lane;  // tile row of this lane's scale words
+            const int r = wid * 64 + sl;  // tile row of this lane's scale words
             asoff = (uint32_t)(a_row(r) * KS);
             bsoff = (uint32_t)((b_row(r) - brow0) * KS);
         }
@@ -402,13 +436,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
             s_unit = nu;
             tick = nu >= 0 ? ticket() : -1;
         }
+        // The accumulators live in the accumulator registers for the whole
+        // tile: empty asm statements with "a" constraints (at the zeroing and
+        // once per stage) keep the register allocator from moving them
+        // through VGPRs around the MFMAs that the fragment count may skip.
         f32x16 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
+                f32x16 z;
 #pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+                for (int q = 0; q < 16; ++q) z[q] = 0.f;
+                __asm__ volatile("" : "=a"(acc[i][j]) : "0"(z));
+            }
+#define MX_PIN_ACC(I)                                                                                    \
+    __asm__ volatile("" : "+a"(acc[I][0]), "+a"(acc[I][1]), "+a"(acc[I][2]), "+a"(acc[I][3]))
         MX_RD_A(fa0, 0u, 0, 0);
         MX_RD_A(fa0, 0u, 0, 1);
         MX_RD_A(fa0, 0u, 0, 2);
@@ -432,6 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         const int sg = G == 1 ? kl : min(kt_ / G + 1, (ke - 1) / G);                                     \
         const int sslot = G == 1 ? st_ : ((kt_ / G) + 1) & 1;                                            \
         const uint32_t nsc = MX_SC_OFF(kt_ + 1);                                                         \
+        MX_PIN_ACC(0); MX_PIN_ACC(1); MX_PIN_ACC(2); MX_PIN_ACC(3);                                      \
         MX_SB;                                                                                           \
         if constexpr (F4) {                                                                              \
             _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                              \
@@ -466,21 +510,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         MX_SB;                                                                                           \
         /* K step 1 on fa1/fb1; stage kt+1's first fragments and scale words are */                     \
         /* read, and the loads of stage kt+2 go into buffer ST */                                        \
-        MX_STEP(fa1, fb1, ss, 1, 0, 0, MX_LOAD_A(kl, st_, 0), MX_RD_A(fa0, nso, 0, 0))                   \
+        MX_STEP(fa1, fb1, ss, 1, 0, 0, MX_LOAD_A_IF(kl, st_, 0), MX_RD_A(fa0, nso, 0, 0))                   \
         MX_STEP(fa1, fb1, ss, 1, 0, 1, MX_LOAD_B(kl, st_, 0), MX_RD_A(fa0, nso, 0, 1))                   \
-        MX_STEP(fa1, fb1, ss, 1, 0, 2, MX_LOAD_A(kl, st_, 1), MX_RD_A(fa0, nso, 0, 2))                   \
+        MX_STEP(fa1, fb1, ss, 1, 0, 2, MX_LOAD_A_IF(kl, st_, 1), MX_RD_A(fa0, nso, 0, 2))                   \
         MX_STEP(fa1, fb1, ss, 1, 0, 3, MX_LOAD_B(kl, st_, 1), MX_RD_A(fa0, nso, 0, 3))                   \
-        MX_STEP(fa1, fb1, ss, 1, 1, 0, MX_LOAD_A(kl, st_, 2), MX_RD_B(fb0, nso, 0, 0))                   \
+        MX_STEP(fa1, fb1, ss, 1, 1, 0, MX_LOAD_A_IF(kl, st_, 2), MX_RD_B(fb0, nso, 0, 0))                   \
         MX_STEP(fa1, fb1, ss, 1, 1, 1, MX_LOAD_B(kl, st_, 2), MX_RD_B(fb0, nso, 0, 1))                   \
-        MX_STEP(fa1, fb1, ss, 1, 1, 2, MX_LOAD_A(kl, st_, 3), MX_RD_B(fb0, nso, 0, 2))                   \
+        MX_STEP(fa1, fb1, ss, 1, 1, 2, MX_LOAD_A_IF(kl, st_, 3), MX_RD_B(fb0, nso, 0, 2))                   \
         MX_STEP(fa1, fb1, ss, 1, 1, 3, MX_LOAD_B(kl, st_, 3), MX_RD_B(fb0, nso, 0, 3))                   \
-        MX_STEP(fa1, fb1, ss, 1, 2, 0, MX_LOAD_A(kl, st_, 4); if (SCL) MX_LOAD_AS(sg, sslot), MX_RD_S(sw, nsc)) \
+        MX_STEP(fa1, fb1, ss, 1, 2, 0, MX_LOAD_A_IF(kl, st_, 4); if (SCL) MX_LOAD_AS(sg, sslot), MX_RD_S(sw, nsc)) \
         MX_STEP(fa1, fb1, ss, 1, 2, 1, MX_LOAD_B(kl, st_, 4), (void)0)                                   \
-        MX_STEP(fa1, fb1, ss, 1, 2, 2, MX_LOAD_A(kl, st_, 5), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 2, 2, MX_LOAD_A_IF(kl, st_, 5), (void)0)                                   \
         MX_STEP(fa1, fb1, ss, 1, 2, 3, MX_LOAD_B(kl, st_, 5), (void)0)                                   \
-        MX_STEP(fa1, fb1, ss, 1, 3, 0, MX_LOAD_A(kl, st_, 6), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 3, 0, MX_LOAD_A_IF(kl, st_, 6), (void)0)                                   \
         MX_STEP(fa1, fb1, ss, 1, 3, 1, MX_LOAD_B(kl, st_, 6), (void)0)                                   \
-        MX_STEP(fa1, fb1, ss, 1, 3, 2, MX_LOAD_A(kl, st_, 7), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 3, 2, MX_LOAD_A_IF(kl, st_, 7), (void)0)                                   \
         MX_STEP(fa1, fb1, ss, 1, 3, 3, MX_LOAD_B(kl, st_, 7); if (SCL) MX_LOAD_BS(sg, sslot), (void)0)   \
         /* the next stage's first fragments and scale words landed (no LDS read */                      \
         /* is in flight when the loop ends) */                                                           \
@@ -506,8 +550,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
             }
         }
 #undef MX_STAGE
+#undef MX_PIN_ACC
         MX_SB;
 #undef MX_LOAD_A
+#undef MX_LOAD_A_IF
 #undef MX_LOAD_B
 #undef MX_LOAD_SC
 #undef MX_LOAD_AS
@@ -526,13 +572,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         const int next_unit = s_unit;
         const int e_row0 = row0, e_row_end = row_end, e_a_end = a_end, e_nt = nt;
         const bool e_valid = valid;
-        // routing weights of this wave's 128 rows, two per lane (rows 2 lane
-        // and 2 lane + 1 of the band), loaded and waited for before setup
-        // issues the next unit's loads
+        // routing weights of this wave's 128 rows, two per lane (its rows
+        // 2 lane and 2 lane + 1; its row i is tile row 32 (2 (i / 32) + wm) +
+        // i % 32), loaded and waited for before setup issues the next unit's
+        // loads
         float rwa = 1.f, rwb = 1.f;
         if constexpr ((EP & 1) != 0) {
             if (e_valid) {
-                const float* const rwp = p.row_w + e_row0 + wm * 128 + 2 * lane;
+                const float* const rwp = p.row_w + e_row0 + 32 * (2 * (lane >> 4) + wm) + ((2 * lane) & 31);
                 rwa = rwp[0];
                 rwb = rwp[1];
             }
@@ -568,7 +615,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
         float v[16];                                                                                     \
         float amax = 0.f;                                                                                \
-        const bool pad = wm * 128 + (MI) * 32 + rr >= alim; /* gather: padding rows are zeros */        \
+        const bool pad = (2 * (MI) + wm) * 32 + rr >= alim; /* gather: padding rows are zeros */        \
         float rw = 1.f;                                                                                  \
         if constexpr ((EP & 1) != 0) {                                                                              \
             const float wa_ = __shfl(rwa, ((MI) * 32 + rr) >> 1, 64);                                    \
@@ -581,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         }                                                                                                \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                                              \
         amax = fmaxf(amax, __shfl_xor(amax, 1, 64));                                                     \
-        const int r = wm * 128 + (MI) * 32 + rr;                                                         \
+        const int r = (2 * (MI) + wm) * 32 + rr;                                                         \
         const int f = e_nt * 128 + wn * 64 + (NI) * 32 + cc;                                             \
         if (r < rlim && f < p.n_out) {                                                                   \
             const size_t row = (size_t)(rbase + r);                                                      \
@@ -634,7 +681,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
                 const int n = e_nt * kTile + wn * 128 + 4 * lc;  // this lane's columns n .. n + 3
 #define MX_EPI_DN(MI)                                                                                    \
     {                                                                                                    \
-        const int rb0 = wm * 128 + (MI) * 32;                                                            \
+        const int rb0 = (2 * (MI) + wm) * 32;                                                            \
         uint2 w[16];                                                                                     \
         float rw[16];                                                                                    \
         if constexpr ((EP & 1) != 0) {                                                                              \
