@@ -453,11 +453,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
 #undef GB_SUBSTEP_LA
 #undef GB_SUBSTEP_LB
 #undef GB_SUBSTEP_NR
-        // Epilogue through LDS, so that each lane handles 8 consecutive
-        // columns of a row: 16-byte bf16 stores (dgrad), two 16-byte float32
-        // stores (weight gradients), 16-byte stash loads and dG / dU stores
-        // (dgrad + dSwiGLU), a quarter (half for float32) of the memory
-        // instructions of lane pairs.  Each wavefront stages its 128 x 128
+        // Weight gradients (float32) are stored straight from the
+        // accumulators: lane l holds column l % 32 of each fragment, so one
+        // 4-byte store per row and fragment writes two whole 128-byte rows
+        // (lanes 0..31 and 32..63, four rows apart) -- the same bytes per
+        // instruction as the LDS-staged form below would give, without its
+        // LDS round trip.
+        // The dgrad epilogues go through LDS, so that each lane handles 8
+        // consecutive columns of a row: 16-byte bf16 stores (dgrad), 16-byte
+        // stash loads and dG / dU stores (dgrad + dSwiGLU), a quarter of the
+        // memory instructions of lane pairs.  Each wavefront stages its 128 x 128
         // float32 sub-tile in two halves of 64 rows in its own 32 KiB of the
         // stage buffers (free once every wave's last loads landed; the barrier
         // at the next tile's claim keeps the next loads out until every wave
@@ -470,9 +475,45 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
         // hoisted out of the tile loop, where it would hold registers).
         int mbase = m0, ln = lane;
         __asm__ volatile("" : "+v"(mbase), "+v"(ln));
+        if constexpr (WG) {
+            // this wave's last loads (repeats of the last stage) landed before
+            // the next tile's loads go out
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const int N = p.N;
+            const int rlim = p.M - mbase;                         // rows of the tile that exist
+            const int col = n0 + wn * 128 + (ln & 31);            // + 32 ni
+            const int r0 = wm * 128 + 4 * (ln >> 5);              // + 32 mi + 8 (q / 4) + q % 4
+            float* const wb = cw + (size_t)mbase * N + col;
+            if (rlim >= kTile && n0 + kTile <= N) {  // uniform: a whole tile, no checks
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        float* const d = wb + (size_t)(r0 + 32 * mi + 8 * (q >> 2) + (q & 3)) * N;
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni) d[32 * ni] = agpr_read(acc[mi][ni][q]);
+                    }
+            } else {
+                bool cok[4];
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) cok[ni] = col + 32 * ni < N;
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int r = r0 + 32 * mi + 8 * (q >> 2) + (q & 3);
+                        float* const d = wb + (size_t)r * N;
+                        const bool rok = r < rlim;
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni)
+                            if (rok && cok[ni]) d[32 * ni] = agpr_read(acc[mi][ni][q]);
+                    }
+            }
+            continue;
+        }
         __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         const int N = p.N;
-        const int rlim = WG ? p.M - mbase : row_end - mbase;  // rows of the tile that exist
+        const int rlim = row_end - mbase;  // rows of the tile that exist
         uint8_t* const stg = &lds[0][0][0] + wid * 32768;
         const int hh = ln >> 5, ca = (ln & 31) >> 2;
         uint8_t* wa[4];  // this lane's write address for fragment ni (row 0 of the half)
@@ -488,12 +529,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
                 ra[par][hl] = stg + rq * 512 + ((((2 * kc8 + hl) ^ (kc8 >> 3)) ^ (par << 3)) << 4);
         const int ncol = n0 + wn * 128 + 8 * kc8;  // this lane's first column
         const bool col_ok = ncol < N;
-        // row 0 of the tile at this lane's columns: weight gradient (float32,
-        // N per row), dgrad (bf16, N per row), dgrad + dSwiGLU (bf16, 2N per
-        // row, stash alike)
+        // row 0 of the tile at this lane's columns: dgrad (bf16, N per row),
+        // dgrad + dSwiGLU (bf16, 2N per row, stash alike)
         const int ldc = MODE == kDgradDswiglu ? 2 * N : N;
-        float* const wbase = WG ? cw + (size_t)mbase * N + ncol : nullptr;
-        uint16_t* const cbase = WG ? nullptr : p.C + (size_t)mbase * ldc + ncol;
+        uint16_t* const cbase = p.C + (size_t)mbase * ldc + ncol;
         const uint16_t* const sbase = MODE == kDgradDswiglu ? p.stash + (size_t)mbase * ldc + ncol : nullptr;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -528,13 +567,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
                 const bool ok = col_ok && r < rlim;
                 const float4 lo = *(const float4*)(ra[ps & 1][0] + ps * 2048);
                 const float4 hi = *(const float4*)(ra[ps & 1][1] + ps * 2048);
-                if (WG) {
-                    if (ok) {
-                        float4* const d = (float4*)(wbase + (size_t)r * N);
-                        d[0] = lo;
-                        d[1] = hi;
-                    }
-                } else if (MODE == kDgrad) {
+                if (MODE == kDgrad) {
                     if (ok)
                         *(uint4*)(cbase + (size_t)r * ldc) = make_uint4(
                             pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w), pack_bf16x2(hi.x, hi.y),
