@@ -51,6 +51,10 @@ def parse():
                    help="HBM bytes per dispatch measured with rocprofv3 counters (optional)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="also run a plain device copy of this many MiB (reference for counter scaling)")
+    p.add_argument("--lds-calibration", type=int, default=0, metavar="MIB",
+                   help="also run one 256 x 256 tile of the bf16 down GEMM whose two operands (this many MiB "
+                        "together) are each read exactly once through direct-to-LDS loads: the reference for "
+                        "scaling the FETCH_SIZE of the grouped GEMMs")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                         "--copy-calibration run into the traffic file and exit (no GPU needed)")
@@ -81,10 +85,33 @@ def kernel_source_hash(dtype: str) -> str:
     return h.hexdigest()[:16]
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, workload: str, out_path: str) -> None:
+def lds_calibration(mib: int, dev) -> None:
+    """One tile of the bf16 down GEMM (E = 1, 256 rows, H = 256, K = F) whose
+    A and B are each read once, as the grouped GEMMs read their operands
+    (direct-to-LDS loads): mib MiB of operand bytes in one dispatch."""
+    import torch
+
+    import routing_permute_grouped_router_amd as moe
+
+    F = (mib << 20) // (2 * 256 * 2)
+    cfg = moe.MoEConfig(256, 256, F, 1, 1)
+    h = torch.ones(256, F, dtype=torch.bfloat16, device=dev)
+    w2 = torch.ones(1, 256, F, dtype=torch.bfloat16, device=dev)
+    offsets = torch.tensor([0, 256], dtype=torch.int32, device=dev)
+    yp = torch.empty(256, 256, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(moe.workspace_size(cfg), 1), dtype=torch.uint8, device=dev)
+    moe.moe_grouped_down_gemm(cfg, h, w2, offsets, yp, ws)
+    torch.cuda.synchronize()
+    del h, w2, yp, ws
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str, out_path: str, lds_mib: int = 0) -> None:
     """Per-dispatch HBM bytes of the grouped GEMM1 from FETCH_SIZE / WRITE_SIZE
-    (KiB per dispatch), each scaled by the ratio the same counter shows for the
-    largest plain device copy in the run (the --copy-calibration copy)."""
+    (KiB per dispatch), each scaled by the ratio the same counter shows for a
+    dispatch of known bytes in the same run: the largest plain device copy (the
+    --copy-calibration copy), and for the GEMM's fetches, when the run had one,
+    the --lds-calibration tile (the first bf16 down-GEMM dispatch), whose loads
+    are of the GEMMs' own kind."""
     import csv
     import collections
 
@@ -94,28 +121,36 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, out_path: str) ->
 
     s = wl.BY_NAME[workload]
     res = {}
+    lds_fetch = None
     for cnt, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         per = collections.defaultdict(list)
         copies = []
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != cnt:
-                continue
+        rows = sorted((r for r in csv.DictReader(open(path)) if r["Counter_Name"] == cnt),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
             v = float(r["Counter_Value"])
             if "copyBuffer" in r["Kernel_Name"]:
                 copies.append(v)
-            per[r["Kernel_Name"].split("(")[0]].append(v)
+            name_ = r["Kernel_Name"].split("(")[0]
+            if cnt == "FETCH_SIZE" and lds_mib and lds_fetch is None and "grouped_gemm_bf16<false" in name_:
+                lds_fetch = v  # the first bf16 down-GEMM dispatch: the calibration tile
+                continue
+            per[name_].append(v)
         kib_copy = max(copies)  # the calibration copy of `cal` MiB is the largest copy
         res[cnt] = (per, kib_copy)
     cal_kib = res["WRITE_SIZE"][1]  # written bytes of a copy are its size (checked below)
     f_scale = cal_kib / res["FETCH_SIZE"][1]
     w_scale = 1.0
+    # the GEMM's own loads: scale by the direct-to-LDS calibration tile if the run had one
+    g_scale = (lds_mib * 1024) / lds_fetch if lds_fetch else f_scale
     name = [n for n in res["FETCH_SIZE"][0] if GEMM1_KERNEL[s.dtype] in n][0]
-    fetch = float(np.mean(res["FETCH_SIZE"][0][name])) * f_scale * 1024
+    fetch = float(np.mean(res["FETCH_SIZE"][0][name])) * g_scale * 1024
     write = float(np.mean(res["WRITE_SIZE"][0][name])) * w_scale * 1024
     out = {"workload": workload, "kernel": "swiglu_gemm", "kernel_name": name,
            "source_hash": kernel_source_hash(s.dtype), "bytes_per_dispatch": round(fetch + write),
            "fetch_bytes": round(fetch), "write_bytes": round(write), "copy_kib": cal_kib,
-           "fetch_scale": round(f_scale, 4), "write_scale": w_scale}
+           "fetch_scale": round(g_scale, 4), "copy_fetch_scale": round(f_scale, 4), "write_scale": w_scale,
+           "lds_calibration_mib": lds_mib if lds_fetch else 0}
     with open(out_path, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
@@ -125,7 +160,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, out_path: str) ->
 def main():
     args = parse()
     if args.pmc_summary:
-        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.traffic)
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.traffic, args.lds_calibration)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the MoE layer; multi-GPU runs are not part of this build "
@@ -236,6 +271,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.lds_calibration:
+        lds_calibration(args.lds_calibration, dev)
 
     for _ in range(args.warmup):
         step()
