@@ -11,7 +11,7 @@ the FFN backward.
 Prints one JSON line: tokens/s of the layer over the K timed steps, each
 kernel's duration in those steps (mean, median, p10, p90; HIP events on the
 launch stream), route / permute / combine again with cold caches (a 512 MiB
-write before each of 50 calls), a route sweep over T, the roofline of the
+read before each of 50 calls), a route sweep over T, the roofline of the
 dominant kernel (the grouped gate/up GEMM) and the CPU oracle timed on a
 bounded token sample.
 """
@@ -42,7 +42,7 @@ def parse():
     # measured the fine-grained step ~7 % slower
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--flush-iters", type=int, default=50,
-                   help="calls of each bandwidth kernel timed with cold caches (512 MiB flush before each)")
+                   help="calls of each bandwidth kernel timed with cold caches (512 MiB read before each)")
     p.add_argument("--workload", default="mixtral_bf16")
     p.add_argument("--no-variants", action="store_true",
                    help="skip the variant timings (gather form, weight placements, clamp): counter passes")
@@ -293,10 +293,13 @@ def main():
     def pct(v, q):
         return v[min(len(v) - 1, int(q * len(v)))]
 
-    # Bandwidth kernels with cold caches: a 512 MiB write (outside the event
+    # Bandwidth kernels with cold caches: a 512 MiB read (outside the event
     # window) evicts L2 and the 256 MiB MALL before each of `flush_iters`
-    # calls, so route, permute and combine read their inputs from HBM.
-    flushbuf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # calls, so route, permute and combine read their inputs from HBM.  A read
+    # leaves clean lines; a write would leave the caches full of dirty ones,
+    # whose write-back to HBM would then be charged to the timed kernel.
+    flushbuf = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+    flush_words = flushbuf.view(torch.int32)
     bw_calls = {
         "route": lambda: moe.moe_route(cfg, logits, buf["idx"], buf["w"]),
         "permute": lambda: moe.moe_permute(cfg, x, buf["idx"], buf["xp"], buf["counts"], buf["offsets"],
@@ -308,7 +311,7 @@ def main():
     for n, f in bw_calls.items():
         samples = []
         for it in range(args.flush_iters):
-            flushbuf.fill_(it & 255)
+            flush_words.sum()
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record(stream)
             f()
@@ -330,7 +333,7 @@ def main():
             moe.moe_route(cs, lg, ix, wt)
         samples = []
         for it in range(20):
-            flushbuf.fill_(it & 255)
+            flush_words.sum()
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record(stream)
             moe.moe_route(cs, lg, ix, wt)
@@ -342,7 +345,7 @@ def main():
         route_sweep.append({"T": Ts, "ms": round(pct(v, 0.5), 4), "gbs": round(nb / (pct(v, 0.5) * 1e-3) / 1e9, 1),
                             "frac_hbm": round(nb / (pct(v, 0.5) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
         del lg, ix, wt
-    del flushbuf
+    del flushbuf, flush_words
     note("route sweep done")
 
     if s.backward:

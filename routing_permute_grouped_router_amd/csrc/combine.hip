@@ -126,8 +126,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                 }
             }
         }
-        V::store(y, t * vec_per_row + c0, acc0);
-        if (two) V::store(y, t * vec_per_row + c1, acc1);
+        // y is not read again here: non-temporal stores keep it from
+        // displacing cached lines
+        V::template store<true>(y, t * vec_per_row + c0, acc0);
+        if (two) V::template store<true>(y, t * vec_per_row + c1, acc1);
     }
 }
 
