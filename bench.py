@@ -163,7 +163,7 @@ def main():
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.traffic, args.lds_calibration)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU's share of the MoE layer; multi-GPU runs are not part of this build "
+        print("bench.py measures one GPU's share of the MoE layer and runs on one GPU only "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
