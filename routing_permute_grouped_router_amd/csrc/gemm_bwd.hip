@@ -21,12 +21,19 @@ int64_t rows_cap(const moe_config& c) { return (int64_t)c.T * c.k + (int64_t)c.E
 
 constexpr int64_t kPartBudget = (int64_t)1 << 30;  // bytes of partial sums a weight gradient may use
 
-// Rows per weight-gradient work unit for an [M][N] gradient: at least 4096,
-// doubled until the partial sums of all split experts fit the budget.  An
-// expert with more than S rows has at most 2 rows / S units, so the experts
-// that are split use at most floor(2 R_cap / S) slots.
+// Rows per weight-gradient work unit for an [M][N] gradient.  A unit's tiles
+// should take at most half of the average work of one of the 256 CUs,
+// T k / 64 stages times the M x N tiles spread over 256 CUs, so that the
+// dealing can still balance them; every split expert costs a float32 partial
+// sum per unit and a reduction pass, so a unit is not cut smaller than that
+// (and never below 4096 rows).  The result is then doubled until the partial
+// sums of all split experts fit the budget.  An expert with more than S rows
+// has at most 2 rows / S units, so the experts that are split use at most
+// floor(2 R_cap / S) slots.  S depends on the config only, so the workspace
+// query and the launch agree.
 int wgrad_split_rows(const moe_config& c, int64_t M, int64_t N) {
-    int64_t S = 4096;
+    const int64_t tiles = cdiv(M, gemm::kTile) * cdiv(N, gemm::kTile);
+    int64_t S = std::max<int64_t>(4096, (int64_t)c.T * c.k * tiles / (2 * 256) / 64 * 64);
     while ((2 * rows_cap(c) / S) * M * N * 4 > kPartBudget) S *= 2;
     return (int)S;
 }

@@ -3,7 +3,7 @@ fused with the SwiGLU backward, gate/up backward, permute backward) against
 the CPU oracle, through the C ABI.
 
 Small shapes (skewed routing; 16-row group alignment), a shape whose experts
-exceed the 4096-row unit of the weight gradients, and the full-size skewed
+exceed the 4096-row unit of its weight gradients, and the full-size skewed
 workload (T=16384, H=2048, F=768, E=128, top-8, Zipf-biased routing): every
 gradient compared in full, normwise and element by element, and dW of every
 empty expert exactly zero (it starts as NaN)."""
@@ -126,7 +126,9 @@ def test_backward_full_size_skewed():
     """The skewed layer (T=16384, H=2048, F=768, E=128, top-8) in the launch
     configuration the benchmark times, every gradient compared in full with
     the oracle's expert-major form: dYp, dGU, dXp and dX, and dW1 / dW2 of
-    every expert, the split hot experts (more than 4096 rows) included."""
+    every expert, the split hot experts included (the weight-gradient unit is
+    max(4096, T k tiles / 512) rows rounded down to 64: 12288 rows for dW1's
+    6 x 8 tiles, 6144 for dW2's 8 x 3)."""
     s = wl.BY_NAME["skewed_bf16"]
     inp = Inputs(s, want_dy=True)
     fwd = run_forward(inp, training=True, poison=False)
@@ -135,9 +137,12 @@ def test_backward_full_size_skewed():
     counts, offsets, row_map, src_map, _ = orc.group(idx, s.E, s.align)
     assert np.array_equal(to_host(fwd["offsets"]), offsets)
     empty = np.where(counts == 0)[0]
+    unit_dw1 = s.T * s.k * 48 // 512 // 64 * 64
+    unit_dw2 = s.T * s.k * 24 // 512 // 64 * 64
+    assert (unit_dw1, unit_dw2) == (12288, 6144)
     print(f"skewed routing: {len(empty)} empty experts, max count {int(counts.max())}, "
-          f"{int((counts > 4096).sum())} experts above 4096 rows")
-    assert (counts > 4096).sum() >= 3, "the hot experts should take the split weight-gradient path"
+          f"{int((counts > unit_dw1).sum())} / {int((counts > unit_dw2).sum())} experts split for dW1 / dW2")
+    assert (counts > unit_dw1).sum() >= 3, "the hot experts should take the split weight-gradient path"
     g = _backward_experts(s, inp, w, src_map, offsets, row_map)
     n = int(offsets[-1])
     for key in ("dyp", "dgu", "dxp"):
@@ -147,7 +152,7 @@ def test_backward_full_size_skewed():
     assert np.all(dw1[empty] == 0) and np.all(dw2[empty] == 0)
     assert np.all(np.isfinite(dw1)) and np.all(np.isfinite(dw2))
     hot = np.argsort(-counts, kind="stable")[:3]
-    for e in list(hot) + [e for e in range(s.E) if 0 < counts[e] <= 4096][:3]:
+    for e in list(hot) + [e for e in range(s.E) if 0 < counts[e] <= unit_dw2][:3]:
         assert_parity(dw1[e], g["dw1"][e], "f32acc", f"dW1 of expert {e} ({counts[e]} rows)")
         assert_parity(dw2[e], g["dw2"][e], "f32acc", f"dW2 of expert {e} ({counts[e]} rows)")
     assert_parity(dw1, g["dw1"], "f32acc", "dW1")
