@@ -147,8 +147,15 @@ hipError_t launch_down_bwd(const moe_config& c, const void* dyp, const void* w2,
     zero_counters_kernel<<<1, 64, 0, s>>>(cnt);
     gemm::BwdArgs d{(const uint16_t*)dyp, (const uint16_t*)w2, offsets, c.E, (int)R, 0, c.F, c.H,
                     (uint16_t*)dgu, nullptr, (const uint16_t*)stash, nullptr, nullptr, 0, 0, cnt};
-    d.lim = c.swiglu_limit > 0.f ? c.swiglu_limit : INFINITY;
-    hipError_t e = launch<gemm::kDgradDswiglu>(d, (R / gemm::kTile + c.E) * cdiv(c.F, gemm::kTile), s);
+    const int64_t dgrad_tiles = (R / gemm::kTile + c.E) * cdiv(c.F, gemm::kTile);
+    hipError_t e;
+    if (c.swiglu_limit > 0.f) {
+        d.lim = c.swiglu_limit;
+        e = launch<gemm::kDgradDswigluClamp>(d, dgrad_tiles, s);
+    } else {
+        d.lim = INFINITY;
+        e = launch<gemm::kDgradDswiglu>(d, dgrad_tiles, s);
+    }
     if (e != hipSuccess) return e;
     gemm::BwdArgs w{(const uint16_t*)dyp, (const uint16_t*)h, offsets, c.E, (int)R, c.H, c.F, 0,
                     nullptr, dw2, nullptr, nullptr, nullptr, 0, 0, nullptr};

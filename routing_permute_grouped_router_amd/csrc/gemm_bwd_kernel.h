@@ -41,7 +41,9 @@
 namespace moe {
 namespace gemm {
 
-enum BwdMode { kDgrad = 0, kDgradDswiglu = 1, kWgrad = 2 };
+// kDgradDswigluClamp: kDgradDswiglu for a forward with the SwiGLU clamp (a
+// separate instance, so the plain one carries no clamp work per element).
+enum BwdMode { kDgrad = 0, kDgradDswiglu = 1, kWgrad = 2, kDgradDswigluClamp = 3 };
 
 struct BwdArgs {
     const uint16_t* A;      // DGRAD: [rows][K]; WGRAD: [rows][M]
@@ -66,7 +68,7 @@ struct BwdArgs {
     // Tile counters, one per XCD, zero at launch: the blocks of an XCD take
     // their next tile from the XCD's list with an atomic increment.
     int* sched;
-    // kDgradDswiglu: the forward's SwiGLU clamp limit (+inf: none); the
+    // kDgradDswigluClamp: the forward's SwiGLU clamp limit; the
     // gradient of a clamped gate or up value is 0, values on a bound pass
     float lim;
 };
@@ -117,6 +119,7 @@ template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
     constexpr int BK = 64;
     constexpr bool WG = MODE == kWgrad;
+    constexpr bool DSW = MODE == kDgradDswiglu || MODE == kDgradDswigluClamp;  // SwiGLU backward epilogue
     constexpr int OPB = kTile * BK * 2;  // bytes of one operand in one stage
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][OPB];
     __shared__ int32_t pre[kMaxExperts + 1];
@@ -531,9 +534,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
         const bool col_ok = ncol < N;
         // row 0 of the tile at this lane's columns: dgrad (bf16, N per row),
         // dgrad + dSwiGLU (bf16, 2N per row, stash alike)
-        const int ldc = MODE == kDgradDswiglu ? 2 * N : N;
+        const int ldc = DSW ? 2 * N : N;
         uint16_t* const cbase = p.C + (size_t)mbase * ldc + ncol;
-        const uint16_t* const sbase = MODE == kDgradDswiglu ? p.stash + (size_t)mbase * ldc + ncol : nullptr;
+        const uint16_t* const sbase = DSW ? p.stash + (size_t)mbase * ldc + ncol : nullptr;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             // dgrad + dSwiGLU: stash rows of the half's 16 passes (4 rows each)
@@ -548,8 +551,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
             uq[(PS) & 7] = *(const uint4*)(sbase + (size_t)r_ * ldc + N);                                \
         }                                                                                                \
     }
-            const bool clamp = MODE == kDgradDswiglu && p.lim < INFINITY;  // uniform
-            if (MODE == kDgradDswiglu) {
+            if (DSW) {
 #pragma unroll
                 for (int ps = 0; ps < 8; ++ps) GB_LOAD_STASH(ps)
             }
@@ -585,16 +587,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
                         for (int h = 0; h < 2; ++h) {
                             float g = __uint_as_float(h ? (gw[j] & 0xffff0000u) : (gw[j] << 16));
                             float u = __uint_as_float(h ? (uw[j] & 0xffff0000u) : (uw[j] << 16));
-                            float mg = 1.f, mu = 1.f;
-                            if (clamp) {
-                                mg = g > p.lim ? 0.f : 1.f;
-                                mu = (u > p.lim || u < -p.lim) ? 0.f : 1.f;
+                            // a = dh sigma(g); dU = a g; dG = a u (1 + g (1 - sigma(g)))
+                            if constexpr (MODE == kDgradDswigluClamp) {
+                                const bool kg = !(g > p.lim), ku = !(u > p.lim || u < -p.lim);
                                 g = fminf(g, p.lim);
                                 u = fminf(fmaxf(u, -p.lim), p.lim);
+                                const float sg = sigmoid_fast(g);
+                                const float a = dh[2 * j + h] * sg;
+                                rg[h] = kg ? a * u * fmaf(g, 1.0f - sg, 1.0f) : 0.f;
+                                ru[h] = ku ? a * g : 0.f;
+                            } else {
+                                const float sg = sigmoid_fast(g);
+                                const float a = dh[2 * j + h] * sg;
+                                rg[h] = a * u * fmaf(g, 1.0f - sg, 1.0f);
+                                ru[h] = a * g;
                             }
-                            const float sg = sigmoid_fast(g);
-                            rg[h] = dh[2 * j + h] * u * sg * (1.0f + g * (1.0f - sg)) * mg;
-                            ru[h] = dh[2 * j + h] * g * sg * mu;
                         }
                         dg[j] = pack_bf16x2(rg[0], rg[1]);
                         du[j] = pack_bf16x2(ru[0], ru[1]);
