@@ -194,6 +194,23 @@ __device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Nontemporal store of a 1-, 4-, 8- or 16-byte value: GEMM outputs are not
+// read again by the kernel that writes them, and leaving them out of the
+// cache's working set keeps the operand panels that neighbouring blocks share
+// resident in L2.
+template <class T>
+__device__ __forceinline__ void st_nt(T* p, const T& v) {
+    if constexpr (sizeof(T) == 16) {
+        typedef unsigned u4v __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(__builtin_bit_cast(u4v, v), (u4v*)p);
+    } else if constexpr (sizeof(T) == 8) {
+        typedef unsigned u2v __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(__builtin_bit_cast(u2v, v), (u2v*)p);
+    } else {
+        __builtin_nontemporal_store(v, p);
+    }
+}
+
 #ifndef GK_BARRIER_AT
 #define GK_BARRIER_AT 40
 #endif
@@ -586,13 +603,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     }
 // Store W[q] (type T) to row q past DST (LD elements per row) for q = 0..3:
 // the lane's rows of the 16-row block at tile row RB0; rows are checked only
-// when the block runs past the group's end.
+// when the block runs past the group's end.  Nontemporal (st_nt).
 #define GB_STORE_ROWS(T, DST, LD, RB0, W)                                                                \
     if ((RB0) + 16 <= rlim) {                                                                            \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) *(T*)((DST) + (size_t)q * (LD)) = (W)[q];          \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) st_nt((T*)((DST) + (size_t)q * (LD)), (W)[q]);      \
     } else {                                                                                             \
         _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                    \
-            if ((RB0) + lr + q < rlim) *(T*)((DST) + (size_t)q * (LD)) = (W)[q];                         \
+            if ((RB0) + lr + q < rlim) st_nt((T*)((DST) + (size_t)q * (LD)), (W)[q]);                     \
     }
 
         if (e_slot >= 0) {

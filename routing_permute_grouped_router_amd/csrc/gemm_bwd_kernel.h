@@ -461,7 +461,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
         // 4-byte store per row and fragment writes two whole 128-byte rows
         // (lanes 0..31 and 32..63, four rows apart) -- the same bytes per
         // instruction as the LDS-staged form below would give, without its
-        // LDS round trip.
+        // LDS round trip.  Every output store of these kernels is
+        // nontemporal (st_nt).
         // The dgrad epilogues go through LDS, so that each lane handles 8
         // consecutive columns of a row: 16-byte bf16 stores (dgrad), 16-byte
         // stash loads and dG / dU stores (dgrad + dSwiGLU), a quarter of the
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
                     for (int q = 0; q < 16; ++q) {
                         float* const d = wb + (size_t)(r0 + 32 * mi + 8 * (q >> 2) + (q & 3)) * N;
 #pragma unroll
-                        for (int ni = 0; ni < 4; ++ni) d[32 * ni] = agpr_read(acc[mi][ni][q]);
+                        for (int ni = 0; ni < 4; ++ni) st_nt(d + 32 * ni, agpr_read(acc[mi][ni][q]));
                     }
             } else {
                 bool cok[4];
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
                         const bool rok = r < rlim;
 #pragma unroll
                         for (int ni = 0; ni < 4; ++ni)
-                            if (rok && cok[ni]) d[32 * ni] = agpr_read(acc[mi][ni][q]);
+                            if (rok && cok[ni]) st_nt(d + 32 * ni, agpr_read(acc[mi][ni][q]));
                     }
             }
             continue;
@@ -571,9 +572,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
                 const float4 hi = *(const float4*)(ra[ps & 1][1] + ps * 2048);
                 if (MODE == kDgrad) {
                     if (ok)
-                        *(uint4*)(cbase + (size_t)r * ldc) = make_uint4(
+                        st_nt((uint4*)(cbase + (size_t)r * ldc), make_uint4(
                             pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w), pack_bf16x2(hi.x, hi.y),
-                            pack_bf16x2(hi.z, hi.w));
+                            pack_bf16x2(hi.z, hi.w)));
                 } else {
                     const float dh[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                     const uint32_t gw[4] = {gq[ps & 7].x, gq[ps & 7].y, gq[ps & 7].z, gq[ps & 7].w};
@@ -607,8 +608,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bwd(BwdArgs p) {
                         du[j] = pack_bf16x2(ru[0], ru[1]);
                     }
                     if (ok) {
-                        *(uint4*)(cbase + (size_t)r * ldc) = make_uint4(dg[0], dg[1], dg[2], dg[3]);
-                        *(uint4*)(cbase + (size_t)r * ldc + N) = make_uint4(du[0], du[1], du[2], du[3]);
+                        st_nt((uint4*)(cbase + (size_t)r * ldc), make_uint4(dg[0], dg[1], dg[2], dg[3]));
+                        st_nt((uint4*)(cbase + (size_t)r * ldc + N), make_uint4(du[0], du[1], du[2], du[3]));
                     }
                 }
             }
