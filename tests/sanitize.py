@@ -41,7 +41,7 @@ def _copy(dst: str) -> None:
     skip = shutil.ignore_patterns("*.so", "*.o", "_build", "__pycache__", "*.tmp")
     for name in ("include", "oracle", "routing_permute_grouped_router_amd", "tests"):
         shutil.copytree(os.path.join(ROOT, name), os.path.join(dst, name), ignore=skip)
-    for name in ("pytest.ini", "__graft_entry__.py"):
+    for name in ("pytest.ini", "__graft_entry__.py", "bench.py"):
         shutil.copy2(os.path.join(ROOT, name), dst)
 
 
