@@ -17,8 +17,10 @@ namespace moe {
 namespace {
 
 // Tuned on MI355X with the Mixtral-shaped and fine-grained layers (kGroupM = 0:
-// tiles expert by expert, each weight panel streamed once).
-constexpr int kSwizzle = 2, kGroupM = 0;
+// tiles expert by expert, each weight panel streamed once; kSwizzle = 0: no
+// LDS bank conflicts in the fragment reads, and half the LDS-active cycles of
+// mode 2 at the same speed).
+constexpr int kSwizzle = 0, kGroupM = 0;
 
 int g_num_cus = 0;
 

@@ -124,6 +124,11 @@ __device__ __forceinline__ Queue xcd_queue(int total, int x, int nb, int nk) {
 // row).  128-byte rows: mode 0 spreads any 8 consecutive rows over distinct
 // banks of a 32-bank LDS, mode 1 also any 16 over a 64-bank one.  64-byte rows
 // (two per 128 bytes): the same two guarantees with the row pair folded in.
+// Which one suits a kernel depends on how its fragment reads map lanes to
+// rows, and was measured (the LDS bank-conflict counter): the bf16 kernel's
+// 16x16x32 reads (lane l: row l % 16) are conflict-free with mode 0, while
+// mode 2 stalls on conflicts in half of its LDS-active cycles; the MXFP8
+// kernel's 32x32x64 reads (lane l: row l % 32) conflict least with mode 1.
 template <int SWZ, int CH = 8>
 __device__ __forceinline__ int swz(int row) {
     if (CH == 8) {
