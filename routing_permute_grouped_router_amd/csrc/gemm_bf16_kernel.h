@@ -267,11 +267,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     constexpr int STAGE_ELEMS = kTile * BK; // one operand of one stage
     constexpr uint32_t kRowBytes = BK * 2;
     constexpr uint32_t kFragBytes = 16 * kRowBytes;  // one 16-row fragment
-    // The stage's barrier sits before MFMA kBar of its first sub-step; the 16
-    // loads of stage k+2 follow it, one per four MFMAs (kLoads0 of them in the
-    // first sub-step, the rest at the start of the second).
+    // The stage's first barrier sits before MFMA kBar of its first sub-step;
+    // the 16 loads of stage k+2 follow it, one per four MFMAs (kLoads0 of them
+    // in the first sub-step, the rest at the start of the second).
     constexpr int kBar = GK_BARRIER_AT;
     constexpr int kLoads0 = (64 - kBar + 3) / 4;
+    // A second barrier, before MFMA kBarB of the second sub-step: stage kt+1
+    // has landed for every wave, and its first fragments are read after it.
+    constexpr int kBarB = 16;
 
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][STAGE_ELEMS];
     __shared__ int32_t pre[kMaxExperts + 1];
@@ -448,13 +451,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
         // other buffer stage kt+1, landed or in flight):
         //   sub-step 0: 64 MFMAs on the fragments fx (K 0..31 of stage kt),
         //     the 16 fragment reads of K 32..63 into fy under the first 32;
-        //     then each wave has read all of stage kt and its loads of stage
-        //     kt+1 have landed (waitcnt), and past the barrier that holds for
-        //     every wave: buffer st is free and stage kt+1 readable.  The 16
+        //     then each wave has read all of stage kt (lgkmcnt), and past the
+        //     barrier that holds for every wave: buffer st is free.  The 16
         //     loads of stage kt+2 into buffer st start there, B (the weights,
         //     first touched in HBM) before A, one per four MFMAs;
-        //   sub-step 1: 64 MFMAs on fy, the rest of those loads and the 16
-        //     fragment reads of stage kt+1's K 0..31 into fx.
+        //   sub-step 1: 64 MFMAs on fy and the rest of those loads; before
+        //     MFMA kBarB each wave waits for its loads of stage kt+1 (those of
+        //     stage kt+2 may stay in flight), and past a second barrier stage
+        //     kt+1 is readable for every wave: the 16 fragment reads of its K
+        //     0..31 into fx follow.  Waiting for stage kt+1 there rather than at
+        //     the first barrier gives its last loads ~100 MFMAs instead of ~70
+        //     to land.
         // One load per four MFMAs per wave is about what the CU's address unit
         // sustains for the four wavefronts.  There are no loads past K.
         bf16x8 fxa[8], fxb[8], fya[8], fyb[8];
@@ -513,8 +520,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             static_for<64>([&](auto mc) __attribute__((always_inline)) {
                 constexpr int m = decltype(mc)::value;
                 if constexpr (m == kBar) {
-                    // own reads of stage kt and own loads of stage kt+1 done; then for every wave
-                    __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier"
+                    // own reads of stage kt done; then for every wave (buffer st is free)
+                    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier"
                                      : "+v"(fya[0]), "+v"(fya[1]), "+v"(fya[2]), "+v"(fya[3]), "+v"(fya[4]),
                                        "+v"(fya[5]), "+v"(fya[6]), "+v"(fya[7]), "+v"(fyb[0]), "+v"(fyb[1]),
                                        "+v"(fyb[2]), "+v"(fyb[3]), "+v"(fyb[4]), "+v"(fyb[5]), "+v"(fyb[6]),
@@ -535,13 +542,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             // unused bytes of the other buffer)
             static_for<64>([&](auto mc) __attribute__((always_inline)) {
                 constexpr int m = decltype(mc)::value;
+                if constexpr (m == kBarB) {
+                    // own loads of stage kt+1 landed: the loads of stage kt+2
+                    // issued so far are younger, and vector memory operations
+                    // complete in issue order; then for every wave
+                    if constexpr (LD) {
+                        static_assert(kLoads0 + (kBarB + 3) / 4 == 10, "the count below is the loads issued so far");
+                        __asm__ volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+                    } else {
+                        __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+                    }
+                    GK_SB;
+                }
                 if constexpr ((m & 3) == 0 && m / 4 < 16 - kLoads0) {
                     GK_LOAD(kLoads0 + m / 4)
                 }
                 acc[m >> 3][m & 7] =
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(fya[m >> 3], fyb[m & 7], acc[m >> 3][m & 7], 0, 0, 0);
-                if constexpr (m < 32 && (m & 1) == 1) {
-                    GK_READ(fxa, fxb, nso, koff0, m / 2)
+                if constexpr (m > kBarB && m < kBarB + 32 && ((m - kBarB) & 1) == 1) {
+                    GK_READ(fxa, fxb, nso, koff0, (m - kBarB) / 2)
                 }
                 GK_SB;
             });
