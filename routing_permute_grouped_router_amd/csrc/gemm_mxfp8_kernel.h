@@ -76,12 +76,15 @@ struct MxArgs {
 // cycle and CU, near what LDS serves; here 64).
 // Two stages of 128 K-bytes of E4M3 codes rotate through LDS; a stage is two
 // K steps of 16 MFMAs each (2048 cycles, as long as a stage of the bf16
-// kernel).  The one barrier per stage sits after the first K step: there
-// this wavefront has read all of stage kt and stage kt+1 has landed.  The 16
-// code loads of stage kt+2 then go into the freed buffer under the 16 MFMAs
-// of the second K step, so each has at least one K step to land before the
-// next barrier, while the fragments of stage kt+1's first K step and its
-// scale words are read.  Scale words (one 32-bit word of four E8M0 bytes per
+// kernel).  Two barriers per stage.  The first, after the first K step, only
+// needs every wavefront to have read all of stage kt: its buffer is free, and
+// the 16 code loads of stage kt+2 go into it under the 16 MFMAs of the second
+// K step, four of B first.  The second, after those four, needs stage kt+1 to
+// have landed (vmcnt(4): only those four loads are younger, and vector memory
+// operations complete in issue order); the fragments of stage kt+1's first K
+// step and its scale words are read after it.  Waiting for stage kt+1 there
+// rather than at the first barrier gives its last loads four more MFMAs (256
+// cycles) to land.  Scale words (one 32-bit word of four E8M0 bytes per
 // row and stage) sit in two slots of their own: with K a multiple of 512, a
 // 16-byte load per row brings the words of four stages (a row's scales are
 // 224 bytes apart at K = 7168, so each 4-byte load touched its own cache
@@ -504,27 +507,32 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mxfp8(MxArgs p) {
         MX_STEP(fa0, fb0, ss, 0, 3, 2, (void)0, (void)0)                                                 \
         MX_STEP(fa0, fb0, ss, 0, 3, 3, (void)0, (void)0)                                                 \
         MX_WAIT_F(fa1, fb1);                                                                             \
-        /* this wave has read all of stage kt and its loads of stage kt+1 landed; */                    \
-        /* past the barrier the same holds for every wave */                                             \
-        __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");                     \
+        /* this wave has read all of stage kt; past the barrier the same holds */                       \
+        /* for every wave, and buffer ST is free */                                                      \
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                              \
         MX_SB;                                                                                           \
-        /* K step 1 on fa1/fb1; stage kt+1's first fragments and scale words are */                     \
-        /* read, and the loads of stage kt+2 go into buffer ST */                                        \
-        MX_STEP(fa1, fb1, ss, 1, 0, 0, MX_LOAD_A_IF(kl, st_, 0), MX_RD_A(fa0, nso, 0, 0))                   \
-        MX_STEP(fa1, fb1, ss, 1, 0, 1, MX_LOAD_B(kl, st_, 0), MX_RD_A(fa0, nso, 0, 1))                   \
-        MX_STEP(fa1, fb1, ss, 1, 0, 2, MX_LOAD_A_IF(kl, st_, 1), MX_RD_A(fa0, nso, 0, 2))                   \
-        MX_STEP(fa1, fb1, ss, 1, 0, 3, MX_LOAD_B(kl, st_, 1), MX_RD_A(fa0, nso, 0, 3))                   \
-        MX_STEP(fa1, fb1, ss, 1, 1, 0, MX_LOAD_A_IF(kl, st_, 2), MX_RD_B(fb0, nso, 0, 0))                   \
-        MX_STEP(fa1, fb1, ss, 1, 1, 1, MX_LOAD_B(kl, st_, 2), MX_RD_B(fb0, nso, 0, 1))                   \
-        MX_STEP(fa1, fb1, ss, 1, 1, 2, MX_LOAD_A_IF(kl, st_, 3), MX_RD_B(fb0, nso, 0, 2))                   \
-        MX_STEP(fa1, fb1, ss, 1, 1, 3, MX_LOAD_B(kl, st_, 3), MX_RD_B(fb0, nso, 0, 3))                   \
-        MX_STEP(fa1, fb1, ss, 1, 2, 0, MX_LOAD_A_IF(kl, st_, 4); if (SCL) MX_LOAD_AS(sg, sslot), MX_RD_S(sw, nsc)) \
-        MX_STEP(fa1, fb1, ss, 1, 2, 1, MX_LOAD_B(kl, st_, 4), (void)0)                                   \
-        MX_STEP(fa1, fb1, ss, 1, 2, 2, MX_LOAD_A_IF(kl, st_, 5), (void)0)                                   \
-        MX_STEP(fa1, fb1, ss, 1, 2, 3, MX_LOAD_B(kl, st_, 5), (void)0)                                   \
-        MX_STEP(fa1, fb1, ss, 1, 3, 0, MX_LOAD_A_IF(kl, st_, 6), (void)0)                                   \
-        MX_STEP(fa1, fb1, ss, 1, 3, 1, MX_LOAD_B(kl, st_, 6), (void)0)                                   \
-        MX_STEP(fa1, fb1, ss, 1, 3, 2, MX_LOAD_A_IF(kl, st_, 7), (void)0)                                   \
+        /* K step 1 on fa1/fb1; the loads of stage kt+2 go into buffer ST, four */                      \
+        /* of B first; then this wave's loads of stage kt+1 (and earlier scale */                       \
+        /* words) have landed: only those four are younger, and vector memory */                        \
+        /* operations complete in issue order; past a second barrier stage */                           \
+        /* kt+1's first fragments and scale words are read */                                            \
+        MX_STEP(fa1, fb1, ss, 1, 0, 0, MX_LOAD_B(kl, st_, 0), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 0, 1, MX_LOAD_B(kl, st_, 1), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 0, 2, MX_LOAD_B(kl, st_, 2), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 0, 3, MX_LOAD_B(kl, st_, 3), (void)0)                                   \
+        __asm__ volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");                                \
+        MX_SB;                                                                                           \
+        MX_STEP(fa1, fb1, ss, 1, 1, 0, MX_LOAD_A_IF(kl, st_, 0), MX_RD_A(fa0, nso, 0, 0))                   \
+        MX_STEP(fa1, fb1, ss, 1, 1, 1, MX_LOAD_A_IF(kl, st_, 1), MX_RD_A(fa0, nso, 0, 1))                   \
+        MX_STEP(fa1, fb1, ss, 1, 1, 2, MX_LOAD_A_IF(kl, st_, 2), MX_RD_A(fa0, nso, 0, 2))                   \
+        MX_STEP(fa1, fb1, ss, 1, 1, 3, MX_LOAD_A_IF(kl, st_, 3), MX_RD_A(fa0, nso, 0, 3))                   \
+        MX_STEP(fa1, fb1, ss, 1, 2, 0, MX_LOAD_A_IF(kl, st_, 4); if (SCL) MX_LOAD_AS(sg, sslot), MX_RD_B(fb0, nso, 0, 0)) \
+        MX_STEP(fa1, fb1, ss, 1, 2, 1, MX_LOAD_A_IF(kl, st_, 5), MX_RD_B(fb0, nso, 0, 1))                   \
+        MX_STEP(fa1, fb1, ss, 1, 2, 2, MX_LOAD_A_IF(kl, st_, 6), MX_RD_B(fb0, nso, 0, 2))                   \
+        MX_STEP(fa1, fb1, ss, 1, 2, 3, MX_LOAD_A_IF(kl, st_, 7), MX_RD_B(fb0, nso, 0, 3))                   \
+        MX_STEP(fa1, fb1, ss, 1, 3, 0, MX_LOAD_B(kl, st_, 4), MX_RD_S(sw, nsc))                          \
+        MX_STEP(fa1, fb1, ss, 1, 3, 1, MX_LOAD_B(kl, st_, 5), (void)0)                                   \
+        MX_STEP(fa1, fb1, ss, 1, 3, 2, MX_LOAD_B(kl, st_, 6), (void)0)                                   \
         MX_STEP(fa1, fb1, ss, 1, 3, 3, MX_LOAD_B(kl, st_, 7); if (SCL) MX_LOAD_BS(sg, sslot), (void)0)   \
         /* the next stage's first fragments and scale words landed (no LDS read */                      \
         /* is in flight when the loop ends) */                                                           \
