@@ -17,8 +17,8 @@ COLS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "
         "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count",
         "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
 COPY = "__amd_rocclr_copyBuffer"
-DOWN = "void moe::gemm::grouped_gemm_bf16<false, 2, 0, 0>(moe::gemm::Args)"
-GEMM1 = "void moe::gemm::grouped_gemm_bf16<true, 2, 0, 0>(moe::gemm::Args)"
+DOWN = "void moe::gemm::grouped_gemm_bf16<false, 0, 0, 0>(moe::gemm::Args)"
+GEMM1 = "void moe::gemm::grouped_gemm_bf16<true, 0, 0, 0>(moe::gemm::Args)"
 
 
 def _write(path, counter, rows, reverse=False):
