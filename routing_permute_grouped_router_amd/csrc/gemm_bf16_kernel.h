@@ -192,6 +192,22 @@ __device__ __forceinline__ void dma_lds4(uint32_t lds, uint32_t voff, const void
                      : "memory", "m0");
 }
 
+// Grouped form of dma_lds16: set_m0 writes M0 once for four loads, and each
+// load's immediate offset is added to both its LDS and its global address (a
+// one-wavefront check with a padded buffer showed both moving by the offset).
+// The grouped GEMM loads four consecutive 1 KiB LDS rows per M0 (offsets 0,
+// 1, 2, 3 KiB); its per-lane global offsets carry a bias of 3 KiB minus the
+// load's offset and the uniform bases are 3 KiB lower, so every global
+// address is the one a plain load would use.  Nothing else in the K loop
+// writes M0.
+__device__ __forceinline__ void set_m0(uint32_t lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0" ::"s"(lds) : "m0");
+}
+template <int OFF>
+__device__ __forceinline__ void dma_lds16_o(uint32_t voff, const void* sbase) {
+    __asm__ volatile("global_load_lds_dwordx4 %0, %1 offset:%2" ::"v"(voff), "s"(sbase), "i"(OFF) : "memory");
+}
+
 template <int OFF>
 __device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
     uint4 v;
@@ -344,12 +360,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
     uint32_t aoff[LOADS], boff[LOADS];
     const char* abase = (const char*)p.A;
     const char* bbase = (const char*)p.B;
+    constexpr uint32_t kBias = 3 * RPL * kRowBytes;  // global offsets are biased by this, the bases lowered
 #define GK_LOAD_A(kt, stage, i)                                                                          \
-    dma_lds16(lds_wave + (uint32_t)(stage) * kStageBytes + (i) * RPL * kRowBytes, aoff[i],               \
-              abase + (size_t)(kt) * (BK * 2))
+    {                                                                                                    \
+        if constexpr ((i) % 4 == 0) set_m0(lds_wave + (uint32_t)(stage) * kStageBytes + (i) * RPL * kRowBytes); \
+        dma_lds16_o<((i) % 4) * RPL * kRowBytes>(aoff[i], abase + (size_t)(kt) * (BK * 2));              \
+    }
 #define GK_LOAD_B(kt, stage, i)                                                                          \
-    dma_lds16(lds_wave + (uint32_t)(stage) * kStageBytes + STAGE_ELEMS * 2 + (i) * RPL * kRowBytes, boff[i], \
-              bbase + (size_t)(kt) * (BK * 2))
+    {                                                                                                    \
+        if constexpr ((i) % 4 == 0)                                                                      \
+            set_m0(lds_wave + (uint32_t)(stage) * kStageBytes + STAGE_ELEMS * 2 + (i) * RPL * kRowBytes);  \
+        dma_lds16_o<((i) % 4) * RPL * kRowBytes>(boff[i], bbase + (size_t)(kt) * (BK * 2));              \
+    }
 // B fragment ni's byte offset from fragment 0 (SwiGLU: up fragments 4..7 are
 // the gate fragments' rows + 128)
 #define GK_BOFF(ni) (SWIGLU ? ((ni) & 3) * kFragBytes + ((ni) >> 2) * 128 * kRowBytes : (ni) * kFragBytes)
@@ -426,21 +448,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
                 br = min(nt * kTile + out_col16(r), p.n_out - 1);
             }
             boff[i] = (uint32_t)(((size_t)(br - brow0) * K + chunk * 8) * 2);
+            aoff[i] += kBias - (uint32_t)((i % 4) * RPL * kRowBytes);
+            boff[i] += kBias - (uint32_t)((i % 4) * RPL * kRowBytes);
         }
-        abase = p.src_map ? (const char*)p.A : (const char*)(p.A + (size_t)row0 * K);
-        bbase = (const char*)(p.B + ((size_t)e * p.b_rows + brow0) * K);
+        abase = (p.src_map ? (const char*)p.A : (const char*)(p.A + (size_t)row0 * K)) - kBias;
+        bbase = (const char*)(p.B + ((size_t)e * p.b_rows + brow0) * K) - kBias;
         GK_SB;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            GK_LOAD_B(kb, 0, i);
-            GK_LOAD_A(kb, 0, i);
-        }
+        static_for<LOADS>([&](auto ic) __attribute__((always_inline)) { GK_LOAD_B(kb, 0, decltype(ic)::value); });
+        static_for<LOADS>([&](auto ic) __attribute__((always_inline)) { GK_LOAD_A(kb, 0, decltype(ic)::value); });
         if (kb + 1 < ke) {
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                GK_LOAD_B(kb + 1, 1, i);
-                GK_LOAD_A(kb + 1, 1, i);
-            }
+            static_for<LOADS>([&](auto ic) __attribute__((always_inline)) { GK_LOAD_B(kb + 1, 1, decltype(ic)::value); });
+            static_for<LOADS>([&](auto ic) __attribute__((always_inline)) { GK_LOAD_A(kb + 1, 1, decltype(ic)::value); });
         }
         GK_SB;
     };
@@ -512,8 +530,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16(Args p) {
             // load j (0..15: B 0..7, then A 0..7) of stage kt+2 into buffer st
 #define GK_LOAD(j)                                                                                       \
     if constexpr (LD) {                                                                                  \
-        if constexpr ((j) < 8) GK_LOAD_B(lkt, st, (j));                                                  \
-        else GK_LOAD_A(lkt, st, (j) - 8);                                                                \
+        if constexpr ((j) < 8) { GK_LOAD_B(lkt, st, (j)); }                                              \
+        else { GK_LOAD_A(lkt, st, (j) - 8); }                                                            \
     }
             GK_SB;
             // sub-step 0
