@@ -229,12 +229,14 @@ def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
 def mxfp4_shapes() -> list:
     """MXFP4 parity shapes (H and F multiples of 512): several GEMM tiles,
     ragged group tails, skewed routing with empty experts and 16-row groups,
-    and a plain-softmax top-2 shape with the down GEMM's K = 1024."""
+    a plain-softmax top-2 shape with the down GEMM's K = 1024, and 128-row
+    groups (most rows of Xp, h and Yp are padding)."""
     return [
         MoEShape("small_mxfp4", 260, 512, 512, 16, 4, "sigmoid", True, "mxfp4", seed=2020),
         MoEShape("small_mxfp4_skew_align", 300, 1024, 512, 16, 4, "softmax", True, "mxfp4", align=16,
                  zipf_bias=1.2, seed=2021),
         MoEShape("small_mxfp4_k1024", 517, 512, 1024, 8, 2, "softmax", False, "mxfp4", seed=2022),
+        MoEShape("small_mxfp4_align128", 260, 512, 512, 8, 2, "sigmoid", True, "mxfp4", align=128, seed=2023),
     ]
 
 

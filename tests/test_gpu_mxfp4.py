@@ -142,7 +142,7 @@ def test_forward_mxfp4_small_full_parity(name):
         assert (counts == 0).any(), "the skewed routing should leave some experts empty"
 
 
-@pytest.mark.parametrize("name", ["small_mxfp4", "small_mxfp4_skew_align"])
+@pytest.mark.parametrize("name", ["small_mxfp4", "small_mxfp4_skew_align", "small_mxfp4_align128"])
 def test_gather_form_equals_materialised(name):
     """moe_forward with xp NULL (the gate/up GEMM reads x through src_map)
     gives the same bytes as the materialised form; padding rows of h are zero
