@@ -1,0 +1,114 @@
+"""GPU parity of the forward at group sizes on the GEMM tile edges.
+
+The grouped GEMMs cut each expert's rows into 256-row M-tiles; the MX kernels
+skip the 32-row fragments of a tile that hold no row of the group.  Here the
+router's logits are set so that top-1 routing gives the experts exactly 256,
+257, 0, 1, 255, 512, 128 and 129 rows: a whole tile, a one-row tail, an empty
+expert, a lone row, a tile one row short, two whole tiles, and half a tile
+with and without one more row.  Every output is compared with the oracle in
+full, as for the small shapes."""
+import numpy as np
+import pytest
+import torch
+
+import routing_permute_grouped_router_amd as moe
+from oracle import oracle as orc
+from routing_permute_grouped_router_amd import workload as wl
+
+from helpers import Inputs, assert_parity, cfg_of, decode, run_forward, to_dev, to_host
+from test_gpu_mxfp4 import check_h
+
+pytestmark = pytest.mark.gpu
+
+SIZES = np.array([256, 257, 0, 1, 255, 512, 128, 129])
+T = int(SIZES.sum())
+EDGE = {
+    "bf16": wl.MoEShape("edge_bf16", T, 512, 384, 8, 1, "softmax", False, "bf16", seed=2030),
+    "mxfp8": wl.MoEShape("edge_mxfp8", T, 512, 256, 8, 1, "softmax", False, "mxfp8", seed=2031),
+    "mxfp4": wl.MoEShape("edge_mxfp4", T, 512, 512, 8, 1, "softmax", False, "mxfp4", seed=2032),
+}
+
+
+def _edge_logits(s, base):
+    """The workload's logits with +8 on one expert per token, the experts
+    dealt to the tokens in a seeded order so that expert e gets SIZES[e]."""
+    owner = np.random.default_rng(s.seed).permutation(np.repeat(np.arange(s.E), SIZES))
+    lg = np.array(base, np.float32)
+    lg[np.arange(s.T), owner] += np.float32(8.0)
+    idx, w = orc.route(lg, s.k, s.score, s.renorm)
+    assert np.array_equal(idx[:, 0], owner)
+    return lg, idx, w
+
+
+def _check_groups(s, buf, idx):
+    assert np.array_equal(to_host(buf["idx"]), idx)
+    counts, offsets, row_map, src_map, _ = orc.group(idx, s.E, s.align)
+    assert np.array_equal(counts, SIZES)
+    for key, ref in (("counts", counts), ("offsets", offsets), ("row_map", row_map), ("src_map", src_map)):
+        assert np.array_equal(to_host(buf[key]), ref), key
+    return offsets, row_map
+
+
+def test_tile_edges_bf16():
+    s = EDGE["bf16"]
+    inp = Inputs(s)
+    inp.logits, idx, w = _edge_logits(s, inp.logits)
+    buf = run_forward(inp, training=True)
+    offsets, row_map = _check_groups(s, buf, idx)
+    n = int(offsets[-1])
+    assert np.array_equal(to_host(buf["xp"])[:n].view(np.uint8), orc.permute(inp.x, row_map, n).view(np.uint8))
+    ref = orc.forward_tokens(s, np.arange(s.T), inp.x, inp.w1, inp.w2, idx, w, want_stash=True)
+    rm = row_map.ravel()
+    assert_parity(decode("bf16", to_host(buf["h"])[rm]), decode("bf16", ref["h"].reshape(-1, s.F)), "bf16", "h")
+    assert_parity(decode("bf16", to_host(buf["gu_stash"])[rm]), decode("bf16", ref["stash"].reshape(-1, 2 * s.F)),
+                  "bf16", "stash")
+    assert_parity(decode("bf16", to_host(buf["yp"])[rm]), decode("bf16", ref["yp"].reshape(-1, s.H)), "bf16", "Yp")
+    assert_parity(decode("bf16", to_host(buf["y"])), decode("bf16", ref["y"]), "bf16", "y")
+
+
+def _quantize(fmt, v):
+    t = to_dev(v, "f32")
+    cols = t.shape[-1] // 2 if fmt == "mxfp4" else t.shape[-1]
+    codes = torch.empty(t.shape[:-1] + (cols,), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(t.shape[:-1] + (t.shape[-1] // 32,), dtype=torch.uint8, device="cuda")
+    (moe.moe_quantize_mxfp4 if fmt == "mxfp4" else moe.moe_quantize_mxfp8)(t, codes, scales)
+    return codes, scales
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_tile_edges_mx(fmt):
+    s = EDGE[fmt]
+    wk = wl.Workload(s)
+    x, w1, w2 = wk.x(), wk.w1(), wk.w2()
+    lg, idx, w = _edge_logits(s, wk.logits())
+    cfg = cfg_of(s)
+    (xq, xs), (w1q, w1s), (w2q, w2s) = _quantize(fmt, x), _quantize(fmt, w1), _quantize(fmt, w2)
+    buf = moe.alloc_forward(cfg, training=True)
+    buf["y"].fill_(float("nan"))
+    buf["gu_stash"].fill_(float("nan"))
+    moe.moe_forward(cfg, to_dev(lg, "f32"), xq, w1q, w2q, buf, x_scale=xs, w1_scale=w1s, w2_scale=w2s)
+    torch.cuda.synchronize()
+    offsets, row_map = _check_groups(s, buf, idx)
+    xq_o, xs_o = orc.mx_quantize(x, fmt)
+    w1q_o, w1s_o = orc.mx_quantize(w1, fmt)
+    w2q_o, w2s_o = orc.mx_quantize(w2, fmt)
+    n = int(offsets[-1])
+    assert np.array_equal(to_host(buf["xp"])[:n], orc.permute(xq_o, row_map, n))
+    assert np.array_equal(to_host(buf["xp_scale"])[:n], orc.permute(xs_o, row_map, n))
+    ref = orc.forward_tokens(s, np.arange(s.T), xq_o, w1q_o, w2q_o, idx, w, xs_o, w1s_o, w2s_o, want_stash=True)
+    rm = row_map.ravel()
+    assert_parity(decode("bf16", to_host(buf["gu_stash"])[rm]), decode("bf16", ref["stash"].reshape(-1, 2 * s.F)),
+                  "bf16", "stash")
+    h, hs = to_host(buf["h"])[rm], to_host(buf["h_scale"])[rm]
+    if fmt == "mxfp8":
+        assert_parity(orc.mx_dequantize(h, hs),
+                      orc.mx_dequantize(ref["h"].reshape(-1, s.F), ref["h_scale"].reshape(-1, s.F // 32)), "e4m3", "h")
+        out = "e4m3_out"
+    else:
+        check_h(h, hs, ref["h"].reshape(-1, s.F // 2), ref["h_scale"].reshape(-1, s.F // 32))
+        out = "e2m1_out"
+    # the down GEMM on the GPU's own h, then y end to end
+    experts = np.searchsorted(offsets, rm, side="right") - 1
+    yp_ref = orc.down_projection(s, experts, h, hs, w2q_o, w2s_o)
+    assert_parity(decode("bf16", to_host(buf["yp"])[rm]), decode("bf16", yp_ref), "bf16", "Yp")
+    assert_parity(decode("bf16", to_host(buf["y"])), decode("bf16", ref["y"]), out, "y")
