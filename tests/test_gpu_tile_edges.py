@@ -6,7 +6,7 @@ router's logits are set so that top-1 routing gives the experts exactly 256,
 257, 0, 1, 255, 512, 128 and 129 rows: a whole tile, a one-row tail, an empty
 expert, a lone row, a tile one row short, two whole tiles, and half a tile
 with and without one more row.  Every output is compared with the oracle in
-full, as for the small shapes."""
+full, as for the small shapes, and the bf16 backward likewise."""
 import numpy as np
 import pytest
 import torch
@@ -64,6 +64,52 @@ def test_tile_edges_bf16():
                   "bf16", "stash")
     assert_parity(decode("bf16", to_host(buf["yp"])[rm]), decode("bf16", ref["yp"].reshape(-1, s.H)), "bf16", "Yp")
     assert_parity(decode("bf16", to_host(buf["y"])), decode("bf16", ref["y"]), "bf16", "y")
+
+
+def test_tile_edges_bf16_backward():
+    """The backward at the same group sizes: the dgrad tiles see the same
+    edges, and the weight gradients contract over 0, 1, 128, 129, 255, 256,
+    257 and 512 rows (K stages of 64 rows, whole and ragged); the empty
+    expert's dW is exactly zero."""
+    s = EDGE["bf16"]
+    inp = Inputs(s, want_dy=True)
+    inp.logits, idx, w = _edge_logits(s, inp.logits)
+    fwd = run_forward(inp, training=True)
+    cfg = cfg_of(s)
+    bwd = moe.alloc_backward(cfg)
+    for key in ("dyp", "dgu", "dxp", "dx", "dw1", "dw2"):
+        bwd[key].fill_(float("nan"))
+    d = inp.dev
+    moe.moe_backward(cfg, d["dy"], d["w1"], d["w2"], fwd, bwd)
+    torch.cuda.synchronize()
+    counts, offsets, row_map, src_map, _ = orc.group(idx, s.E, s.align)
+    ref = orc.forward_tokens(s, np.arange(s.T), inp.x, inp.w1, inp.w2, idx, w, want_stash=True)
+    R = src_map.shape[0]
+    h_rows = np.zeros((R, s.F), np.uint16)
+    st_rows = np.zeros((R, 2 * s.F), np.uint16)
+    rm = row_map.ravel()
+    h_rows[rm] = ref["h"].reshape(-1, s.F)
+    st_rows[rm] = ref["stash"].reshape(-1, 2 * s.F)
+    g = orc.backward(s, inp.x, inp.w1, inp.w2, w, row_map, src_map, offsets, h_rows, st_rows, inp.dy)
+    n = int(offsets[-1])
+    for key in ("dyp", "dgu", "dxp"):
+        assert_parity(decode("bf16", to_host(bwd[key])[:n]), decode("bf16", g[key][:n]), "bf16", key)
+    assert_parity(decode("bf16", to_host(bwd["dx"])), decode("bf16", g["dx"]), "bf16", "dX")
+    dw1, dw2 = to_host(bwd["dw1"]), to_host(bwd["dw2"])
+    assert_parity(dw1, g["dw1"], "f32acc", "dW1")
+    assert_parity(dw2, g["dw2"], "f32acc", "dW2")
+    empty = np.where(counts == 0)[0]
+    assert len(empty) == 1 and np.all(dw1[empty] == 0) and np.all(dw2[empty] == 0)
+    # Against float64 products of the GPU's own bf16 operands only the float32
+    # accumulation separates the weight gradients (a rounding flip of h or dYp
+    # moves an element of dW by up to a few bounds above)
+    h_g, xp_g = (decode("bf16", to_host(fwd[key])).astype(np.float64) for key in ("h", "xp"))
+    dyp_g, dgu_g = (decode("bf16", to_host(bwd[key])).astype(np.float64) for key in ("dyp", "dgu"))
+    for e in range(s.E):
+        r = slice(int(offsets[e]), int(offsets[e + 1]))
+        for got, ref, name in ((dw2[e], dyp_g[r].T @ h_g[r], "dW2"), (dw1[e], dgu_g[r].T @ xp_g[r], "dW1")):
+            err = float(np.abs(got - ref).max()) if ref.size else 0.0
+            assert err <= 2.0 ** -16 * max(float(np.abs(ref).max()), 1e-30), (name, e, err)
 
 
 def _quantize(fmt, v):
