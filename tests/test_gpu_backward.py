@@ -157,6 +157,20 @@ def test_backward_full_size_skewed():
         assert_parity(dw2[e], g["dw2"][e], "f32acc", f"dW2 of expert {e} ({counts[e]} rows)")
     assert_parity(dw1, g["dw1"], "f32acc", "dW1")
     assert_parity(dw2, g["dw2"], "f32acc", "dW2")
+    # The two hottest (split) experts against float64 products of the call's
+    # own bf16 operands (torch float64 matmuls on the device): only the float32
+    # accumulation and the order in which the units' partial sums are added
+    # separate them, so a unit, slot or reduction fault cannot hide in the
+    # rounding flips that the oracle comparison has to allow.
+    for e in hot[:2]:
+        r = slice(int(offsets[e]), int(offsets[e + 1]))
+        pairs = (("dW2", bwd["dw2"][e], bwd["dyp"][r], fwd["h"][r]), ("dW1", bwd["dw1"][e], bwd["dgu"][r], fwd["xp"][r]))
+        for name, got, a, b in pairs:
+            ref = torch.mm(a.to(torch.float64).t().contiguous(), b.to(torch.float64))
+            err = float((got.to(torch.float64) - ref).abs().max())
+            top = float(ref.abs().max())
+            print(f"{name} of expert {e} ({counts[e]} rows) against its own operands: max error {err / top:.2e} of the maximum")
+            assert err <= 2.0 ** -14 * top, (name, int(e), err, top)
 
 
 def test_backward_graph_capture_replays():
