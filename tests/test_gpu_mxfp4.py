@@ -241,3 +241,39 @@ def test_forward_mxfp4_full_size():
     yp_ref = orc.down_projection(s, _experts_of_rows(offsets, rows_np), h, hs, w2q_o, w2s_o)
     assert_parity(decode("bf16", to_host(buf["yp"][rows])), decode("bf16", yp_ref), "bf16", "Yp")
     assert_parity(decode("bf16", to_host(buf["y"])[toks]), decode("bf16", ref["y"]), "e2m1_out", "y")
+
+
+def test_forward_graph_capture_replays():
+    """The MXFP4 forward captures into a HIP graph; replays, with eager work
+    between them and the outputs overwritten before each, give the eager
+    bytes."""
+    s = SHAPES["small_mxfp4_skew_align"]
+    w = wl.Workload(s)
+    cfg = cfg_of(s)
+    (xq, xs), (w1q, w1s), (w2q, w2s) = _gpu_quantize(w.x()), _gpu_quantize(w.w1()), _gpu_quantize(w.w2())
+    logits = to_dev(w.logits(), "f32")
+    sc = dict(x_scale=xs, w1_scale=w1s, w2_scale=w2s)
+    buf = moe.alloc_forward(cfg)
+    moe.moe_forward(cfg, logits, xq, w1q, w2q, buf, **sc)
+    torch.cuda.synchronize()
+    keys = [k for k, v in buf.items() if v is not None and k not in ("ws", "err")]
+    eager = {k: to_host(buf[k]).copy() for k in keys}
+    n = int(eager["offsets"][-1])
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            moe.moe_forward(cfg, logits, xq, w1q, w2q, buf, **sc)
+    for rep in range(3):
+        buf["y"].fill_(float("nan"))
+        buf["yp"].fill_(float("nan"))
+        buf["h"].fill_(0x5A)
+        buf["xp"].fill_(0xA5)
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (logits * 2).sum().item()  # unrelated eager work between replays
+        for k in keys:
+            got, v = to_host(buf[k]), eager[k]
+            if k in ("xp", "xp_scale", "h", "h_scale", "yp", "src_map"):
+                got, v = got[:n], v[:n]
+            assert np.array_equal(got.view(np.uint8), v.view(np.uint8)), f"replay {rep}: {k} differs"
