@@ -112,13 +112,13 @@ class Inputs:
         self.s = shape
         w = wl.Workload(shape)
         self.logits = w.logits()
-        if shape.dtype == "mxfp8":
+        if shape.dtype in ("mxfp8", "mxfp4"):
             self.x_f32 = w.x()
             self.w1_f32 = w.w1()
             self.w2_f32 = w.w2()
-            self.x, self.x_scale = orc.mx_quantize(self.x_f32)
-            self.w1, self.w1_scale = orc.mx_quantize(self.w1_f32)
-            self.w2, self.w2_scale = orc.mx_quantize(self.w2_f32)
+            self.x, self.x_scale = orc.mx_quantize(self.x_f32, shape.dtype)
+            self.w1, self.w1_scale = orc.mx_quantize(self.w1_f32, shape.dtype)
+            self.w2, self.w2_scale = orc.mx_quantize(self.w2_f32, shape.dtype)
         else:
             self.x = w.x()
             self.w1 = w.w1()
@@ -132,7 +132,7 @@ class Inputs:
         f = self.s.dtype
         d = {"logits": to_dev(self.logits, "f32"), "x": to_dev(self.x, f), "w1": to_dev(self.w1, f),
              "w2": to_dev(self.w2, f)}
-        if f == "mxfp8":
+        if f in ("mxfp8", "mxfp4"):
             d["x_scale"] = to_dev(self.x_scale, "u8")
             d["w1_scale"] = to_dev(self.w1_scale, "u8")
             d["w2_scale"] = to_dev(self.w2_scale, "u8")

@@ -2,7 +2,7 @@
 instead of a caller workspace) against moe_forward, through the C ABI: every
 output byte for byte, on two calls in a row, the second on a smaller input (the
 array keeps the first call's contents), for bf16 with the per-row epilogue
-weights and the SwiGLU clamp, and for MXFP8."""
+weights and the SwiGLU clamp, and for MXFP8 and MXFP4."""
 import numpy as np
 import pytest
 import torch
@@ -46,9 +46,10 @@ def _same(a, b, label):
     ("finegrained_bf16", "small_bf16_renorm", "combine", 0.0),
     ("small_bf16_sigmoid_align", "small_bf16_softmax", "fc2", 7.0),
     ("small_mxfp8", "small_mxfp8_k512", "fc1", 0.0),
+    ("small_mxfp4", "small_mxfp4_align128", "combine", 0.0),
 ])
 def test_noalloc_forward_matches_forward_twice(first, second, site, limit):
-    shapes = {s.name: s for s in wl.small_shapes() + wl.WORKLOADS}
+    shapes = {s.name: s for s in wl.small_shapes() + wl.mxfp4_shapes() + wl.WORKLOADS}
     for name in (first, second):  # the second call is smaller than the first
         s = shapes[name]
         cfg = moe.MoEConfig(s.T, s.H, s.F, s.E, s.k, s.align, s.score, bool(s.renorm), s.dtype, site, limit)
