@@ -29,10 +29,10 @@ EDGE = {
 }
 
 
-def _edge_logits(s, base):
+def _edge_logits(s, base, sizes=SIZES):
     """The workload's logits with +8 on one expert per token, the experts
-    dealt to the tokens in a seeded order so that expert e gets SIZES[e]."""
-    owner = np.random.default_rng(s.seed).permutation(np.repeat(np.arange(s.E), SIZES))
+    dealt to the tokens in a seeded order so that expert e gets sizes[e]."""
+    owner = np.random.default_rng(s.seed).permutation(np.repeat(np.arange(s.E), sizes))
     lg = np.array(base, np.float32)
     lg[np.arange(s.T), owner] += np.float32(8.0)
     idx, w = orc.route(lg, s.k, s.score, s.renorm)
@@ -40,10 +40,10 @@ def _edge_logits(s, base):
     return lg, idx, w
 
 
-def _check_groups(s, buf, idx):
+def _check_groups(s, buf, idx, sizes=SIZES):
     assert np.array_equal(to_host(buf["idx"]), idx)
     counts, offsets, row_map, src_map, _ = orc.group(idx, s.E, s.align)
-    assert np.array_equal(counts, SIZES)
+    assert np.array_equal(counts, sizes)
     for key, ref in (("counts", counts), ("offsets", offsets), ("row_map", row_map), ("src_map", src_map)):
         assert np.array_equal(to_host(buf[key]), ref), key
     return offsets, row_map
@@ -74,7 +74,30 @@ def test_tile_edges_bf16_backward():
     s = EDGE["bf16"]
     inp = Inputs(s, want_dy=True)
     inp.logits, idx, w = _edge_logits(s, inp.logits)
+    _backward_parity(s, inp, idx, w, SIZES)
+
+
+# Groups on the edges of the weight gradients' row units: with one 128 x 64
+# tile per gradient the unit is max(4096, T k / 512) rounded down to 64 =
+# 4096 rows, so these experts take one unit (4095, 4096), two (4097: the
+# second of one row; 8192), three (8193) or none (0), beside small ones.
+UNIT_SIZES = np.array([4096, 4097, 1, 8192, 0, 4095, 64, 8193])
+
+
+def test_weight_gradient_unit_edges():
+    s = wl.MoEShape("edge_units_bf16", int(UNIT_SIZES.sum()), 128, 64, 8, 1, "softmax", False, "bf16",
+                    backward=True, seed=2033)
+    assert max(4096, s.T * s.k // 512 // 64 * 64) == 4096
+    inp = Inputs(s, want_dy=True)
+    inp.logits, idx, w = _edge_logits(s, inp.logits, UNIT_SIZES)
+    _backward_parity(s, inp, idx, w, UNIT_SIZES)
+
+
+def _backward_parity(s, inp, idx, w, sizes):
+    """The backward of a forward with these group sizes against the oracle in
+    full, and the weight gradients against their own operands."""
     fwd = run_forward(inp, training=True)
+    _check_groups(s, fwd, idx, sizes)
     cfg = cfg_of(s)
     bwd = moe.alloc_backward(cfg)
     for key in ("dyp", "dgu", "dxp", "dx", "dw1", "dw2"):
